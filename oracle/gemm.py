@@ -1,0 +1,117 @@
+"""Grouped GEMMs as per-expert dense products of dequantized operands, in fp64
+(oracle; test infrastructure only).
+
+The grouped GEMM equals, group by group, a dense GEMM of the dequantized
+operands: the pure-JAX fallback ("gemm.py", ``_jax_scaled_matmul``: TN, data
+(B, M, K) x (B, N, K) with scales (B, M, K/block)) and the parity tests of
+"[Common][PyTorch] Add row-scaled NVFP4 support to grouped-tensor GEMM"
+(per-expert dense GEMM over byte-identical operands) define it that way.
+Each product of two decoded elements is exact in fp64 and the K-sums carry
+only fp64 rounding, far below the GEMM tolerance.
+"""
+
+import numpy as np
+
+from .quantize import mxfp8_dequant_rows, nvfp4_block_dequant, mx_scale_row_len, MX_BLOCK
+
+
+def _group_of_rows(offsets, rows):
+    off = np.asarray(offsets, dtype=np.int64)
+    return np.searchsorted(off, np.asarray(rows), side="right") - 1
+
+
+def mxfp8_fprop(a_data, a_scales, b_data, b_scales, offsets, k, rows=None):
+    """FPROP (TN, ragged rows; "gemm.py", ``grouped_gemm`` with lhs first dims
+    ragged, rhs [G, N, K]):
+        Y[r, n] = sum_k dq(A)[r, k] * dq(B)[g, n, k]  for r in [off[g], off[g+1]).
+
+    a_data [>=live, k], a_scales [>=live, roundup(k/32,4)], b_data [G, N, k],
+    b_scales [G, N, roundup(k/32,4)].  ``rows`` (optional) selects live rows to
+    compute; default all live rows.  Returns float64 [len(rows), N]."""
+    off = np.asarray(offsets, dtype=np.int64)
+    G, N = b_data.shape[0], b_data.shape[1]
+    srow = mx_scale_row_len(k)
+    if rows is None:
+        rows = np.arange(int(off[-1]))
+    rows = np.asarray(rows, dtype=np.int64)
+    a_data = np.asarray(a_data).reshape(-1, k)
+    a_scales = np.asarray(a_scales).reshape(-1, srow)
+    out = np.zeros((len(rows), N), dtype=np.float64)
+    grp = _group_of_rows(off, rows)
+    for g in range(G):
+        sel = np.nonzero(grp == g)[0]
+        if len(sel) == 0:
+            continue
+        dqa = mxfp8_dequant_rows(a_data[rows[sel]], a_scales[rows[sel]], k)
+        dqb = mxfp8_dequant_rows(np.asarray(b_data[g]).reshape(N, k),
+                                 np.asarray(b_scales[g]).reshape(N, srow), k)
+        out[sel] = dqa @ dqb.T
+    return out
+
+
+def mxfp8_wgrad(dy_col, dy_col_scales, x_col, x_col_scales, padded_offsets, n, k, groups=None,
+                out_rows=None):
+    """WGRAD (NT, ragged contraction; "gemm.py", ``grouped_gemm`` with rhs first
+    dims ragged, uniform (G, ...) output):
+        dW[g, i, j] = sum_{t < m_g} dq(dY)[off[g] + t, i] * dq(X)[off[g] + t, j]
+
+    taken from the columnwise copies (group g: dY^T block [n, m~_g], X^T block
+    [k, m~_g], zero padding beyond m_g).  An empty group gives dW[g] = 0.
+    ``groups`` / ``out_rows`` optionally restrict the computed groups / rows i.
+    Returns float64 [len(groups), len(out_rows), k]."""
+    poff = np.asarray(padded_offsets, dtype=np.int64)
+    G = len(poff) - 1
+    groups = list(range(G)) if groups is None else list(groups)
+    out_rows = np.arange(n) if out_rows is None else np.asarray(out_rows, dtype=np.int64)
+    out = np.zeros((len(groups), len(out_rows), k), dtype=np.float64)
+    for gi, g in enumerate(groups):
+        mp = int(poff[g + 1] - poff[g])
+        if mp == 0:
+            continue
+        srow = mx_scale_row_len(mp)
+        a = np.asarray(dy_col[poff[g] * n:poff[g + 1] * n]).reshape(n, mp)[out_rows]
+        a_s = np.asarray(dy_col_scales[poff[g] * n // MX_BLOCK:poff[g + 1] * n // MX_BLOCK]
+                         ).reshape(n, srow)[out_rows]
+        b = np.asarray(x_col[poff[g] * k:poff[g + 1] * k]).reshape(k, mp)
+        b_s = np.asarray(x_col_scales[poff[g] * k // MX_BLOCK:poff[g + 1] * k // MX_BLOCK]
+                         ).reshape(k, srow)
+        out[gi] = mxfp8_dequant_rows(a, a_s, mp) @ mxfp8_dequant_rows(b, b_s, mp).T
+    return out
+
+
+def nvfp4_rowscaled_fprop(a_packed, a_bscales, a_tsi, offsets, b_packed, b_bscales, b_tsi,
+                          n_per_group, k, rows=None):
+    """Row-scaled NVFP4 FPROP ("[Common][PyTorch] Add row-scaled NVFP4 support to
+    grouped-tensor GEMM": the outer scales are neutralized in the GEMM, the
+    product goes to an FP32 scratch, and the outer scales are applied afterwards
+    over each group's own rows and columns):
+        S[r, n] = sum_k (e2m1(A) * sd_A)[r, k] * (e2m1(B_g) * sd_B)[n, k]
+        Y[r, n] = S[r, n] * tsi_A[r] * tsi_B_g[n]   for live r in g, n < N_g.
+
+    B holds the experts' [N_g, k] weights one after another (rows
+    sum(N_g)); b_tsi is indexed the same way.  Returns a list, per group, of
+    (row indices, float64 [len(rows in g), N_g])."""
+    off = np.asarray(offsets, dtype=np.int64)
+    npg = [int(v) for v in n_per_group]
+    boff = np.concatenate([[0], np.cumsum(npg)]).astype(np.int64)
+    if rows is None:
+        rows = np.arange(int(off[-1]))
+    rows = np.asarray(rows, dtype=np.int64)
+    grp = _group_of_rows(off, rows)
+    a_packed = np.asarray(a_packed).reshape(-1, k // 2)
+    a_bscales = np.asarray(a_bscales).reshape(-1, k // 16)
+    b_packed = np.asarray(b_packed).reshape(-1, k // 2)
+    b_bscales = np.asarray(b_bscales).reshape(-1, k // 16)
+    result = []
+    for g in range(len(npg)):
+        sel = rows[grp == g]
+        if len(sel) == 0 or npg[g] == 0:
+            result.append((sel, np.zeros((len(sel), npg[g]))))
+            continue
+        a = nvfp4_block_dequant(a_packed[sel], a_bscales[sel], k)
+        b = nvfp4_block_dequant(b_packed[boff[g]:boff[g + 1]], b_bscales[boff[g]:boff[g + 1]], k)
+        s = a @ b.T
+        y = s * np.asarray(a_tsi, np.float64)[sel][:, None] * \
+            np.asarray(b_tsi, np.float64)[boff[g]:boff[g + 1]][None, :]
+        result.append((sel, y))
+    return result

@@ -1,0 +1,163 @@
+"""Grouped MXFP8 and row-scaled NVFP4 quantize, and the matching dequantize
+(oracle; test infrastructure only).
+
+Operands are bf16 bit patterns (uint16) of a row-major [rows, cols] tensor whose
+first ``offsets[G]`` rows are live and split into G consecutive groups
+(``offsets`` as produced by ``oracle.offsets.group_offsets``).  Rows at or past
+``offsets[G]`` are capacity rows: never read, never written.
+"""
+
+import numpy as np
+
+from .formats import (bf16_bits_to_f64, e4m3_encode, e4m3_decode, e2m1_encode, e2m1_decode,
+                      e8m0_from_amax, e8m0_decode, f32, E2M1_MAX, E4M3_MAX)
+from .layout import (mx_scales_to_gemm_order, mx_scales_from_gemm_order, mx_scale_row_bytes,
+                     fp4_pack, fp4_unpack)
+
+MX_BLOCK = 32
+NVFP4_BLOCK = 16
+COLWISE_PAD = 128
+FLT_MAX = np.float32(np.finfo(np.float32).max)
+
+
+def _mx_encode_blocks(vals):
+    """[..., 32] exact values -> (E4M3 codes [..., 32], E8M0 bytes [...]).
+
+    One MX block: shared scale from the block's largest magnitude, each element
+    divided by that power of two (exact) and rounded to E4M3 (ties to even,
+    saturating)."""
+    amax = np.abs(vals).max(axis=-1)
+    sbyte = e8m0_from_amax(amax)
+    scaled = vals / e8m0_decode(sbyte)[..., None]
+    return e4m3_encode(scaled), sbyte
+
+
+def mxfp8_rowwise(x_bits, offsets):
+    """Rowwise MXFP8 quantize: 32-element blocks along each row (the contraction
+    dim of an fprop activation or of a weight, "gemm.py",
+    ``_quantize_gemm_operands``).
+
+    Returns (data [live, C] uint8 E4M3, scales [live, roundup(C/32, 4)] uint8
+    E8M0 in the GEMM-ready order)."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    rows, cols = x_bits.shape
+    if cols % MX_BLOCK:
+        raise ValueError("cols must be a multiple of 32")
+    live = int(offsets[-1])
+    if live > rows:
+        raise ValueError("sum of group sizes exceeds the row capacity")
+    x = bf16_bits_to_f64(x_bits[:live]).reshape(live, cols // MX_BLOCK, MX_BLOCK)
+    codes, sbyte = _mx_encode_blocks(x)
+    return codes.reshape(live, cols), mx_scales_to_gemm_order(sbyte)
+
+
+def mxfp8_colwise(x_bits, offsets, padded_offsets):
+    """Columnwise MXFP8 quantize for a contraction over ragged token rows
+    (wgrad): per group g and column c, 32-token blocks starting at the group's
+    first row, written transposed.
+
+    Reading: a group's token count is padded to a multiple of 128 with zero
+    values (so padding encodes to 0x00 and all-padding blocks get scale 0x00),
+    following "padding is included in the group sizes" ("gemm.py",
+    ``grouped_gemm``) and the 128-alignment of the V2 kernels ("[JAX] MXFP8
+    Grouped Quant+GEMM", review threads).
+
+    Group g's data is a row-major [C, m~_g] block at element offset
+    ``padded_offsets[g] * C`` and its scales a [C, m~_g / 32] block (GEMM-ready
+    order) at ``padded_offsets[g] * C / 32``.  Returns (data, scales) as flat
+    uint8 arrays of padded_offsets[G] * C and padded_offsets[G] * C / 32 bytes."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    rows, cols = x_bits.shape
+    off = np.asarray(offsets, dtype=np.int64)
+    poff = np.asarray(padded_offsets, dtype=np.int64)
+    if int(off[-1]) > rows:
+        raise ValueError("sum of group sizes exceeds the row capacity")
+    data = np.zeros(int(poff[-1]) * cols, dtype=np.uint8)
+    scales = np.zeros(int(poff[-1]) * cols // MX_BLOCK, dtype=np.uint8)
+    for g in range(len(off) - 1):
+        m = int(off[g + 1] - off[g])
+        mp = int(poff[g + 1] - poff[g])
+        if mp < m or mp % COLWISE_PAD:
+            raise ValueError("padded offsets inconsistent with the group sizes")
+        if mp == 0:
+            continue
+        xt = np.zeros((cols, mp), dtype=np.float64)
+        xt[:, :m] = bf16_bits_to_f64(x_bits[off[g]:off[g + 1]]).T
+        codes, sbyte = _mx_encode_blocks(xt.reshape(cols, mp // MX_BLOCK, MX_BLOCK))
+        data[poff[g] * cols:poff[g + 1] * cols] = codes.reshape(-1)
+        scales[poff[g] * cols // MX_BLOCK:poff[g + 1] * cols // MX_BLOCK] = \
+            mx_scales_to_gemm_order(sbyte).reshape(-1)
+    return data, scales
+
+
+def mxfp8_dequant_rows(data, stored_scales, cols):
+    """Q->DQ of MXFP8 rows: undo the GEMM-ready scale order, then
+    element * 2**(scale - 127).  data [R, cols], stored_scales [R, roundup(cols/32, 4)]."""
+    data = np.asarray(data, dtype=np.uint8).reshape(-1, cols)
+    sbyte = mx_scales_from_gemm_order(np.asarray(stored_scales).reshape(data.shape[0], -1),
+                                      cols // MX_BLOCK)
+    vals = e4m3_decode(data).reshape(data.shape[0], cols // MX_BLOCK, MX_BLOCK)
+    return (vals * e8m0_decode(sbyte)[..., None]).reshape(data.shape[0], cols)
+
+
+def nvfp4_rowscaled(x_bits, offsets):
+    """Row-scaled NVFP4 quantize of the live rows.
+
+    Per row r: an FP32 outer scale from the row's largest magnitude, the
+    per-row analogue of the tensor scale ``amax / (6 * 448)`` ("gemm.py",
+    ``_get_nvfp4_tensor_scale_inv``; per-row / per-column outer scales: "[Common]
+    [PyTorch] Add row-scaled NVFP4 support to grouped-tensor GEMM").  Per
+    16-element block: an E4M3 scale; elements in E2M1.
+
+    Reading of the float32 steps (the pages fix only the outer scale), in this
+    order, every operation rounded to float32:
+      S    = 2688 / amax_r (1 if amax_r == 0; capped at FLT_MAX)
+      s_f  = (bmax / 6) * S          -> s8 = E4M3(s_f), sd = decode(s8)
+      enc  = S / sd (0 if sd == 0; capped at FLT_MAX)
+      q    = E2M1(x * enc)
+    so that x ~= e2m1(q) * sd * tsi_r with tsi_r = amax_r / 2688.
+
+    Returns (packed [live, C/2] uint8, block scales [live, C/16] uint8 E4M3,
+    outer scale tsi [live] float32)."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    rows, cols = x_bits.shape
+    if cols % MX_BLOCK:
+        raise ValueError("cols must be a multiple of 32")
+    live = int(offsets[-1])
+    if live > rows:
+        raise ValueError("sum of group sizes exceeds the row capacity")
+    x = f32(bf16_bits_to_f64(x_bits[:live]))                    # exact in float32
+    two688 = np.float32(E2M1_MAX * E4M3_MAX)
+    with np.errstate(divide="ignore", over="ignore", invalid="ignore"):
+        amax = np.abs(x).max(axis=1) if cols else np.zeros(live, np.float32)
+        tsi = f32(amax / two688)
+        big_s = np.where(amax > 0, f32(two688 / amax), np.float32(1.0))
+        big_s = np.minimum(big_s, FLT_MAX).astype(np.float32)
+        blocks = x.reshape(live, cols // NVFP4_BLOCK, NVFP4_BLOCK)
+        bmax = np.abs(blocks).max(axis=2)
+        s_f = f32(f32(bmax / np.float32(E2M1_MAX)) * big_s[:, None])
+        s8 = e4m3_encode(s_f.astype(np.float64))
+        sd = f32(e4m3_decode(s8))
+        enc = np.where(sd == 0, np.float32(0.0), np.minimum(f32(big_s[:, None] / sd), FLT_MAX))
+        enc = enc.astype(np.float32)
+        v = f32(blocks * enc[..., None])
+    q = e2m1_encode(v.astype(np.float64)).reshape(live, cols)
+    return fp4_pack(q), s8, tsi.astype(np.float32)
+
+
+def nvfp4_block_dequant(packed, block_scales, cols):
+    """E2M1 element times its decoded E4M3 block scale (no outer scale)."""
+    q = fp4_unpack(np.asarray(packed).reshape(-1, cols // 2))
+    vals = e2m1_decode(q).reshape(q.shape[0], cols // NVFP4_BLOCK, NVFP4_BLOCK)
+    sd = e4m3_decode(np.asarray(block_scales).reshape(q.shape[0], cols // NVFP4_BLOCK))
+    return (vals * sd[..., None]).reshape(q.shape[0], cols)
+
+
+def nvfp4_dequant(packed, block_scales, tsi, cols):
+    """Full Q->DQ: e2m1 * block scale * outer scale."""
+    return nvfp4_block_dequant(packed, block_scales, cols) * \
+        np.asarray(tsi, dtype=np.float64)[:, None]
+
+
+def mx_scale_row_len(cols):
+    return mx_scale_row_bytes(cols // MX_BLOCK)

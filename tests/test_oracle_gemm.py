@@ -1,0 +1,150 @@
+"""Pins of the oracle's grouped GEMMs (CPU only).
+
+* exact integer arithmetic: inputs whose quantization is lossless (small
+  integers), so every grouped product must equal the integer per-expert
+  product of the raw inputs -- this catches a wrong group, a transposed
+  operand, a wrong contraction range or a dropped padding rule;
+* correctly rounded sums (math.fsum over exact fp64 products) of the test's
+  own decode of the stored bytes;
+* grouped == per-expert calls on slices.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import formats as F
+from oracle import gemm as GM
+from oracle import offsets as O
+from oracle import quantize as Q
+import workloads
+
+
+def _int_bits(rng, shape, lo=-3, hi=3):
+    v = rng.integers(lo, hi + 1, shape).astype(np.float32)
+    return F.f32_to_bf16_bits_rne(v), v.astype(np.int64)
+
+
+def test_fprop_exact_on_lossless_inputs():
+    rng = np.random.default_rng(21)
+    sizes = np.array([32, 0, 64, 32], np.int32)
+    K, N, G = 128, 48, 4
+    xb, xi = _int_bits(rng, (128, K))
+    wb, wi = _int_bits(rng, (G * N, K))
+    _, off = O.group_offsets(sizes)
+    ad, asc = Q.mxfp8_rowwise(xb, off)
+    bd, bsc = Q.mxfp8_rowwise(wb, np.array([0, G * N]))
+    y = GM.mxfp8_fprop(ad, asc, bd.reshape(G, N, K), bsc.reshape(G, N, -1), off, K)
+    for g in range(G):
+        want = xi[off[g]:off[g + 1]] @ wi[g * N:(g + 1) * N].T
+        assert np.array_equal(y[off[g]:off[g + 1]], want.astype(np.float64))
+
+
+def test_wgrad_exact_on_lossless_inputs():
+    rng = np.random.default_rng(22)
+    sizes = np.array([37, 0, 130, 5], np.int32)
+    M, N, K = int(sizes.sum()), 40, 64
+    dyb, dyi = _int_bits(rng, (M, N))
+    xb, xi = _int_bits(rng, (M, K))
+    _, off = O.group_offsets(sizes)
+    _, poff = O.group_offsets(sizes, pad_to=128)
+    dyc, dys = Q.mxfp8_colwise(dyb, off, poff)
+    xc, xs = Q.mxfp8_colwise(xb, off, poff)
+    dw = GM.mxfp8_wgrad(dyc, dys, xc, xs, poff, N, K)
+    for g in range(4):
+        want = dyi[off[g]:off[g + 1]].T @ xi[off[g]:off[g + 1]]
+        assert np.array_equal(dw[g], want.astype(np.float64)), g
+    assert np.all(dw[1] == 0)
+
+
+def _decode_rows_fsum_check(data, stored, k):
+    """The test's own decode: bit fields -> value, scale order undone by hand."""
+    rows = data.shape[0]
+    vals = np.zeros((rows, k))
+    for r in range(rows):
+        logical = []
+        for q in range(0, stored.shape[1], 4):
+            s0, s2, s1, s3 = stored[r, q:q + 4]
+            logical += [s0, s1, s2, s3]
+        for j in range(k):
+            c = int(data[r, j])
+            e, m = (c >> 3) & 15, c & 7
+            v = m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+            if c & 0x80:
+                v = -v
+            vals[r, j] = v * 2.0 ** (int(logical[j // 32]) - 127)
+    return vals
+
+
+def test_fprop_fsum_on_tiny_config():
+    w = workloads.get("tiny")
+    t = workloads.tensors(w)
+    xb, wb = workloads.bf16_bits(t["x"]), workloads.bf16_bits(t["w"])
+    K, N, G = w.k, w.n, w.G
+    _, off = O.group_offsets(w.sizes)
+    ad, asc = Q.mxfp8_rowwise(xb, off)
+    bd, bsc = Q.mxfp8_rowwise(wb.reshape(G * N, K), np.array([0, G * N]))
+    y = GM.mxfp8_fprop(ad, asc, bd.reshape(G, N, K), bsc.reshape(G, N, -1), off, K)
+    a = _decode_rows_fsum_check(ad, asc, K)
+    b = _decode_rows_fsum_check(bd, bsc, K)
+    for r in range(0, 128, 5):
+        g = int(np.searchsorted(off, r, side="right") - 1)
+        for n in range(0, N, 3):
+            ref = math.fsum(a[r] * b[g * N + n])
+            assert abs(y[r, n] - ref) <= 1e-12 * max(1.0, abs(ref))
+
+
+def test_grouped_equals_per_expert_gemm():
+    rng = np.random.default_rng(23)
+    sizes = np.array([10, 0, 33, 21], np.int32)
+    K, N, G = 96, 24, 4
+    xb = F.f32_to_bf16_bits_rne(rng.standard_normal((64, K)).astype(np.float32))
+    wb = F.f32_to_bf16_bits_rne(rng.standard_normal((G * N, K)).astype(np.float32))
+    _, off = O.group_offsets(sizes)
+    ad, asc = Q.mxfp8_rowwise(xb, off)
+    bd, bsc = Q.mxfp8_rowwise(wb, np.array([0, G * N]))
+    bd, bsc = bd.reshape(G, N, K), bsc.reshape(G, N, -1)
+    y = GM.mxfp8_fprop(ad, asc, bd, bsc, off, K)
+    for g in range(G):
+        one = GM.mxfp8_fprop(ad[off[g]:off[g + 1]], asc[off[g]:off[g + 1]], bd[g:g + 1],
+                             bsc[g:g + 1], np.array([0, sizes[g]]), K)
+        assert np.array_equal(y[off[g]:off[g + 1]], one)
+    sub = GM.mxfp8_fprop(ad, asc, bd, bsc, off, K, rows=np.array([5, 40, 63]))
+    assert np.array_equal(sub, y[[5, 40, 63]])
+
+
+def test_nvfp4_exact_on_lossless_inputs_and_widths():
+    """Values on the E2M1 grid with row max 6: S = 448, every block scale 448,
+    enc = 1, so the codes are the values; Y must equal the integer product times
+    the two outer scales, per group over its own N_g columns."""
+    rng = np.random.default_rng(24)
+    grid = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -.5, -1, -1.5, -2, -3, -4, -6])
+    sizes = np.array([3, 0, 5], np.int32)
+    npg = [8, 16, 24]
+    K = 64
+
+    def mk(rows):
+        v = rng.choice(grid, (rows, K))
+        v[:, ::16] = 6.0                  # every block's max is 6
+        return F.f32_to_bf16_bits_rne(v.astype(np.float32)), v
+
+    xb, xv = mk(int(sizes.sum()) + 2)     # 2 capacity rows
+    wb, wv = mk(sum(npg))
+    _, off = O.group_offsets(sizes)
+    ap, asc, at = Q.nvfp4_rowscaled(xb, off)
+    bp, bsc, bt = Q.nvfp4_rowscaled(wb, np.array([0, sum(npg)]))
+    assert np.all(asc == 0x7E) and np.all(bsc == 0x7E)
+    res = GM.nvfp4_rowscaled_fprop(ap, asc, at, off, bp, bsc, bt, npg, K)
+    boff = np.concatenate([[0], np.cumsum(npg)])
+    for g in range(3):
+        rows, y = res[g]
+        assert list(rows) == list(range(off[g], off[g + 1]))
+        assert y.shape == (sizes[g], npg[g])
+        if sizes[g] == 0:
+            continue
+        exact = (xv[rows] @ wv[boff[g]:boff[g + 1]].T) * 448.0 * 448.0
+        want = exact * at[rows].astype(np.float64)[:, None] * bt[boff[g]:boff[g + 1]].astype(np.float64)
+        assert np.allclose(y, want, rtol=1e-14, atol=0)
+        # and this is the raw product within float32 rounding of the outer scales
+        assert np.allclose(y, xv[rows] @ wv[boff[g]:boff[g + 1]].T, rtol=1e-6, atol=1e-9)
