@@ -1,0 +1,205 @@
+"""Python binding of libbsg (include/bsg.h): block-scaled grouped quantize and
+grouped GEMM for MoE expert products on MI355X.
+
+Argument marshalling only.  Every function has the name of its C entry point,
+takes torch tensors (device memory) and enqueues on the current torch stream;
+outputs the caller does not pass are allocated with torch.  Every step of the
+computation runs in the HIP library: if ``libbsg.so`` is missing or fails to
+load, every call raises.
+"""
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbsg.so")
+
+BSG_FPROP_TN = 0
+BSG_WGRAD_NT = 1
+BSG_OUT_BF16 = 0
+BSG_OUT_F32 = 1
+BSG_MAX_GROUPS = 256
+BSG_COLWISE_PAD = 128
+DEV_NEGATIVE_SIZE = 1
+DEV_OVER_CAPACITY = 2
+DEV_BAD_PADDING = 4
+
+EXPORTS = ("bsg_last_error", "bsg_version", "group_offsets_i32_to_i64", "grouped_quantize_mxfp8",
+           "grouped_quantize_nvfp4_rowscaled", "grouped_gemm_mxfp8", "grouped_gemm_nvfp4_rowscaled")
+
+_lib = None
+
+
+class BsgError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__("bsg status %d: %s" % (code, msg))
+        self.code = code
+
+
+def load_library(path=LIB_PATH):
+    """Loads libbsg.so once; raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("libbsg.so not built at %s (run python -m block_scaled_grouped_amd.build)"
+                           % path)
+    lib = ctypes.CDLL(path)
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.bsg_last_error.restype = ctypes.c_char_p
+    lib.bsg_last_error.argtypes = []
+    lib.bsg_version.restype = I32
+    lib.bsg_version.argtypes = []
+    lib.group_offsets_i32_to_i64.restype = I32
+    lib.group_offsets_i32_to_i64.argtypes = [P, I64, I64, I64, P, P, I64, P, P]
+    lib.grouped_quantize_mxfp8.restype = I32
+    lib.grouped_quantize_mxfp8.argtypes = [P, I64, I64, I64, P, P, P, P, I64, P, P, P, P]
+    lib.grouped_quantize_nvfp4_rowscaled.restype = I32
+    lib.grouped_quantize_nvfp4_rowscaled.argtypes = [P, I64, I64, I64, P, P, P, P, P, P]
+    lib.grouped_gemm_mxfp8.restype = I32
+    lib.grouped_gemm_mxfp8.argtypes = [I32, I64, P, P, P, P, P, I64, I64, I64, P, I32, P, P]
+    lib.grouped_gemm_nvfp4_rowscaled.restype = I32
+    lib.grouped_gemm_nvfp4_rowscaled.argtypes = [I64, P, P, P, P, I64, I64, P, P, P, P, P, I64, I32,
+                                                 P, P, P]
+    _lib = lib
+    return lib
+
+
+def _check(rc):
+    if rc != 0:
+        raise BsgError(rc, _lib.bsg_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("bsg operates on device tensors")
+
+
+def mx_scale_row_bytes(cols):
+    """Stored E8M0 bytes per rowwise scale row (cols / 32 rounded up to 4)."""
+    return ((cols // 32 + 3) // 4) * 4
+
+
+def group_offsets_i32_to_i64(sizes, multiplier=1, pad_to=1, capacity=0, sizes_i64=None,
+                             offsets=None, status=None):
+    """int32 [G] sizes -> (int64 [G] sizes * multiplier, int64 [G+1] offsets)."""
+    import torch
+    lib = load_library()
+    _need_cuda(sizes)
+    G = sizes.numel()
+    if sizes_i64 is None:
+        sizes_i64 = torch.empty(G, dtype=torch.int64, device=sizes.device)
+    if offsets is None:
+        offsets = torch.empty(G + 1, dtype=torch.int64, device=sizes.device)
+    _check(lib.group_offsets_i32_to_i64(_ptr(sizes), G, multiplier, pad_to, _ptr(sizes_i64),
+                                        _ptr(offsets), capacity, _ptr(status), _stream(sizes)))
+    return sizes_i64, offsets
+
+
+def grouped_quantize_mxfp8(x, offsets, G=None, rowwise=True, padded_offsets=None,
+                           col_rows_cap=None, row_data=None, row_scales=None, col_data=None,
+                           col_scales=None, status=None):
+    """bf16 [rows_cap, cols] -> dict with "row_data"/"row_scales" (rowwise) and
+    "col_data"/"col_scales" (when padded_offsets is given), uint8 tensors."""
+    import torch
+    lib = load_library()
+    _need_cuda(x, offsets)
+    rows_cap, cols = x.shape
+    G = offsets.numel() - 1 if G is None else G
+    out = {}
+    if rowwise:
+        if row_data is None:
+            row_data = torch.empty((rows_cap, cols), dtype=torch.uint8, device=x.device)
+        if row_scales is None:
+            row_scales = torch.empty((rows_cap, mx_scale_row_bytes(cols)), dtype=torch.uint8,
+                                     device=x.device)
+        out["row_data"], out["row_scales"] = row_data, row_scales
+    else:
+        row_data = row_scales = None
+    if padded_offsets is not None:
+        if col_rows_cap is None:
+            col_rows_cap = rows_cap + BSG_COLWISE_PAD * G
+        if col_data is None:
+            col_data = torch.empty(col_rows_cap * cols, dtype=torch.uint8, device=x.device)
+        if col_scales is None:
+            col_scales = torch.empty(col_rows_cap * cols // 32, dtype=torch.uint8, device=x.device)
+        out["col_data"], out["col_scales"] = col_data, col_scales
+        out["col_rows_cap"] = col_rows_cap
+    _check(lib.grouped_quantize_mxfp8(_ptr(x), rows_cap, cols, G, _ptr(offsets), _ptr(row_data),
+                                      _ptr(row_scales), _ptr(padded_offsets),
+                                      col_rows_cap or 0, _ptr(col_data), _ptr(col_scales),
+                                      _ptr(status), _stream(x)))
+    return out
+
+
+def grouped_quantize_nvfp4_rowscaled(x, offsets, G=None, data=None, block_scales=None, outer=None,
+                                     status=None):
+    """bf16 [rows_cap, cols] -> (E2M1 [rows_cap, cols/2], E4M3 [rows_cap, cols/16], f32 [rows_cap])."""
+    import torch
+    lib = load_library()
+    _need_cuda(x, offsets)
+    rows_cap, cols = x.shape
+    G = offsets.numel() - 1 if G is None else G
+    if data is None:
+        data = torch.empty((rows_cap, cols // 2), dtype=torch.uint8, device=x.device)
+    if block_scales is None:
+        block_scales = torch.empty((rows_cap, cols // 16), dtype=torch.uint8, device=x.device)
+    if outer is None:
+        outer = torch.empty(rows_cap, dtype=torch.float32, device=x.device)
+    _check(lib.grouped_quantize_nvfp4_rowscaled(_ptr(x), rows_cap, cols, G, _ptr(offsets),
+                                                _ptr(data), _ptr(block_scales), _ptr(outer),
+                                                _ptr(status), _stream(x)))
+    return data, block_scales, outer
+
+
+def grouped_gemm_mxfp8(mode, a, a_scales, b, b_scales, offsets, rows_cap, n, k, out=None,
+                       out_dtype=BSG_OUT_BF16, G=None, status=None):
+    """FPROP_TN: out [rows_cap, n]; WGRAD_NT: out [G, n, k].  See include/bsg.h."""
+    import torch
+    lib = load_library()
+    _need_cuda(a, a_scales, b, b_scales, offsets)
+    G = offsets.numel() - 1 if G is None else G
+    if out is None:
+        dt = torch.float32 if out_dtype == BSG_OUT_F32 else torch.bfloat16
+        shape = (rows_cap, n) if mode == BSG_FPROP_TN else (G, n, k)
+        out = torch.empty(shape, dtype=dt, device=a.device)
+    _check(lib.grouped_gemm_mxfp8(mode, G, _ptr(a), _ptr(a_scales), _ptr(b), _ptr(b_scales),
+                                  _ptr(offsets), rows_cap, n, k, _ptr(out), out_dtype, _ptr(status),
+                                  _stream(a)))
+    return out
+
+
+def grouped_gemm_nvfp4_rowscaled(a, a_scales, a_outer, offsets, k, b, b_scales, b_outer,
+                                 n_per_group, out=None, ld_out=None, out_dtype=BSG_OUT_BF16,
+                                 scratch=None, G=None, status=None):
+    """Row-scaled NVFP4 fprop: out [rows_cap, ld_out]; n_per_group is a host list."""
+    import torch
+    lib = load_library()
+    _need_cuda(a, a_scales, a_outer, offsets, b, b_scales, b_outer)
+    rows_cap = a.shape[0]
+    G = offsets.numel() - 1 if G is None else G
+    npg = [int(v) for v in n_per_group]
+    if len(npg) != G:
+        raise ValueError("n_per_group needs G entries")
+    if ld_out is None:
+        ld_out = max(npg) if out is None else out.shape[1]
+    if out is None:
+        dt = torch.float32 if out_dtype == BSG_OUT_F32 else torch.bfloat16
+        out = torch.empty((rows_cap, ld_out), dtype=dt, device=a.device)
+    host_n = (ctypes.c_int64 * G)(*npg)
+    _check(lib.grouped_gemm_nvfp4_rowscaled(G, _ptr(a), _ptr(a_scales), _ptr(a_outer),
+                                            _ptr(offsets), rows_cap, k, _ptr(b), _ptr(b_scales),
+                                            _ptr(b_outer), ctypes.cast(host_n, ctypes.c_void_p),
+                                            _ptr(out), ld_out, out_dtype, _ptr(scratch),
+                                            _ptr(status), _stream(a)))
+    return out

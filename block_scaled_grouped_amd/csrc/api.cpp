@@ -1,0 +1,208 @@
+// C-ABI entry points of libbsg (declared in include/bsg.h): host-side argument
+// validation, then the kernel launchers.  No allocation, no synchronization, no
+// device reads from the host.
+#include "../../include/bsg.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "bsg_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return BSG_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int hip_result(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(BSG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// Largest byte span a single GEMM / quantize tile addresses with 32-bit offsets.
+constexpr int64_t kMaxTileBytes = (int64_t)1 << 31;
+
+}  // namespace
+
+extern "C" {
+
+const char* bsg_last_error(void) { return g_err; }
+
+int bsg_version(void) { return (0 << 16) | 1; }
+
+int group_offsets_i32_to_i64(const int32_t* sizes, int64_t G, int64_t multiplier, int64_t pad_to,
+                             int64_t* sizes_i64, int64_t* offsets, int64_t capacity,
+                             uint32_t* dev_status, void* stream) {
+  if (sizes == nullptr || offsets == nullptr)
+    return fail(BSG_ERR_NULL, "group_offsets_i32_to_i64: sizes and offsets must be non-NULL");
+  if (G < 1 || G > BSG_MAX_GROUPS)
+    return fail(BSG_ERR_SHAPE, "group_offsets_i32_to_i64: G=%lld outside [1, %d]", (long long)G,
+                BSG_MAX_GROUPS);
+  if (multiplier < 1 || pad_to < 1)
+    return fail(BSG_ERR_SHAPE, "group_offsets_i32_to_i64: multiplier=%lld and pad_to=%lld must be >= 1",
+                (long long)multiplier, (long long)pad_to);
+  if (((int64_t)1 << 31) * pad_to > ((int64_t)1 << 62) / multiplier)
+    return fail(BSG_ERR_SHAPE, "group_offsets_i32_to_i64: multiplier * pad_to too large");
+  return hip_result(bsg::launch_group_offsets(sizes, (int)G, multiplier, pad_to, sizes_i64, offsets,
+                                              capacity, dev_status, (hipStream_t)stream),
+                    "group_offsets_i32_to_i64");
+}
+
+int grouped_quantize_mxfp8(const void* x, int64_t rows_cap, int64_t cols, int64_t G,
+                           const int64_t* offsets, uint8_t* row_data, uint8_t* row_scales,
+                           const int64_t* padded_offsets, int64_t col_rows_cap, uint8_t* col_data,
+                           uint8_t* col_scales, uint32_t* dev_status, void* stream) {
+  const char* fn = "grouped_quantize_mxfp8";
+  if (x == nullptr || offsets == nullptr) return fail(BSG_ERR_NULL, "%s: x and offsets must be non-NULL", fn);
+  const bool row = row_data != nullptr || row_scales != nullptr;
+  const bool col = padded_offsets != nullptr || col_data != nullptr || col_scales != nullptr;
+  if (row && (row_data == nullptr || row_scales == nullptr))
+    return fail(BSG_ERR_NULL, "%s: row_data and row_scales go together", fn);
+  if (col && (padded_offsets == nullptr || col_data == nullptr || col_scales == nullptr))
+    return fail(BSG_ERR_NULL, "%s: padded_offsets, col_data and col_scales go together", fn);
+  if (!row && !col) return fail(BSG_ERR_NULL, "%s: no output requested", fn);
+  if (G < 1 || G > BSG_MAX_GROUPS)
+    return fail(BSG_ERR_SHAPE, "%s: G=%lld outside [1, %d]", fn, (long long)G, BSG_MAX_GROUPS);
+  if (rows_cap < 0 || cols <= 0 || cols % 32 != 0)
+    return fail(BSG_ERR_SHAPE, "%s: need rows_cap >= 0 and cols a positive multiple of 32 (got %lld, %lld)",
+                fn, (long long)rows_cap, (long long)cols);
+  if (col && (col_rows_cap < 0 || col_rows_cap * cols >= ((int64_t)1 << 40)))
+    return fail(BSG_ERR_SHAPE, "%s: col_rows_cap=%lld out of range", fn, (long long)col_rows_cap);
+  if (!aligned16(x) || (row && !aligned16(row_data)) || (col && !aligned16(col_data)))
+    return fail(BSG_ERR_ALIGN, "%s: x, row_data and col_data must be 16-byte aligned", fn);
+  if (row && !aligned4(row_scales))
+    return fail(BSG_ERR_ALIGN, "%s: row_scales must be 4-byte aligned", fn);
+  hipStream_t s = (hipStream_t)stream;
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  if (col) {
+    // one pass over x for both directions when both are requested
+    return hip_result(bsg::launch_quantize_mxfp8_colwise(xb, rows_cap, cols, (int)G, offsets,
+                                                         padded_offsets, col_rows_cap, col_data,
+                                                         col_scales, row ? row_data : nullptr,
+                                                         row ? row_scales : nullptr, dev_status, s),
+                      fn);
+  }
+  return hip_result(bsg::launch_quantize_mxfp8_rowwise(xb, rows_cap, cols, (int)G, offsets, row_data,
+                                                       row_scales, dev_status, s),
+                    fn);
+}
+
+int grouped_quantize_nvfp4_rowscaled(const void* x, int64_t rows_cap, int64_t cols, int64_t G,
+                                     const int64_t* offsets, uint8_t* data, uint8_t* block_scales,
+                                     float* outer, uint32_t* dev_status, void* stream) {
+  const char* fn = "grouped_quantize_nvfp4_rowscaled";
+  if (x == nullptr || offsets == nullptr || data == nullptr || block_scales == nullptr || outer == nullptr)
+    return fail(BSG_ERR_NULL, "%s: x, offsets, data, block_scales and outer must be non-NULL", fn);
+  if (G < 1 || G > BSG_MAX_GROUPS)
+    return fail(BSG_ERR_SHAPE, "%s: G=%lld outside [1, %d]", fn, (long long)G, BSG_MAX_GROUPS);
+  if (rows_cap < 0 || cols <= 0 || cols % 32 != 0)
+    return fail(BSG_ERR_SHAPE, "%s: need rows_cap >= 0 and cols a positive multiple of 32", fn);
+  if (cols > 16384)
+    return fail(BSG_ERR_UNSUPPORTED, "%s: cols=%lld above the supported 16384", fn, (long long)cols);
+  if (rows_cap > 0x7fffffffLL) return fail(BSG_ERR_SHAPE, "%s: rows_cap too large", fn);
+  if (!aligned16(x) || !aligned16(data) || !aligned4(outer))
+    return fail(BSG_ERR_ALIGN, "%s: x and data must be 16-byte aligned, outer 4-byte", fn);
+  return hip_result(bsg::launch_quantize_nvfp4_rowscaled(static_cast<const uint16_t*>(x), rows_cap,
+                                                         cols, (int)G, offsets, data, block_scales,
+                                                         outer, dev_status, (hipStream_t)stream),
+                    fn);
+}
+
+int grouped_gemm_mxfp8(int mode, int64_t G, const uint8_t* a, const uint8_t* a_scales,
+                       const uint8_t* b, const uint8_t* b_scales, const int64_t* offsets,
+                       int64_t rows_cap, int64_t n, int64_t k, void* out, int out_dtype,
+                       uint32_t* dev_status, void* stream) {
+  const char* fn = "grouped_gemm_mxfp8";
+  if (a == nullptr || a_scales == nullptr || b == nullptr || b_scales == nullptr || offsets == nullptr ||
+      out == nullptr)
+    return fail(BSG_ERR_NULL, "%s: operands, scales, offsets and out must be non-NULL", fn);
+  if (mode != BSG_FPROP_TN && mode != BSG_WGRAD_NT)
+    return fail(BSG_ERR_UNSUPPORTED, "%s: unknown mode %d", fn, mode);
+  if (out_dtype != BSG_OUT_BF16 && out_dtype != BSG_OUT_F32)
+    return fail(BSG_ERR_UNSUPPORTED, "%s: unknown out_dtype %d", fn, out_dtype);
+  if (G < 1 || G > BSG_MAX_GROUPS)
+    return fail(BSG_ERR_SHAPE, "%s: G=%lld outside [1, %d]", fn, (long long)G, BSG_MAX_GROUPS);
+  if (rows_cap < 0 || n < 1 || k < 1)
+    return fail(BSG_ERR_SHAPE, "%s: need rows_cap >= 0, n >= 1, k >= 1", fn);
+  const int64_t esz = out_dtype == BSG_OUT_F32 ? 4 : 2;
+  if (mode == BSG_FPROP_TN) {
+    if (k % 128 != 0)
+      return fail(BSG_ERR_SHAPE, "%s: FPROP needs k %% 128 == 0 (got %lld)", fn, (long long)k);
+    if (256 * k >= kMaxTileBytes || 256 * n * esz >= kMaxTileBytes || n > 0x7fffffffLL)
+      return fail(BSG_ERR_SHAPE, "%s: n or k too large for one tile's 32-bit offsets", fn);
+  } else {
+    if (n % 32 != 0 || k % 32 != 0)
+      return fail(BSG_ERR_SHAPE, "%s: WGRAD needs n and k multiples of 32", fn);
+    if (256 * rows_cap >= kMaxTileBytes || 256 * k * esz >= kMaxTileBytes)
+      return fail(BSG_ERR_SHAPE, "%s: token capacity or k too large for 32-bit tile offsets", fn);
+  }
+  if (!aligned16(a) || !aligned16(b) || !aligned4(a_scales) || !aligned4(b_scales) || !aligned4(out))
+    return fail(BSG_ERR_ALIGN, "%s: a and b must be 16-byte aligned; scales and out 4-byte", fn);
+  return hip_result(bsg::launch_gemm_mxfp8(mode, (int)G, a, a_scales, b, b_scales, offsets, rows_cap,
+                                           n, k, out, out_dtype == BSG_OUT_F32, dev_status,
+                                           (hipStream_t)stream),
+                    fn);
+}
+
+int grouped_gemm_nvfp4_rowscaled(int64_t G, const uint8_t* a, const uint8_t* a_scales,
+                                 const float* a_outer, const int64_t* offsets, int64_t rows_cap,
+                                 int64_t k, const uint8_t* b, const uint8_t* b_scales,
+                                 const float* b_outer, const int64_t* n_per_group, void* out,
+                                 int64_t ld_out, int out_dtype, float* scratch,
+                                 uint32_t* dev_status, void* stream) {
+  const char* fn = "grouped_gemm_nvfp4_rowscaled";
+  if (a == nullptr || a_scales == nullptr || a_outer == nullptr || offsets == nullptr || b == nullptr ||
+      b_scales == nullptr || b_outer == nullptr || n_per_group == nullptr || out == nullptr)
+    return fail(BSG_ERR_NULL, "%s: operands, scales, offsets, n_per_group and out must be non-NULL", fn);
+  if (out_dtype != BSG_OUT_BF16 && out_dtype != BSG_OUT_F32)
+    return fail(BSG_ERR_UNSUPPORTED, "%s: unknown out_dtype %d", fn, out_dtype);
+  if (G < 1 || G > BSG_MAX_GROUPS)
+    return fail(BSG_ERR_SHAPE, "%s: G=%lld outside [1, %d]", fn, (long long)G, BSG_MAX_GROUPS);
+  if (rows_cap < 0 || k < 64 || k % 64 != 0)
+    return fail(BSG_ERR_SHAPE, "%s: need rows_cap >= 0 and k a positive multiple of 64 (got %lld)", fn,
+                (long long)k);
+  bsg::NvGroupTable tab;
+  memset(&tab, 0, sizeof tab);
+  int64_t max_n = 0, brow = 0;
+  for (int64_t g = 0; g < G; ++g) {
+    const int64_t ng = n_per_group[g];
+    if (ng < 0 || ng > 0x7fffffffLL) return fail(BSG_ERR_SHAPE, "%s: n_per_group[%lld] out of range", fn, (long long)g);
+    tab.n[g] = (int32_t)ng;
+    tab.brow[g] = (int32_t)brow;
+    brow += ng;
+    if (brow > 0x7fffffffLL) return fail(BSG_ERR_SHAPE, "%s: sum of n_per_group too large", fn);
+    if (ng > max_n) max_n = ng;
+  }
+  tab.brow[G] = (int32_t)brow;
+  if (ld_out < max_n || ld_out < 1)
+    return fail(BSG_ERR_SHAPE, "%s: ld_out=%lld below the widest group (%lld)", fn, (long long)ld_out,
+                (long long)max_n);
+  const int64_t esz = (out_dtype == BSG_OUT_F32 || scratch != nullptr) ? 4 : 2;
+  if (256 * (k / 2) >= kMaxTileBytes || 256 * ld_out * esz >= kMaxTileBytes)
+    return fail(BSG_ERR_SHAPE, "%s: k or ld_out too large for 32-bit tile offsets", fn);
+  if (!aligned16(a) || !aligned16(b) || !aligned4(a_scales) || !aligned4(b_scales) || !aligned4(out) ||
+      (scratch != nullptr && !aligned4(scratch)))
+    return fail(BSG_ERR_ALIGN, "%s: a and b must be 16-byte aligned; scales, out and scratch 4-byte", fn);
+  return hip_result(bsg::launch_gemm_nvfp4((int)G, a, a_scales, a_outer, offsets, rows_cap, k, b,
+                                           b_scales, b_outer, tab, (int)max_n, out, ld_out,
+                                           out_dtype == BSG_OUT_F32, scratch, dev_status,
+                                           (hipStream_t)stream),
+                    fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,208 @@
+/*
+ * bsg.h -- block-scaled grouped quantize and grouped GEMM for MoE expert products
+ * on AMD Instinct MI355X (gfx950).  C ABI of libbsg.so.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers are DEVICE pointers unless the argument comment says [host].
+ * - All buffers belong to the caller.  The library keeps no per-call state,
+ *   allocates no device memory, never synchronizes and never reads device memory
+ *   from the host: each call only enqueues kernels on `stream` (a hipStream_t;
+ *   NULL = the legacy default stream), so calls can be captured into a HIP graph.
+ * - Return value: 0 (BSG_OK) on success, otherwise a bsg_status code; the
+ *   message is in bsg_last_error() (thread-local, valid until the next call on
+ *   the same thread).  Argument errors are detected on the host before any HIP
+ *   call is made; nothing is enqueued then.
+ * - Errors only the device can see (a negative group size, groups that add up
+ *   to more rows than the buffers hold, padded offsets that do not fit the
+ *   sizes) never cause an out-of-bounds access: offsets are clamped on the
+ *   device into [0, capacity] and made non-decreasing, and the bit below is
+ *   OR-ed into *dev_status (a device uint32, optional: may be NULL; the caller
+ *   clears it).
+ * - Row-major everywhere.  "bf16" is IEEE bfloat16 bits (uint16).  E4M3 is
+ *   the OCP float8 "fn" variant (max 448, no infinities); E8M0 is a biased
+ *   power-of-two exponent byte; E2M1 is the OCP fp4 element.
+ */
+#ifndef BSG_H
+#define BSG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BSG_OK = 0,
+  BSG_ERR_NULL = 1,        /* a required pointer is NULL */
+  BSG_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  BSG_ERR_ALIGN = 3,       /* a data pointer is not 16-byte aligned */
+  BSG_ERR_UNSUPPORTED = 4, /* a mode / dtype / flag value this build does not support */
+  BSG_ERR_HIP = 6          /* a HIP launch failed */
+} bsg_status;
+
+/* Bits OR-ed into *dev_status by the kernels. */
+#define BSG_DEV_NEGATIVE_SIZE 1u   /* a group size < 0 was treated as 0 */
+#define BSG_DEV_OVER_CAPACITY 2u   /* offsets ran past the buffer capacity; clamped */
+#define BSG_DEV_BAD_PADDING   4u   /* padded offsets not multiples of 128 or smaller than
+                                      the live sizes; that group was skipped */
+
+typedef enum { BSG_FPROP_TN = 0, BSG_WGRAD_NT = 1 } bsg_gemm_mode;
+typedef enum { BSG_OUT_BF16 = 0, BSG_OUT_F32 = 1 } bsg_out_dtype;
+
+#define BSG_MAX_GROUPS 256
+#define BSG_COLWISE_PAD 128
+
+/* Thread-local message of the last failing call on this thread ("" if none). */
+const char* bsg_last_error(void);
+
+/* Library version, (major << 16) | minor. */
+int bsg_version(void);
+
+/*
+ * group_offsets_i32_to_i64
+ *
+ * "[JAX] MXFP8 Grouped Quant+GEMM" (Changes list; review thread on
+ * cublaslt_grouped_gemm.cu): int32 group sizes become int64 on the device, times
+ * a multiplier, and their exclusive prefix sums give G + 1 offsets.  Padding to
+ * a multiple (pad_to) gives the offsets of the 128-padded columnwise copies.
+ *
+ *   sizes      [G] int32, device.  Negative entries count as 0 (status bit 1).
+ *   G          1 .. BSG_MAX_GROUPS.
+ *   multiplier >= 1.  sizes_i64[g] = sizes[g] * multiplier.
+ *   pad_to     >= 1.  offsets[g+1] = offsets[g] + roundup(sizes[g], pad_to) * multiplier.
+ *   sizes_i64  [G] int64 output, or NULL.
+ *   offsets    [G+1] int64 output; offsets[0] = 0.
+ *   capacity   if > 0, offsets[G] > capacity sets status bit 2 (the offsets are
+ *              still written unclamped; every consumer clamps them).
+ * One wavefront-sized scan kernel; latency bound.
+ */
+int group_offsets_i32_to_i64(const int32_t* sizes, int64_t G, int64_t multiplier, int64_t pad_to,
+                             int64_t* sizes_i64, int64_t* offsets, int64_t capacity,
+                             uint32_t* dev_status, void* stream);
+
+/*
+ * grouped_quantize_mxfp8
+ *
+ * Grouped MXFP8 quantize of a bf16 activation split into G consecutive row
+ * groups ("[JAX] MXFP8 Grouped Quant+GEMM": V2 grouped quantize with the scale
+ * swizzle fused into it; contraction-direction rule of "gemm.py",
+ * _quantize_gemm_operands: rowwise when the contraction is the last dim,
+ * columnwise/transposed otherwise).  E4M3 elements; one E8M0 scale per 32
+ * elements along the contraction dim; scale exponent = floor(log2(block amax))
+ * - 8, elements rounded to nearest even and saturated at +-448.
+ *
+ *   x            [rows_cap, cols] bf16.  Only rows < offsets[G] are read.
+ *   rows_cap     >= 0.  cols: multiple of 32, > 0.
+ *   offsets      [G+1] int64 live row offsets (from group_offsets_i32_to_i64, pad 1).
+ *   Rowwise output (both or neither):
+ *     row_data   [rows_cap, cols] E4M3; rows >= offsets[G] untouched.
+ *     row_scales [rows_cap, S] E8M0, S = roundup(cols/32, 4).  Within every 4
+ *                consecutive scale bytes of a row (one 128-element stretch) the
+ *                stored order is b0, b2, b1, b3 -- the order the grouped GEMM
+ *                reads; bytes past cols/32 are 0.
+ *   Columnwise output (all three or none):
+ *     padded_offsets [G+1] int64 (group_offsets_i32_to_i64 with pad_to 128).
+ *     col_rows_cap   capacity of the columnwise buffers in padded tokens.
+ *     col_data   group g: a [cols, m~_g] block (m~_g = padded_offsets[g+1] -
+ *                padded_offsets[g]) at byte padded_offsets[g] * cols; token t of
+ *                column c at [c, t]; tokens t >= m_g are 0x00.
+ *     col_scales group g: a [cols, m~_g/32] block at byte padded_offsets[g] * cols / 32,
+ *                same b0, b2, b1, b3 order along the token dim; padding blocks 0x00.
+ * Both directions requested in one call read x once.
+ */
+int grouped_quantize_mxfp8(const void* x, int64_t rows_cap, int64_t cols, int64_t G,
+                           const int64_t* offsets, uint8_t* row_data, uint8_t* row_scales,
+                           const int64_t* padded_offsets, int64_t col_rows_cap, uint8_t* col_data,
+                           uint8_t* col_scales, uint32_t* dev_status, void* stream);
+
+/*
+ * grouped_quantize_nvfp4_rowscaled
+ *
+ * Row-scaled NVFP4 quantize ("[Common][PyTorch] Add row-scaled NVFP4 support to
+ * grouped-tensor GEMM": per-row FP32 outer scale, E4M3 scale per 16 elements,
+ * E2M1 elements, amax fused into the cast; outer scale amax / (6 * 448) as the
+ * tensor scale of "gemm.py", _get_nvfp4_tensor_scale_inv, taken per row).
+ * Float32 steps per row r and 16-element block: S = 2688 / amax_r (1 if
+ * amax_r = 0, capped at FLT_MAX); s8 = E4M3((bmax / 6) * S); enc = S / decode(s8)
+ * (0 if the scale is 0, capped at FLT_MAX); q = E2M1(x * enc), ties to even,
+ * saturated at 6; outer[r] = amax_r / 2688.  Quantize weights with the same
+ * call (rows = sum of N_e): the outer scale then is per output column.
+ *
+ *   x            [rows_cap, cols] bf16; rows >= offsets[G] are not read.
+ *   cols         multiple of 32.
+ *   data         [rows_cap, cols/2]; element 2j in the low nibble of byte j.
+ *   block_scales [rows_cap, cols/16] E4M3, row-major (the GEMM reads this order).
+ *   outer        [rows_cap] float32.
+ */
+int grouped_quantize_nvfp4_rowscaled(const void* x, int64_t rows_cap, int64_t cols, int64_t G,
+                                     const int64_t* offsets, uint8_t* data, uint8_t* block_scales,
+                                     float* outer, uint32_t* dev_status, void* stream);
+
+/*
+ * grouped_gemm_mxfp8
+ *
+ * One launch over all groups of a grouped MXFP8 GEMM with FP32 accumulation
+ * ("gemm.py", grouped_gemm; "[JAX] MXFP8 Grouped Quant+GEMM": V2 grouped GEMM
+ * extended to MXFP8, graph-safe).  Each operand is K-major E4M3 data with E8M0
+ * scales per 32 along the contraction in the order grouped_quantize_mxfp8 writes.
+ *
+ * mode BSG_FPROP_TN (ragged rows; output rows follow the lhs groups):
+ *   Y[r, n] = sum_k A[r, k] * B[g, n, k]   for r in [offsets[g], offsets[g+1])
+ *   a        [rows_cap, k] E4M3 rowwise,  a_scales [rows_cap, roundup(k/32,4)]
+ *   b        [G, n, k] E4M3 rowwise,      b_scales [G, n, roundup(k/32,4)]
+ *   offsets  [G+1] live row offsets; rows_cap = rows of a and out
+ *   out      [rows_cap, n]; rows >= offsets[G] untouched.
+ * mode BSG_WGRAD_NT (ragged contraction; uniform (G, n, k) output):
+ *   dW[g, i, j] = sum_t dY[t, i] * X[t, j] over the tokens t of group g
+ *   a        columnwise dY copy (grouped_quantize_mxfp8 col_data with cols = n)
+ *   b        columnwise X copy (cols = k); a_scales / b_scales their col_scales
+ *   offsets  [G+1] padded (multiple-of-128) token offsets of those copies;
+ *            rows_cap = their capacity in padded tokens
+ *   out      [G, n, k]; a group with no tokens gets zeros.
+ * k must be a multiple of 128 (FPROP); n >= 1.  out_dtype: BSG_OUT_BF16 (round to
+ * nearest even) or BSG_OUT_F32.
+ */
+int grouped_gemm_mxfp8(int mode, int64_t G, const uint8_t* a, const uint8_t* a_scales,
+                       const uint8_t* b, const uint8_t* b_scales, const int64_t* offsets,
+                       int64_t rows_cap, int64_t n, int64_t k, void* out, int out_dtype,
+                       uint32_t* dev_status, void* stream);
+
+/*
+ * grouped_gemm_nvfp4_rowscaled
+ *
+ * Row-scaled NVFP4 grouped GEMM ("[Common][PyTorch] Add row-scaled NVFP4
+ * support to grouped-tensor GEMM": the per-row / per-column FP32 outer scale is
+ * neutralized in the GEMM, the product is accumulated in FP32, and the outer
+ * scales are applied afterwards over each group's own live rows and its own
+ * output width -- the Greptile finding on differing output widths and capacity
+ * rows, and its fix):
+ *   S[r, n] = sum_k e2m1(A)[r,k] * sA[r, k/16] * e2m1(B_g)[n,k] * sB_g[n, k/16]
+ *   Y[r, n] = S[r, n] * a_outer[r] * b_outer_g[n]   for r live in g, n < N_g
+ *
+ *   a, a_scales, a_outer  grouped_quantize_nvfp4_rowscaled outputs, [rows_cap] rows
+ *   offsets               [G+1] live row offsets
+ *   b, b_scales, b_outer  the experts' [N_g, k] weights quantized one after
+ *                         another (sum N_g rows)
+ *   n_per_group           [host] [G] int64 output width of each group, >= 0
+ *   out                   [rows_cap, ld_out]; ld_out >= max N_g.  Columns >= N_g of
+ *                         group g's rows and rows >= offsets[G] are untouched.
+ *   scratch               NULL: the outer scales are applied in the GEMM's
+ *                         epilogue.  Otherwise a [rows_cap, ld_out] float32 buffer:
+ *                         S is stored there first and a second kernel applies the
+ *                         outer scales into out (the pages' two-step flow).
+ * k must be a multiple of 32.
+ */
+int grouped_gemm_nvfp4_rowscaled(int64_t G, const uint8_t* a, const uint8_t* a_scales,
+                                 const float* a_outer, const int64_t* offsets, int64_t rows_cap,
+                                 int64_t k, const uint8_t* b, const uint8_t* b_scales,
+                                 const float* b_outer, const int64_t* n_per_group, void* out,
+                                 int64_t ld_out, int out_dtype, float* scratch,
+                                 uint32_t* dev_status, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSG_H */

@@ -1,0 +1,96 @@
+"""The C-ABI library loads without a GPU, exports every entry point include/bsg.h
+declares, and rejects bad arguments on the host before any HIP call (no
+compute calls here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_grouped_amd as bsg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsg.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(?:int|const char\*)\s+(\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bsg.LIB_PATH):
+        pytest.fail("libbsg.so is not built; run python -m block_scaled_grouped_amd.build")
+    return bsg.load_library()
+
+
+def test_exports_match_header(lib):
+    declared = _declared_functions()
+    assert set(declared) == set(bsg.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.bsg_version() >= 1
+
+
+def _buf(n=4096):
+    # host buffers aligned to 16 bytes stand in for device pointers: the calls
+    # below must fail validation before dereferencing or launching anything
+    raw = ctypes.create_string_buffer(n + 16)
+    addr = (ctypes.addressof(raw) + 15) & ~15
+    return raw, ctypes.c_void_p(addr)
+
+
+def test_offsets_validation(lib):
+    _, p = _buf()
+    assert lib.group_offsets_i32_to_i64(None, 4, 1, 1, None, p, 0, None, None) == 1
+    assert lib.group_offsets_i32_to_i64(p, 0, 1, 1, None, p, 0, None, None) == 2
+    assert lib.group_offsets_i32_to_i64(p, 257, 1, 1, None, p, 0, None, None) == 2
+    assert lib.group_offsets_i32_to_i64(p, 4, 0, 1, None, p, 0, None, None) == 2
+    assert lib.group_offsets_i32_to_i64(p, 4, 1, 0, None, p, 0, None, None) == 2
+    lib.group_offsets_i32_to_i64(p, 0, 1, 1, None, p, 0, None, None)
+    assert b"G=0" in lib.bsg_last_error()
+
+
+def test_quantize_validation(lib):
+    _, p = _buf()
+    q = lib.grouped_quantize_mxfp8
+    assert q(None, 128, 128, 4, p, p, p, None, 0, None, None, None, None) == 1
+    assert q(p, 128, 128, 4, p, None, None, None, 0, None, None, None, None) == 1   # nothing requested
+    assert q(p, 128, 128, 4, p, p, None, None, 0, None, None, None, None) == 1      # half a pair
+    assert q(p, 128, 100, 4, p, p, p, None, 0, None, None, None, None) == 2         # cols % 32
+    assert q(p, 128, 128, 0, p, p, p, None, 0, None, None, None, None) == 2         # G
+    mis = ctypes.c_void_p(p.value + 2)
+    assert q(mis, 128, 128, 4, p, p, p, None, 0, None, None, None, None) == 3       # alignment
+    n = lib.grouped_quantize_nvfp4_rowscaled
+    assert n(p, 128, 128, 4, p, p, p, None, None, None) == 1
+    assert n(p, 128, 48, 4, p, p, p, p, None, None) == 2
+    assert n(p, 128, 32768, 4, p, p, p, p, None, None) == 4
+
+
+def test_gemm_validation(lib):
+    _, p = _buf()
+    g = lib.grouped_gemm_mxfp8
+    assert g(0, 4, None, p, p, p, p, 128, 128, 128, p, 0, None, None) == 1
+    assert g(7, 4, p, p, p, p, p, 128, 128, 128, p, 0, None, None) == 4
+    assert g(0, 4, p, p, p, p, p, 128, 128, 128, p, 9, None, None) == 4
+    assert g(0, 4, p, p, p, p, p, 128, 128, 96, p, 0, None, None) == 2             # fprop k % 128
+    assert g(1, 4, p, p, p, p, p, 128, 100, 128, p, 0, None, None) == 2            # wgrad n % 32
+    assert g(0, 300, p, p, p, p, p, 128, 128, 128, p, 0, None, None) == 2
+    nv = lib.grouped_gemm_nvfp4_rowscaled
+    npg = (ctypes.c_int64 * 2)(64, 128)
+    hp = ctypes.cast(npg, ctypes.c_void_p)
+    assert nv(2, p, p, p, p, 64, 128, p, p, p, None, p, 128, 0, None, None, None) == 1
+    assert nv(2, p, p, p, p, 64, 96, p, p, p, hp, p, 128, 0, None, None, None) == 2   # k % 64
+    assert nv(2, p, p, p, p, 64, 128, p, p, p, hp, p, 100, 0, None, None, None) == 2  # ld_out
+    neg = (ctypes.c_int64 * 2)(64, -1)
+    assert nv(2, p, p, p, p, 64, 128, p, p, p, ctypes.cast(neg, ctypes.c_void_p), p, 128, 0,
+              None, None, None) == 2
+
+
+def test_binding_requires_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(bsg, "_lib", None)
+    with pytest.raises(RuntimeError):
+        bsg.load_library(str(tmp_path / "missing.so"))

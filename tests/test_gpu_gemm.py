@@ -1,0 +1,302 @@
+"""GPU parity of the grouped GEMMs against the fp64 oracle.
+
+The operands the GPU multiplies are the oracle's own quantized bytes (uploaded),
+so the GEMM is checked in isolation; the end-to-end tests chain the GPU
+quantize and GPU GEMM and compare with the oracle's quantize + GEMM.  Shapes
+span several 256-wide tiles with ragged tails, empty groups and capacity rows.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_grouped_amd as bsg
+from oracle import formats as F
+from oracle import gemm as GM
+from oracle import offsets as O
+from oracle import quantize as Q
+import workloads
+from gpu_util import (bf16_dev, bf16_out_to_f64, device, gemm_tolerance_check, host, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(rng, shape, std=1.0):
+    return F.f32_to_bf16_bits_rne((rng.standard_normal(shape) * std).astype(np.float32))
+
+
+def _fprop_operands(rng, sizes, K, N, rows_cap=None):
+    sizes = np.array(sizes, np.int32)
+    G, live = len(sizes), int(sizes.sum())
+    rows_cap = live if rows_cap is None else rows_cap
+    x = _bits(rng, (rows_cap, K))
+    w = _bits(rng, (G * N, K), 0.02)
+    _, off = O.group_offsets(sizes)
+    ad, asc = Q.mxfp8_rowwise(x, off)
+    bd, bsc = Q.mxfp8_rowwise(w, np.array([0, G * N]))
+    return sizes, off, x, w, ad, asc, bd.reshape(G, N, K), bsc.reshape(G, N, -1), rows_cap
+
+
+def _upload_rows(data, scales, rows_cap):
+    d = np.zeros((rows_cap, data.shape[1]), np.uint8)
+    s = np.zeros((rows_cap, scales.shape[1]), np.uint8)
+    d[:data.shape[0]] = data
+    s[:scales.shape[0]] = scales
+    return to_dev(d), to_dev(s)
+
+
+FPROP_CASES = [
+    ([300, 0, 17, 513, 130], 512, 640, 1000),
+    ([32, 0, 64, 32], 128, 128, 128),
+    ([0, 0, 700], 256, 300, 700),
+    ([1], 128, 1, 1),
+]
+
+
+@pytest.mark.parametrize("sizes,K,N,rows_cap", FPROP_CASES)
+@pytest.mark.parametrize("out_f32", [True, False])
+def test_fprop_parity(sizes, K, N, rows_cap, out_f32):
+    rng = np.random.default_rng(K + N + len(sizes))
+    sizes, off, x, w, ad, asc, bd, bsc, rows_cap = _fprop_operands(rng, sizes, K, N, rows_cap)
+    ref = GM.mxfp8_fprop(ad, asc, bd, bsc, off, K)
+    a, a_s = _upload_rows(ad, asc, rows_cap)
+    dt = torch.float32 if out_f32 else torch.bfloat16
+    out = torch.full((rows_cap, N), float("nan"), dtype=dt, device=device())
+    bsg.grouped_gemm_mxfp8(bsg.BSG_FPROP_TN, a, a_s, to_dev(bd), to_dev(bsc), to_dev(off), rows_cap,
+                           N, K, out=out, out_dtype=bsg.BSG_OUT_F32 if out_f32 else bsg.BSG_OUT_BF16)
+    y = bf16_out_to_f64(out)
+    live = int(off[-1])
+    for g in range(len(sizes)):
+        gemm_tolerance_check(y[off[g]:off[g + 1]], ref[off[g]:off[g + 1]], out_f32, "group %d" % g)
+    assert np.all(np.isnan(y[live:])), "capacity rows must stay untouched"
+
+
+WGRAD_CASES = [
+    ([37, 0, 130, 5, 300], 160, 96),
+    ([2049, 0, 3001, 0], 256, 288),
+    ([0, 0], 64, 64),
+]
+
+
+@pytest.mark.parametrize("sizes,N,K", WGRAD_CASES)
+@pytest.mark.parametrize("out_f32", [True, False])
+def test_wgrad_parity(sizes, N, K, out_f32):
+    rng = np.random.default_rng(N * 3 + K)
+    sizes = np.array(sizes, np.int32)
+    G, M = len(sizes), int(sizes.sum())
+    dy = _bits(rng, (max(M, 1), N))
+    x = _bits(rng, (max(M, 1), K))
+    _, off = O.group_offsets(sizes)
+    _, poff = O.group_offsets(sizes, pad_to=128)
+    dyc, dys = Q.mxfp8_colwise(dy, off, poff)
+    xc, xs = Q.mxfp8_colwise(x, off, poff)
+    ref = GM.mxfp8_wgrad(dyc, dys, xc, xs, poff, N, K)
+    cap = max(int(poff[-1]), 128)
+
+    def pad(a, n):
+        o = np.zeros(n, np.uint8)
+        o[:len(a)] = a
+        return to_dev(o)
+
+    dt = torch.float32 if out_f32 else torch.bfloat16
+    out = torch.full((G, N, K), float("nan"), dtype=dt, device=device())
+    bsg.grouped_gemm_mxfp8(bsg.BSG_WGRAD_NT, pad(dyc, cap * N), pad(dys, cap * N // 32),
+                           pad(xc, cap * K), pad(xs, cap * K // 32), to_dev(poff), cap, N, K,
+                           out=out, out_dtype=bsg.BSG_OUT_F32 if out_f32 else bsg.BSG_OUT_BF16)
+    y = bf16_out_to_f64(out)
+    for g in range(G):
+        if sizes[g] == 0:
+            assert np.all(y[g] == 0.0) and not np.any(np.signbit(y[g])), "empty expert must be +0"
+        else:
+            gemm_tolerance_check(y[g], ref[g], out_f32, "group %d" % g)
+
+
+def test_fprop_end_to_end_tiny_config():
+    """The tiny MoE config: GPU quantize -> GPU GEMM vs oracle quantize -> oracle GEMM."""
+    w = workloads.get("tiny")
+    t = workloads.tensors(w, device=device())
+    xb, wb = workloads.bf16_bits(t["x"]), workloads.bf16_bits(t["w"])
+    G, N, K = w.G, w.n, w.k
+    _, off = O.group_offsets(w.sizes)
+    ad, asc = Q.mxfp8_rowwise(xb, off)
+    bd, bsc = Q.mxfp8_rowwise(wb.reshape(G * N, K), np.array([0, G * N]))
+    ref = GM.mxfp8_fprop(ad, asc, bd.reshape(G, N, K), bsc.reshape(G, N, -1), off, K)
+
+    _, doff = bsg.group_offsets_i32_to_i64(to_dev(w.sizes))
+    qa = bsg.grouped_quantize_mxfp8(t["x"], doff)
+    woff = to_dev(np.array([0, G * N]))
+    qb = bsg.grouped_quantize_mxfp8(t["w"].view(G * N, K), woff)
+    y = bsg.grouped_gemm_mxfp8(bsg.BSG_FPROP_TN, qa["row_data"], qa["row_scales"], qb["row_data"],
+                               qb["row_scales"], doff, w.rows_cap, N, K, out_dtype=bsg.BSG_OUT_F32)
+    y = host(y).astype(np.float64)
+    for g in range(G):
+        gemm_tolerance_check(y[off[g]:off[g + 1]], ref[off[g]:off[g + 1]], True, "group %d" % g)
+
+
+def test_grouped_equals_separate_calls_and_determinism():
+    rng = np.random.default_rng(31)
+    sizes, off, x, w, ad, asc, bd, bsc, rows_cap = _fprop_operands(rng, [257, 0, 90, 400], 384, 512)
+    a, a_s = _upload_rows(ad, asc, rows_cap)
+    B, Bs, doff = to_dev(bd), to_dev(bsc), to_dev(off)
+    y = bsg.grouped_gemm_mxfp8(bsg.BSG_FPROP_TN, a, a_s, B, Bs, doff, rows_cap, 512, 384,
+                               out_dtype=bsg.BSG_OUT_F32)
+    y2 = bsg.grouped_gemm_mxfp8(bsg.BSG_FPROP_TN, a, a_s, B, Bs, doff, rows_cap, 512, 384,
+                                out_dtype=bsg.BSG_OUT_F32)
+    assert torch.equal(y, y2)
+    for g in range(4):
+        if sizes[g] == 0:
+            continue
+        r0, r1 = int(off[g]), int(off[g + 1])
+        one = bsg.grouped_gemm_mxfp8(bsg.BSG_FPROP_TN, a[r0:r1].contiguous(), a_s[r0:r1].contiguous(),
+                                     B[g:g + 1].contiguous(), Bs[g:g + 1].contiguous(),
+                                     to_dev(np.array([0, r1 - r0])), r1 - r0, 512, 384,
+                                     out_dtype=bsg.BSG_OUT_F32)
+        assert torch.equal(one, y[r0:r1])
+
+
+def test_all_empty_routing():
+    rng = np.random.default_rng(4)
+    K, N = 128, 256
+    a = to_dev(np.zeros((64, K), np.uint8))
+    a_s = to_dev(np.zeros((64, K // 32), np.uint8))
+    b = to_dev(rng.integers(0, 255, (2, N, K)).astype(np.uint8) & 0x77)
+    b_s = to_dev(np.full((2, N, K // 32), 127, np.uint8))
+    out = torch.full((64, N), float("nan"), dtype=torch.float32, device=device())
+    bsg.grouped_gemm_mxfp8(bsg.BSG_FPROP_TN, a, a_s, b, b_s, to_dev(np.zeros(3, np.int64)), 64, N, K,
+                           out=out, out_dtype=bsg.BSG_OUT_F32)
+    assert torch.isnan(out).all()
+
+
+def test_hip_graph_replay_with_new_sizes():
+    """Sizes live on the device: a captured quantize + GEMM replays correctly
+    after the sizes change, with no host dependence on them."""
+    dev = device()
+    rng = np.random.default_rng(8)
+    G, K, N, rows_cap = 3, 256, 256, 600
+    xb = _bits(rng, (rows_cap, K))
+    wb = _bits(rng, (G * N, K), 0.02)
+    x, wt = bf16_dev(xb), bf16_dev(wb)
+    sizes = torch.tensor([100, 0, 200], dtype=torch.int32, device=dev)
+    qb = bsg.grouped_quantize_mxfp8(wt, to_dev(np.array([0, G * N])))
+    s64 = torch.empty(G, dtype=torch.int64, device=dev)
+    off = torch.empty(G + 1, dtype=torch.int64, device=dev)
+    rd = torch.empty((rows_cap, K), dtype=torch.uint8, device=dev)
+    rs = torch.empty((rows_cap, K // 32), dtype=torch.uint8, device=dev)
+    out = torch.empty((rows_cap, N), dtype=torch.float32, device=dev)
+
+    def step():
+        bsg.group_offsets_i32_to_i64(sizes, sizes_i64=s64, offsets=off)
+        bsg.grouped_quantize_mxfp8(x, off, row_data=rd, row_scales=rs)
+        bsg.grouped_gemm_mxfp8(bsg.BSG_FPROP_TN, rd, rs, qb["row_data"], qb["row_scales"], off,
+                               rows_cap, N, K, out=out, out_dtype=bsg.BSG_OUT_F32)
+
+    step()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.synchronize()
+    bd, bsc = Q.mxfp8_rowwise(wb, np.array([0, G * N]))
+    for new in ([100, 0, 200], [50, 250, 300], [0, 0, 600], [600, 0, 0]):
+        sizes.copy_(torch.tensor(new, dtype=torch.int32))
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _, o = O.group_offsets(np.array(new))
+        ad, asc = Q.mxfp8_rowwise(xb, o)
+        ref = GM.mxfp8_fprop(ad, asc, bd.reshape(G, N, K), bsc.reshape(G, N, -1), o, K)
+        y = host(out).astype(np.float64)
+        for gi in range(G):
+            gemm_tolerance_check(y[o[gi]:o[gi + 1]], ref[o[gi]:o[gi + 1]], True, str(new))
+        eager = out.clone()
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(eager[:int(o[-1])], out[:int(o[-1])])
+
+
+# ---------------------------------------------------------------- NVFP4
+
+def _nv_operands(rng, sizes, npg, K, rows_cap):
+    sizes = np.array(sizes, np.int32)
+    _, off = O.group_offsets(sizes)
+    x = _bits(rng, (rows_cap, K))
+    w = _bits(rng, (sum(npg), K), 0.02)
+    ap, asc, at = Q.nvfp4_rowscaled(x, off)
+    bp, bsc, bt = Q.nvfp4_rowscaled(w, np.array([0, sum(npg)]))
+    return sizes, off, ap, asc, at, bp, bsc, bt
+
+
+NV_CASES = [
+    ([100, 0, 257, 31], [64, 128, 96, 256], 256, 450),
+    ([300, 211], [2048, 4096], 512, 600),
+    ([0, 0], [64, 64], 64, 16),
+]
+
+
+@pytest.mark.parametrize("sizes,npg,K,rows_cap", NV_CASES)
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("out_f32", [True, False])
+def test_nvfp4_gemm_parity(sizes, npg, K, rows_cap, fused, out_f32):
+    rng = np.random.default_rng(K + rows_cap)
+    sizes, off, ap, asc, at, bp, bsc, bt = _nv_operands(rng, sizes, npg, K, rows_cap)
+    live = int(off[-1])
+    ld = max(npg) + 8
+
+    def pad_rows(a, rows, dtype=None):
+        o = np.zeros((rows,) + a.shape[1:], a.dtype)
+        o[:a.shape[0]] = a
+        return to_dev(o)
+
+    dt = torch.float32 if out_f32 else torch.bfloat16
+    out = torch.full((rows_cap, ld), float("nan"), dtype=dt, device=device())
+    scratch = None if fused else torch.empty((rows_cap, ld), dtype=torch.float32, device=device())
+    bsg.grouped_gemm_nvfp4_rowscaled(pad_rows(ap, rows_cap), pad_rows(asc, rows_cap),
+                                     pad_rows(at, rows_cap), to_dev(off), K, to_dev(bp),
+                                     to_dev(bsc), to_dev(bt), npg, out=out, ld_out=ld,
+                                     out_dtype=bsg.BSG_OUT_F32 if out_f32 else bsg.BSG_OUT_BF16,
+                                     scratch=scratch)
+    y = bf16_out_to_f64(out)
+    ref = GM.nvfp4_rowscaled_fprop(ap, asc, at, off, bp, bsc, bt, npg, K)
+    for g, (rows, r) in enumerate(ref):
+        if len(rows) == 0:
+            continue
+        gemm_tolerance_check(y[rows][:, :npg[g]], r, out_f32, "group %d" % g)
+        assert np.all(np.isnan(y[rows][:, npg[g]:])), "columns past N_g must stay untouched"
+    assert np.all(np.isnan(y[live:])), "capacity rows must stay untouched"
+
+
+def test_nvfp4_fused_equals_unfused():
+    rng = np.random.default_rng(77)
+    sizes, off, ap, asc, at, bp, bsc, bt = _nv_operands(rng, [130, 260], [256, 512], 512, 390)
+    args = (to_dev(ap), to_dev(asc), to_dev(at), to_dev(off), 512, to_dev(bp), to_dev(bsc), to_dev(bt),
+            [256, 512])
+    y1 = bsg.grouped_gemm_nvfp4_rowscaled(*args, ld_out=512)
+    scratch = torch.empty((390, 512), dtype=torch.float32, device=device())
+    y2 = bsg.grouped_gemm_nvfp4_rowscaled(*args, ld_out=512, scratch=scratch)
+    torch.cuda.synchronize()
+    assert torch.equal(y1[:130, :256], y2[:130, :256]) and torch.equal(y1[130:], y2[130:])
+
+
+def test_nvfp4_end_to_end():
+    rng = np.random.default_rng(12)
+    sizes = np.array([150, 0, 106], np.int32)
+    npg = [128, 256, 384]
+    K, rows_cap = 256, 300
+    xb = _bits(rng, (rows_cap, K))
+    wb = _bits(rng, (sum(npg), K), 0.02)
+    _, off = O.group_offsets(sizes)
+    doff = to_dev(off)
+    a = bsg.grouped_quantize_nvfp4_rowscaled(bf16_dev(xb), doff)
+    b = bsg.grouped_quantize_nvfp4_rowscaled(bf16_dev(wb), to_dev(np.array([0, sum(npg)])))
+    y = bsg.grouped_gemm_nvfp4_rowscaled(a[0], a[1], a[2], doff, K, b[0], b[1], b[2], npg,
+                                         out_dtype=bsg.BSG_OUT_F32)
+    y = host(y).astype(np.float64)
+    ap, asc, at = Q.nvfp4_rowscaled(xb, off)
+    bp, bsc, bt = Q.nvfp4_rowscaled(wb, np.array([0, sum(npg)]))
+    for g, (rows, r) in enumerate(GM.nvfp4_rowscaled_fprop(ap, asc, at, off, bp, bsc, bt, npg, K)):
+        if len(rows):
+            gemm_tolerance_check(y[rows][:, :npg[g]], r, True, "group %d" % g)
