@@ -1,0 +1,375 @@
+"""Benchmark of the grouped block-scaled quantize + grouped GEMM hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
+
+One step = one pass of the MoE expert-product hot path over one batch of
+seeded synthetic input, inputs already resident in HBM:
+
+  fprop (8 experts, 16384 routed rows, K = 4096, N = 14336; the headline):
+      int32 sizes -> int64 offsets (live, and 128-padded)
+      -> MXFP8 quantize of the activations, rowwise + columnwise in one pass
+      -> MXFP8 quantize of the expert weights (rowwise)
+      -> grouped MXFP8 GEMM, fprop TN, bf16 out.
+
+The other MoE shapes (tiny, wgrad, 64-expert Zipf, row-scaled NVFP4) are timed
+the same way and reported under "configs".  Before every timed step a 512 MiB
+buffer is overwritten so the 256 MB MALL holds none of the step's inputs (cold
+numbers); per-kernel times come from HIP events recorded on the stream the
+kernels run on, around each launch.
+
+Prints ONE JSON line on stdout (details go to stderr).
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+import block_scaled_grouped_amd as bsg
+import workloads
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "fp4": 10100.0, "bf16": 2500.0}
+METRIC = "MXFP8 grouped GEMM TFLOP/s + grouped quantize GB/s (1 MI355X, % roofline)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- cases
+
+class Case:
+    """Allocates a workload's buffers on the device and launches one step."""
+
+    kernels = ()
+
+    def step(self, ev=None):
+        raise NotImplementedError
+
+    def _rec(self, ev, i):
+        if ev is not None:
+            ev[i].record()
+
+
+class MxFprop(Case):
+    """offsets -> quantize X (row [+ col]) -> quantize W -> grouped GEMM fprop."""
+
+    def __init__(self, name, dev, with_colwise=True):
+        self.name = name
+        self.w = w = workloads.get(name)
+        t = workloads.tensors(w, device=dev)
+        self.x, self.wt = t["x"], t["w"]
+        G, N, K, R = w.G, w.n, w.k, w.rows_cap
+        self.G, self.N, self.K, self.R = G, N, K, R
+        self.sizes = torch.from_numpy(w.sizes).to(dev)
+        self.s64 = torch.empty(G, dtype=torch.int64, device=dev)
+        self.off = torch.empty(G + 1, dtype=torch.int64, device=dev)
+        self.with_colwise = with_colwise
+        self.poff = torch.empty(G + 1, dtype=torch.int64, device=dev)
+        self.col_cap = R + 128 * G
+        self.xr = torch.empty((R, K), dtype=torch.uint8, device=dev)
+        self.xrs = torch.empty((R, bsg.mx_scale_row_bytes(K)), dtype=torch.uint8, device=dev)
+        if with_colwise:
+            self.xc = torch.empty(self.col_cap * K, dtype=torch.uint8, device=dev)
+            self.xcs = torch.empty(self.col_cap * K // 32, dtype=torch.uint8, device=dev)
+        self.woff = torch.tensor([0, G * N], dtype=torch.int64, device=dev)
+        self.wq = torch.empty((G * N, K), dtype=torch.uint8, device=dev)
+        self.wqs = torch.empty((G * N, bsg.mx_scale_row_bytes(K)), dtype=torch.uint8, device=dev)
+        self.y = torch.empty((R, N), dtype=torch.bfloat16, device=dev)
+        self.kernels = ("offsets", "quantize_x", "quantize_w", "gemm")
+        live = w.live_rows
+        self.flops = 2.0 * live * N * K
+        per_dir = 1.0 + 1.0 / 32
+        self.bytes = {
+            "offsets": 0.0,
+            "quantize_x": live * K * (2.0 + per_dir * (2 if with_colwise else 1)),
+            "quantize_w": G * N * K * (2.0 + per_dir),
+            "gemm": (live * K * per_dir + sum(N * K * per_dir for s in w.sizes if s > 0)
+                     + live * N * 2.0),
+        }
+
+    def step(self, ev=None):
+        self._rec(ev, 0)
+        bsg.group_offsets_i32_to_i64(self.sizes, sizes_i64=self.s64, offsets=self.off,
+                                     capacity=self.R)
+        if self.with_colwise:
+            bsg.group_offsets_i32_to_i64(self.sizes, pad_to=128, offsets=self.poff)
+        self._rec(ev, 1)
+        if self.with_colwise:
+            bsg.grouped_quantize_mxfp8(self.x, self.off, row_data=self.xr, row_scales=self.xrs,
+                                       padded_offsets=self.poff, col_rows_cap=self.col_cap,
+                                       col_data=self.xc, col_scales=self.xcs)
+        else:
+            bsg.grouped_quantize_mxfp8(self.x, self.off, row_data=self.xr, row_scales=self.xrs)
+        self._rec(ev, 2)
+        bsg.grouped_quantize_mxfp8(self.wt.view(self.G * self.N, self.K), self.woff, row_data=self.wq,
+                                   row_scales=self.wqs)
+        self._rec(ev, 3)
+        bsg.grouped_gemm_mxfp8(bsg.BSG_FPROP_TN, self.xr, self.xrs, self.wq, self.wqs, self.off,
+                               self.R, self.N, self.K, out=self.y, out_dtype=bsg.BSG_OUT_BF16)
+        self._rec(ev, 4)
+
+
+class MxWgrad(Case):
+    """offsets -> columnwise quantize of dY and X -> grouped GEMM wgrad."""
+
+    def __init__(self, name, dev):
+        self.name = name
+        self.w = w = workloads.get(name)
+        t = workloads.tensors(w, device=dev)
+        self.dy, self.x = t["dy"], t["x"]
+        G, N, K, R = w.G, w.n, w.k, w.rows_cap
+        self.G, self.N, self.K, self.R = G, N, K, R
+        self.sizes = torch.from_numpy(w.sizes).to(dev)
+        self.off = torch.empty(G + 1, dtype=torch.int64, device=dev)
+        self.poff = torch.empty(G + 1, dtype=torch.int64, device=dev)
+        self.cap = R + 128 * G
+        self.dyc = torch.empty(self.cap * N, dtype=torch.uint8, device=dev)
+        self.dycs = torch.empty(self.cap * N // 32, dtype=torch.uint8, device=dev)
+        self.xc = torch.empty(self.cap * K, dtype=torch.uint8, device=dev)
+        self.xcs = torch.empty(self.cap * K // 32, dtype=torch.uint8, device=dev)
+        self.dw = torch.empty((G, N, K), dtype=torch.bfloat16, device=dev)
+        self.kernels = ("offsets", "quantize_dy", "quantize_x", "gemm")
+        live = w.live_rows
+        per = 1.0 + 1.0 / 32
+        self.flops = 2.0 * live * N * K
+        self.bytes = {"offsets": 0.0, "quantize_dy": live * N * (2.0 + per),
+                      "quantize_x": live * K * (2.0 + per),
+                      "gemm": live * (N + K) * per + G * N * K * 2.0}
+
+    def step(self, ev=None):
+        self._rec(ev, 0)
+        bsg.group_offsets_i32_to_i64(self.sizes, offsets=self.off, capacity=self.R)
+        bsg.group_offsets_i32_to_i64(self.sizes, pad_to=128, offsets=self.poff)
+        self._rec(ev, 1)
+        bsg.grouped_quantize_mxfp8(self.dy, self.off, rowwise=False, padded_offsets=self.poff,
+                                   col_rows_cap=self.cap, col_data=self.dyc, col_scales=self.dycs)
+        self._rec(ev, 2)
+        bsg.grouped_quantize_mxfp8(self.x, self.off, rowwise=False, padded_offsets=self.poff,
+                                   col_rows_cap=self.cap, col_data=self.xc, col_scales=self.xcs)
+        self._rec(ev, 3)
+        bsg.grouped_gemm_mxfp8(bsg.BSG_WGRAD_NT, self.dyc, self.dycs, self.xc, self.xcs, self.poff,
+                               self.cap, self.N, self.K, out=self.dw, out_dtype=bsg.BSG_OUT_BF16)
+        self._rec(ev, 4)
+
+
+class Nvfp4Fprop(Case):
+    """offsets -> row-scaled NVFP4 quantize of X and W -> grouped GEMM with the
+    fused outer-scale epilogue."""
+
+    def __init__(self, name, dev):
+        self.name = name
+        self.w = w = workloads.get(name)
+        t = workloads.tensors(w, device=dev)
+        self.x, self.wt = t["x"], t["w"]
+        G, K, R = w.G, w.k, w.rows_cap
+        self.npg = list(w.n_per_group)
+        NB = sum(self.npg)
+        self.G, self.K, self.R, self.ld = G, K, R, max(self.npg)
+        self.sizes = torch.from_numpy(w.sizes).to(dev)
+        self.off = torch.empty(G + 1, dtype=torch.int64, device=dev)
+        self.xd = torch.empty((R, K // 2), dtype=torch.uint8, device=dev)
+        self.xs = torch.empty((R, K // 16), dtype=torch.uint8, device=dev)
+        self.xo = torch.empty(R, dtype=torch.float32, device=dev)
+        self.woff = torch.tensor([0, NB], dtype=torch.int64, device=dev)
+        self.wd = torch.empty((NB, K // 2), dtype=torch.uint8, device=dev)
+        self.ws = torch.empty((NB, K // 16), dtype=torch.uint8, device=dev)
+        self.wo = torch.empty(NB, dtype=torch.float32, device=dev)
+        self.y = torch.empty((R, self.ld), dtype=torch.bfloat16, device=dev)
+        self.kernels = ("offsets", "quantize_x", "quantize_w", "gemm")
+        live = w.live_rows
+        self.flops = 2.0 * K * float(sum(int(m) * n for m, n in zip(w.sizes, self.npg)))
+        per = 0.5 + 1.0 / 16
+        self.bytes = {"offsets": 0.0, "quantize_x": live * (K * (2.0 + per) + 4),
+                      "quantize_w": NB * (K * (2.0 + per) + 4),
+                      "gemm": live * K * per + NB * K * per
+                      + 2.0 * float(sum(int(m) * n for m, n in zip(w.sizes, self.npg)))}
+
+    def step(self, ev=None):
+        self._rec(ev, 0)
+        bsg.group_offsets_i32_to_i64(self.sizes, offsets=self.off, capacity=self.R)
+        self._rec(ev, 1)
+        bsg.grouped_quantize_nvfp4_rowscaled(self.x, self.off, data=self.xd, block_scales=self.xs,
+                                             outer=self.xo)
+        self._rec(ev, 2)
+        bsg.grouped_quantize_nvfp4_rowscaled(self.wt, self.woff, data=self.wd, block_scales=self.ws,
+                                             outer=self.wo)
+        self._rec(ev, 3)
+        bsg.grouped_gemm_nvfp4_rowscaled(self.xd, self.xs, self.xo, self.off, self.K, self.wd, self.ws,
+                                         self.wo, self.npg, out=self.y, ld_out=self.ld,
+                                         out_dtype=bsg.BSG_OUT_BF16)
+        self._rec(ev, 4)
+
+
+def make_case(name, dev):
+    if name in ("tiny", "zipf"):
+        return MxFprop(name, dev, with_colwise=False)
+    if name == "fprop":
+        return MxFprop(name, dev, with_colwise=True)
+    if name == "wgrad":
+        return MxWgrad(name, dev)
+    if name == "nvfp4":
+        return Nvfp4Fprop(name, dev)
+    raise KeyError(name)
+
+
+# ---------------------------------------------------------------- timing
+
+def time_case(case, steps, warmup, flush_buf):
+    for _ in range(warmup):
+        case.step()
+    torch.cuda.synchronize()
+    nk = len(case.kernels)
+    per_kernel = np.zeros((steps, nk))
+    step_ms = np.zeros(steps)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        if flush_buf is not None:
+            flush_buf.zero_()
+        case.step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for s in range(steps):
+        for i in range(nk):
+            per_kernel[s, i] = evs[s][i].elapsed_time(evs[s][i + 1])
+        step_ms[s] = evs[s][0].elapsed_time(evs[s][nk])
+    return {
+        "step_ms": float(step_ms.mean()),
+        "wall_ms_per_step": 1e3 * wall / steps,
+        "kernel_ms": {k: float(per_kernel[:, i].mean()) for i, k in enumerate(case.kernels)},
+    }
+
+
+def summarize(case, t, mfma_dtype):
+    km = t["kernel_ms"]
+    out = {"workload": case.name, "step_ms": round(t["step_ms"], 4),
+           "step_tflops": round(case.flops / (t["step_ms"] * 1e-3) / 1e12, 2),
+           "gemm_us": round(km["gemm"] * 1e3, 2),
+           "gemm_tflops": round(case.flops / (km["gemm"] * 1e-3) / 1e12, 2),
+           "gemm_frac_of_peak": round(case.flops / (km["gemm"] * 1e-3) / 1e12
+                                      / MFMA_PEAK_TFLOPS[mfma_dtype], 4),
+           "mfma_peak_tflops": MFMA_PEAK_TFLOPS[mfma_dtype], "kernels_us": {}}
+    for k, ms in km.items():
+        ent = {"us": round(ms * 1e3, 2)}
+        b = case.bytes.get(k, 0.0)
+        if b and k != "gemm":
+            gbs = b / (ms * 1e-3) / 1e9
+            ent.update({"algorithmic_bytes": int(b), "GB_s": round(gbs, 1),
+                        "frac_of_hbm": round(gbs / HBM_PEAK_GBS, 4)})
+        out["kernels_us"][k] = ent
+    return out
+
+
+# ---------------------------------------------------------------- CPU baseline (the oracle)
+
+def cpu_baseline():
+    """The oracle, untuned, on a bounded sample of the fprop workload: one
+    expert's 512 token rows and a 4096-row slice of its weight, quantized
+    (MXFP8, rowwise) and multiplied in fp64.  Reported in the metric's unit."""
+    from oracle import gemm as GM
+    from oracle import quantize as Q
+    w = workloads.get("fprop")
+    gen = torch.Generator().manual_seed(w.seed)
+    rows, nrows, K = 512, 4096, w.k
+    x = torch.randn((rows, K), generator=gen)
+    x = torch.where(torch.rand((rows, K), generator=gen) < 0.01, x * 20, x).to(torch.bfloat16)
+    wt = (torch.randn((nrows, K), generator=gen) * 0.02).to(torch.bfloat16)
+    xb, wb = workloads.bf16_bits(x), workloads.bf16_bits(wt)
+    t0 = time.perf_counter()
+    ad, asc = Q.mxfp8_rowwise(xb, np.array([0, rows]))
+    bd, bsc = Q.mxfp8_rowwise(wb, np.array([0, nrows]))
+    GM.mxfp8_fprop(ad, asc, bd.reshape(1, nrows, K), bsc.reshape(1, nrows, -1),
+                   np.array([0, rows]), K)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * nrows * K
+    try:
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    except Exception:
+        threads = os.cpu_count() or 1
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": "fprop workload, 1 expert: 512 token rows x 4096 weight rows x K=4096; "
+                      "oracle MXFP8 quantize of both + fp64 GEMM (numpy; quantize single-"
+                      "threaded, matmul on BLAS threads)"}
+
+
+# ---------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="time only the headline workload")
+    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--only", default=None, help="comma list of workloads to time")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    bsg.load_library()
+    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    names = ["fprop"] if args.no_extra else ["fprop", "tiny", "wgrad", "zipf", "nvfp4"]
+    if args.only:
+        names = args.only.split(",")
+    results = {}
+    for name in names:
+        log("[bench] %s: setup" % name)
+        case = make_case(name, dev)
+        torch.cuda.synchronize()
+        steps = args.steps if name == "fprop" else max(5, args.steps // 2)
+        t = time_case(case, steps, args.warmup, flush)
+        results[name] = summarize(case, t, "bf16" if name == "nvfp4" else "fp8")
+        results[name]["steps"] = steps
+        log("[bench] %s: %s" % (name, json.dumps(results[name])))
+        del case
+        torch.cuda.empty_cache()
+
+    head = results.get("fprop") or results[names[0]]
+    achieved = head["gemm_tflops"]
+    qx = head["kernels_us"]["quantize_x"]
+    line = {
+        "metric": METRIC,
+        "value": head["step_tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": results.get("fprop", head)["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": head["step_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 x fp8_e4m3 (e8m0/32), fp32 accumulate, bf16 out",
+        "data": "synthetic (seeded; no dataset)",
+        "config": {"workload": "MoE fprop MXFP8: 8 experts, 16384 routed rows (uneven multiples "
+                               "of 128), K=4096, N=14336; step = offsets + quantize X (row+col) + "
+                               "quantize W + grouped GEMM",
+                   "cache": "cold (512 MiB overwritten before each step)" if flush is not None
+                   else "warm"},
+        "quantize_x_GB_s": qx.get("GB_s"),
+        "quantize_x_frac_of_hbm": qx.get("frac_of_hbm"),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": MFMA_PEAK_TFLOPS["fp8"], "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_PEAK_TFLOPS["fp8"], 4), "traffic": None,
+                     "kernel": "grouped_gemm_mxfp8 (fprop)"},
+        "configs": results,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,177 @@
+"""Full-size parity in the launch configuration bench.py times.
+
+Each MoE workload is built and stepped exactly as the benchmark does (same
+case objects, same buffers, same calls); then sampled outputs are compared
+with the oracle, which recomputes only what those samples need: rowwise
+quantization is row-local and columnwise quantization column-local within a
+group, so a sampled output needs only its own rows / columns quantized.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import bench
+from oracle import formats as F
+from oracle import gemm as GM
+from oracle import offsets as O
+from oracle import quantize as Q
+import workloads
+from gpu_util import bf16_out_to_f64, device, gemm_tolerance_check, host_u8
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_rows(off, rng, per_group=3):
+    rows = []
+    for g in range(len(off) - 1):
+        a, b = int(off[g]), int(off[g + 1])
+        if b > a:
+            rows += [a, b - 1] + list(rng.integers(a, b, per_group))
+    return np.unique(np.array(rows, dtype=np.int64))
+
+
+def _check_fprop_case(name):
+    dev = device()
+    case = bench.make_case(name, dev)
+    case.y.fill_(float("nan"))
+    case.step()
+    torch.cuda.synchronize()
+    w = case.w
+    G, N, K = w.G, w.n, w.k
+    _, off = O.group_offsets(w.sizes)
+    rng = np.random.default_rng(2024)
+    rows = _sample_rows(off, rng)
+    cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 30)]))
+    xb = workloads.bf16_bits(case.x[torch.from_numpy(rows).to(dev)])
+    ad, asc = Q.mxfp8_rowwise(xb, np.array([0, len(rows)]))
+    gx = host_u8(case.xr)[rows]
+    gxs = host_u8(case.xrs)[rows]
+    assert np.array_equal(gx, ad) and np.array_equal(gxs, asc), "activation quantize"
+    grp = np.searchsorted(off, rows, side="right") - 1
+    y = bf16_out_to_f64(case.y)
+    wq, wqs = host_u8(case.wq), host_u8(case.wqs)
+    for g in np.unique(grp):
+        wrows = g * N + cols
+        wb = workloads.bf16_bits(case.wt.view(G * N, K)[torch.from_numpy(wrows).to(dev)])
+        bd, bsc = Q.mxfp8_rowwise(wb, np.array([0, len(cols)]))
+        assert np.array_equal(wq[wrows], bd) and np.array_equal(wqs[wrows], bsc), "weight quantize"
+        sel = np.nonzero(grp == g)[0]
+        ref = GM.mxfp8_fprop(ad[sel], asc[sel], bd.reshape(1, len(cols), K),
+                             bsc.reshape(1, len(cols), -1), np.array([0, len(sel)]), K)
+        gemm_tolerance_check(y[rows[sel]][:, cols], ref, False, "%s group %d" % (name, g))
+    assert not np.isnan(y[:int(off[-1])]).any(), "every live output row written"
+    return case, off
+
+
+def test_full_fprop_headline():
+    """8 experts, 16384 rows, K=4096, N=14336 (rowwise + columnwise X)."""
+    case, off = _check_fprop_case("fprop")
+    # the columnwise copy of the activations (used by the wgrad), on sampled columns
+    w = case.w
+    K = w.k
+    _, poff = O.group_offsets(w.sizes, pad_to=128)
+    c0 = 32 * 37
+    xb = workloads.bf16_bits(case.x[:, c0:c0 + 32])
+    cd, cs = Q.mxfp8_colwise(xb, off, poff)
+    gd, gs = host_u8(case.xc), host_u8(case.xcs)
+    for g in range(w.G):
+        mp = int(poff[g + 1] - poff[g])
+        if mp == 0:
+            continue
+        blk = gd[poff[g] * K:poff[g + 1] * K].reshape(K, mp)[c0:c0 + 32]
+        want = cd[poff[g] * 32:poff[g + 1] * 32].reshape(32, mp)
+        assert np.array_equal(blk, want), g
+        sblk = gs[poff[g] * K // 32:poff[g + 1] * K // 32].reshape(K, mp // 32)[c0:c0 + 32]
+        swant = cs[poff[g]:poff[g + 1]].reshape(32, mp // 32)
+        assert np.array_equal(sblk, swant), g
+
+
+def test_full_zipf_64_experts():
+    """64 experts (4 empty), 32768 Zipf-routed rows, K=7168, N=2048."""
+    _check_fprop_case("zipf")
+
+
+def test_full_tiny_all_outputs():
+    dev = device()
+    case = bench.make_case("tiny", dev)
+    case.step()
+    torch.cuda.synchronize()
+    w = case.w
+    G, N, K = w.G, w.n, w.k
+    _, off = O.group_offsets(w.sizes)
+    ad, asc = Q.mxfp8_rowwise(workloads.bf16_bits(case.x), off)
+    bd, bsc = Q.mxfp8_rowwise(workloads.bf16_bits(case.wt).reshape(G * N, K), np.array([0, G * N]))
+    ref = GM.mxfp8_fprop(ad, asc, bd.reshape(G, N, K), bsc.reshape(G, N, -1), off, K)
+    y = bf16_out_to_f64(case.y)
+    for g in range(G):
+        gemm_tolerance_check(y[off[g]:off[g + 1]], ref[off[g]:off[g + 1]], False, "group %d" % g)
+
+
+def test_full_wgrad():
+    """8 experts (2 empty), 16384 ragged tokens, dW [8, 4096, 4096]."""
+    dev = device()
+    case = bench.make_case("wgrad", dev)
+    case.dw.fill_(float("nan"))
+    case.step()
+    torch.cuda.synchronize()
+    w = case.w
+    G, N, K = w.G, w.n, w.k
+    _, off = O.group_offsets(w.sizes)
+    _, poff = O.group_offsets(w.sizes, pad_to=128)
+    rng = np.random.default_rng(7)
+    i0, j0 = 32 * int(rng.integers(0, N // 32)), 32 * int(rng.integers(0, K // 32))
+    dyb = workloads.bf16_bits(case.dy[:, i0:i0 + 32])
+    xb = workloads.bf16_bits(case.x[:, j0:j0 + 32])
+    dyc, dys = Q.mxfp8_colwise(dyb, off, poff)
+    xc, xs = Q.mxfp8_colwise(xb, off, poff)
+    ref = GM.mxfp8_wgrad(dyc, dys, xc, xs, poff, 32, 32)
+    gd = host_u8(case.dyc)
+    dw = case.dw
+    for g in range(G):
+        mp = int(poff[g + 1] - poff[g])
+        if w.sizes[g] == 0:
+            assert bool((dw[g] == 0).all()), "empty expert %d must get zeros" % g
+            continue
+        blk = gd[poff[g] * N:poff[g + 1] * N].reshape(N, mp)[i0:i0 + 32]
+        assert np.array_equal(blk, dyc[poff[g] * 32:poff[g + 1] * 32].reshape(32, mp)), g
+        y = dw[g, i0:i0 + 32, j0:j0 + 32].float().cpu().numpy().astype(np.float64)
+        gemm_tolerance_check(y, ref[g], False, "wgrad group %d" % g)
+    assert not torch.isnan(dw).any()
+
+
+def test_full_nvfp4_rowscaled():
+    """8 experts, 16384 live rows of 18432, K=4096, N_e in {2048, 4096}."""
+    dev = device()
+    case = bench.make_case("nvfp4", dev)
+    case.y.fill_(float("nan"))
+    case.step()
+    torch.cuda.synchronize()
+    w = case.w
+    K, npg = w.k, case.npg
+    _, off = O.group_offsets(w.sizes)
+    boff = np.concatenate([[0], np.cumsum(npg)])
+    rng = np.random.default_rng(11)
+    rows = _sample_rows(off, rng)
+    xb = workloads.bf16_bits(case.x[torch.from_numpy(rows).to(dev)])
+    ap, asc, at = Q.nvfp4_rowscaled(xb, np.array([0, len(rows)]))
+    assert np.array_equal(host_u8(case.xd)[rows], ap)
+    assert np.array_equal(host_u8(case.xs)[rows], asc)
+    assert np.array_equal(case.xo.cpu().numpy()[rows].view(np.uint32), at.view(np.uint32))
+    grp = np.searchsorted(off, rows, side="right") - 1
+    y = bf16_out_to_f64(case.y)
+    for g in np.unique(grp):
+        cols = np.unique(np.concatenate([[0, npg[g] - 1], rng.integers(0, npg[g], 24)]))
+        wrows = boff[g] + cols
+        wb = workloads.bf16_bits(case.wt[torch.from_numpy(wrows).to(dev)])
+        bp, bsc, bt = Q.nvfp4_rowscaled(wb, np.array([0, len(cols)]))
+        assert np.array_equal(host_u8(case.wd)[wrows], bp)
+        sel = np.nonzero(grp == g)[0]
+        (_, ref), = GM.nvfp4_rowscaled_fprop(ap[sel], asc[sel], at[sel], np.array([0, len(sel)]),
+                                             bp, bsc, bt, [len(cols)], K)
+        gemm_tolerance_check(y[rows[sel]][:, cols], ref, False, "nvfp4 group %d" % g)
+        if npg[g] < case.ld:
+            assert np.isnan(y[rows[sel]][:, npg[g]:]).all(), "columns past N_g untouched"
+    live = int(off[-1])
+    assert np.isnan(y[live:]).all(), "capacity rows untouched"
+    assert not np.isnan(y[:live, :min(npg)]).any()
