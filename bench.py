@@ -73,13 +73,13 @@ class MxFprop(Case):
         self.poff = torch.empty(G + 1, dtype=torch.int64, device=dev)
         self.col_cap = R + 128 * G
         self.xr = torch.empty((R, K), dtype=torch.uint8, device=dev)
-        self.xrs = torch.empty((R, bsg.mx_scale_row_bytes(K)), dtype=torch.uint8, device=dev)
+        self.xrs = torch.empty(bsg.mx_scale_shape(R, K), dtype=torch.uint8, device=dev)
         if with_colwise:
             self.xc = torch.empty(self.col_cap * K, dtype=torch.uint8, device=dev)
             self.xcs = torch.empty(self.col_cap * K // 32, dtype=torch.uint8, device=dev)
         self.woff = torch.tensor([0, G * N], dtype=torch.int64, device=dev)
         self.wq = torch.empty((G * N, K), dtype=torch.uint8, device=dev)
-        self.wqs = torch.empty((G * N, bsg.mx_scale_row_bytes(K)), dtype=torch.uint8, device=dev)
+        self.wqs = torch.empty(bsg.mx_scale_shape(G * N, K), dtype=torch.uint8, device=dev)
         self.y = torch.empty((R, N), dtype=torch.bfloat16, device=dev)
         self.kernels = ("offsets", "quantize_x", "quantize_w", "gemm")
         live = w.live_rows
@@ -285,8 +285,7 @@ def cpu_baseline():
     t0 = time.perf_counter()
     ad, asc = Q.mxfp8_rowwise(xb, np.array([0, rows]))
     bd, bsc = Q.mxfp8_rowwise(wb, np.array([0, nrows]))
-    GM.mxfp8_fprop(ad, asc, bd.reshape(1, nrows, K), bsc.reshape(1, nrows, -1),
-                   np.array([0, rows]), K)
+    GM.mxfp8_fprop(ad, asc, bd.reshape(1, nrows, K), bsc, np.array([0, rows]), K)
     dt = time.perf_counter() - t0
     flops = 2.0 * rows * nrows * K
     try:
@@ -311,6 +310,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--only", default=None, help="comma list of workloads to time")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 256 MiB device copy (3x), the reference for "
+                         "scaling FETCH_SIZE / WRITE_SIZE counter readings")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -319,6 +321,14 @@ def main():
     dev = torch.device("cuda:0")
     bsg.load_library()
     flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    if args.copy_calibration:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 3 x 268435456 bytes read + written")
+        del src, dst
 
     names = ["fprop"] if args.no_extra else ["fprop", "tiny", "wgrad", "zipf", "nvfp4"]
     if args.only:

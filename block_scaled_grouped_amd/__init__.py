@@ -86,8 +86,13 @@ def _need_cuda(*ts):
 
 
 def mx_scale_row_bytes(cols):
-    """Stored E8M0 bytes per rowwise scale row (cols / 32 rounded up to 4)."""
+    """Stored E8M0 bytes per row of a rowwise MXFP8 tensor (cols / 32 rounded up to 4)."""
     return ((cols // 32 + 3) // 4) * 4
+
+
+def mx_scale_shape(rows, cols):
+    """Shape of rowwise MXFP8 scales: [NQ][rows] words of 4 bytes, NQ = ceil(cols / 128)."""
+    return (mx_scale_row_bytes(cols) // 4, rows, 4)
 
 
 def group_offsets_i32_to_i64(sizes, multiplier=1, pad_to=1, capacity=0, sizes_i64=None,
@@ -121,7 +126,7 @@ def grouped_quantize_mxfp8(x, offsets, G=None, rowwise=True, padded_offsets=None
         if row_data is None:
             row_data = torch.empty((rows_cap, cols), dtype=torch.uint8, device=x.device)
         if row_scales is None:
-            row_scales = torch.empty((rows_cap, mx_scale_row_bytes(cols)), dtype=torch.uint8,
+            row_scales = torch.empty(mx_scale_shape(rows_cap, cols), dtype=torch.uint8,
                                      device=x.device)
         out["row_data"], out["row_scales"] = row_data, row_scales
     else:

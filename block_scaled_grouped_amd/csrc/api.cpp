@@ -145,10 +145,13 @@ int grouped_gemm_mxfp8(int mode, int64_t G, const uint8_t* a, const uint8_t* a_s
       return fail(BSG_ERR_SHAPE, "%s: FPROP needs k %% 128 == 0 (got %lld)", fn, (long long)k);
     if (256 * k >= kMaxTileBytes || 256 * n * esz >= kMaxTileBytes || n > 0x7fffffffLL)
       return fail(BSG_ERR_SHAPE, "%s: n or k too large for one tile's 32-bit offsets", fn);
+    if ((k / 128) * 4 * rows_cap >= kMaxTileBytes || (k / 128) * 4 * G * n >= kMaxTileBytes)
+      return fail(BSG_ERR_SHAPE, "%s: scale arrays too large for 32-bit offsets", fn);
   } else {
     if (n % 32 != 0 || k % 32 != 0)
       return fail(BSG_ERR_SHAPE, "%s: WGRAD needs n and k multiples of 32", fn);
-    if (256 * rows_cap >= kMaxTileBytes || 256 * k * esz >= kMaxTileBytes)
+    if (256 * rows_cap >= kMaxTileBytes || 256 * k * esz >= kMaxTileBytes ||
+        (rows_cap / 128) * 4 * (n > k ? n : k) >= kMaxTileBytes)
       return fail(BSG_ERR_SHAPE, "%s: token capacity or k too large for 32-bit tile offsets", fn);
   }
   if (!aligned16(a) || !aligned16(b) || !aligned4(a_scales) || !aligned4(b_scales) || !aligned4(out))

@@ -14,30 +14,62 @@
 //   WGRAD_NT:  A = dY^T of group g [N, m~_g],    B = X^T of group g [K, m~_g]
 // (the columnwise copies are already transposed and 128-padded with zeros).
 //
-// Tile 256 x 256 x 128, 4 wavefronts (one per SIMD) in a 2 x 2 grid, each
-// owning 128 x 128 of the output as 4 x 4 MFMA blocks of 32 x 32 (256
-// accumulator registers per lane).  Operands are staged through LDS
-// in 128-byte rows whose 16-byte chunks are XOR-swizzled by (row / 2) % 8 so
-// that the MFMA fragment reads (32 rows, same chunk) spread over all banks.
-// Global loads of K-step k+1 are issued before the MFMAs of step k and written
-// to the other LDS buffer afterwards (one barrier per K-step).
+// Tile 256 x 256, K-steps of 64 (one MFMA deep), 4 wavefronts (one per SIMD)
+// in a 2 x 2 grid, each owning 128 x 128 of the output as 4 x 4 MFMA blocks of
+// 32 x 32 (256 accumulator registers per lane).
+//
+// Operands go global -> LDS by the buffer unit directly (LDS-DMA: lane l of a
+// load lands at LDS base + 16 l, so a swizzled layout is made by permuting each
+// lane's source address) into a ring of 4 LDS stages; K-step k + 3 is in flight
+// while the MFMAs of step k run, so a fetch has three K-steps (~3000 cycles) to
+// arrive.  LDS rows are 64 bytes; 16-byte chunk c of row r sits in slot
+// c ^ ((r / 4) % 4), which spreads the MFMA fragment reads (32 rows, same
+// chunk) over all banks.  One barrier per K-step; the schedule of a K-step is
+// written out MFMA by MFMA (DMA issues and next-step fragment reads placed
+// between them) and fenced so the compiler keeps it.
+//
+// Tiles are handed out XCD-aware: workgroup b runs on XCD b % 8, and the 32
+// workgroups of one XCD take a 4 x 8 block of output tiles of one group at a
+// time, so the A rows and B columns they stream are shared through that XCD's
+// L2.
 //
 // Scaled-MFMA operand layout (measured on the device): lane l holds row l % 32;
 // its 32 bytes are two 16-byte chunks covering K = 32c + 16 (l / 32) + [0, 16),
 // c = 0, 1; the lane's scale byte (picked by op_sel) scales K-block l / 32 of
 // its row.  With the quantizer's b0, b2, b1, b3 order, half h of a row's scale
-// dword holds the bytes of blocks h and 2 + h: op_sel 0 and 1 of the two MFMAs
-// of a 128-wide K-step.
+// dword (one dword per 128 K) holds the bytes of blocks h and 2 + h: op_sel 0
+// for the first 64-wide K-step of the dword and op_sel 1 for the second.
+#include <utility>
+
 #include "bsg_internal.h"
 
 namespace bsg {
 
 namespace {
 
+// Compile-time loop: f(std::integral_constant<int, 0>{}) ... f(<N-1>), so every
+// register-array index in the K-step schedule is a constant.
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 constexpr int BM = 256;
 constexpr int BN = 256;
-constexpr int BK = 128;
+constexpr int BK = 64;                 // bytes (= E4M3 elements) per row per K-step
 constexpr int kThreads = 256;
+constexpr int kStages = 4;
+constexpr int kTileA = BM * BK;        // 16 KiB
+constexpr int kTileB = BN * BK;
+constexpr int kStageBytes = kTileA + kTileB + 4 * BM + 4 * BN;
+constexpr int kDmaPerStep = 10;        // per wave: 4 A, 4 B, 1 A-scale, 1 B-scale
+constexpr int kBarrierAfter = 7;       // MFMA index after which a K-step waits + barriers
+constexpr int kSuperM = 4, kSuperN = 8;  // tile block one XCD works on
+constexpr int kXcds = 8;
 
 struct MxArgs {
   const uint8_t* a;
@@ -56,107 +88,253 @@ struct MxArgs {
 
 struct TileDesc {
   const uint8_t* a;   // row 0 of the A tile, K offset 0
-  const uint8_t* as;  // its scale row 0
+  const uint8_t* as;  // scale word (K-group 0, tile row 0)
   const uint8_t* b;
   const uint8_t* bs;
   int64_t lda, ldb;   // bytes per data row
-  int64_t ldas, ldbs; // bytes per scale row
+  int64_t sqa, sqb;   // bytes between the scale words of consecutive 128-wide K-groups
+  int64_t as_bytes, bs_bytes;  // scale bytes readable from `as` / `bs`
   int a_rows, b_rows; // valid rows (rows past them load as zeros)
-  int64_t kl;         // contraction length, multiple of BK
+  int64_t kl;         // contraction length, multiple of 128
   char* out;          // element (0, 0) of the output tile
   int64_t ldc;        // output row stride in elements
   int out_rows, out_cols;
 };
 
-struct Smem {
-  uint8_t a[2][BM * BK];
-  uint8_t b[2][BN * BK];
-  uint32_t sa[2][BM];
-  uint32_t sb[2][BN];
+struct Sched {
   int64_t off[kMaxGroups + 1];
   int32_t cnt[kMaxGroups];
   int32_t pre[kMaxGroups + 1];
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * BK + ((chunk ^ ((row >> 1) & 7)) << 4);
+typedef __attribute__((address_space(3))) v4i lds_v4i;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+
+__device__ __forceinline__ v4i lds_read16(uint32_t addr) {
+  return *reinterpret_cast<const lds_v4i*>((size_t)addr);
+}
+__device__ __forceinline__ uint32_t lds_read4(uint32_t addr) {
+  return *reinterpret_cast<const lds_u32*>((size_t)addr);
+}
+template <typename T>
+__device__ __forceinline__ uint32_t lds_offset(T* shared_ptr) {
+  return (uint32_t)(size_t)(__attribute__((address_space(3))) T*)(shared_ptr);
 }
 
-struct Prefetch {
-  v4i a[8];
-  v4i b[8];
-  int sa, sb;
-};
+// Stage s of the ring: A tile, B tile, A scale dwords, B scale dwords.
+__device__ __forceinline__ uint32_t st_a(uint32_t base, int s) { return base + s * kStageBytes; }
+__device__ __forceinline__ uint32_t st_b(uint32_t base, int s) { return st_a(base, s) + kTileA; }
+__device__ __forceinline__ uint32_t st_sa(uint32_t base, int s) { return st_b(base, s) + kTileB; }
+__device__ __forceinline__ uint32_t st_sb(uint32_t base, int s) { return st_sa(base, s) + 4 * BM; }
 
-// Raw buffer descriptor over [base, base + bytes): loads past the end return 0.
+// Raw buffer descriptor over [base, base + bytes): accesses past the end are
+// dropped (loads return 0).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
 }
 
-struct TileRsrc {
-  __amdgpu_buffer_rsrc_t a, b, as, bs;
-};
-
-__device__ __forceinline__ TileRsrc tile_rsrc(const TileDesc& t) {
-  TileRsrc r;
-  r.a = make_rsrc(t.a, (int64_t)t.a_rows * t.lda);
-  r.b = make_rsrc(t.b, (int64_t)t.b_rows * t.ldb);
-  r.as = make_rsrc(t.as, (int64_t)t.a_rows * t.ldas);
-  r.bs = make_rsrc(t.bs, (int64_t)t.b_rows * t.ldbs);
+// The same descriptor as four uniform dwords, for the inline-asm LDS-DMA loads.
+__device__ __forceinline__ v4i make_rsrc_words(const void* base, int64_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  v4i r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(b & 0xffffffffu));
+  r[1] = __builtin_amdgcn_readfirstlane((int)(b >> 32));
+  r[2] = __builtin_amdgcn_readfirstlane((int)(bytes > 0 ? bytes : 0));
+  r[3] = 0x00020000;
   return r;
 }
 
-// Thread tid loads 16-byte chunk (tid % 8) of rows tid / 8 + 32 p, p = 0..7, of
-// both operand tiles, and the scale dwords of row tid.  Rows past the valid
-// ones read as zeros (buffer range check).
-__device__ __forceinline__ void load_step(const TileDesc& t, const TileRsrc& rs, int64_t kt,
-                                          int tid, Prefetch& pf) {
-  const int row = tid >> 3, ch = tid & 7;
-  const int koff = (int)(kt * BK) + ch * 16;
-  const int oa = row * (int)t.lda + koff;
-  const int ob = row * (int)t.ldb + koff;
-#pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    pf.a[p] = __builtin_amdgcn_raw_buffer_load_b128(rs.a, oa, 32 * p * (int)t.lda, 0);
-    pf.b[p] = __builtin_amdgcn_raw_buffer_load_b128(rs.b, ob, 32 * p * (int)t.ldb, 0);
-  }
-  pf.sa = __builtin_amdgcn_raw_buffer_load_b32(rs.as, tid * (int)t.ldas + (int)kt * (BK / 32), 0, 0);
-  pf.sb = __builtin_amdgcn_raw_buffer_load_b32(rs.bs, tid * (int)t.ldbs + (int)kt * (BK / 32), 0, 0);
+// LDS-DMA: lane l copies 16 (or 4) bytes from rsrc + voff to LDS address
+// m0 + 16 l (or 4 l); the whole offset is in voff, so the buffer range check
+// covers it (a lane past the valid rows copies zeros instead of reading).
+// Issued through inline asm so that the compiler does not add waits for it in
+// front of LDS reads of other stages; the K-loop waits for it explicitly
+// (vmcnt) before its barrier.  m0 is saved and restored around the load.
+__device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds, int voff) {
+  int save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(lds), "v"(voff), "s"(rsrc)
+      : "memory");
 }
 
-__device__ __forceinline__ void store_step(Smem& sm, int st, int tid, const Prefetch& pf) {
-  const int row = tid >> 3, ch = tid & 7;
-#pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    *reinterpret_cast<v4i*>(&sm.a[st][swz(row + 32 * p, ch)]) = pf.a[p];
-    *reinterpret_cast<v4i*>(&sm.b[st][swz(row + 32 * p, ch)]) = pf.b[p];
-  }
-  sm.sa[st][tid] = (uint32_t)pf.sa;
-  sm.sb[st][tid] = (uint32_t)pf.sb;
+__device__ __forceinline__ void dma4(v4i rsrc, uint32_t lds, int voff) {
+  int save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(lds), "v"(voff), "s"(rsrc)
+      : "memory");
 }
 
-__device__ __forceinline__ v8i frag(const uint8_t* base, int row, int c0, int c1) {
-  const v4i lo = *reinterpret_cast<const v4i*>(base + swz(row, c0));
-  const v4i hi = *reinterpret_cast<const v4i*>(base + swz(row, c1));
+// Vector-memory operations complete in issue order, so "at most N
+// outstanding" means everything but the N most recent has landed.  Also waits
+// for this wave's LDS reads, then joins the barrier: afterwards the stage whose
+// copies were older than the last N is complete for every wave, and no wave
+// still reads the stage that the next copies overwrite.
+template <int N>
+__device__ __forceinline__ void wait_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// A wavefront's share of one K-step's copies.  Wave w fills rows
+// [64 w, 64 w + 64) of both operand tiles, sixteen 64-byte rows (1 KiB) per
+// load: in load q lane l writes row 64 w + 16 q + l / 4, slot l % 4, which must
+// hold logical chunk (l % 4) ^ ((row / 4) % 4) = (l % 4) ^ ((l / 16) % 4).  The
+// scale words of its 64 rows for one 128-wide K-group are 256 contiguous bytes.
+struct Dma {
+  v4i ra, rb, rsa, rsb;  // descriptors (uniform)
+  v4i rnone;             // zero-length descriptor: turns a copy into a no-op
+  int a, b;              // lane source offsets for q = 0, K-step 0
+  int s;                 // lane scale-word offset (row 64 w + l, K-group 0)
+  int lda16, ldb16;      // 16 rows of stride (uniform)
+  int sqa, sqb;          // scale K-group strides (uniform)
+};
+
+__device__ __forceinline__ Dma make_dma(const TileDesc& t, int w, int lane) {
+  Dma d;
+  d.ra = make_rsrc_words(t.a, (int64_t)t.a_rows * t.lda);
+  d.rb = make_rsrc_words(t.b, (int64_t)t.b_rows * t.ldb);
+  d.rsa = make_rsrc_words(t.as, t.as_bytes);
+  d.rsb = make_rsrc_words(t.bs, t.bs_bytes);
+  d.rnone = make_rsrc_words(t.a, 0);
+  const int row = 64 * w + (lane >> 2);
+  const int c = (lane & 3) ^ ((lane >> 4) & 3);
+  d.a = row * (int)t.lda + c * 16;
+  d.b = row * (int)t.ldb + c * 16;
+  d.s = 4 * (64 * w + lane);
+  d.lda16 = __builtin_amdgcn_readfirstlane(16 * (int)t.lda);
+  d.ldb16 = __builtin_amdgcn_readfirstlane(16 * (int)t.ldb);
+  d.sqa = __builtin_amdgcn_readfirstlane((int)t.sqa);
+  d.sqb = __builtin_amdgcn_readfirstlane((int)t.sqb);
+  return d;
+}
+
+// Copy piece P (0..3 A rows, 4..7 B rows, 8 A scales, 9 B scales) of K-step kt
+// into stage s; `live` false makes it a no-op copy (past the last K-step).
+template <int P>
+__device__ __forceinline__ void dma_piece(const Dma& d, uint32_t lds, int w, int s, int kt,
+                                          bool live) {
+  const int koff = kt * BK;
+  if constexpr (P < 4) {
+    dma16(live ? d.ra : d.rnone, st_a(lds, s) + (64 * w + 16 * P) * BK, d.a + P * d.lda16 + koff);
+  } else if constexpr (P < 8) {
+    dma16(live ? d.rb : d.rnone, st_b(lds, s) + (64 * w + 16 * (P - 4)) * BK,
+          d.b + (P - 4) * d.ldb16 + koff);
+  } else if constexpr (P == 8) {
+    dma4(live ? d.rsa : d.rnone, st_sa(lds, s) + 4 * 64 * w, d.s + (kt >> 1) * d.sqa);
+  } else {
+    dma4(live ? d.rsb : d.rnone, st_sb(lds, s) + 4 * 64 * w, d.s + (kt >> 1) * d.sqb);
+  }
+}
+
+// Per-lane LDS offsets of the fragment reads.  Lane (r, h) of wave (wm, wn)
+// reads rows wm*128 + 32 i + r of A (wn*128 + 32 j + r of B), chunks h and
+// 2 + h; the swizzle term (row / 4) % 4 = (r / 4) % 4 is the same for all four
+// rows of a lane, so each part needs one offset and the 32-row steps are
+// immediates.
+struct FragOff {
+  int a[2], b[2];
+};
+
+__device__ __forceinline__ FragOff make_frag_off(int wm, int wn, int r, int h) {
+  FragOff f;
+  const int x = (r >> 2) & 3;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int c = ((2 * p + h) ^ x) << 4;
+    f.a[p] = (wm * 128 + r) * BK + c;
+    f.b[p] = (wn * 128 + r) * BK + c;
+    asm volatile("" : "+v"(f.a[p]));
+    asm volatile("" : "+v"(f.b[p]));
+  }
+  return f;
+}
+
+__device__ __forceinline__ v8i frag2(uint32_t base, int off0, int off1, int rowstep) {
+  const v4i lo = lds_read16(base + off0 + rowstep);
+  const v4i hi = lds_read16(base + off1 + rowstep);
   return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-template <int S>
-__device__ __forceinline__ void mfma_substep(const Smem& sm, int st, int wm, int wn, int r, int h,
-                                             const int (&sa)[4], const int (&sb)[4],
-                                             v16f (&acc)[4][4]) {
-  v8i af[4], bf[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) af[i] = frag(sm.a[st], wm * 128 + 32 * i + r, 4 * S + h, 4 * S + 2 + h);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) bf[j] = frag(sm.b[st], wn * 128 + 32 * j + r, 4 * S + h, 4 * S + 2 + h);
+// Fragment K of the 8 a K-step needs, in the order the MFMAs (i-major over the
+// 4 x 4 blocks) first use them: A0, B0, B1, B2, B3, A1, A2, A3.
+template <int K>
+__device__ __forceinline__ void read_frag(uint32_t lds, int s, const FragOff& fo, v8i (&fa)[4],
+                                          v8i (&fb)[4]) {
+  if constexpr (K == 0 || K >= 5) {
+    constexpr int ia = K == 0 ? 0 : K - 4;
+    fa[ia] = frag2(st_a(lds, s), fo.a[0], fo.a[1], 32 * ia * BK);
+  } else {
+    constexpr int jb = K - 1;
+    fb[jb] = frag2(st_b(lds, s), fo.b[0], fo.b[1], 32 * jb * BK);
+  }
+}
+
+// This lane's two scale bytes of each of its rows (half h of the row's dword).
+__device__ __forceinline__ void read_scales(uint32_t lds, int s, int wm, int wn, int r, int h,
+                                            int (&sa)[4], int (&sb)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
+    sa[i] = (int)((lds_read4(st_sa(lds, s) + 4 * (wm * 128 + 32 * i + r)) >> (16 * h)) & 0xffffu);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, S,
-                                                                  sa[i], S, sb[j]);
+  for (int j = 0; j < 4; ++j)
+    sb[j] = (int)((lds_read4(st_sb(lds, s) + 4 * (wn * 128 + 32 * j + r)) >> (16 * h)) & 0xffffu);
+}
+
+template <int OPSEL, int M>
+__device__ __forceinline__ void mfma(const v8i (&fa)[4], const v8i (&fb)[4], const int (&sa)[4],
+                                     const int (&sb)[4], v16f (&acc)[4][4]) {
+  constexpr int i = M >> 2, j = M & 3;
+  acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, OPSEL,
+                                                              sa[i], OPSEL, sb[j]);
+}
+
+// One K-step kt (stage kt % 4; scale byte OPSEL = kt % 2 of the lane's half
+// dword).  Between its 16 MFMAs: the copies of K-step kt + 3 into stage
+// (kt + 3) % 4; after MFMA kBarrierAfter, a wait until at most the copies
+// issued after K-step kt + 1's remain (those of kt + 2 and the kt + 3 pieces
+// issued so far) and a barrier; then the fragments and scales of K-step kt + 1
+// are read between the remaining MFMAs.
+template <int OPSEL>
+__device__ __forceinline__ void k_step(uint32_t lds, const Dma& d, const FragOff& fo, int w,
+                                       int wm, int wn, int r, int h, int kt, int nk,
+                                       const v8i (&fa)[4], const v8i (&fb)[4], const int (&sa)[4],
+                                       const int (&sb)[4], v8i (&na)[4], v8i (&nb)[4],
+                                       int (&nsa)[4], int (&nsb)[4], v16f (&acc)[4][4]) {
+  constexpr int kIssuedBeforeWait =
+      kBarrierAfter + 1 < kDmaPerStep ? kBarrierAfter + 1 : kDmaPerStep;
+  const int s_dma = (kt + 3) & (kStages - 1);
+  const int s_next = (kt + 1) & (kStages - 1);
+  const bool live = kt + 3 < nk;
+  static_for<16>([&](auto mc) {
+    constexpr int m = decltype(mc)::value;
+    mfma<OPSEL, m>(fa, fb, sa, sb, acc);
+    fence();
+    if constexpr (m < kDmaPerStep) dma_piece<m>(d, lds, w, s_dma, kt + 3, live);
+    if constexpr (m == kBarrierAfter) {
+      wait_and_barrier<kDmaPerStep + kIssuedBeforeWait>();
+      read_scales(lds, s_next, wm, wn, r, h, nsa, nsb);
+    }
+    if constexpr (m >= kBarrierAfter && m - kBarrierAfter < 8)
+      read_frag<m - kBarrierAfter>(lds, s_next, fo, na, nb);
+    if constexpr (m == 15 && 16 - kBarrierAfter < 8) {
+      static_for<8 - (16 - kBarrierAfter)>([&](auto kc) {
+        read_frag<16 - kBarrierAfter + decltype(kc)::value>(lds, s_next, fo, na, nb);
+      });
+    }
+    fence();
+  });
 }
 
 // Stores one 32 x 32 accumulator block: lane (column r, half h), register v
@@ -177,12 +355,13 @@ __device__ __forceinline__ void store_block(const v16f& acc, __amdgpu_buffer_rsr
   }
 }
 
-__device__ void run_tile(Smem& sm, const TileDesc& t, int out_f32) {
+__device__ void run_tile(uint32_t lds, const TileDesc& t, int out_f32) {
   // opaque per-tile copy of the thread index: keeps the compiler from hoisting
   // every LDS / global offset of the tile body out of the persistent tile loop
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w >> 1, wn = w & 1;
   const int r = lane & 31, h = lane >> 5;
 
@@ -192,27 +371,32 @@ __device__ void run_tile(Smem& sm, const TileDesc& t, int out_f32) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
 
-  const int64_t nk = t.kl / BK;
-  Prefetch pf;
-  const TileRsrc rs = tile_rsrc(t);
+  const int nk = (int)(t.kl / BK);  // even: kl is a multiple of 128
   if (nk > 0) {
-    load_step(t, rs, 0, tid, pf);
-    store_step(sm, 0, tid, pf);
+    const Dma d = make_dma(t, w, lane);
+    const FragOff fo = make_frag_off(wm, wn, r, h);
+    // prologue: K-steps 0, 1, 2 into stages 0, 1, 2; wait for step 0
+    static_for<3>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      const bool live = s < nk;
+      static_for<kDmaPerStep>([&](auto pc) {
+        dma_piece<decltype(pc)::value>(d, lds, w, s, s, live);
+      });
+    });
+    wait_and_barrier<2 * kDmaPerStep>();
+    v8i f0a[4], f0b[4], f1a[4], f1b[4];
+    int s0a[4], s0b[4], s1a[4], s1b[4];
+    read_scales(lds, 0, wm, wn, r, h, s0a, s0b);
+    static_for<8>([&](auto kc) { read_frag<decltype(kc)::value>(lds, 0, fo, f0a, f0b); });
+    for (int kt = 0; kt < nk; kt += 2) {
+      k_step<0>(lds, d, fo, w, wm, wn, r, h, kt, nk, f0a, f0b, s0a, s0b, f1a, f1b, s1a, s1b, acc);
+      k_step<1>(lds, d, fo, w, wm, wn, r, h, kt + 1, nk, f1a, f1b, s1a, s1b, f0a, f0b, s0a, s0b,
+                acc);
+    }
   }
-  __syncthreads();
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const int st = (int)(kt & 1);
-    if (kt + 1 < nk) load_step(t, rs, kt + 1, tid, pf);
-    int sa[4], sb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sa[i] = (int)((sm.sa[st][wm * 128 + 32 * i + r] >> (16 * h)) & 0xffffu);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sb[j] = (int)((sm.sb[st][wn * 128 + 32 * j + r] >> (16 * h)) & 0xffffu);
-    mfma_substep<0>(sm, st, wm, wn, r, h, sa, sb, acc);
-    mfma_substep<1>(sm, st, wm, wn, r, h, sa, sb, acc);
-    if (kt + 1 < nk) store_step(sm, st ^ 1, tid, pf);
-    __syncthreads();
-  }
+  // every copy has landed and no wave still reads a stage before the next
+  // tile's prologue copies into them
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   const int esz = out_f32 ? 4 : 2;
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(t.out, (int64_t)t.out_rows * t.ldc * esz);
@@ -228,9 +412,33 @@ __device__ void run_tile(Smem& sm, const TileDesc& t, int out_f32) {
                   t.out_cols, out_f32);
 }
 
+// Position (mt, nt) of local tile u of a group with mtiles x ntiles tiles,
+// enumerated in blocks of kSuperM x kSuperN tiles (row of blocks by row of
+// blocks, m fastest inside a block); only the last block row / column can be
+// partial, so the block of u follows from two divisions.
+__device__ __forceinline__ void super_tile(int u, int mtiles, int ntiles, int& mt, int& nt) {
+  const int full_rows = mtiles / kSuperM;
+  int br, hgt, u2;
+  if (u < full_rows * kSuperM * ntiles) {
+    br = u / (kSuperM * ntiles);
+    hgt = kSuperM;
+    u2 = u - br * kSuperM * ntiles;
+  } else {
+    br = full_rows;
+    hgt = mtiles - full_rows * kSuperM;
+    u2 = u - full_rows * kSuperM * ntiles;
+  }
+  const int bc = u2 / (kSuperN * hgt);
+  const int u3 = u2 - bc * kSuperN * hgt;
+  mt = br * kSuperM + u3 % hgt;
+  nt = bc * kSuperN + u3 / hgt;
+}
+
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(MxArgs p) {
-  __shared__ Smem sm;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_ring[kStages * kStageBytes];
+  __shared__ Sched sm;
+  const uint32_t lds = lds_offset(lds_ring);
   const int G = p.G;
   const int tid = threadIdx.x;
   uint32_t* status = blockIdx.x == 0 ? p.status : nullptr;
@@ -253,23 +461,36 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(MxArgs p) {
   const int total = sm.pre[G];
   const int out_elem = p.out_f32 ? 4 : 2;
 
-  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+  // XCD-aware order: in each round of gridDim.x tiles, the workgroups of XCD x
+  // (b % 8 == x) take consecutive tile indices.
+  const int nxcd = gridDim.x % kXcds == 0 ? kXcds : 1;
+  const int per_xcd = gridDim.x / nxcd;
+  const int slot = (blockIdx.x % nxcd) * per_xcd + blockIdx.x / nxcd;
+
+  for (int round = 0;; ++round) {
+    const int tile = round * gridDim.x + slot;
+    if (tile >= total) break;
     const int g = find_group(sm.pre, G, tile);
     const int local = tile - sm.pre[g];
     TileDesc t;
     if (MODE == 0) {
       const int64_t m = group_extent(sm.off, g);
-      const int64_t mtiles = (m + BM - 1) / BM;
-      const int64_t mt = local % mtiles, nt = local / mtiles;
-      const int64_t row0 = sm.off[g] + mt * BM;
-      const int64_t n0 = nt * BN;
-      const int64_t ks = ((p.k / 32 + 3) / 4) * 4;
+      const int mtiles = (int)((m + BM - 1) / BM);
+      int mt, nt;
+      super_tile(local, mtiles, (int)ntn, mt, nt);
+      const int64_t row0 = sm.off[g] + (int64_t)mt * BM;
+      const int64_t n0 = (int64_t)nt * BN;
+      const int64_t nq = p.k / 128;            // scale words per row
+      const int64_t brow0 = (int64_t)g * p.n + n0;
       t.a = p.a + row0 * p.k;
-      t.as = p.as + row0 * ks;
-      t.b = p.b + ((int64_t)g * p.n + n0) * p.k;
-      t.bs = p.bs + ((int64_t)g * p.n + n0) * ks;
+      t.b = p.b + brow0 * p.k;
+      t.as = p.as + 4 * row0;                  // A scales: [nq][rows_cap] words
+      t.sqa = 4 * p.rows_cap;
+      t.as_bytes = nq * t.sqa - 4 * row0;
+      t.bs = p.bs + 4 * brow0;                 // B scales: [nq][G * n] words
+      t.sqb = 4 * (int64_t)G * p.n;
+      t.bs_bytes = nq * t.sqb - 4 * brow0;
       t.lda = t.ldb = p.k;
-      t.ldas = t.ldbs = ks;
       const int64_t rv = sm.off[g] + m - row0;
       t.a_rows = (int)(rv < BM ? rv : BM);
       const int64_t cv = p.n - n0;
@@ -282,16 +503,21 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(MxArgs p) {
     } else {
       const int64_t mp = group_extent(sm.off, g);
       const bool ok = (sm.off[g] % kColPad) == 0 && (mp % kColPad) == 0;
-      const int64_t ntk = (p.k + BN - 1) / BN;
-      const int64_t it = local / ntk, jt = local % ntk;
-      const int64_t n0 = it * BM, c0 = jt * BN;
+      const int ntm = (int)((p.n + BM - 1) / BM), ntk = (int)((p.k + BN - 1) / BN);
+      int it, jt;
+      super_tile(local, ntm, ntk, it, jt);
+      const int64_t n0 = (int64_t)it * BM, c0 = (int64_t)jt * BN;
       const int64_t t0 = sm.off[g];
+      // group g's blocks: data [n or k][mp], scales [mp / 128][n or k] words
       t.a = p.a + t0 * p.n + n0 * mp;
-      t.as = p.as + t0 * p.n / 32 + n0 * (mp / 32);
       t.b = p.b + t0 * p.k + c0 * mp;
-      t.bs = p.bs + t0 * p.k / 32 + c0 * (mp / 32);
+      t.as = p.as + t0 * p.n / 32 + 4 * n0;
+      t.sqa = 4 * p.n;
+      t.as_bytes = (mp / 128) * t.sqa - 4 * n0;
+      t.bs = p.bs + t0 * p.k / 32 + 4 * c0;
+      t.sqb = 4 * p.k;
+      t.bs_bytes = (mp / 128) * t.sqb - 4 * c0;
       t.lda = t.ldb = mp;
-      t.ldas = t.ldbs = mp / 32;
       const int64_t rv = p.n - n0, cv = p.k - c0;
       t.a_rows = (int)(rv < BM ? rv : BM);
       t.b_rows = (int)(cv < BN ? cv : BN);
@@ -301,7 +527,7 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(MxArgs p) {
       t.out_rows = t.a_rows;
       t.out_cols = t.b_rows;
     }
-    run_tile(sm, t, p.out_f32);
+    run_tile(lds, t, p.out_f32);
   }
 }
 

@@ -92,7 +92,6 @@ __global__ __launch_bounds__(256) void mx_rowwise_kernel(const uint16_t* __restr
   const int64_t row = unit / chunks;
   if (row >= live) return;
   const int64_t base = (unit % chunks) * kRowChunk;
-  const int64_t srow = ((cols / 32 + 3) / 4) * 4;  // stored scale bytes per row
 
   const uint16_t* xr = x + row * cols;
   int64_t e[2] = {base + 8 * lane, base + 512 + 8 * lane};
@@ -117,7 +116,8 @@ __global__ __launch_bounds__(256) void mx_rowwise_kernel(const uint16_t* __restr
       *reinterpret_cast<uint2*>(data + row * cols + e[h]) = q;
       if ((lane & 15) == 0) {
         const uint32_t dw = byte | (b2 << 8) | (b1 << 16) | (b3 << 24);
-        *reinterpret_cast<uint32_t*>(scales + row * srow + e[h] / 32) = dw;
+        // word (q, row) of the [NQ][rows_cap] scale array, q = 128-element stretch
+        *reinterpret_cast<uint32_t*>(scales + 4 * ((e[h] / 128) * rows_cap + row)) = dw;
       }
     }
   }
@@ -223,7 +223,9 @@ __global__ __launch_bounds__(256) void mx_colwise_kernel(
       uint8_t* dst = col_data + s_poff[g] * cols + (c0 + c) * mp + tt + 32 * w;
       reinterpret_cast<uint4*>(dst)[0] = make_uint4(q[0], q[1], q[2], q[3]);
       reinterpret_cast<uint4*>(dst)[1] = make_uint4(q[4], q[5], q[6], q[7]);
-      col_scales[s_poff[g] * cols / 32 + (c0 + c) * (mp / 32) + scale_pos(tt / 32 + w)] =
+      // word (tt / 128, column) of the group's [m~/128][cols] scale array; byte w
+      // in the b0, b2, b1, b3 order
+      col_scales[s_poff[g] * cols / 32 + 4 * ((tt / 128) * cols + c0 + c) + scale_pos(w)] =
           (uint8_t)byte;
     }
   }
@@ -249,12 +251,15 @@ __global__ __launch_bounds__(256) void mx_colwise_kernel(
       uint8_t* dst = row_data + row * cols + col;
       reinterpret_cast<uint4*>(dst)[0] = make_uint4(q0.x, q0.y, q1.x, q1.y);
       reinterpret_cast<uint4*>(dst)[1] = make_uint4(q2.x, q2.y, q3.x, q3.y);
-      const int64_t srow = ((cols / 32 + 3) / 4) * 4;
-      row_scales[row * srow + scale_pos(col / 32)] = (uint8_t)byte;
+      // word (q, row) of the [NQ][rows_cap] scale array, byte of block col / 32
+      const int64_t jb = col / 32;
+      row_scales[4 * ((jb / 4) * rows_cap + row) + scale_pos(jb & 3)] = (uint8_t)byte;
       // a row whose last 128-element stretch is short gets zero pad bytes
       if (col + 32 >= cols) {
         const int64_t nblk = cols / 32;
-        for (int64_t j = nblk; j < srow; ++j) row_scales[row * srow + scale_pos(j)] = 0;
+        const int64_t srow = ((nblk + 3) / 4) * 4;
+        for (int64_t j = nblk; j < srow; ++j)
+          row_scales[4 * ((j / 4) * rows_cap + row) + scale_pos(j & 3)] = 0;
       }
     }
   }

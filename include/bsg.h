@@ -98,18 +98,23 @@ int group_offsets_i32_to_i64(const int32_t* sizes, int64_t G, int64_t multiplier
  *   offsets      [G+1] int64 live row offsets (from group_offsets_i32_to_i64, pad 1).
  *   Rowwise output (both or neither):
  *     row_data   [rows_cap, cols] E4M3; rows >= offsets[G] untouched.
- *     row_scales [rows_cap, S] E8M0, S = roundup(cols/32, 4).  Within every 4
- *                consecutive scale bytes of a row (one 128-element stretch) the
- *                stored order is b0, b2, b1, b3 -- the order the grouped GEMM
- *                reads; bytes past cols/32 are 0.
+ *     row_scales E8M0 as [NQ][rows_cap] 4-byte words, NQ = ceil(cols/128): word
+ *                (q, r) holds row r's four scale bytes of columns
+ *                [128 q, 128 q + 128) in the order b0, b2, b1, b3; bytes past
+ *                cols/32 are 0 (rows_cap * 4 * NQ bytes).  This is the order the
+ *                grouped GEMM reads: 64 consecutive rows of one K-group are 256
+ *                contiguous bytes, and the two bytes each half of a wavefront
+ *                needs share one 16-bit half.
  *   Columnwise output (all three or none):
  *     padded_offsets [G+1] int64 (group_offsets_i32_to_i64 with pad_to 128).
  *     col_rows_cap   capacity of the columnwise buffers in padded tokens.
  *     col_data   group g: a [cols, m~_g] block (m~_g = padded_offsets[g+1] -
  *                padded_offsets[g]) at byte padded_offsets[g] * cols; token t of
  *                column c at [c, t]; tokens t >= m_g are 0x00.
- *     col_scales group g: a [cols, m~_g/32] block at byte padded_offsets[g] * cols / 32,
- *                same b0, b2, b1, b3 order along the token dim; padding blocks 0x00.
+ *     col_scales group g: an [m~_g/128][cols] array of words at byte
+ *                padded_offsets[g] * cols / 32, word (q, c) holding column c's scale
+ *                bytes of tokens [128 q, 128 q + 128) in the b0, b2, b1, b3 order;
+ *                padding blocks 0x00.
  * Both directions requested in one call read x once.
  */
 int grouped_quantize_mxfp8(const void* x, int64_t rows_cap, int64_t cols, int64_t G,
@@ -150,8 +155,9 @@ int grouped_quantize_nvfp4_rowscaled(const void* x, int64_t rows_cap, int64_t co
  *
  * mode BSG_FPROP_TN (ragged rows; output rows follow the lhs groups):
  *   Y[r, n] = sum_k A[r, k] * B[g, n, k]   for r in [offsets[g], offsets[g+1])
- *   a        [rows_cap, k] E4M3 rowwise,  a_scales [rows_cap, roundup(k/32,4)]
- *   b        [G, n, k] E4M3 rowwise,      b_scales [G, n, roundup(k/32,4)]
+ *   a        [rows_cap, k] E4M3 rowwise,  a_scales [k/128][rows_cap] words
+ *   b        [G, n, k] E4M3 rowwise,      b_scales [k/128][G * n] words (the weights
+ *            quantized by grouped_quantize_mxfp8 as G * n rows)
  *   offsets  [G+1] live row offsets; rows_cap = rows of a and out
  *   out      [rows_cap, n]; rows >= offsets[G] untouched.
  * mode BSG_WGRAD_NT (ragged contraction; uniform (G, n, k) output):

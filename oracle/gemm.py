@@ -12,7 +12,7 @@ only fp64 rounding, far below the GEMM tolerance.
 
 import numpy as np
 
-from .quantize import mxfp8_dequant_rows, nvfp4_block_dequant, mx_scale_row_len, MX_BLOCK
+from .quantize import mxfp8_dequant_rows, nvfp4_block_dequant, mx_scale_words, MX_BLOCK
 
 
 def _group_of_rows(offsets, rows):
@@ -25,26 +25,28 @@ def mxfp8_fprop(a_data, a_scales, b_data, b_scales, offsets, k, rows=None):
     ragged, rhs [G, N, K]):
         Y[r, n] = sum_k dq(A)[r, k] * dq(B)[g, n, k]  for r in [off[g], off[g+1]).
 
-    a_data [>=live, k], a_scales [>=live, roundup(k/32,4)], b_data [G, N, k],
-    b_scales [G, N, roundup(k/32,4)].  ``rows`` (optional) selects live rows to
-    compute; default all live rows.  Returns float64 [len(rows), N]."""
+    a_data [R_a, k] with scales [NQ, R_a, 4] (rowwise, R_a >= live rows);
+    b_data [G, N, k] with scales [NQ, G * N, 4] (the weights quantized as G * N
+    rows).  ``rows`` (optional) selects live rows to compute; default all live
+    rows.  Returns float64 [len(rows), N]."""
     off = np.asarray(offsets, dtype=np.int64)
     G, N = b_data.shape[0], b_data.shape[1]
-    srow = mx_scale_row_len(k)
+    nq = mx_scale_words(k)
     if rows is None:
         rows = np.arange(int(off[-1]))
     rows = np.asarray(rows, dtype=np.int64)
     a_data = np.asarray(a_data).reshape(-1, k)
-    a_scales = np.asarray(a_scales).reshape(-1, srow)
+    a_scales = np.asarray(a_scales).reshape(nq, -1, 4)
+    b_scales = np.asarray(b_scales).reshape(nq, G * N, 4)
     out = np.zeros((len(rows), N), dtype=np.float64)
     grp = _group_of_rows(off, rows)
     for g in range(G):
         sel = np.nonzero(grp == g)[0]
         if len(sel) == 0:
             continue
-        dqa = mxfp8_dequant_rows(a_data[rows[sel]], a_scales[rows[sel]], k)
+        dqa = mxfp8_dequant_rows(a_data[rows[sel]], a_scales[:, rows[sel], :], k)
         dqb = mxfp8_dequant_rows(np.asarray(b_data[g]).reshape(N, k),
-                                 np.asarray(b_scales[g]).reshape(N, srow), k)
+                                 b_scales[:, g * N:(g + 1) * N, :], k)
         out[sel] = dqa @ dqb.T
     return out
 
@@ -56,7 +58,7 @@ def mxfp8_wgrad(dy_col, dy_col_scales, x_col, x_col_scales, padded_offsets, n, k
         dW[g, i, j] = sum_{t < m_g} dq(dY)[off[g] + t, i] * dq(X)[off[g] + t, j]
 
     taken from the columnwise copies (group g: dY^T block [n, m~_g], X^T block
-    [k, m~_g], zero padding beyond m_g).  An empty group gives dW[g] = 0.
+    [k, m~_g], zero padding beyond m_g; scales [m~_g/128, n or k, 4] words).  An empty group gives dW[g] = 0.
     ``groups`` / ``out_rows`` optionally restrict the computed groups / rows i.
     Returns float64 [len(groups), len(out_rows), k]."""
     poff = np.asarray(padded_offsets, dtype=np.int64)
@@ -68,13 +70,13 @@ def mxfp8_wgrad(dy_col, dy_col_scales, x_col, x_col_scales, padded_offsets, n, k
         mp = int(poff[g + 1] - poff[g])
         if mp == 0:
             continue
-        srow = mx_scale_row_len(mp)
+        nq = mx_scale_words(mp)
         a = np.asarray(dy_col[poff[g] * n:poff[g + 1] * n]).reshape(n, mp)[out_rows]
         a_s = np.asarray(dy_col_scales[poff[g] * n // MX_BLOCK:poff[g + 1] * n // MX_BLOCK]
-                         ).reshape(n, srow)[out_rows]
+                         ).reshape(nq, n, 4)[:, out_rows, :]
         b = np.asarray(x_col[poff[g] * k:poff[g + 1] * k]).reshape(k, mp)
         b_s = np.asarray(x_col_scales[poff[g] * k // MX_BLOCK:poff[g + 1] * k // MX_BLOCK]
-                         ).reshape(k, srow)
+                         ).reshape(nq, k, 4)
         out[gi] = mxfp8_dequant_rows(a, a_s, mp) @ mxfp8_dequant_rows(b, b_s, mp).T
     return out
 

@@ -37,8 +37,8 @@ def mxfp8_rowwise(x_bits, offsets):
     dim of an fprop activation or of a weight, "gemm.py",
     ``_quantize_gemm_operands``).
 
-    Returns (data [live, C] uint8 E4M3, scales [live, roundup(C/32, 4)] uint8
-    E8M0 in the GEMM-ready order)."""
+    Returns (data [live, C] uint8 E4M3, scales [NQ, live, 4] uint8 E8M0 words in
+    the GEMM-ready order, NQ = ceil(C / 128))."""
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     rows, cols = x_bits.shape
     if cols % MX_BLOCK:
@@ -63,8 +63,8 @@ def mxfp8_colwise(x_bits, offsets, padded_offsets):
     Grouped Quant+GEMM", review threads).
 
     Group g's data is a row-major [C, m~_g] block at element offset
-    ``padded_offsets[g] * C`` and its scales a [C, m~_g / 32] block (GEMM-ready
-    order) at ``padded_offsets[g] * C / 32``.  Returns (data, scales) as flat
+    ``padded_offsets[g] * C`` and its scales an [m~_g / 128, C, 4] block of words
+    (GEMM-ready order) at ``padded_offsets[g] * C / 32``.  Returns (data, scales) as flat
     uint8 arrays of padded_offsets[G] * C and padded_offsets[G] * C / 32 bytes."""
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     rows, cols = x_bits.shape
@@ -92,9 +92,10 @@ def mxfp8_colwise(x_bits, offsets, padded_offsets):
 
 def mxfp8_dequant_rows(data, stored_scales, cols):
     """Q->DQ of MXFP8 rows: undo the GEMM-ready scale order, then
-    element * 2**(scale - 127).  data [R, cols], stored_scales [R, roundup(cols/32, 4)]."""
+    element * 2**(scale - 127).  data [R, cols], stored_scales [NQ, R, 4]."""
     data = np.asarray(data, dtype=np.uint8).reshape(-1, cols)
-    sbyte = mx_scales_from_gemm_order(np.asarray(stored_scales).reshape(data.shape[0], -1),
+    nq = mx_scale_row_bytes(cols // MX_BLOCK) // 4
+    sbyte = mx_scales_from_gemm_order(np.asarray(stored_scales).reshape(nq, data.shape[0], 4),
                                       cols // MX_BLOCK)
     vals = e4m3_decode(data).reshape(data.shape[0], cols // MX_BLOCK, MX_BLOCK)
     return (vals * e8m0_decode(sbyte)[..., None]).reshape(data.shape[0], cols)
@@ -159,5 +160,6 @@ def nvfp4_dequant(packed, block_scales, tsi, cols):
         np.asarray(tsi, dtype=np.float64)[:, None]
 
 
-def mx_scale_row_len(cols):
-    return mx_scale_row_bytes(cols // MX_BLOCK)
+def mx_scale_words(cols):
+    """Number of 4-byte scale words (128-element groups) per MXFP8 row."""
+    return mx_scale_row_bytes(cols // MX_BLOCK) // 4

@@ -46,7 +46,7 @@ def _check_fprop_case(name):
     xb = workloads.bf16_bits(case.x[torch.from_numpy(rows).to(dev)])
     ad, asc = Q.mxfp8_rowwise(xb, np.array([0, len(rows)]))
     gx = host_u8(case.xr)[rows]
-    gxs = host_u8(case.xrs)[rows]
+    gxs = host_u8(case.xrs)[:, rows, :]
     assert np.array_equal(gx, ad) and np.array_equal(gxs, asc), "activation quantize"
     grp = np.searchsorted(off, rows, side="right") - 1
     y = bf16_out_to_f64(case.y)
@@ -55,10 +55,11 @@ def _check_fprop_case(name):
         wrows = g * N + cols
         wb = workloads.bf16_bits(case.wt.view(G * N, K)[torch.from_numpy(wrows).to(dev)])
         bd, bsc = Q.mxfp8_rowwise(wb, np.array([0, len(cols)]))
-        assert np.array_equal(wq[wrows], bd) and np.array_equal(wqs[wrows], bsc), "weight quantize"
+        assert np.array_equal(wq[wrows], bd) and np.array_equal(wqs[:, wrows, :], bsc), \
+            "weight quantize"
         sel = np.nonzero(grp == g)[0]
-        ref = GM.mxfp8_fprop(ad[sel], asc[sel], bd.reshape(1, len(cols), K),
-                             bsc.reshape(1, len(cols), -1), np.array([0, len(sel)]), K)
+        ref = GM.mxfp8_fprop(ad[sel], asc[:, sel], bd.reshape(1, len(cols), K), bsc,
+                             np.array([0, len(sel)]), K)
         gemm_tolerance_check(y[rows[sel]][:, cols], ref, False, "%s group %d" % (name, g))
     assert not np.isnan(y[:int(off[-1])]).any(), "every live output row written"
     return case, off
@@ -82,8 +83,8 @@ def test_full_fprop_headline():
         blk = gd[poff[g] * K:poff[g + 1] * K].reshape(K, mp)[c0:c0 + 32]
         want = cd[poff[g] * 32:poff[g + 1] * 32].reshape(32, mp)
         assert np.array_equal(blk, want), g
-        sblk = gs[poff[g] * K // 32:poff[g + 1] * K // 32].reshape(K, mp // 32)[c0:c0 + 32]
-        swant = cs[poff[g]:poff[g + 1]].reshape(32, mp // 32)
+        sblk = gs[poff[g] * K // 32:poff[g + 1] * K // 32].reshape(mp // 128, K, 4)[:, c0:c0 + 32]
+        swant = cs[poff[g]:poff[g + 1]].reshape(mp // 128, 32, 4)
         assert np.array_equal(sblk, swant), g
 
 
@@ -102,7 +103,7 @@ def test_full_tiny_all_outputs():
     _, off = O.group_offsets(w.sizes)
     ad, asc = Q.mxfp8_rowwise(workloads.bf16_bits(case.x), off)
     bd, bsc = Q.mxfp8_rowwise(workloads.bf16_bits(case.wt).reshape(G * N, K), np.array([0, G * N]))
-    ref = GM.mxfp8_fprop(ad, asc, bd.reshape(G, N, K), bsc.reshape(G, N, -1), off, K)
+    ref = GM.mxfp8_fprop(ad, asc, bd.reshape(G, N, K), bsc, off, K)
     y = bf16_out_to_f64(case.y)
     for g in range(G):
         gemm_tolerance_check(y[off[g]:off[g + 1]], ref[off[g]:off[g + 1]], False, "group %d" % g)

@@ -34,14 +34,16 @@ def _fprop_operands(rng, sizes, K, N, rows_cap=None):
     _, off = O.group_offsets(sizes)
     ad, asc = Q.mxfp8_rowwise(x, off)
     bd, bsc = Q.mxfp8_rowwise(w, np.array([0, G * N]))
-    return sizes, off, x, w, ad, asc, bd.reshape(G, N, K), bsc.reshape(G, N, -1), rows_cap
+    return sizes, off, x, w, ad, asc, bd.reshape(G, N, K), bsc, rows_cap
 
 
 def _upload_rows(data, scales, rows_cap):
+    """Live rows' data [live, K] and scales [NQ, live, 4] -> device buffers of
+    rows_cap rows (zero capacity rows)."""
     d = np.zeros((rows_cap, data.shape[1]), np.uint8)
-    s = np.zeros((rows_cap, scales.shape[1]), np.uint8)
+    s = np.zeros((scales.shape[0], rows_cap, 4), np.uint8)
     d[:data.shape[0]] = data
-    s[:scales.shape[0]] = scales
+    s[:, :scales.shape[1]] = scales
     return to_dev(d), to_dev(s)
 
 
@@ -120,7 +122,7 @@ def test_fprop_end_to_end_tiny_config():
     _, off = O.group_offsets(w.sizes)
     ad, asc = Q.mxfp8_rowwise(xb, off)
     bd, bsc = Q.mxfp8_rowwise(wb.reshape(G * N, K), np.array([0, G * N]))
-    ref = GM.mxfp8_fprop(ad, asc, bd.reshape(G, N, K), bsc.reshape(G, N, -1), off, K)
+    ref = GM.mxfp8_fprop(ad, asc, bd.reshape(G, N, K), bsc, off, K)
 
     _, doff = bsg.group_offsets_i32_to_i64(to_dev(w.sizes))
     qa = bsg.grouped_quantize_mxfp8(t["x"], doff)
@@ -147,8 +149,9 @@ def test_grouped_equals_separate_calls_and_determinism():
         if sizes[g] == 0:
             continue
         r0, r1 = int(off[g]), int(off[g + 1])
-        one = bsg.grouped_gemm_mxfp8(bsg.BSG_FPROP_TN, a[r0:r1].contiguous(), a_s[r0:r1].contiguous(),
-                                     B[g:g + 1].contiguous(), Bs[g:g + 1].contiguous(),
+        one = bsg.grouped_gemm_mxfp8(bsg.BSG_FPROP_TN, a[r0:r1].contiguous(),
+                                     a_s[:, r0:r1].contiguous(), B[g:g + 1].contiguous(),
+                                     Bs[:, g * 512:(g + 1) * 512].contiguous(),
                                      to_dev(np.array([0, r1 - r0])), r1 - r0, 512, 384,
                                      out_dtype=bsg.BSG_OUT_F32)
         assert torch.equal(one, y[r0:r1])
@@ -158,9 +161,9 @@ def test_all_empty_routing():
     rng = np.random.default_rng(4)
     K, N = 128, 256
     a = to_dev(np.zeros((64, K), np.uint8))
-    a_s = to_dev(np.zeros((64, K // 32), np.uint8))
+    a_s = to_dev(np.zeros(bsg.mx_scale_shape(64, K), np.uint8))
     b = to_dev(rng.integers(0, 255, (2, N, K)).astype(np.uint8) & 0x77)
-    b_s = to_dev(np.full((2, N, K // 32), 127, np.uint8))
+    b_s = to_dev(np.full(bsg.mx_scale_shape(2 * N, K), 127, np.uint8))
     out = torch.full((64, N), float("nan"), dtype=torch.float32, device=device())
     bsg.grouped_gemm_mxfp8(bsg.BSG_FPROP_TN, a, a_s, b, b_s, to_dev(np.zeros(3, np.int64)), 64, N, K,
                            out=out, out_dtype=bsg.BSG_OUT_F32)
@@ -181,7 +184,7 @@ def test_hip_graph_replay_with_new_sizes():
     s64 = torch.empty(G, dtype=torch.int64, device=dev)
     off = torch.empty(G + 1, dtype=torch.int64, device=dev)
     rd = torch.empty((rows_cap, K), dtype=torch.uint8, device=dev)
-    rs = torch.empty((rows_cap, K // 32), dtype=torch.uint8, device=dev)
+    rs = torch.empty(bsg.mx_scale_shape(rows_cap, K), dtype=torch.uint8, device=dev)
     out = torch.empty((rows_cap, N), dtype=torch.float32, device=dev)
 
     def step():
@@ -208,7 +211,7 @@ def test_hip_graph_replay_with_new_sizes():
         torch.cuda.synchronize()
         _, o = O.group_offsets(np.array(new))
         ad, asc = Q.mxfp8_rowwise(xb, o)
-        ref = GM.mxfp8_fprop(ad, asc, bd.reshape(G, N, K), bsc.reshape(G, N, -1), o, K)
+        ref = GM.mxfp8_fprop(ad, asc, bd.reshape(G, N, K), bsc, o, K)
         y = host(out).astype(np.float64)
         for gi in range(G):
             gemm_tolerance_check(y[o[gi]:o[gi + 1]], ref[o[gi]:o[gi + 1]], True, str(new))

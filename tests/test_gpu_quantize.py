@@ -66,14 +66,13 @@ def test_rowwise_bit_exact(rows_cap, cols, sizes):
     bits[live:] = workloads.BF16_NAN_BITS
     _, off = O.group_offsets(sizes)
     want_d, want_s = Q.mxfp8_rowwise(bits, off)
-    srow = bsg.mx_scale_row_bytes(cols)
     d = filled_u8((rows_cap, cols))
-    s = filled_u8((rows_cap, srow))
+    s = filled_u8(bsg.mx_scale_shape(rows_cap, cols))
     out = bsg.grouped_quantize_mxfp8(bf16_dev(bits), to_dev(off), row_data=d, row_scales=s)
     d, s = host_u8(out["row_data"]), host_u8(out["row_scales"])
     assert np.array_equal(d[:live], want_d)
-    assert np.array_equal(s[:live], want_s)
-    assert np.all(d[live:] == SENTINEL) and np.all(s[live:] == SENTINEL)
+    assert np.array_equal(s[:, :live], want_s)
+    assert np.all(d[live:] == SENTINEL) and np.all(s[:, live:] == SENTINEL)
 
 
 def test_rowwise_codec_sweep_every_exponent():
@@ -127,7 +126,7 @@ def test_colwise_bit_exact(rows_cap, cols, sizes, with_rows):
     kw = {}
     if with_rows:
         kw = dict(row_data=filled_u8((rows_cap, cols)),
-                  row_scales=filled_u8((rows_cap, bsg.mx_scale_row_bytes(cols))))
+                  row_scales=filled_u8(bsg.mx_scale_shape(rows_cap, cols)))
     out = bsg.grouped_quantize_mxfp8(bf16_dev(bits), to_dev(off), rowwise=with_rows,
                                      padded_offsets=to_dev(poff), col_rows_cap=cap, col_data=cd,
                                      col_scales=cs, **kw)
@@ -139,7 +138,8 @@ def test_colwise_bit_exact(rows_cap, cols, sizes, with_rows):
     if with_rows:
         rd, rs = Q.mxfp8_rowwise(bits, off)
         assert np.array_equal(host_u8(out["row_data"])[:live], rd)
-        assert np.array_equal(host_u8(out["row_scales"])[:live], rs)
+        assert np.array_equal(host_u8(out["row_scales"])[:, :live], rs)
+        assert np.all(host_u8(out["row_scales"])[:, live:] == SENTINEL)
         assert np.all(host_u8(out["row_data"])[live:] == SENTINEL)
 
 

@@ -47,7 +47,7 @@ def test_mx_hand_blocks():
         bits = F.f32_to_bf16_bits_rne(block.astype(np.float32))
         assert np.array_equal(F.bf16_bits_to_f64(bits), block), "fixture value not bf16-exact"
         data, scales = Q.mxfp8_rowwise(bits.reshape(1, 32), np.array([0, 1]))
-        assert scales[0, 0] == int(sb_s, 16), (amax_s, val_s)
+        assert scales[0, 0, 0] == int(sb_s, 16), (amax_s, val_s)
         assert data[0, 1] == int(code_s, 16), (amax_s, val_s, hex(data[0, 1]))
 
 

@@ -35,7 +35,7 @@ def test_fprop_exact_on_lossless_inputs():
     _, off = O.group_offsets(sizes)
     ad, asc = Q.mxfp8_rowwise(xb, off)
     bd, bsc = Q.mxfp8_rowwise(wb, np.array([0, G * N]))
-    y = GM.mxfp8_fprop(ad, asc, bd.reshape(G, N, K), bsc.reshape(G, N, -1), off, K)
+    y = GM.mxfp8_fprop(ad, asc, bd.reshape(G, N, K), bsc, off, K)
     for g in range(G):
         want = xi[off[g]:off[g + 1]] @ wi[g * N:(g + 1) * N].T
         assert np.array_equal(y[off[g]:off[g + 1]], want.astype(np.float64))
@@ -64,8 +64,8 @@ def _decode_rows_fsum_check(data, stored, k):
     vals = np.zeros((rows, k))
     for r in range(rows):
         logical = []
-        for q in range(0, stored.shape[1], 4):
-            s0, s2, s1, s3 = stored[r, q:q + 4]
+        for q in range(stored.shape[0]):          # word (q, r): b0, b2, b1, b3
+            s0, s2, s1, s3 = stored[q, r]
             logical += [s0, s1, s2, s3]
         for j in range(k):
             c = int(data[r, j])
@@ -85,7 +85,7 @@ def test_fprop_fsum_on_tiny_config():
     _, off = O.group_offsets(w.sizes)
     ad, asc = Q.mxfp8_rowwise(xb, off)
     bd, bsc = Q.mxfp8_rowwise(wb.reshape(G * N, K), np.array([0, G * N]))
-    y = GM.mxfp8_fprop(ad, asc, bd.reshape(G, N, K), bsc.reshape(G, N, -1), off, K)
+    y = GM.mxfp8_fprop(ad, asc, bd.reshape(G, N, K), bsc, off, K)
     a = _decode_rows_fsum_check(ad, asc, K)
     b = _decode_rows_fsum_check(bd, bsc, K)
     for r in range(0, 128, 5):
@@ -104,11 +104,11 @@ def test_grouped_equals_per_expert_gemm():
     _, off = O.group_offsets(sizes)
     ad, asc = Q.mxfp8_rowwise(xb, off)
     bd, bsc = Q.mxfp8_rowwise(wb, np.array([0, G * N]))
-    bd, bsc = bd.reshape(G, N, K), bsc.reshape(G, N, -1)
+    bd = bd.reshape(G, N, K)
     y = GM.mxfp8_fprop(ad, asc, bd, bsc, off, K)
     for g in range(G):
-        one = GM.mxfp8_fprop(ad[off[g]:off[g + 1]], asc[off[g]:off[g + 1]], bd[g:g + 1],
-                             bsc[g:g + 1], np.array([0, sizes[g]]), K)
+        one = GM.mxfp8_fprop(ad[off[g]:off[g + 1]], asc[:, off[g]:off[g + 1]], bd[g:g + 1],
+                             bsc[:, g * N:(g + 1) * N], np.array([0, sizes[g]]), K)
         assert np.array_equal(y[off[g]:off[g + 1]], one)
     sub = GM.mxfp8_fprop(ad, asc, bd, bsc, off, K, rows=np.array([5, 40, 63]))
     assert np.array_equal(sub, y[[5, 40, 63]])

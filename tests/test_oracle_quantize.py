@@ -54,7 +54,11 @@ def test_workload_size_invariants(name):
 def test_mx_scale_order_hand_example_and_inverse():
     logical = np.array([[10, 11, 12, 13, 14, 15]], np.uint8)
     stored = L.mx_scales_to_gemm_order(logical)
-    assert stored.tolist() == [[10, 12, 11, 13, 14, 0, 15, 0]]
+    assert stored.reshape(-1).tolist() == [10, 12, 11, 13, 14, 0, 15, 0]
+    # two rows, two 128-element groups: words ordered group-major, then row
+    two = np.array([[1, 2, 3, 4, 5, 6, 7, 8], [11, 12, 13, 14, 15, 16, 17, 18]], np.uint8)
+    assert L.mx_scales_to_gemm_order(two).reshape(-1).tolist() == \
+        [1, 3, 2, 4, 11, 13, 12, 14, 5, 7, 6, 8, 15, 17, 16, 18]
     rng = np.random.default_rng(0)
     for nb in (1, 3, 4, 7, 8, 128):
         lg = rng.integers(0, 255, (5, nb)).astype(np.uint8)
@@ -123,7 +127,7 @@ def test_rowwise_matches_slow_rederivation():
     xv = F.bf16_bits_to_f64(bits)
     off = np.array([0, 3, 3, 7])                # 7 live rows of 9
     data, scales = Q.mxfp8_rowwise(bits, off)
-    assert data.shape == (7, 160) and scales.shape == (7, 8)
+    assert data.shape == (7, 160) and scales.shape == (2, 7, 4)
     for r in range(7):
         logical = []
         for blk in range(5):
@@ -131,7 +135,7 @@ def test_rowwise_matches_slow_rederivation():
             logical.append(b)
             assert list(data[r, blk * 32:(blk + 1) * 32]) == codes
         stored = [logical[0], logical[2], logical[1], logical[3], logical[4], 0, 0, 0]
-        assert list(scales[r]) == stored
+        assert list(scales[:, r, :].reshape(-1)) == stored
 
 
 def test_colwise_matches_slow_rederivation():
@@ -147,7 +151,7 @@ def test_colwise_matches_slow_rederivation():
     for g in range(4):
         m, mp = int(sizes[g]), int(poff[g + 1] - poff[g])
         blk_data = data[poff[g] * C:poff[g + 1] * C].reshape(C, mp)
-        blk_sc = scales[poff[g] * C // 32:poff[g + 1] * C // 32].reshape(C, mp // 32)
+        blk_sc = scales[poff[g] * C // 32:poff[g + 1] * C // 32].reshape(mp // 128, C, 4)
         for c in range(0, C, 7):
             col = [xv[off[g] + t, c] if t < m else 0.0 for t in range(mp)]
             logical = []
@@ -159,7 +163,7 @@ def test_colwise_matches_slow_rederivation():
             for q in range(0, len(logical), 4):
                 grp = logical[q:q + 4]
                 want += [grp[0], grp[2], grp[1], grp[3]]
-            assert list(blk_sc[c]) == want
+            assert list(blk_sc[:, c, :].reshape(-1)) == want
         assert np.all(blk_data[:, m:] == 0)
 
 
@@ -177,7 +181,7 @@ def test_grouped_equals_per_expert_concatenation():
         one = np.array([0, sizes[g]])
         d, s = Q.mxfp8_rowwise(part, one)
         assert np.array_equal(d, d_all[off[g]:off[g + 1]])
-        assert np.array_equal(s, s_all[off[g]:off[g + 1]])
+        assert np.array_equal(s, s_all[:, off[g]:off[g + 1]])
         _, p1 = O.group_offsets(sizes[g:g + 1], pad_to=128)
         cd, cs = Q.mxfp8_colwise(part, one, p1)
         assert np.array_equal(cd, cd_all[poff[g] * 96:poff[g + 1] * 96])
