@@ -198,7 +198,7 @@ int grouped_gemm_mxfp8(int mode, int64_t G, const uint8_t* a, const uint8_t* a_s
  *                         epilogue.  Otherwise a [rows_cap, ld_out] float32 buffer:
  *                         S is stored there first and a second kernel applies the
  *                         outer scales into out (the pages' two-step flow).
- * k must be a multiple of 32.
+ * k must be a positive multiple of 64 (one MFMA K-step).
  */
 int grouped_gemm_nvfp4_rowscaled(int64_t G, const uint8_t* a, const uint8_t* a_scales,
                                  const float* a_outer, const int64_t* offsets, int64_t rows_cap,
