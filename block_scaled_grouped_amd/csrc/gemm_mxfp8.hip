@@ -292,12 +292,16 @@ __device__ __forceinline__ void read_scales(uint32_t lds, int s, int wm, int wn,
     sb[j] = (int)((lds_read4(st_sb(lds, s) + 4 * (wn * 128 + 32 * j + r)) >> (16 * h)) & 0xffffu);
 }
 
+// B is the MFMA's first operand and A its second, so the accumulator of block
+// (i, j) is its transpose: lane (r, h) holds output row 32 i + r, and register
+// v column 32 j + 8 (v / 4) + 4 h + v % 4 -- four runs of four consecutive
+// columns, which the epilogue stores as whole 8- or 16-byte pieces.
 template <int OPSEL, int M>
 __device__ __forceinline__ void mfma(const v8i (&fa)[4], const v8i (&fb)[4], const int (&sa)[4],
                                      const int (&sb)[4], v16f (&acc)[4][4]) {
   constexpr int i = M >> 2, j = M & 3;
-  acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, OPSEL,
-                                                              sa[i], OPSEL, sb[j]);
+  acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, OPSEL,
+                                                              sb[j], OPSEL, sa[i]);
 }
 
 // One K-step kt (stage kt % 4; scale byte OPSEL = kt % 2 of the lane's half
@@ -337,22 +341,57 @@ __device__ __forceinline__ void k_step(uint32_t lds, const Dma& d, const FragOff
   });
 }
 
-// Stores one 32 x 32 accumulator block: lane (column r, half h), register v
-// holds row 8 (v / 4) + 4 h + v % 4.  `ro` covers the tile's valid rows, so
-// stores to rows past them are dropped by the buffer range check; columns are
-// masked here.
+// Stores one 32 x 32 accumulator block: this lane's row `row`, columns
+// col0 + 8 q + [0, 4) in registers 4 q .. 4 q + 3.  `ro` covers the tile's
+// valid rows, so stores to rows past them are dropped by the buffer range
+// check; a column past out_cols gets an offset past every range (kDropped),
+// which drops it the same way, without a branch.  WIDE (row stride and out_cols
+// multiples of 4, so a run of four is all in or all out and 8- / 16-byte
+// aligned): one store per run.  Otherwise one store per element.
+constexpr uint32_t kDropped = 0xfffffff0u;
+
+template <bool WIDE, bool F32>
 __device__ __forceinline__ void store_block(const v16f& acc, __amdgpu_buffer_rsrc_t ro, int ldc,
-                                            int row0, int col, int h, int out_cols, int out_f32) {
-  if (col >= out_cols) return;
+                                            int row, int col0, int out_cols) {
+  constexpr int esz = F32 ? 4 : 2;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int row = row0 + 8 * (v >> 2) + 4 * h + (v & 3);
+  for (int q = 0; q < 4; ++q) {
+    const int col = col0 + 8 * q;
     const int idx = row * ldc + col;
-    if (out_f32)
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(acc[v]), ro, idx * 4, 0, 0);
-    else
-      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16_rne(acc[v]), ro, idx * 2, 0, 0);
+    if constexpr (WIDE) {
+      const int off = col < out_cols ? idx * esz : (int)kDropped;
+      if constexpr (F32) {
+        const v4i v = {__float_as_int(acc[4 * q]), __float_as_int(acc[4 * q + 1]),
+                       __float_as_int(acc[4 * q + 2]), __float_as_int(acc[4 * q + 3])};
+        __builtin_amdgcn_raw_buffer_store_b128(v, ro, off, 0, 0);
+      } else {
+        const v2bf lo = __builtin_convertvector((v2f){acc[4 * q], acc[4 * q + 1]}, v2bf);
+        const v2bf hi = __builtin_convertvector((v2f){acc[4 * q + 2], acc[4 * q + 3]}, v2bf);
+        const v2i v = {__builtin_bit_cast(int, lo), __builtin_bit_cast(int, hi)};
+        __builtin_amdgcn_raw_buffer_store_b64(v, ro, off, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int off = col + e < out_cols ? (idx + e) * esz : (int)kDropped;
+        if constexpr (F32)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(acc[4 * q + e]), ro, off, 0, 0);
+        else
+          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16_rne(acc[4 * q + e]),
+                                                ro, off, 0, 0);
+      }
+    }
   }
+}
+
+template <bool WIDE, bool F32>
+__device__ __forceinline__ void store_tile(const v16f (&acc)[4][4], __amdgpu_buffer_rsrc_t ro,
+                                           int ldc, int row, int col, int out_cols) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      store_block<WIDE, F32>(acc[i][j], ro, ldc, row + 32 * i, col + 32 * j, out_cols);
 }
 
 __device__ void run_tile(uint32_t lds, const TileDesc& t, int out_f32) {
@@ -404,12 +443,15 @@ __device__ void run_tile(uint32_t lds, const TileDesc& t, int out_f32) {
   // store offsets out of the persistent tile loop into registers
   int ldc = (int)t.ldc;
   asm volatile("" : "+s"(ldc));
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      store_block(acc[i][j], ro, ldc, wm * 128 + 32 * i, wn * 128 + 32 * j + r, h,
-                  t.out_cols, out_f32);
+  const int row = wm * 128 + r, col = wn * 128 + 4 * h;
+  const bool wide = (ldc & 3) == 0 && (t.out_cols & 3) == 0;
+  if (out_f32) {
+    if (wide) store_tile<true, true>(acc, ro, ldc, row, col, t.out_cols);
+    else store_tile<false, true>(acc, ro, ldc, row, col, t.out_cols);
+  } else {
+    if (wide) store_tile<true, false>(acc, ro, ldc, row, col, t.out_cols);
+    else store_tile<false, false>(acc, ro, ldc, row, col, t.out_cols);
+  }
 }
 
 // Position (mt, nt) of local tile u of a group with mtiles x ntiles tiles,

@@ -32,7 +32,7 @@ constexpr int BK = 64;          // elements per K-step (32 bytes of E2M1 per row
 constexpr int kThreads = 256;
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef float v2f __attribute__((ext_vector_type(2)));
+
 
 struct NvArgs {
   const uint8_t* a;

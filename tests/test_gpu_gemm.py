@@ -52,6 +52,8 @@ FPROP_CASES = [
     ([32, 0, 64, 32], 128, 128, 128),
     ([0, 0, 700], 256, 300, 700),
     ([1], 128, 1, 1),
+    ([5, 300, 0, 40], 128, 258, 400),   # row stride not a multiple of 4: per-element stores
+    ([260, 3], 256, 260, 263),          # a 4-column last tile
 ]
 
 
