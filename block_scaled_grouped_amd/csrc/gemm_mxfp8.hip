@@ -20,9 +20,10 @@
 //
 // Operands go global -> LDS by the buffer unit directly (LDS-DMA: lane l of a
 // load lands at LDS base + 16 l, so a swizzled layout is made by permuting each
-// lane's source address) into a ring of 4 LDS stages; K-step k + 3 is in flight
-// while the MFMAs of step k run, so a fetch has three K-steps (~3000 cycles) to
-// arrive.  LDS rows are 64 bytes; 16-byte chunk c of row r sits in slot
+// lane's source address) into a ring of 4 LDS stages.  A stage is free as soon
+// as its fragments are in registers (one step before its MFMAs run), so the
+// copies of K-step k + 4 are issued during step k and have three K-steps
+// (~3000 cycles) to arrive.  LDS rows are 64 bytes; 16-byte chunk c of row r sits in slot
 // c ^ ((r / 4) % 4), which spreads the MFMA fragment reads (32 rows, same
 // chunk) over all banks.  One barrier per K-step; the schedule of a K-step is
 // written out MFMA by MFMA (DMA issues and next-step fragment reads placed
@@ -67,7 +68,8 @@ constexpr int kTileA = BM * BK;        // 16 KiB
 constexpr int kTileB = BN * BK;
 constexpr int kStageBytes = kTileA + kTileB + 4 * BM + 4 * BN;
 constexpr int kDmaPerStep = 10;        // per wave: 4 A, 4 B, 1 A-scale, 1 B-scale
-constexpr int kBarrierAfter = 7;       // MFMA index after which a K-step waits + barriers
+constexpr int kBarrierAfter = 1;       // MFMA index after which a K-step waits + barriers
+constexpr int kAhead = kStages;        // a K-step's copies are issued this many steps early
 constexpr int kSuperM = 4, kSuperN = 8;  // tile block one XCD works on
 constexpr int kXcds = 8;
 
@@ -304,37 +306,42 @@ __device__ __forceinline__ void mfma(const v8i (&fa)[4], const v8i (&fb)[4], con
                                                               sb[j], OPSEL, sa[i]);
 }
 
-// One K-step kt (stage kt % 4; scale byte OPSEL = kt % 2 of the lane's half
-// dword).  Between its 16 MFMAs: the copies of K-step kt + 3 into stage
-// (kt + 3) % 4; after MFMA kBarrierAfter, a wait until at most the copies
-// issued after K-step kt + 1's remain (those of kt + 2 and the kt + 3 pieces
-// issued so far) and a barrier; then the fragments and scales of K-step kt + 1
-// are read between the remaining MFMAs.
+// One K-step kt (its fragments already in registers; scale byte OPSEL = kt % 2
+// of the lane's half dword).  After MFMA kBarrierAfter: wait until at most the
+// copies of K-steps kt + 2 and kt + 3 are outstanding (so kt + 1 has landed)
+// and no LDS read of this wave is pending, then a barrier: now stage
+// (kt + 1) % 4 is complete for every wave and stage kt % 4 (read during step
+// kt - 1) is free.  Between the remaining MFMAs: the fragments and scales of
+// K-step kt + 1, and the copies of K-step kt + 4 into stage kt % 4.  A copy thus
+// has three K-steps to arrive, and the LDS reads of a step are spread over 14
+// of its 16 MFMAs.
 template <int OPSEL>
 __device__ __forceinline__ void k_step(uint32_t lds, const Dma& d, const FragOff& fo, int w,
                                        int wm, int wn, int r, int h, int kt, int nk,
                                        const v8i (&fa)[4], const v8i (&fb)[4], const int (&sa)[4],
                                        const int (&sb)[4], v8i (&na)[4], v8i (&nb)[4],
                                        int (&nsa)[4], int (&nsb)[4], v16f (&acc)[4][4]) {
-  constexpr int kIssuedBeforeWait =
-      kBarrierAfter + 1 < kDmaPerStep ? kBarrierAfter + 1 : kDmaPerStep;
-  const int s_dma = (kt + 3) & (kStages - 1);
+  static_assert(kBarrierAfter >= 0 && kBarrierAfter < 16, "K-step schedule");
+  const int s_dma = kt & (kStages - 1);
   const int s_next = (kt + 1) & (kStages - 1);
-  const bool live = kt + 3 < nk;
+  const bool live = kt + kAhead < nk;
   static_for<16>([&](auto mc) {
     constexpr int m = decltype(mc)::value;
     mfma<OPSEL, m>(fa, fb, sa, sb, acc);
     fence();
-    if constexpr (m < kDmaPerStep) dma_piece<m>(d, lds, w, s_dma, kt + 3, live);
     if constexpr (m == kBarrierAfter) {
-      wait_and_barrier<kDmaPerStep + kIssuedBeforeWait>();
+      wait_and_barrier<(kAhead - 2) * kDmaPerStep>();
       read_scales(lds, s_next, wm, wn, r, h, nsa, nsb);
     }
-    if constexpr (m >= kBarrierAfter && m - kBarrierAfter < 8)
-      read_frag<m - kBarrierAfter>(lds, s_next, fo, na, nb);
-    if constexpr (m == 15 && 16 - kBarrierAfter < 8) {
-      static_for<8 - (16 - kBarrierAfter)>([&](auto kc) {
-        read_frag<16 - kBarrierAfter + decltype(kc)::value>(lds, s_next, fo, na, nb);
+    if constexpr (m >= kBarrierAfter) {
+      // slot q after the barrier; whatever does not fit before the last MFMA
+      // is issued after it
+      constexpr int q = m - kBarrierAfter;
+      constexpr int qend = m == 15 ? 16 : q + 1;
+      static_for<qend - q>([&](auto uc) {
+        constexpr int u = q + decltype(uc)::value;
+        if constexpr (u < 8) read_frag<u>(lds, s_next, fo, na, nb);
+        if constexpr (u < kDmaPerStep) dma_piece<u>(d, lds, w, s_dma, kt + kAhead, live);
       });
     }
     fence();
@@ -436,15 +443,15 @@ __device__ void run_tile(uint32_t lds, const TileDesc& t, int out_f32) {
   if (nk > 0) {
     const Dma d = make_dma(t, w, lane);
     const FragOff fo = make_frag_off(wm, wn, r, h);
-    // prologue: K-steps 0, 1, 2 into stages 0, 1, 2; wait for step 0
-    static_for<3>([&](auto sc) {
+    // prologue: K-steps 0 .. 3 into stages 0 .. 3; wait for step 0
+    static_for<kAhead>([&](auto sc) {
       constexpr int s = decltype(sc)::value;
       const bool live = s < nk;
       static_for<kDmaPerStep>([&](auto pc) {
         dma_piece<decltype(pc)::value>(d, lds, w, s, s, live);
       });
     });
-    wait_and_barrier<2 * kDmaPerStep>();
+    wait_and_barrier<(kAhead - 1) * kDmaPerStep>();
     v8i f0a[4], f0b[4], f1a[4], f1b[4];
     int s0a[4], s0b[4], s1a[4], s1b[4];
     read_scales(lds, 0, wm, wn, r, h, s0a, s0b);
