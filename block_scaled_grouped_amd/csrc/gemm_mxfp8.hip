@@ -20,13 +20,14 @@
 //
 // Operands go global -> LDS by the buffer unit directly (LDS-DMA: lane l of a
 // load lands at LDS base + 16 l, so a swizzled layout is made by permuting each
-// lane's source address) into a ring of 4 LDS stages.  A stage is free as soon
-// as its fragments are in registers (one step before its MFMAs run), so the
-// copies of K-step k + 4 are issued during step k and have three K-steps
-// (~3000 cycles) to arrive.  LDS rows are 64 bytes; 16-byte chunk c of row r sits in slot
-// c ^ ((r / 4) % 4), which spreads the MFMA fragment reads (32 rows, same
-// chunk) over all banks.  One barrier per K-step; the schedule of a K-step is
-// written out MFMA by MFMA (DMA issues and next-step fragment reads placed
+// lane's source address).  An LDS buffer holds two K-steps: 128-byte rows, so
+// every copy request is one whole 128-byte line, plus the one scale dword per
+// row that covers those 128 K.  Two buffers: while pair p is consumed from one,
+// pair p + 1 lands in the other, and the copies of pair p + 2 are issued as soon
+// as pair p's last fragments are in registers.  16-byte chunk c of row r sits
+// in slot c ^ ((r / 2) % 8), which spreads the MFMA fragment reads (32 rows,
+// same chunk) over all banks.  One barrier per pair; the schedule of a K-step
+// is written out MFMA by MFMA (copy issues and next-step fragment reads placed
 // between them) and fenced so the compiler keeps it.
 //
 // Tiles are handed out XCD-aware: workgroup b runs on XCD b % 8, and the 32
@@ -62,14 +63,16 @@ __device__ __forceinline__ void static_for(F&& f) {
 constexpr int BM = 256;
 constexpr int BN = 256;
 constexpr int BK = 64;                 // bytes (= E4M3 elements) per row per K-step
+constexpr int kPairK = 2 * BK;         // bytes per row per LDS buffer: two K-steps,
+                                       // one scale word (one full 128-byte line)
 constexpr int kThreads = 256;
-constexpr int kStages = 4;
-constexpr int kTileA = BM * BK;        // 16 KiB
-constexpr int kTileB = BN * BK;
-constexpr int kStageBytes = kTileA + kTileB + 4 * BM + 4 * BN;
-constexpr int kDmaPerStep = 10;        // per wave: 4 A, 4 B, 1 A-scale, 1 B-scale
-constexpr int kBarrierAfter = 1;       // MFMA index after which a K-step waits + barriers
-constexpr int kAhead = kStages;        // a K-step's copies are issued this many steps early
+constexpr int kBufs = 2;
+constexpr int kTileA = BM * kPairK;    // 32 KiB
+constexpr int kTileB = BN * kPairK;
+constexpr int kBufBytes = kTileA + kTileB + 4 * BM + 4 * BN;
+constexpr int kDmaPerPair = 18;        // per wave: 8 A, 8 B, 1 A-scale, 1 B-scale
+constexpr int kBarrierAfter = 0;       // MFMA index of a pair's second step after which it
+                                       // waits + barriers
 constexpr int kSuperM = 4, kSuperN = 8;  // tile block one XCD works on
 constexpr int kXcds = 8;
 
@@ -123,8 +126,8 @@ __device__ __forceinline__ uint32_t lds_offset(T* shared_ptr) {
   return (uint32_t)(size_t)(__attribute__((address_space(3))) T*)(shared_ptr);
 }
 
-// Stage s of the ring: A tile, B tile, A scale dwords, B scale dwords.
-__device__ __forceinline__ uint32_t st_a(uint32_t base, int s) { return base + s * kStageBytes; }
+// Buffer s: A tile, B tile, A scale dwords, B scale dwords.
+__device__ __forceinline__ uint32_t st_a(uint32_t base, int s) { return base + s * kBufBytes; }
 __device__ __forceinline__ uint32_t st_b(uint32_t base, int s) { return st_a(base, s) + kTileA; }
 __device__ __forceinline__ uint32_t st_sa(uint32_t base, int s) { return st_b(base, s) + kTileB; }
 __device__ __forceinline__ uint32_t st_sb(uint32_t base, int s) { return st_sa(base, s) + 4 * BM; }
@@ -189,15 +192,16 @@ __device__ __forceinline__ void wait_and_barrier() {
 
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 
-// A wavefront's share of one K-step's copies.  Wave w fills rows
-// [64 w, 64 w + 64) of both operand tiles, sixteen 64-byte rows (1 KiB) per
-// load: in load q lane l writes row 64 w + 16 q + l / 4, slot l % 4, which must
-// hold logical chunk (l % 4) ^ ((row / 4) % 4) = (l % 4) ^ ((l / 16) % 4).  The
-// scale words of its 64 rows for one 128-wide K-group are 256 contiguous bytes.
+// A wavefront's share of one pair's copies.  Wave w fills rows
+// [64 w, 64 w + 64) of both operand tiles, eight 128-byte rows (1 KiB) per
+// load: in load q lane l writes row 64 w + 8 q + l / 8, slot l % 8, which must
+// hold logical chunk (l % 8) ^ ((row / 2) % 8) = (l % 8) ^ (4 (q % 2) + l / 16),
+// so even and odd loads need their own lane offsets.  The scale words of its 64
+// rows for the pair's 128-wide K-group are 256 contiguous bytes.
 struct Dma {
   v4i ra, rb, rsa, rsb;  // descriptors (uniform)
   v4i rnone;             // zero-length descriptor: turns a copy into a no-op
-  int a, b;              // lane source offsets for q = 0, K-step 0
+  int a[2], b[2];        // lane source offsets of even / odd loads (q = 0, 1), pair 0
   int s;                 // lane scale-word offset (row 64 w + l, K-group 0)
   int lda16, ldb16;      // 16 rows of stride (uniform)
   int sqa, sqb;          // scale K-group strides (uniform)
@@ -210,10 +214,13 @@ __device__ __forceinline__ Dma make_dma(const TileDesc& t, int w, int lane) {
   d.rsa = make_rsrc_words(t.as, t.as_bytes);
   d.rsb = make_rsrc_words(t.bs, t.bs_bytes);
   d.rnone = make_rsrc_words(t.a, 0);
-  const int row = 64 * w + (lane >> 2);
-  const int c = (lane & 3) ^ ((lane >> 4) & 3);
-  d.a = row * (int)t.lda + c * 16;
-  d.b = row * (int)t.ldb + c * 16;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int row = 64 * w + 8 * e + (lane >> 3);
+    const int c = (lane & 7) ^ (4 * e + (lane >> 4));
+    d.a[e] = row * (int)t.lda + c * 16;
+    d.b[e] = row * (int)t.ldb + c * 16;
+  }
   d.s = 4 * (64 * w + lane);
   d.lda16 = __builtin_amdgcn_readfirstlane(16 * (int)t.lda);
   d.ldb16 = __builtin_amdgcn_readfirstlane(16 * (int)t.ldb);
@@ -222,44 +229,51 @@ __device__ __forceinline__ Dma make_dma(const TileDesc& t, int w, int lane) {
   return d;
 }
 
-// Copy piece P (0..3 A rows, 4..7 B rows, 8 A scales, 9 B scales) of K-step kt
-// into stage s; `live` false makes it a no-op copy (past the last K-step).
+// Copy piece P (0..7 A rows, 8..15 B rows, 16 A scales, 17 B scales) of pair
+// kp (K bytes [128 kp, 128 kp + 128)) into buffer s; `live` false makes it a
+// no-op copy (past the last pair).
 template <int P>
-__device__ __forceinline__ void dma_piece(const Dma& d, uint32_t lds, int w, int s, int kt,
+__device__ __forceinline__ void dma_piece(const Dma& d, uint32_t lds, int w, int s, int kp,
                                           bool live) {
-  const int koff = kt * BK;
-  if constexpr (P < 4) {
-    dma16(live ? d.ra : d.rnone, st_a(lds, s) + (64 * w + 16 * P) * BK, d.a + P * d.lda16 + koff);
-  } else if constexpr (P < 8) {
-    dma16(live ? d.rb : d.rnone, st_b(lds, s) + (64 * w + 16 * (P - 4)) * BK,
-          d.b + (P - 4) * d.ldb16 + koff);
-  } else if constexpr (P == 8) {
-    dma4(live ? d.rsa : d.rnone, st_sa(lds, s) + 4 * 64 * w, d.s + (kt >> 1) * d.sqa);
+  const int koff = kp * kPairK;
+  if constexpr (P < 8) {
+    dma16(live ? d.ra : d.rnone, st_a(lds, s) + (64 * w + 8 * P) * kPairK,
+          d.a[P & 1] + (P >> 1) * d.lda16 + koff);
+  } else if constexpr (P < 16) {
+    constexpr int q = P - 8;
+    dma16(live ? d.rb : d.rnone, st_b(lds, s) + (64 * w + 8 * q) * kPairK,
+          d.b[q & 1] + (q >> 1) * d.ldb16 + koff);
+  } else if constexpr (P == 16) {
+    dma4(live ? d.rsa : d.rnone, st_sa(lds, s) + 4 * 64 * w, d.s + kp * d.sqa);
   } else {
-    dma4(live ? d.rsb : d.rnone, st_sb(lds, s) + 4 * 64 * w, d.s + (kt >> 1) * d.sqb);
+    dma4(live ? d.rsb : d.rnone, st_sb(lds, s) + 4 * 64 * w, d.s + kp * d.sqb);
   }
 }
 
 // Per-lane LDS offsets of the fragment reads.  Lane (r, h) of wave (wm, wn)
-// reads rows wm*128 + 32 i + r of A (wn*128 + 32 j + r of B), chunks h and
-// 2 + h; the swizzle term (row / 4) % 4 = (r / 4) % 4 is the same for all four
-// rows of a lane, so each part needs one offset and the 32-row steps are
-// immediates.
+// reads rows wm*128 + 32 i + r of A (wn*128 + 32 j + r of B); for K-step S of
+// the pair, logical chunks 4 S + h and 4 S + 2 + h.  The swizzle term
+// (row / 2) % 8 = (r / 2) % 8 is the same for all four rows of a lane, so each
+// (S, part) needs one offset and the 32-row steps are immediates.  With 64-bank
+// LDS, 16 lanes reading one chunk of 16 consecutive rows hit 16 distinct 16-byte
+// bank groups.
 struct FragOff {
-  int a[2], b[2];
+  int a[2][2], b[2][2];
 };
 
 __device__ __forceinline__ FragOff make_frag_off(int wm, int wn, int r, int h) {
   FragOff f;
-  const int x = (r >> 2) & 3;
+  const int x = (r >> 1) & 7;
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int c = ((2 * p + h) ^ x) << 4;
-    f.a[p] = (wm * 128 + r) * BK + c;
-    f.b[p] = (wn * 128 + r) * BK + c;
-    asm volatile("" : "+v"(f.a[p]));
-    asm volatile("" : "+v"(f.b[p]));
-  }
+  for (int S = 0; S < 2; ++S)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int c = ((4 * S + 2 * p + h) ^ x) << 4;
+      f.a[S][p] = (wm * 128 + r) * kPairK + c;
+      f.b[S][p] = (wn * 128 + r) * kPairK + c;
+      asm volatile("" : "+v"(f.a[S][p]));
+      asm volatile("" : "+v"(f.b[S][p]));
+    }
   return f;
 }
 
@@ -269,17 +283,17 @@ __device__ __forceinline__ v8i frag2(uint32_t base, int off0, int off1, int rows
   return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// Fragment K of the 8 a K-step needs, in the order the MFMAs (i-major over the
-// 4 x 4 blocks) first use them: A0, B0, B1, B2, B3, A1, A2, A3.
-template <int K>
+// Fragment K of the 8 K-step S of a pair needs, in the order the MFMAs
+// (i-major over the 4 x 4 blocks) first use them: A0, B0, B1, B2, B3, A1, A2, A3.
+template <int S, int K>
 __device__ __forceinline__ void read_frag(uint32_t lds, int s, const FragOff& fo, v8i (&fa)[4],
                                           v8i (&fb)[4]) {
   if constexpr (K == 0 || K >= 5) {
     constexpr int ia = K == 0 ? 0 : K - 4;
-    fa[ia] = frag2(st_a(lds, s), fo.a[0], fo.a[1], 32 * ia * BK);
+    fa[ia] = frag2(st_a(lds, s), fo.a[S][0], fo.a[S][1], 32 * ia * kPairK);
   } else {
     constexpr int jb = K - 1;
-    fb[jb] = frag2(st_b(lds, s), fo.b[0], fo.b[1], 32 * jb * BK);
+    fb[jb] = frag2(st_b(lds, s), fo.b[S][0], fo.b[S][1], 32 * jb * kPairK);
   }
 }
 
@@ -304,45 +318,66 @@ __device__ __forceinline__ void mfma(const v8i (&fa)[4], const v8i (&fb)[4], con
   constexpr int i = M >> 2, j = M & 3;
   acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, OPSEL,
                                                               sb[j], OPSEL, sa[i]);
+  // the MFMA intrinsic has no side effects, so IR passes may sink it past the
+  // schedule's fences; an opaque use of its result keeps it in place
+  asm volatile("" : "+a"(acc[i][j]));
 }
 
-// One K-step kt (its fragments already in registers; scale byte OPSEL = kt % 2
-// of the lane's half dword).  After MFMA kBarrierAfter: wait until at most the
-// copies of K-steps kt + 2 and kt + 3 are outstanding (so kt + 1 has landed)
-// and no LDS read of this wave is pending, then a barrier: now stage
-// (kt + 1) % 4 is complete for every wave and stage kt % 4 (read during step
-// kt - 1) is free.  Between the remaining MFMAs: the fragments and scales of
-// K-step kt + 1, and the copies of K-step kt + 4 into stage kt % 4.  A copy thus
-// has three K-steps to arrive, and the LDS reads of a step are spread over 14
-// of its 16 MFMAs.
-template <int OPSEL>
-__device__ __forceinline__ void k_step(uint32_t lds, const Dma& d, const FragOff& fo, int w,
-                                       int wm, int wn, int r, int h, int kt, int nk,
-                                       const v8i (&fa)[4], const v8i (&fb)[4], const int (&sa)[4],
-                                       const int (&sb)[4], v8i (&na)[4], v8i (&nb)[4],
-                                       int (&nsa)[4], int (&nsb)[4], v16f (&acc)[4][4]) {
-  static_assert(kBarrierAfter >= 0 && kBarrierAfter < 16, "K-step schedule");
-  const int s_dma = kt & (kStages - 1);
-  const int s_next = (kt + 1) & (kStages - 1);
-  const bool live = kt + kAhead < nk;
+// The first K-step of pair kp (buffer s = kp % 2, scale byte 0 of the lane's
+// half dword): its 16 MFMAs, and between them the fragments of the pair's
+// second K-step (same buffer, which has landed).
+__device__ __forceinline__ void step_even(uint32_t lds, int s, const FragOff& fo,
+                                          const v8i (&fa)[4], const v8i (&fb)[4],
+                                          const int (&sa)[4], const int (&sb)[4], v8i (&na)[4],
+                                          v8i (&nb)[4], v16f (&acc)[4][4]) {
   static_for<16>([&](auto mc) {
     constexpr int m = decltype(mc)::value;
-    mfma<OPSEL, m>(fa, fb, sa, sb, acc);
+    mfma<0, m>(fa, fb, sa, sb, acc);
+    fence();
+    if constexpr (m < 8) read_frag<1, m>(lds, s, fo, na, nb);
+    fence();
+  });
+}
+
+// The second K-step of pair kp (scale byte 1).  After MFMA kBarrierAfter: wait
+// for every outstanding copy (pair kp + 1) and this wave's LDS reads, then a
+// barrier: now buffer s ^ 1 holds pair kp + 1 for every wave, and buffer s
+// (whose last fragments were read during the first K-step) is free.  Between
+// the remaining MFMAs: the scales and first-step fragments of pair kp + 1, and
+// the copies of pair kp + 2 into buffer s.  A copy thus has between one and two
+// K-steps to arrive.
+__device__ __forceinline__ void step_odd(uint32_t lds, const Dma& d, int w, int s, int kp, int np,
+                                         const FragOff& fo, int wm, int wn, int r, int h,
+                                         const v8i (&fa)[4], const v8i (&fb)[4],
+                                         const int (&sa)[4], const int (&sb)[4], v8i (&na)[4],
+                                         v8i (&nb)[4], int (&nsa)[4], int (&nsb)[4],
+                                         v16f (&acc)[4][4]) {
+  static_assert(kBarrierAfter >= 0 && kBarrierAfter < 16, "K-step schedule");
+  const bool live = kp + 2 < np;
+  static_for<16>([&](auto mc) {
+    constexpr int m = decltype(mc)::value;
+    mfma<1, m>(fa, fb, sa, sb, acc);
     fence();
     if constexpr (m == kBarrierAfter) {
-      wait_and_barrier<(kAhead - 2) * kDmaPerStep>();
-      read_scales(lds, s_next, wm, wn, r, h, nsa, nsb);
+      wait_and_barrier<0>();
+      read_scales(lds, s ^ 1, wm, wn, r, h, nsa, nsb);
     }
     if constexpr (m >= kBarrierAfter) {
-      // slot q after the barrier; whatever does not fit before the last MFMA
-      // is issued after it
+      // slot q after the barrier; what does not fit before the last MFMA is
+      // issued after it
       constexpr int q = m - kBarrierAfter;
-      constexpr int qend = m == 15 ? 16 : q + 1;
-      static_for<qend - q>([&](auto uc) {
-        constexpr int u = q + decltype(uc)::value;
-        if constexpr (u < 8) read_frag<u>(lds, s_next, fo, na, nb);
-        if constexpr (u < kDmaPerStep) dma_piece<u>(d, lds, w, s_dma, kt + kAhead, live);
+      constexpr int per = (kDmaPerPair + 15 - kBarrierAfter) / (16 - kBarrierAfter);
+      constexpr int qend = m == 15 ? kDmaPerPair : (q + 1) * per;
+      static_for<(qend > q * per ? qend - q * per : 0)>([&](auto uc) {
+        constexpr int u = q * per + decltype(uc)::value;
+        if constexpr (u < kDmaPerPair) dma_piece<u>(d, lds, w, s, kp + 2, live);
       });
+      if constexpr (q < 8) read_frag<0, q>(lds, s ^ 1, fo, na, nb);
+      if constexpr (m == 15 && 16 - kBarrierAfter < 8) {
+        static_for<8 - (16 - kBarrierAfter)>([&](auto kc) {
+          read_frag<0, 16 - kBarrierAfter + decltype(kc)::value>(lds, s ^ 1, fo, na, nb);
+        });
+      }
     }
     fence();
   });
@@ -439,27 +474,32 @@ __device__ void run_tile(uint32_t lds, const TileDesc& t, int out_f32) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
 
-  const int nk = (int)(t.kl / BK);  // even: kl is a multiple of 128
-  if (nk > 0) {
+  const int np = (int)(t.kl / kPairK);  // pairs of K-steps (kl is a multiple of 128)
+  if (np > 0) {
     const Dma d = make_dma(t, w, lane);
     const FragOff fo = make_frag_off(wm, wn, r, h);
-    // prologue: K-steps 0 .. 3 into stages 0 .. 3; wait for step 0
-    static_for<kAhead>([&](auto sc) {
+    // prologue: pairs 0 and 1 into buffers 0 and 1; wait for pair 0
+    static_for<2>([&](auto sc) {
       constexpr int s = decltype(sc)::value;
-      const bool live = s < nk;
-      static_for<kDmaPerStep>([&](auto pc) {
+      const bool live = s < np;
+      static_for<kDmaPerPair>([&](auto pc) {
         dma_piece<decltype(pc)::value>(d, lds, w, s, s, live);
       });
     });
-    wait_and_barrier<(kAhead - 1) * kDmaPerStep>();
+    wait_and_barrier<kDmaPerPair>();
     v8i f0a[4], f0b[4], f1a[4], f1b[4];
-    int s0a[4], s0b[4], s1a[4], s1b[4];
-    read_scales(lds, 0, wm, wn, r, h, s0a, s0b);
-    static_for<8>([&](auto kc) { read_frag<decltype(kc)::value>(lds, 0, fo, f0a, f0b); });
-    for (int kt = 0; kt < nk; kt += 2) {
-      k_step<0>(lds, d, fo, w, wm, wn, r, h, kt, nk, f0a, f0b, s0a, s0b, f1a, f1b, s1a, s1b, acc);
-      k_step<1>(lds, d, fo, w, wm, wn, r, h, kt + 1, nk, f1a, f1b, s1a, s1b, f0a, f0b, s0a, s0b,
-                acc);
+    int sca[4], scb[4], nsa[4], nsb[4];
+    read_scales(lds, 0, wm, wn, r, h, sca, scb);
+    static_for<8>([&](auto kc) { read_frag<0, decltype(kc)::value>(lds, 0, fo, f0a, f0b); });
+    for (int kp = 0; kp < np; ++kp) {
+      const int s = kp & 1;
+      step_even(lds, s, fo, f0a, f0b, sca, scb, f1a, f1b, acc);
+      step_odd(lds, d, w, s, kp, np, fo, wm, wn, r, h, f1a, f1b, sca, scb, f0a, f0b, nsa, nsb, acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sca[i] = nsa[i];
+        scb[i] = nsb[i];
+      }
     }
   }
   // every copy has landed and no wave still reads a stage before the next
@@ -510,7 +550,7 @@ __device__ __forceinline__ void super_tile(int u, int mtiles, int ntiles, int& m
 
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(MxArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_ring[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_ring[kBufs * kBufBytes];
   __shared__ Sched sm;
   const uint32_t lds = lds_offset(lds_ring);
   const int G = p.G;
