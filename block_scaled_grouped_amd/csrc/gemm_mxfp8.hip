@@ -70,7 +70,9 @@ constexpr int kBufs = 2;
 constexpr int kTileA = BM * kPairK;    // 32 KiB
 constexpr int kTileB = BN * kPairK;
 constexpr int kBufBytes = kTileA + kTileB + 4 * BM + 4 * BN;
-constexpr int kDmaPerPair = 18;        // per wave: 8 A, 8 B, 1 A-scale, 1 B-scale
+constexpr int kDmaPerPair = 18;        // per wave and pair: 8 A, 8 B, 1 A-scale, 1 B-scale
+constexpr int kLdsDmaPerPair = 10;     // of which copied global -> LDS directly: A, scales
+constexpr int kRegPerPair = 8;         // and global -> registers -> LDS: B
 constexpr int kBarrierAfter = 0;       // MFMA index of a pair's second step after which it
                                        // waits + barriers
 constexpr int kSuperM = 4, kSuperN = 8;  // tile block one XCD works on
@@ -205,6 +207,11 @@ struct Dma {
   int s;                 // lane scale-word offset (row 64 w + l, K-group 0)
   int lda16, ldb16;      // 16 rows of stride (uniform)
   int sqa, sqb;          // scale K-group strides (uniform)
+  __amdgpu_buffer_rsrc_t rbv, rbv_none;  // B descriptors for the register path
+  int bl;                // lane offset of a register-path B load (q = 0, pair 0)
+  int bw[2];             // lane LDS offset of its store in the B tile, q = 0 rows, with
+                         // the slot swizzle of an even / odd q
+  int ldb8;              // 8 rows of B stride (uniform)
 };
 
 __device__ __forceinline__ Dma make_dma(const TileDesc& t, int w, int lane) {
@@ -222,6 +229,13 @@ __device__ __forceinline__ Dma make_dma(const TileDesc& t, int w, int lane) {
     d.b[e] = row * (int)t.ldb + c * 16;
   }
   d.s = 4 * (64 * w + lane);
+  d.rbv = make_rsrc(t.b, (int64_t)t.b_rows * t.ldb);
+  d.rbv_none = make_rsrc(t.b, 0);
+  d.bl = (64 * w + (lane >> 3)) * (int)t.ldb + (lane & 7) * 16;
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+    d.bw[e] = (64 * w + (lane >> 3)) * kPairK + (((lane & 7) ^ (4 * e + (lane >> 4))) << 4);
+  d.ldb8 = __builtin_amdgcn_readfirstlane(8 * (int)t.ldb);
   d.lda16 = __builtin_amdgcn_readfirstlane(16 * (int)t.lda);
   d.ldb16 = __builtin_amdgcn_readfirstlane(16 * (int)t.ldb);
   d.sqa = __builtin_amdgcn_readfirstlane((int)t.sqa);
@@ -248,6 +262,22 @@ __device__ __forceinline__ void dma_piece(const Dma& d, uint32_t lds, int w, int
   } else {
     dma4(live ? d.rsb : d.rnone, st_sb(lds, s) + 4 * 64 * w, d.s + kp * d.sqb);
   }
+}
+
+// Register path for the B tile (the LDS-DMA path alone cannot feed a CU at the
+// rate the MFMAs consume: it sustains about one 1 KiB copy per 32 cycles).
+// Load q of pair kp: lane l reads row 64 w + 8 q + l / 8, logical chunk l % 8,
+// into registers; store_b writes it one K-step later to its swizzled slot.
+template <int Q>
+__device__ __forceinline__ void load_b(const Dma& d, int kp, bool live, v4i (&stage)[kRegPerPair]) {
+  stage[Q] = __builtin_amdgcn_raw_buffer_load_b128(live ? d.rbv : d.rbv_none,
+                                                   d.bl + Q * d.ldb8 + kp * kPairK, 0, 0);
+}
+
+template <int Q>
+__device__ __forceinline__ void store_b(const Dma& d, uint32_t lds, int s,
+                                        const v4i (&stage)[kRegPerPair]) {
+  *reinterpret_cast<lds_v4i*>((size_t)(st_b(lds, s) + d.bw[Q & 1] + Q * 8 * kPairK)) = stage[Q];
 }
 
 // Per-lane LDS offsets of the fragment reads.  Lane (r, h) of wave (wm, wn)
@@ -325,16 +355,19 @@ __device__ __forceinline__ void mfma(const v8i (&fa)[4], const v8i (&fb)[4], con
 
 // The first K-step of pair kp (buffer s = kp % 2, scale byte 0 of the lane's
 // half dword): its 16 MFMAs, and between them the fragments of the pair's
-// second K-step (same buffer, which has landed).
-__device__ __forceinline__ void step_even(uint32_t lds, int s, const FragOff& fo,
+// second K-step (same buffer, which has landed) and the register-path B rows
+// of pair kp + 1 (loaded during the previous K-step) into buffer s ^ 1.
+__device__ __forceinline__ void step_even(uint32_t lds, const Dma& d, int s, const FragOff& fo,
                                           const v8i (&fa)[4], const v8i (&fb)[4],
                                           const int (&sa)[4], const int (&sb)[4], v8i (&na)[4],
-                                          v8i (&nb)[4], v16f (&acc)[4][4]) {
+                                          v8i (&nb)[4], const v4i (&stage)[kRegPerPair],
+                                          v16f (&acc)[4][4]) {
   static_for<16>([&](auto mc) {
     constexpr int m = decltype(mc)::value;
     mfma<0, m>(fa, fb, sa, sb, acc);
     fence();
     if constexpr (m < 8) read_frag<1, m>(lds, s, fo, na, nb);
+    if constexpr (m >= 8) store_b<m - 8>(d, lds, s ^ 1, stage);
     fence();
   });
 }
@@ -344,14 +377,15 @@ __device__ __forceinline__ void step_even(uint32_t lds, int s, const FragOff& fo
 // barrier: now buffer s ^ 1 holds pair kp + 1 for every wave, and buffer s
 // (whose last fragments were read during the first K-step) is free.  Between
 // the remaining MFMAs: the scales and first-step fragments of pair kp + 1, and
-// the copies of pair kp + 2 into buffer s.  A copy thus has between one and two
-// K-steps to arrive.
+// the copies of pair kp + 2 into buffer s (A rows and scales; the B rows go to
+// registers and reach buffer s during the next K-step).  A copy thus has
+// between one and two K-steps to arrive.
 __device__ __forceinline__ void step_odd(uint32_t lds, const Dma& d, int w, int s, int kp, int np,
                                          const FragOff& fo, int wm, int wn, int r, int h,
                                          const v8i (&fa)[4], const v8i (&fb)[4],
                                          const int (&sa)[4], const int (&sb)[4], v8i (&na)[4],
                                          v8i (&nb)[4], int (&nsa)[4], int (&nsb)[4],
-                                         v16f (&acc)[4][4]) {
+                                         v4i (&stage)[kRegPerPair], v16f (&acc)[4][4]) {
   static_assert(kBarrierAfter >= 0 && kBarrierAfter < 16, "K-step schedule");
   const bool live = kp + 2 < np;
   static_for<16>([&](auto mc) {
@@ -369,8 +403,13 @@ __device__ __forceinline__ void step_odd(uint32_t lds, const Dma& d, int w, int 
       constexpr int per = (kDmaPerPair + 15 - kBarrierAfter) / (16 - kBarrierAfter);
       constexpr int qend = m == 15 ? kDmaPerPair : (q + 1) * per;
       static_for<(qend > q * per ? qend - q * per : 0)>([&](auto uc) {
+        // LDS-DMA pieces (A rows, then the scales) first, register loads after
+        // them: the compiler counts only its own loads when it waits for the
+        // staged registers, which is exact when every LDS-DMA copy is older
         constexpr int u = q * per + decltype(uc)::value;
-        if constexpr (u < kDmaPerPair) dma_piece<u>(d, lds, w, s, kp + 2, live);
+        if constexpr (u < 8) dma_piece<u>(d, lds, w, s, kp + 2, live);
+        else if constexpr (u < kLdsDmaPerPair) dma_piece<u + 8>(d, lds, w, s, kp + 2, live);
+        else if constexpr (u < kDmaPerPair) load_b<u - kLdsDmaPerPair>(d, kp + 2, live, stage);
       });
       if constexpr (q < 8) read_frag<0, q>(lds, s ^ 1, fo, na, nb);
       if constexpr (m == 15 && 16 - kBarrierAfter < 8) {
@@ -478,23 +517,26 @@ __device__ void run_tile(uint32_t lds, const TileDesc& t, int out_f32) {
   if (np > 0) {
     const Dma d = make_dma(t, w, lane);
     const FragOff fo = make_frag_off(wm, wn, r, h);
-    // prologue: pairs 0 and 1 into buffers 0 and 1; wait for pair 0
-    static_for<2>([&](auto sc) {
-      constexpr int s = decltype(sc)::value;
-      const bool live = s < np;
-      static_for<kDmaPerPair>([&](auto pc) {
-        dma_piece<decltype(pc)::value>(d, lds, w, s, s, live);
-      });
-    });
-    wait_and_barrier<kDmaPerPair>();
+    // prologue: pair 0 into buffer 0; pair 1's A rows and scales into buffer 1
+    // and its B rows into registers (stored during pair 0's first K-step);
+    // wait for pair 0
+    v4i stage[kRegPerPair];
+    static_for<kDmaPerPair>([&](auto pc) { dma_piece<decltype(pc)::value>(d, lds, w, 0, 0, true); });
+    const bool live1 = np > 1;
+    static_for<8>([&](auto pc) { dma_piece<decltype(pc)::value>(d, lds, w, 1, 1, live1); });
+    dma_piece<16>(d, lds, w, 1, 1, live1);
+    dma_piece<17>(d, lds, w, 1, 1, live1);
+    static_for<kRegPerPair>([&](auto qc) { load_b<decltype(qc)::value>(d, 1, live1, stage); });
+    wait_and_barrier<kLdsDmaPerPair + kRegPerPair>();
     v8i f0a[4], f0b[4], f1a[4], f1b[4];
     int sca[4], scb[4], nsa[4], nsb[4];
     read_scales(lds, 0, wm, wn, r, h, sca, scb);
     static_for<8>([&](auto kc) { read_frag<0, decltype(kc)::value>(lds, 0, fo, f0a, f0b); });
     for (int kp = 0; kp < np; ++kp) {
       const int s = kp & 1;
-      step_even(lds, s, fo, f0a, f0b, sca, scb, f1a, f1b, acc);
-      step_odd(lds, d, w, s, kp, np, fo, wm, wn, r, h, f1a, f1b, sca, scb, f0a, f0b, nsa, nsb, acc);
+      step_even(lds, d, s, fo, f0a, f0b, sca, scb, f1a, f1b, stage, acc);
+      step_odd(lds, d, w, s, kp, np, fo, wm, wn, r, h, f1a, f1b, sca, scb, f0a, f0b, nsa, nsb, stage,
+               acc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         sca[i] = nsa[i];
