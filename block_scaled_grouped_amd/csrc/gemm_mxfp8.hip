@@ -73,7 +73,7 @@ constexpr int kBufBytes = kTileA + kTileB + 4 * BM + 4 * BN;
 constexpr int kDmaPerPair = 18;        // per wave and pair: 8 A, 8 B, 1 A-scale, 1 B-scale
 constexpr int kLdsDmaPerPair = 10;     // of which copied global -> LDS directly: A, scales
 constexpr int kRegPerPair = 8;         // and global -> registers -> LDS: B
-constexpr int kBarrierAfter = 0;       // MFMA index of a pair's second step after which it
+constexpr int kBarrierAfter = 2;       // MFMA index of a pair's second step after which it
                                        // waits + barriers
 constexpr int kSuperM = 4, kSuperN = 8;  // tile block one XCD works on
 constexpr int kXcds = 8;
@@ -355,68 +355,58 @@ __device__ __forceinline__ void mfma(const v8i (&fa)[4], const v8i (&fb)[4], con
 
 // The first K-step of pair kp (buffer s = kp % 2, scale byte 0 of the lane's
 // half dword): its 16 MFMAs, and between them the fragments of the pair's
-// second K-step (same buffer, which has landed) and the register-path B rows
-// of pair kp + 1 (loaded during the previous K-step) into buffer s ^ 1.
-__device__ __forceinline__ void step_even(uint32_t lds, const Dma& d, int s, const FragOff& fo,
-                                          const v8i (&fa)[4], const v8i (&fb)[4],
-                                          const int (&sa)[4], const int (&sb)[4], v8i (&na)[4],
-                                          v8i (&nb)[4], const v4i (&stage)[kRegPerPair],
-                                          v16f (&acc)[4][4]) {
+// second K-step (same buffer, which has landed); then, one register at a time,
+// the staged B rows of pair kp + 1 into buffer s ^ 1 (free since the last
+// barrier) and the loads of pair kp + 2's B rows into the freed register.
+__device__ __forceinline__ void step_even(uint32_t lds, const Dma& d, int s, int kp, int np,
+                                          const FragOff& fo, const v8i (&fa)[4],
+                                          const v8i (&fb)[4], const int (&sa)[4],
+                                          const int (&sb)[4], v8i (&na)[4], v8i (&nb)[4],
+                                          v4i (&stage)[kRegPerPair], v16f (&acc)[4][4]) {
+  const bool live = kp + 2 < np;
   static_for<16>([&](auto mc) {
     constexpr int m = decltype(mc)::value;
     mfma<0, m>(fa, fb, sa, sb, acc);
     fence();
     if constexpr (m < 8) read_frag<1, m>(lds, s, fo, na, nb);
-    if constexpr (m >= 8) store_b<m - 8>(d, lds, s ^ 1, stage);
+    if constexpr (m >= 8) {
+      store_b<m - 8>(d, lds, s ^ 1, stage);
+      load_b<m - 8>(d, kp + 2, live, stage);
+    }
     fence();
   });
 }
 
 // The second K-step of pair kp (scale byte 1).  After MFMA kBarrierAfter: wait
-// for every outstanding copy (pair kp + 1) and this wave's LDS reads, then a
-// barrier: now buffer s ^ 1 holds pair kp + 1 for every wave, and buffer s
-// (whose last fragments were read during the first K-step) is free.  Between
-// the remaining MFMAs: the scales and first-step fragments of pair kp + 1, and
-// the copies of pair kp + 2 into buffer s (A rows and scales; the B rows go to
-// registers and reach buffer s during the next K-step).  A copy thus has
-// between one and two K-steps to arrive.
+// until only the B loads of pair kp + 2 (the newest copies) are outstanding,
+// so pair kp + 1's LDS copies have landed, and for this wave's LDS accesses
+// (pair kp + 1's B rows stored); then a barrier: now buffer s ^ 1 holds pair
+// kp + 1 for every wave, and buffer s (whose last fragments were read during
+// the first K-step) is free.  Between the remaining MFMAs, one per slot: the
+// LDS copies of pair kp + 2's A rows and scales into buffer s, and the scales
+// and first-step fragments of pair kp + 1.
 __device__ __forceinline__ void step_odd(uint32_t lds, const Dma& d, int w, int s, int kp, int np,
                                          const FragOff& fo, int wm, int wn, int r, int h,
                                          const v8i (&fa)[4], const v8i (&fb)[4],
                                          const int (&sa)[4], const int (&sb)[4], v8i (&na)[4],
                                          v8i (&nb)[4], int (&nsa)[4], int (&nsb)[4],
-                                         v4i (&stage)[kRegPerPair], v16f (&acc)[4][4]) {
-  static_assert(kBarrierAfter >= 0 && kBarrierAfter < 16, "K-step schedule");
+                                         v16f (&acc)[4][4]) {
+  static_assert(kBarrierAfter >= 0 && kBarrierAfter + kLdsDmaPerPair <= 16 &&
+                    kBarrierAfter + 8 <= 16, "K-step schedule");
   const bool live = kp + 2 < np;
   static_for<16>([&](auto mc) {
     constexpr int m = decltype(mc)::value;
     mfma<1, m>(fa, fb, sa, sb, acc);
     fence();
     if constexpr (m == kBarrierAfter) {
-      wait_and_barrier<0>();
+      wait_and_barrier<kRegPerPair>();
       read_scales(lds, s ^ 1, wm, wn, r, h, nsa, nsb);
     }
     if constexpr (m >= kBarrierAfter) {
-      // slot q after the barrier; what does not fit before the last MFMA is
-      // issued after it
       constexpr int q = m - kBarrierAfter;
-      constexpr int per = (kDmaPerPair + 15 - kBarrierAfter) / (16 - kBarrierAfter);
-      constexpr int qend = m == 15 ? kDmaPerPair : (q + 1) * per;
-      static_for<(qend > q * per ? qend - q * per : 0)>([&](auto uc) {
-        // LDS-DMA pieces (A rows, then the scales) first, register loads after
-        // them: the compiler counts only its own loads when it waits for the
-        // staged registers, which is exact when every LDS-DMA copy is older
-        constexpr int u = q * per + decltype(uc)::value;
-        if constexpr (u < 8) dma_piece<u>(d, lds, w, s, kp + 2, live);
-        else if constexpr (u < kLdsDmaPerPair) dma_piece<u + 8>(d, lds, w, s, kp + 2, live);
-        else if constexpr (u < kDmaPerPair) load_b<u - kLdsDmaPerPair>(d, kp + 2, live, stage);
-      });
+      if constexpr (q < 8) dma_piece<q>(d, lds, w, s, kp + 2, live);
+      else if constexpr (q < kLdsDmaPerPair) dma_piece<q + 8>(d, lds, w, s, kp + 2, live);
       if constexpr (q < 8) read_frag<0, q>(lds, s ^ 1, fo, na, nb);
-      if constexpr (m == 15 && 16 - kBarrierAfter < 8) {
-        static_for<8 - (16 - kBarrierAfter)>([&](auto kc) {
-          read_frag<0, 16 - kBarrierAfter + decltype(kc)::value>(lds, s ^ 1, fo, na, nb);
-        });
-      }
     }
     fence();
   });
@@ -534,9 +524,8 @@ __device__ void run_tile(uint32_t lds, const TileDesc& t, int out_f32) {
     static_for<8>([&](auto kc) { read_frag<0, decltype(kc)::value>(lds, 0, fo, f0a, f0b); });
     for (int kp = 0; kp < np; ++kp) {
       const int s = kp & 1;
-      step_even(lds, d, s, fo, f0a, f0b, sca, scb, f1a, f1b, stage, acc);
-      step_odd(lds, d, w, s, kp, np, fo, wm, wn, r, h, f1a, f1b, sca, scb, f0a, f0b, nsa, nsb, stage,
-               acc);
+      step_even(lds, d, s, kp, np, fo, f0a, f0b, sca, scb, f1a, f1b, stage, acc);
+      step_odd(lds, d, w, s, kp, np, fo, wm, wn, r, h, f1a, f1b, sca, scb, f0a, f0b, nsa, nsb, acc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         sca[i] = nsa[i];
