@@ -10,18 +10,16 @@
 // Per 32-element block: amax = largest |x| (integer max of the bf16 magnitude
 // bits), scale byte = max(exponent(amax) - 8, 0) (the E4M3 maximum 448 sits in
 // binade 8), element = E4M3(x * 2^(127 - byte)), ties to even, saturated at
-// 448.  The multiply by a power of two is exact in fp32; the values are
-// clamped to +-448 before the hardware convert, which rounds to nearest even
-// but would give NaN from 464 up.
+// 448.  gfx950's v_cvt_scalef32_pk_fp8_bf16 converts two bf16 directly, divided
+// by the power of two whose exponent field is the scale byte, rounding to
+// nearest even -- exactly this -- except that magnitudes above 464 come out as
+// the NaN code S.1111.111 instead of saturating; finite input never yields NaN
+// otherwise, so those bytes are mapped to S.1111.110 (448) afterwards.
 #include "bsg_internal.h"
 
 namespace bsg {
 
 namespace {
-
-__device__ __forceinline__ float clamp448(float v) {
-  return __builtin_fminf(__builtin_fmaxf(v, -448.0f), 448.0f);
-}
 
 // E8M0 byte from the largest bf16 magnitude bits of a block.
 __device__ __forceinline__ uint32_t e8m0_from_amax_bits(uint32_t amax_bits) {
@@ -29,37 +27,53 @@ __device__ __forceinline__ uint32_t e8m0_from_amax_bits(uint32_t amax_bits) {
   return e > 8u ? e - 8u : 0u;
 }
 
-// 2^(127 - byte) as float; byte <= 247 for finite input, so always normal.
-__device__ __forceinline__ float inv_scale(uint32_t byte) {
-  return __uint_as_float((254u - byte) << 23);
+// The scale operand of the scaled converts: a float whose exponent field is the
+// E8M0 byte (the instruction reads only the exponent field).
+__device__ __forceinline__ float e8m0_scale(uint32_t byte) { return __uint_as_float(byte << 23); }
+
+typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+
+// Lane moves inside 16-lane rows (DPP): the value of lane l ^ 1, and of lane
+// l + N (only read where l + N stays inside the row).
+__device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+}
+template <int N>
+__device__ __forceinline__ uint32_t dpp_down(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x100 + N, 0xF, 0xF, false);  // row_shl N
 }
 
-__device__ __forceinline__ uint32_t amax_bits_of(uint32_t w) {
-  return max(w & 0x7fffu, (w >> 16) & 0x7fffu);
+// Largest of the two bf16 magnitudes in each 16-bit half of a and b.
+__device__ __forceinline__ uint32_t amax2(uint32_t a, uint32_t b) {
+  const v2u16 x = __builtin_bit_cast(v2u16, a & 0x7fff7fffu);
+  const v2u16 y = __builtin_bit_cast(v2u16, b & 0x7fff7fffu);
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(x, y));
 }
 
-// Two packed bf16 (low element first) times f -> two E4M3 bytes in the low
+// Combines the two halves of an amax2 result.
+__device__ __forceinline__ uint32_t amax_fold(uint32_t m) { return max(m & 0xffffu, m >> 16); }
+
+// Overflowed E4M3 codes (S.1111.111, only produced for magnitudes above 464)
+// become the largest finite code S.1111.110, in each byte of a word.
+__device__ __forceinline__ uint32_t e4m3_saturate(uint32_t x) {
+  const uint32_t m = ((x & 0x7f7f7f7fu) + 0x01010101u) & 0x80808080u;
+  return x - (m >> 7);
+}
+
+// Two packed bf16 (low element first), scaled -> two E4M3 bytes in the low
 // (HI = false) or high half of `old`.
 template <bool HI>
-__device__ __forceinline__ int cvt2(uint32_t w, float f, int old) {
-  float a = clamp448(bf16_to_f32(w & 0xffffu) * f);
-  float b = clamp448(__uint_as_float(w & 0xffff0000u) * f);
-  return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+__device__ __forceinline__ uint32_t cvt2(uint32_t w, float scale, uint32_t old) {
+  const v2s r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(
+      __builtin_bit_cast(v2s, old), __builtin_bit_cast(v2bf, w), scale, HI);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 // 8 bf16 (4 dwords) -> 8 E4M3 bytes (2 dwords).
-__device__ __forceinline__ uint2 cvt8(uint4 v, float f) {
-  int lo = cvt2<false>(v.x, f, 0);
-  lo = cvt2<true>(v.y, f, lo);
-  int hi = cvt2<false>(v.z, f, 0);
-  hi = cvt2<true>(v.w, f, hi);
-  return make_uint2((uint32_t)lo, (uint32_t)hi);
-}
-
-// Position of logical scale byte j of a row in the GEMM-ready order: within
-// every 4 bytes the stored order is b0, b2, b1, b3.
-__device__ __forceinline__ int64_t scale_pos(int64_t j) {
-  return (j & ~int64_t(3)) + ((j & 1) << 1) + ((j >> 1) & 1);
+__device__ __forceinline__ uint2 cvt8(uint4 v, float scale) {
+  const uint32_t lo = cvt2<true>(v.y, scale, cvt2<false>(v.x, scale, 0u));
+  const uint32_t hi = cvt2<true>(v.w, scale, cvt2<false>(v.z, scale, 0u));
+  return make_uint2(e4m3_saturate(lo), e4m3_saturate(hi));
 }
 
 }  // namespace
@@ -102,8 +116,7 @@ __global__ __launch_bounds__(256) void mx_rowwise_kernel(const uint16_t* __restr
 
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    uint32_t am = max(max(amax_bits_of(v[h].x), amax_bits_of(v[h].y)),
-                      max(amax_bits_of(v[h].z), amax_bits_of(v[h].w)));
+    uint32_t am = amax_fold(amax2(amax2(v[h].x, v[h].y), amax2(v[h].z, v[h].w)));
     am = max(am, (uint32_t)__shfl_xor((int)am, 1, 64));
     am = max(am, (uint32_t)__shfl_xor((int)am, 2, 64));
     const uint32_t byte = e8m0_from_amax_bits(am);
@@ -112,7 +125,7 @@ __global__ __launch_bounds__(256) void mx_rowwise_kernel(const uint16_t* __restr
     const uint32_t b2 = (uint32_t)__shfl_down((int)byte, 8, 16);
     const uint32_t b3 = (uint32_t)__shfl_down((int)byte, 12, 16);
     if (e[h] < cols) {
-      uint2 q = cvt8(v[h], inv_scale(byte));
+      uint2 q = cvt8(v[h], e8m0_scale(byte));
       *reinterpret_cast<uint2*>(data + row * cols + e[h]) = q;
       if ((lane & 15) == 0) {
         const uint32_t dw = byte | (b2 << 8) | (b1 << 16) | (b3 << 24);
@@ -137,16 +150,166 @@ hipError_t launch_quantize_mxfp8_rowwise(const uint16_t* x, int64_t rows_cap, in
 
 // ---------------------------------------------------------------- columnwise
 //
-// One 256-thread block per (128-token tile of a group, 64-column slab).  The
-// bf16 tile is staged in LDS (128 rows x 128 B).  Columnwise: wave w takes the
-// 32-token block w and lane l the column l, so LDS reads are conflict-free row
-// reads; each lane writes its column's 32 E4M3 bytes (two 16-byte stores) and
-// one scale byte.  Rowwise (when requested): thread t takes row t/2 and the
-// 32-column block t%2 of the same LDS tile, so the input is read from HBM once
-// for both outputs.  Tokens past the group's size are zeros (pad bytes 0x00,
-// all-padding blocks get scale 0x00).
+// Three blocks of 4 waves per CU loop over tiles of (128 tokens of a group) x
+// (128 columns).  A block stages a tile's bf16 values in LDS from registers
+// loaded one tile ahead (rows past the group's live tokens and columns past the
+// end are zeros), so the next tile's loads are in flight while the current one
+// is converted: columnwise, then rowwise (when requested), so the input is read
+// from HBM once for both outputs.  Each 32-element block's E4M3 bytes and scale
+// are produced as described at the top of this file.
+// Tokens past the group's size are zeros (pad bytes 0x00, all-padding blocks
+// get scale 0x00).  In LDS, 16-byte chunk c of tile row r sits in slot
+// c ^ ((r % 8) ^ ((r / 16) % 8)), which keeps the row-major stores and both
+// read patterns (nearly) free of bank conflicts.
 constexpr int kColTokens = 128;
-constexpr int kColCols = 64;
+constexpr int kColCols = 128;
+constexpr int kColTileBytes = kColTokens * kColCols * 2;   // 32 KiB
+constexpr int kColBlocksPerCu = 3;
+
+__device__ __forceinline__ uint32_t col_tile_slot(int r, int c16) {
+  return (uint32_t)(r * 256 + ((c16 ^ ((r & 7) ^ ((r >> 4) & 7))) << 4));
+}
+
+typedef __attribute__((address_space(3))) v4i lds_v4i;
+
+__device__ __forceinline__ uint4 lds_ld16(uint32_t a) {
+  const v4i v = *reinterpret_cast<const lds_v4i*>((size_t)a);
+  return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+}
+__device__ __forceinline__ uint32_t lds_ld4(uint32_t a) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>((size_t)a);
+}
+
+// 16 E4M3 bytes from 16 values given as bf16 bits (element i in halves of w[i/2]).
+__device__ __forceinline__ uint4 cvt16(const uint32_t (&w)[8], float f) {
+  const uint2 a = cvt8(make_uint4(w[0], w[1], w[2], w[3]), f);
+  const uint2 b = cvt8(make_uint4(w[4], w[5], w[6], w[7]), f);
+  return make_uint4(a.x, a.y, b.x, b.y);
+}
+
+// Where tile `id` sits: its group, token offset, live tokens, first row.
+struct ColTile {
+  int64_t t0, c0, tt, row0, mp;
+  int g, nv;
+  bool ok;
+};
+
+__device__ __forceinline__ ColTile col_tile_info(int64_t id, int64_t nslab, int G,
+                                                 const int64_t* s_off, const int64_t* s_poff) {
+  ColTile t;
+  t.t0 = (id / nslab) * kColTokens;
+  t.c0 = (id % nslab) * kColCols;
+  int lo = 0, hi = G - 1;  // group: largest g with s_poff[g] <= t0
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (s_poff[mid] <= t.t0) lo = mid; else hi = mid - 1;
+  }
+  t.g = lo;
+  const int64_t m = group_extent(s_off, t.g);
+  t.mp = group_extent(s_poff, t.g);
+  t.tt = t.t0 - s_poff[t.g];
+  t.ok = s_poff[t.g] % kColPad == 0 && t.mp % kColPad == 0 && t.mp >= m && t.tt < t.mp;
+  const int64_t nv = m - t.tt;  // live tokens in this tile
+  t.nv = (int)(nv < 0 ? 0 : (nv > kColTokens ? kColTokens : nv));
+  t.row0 = s_off[t.g] + t.tt;
+  return t;
+}
+
+// Columnwise part of a staged tile, NW waves: per pass, lane (k, q) of wave w
+// takes a column pair 2 pc, 2 pc + 1 (pc = 8 w + q + the pass's base) and
+// tokens [16 k, 16 k + 16) (4-byte LDS reads), so a column's 32-token block is split over lanes k, k ^ 1 and its 128
+// output bytes are written by 8 neighbouring lanes, 16 bytes each; the column's
+// four block scales become one word of the GEMM order.
+template <int NW>
+__device__ __forceinline__ void col_convert_columns(uint32_t lds, const ColTile& t, int64_t cols,
+                                                    int64_t poff, int w, int lane,
+                                                    uint8_t* __restrict__ col_data,
+                                                    uint8_t* __restrict__ col_scales) {
+  const int k = lane & 7;               // tokens [16 k, 16 k + 16)
+#pragma unroll
+  for (int pass = 0; pass < 8 / NW; ++pass) {
+  const int pc = 64 / (8 / NW) * pass + 8 * w + (lane >> 3);   // columns 2 pc, 2 pc + 1
+  uint32_t cw[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    cw[i] = lds_ld4(lds + col_tile_slot(16 * k + i, pc >> 2) + 4 * (pc & 3));
+  const int64_t scale_base = poff * cols / 32 + 4 * ((t.tt / 128) * cols);
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    uint32_t pk[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)  // tokens 2 i, 2 i + 1 of the column, as one bf16 pair
+      pk[i] = __builtin_amdgcn_perm(cw[2 * i + 1], cw[2 * i], e ? 0x07060302u : 0x05040100u);
+    uint32_t am = amax_fold(amax2(amax2(amax2(pk[0], pk[1]), amax2(pk[2], pk[3])),
+                                  amax2(amax2(pk[4], pk[5]), amax2(pk[6], pk[7]))));
+    am = max(am, dpp_xor1(am));   // the block's other 16 tokens
+    const uint32_t byte = e8m0_from_amax_bits(am);
+    const uint4 q = cvt16(pk, e8m0_scale(byte));
+    // block bytes of tokens [0, 32), [32, 64), ... sit in lanes k = 0, 2, 4, 6
+    const uint32_t b1 = dpp_down<2>(byte), b2 = dpp_down<4>(byte), b3 = dpp_down<6>(byte);
+    const int64_t c = t.c0 + 2 * pc + e;
+    if (c < cols) {
+      *reinterpret_cast<uint4*>(col_data + poff * cols + c * t.mp + t.tt + 16 * k) = q;
+      if (k == 0)
+        *reinterpret_cast<uint32_t*>(col_scales + scale_base + 4 * c) =
+            byte | (b2 << 8) | (b1 << 16) | (b3 << 24);
+    }
+  }
+  }
+}
+
+// Rowwise part, NW waves: per pass, 8 lanes per row, 16 columns each; the
+// row's four block scales become one word.
+template <int NW>
+__device__ __forceinline__ void col_convert_rows(uint32_t lds, const ColTile& t, int64_t cols,
+                                                 int64_t rows_cap, int w, int lane,
+                                                 uint8_t* __restrict__ row_data,
+                                                 uint8_t* __restrict__ row_scales) {
+  const int j = lane & 7;
+#pragma unroll
+  for (int pass = 0; pass < 16 / NW; ++pass) {
+    const int r = 8 * NW * pass + 8 * w + (lane >> 3);
+    const uint4 a = lds_ld16(lds + col_tile_slot(r, 2 * j));
+    const uint4 b = lds_ld16(lds + col_tile_slot(r, 2 * j + 1));
+    uint32_t am = amax_fold(amax2(amax2(amax2(a.x, a.y), amax2(a.z, a.w)),
+                                  amax2(amax2(b.x, b.y), amax2(b.z, b.w))));
+    am = max(am, dpp_xor1(am));   // the block's other 16 columns
+    const uint32_t byte = e8m0_from_amax_bits(am);
+    const float f = e8m0_scale(byte);
+    const uint2 qa = cvt8(a, f), qb = cvt8(b, f);
+    const uint32_t b1 = dpp_down<2>(byte), b2 = dpp_down<4>(byte), b3 = dpp_down<6>(byte);
+    if (r < t.nv) {
+      const int64_t row = t.row0 + r;
+      const int64_t col = t.c0 + 16 * j;
+      if (col < cols)
+        *reinterpret_cast<uint4*>(row_data + row * cols + col) = make_uint4(qa.x, qa.y, qb.x, qb.y);
+      // word (c0 / 128, row) of the [NQ][rows_cap] scale array, b0, b2, b1, b3
+      // (blocks past the last column read zeros: byte 0)
+      if (j == 0)
+        *reinterpret_cast<uint32_t*>(row_scales + 4 * ((t.c0 / 128) * rows_cap + row)) =
+            byte | (b2 << 8) | (b1 << 16) | (b3 << 24);
+    }
+  }
+}
+
+
+__device__ __forceinline__ void col_tile_load(const uint16_t* __restrict__ x, int64_t cols,
+                                              const ColTile& t, uint4 (&v)[8]) {
+  const int tid = threadIdx.x;
+  const int c16 = tid & 15;
+  const bool colok = t.ok && t.c0 + 8 * c16 < cols;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int r = (tid >> 4) + 16 * p;
+    v[p] = make_uint4(0, 0, 0, 0);
+    if (r < t.nv && colok)
+      v[p] = *reinterpret_cast<const uint4*>(x + (t.row0 + r) * cols + t.c0 + 8 * c16);
+  }
+}
+
+__device__ __forceinline__ void lds_st16(uint32_t a, uint4 v) {
+  *reinterpret_cast<lds_v4i*>((size_t)a) = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+}
 
 __global__ __launch_bounds__(256) void mx_colwise_kernel(
     const uint16_t* __restrict__ x, int64_t rows_cap, int64_t cols, int G,
@@ -155,113 +318,37 @@ __global__ __launch_bounds__(256) void mx_colwise_kernel(
     uint8_t* __restrict__ row_scales, uint32_t* status) {
   __shared__ int64_t s_off[kMaxGroups + 1];
   __shared__ int64_t s_poff[kMaxGroups + 1];
-  __shared__ uint16_t tile[kColTokens][kColCols];
-
-  const int64_t nslab = (cols + kColCols - 1) / kColCols;
-  const int64_t ttile = blockIdx.x / nslab;
-  const int64_t c0 = (blockIdx.x % nslab) * kColCols;
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kColTileBytes];
   const bool report = blockIdx.x == 0;
   load_offsets_clamped(offsets, G, rows_cap, s_off, report ? status : nullptr);
   load_offsets_clamped(poffsets, G, col_cap, s_poff, report ? status : nullptr);
-
-  const int64_t t0 = ttile * kColTokens;  // padded token index of the tile
-  if (t0 >= s_poff[G]) return;
-  int lo = 0, hi = G - 1;  // group: largest g with s_poff[g] <= t0
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (s_poff[mid] <= t0) lo = mid; else hi = mid - 1;
-  }
-  const int g = lo;
-  const int64_t m = group_extent(s_off, g);
-  const int64_t mp = group_extent(s_poff, g);
-  if (s_poff[g] % kColPad != 0 || mp % kColPad != 0 || mp < m) {
-    if (threadIdx.x == 0 && t0 == s_poff[g] && c0 == 0) dev_status_or(status, kDevBadPadding);
-    return;
-  }
-  const int64_t tt = t0 - s_poff[g];           // token offset of the tile inside the group
-  if (tt >= mp) return;                        // only with invalid (decreasing) padded offsets
-  int64_t nv = m - tt;                         // live tokens in this tile
-  nv = nv < 0 ? 0 : (nv > kColTokens ? kColTokens : nv);
-  const int64_t row0 = s_off[g] + tt;
-
-  // stage the bf16 tile (zeros past the live tokens and past the last column)
+  const uint32_t lds = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)tile;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane((int)(tid >> 6));
+  const int64_t nslab = (cols + kColCols - 1) / kColCols;
+  const int64_t ntiles = ((s_poff[G] + kColTokens - 1) / kColTokens) * nslab;
+  int64_t id = blockIdx.x;
+  if (id >= ntiles) return;
+  ColTile cur = col_tile_info(id, nslab, G, s_off, s_poff);
+  uint4 v[8];
+  col_tile_load(x, cols, cur, v);
+  for (; id < ntiles; id += gridDim.x) {
+    __syncthreads();
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int r = (tid >> 3) + 32 * p;
-    const int ch = tid & 7;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < nv && c0 + ch * 8 < cols)
-      v = *reinterpret_cast<const uint4*>(x + (row0 + r) * cols + c0 + ch * 8);
-    *reinterpret_cast<uint4*>(&tile[r][ch * 8]) = v;
-  }
-  __syncthreads();
-
-  // columnwise
-  {
-    const int w = tid >> 6;     // 32-token block
-    const int c = tid & 63;     // column within the slab
-    if (c0 + c < cols) {
-      uint32_t wv[16];
-      uint32_t am = 0;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        uint32_t lo16 = tile[32 * w + 2 * i][c];
-        uint32_t hi16 = tile[32 * w + 2 * i + 1][c];
-        wv[i] = lo16 | (hi16 << 16);
-        am = max(am, max(lo16 & 0x7fffu, hi16 & 0x7fffu));
-      }
-      const uint32_t byte = e8m0_from_amax_bits(am);
-      const float f = inv_scale(byte);
-      uint32_t q[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint2 r = cvt8(make_uint4(wv[4 * i], wv[4 * i + 1], wv[4 * i + 2], wv[4 * i + 3]), f);
-        q[2 * i] = r.x;
-        q[2 * i + 1] = r.y;
-      }
-      uint8_t* dst = col_data + s_poff[g] * cols + (c0 + c) * mp + tt + 32 * w;
-      reinterpret_cast<uint4*>(dst)[0] = make_uint4(q[0], q[1], q[2], q[3]);
-      reinterpret_cast<uint4*>(dst)[1] = make_uint4(q[4], q[5], q[6], q[7]);
-      // word (tt / 128, column) of the group's [m~/128][cols] scale array; byte w
-      // in the b0, b2, b1, b3 order
-      col_scales[s_poff[g] * cols / 32 + 4 * ((tt / 128) * cols + c0 + c) + scale_pos(w)] =
-          (uint8_t)byte;
+    for (int p = 0; p < 8; ++p) lds_st16(lds + col_tile_slot((tid >> 4) + 16 * p, tid & 15), v[p]);
+    __syncthreads();
+    const ColTile t = cur;
+    if (id + gridDim.x < ntiles) {
+      cur = col_tile_info(id + gridDim.x, nslab, G, s_off, s_poff);
+      col_tile_load(x, cols, cur, v);
     }
-  }
-
-  // rowwise from the same tile
-  if (row_data != nullptr) {
-    const int r = tid >> 1;
-    const int hb = tid & 1;
-    const int64_t col = c0 + 32 * hb;
-    if (r < nv && col < cols) {
-      uint4 v[4];
-      uint32_t am = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[i] = *reinterpret_cast<const uint4*>(&tile[r][32 * hb + 8 * i]);
-        am = max(am, max(max(amax_bits_of(v[i].x), amax_bits_of(v[i].y)),
-                         max(amax_bits_of(v[i].z), amax_bits_of(v[i].w))));
-      }
-      const uint32_t byte = e8m0_from_amax_bits(am);
-      const float f = inv_scale(byte);
-      uint2 q0 = cvt8(v[0], f), q1 = cvt8(v[1], f), q2 = cvt8(v[2], f), q3 = cvt8(v[3], f);
-      const int64_t row = row0 + r;
-      uint8_t* dst = row_data + row * cols + col;
-      reinterpret_cast<uint4*>(dst)[0] = make_uint4(q0.x, q0.y, q1.x, q1.y);
-      reinterpret_cast<uint4*>(dst)[1] = make_uint4(q2.x, q2.y, q3.x, q3.y);
-      // word (q, row) of the [NQ][rows_cap] scale array, byte of block col / 32
-      const int64_t jb = col / 32;
-      row_scales[4 * ((jb / 4) * rows_cap + row) + scale_pos(jb & 3)] = (uint8_t)byte;
-      // a row whose last 128-element stretch is short gets zero pad bytes
-      if (col + 32 >= cols) {
-        const int64_t nblk = cols / 32;
-        const int64_t srow = ((nblk + 3) / 4) * 4;
-        for (int64_t j = nblk; j < srow; ++j)
-          row_scales[4 * ((j / 4) * rows_cap + row) + scale_pos(j & 3)] = 0;
-      }
+    if (!t.ok) {
+      if (tid == 0 && t.t0 == s_poff[t.g] && t.c0 == 0) dev_status_or(status, kDevBadPadding);
+      continue;
     }
+    col_convert_columns<4>(lds, t, cols, s_poff[t.g], w, lane, col_data, col_scales);
+    if (row_data != nullptr) col_convert_rows<4>(lds, t, cols, rows_cap, w, lane, row_data, row_scales);
   }
 }
 
@@ -271,10 +358,11 @@ hipError_t launch_quantize_mxfp8_colwise(const uint16_t* x, int64_t rows_cap, in
                                          uint8_t* col_scales, uint8_t* row_data,
                                          uint8_t* row_scales, uint32_t* status,
                                          hipStream_t stream) {
-  const int64_t ttiles = (col_rows_cap + kColTokens - 1) / kColTokens;
-  const int64_t nslab = (cols + kColCols - 1) / kColCols;
-  const int64_t blocks = ttiles * nslab;
-  if (blocks == 0) return hipSuccess;
+  // upper bound of the tile count from the host-known capacity
+  const int64_t bound = ((col_rows_cap + kColTokens - 1) / kColTokens) * ((cols + kColCols - 1) / kColCols);
+  int64_t blocks = (int64_t)device_cu_count() * kColBlocksPerCu;
+  if (bound < blocks) blocks = bound;
+  if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL(mx_colwise_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, rows_cap,
                      cols, G, offsets, padded_offsets, col_rows_cap, col_data, col_scales, row_data,
                      row_scales, status);
