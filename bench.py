@@ -34,6 +34,10 @@ import block_scaled_grouped_amd as bsg
 import workloads
 
 HBM_PEAK_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+# HBM bytes per fprop GEMM launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs (scaled by a copy of
+# known size), recorded with the hash of the kernel source they were taken with
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gemm_mxfp8_fprop_moe_8exp_16384x4096x14336_traffic.json")
 MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "fp4": 10100.0, "bf16": 2500.0}
 METRIC = "MXFP8 grouped GEMM TFLOP/s + grouped quantize GB/s (1 MI355X, % roofline)"
 
@@ -270,6 +274,20 @@ def summarize(case, t, mfma_dtype):
 
 # ---------------------------------------------------------------- CPU baseline (the oracle)
 
+def gemm_traffic():
+    """Counter-measured HBM bytes of one fprop GEMM launch, or None when no
+    record exists or the kernel source has changed since it was taken."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_RECORD))
+        src = open(os.path.join(ROOT, rec["kernel_source"]), "rb").read()
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec.get("kernel_source_sha256"):
+        return None
+    return int(rec["traffic_bytes"])
+
+
 def cpu_baseline():
     """The oracle, untuned, on a bounded sample of the fprop workload: one
     expert's 512 token rows and a 4096-row slice of its weight, quantized
@@ -374,7 +392,8 @@ def main():
         "quantize_x_frac_of_hbm": qx.get("frac_of_hbm"),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": MFMA_PEAK_TFLOPS["fp8"], "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_PEAK_TFLOPS["fp8"], 4), "traffic": None,
+                     "frac": round(achieved / MFMA_PEAK_TFLOPS["fp8"], 4),
+                     "traffic": gemm_traffic() if head is results.get("fprop") else None,
                      "kernel": "grouped_gemm_mxfp8 (fprop)"},
         "configs": results,
     }
