@@ -44,6 +44,7 @@
 #include <utility>
 
 #include "bsg_internal.h"
+#include "store_tile.h"
 
 namespace bsg {
 
@@ -410,81 +411,6 @@ __device__ __forceinline__ void step_odd(uint32_t lds, const Dma& d, int w, int 
     }
     fence();
   });
-}
-
-// Stores one 32 x 32 accumulator block: this lane's row `row`, columns
-// col0 + 8 q + [0, 4) in registers 4 q .. 4 q + 3 (col0 = 32 j + 4 h).  `ro`
-// covers the tile's valid rows, so stores to rows past them are dropped by the
-// buffer range check; a column past out_cols gets an offset past every range
-// (kDropped), which drops it the same way, without a branch.
-//   WIDE, bf16 (row stride and out_cols multiples of 8): the two lanes of a row
-//     trade halves with v_permlane32_swap so that lane h holds columns
-//     16 h .. 16 h + 15 of the block, stored as two 16-byte pieces.
-//   WIDE, f32 (multiples of 4): each run of four columns is one 16-byte store.
-//   Otherwise: one store per element.
-constexpr uint32_t kDropped = 0xfffffff0u;
-
-template <bool WIDE, bool F32>
-__device__ __forceinline__ void store_block(const v16f& acc, __amdgpu_buffer_rsrc_t ro, int ldc,
-                                            int row, int col0, int h, int out_cols) {
-  constexpr int esz = F32 ? 4 : 2;
-  if constexpr (WIDE && !F32) {
-    // d[2 q + e] = columns col0 + 8 q + 2 e, + 1 (bf16 pairs)
-    int d[8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-        d[2 * q + e] = __builtin_bit_cast(
-            int, __builtin_convertvector((v2f){acc[4 * q + 2 * e], acc[4 * q + 2 * e + 1]}, v2bf));
-    }
-    // lane (r, 0) keeps d[0..3] and receives lane (r, 1)'s d[0..3] as d[4..7];
-    // lane (r, 1) receives lane (r, 0)'s d[4..7] as d[0..3] and keeps d[4..7]
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const auto sw = __builtin_amdgcn_permlane32_swap(d[k], d[4 + k], false, false);
-      d[k] = sw[0];
-      d[4 + k] = sw[1];
-    }
-    const int col = col0 - 4 * h + 16 * h;
-    const int base = row * ldc + col;
-    const int off0 = col < out_cols ? base * esz : (int)kDropped;
-    const int off1 = col + 8 < out_cols ? (base + 8) * esz : (int)kDropped;
-    __builtin_amdgcn_raw_buffer_store_b128((v4i){d[0], d[1], d[4], d[5]}, ro, off0, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b128((v4i){d[2], d[3], d[6], d[7]}, ro, off1, 0, 0);
-  } else {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int col = col0 + 8 * q;
-      const int idx = row * ldc + col;
-      if constexpr (WIDE) {
-        const int off = col < out_cols ? idx * esz : (int)kDropped;
-        const v4i v = {__float_as_int(acc[4 * q]), __float_as_int(acc[4 * q + 1]),
-                       __float_as_int(acc[4 * q + 2]), __float_as_int(acc[4 * q + 3])};
-        __builtin_amdgcn_raw_buffer_store_b128(v, ro, off, 0, 0);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int off = col + e < out_cols ? (idx + e) * esz : (int)kDropped;
-          if constexpr (F32)
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(acc[4 * q + e]), ro, off, 0, 0);
-          else
-            __builtin_amdgcn_raw_buffer_store_b16(
-                (unsigned short)f32_to_bf16_rne(acc[4 * q + e]), ro, off, 0, 0);
-        }
-      }
-    }
-  }
-}
-
-template <bool WIDE, bool F32>
-__device__ __forceinline__ void store_tile(const v16f (&acc)[4][4], __amdgpu_buffer_rsrc_t ro,
-                                           int ldc, int row, int col, int h, int out_cols) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      store_block<WIDE, F32>(acc[i][j], ro, ldc, row + 32 * i, col + 32 * j, h, out_cols);
 }
 
 __device__ void run_tile(uint32_t lds, const TileDesc& t, int out_f32) {

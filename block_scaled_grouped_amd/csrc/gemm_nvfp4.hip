@@ -18,21 +18,43 @@
 // magnitudes in [2^-10, 2688]).  The product then runs on bf16 MFMA
 // (v_mfma_f32_32x32x16_bf16) with FP32 accumulation: exact products, FP32 sums.
 //
-// Tile 256 x 256 x 64, 4 wavefronts (2 x 2), 128 x 128 per wavefront; LDS holds
-// bf16 rows of 128 bytes with the same XOR chunk swizzle as the MXFP8 GEMM.
-#include "bsg_internal.h"
+// Tile 256 x 256, K-steps of 64, 4 wavefronts (2 x 2) of 128 x 128, each as
+// 4 x 4 MFMA blocks of 32 x 32 (256 accumulator registers per lane).  LDS holds
+// two stages of bf16 rows (128 bytes per row per K-step) with an XOR chunk
+// swizzle that keeps both the row-wise stores and the fragment reads free of
+// bank conflicts.  Thread t decodes row t of both operand tiles: the raw E2M1
+// bytes and E4M3 scales of K-step k + 1 are decoded into the other stage in
+// four pieces placed between the MFMAs of step k, and the raw bytes of step
+// k + 2 are already being loaded.  One barrier per K-step, placed before the
+// last MFMAs so that the next step's first fragments are read under them.  B is
+// the MFMA's first operand, so each lane holds an output row (see store_tile.h).
+#include <utility>
+
+#include "store_tile.h"
 
 namespace bsg {
 
 namespace {
 
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 constexpr int BM = 256;
 constexpr int BN = 256;
 constexpr int BK = 64;          // elements per K-step (32 bytes of E2M1 per row)
 constexpr int kThreads = 256;
+constexpr int kDecodeSlots = 48; // the next step's decode is spread over MFMA slots 0 .. 47
+constexpr int kBarrierSlot = 4;  // MFMA slot of the last substep after which the step barriers
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-
+typedef __attribute__((address_space(3))) v4i lds_v4i;
+typedef __attribute__((address_space(3))) float lds_f32;
 
 struct NvArgs {
   const uint8_t* a;
@@ -53,9 +75,10 @@ struct NvArgs {
   NvGroupTable tab;
 };
 
+constexpr int kStageBytes = (BM + BN) * 128;
+
 struct Smem {
-  uint8_t a[2][BM * 128];
-  uint8_t b[2][BN * 128];
+  uint8_t stage[2][kStageBytes];  // A rows, then B rows, bf16
   float aout[BM];
   float bout[BN];
   int64_t off[kMaxGroups + 1];
@@ -63,13 +86,16 @@ struct Smem {
   int32_t pre[kMaxGroups + 1];
 };
 
+// LDS byte offset of 16-byte chunk c (bf16 elements 8 c .. 8 c + 7) of row r.
 __device__ __forceinline__ int swz(int row, int chunk) {
   return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
+__device__ __forceinline__ v4i lds_read16(uint32_t addr) {
+  return *reinterpret_cast<const lds_v4i*>((size_t)addr);
+}
+__device__ __forceinline__ void lds_write16(uint32_t addr, v4i v) {
+  *reinterpret_cast<lds_v4i*>((size_t)addr) = v;
 }
 
 __device__ __forceinline__ float e4m3_decode(uint32_t c) {
@@ -79,7 +105,8 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
 }
 
 // One byte (two E2M1 nibbles, low nibble first) of dword w, times sd, as a
-// packed bf16 pair (low element in the low half).
+// packed bf16 pair (low element in the low half).  The product has at most 6
+// significant bits, so keeping the upper half of the fp32 bits is exact.
 template <int SEL>
 __device__ __forceinline__ uint32_t dq_pair(uint32_t w, float sd) {
   const v2f f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
@@ -88,19 +115,49 @@ __device__ __forceinline__ uint32_t dq_pair(uint32_t w, float sd) {
   return __builtin_amdgcn_perm(hi, lo, 0x07060302u);
 }
 
-// 16 bytes (32 elements, two 16-element blocks with scales s0, s1) -> 32 bf16.
-__device__ __forceinline__ void dq32(const v4i& d, float s0, float s1, v4i (&o)[4]) {
+// Per-lane LDS offsets, computed once per tile and kept opaque so that the
+// compiler does not materialize one address per access.
+struct Offs {
+  int dec[8];       // this thread's decoded row: chunk c of row tid
+  int fa[4], fb[4]; // fragment part S: row wm*128 + r (A) / wn*128 + r (B), chunk 2 S + h
+};
+
+__device__ __forceinline__ Offs make_offs(int tid, int wm, int wn, int r, int h) {
+  Offs o;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    o.dec[c] = swz(tid, c);
+    asm volatile("" : "+v"(o.dec[c]));
+  }
+#pragma unroll
+  for (int S = 0; S < 4; ++S) {
+    o.fa[S] = swz(wm * 128 + r, 2 * S + h);
+    o.fb[S] = BM * 128 + swz(wn * 128 + r, 2 * S + h);
+    asm volatile("" : "+v"(o.fa[S]));
+    asm volatile("" : "+v"(o.fb[S]));
+  }
+  return o;
+}
+
+// 16 raw bytes (32 elements, two 16-element blocks with scales s0, s1) -> 32
+// bf16, written as four 16-byte chunks c0 .. c0 + 3 of this thread's row.
+template <int C0>
+__device__ __forceinline__ void decode_store(uint32_t base, const Offs& o, const v4i& d, float s0,
+                                             float s1) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const uint32_t w = (uint32_t)d[q];
     const float sd = q < 2 ? s0 : s1;
-    o[q][0] = (int)dq_pair<0>(w, sd);
-    o[q][1] = (int)dq_pair<1>(w, sd);
-    o[q][2] = (int)dq_pair<2>(w, sd);
-    o[q][3] = (int)dq_pair<3>(w, sd);
+    v4i v;
+    v[0] = (int)dq_pair<0>(w, sd);
+    v[1] = (int)dq_pair<1>(w, sd);
+    v[2] = (int)dq_pair<2>(w, sd);
+    v[3] = (int)dq_pair<3>(w, sd);
+    lds_write16(base + o.dec[C0 + q], v);
   }
 }
 
+// Raw bytes of one K-step for this thread's row of A and of B.
 struct Raw {
   v4i a[2], b[2];
   int sa, sb;
@@ -116,58 +173,134 @@ struct TileDesc {
   int64_t kl;
 };
 
-// Thread t loads row t of both operand tiles for one K-step: 32 bytes of E2M1
-// and 4 scale bytes each.  Rows past the valid ones read as zeros.
-__device__ __forceinline__ void load_raw(const TileDesc& t, __amdgpu_buffer_rsrc_t ra,
-                                         __amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rsa,
-                                         __amdgpu_buffer_rsrc_t rsb, int64_t kt, int tid, Raw& x) {
-  const int od = tid * (int)t.lda + (int)kt * (BK / 2);
-  x.a[0] = __builtin_amdgcn_raw_buffer_load_b128(ra, od, 0, 0);
-  x.a[1] = __builtin_amdgcn_raw_buffer_load_b128(ra, od + 16, 0, 0);
-  x.b[0] = __builtin_amdgcn_raw_buffer_load_b128(rb, od, 0, 0);
-  x.b[1] = __builtin_amdgcn_raw_buffer_load_b128(rb, od + 16, 0, 0);
-  const int os = tid * (int)t.ldas + (int)kt * (BK / 16);
-  x.sa = __builtin_amdgcn_raw_buffer_load_b32(rsa, os, 0, 0);
-  x.sb = __builtin_amdgcn_raw_buffer_load_b32(rsb, os, 0, 0);
+struct Rsrc {
+  __amdgpu_buffer_rsrc_t a, b, sa, sb, none;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
 }
 
-__device__ __forceinline__ void dequant_store(uint8_t* lds, int row, const v4i (&d)[2], int s) {
-  const uint32_t sc = (uint32_t)s;
-  v4i o[4];
-  dq32(d[0], e4m3_decode(sc & 0xffu), e4m3_decode((sc >> 8) & 0xffu), o);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) *reinterpret_cast<v4i*>(lds + swz(row, q)) = o[q];
-  dq32(d[1], e4m3_decode((sc >> 16) & 0xffu), e4m3_decode(sc >> 24), o);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) *reinterpret_cast<v4i*>(lds + swz(row, 4 + q)) = o[q];
+// Thread t loads row t of both operand tiles for K-step kt: 32 bytes of E2M1
+// and 4 scale bytes each.  Rows past the valid ones, and steps past the last
+// (`live` false), read as zeros.
+__device__ __forceinline__ void load_raw(const TileDesc& t, const Rsrc& rs, int kt, bool live,
+                                         int tid, Raw& x) {
+  const int od = tid * (int)t.lda + kt * (BK / 2);
+  const int os = tid * (int)t.ldas + kt * (BK / 16);
+  x.a[0] = __builtin_amdgcn_raw_buffer_load_b128(live ? rs.a : rs.none, od, 0, 0);
+  x.a[1] = __builtin_amdgcn_raw_buffer_load_b128(live ? rs.a : rs.none, od + 16, 0, 0);
+  x.b[0] = __builtin_amdgcn_raw_buffer_load_b128(live ? rs.b : rs.none, od, 0, 0);
+  x.b[1] = __builtin_amdgcn_raw_buffer_load_b128(live ? rs.b : rs.none, od + 16, 0, 0);
+  x.sa = __builtin_amdgcn_raw_buffer_load_b32(live ? rs.sa : rs.none, os, 0, 0);
+  x.sb = __builtin_amdgcn_raw_buffer_load_b32(live ? rs.sb : rs.none, os, 0, 0);
 }
 
+// Piece P (0: A elements 0..31, 1: A 32..63, 2: B 0..31, 3: B 32..63) of this
+// thread's decode of one K-step into stage buffer `st`.
+template <int P>
+__device__ __forceinline__ void decode_piece(uint32_t st, const Offs& o, const Raw& x) {
+  constexpr bool isb = P >= 2;
+  constexpr int half = P & 1;
+  const uint32_t sc = (uint32_t)(isb ? x.sb : x.sa);
+  const float s0 = e4m3_decode((sc >> (16 * half)) & 0xffu);
+  const float s1 = e4m3_decode((sc >> (16 * half + 8)) & 0xffu);
+  decode_store<4 * half>(st + (isb ? BM * 128 : 0), o, isb ? x.b[half] : x.a[half], s0, s1);
+}
+
+// Decode unit U (0..63) of a K-step: piece U / 16 (as decode_piece), word
+// (U / 4) % 4 of its 16 raw bytes, nibble pair U % 4 -> one bf16 pair into
+// `buf`; the fourth pair of a word writes the 16-byte chunk to LDS.  Spread one
+// or two per MFMA slot, the decode's VALU work runs under the MFMAs.
+template <int U>
+__device__ __forceinline__ void decode_unit(uint32_t st, const Offs& o, const Raw& x, float (&sd)[2],
+                                            v4i& buf) {
+  constexpr int P = U / 16, q = (U / 4) % 4, pr = U % 4;
+  constexpr bool isb = P >= 2;
+  constexpr int half = P & 1;
+  if constexpr (U % 16 == 0) {
+    const uint32_t sc = (uint32_t)(isb ? x.sb : x.sa);
+    sd[0] = e4m3_decode((sc >> (16 * half)) & 0xffu);
+    sd[1] = e4m3_decode((sc >> (16 * half + 8)) & 0xffu);
+  }
+  const uint32_t w = (uint32_t)(isb ? x.b[half] : x.a[half])[q];
+  buf[pr] = (int)dq_pair<pr>(w, q < 2 ? sd[0] : sd[1]);
+  if constexpr (pr == 3) lds_write16(st + (isb ? BM * 128 : 0) + o.dec[4 * half + q], buf);
+}
+
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// The fragments of substep S (16 elements of the K-step) for this lane: rows
+// wm*128 + 32 i + r of A, wn*128 + 32 j + r of B, elements 16 S + 8 h .. + 7.
 template <int S>
-__device__ __forceinline__ void mfma_substep(const Smem& sm, int st, int wm, int wn, int r, int h,
-                                             v16f (&acc)[4][4]) {
-  v8bf af[4], bf[4];
+__device__ __forceinline__ void read_frags(uint32_t st, const Offs& o, v8bf (&fa)[4],
+                                           v8bf (&fb)[4]) {
+  // rows 32 apart share the lane's swizzle term: the row step is an immediate
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    af[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(
-                                         sm.a[st] + swz(wm * 128 + 32 * i + r, 2 * S + h)));
+    fa[i] = __builtin_bit_cast(v8bf, lds_read16(st + o.fa[S] + 32 * i * 128));
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    bf[j] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(
-                                         sm.b[st] + swz(wn * 128 + 32 * j + r, 2 * S + h)));
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    fb[j] = __builtin_bit_cast(v8bf, lds_read16(st + o.fb[S] + 32 * j * 128));
+}
+
+template <int M>
+__device__ __forceinline__ void mfma(const v8bf (&fa)[4], const v8bf (&fb)[4], v16f (&acc)[4][4]) {
+  constexpr int i = M >> 2, j = M & 3;
+  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+  asm volatile("" : "+a"(acc[i][j]));  // keeps the pure intrinsic in schedule order
+}
+
+// One K-step from stage `cur` (its substep-0 fragments already in f0): while
+// its 64 MFMAs run, decode the raw bytes of the next step (xn) into stage
+// `nxt`, load the raw bytes of the step after it (into xl), read each next
+// substep's fragments, and after the barrier the next step's first fragments.
+__device__ __forceinline__ void k_step(uint32_t cur, uint32_t nxt, const TileDesc& t,
+                                       const Rsrc& rs, int kt, int nk, int tid, const Offs& o,
+                                       const Raw& xn, Raw& xl, v8bf (&f0a)[4],
+                                       v8bf (&f0b)[4], v8bf (&f1a)[4], v8bf (&f1b)[4],
+                                       v16f (&acc)[4][4]) {
+  load_raw(t, rs, kt + 2, kt + 2 < nk, tid, xl);
+  float sd[2];
+  v4i buf;
+  static_for<4>([&](auto sc) {
+    constexpr int S = decltype(sc)::value;
+    v8bf(&ca)[4] = (S & 1) ? f1a : f0a;
+    v8bf(&cb)[4] = (S & 1) ? f1b : f0b;
+    v8bf(&na)[4] = (S & 1) ? f0a : f1a;
+    v8bf(&nb)[4] = (S & 1) ? f0b : f1b;
+    static_for<16>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      mfma<m>(ca, cb, acc);
+      fence();
+      if constexpr (m == 0 && S < 3) read_frags<S + 1>(cur, o, na, nb);
+      // decode units assigned to this slot: U with floor(U * kDecodeSlots / 64) == slot
+      constexpr int slot = 16 * S + m;
+      constexpr int u0 = (slot * 64 + kDecodeSlots - 1) / kDecodeSlots;
+      constexpr int u1 = ((slot + 1) * 64 + kDecodeSlots - 1) / kDecodeSlots;
+      if constexpr (slot < kDecodeSlots) {
+        static_for<(u1 < 64 ? u1 : 64) - u0>([&](auto uc) {
+          decode_unit<u0 + decltype(uc)::value>(nxt, o, xn, sd, buf);
+        });
+      }
+      if constexpr (S == 3 && m == kBarrierSlot) {
+        // the decode of the next step is in LDS and nobody still reads `cur`
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        read_frags<0>(nxt, o, na, nb);
+      }
+      fence();
+    });
+  });
 }
 
 __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
   __shared__ Smem sm;
   const int G = p.G;
-  const int tid = threadIdx.x;
+  const int tid0 = threadIdx.x;
   uint32_t* status = blockIdx.x == 0 ? p.status : nullptr;
   load_offsets_clamped(p.offsets, G, p.rows_cap, sm.off, status);
-  for (int g = tid; g < G; g += kThreads) {
+  for (int g = tid0; g < G; g += kThreads) {
     const int64_t m = group_extent(sm.off, g);
     const int64_t ng = p.tab.n[g];
     sm.cnt[g] = (int32_t)(((m + BM - 1) / BM) * ((ng + BN - 1) / BN));
@@ -176,13 +309,16 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
   wave0_exclusive_scan(sm.cnt, G, sm.pre);
   __syncthreads();
   const int total = sm.pre[G];
+  const uint32_t st0 = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)sm.stage[0];
+  const uint32_t st1 = st0 + kStageBytes;
 
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
     // opaque per-tile copy of the thread index: keeps the compiler from
     // hoisting every LDS / global offset of the tile body out of the tile loop
-    int tix = tid;
-    asm volatile("" : "+v"(tix));
-    const int lane = tix & 63, w = tix >> 6;
+    int tid = tid0;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = w >> 1, wn = w & 1;
     const int r = lane & 31, h = lane >> 5;
     const int g = find_group(sm.pre, G, tile);
@@ -205,15 +341,16 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
     t.a_rows = (int)(rv < BM ? rv : BM);
     t.b_rows = (int)(cv < BN ? cv : BN);
     t.kl = p.k;
-
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(t.a, (int64_t)t.a_rows * t.lda);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(t.b, (int64_t)t.b_rows * t.lda);
-    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(t.as, (int64_t)t.a_rows * t.ldas);
-    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(t.bs, (int64_t)t.b_rows * t.ldas);
+    Rsrc rs;
+    rs.a = make_rsrc(t.a, (int64_t)t.a_rows * t.lda);
+    rs.b = make_rsrc(t.b, (int64_t)t.b_rows * t.lda);
+    rs.sa = make_rsrc(t.as, (int64_t)t.a_rows * t.ldas);
+    rs.sb = make_rsrc(t.bs, (int64_t)t.b_rows * t.ldas);
+    rs.none = make_rsrc(t.a, 0);
 
     // outer scales of this tile's rows and columns, for the epilogue
-    sm.aout[tix] = tix < t.a_rows ? p.aout[row0 + tix] : 0.0f;
-    sm.bout[tix] = tix < t.b_rows ? p.bout[brow0 + tix] : 0.0f;
+    sm.aout[tid] = tid < t.a_rows ? p.aout[row0 + tid] : 0.0f;
+    sm.bout[tid] = tid < t.b_rows ? p.bout[brow0 + tid] : 0.0f;
 
     v16f acc[4][4];
 #pragma unroll
@@ -221,61 +358,64 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
 
-    const int64_t nk = t.kl / BK;
-    Raw x;
-    if (nk > 0) {
-      load_raw(t, ra, rb, rsa, rsb, 0, tix, x);
-      dequant_store(sm.a[0], tix, x.a, x.sa);
-      dequant_store(sm.b[0], tix, x.b, x.sb);
-    }
-    __syncthreads();
-    for (int64_t kt = 0; kt < nk; ++kt) {
-      const int st = (int)(kt & 1);
-      if (kt + 1 < nk) load_raw(t, ra, rb, rsa, rsb, kt + 1, tix, x);
-      mfma_substep<0>(sm, st, wm, wn, r, h, acc);
-      mfma_substep<1>(sm, st, wm, wn, r, h, acc);
-      mfma_substep<2>(sm, st, wm, wn, r, h, acc);
-      mfma_substep<3>(sm, st, wm, wn, r, h, acc);
-      if (kt + 1 < nk) {
-        dequant_store(sm.a[st ^ 1], tix, x.a, x.sa);
-        dequant_store(sm.b[st ^ 1], tix, x.b, x.sb);
+    const int nk = (int)(t.kl / BK);   // >= 1
+    const int nk2 = (nk + 1) & ~1;     // an odd last step runs on zeros
+    {
+      const Offs o = make_offs(tid, wm, wn, r, h);
+      Raw x0, x1;
+      v8bf f0a[4], f0b[4], f1a[4], f1b[4];
+      load_raw(t, rs, 0, true, tid, x0);
+      load_raw(t, rs, 1, 1 < nk, tid, x1);
+      static_for<4>([&](auto pc) { decode_piece<decltype(pc)::value>(st0, o, x0); });
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      read_frags<0>(st0, o, f0a, f0b);
+      for (int kt = 0; kt < nk2; kt += 2) {
+        k_step(st0, st1, t, rs, kt, nk, tid, o, x1, x0, f0a, f0b, f1a, f1b, acc);
+        k_step(st1, st0, t, rs, kt + 1, nk, tid, o, x0, x1, f0a, f0b, f1a, f1b, acc);
       }
-      __syncthreads();
     }
 
     // epilogue: S -> (S * a_outer) * b_outer, or S itself into the scratch
     const bool fused = p.scratch == nullptr;
-    const int esz = (fused && !p.out_f32) ? 2 : 4;
+    const bool f32out = !fused || p.out_f32;
+    const int esz = f32out ? 4 : 2;
     char* obase = fused ? reinterpret_cast<char*>(p.out) : reinterpret_cast<char*>(p.scratch);
     obase += (row0 * p.ld_out + n0) * esz;
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(obase, (int64_t)t.a_rows * p.ld_out * esz);
     int ldc = (int)p.ld_out;
     asm volatile("" : "+s"(ldc));
+    const int row = wm * 128 + r, col = wn * 128 + 4 * h;
+    const uint32_t ao_base = (uint32_t)(size_t)(__attribute__((address_space(3))) float*)sm.aout;
+    const uint32_t bo_base = (uint32_t)(size_t)(__attribute__((address_space(3))) float*)sm.bout;
+    const bool wide = f32out ? ((ldc & 3) == 0 && (t.b_rows & 3) == 0)
+                             : ((ldc & 7) == 0 && (t.b_rows & 7) == 0);
+    // one 32 x 32 block at a time: scaled into a temporary (fused) and stored
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      const float ao = fused ? *reinterpret_cast<const lds_f32*>((size_t)(ao_base + 4 * (row + 32 * i)))
+                             : 1.0f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int col = wn * 128 + 32 * j + r;
-        if (col >= t.b_rows) continue;
-        const float bo = sm.bout[col];
+        v16f y = acc[i][j];
+        if (fused) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = wm * 128 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-          const int idx = row * ldc + col;
-          float y = acc[i][j][v];
-          if (fused) {
-            y = (y * sm.aout[row < BM ? row : 0]) * bo;
-            if (p.out_f32)
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(y), ro, idx * 4, 0, 0);
-            else
-              __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16_rne(y), ro, idx * 2,
-                                                    0, 0);
-          } else {
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(y), ro, idx * 4, 0, 0);
+          for (int q = 0; q < 4; ++q) {
+            const v4i bo = lds_read16(bo_base + 4 * (col + 32 * j + 8 * q));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[4 * q + e] = (y[4 * q + e] * ao) * __int_as_float(bo[e]);
           }
         }
+        const int rr = row + 32 * i, cc = col + 32 * j;
+        if (f32out) {
+          if (wide) store_block<true, true>(y, ro, ldc, rr, cc, h, t.b_rows);
+          else store_block<false, true>(y, ro, ldc, rr, cc, h, t.b_rows);
+        } else {
+          if (wide) store_block<true, false>(y, ro, ldc, rr, cc, h, t.b_rows);
+          else store_block<false, false>(y, ro, ldc, rr, cc, h, t.b_rows);
+        }
       }
-    __syncthreads();  // aout / bout are rewritten by the next tile
+    }
+    __syncthreads();  // aout / bout and the stages are rewritten by the next tile
   }
 }
 
