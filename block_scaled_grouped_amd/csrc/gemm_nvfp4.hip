@@ -13,14 +13,15 @@
 // gfx950's scaled MFMA takes only power-of-two (E8M0) scales per 32 elements,
 // and E2M1 x E4M3 needs up to 6 significant bits, so no FP8/FP6/FP4 MFMA input
 // holds it exactly.  Each element is instead decoded while it is staged into
-// LDS: E2M1 -> fp32 (hardware convert, unit scale), times its decoded E4M3 block
-// scale (exact in fp32), truncated to bf16 (exact: at most 6 significant bits,
-// magnitudes in [2^-10, 2688]).  The product then runs on bf16 MFMA
-// (v_mfma_f32_32x32x16_bf16) with FP32 accumulation: exact products, FP32 sums.
+// LDS: E2M1 -> fp16 pairs (hardware convert, unit scale), times its decoded E4M3
+// block scale with one packed fp16 multiply per pair -- exact, since the product
+// has at most 6 significant bits and lies in [2^-10, 2688], all normal fp16.
+// The product then runs on fp16 MFMA (v_mfma_f32_32x32x16_f16, the bf16 rate)
+// with FP32 accumulation: exact products, FP32 sums.
 //
 // Tile 256 x 256, K-steps of 64, 4 wavefronts (2 x 2) of 128 x 128, each as
 // 4 x 4 MFMA blocks of 32 x 32 (256 accumulator registers per lane).  LDS holds
-// two stages of bf16 rows (128 bytes per row per K-step) with an XOR chunk
+// two stages of fp16 rows (128 bytes per row per K-step) with an XOR chunk
 // swizzle that keeps both the row-wise stores and the fragment reads free of
 // bank conflicts.  Thread t decodes row t of both operand tiles: the raw E2M1
 // bytes and E4M3 scales of K-step k + 1 are decoded into the other stage in
@@ -52,7 +53,8 @@ constexpr int kThreads = 256;
 constexpr int kDecodeSlots = 48; // the next step's decode is spread over MFMA slots 0 .. 47
 constexpr int kBarrierSlot = 4;  // MFMA slot of the last substep after which the step barriers
 
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v4i lds_v4i;
 typedef __attribute__((address_space(3))) float lds_f32;
 
@@ -78,7 +80,7 @@ struct NvArgs {
 constexpr int kStageBytes = (BM + BN) * 128;
 
 struct Smem {
-  uint8_t stage[2][kStageBytes];  // A rows, then B rows, bf16
+  uint8_t stage[2][kStageBytes];  // A rows, then B rows, fp16
   float aout[BM];
   float bout[BN];
   int64_t off[kMaxGroups + 1];
@@ -86,9 +88,13 @@ struct Smem {
   int32_t pre[kMaxGroups + 1];
 };
 
-// LDS byte offset of 16-byte chunk c (bf16 elements 8 c .. 8 c + 7) of row r.
+// LDS byte offset of 16-byte chunk c (fp16 elements 8 c .. 8 c + 7) of row r.
+// The XOR term takes 8 distinct values over any 8 consecutive rows, and
+// (row % 2, term) 16 distinct values over any 16, so a 16-byte access by lanes
+// of consecutive rows and one chunk is conflict-free whether the LDS serves 8
+// lanes per 128-byte bank window or 16 lanes per 256-byte window.
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
+  return row * 128 + ((chunk ^ ((row >> 1) & 7) ^ ((row & 1) << 2)) << 4);
 }
 
 __device__ __forceinline__ v4i lds_read16(uint32_t addr) {
@@ -98,21 +104,22 @@ __device__ __forceinline__ void lds_write16(uint32_t addr, v4i v) {
   *reinterpret_cast<lds_v4i*>((size_t)addr) = v;
 }
 
-__device__ __forceinline__ float e4m3_decode(uint32_t c) {
-  const uint32_t e = (c >> 3) & 0xfu, m = c & 7u;
-  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
-  return (c & 0x80u) ? -mag : mag;
+// One byte (two E2M1 nibbles, low nibble first) of dword w, times the block
+// scale (in both halves of sd2), as a packed fp16 pair (low element first).
+template <int SEL>
+__device__ __forceinline__ uint32_t dq_pair(uint32_t w, v2h sd2) {
+  const v2h f = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+  return __builtin_bit_cast(uint32_t, f * sd2);
 }
 
-// One byte (two E2M1 nibbles, low nibble first) of dword w, times sd, as a
-// packed bf16 pair (low element in the low half).  The product has at most 6
-// significant bits, so keeping the upper half of the fp32 bits is exact.
-template <int SEL>
-__device__ __forceinline__ uint32_t dq_pair(uint32_t w, float sd) {
-  const v2f f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
-  const uint32_t lo = __float_as_uint(f[0] * sd);
-  const uint32_t hi = __float_as_uint(f[1] * sd);
-  return __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+// Two E4M3 codes (bytes 0 and 1 of c) as fp16 (exact: every E4M3 value is a
+// normal fp16), without branches: the 7 magnitude bits placed under an fp16
+// exponent field read as 2^(e - 15) (1 + m/8), or m 2^-17 for e = 0, so one
+// multiply by 2^8 gives the E4M3 value 2^(e - 7) (1 + m/8), or m 2^-9.
+__device__ __forceinline__ v2h e4m3_pair_h2(uint32_t c) {
+  const uint32_t lo = ((c & 0x7fu) << 7) | ((c & 0x80u) << 8);
+  const uint32_t hi = ((c & 0x7f00u) << 15) | ((c & 0x8000u) << 16);
+  return __builtin_bit_cast(v2h, lo | hi) * v2h{(_Float16)256.0f, (_Float16)256.0f};
 }
 
 // Per-lane LDS offsets, computed once per tile and kept opaque so that the
@@ -140,14 +147,14 @@ __device__ __forceinline__ Offs make_offs(int tid, int wm, int wn, int r, int h)
 }
 
 // 16 raw bytes (32 elements, two 16-element blocks with scales s0, s1) -> 32
-// bf16, written as four 16-byte chunks c0 .. c0 + 3 of this thread's row.
+// fp16, written as four 16-byte chunks c0 .. c0 + 3 of this thread's row.
 template <int C0>
-__device__ __forceinline__ void decode_store(uint32_t base, const Offs& o, const v4i& d, float s0,
-                                             float s1) {
+__device__ __forceinline__ void decode_store(uint32_t base, const Offs& o, const v4i& d, v2h s0,
+                                             v2h s1) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const uint32_t w = (uint32_t)d[q];
-    const float sd = q < 2 ? s0 : s1;
+    const v2h sd = q < 2 ? s0 : s1;
     v4i v;
     v[0] = (int)dq_pair<0>(w, sd);
     v[1] = (int)dq_pair<1>(w, sd);
@@ -204,25 +211,26 @@ __device__ __forceinline__ void decode_piece(uint32_t st, const Offs& o, const R
   constexpr bool isb = P >= 2;
   constexpr int half = P & 1;
   const uint32_t sc = (uint32_t)(isb ? x.sb : x.sa);
-  const float s0 = e4m3_decode((sc >> (16 * half)) & 0xffu);
-  const float s1 = e4m3_decode((sc >> (16 * half + 8)) & 0xffu);
-  decode_store<4 * half>(st + (isb ? BM * 128 : 0), o, isb ? x.b[half] : x.a[half], s0, s1);
+  const v2h s01 = e4m3_pair_h2(sc >> (16 * half));
+  decode_store<4 * half>(st + (isb ? BM * 128 : 0), o, isb ? x.b[half] : x.a[half],
+                         v2h{s01[0], s01[0]}, v2h{s01[1], s01[1]});
 }
 
 // Decode unit U (0..63) of a K-step: piece U / 16 (as decode_piece), word
-// (U / 4) % 4 of its 16 raw bytes, nibble pair U % 4 -> one bf16 pair into
+// (U / 4) % 4 of its 16 raw bytes, nibble pair U % 4 -> one fp16 pair into
 // `buf`; the fourth pair of a word writes the 16-byte chunk to LDS.  Spread one
 // or two per MFMA slot, the decode's VALU work runs under the MFMAs.
 template <int U>
-__device__ __forceinline__ void decode_unit(uint32_t st, const Offs& o, const Raw& x, float (&sd)[2],
+__device__ __forceinline__ void decode_unit(uint32_t st, const Offs& o, const Raw& x, v2h (&sd)[2],
                                             v4i& buf) {
   constexpr int P = U / 16, q = (U / 4) % 4, pr = U % 4;
   constexpr bool isb = P >= 2;
   constexpr int half = P & 1;
   if constexpr (U % 16 == 0) {
     const uint32_t sc = (uint32_t)(isb ? x.sb : x.sa);
-    sd[0] = e4m3_decode((sc >> (16 * half)) & 0xffu);
-    sd[1] = e4m3_decode((sc >> (16 * half + 8)) & 0xffu);
+    const v2h s01 = e4m3_pair_h2(sc >> (16 * half));
+    sd[0] = v2h{s01[0], s01[0]};
+    sd[1] = v2h{s01[1], s01[1]};
   }
   const uint32_t w = (uint32_t)(isb ? x.b[half] : x.a[half])[q];
   buf[pr] = (int)dq_pair<pr>(w, q < 2 ? sd[0] : sd[1]);
@@ -234,21 +242,21 @@ __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 // The fragments of substep S (16 elements of the K-step) for this lane: rows
 // wm*128 + 32 i + r of A, wn*128 + 32 j + r of B, elements 16 S + 8 h .. + 7.
 template <int S>
-__device__ __forceinline__ void read_frags(uint32_t st, const Offs& o, v8bf (&fa)[4],
-                                           v8bf (&fb)[4]) {
+__device__ __forceinline__ void read_frags(uint32_t st, const Offs& o, v8h (&fa)[4],
+                                           v8h (&fb)[4]) {
   // rows 32 apart share the lane's swizzle term: the row step is an immediate
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    fa[i] = __builtin_bit_cast(v8bf, lds_read16(st + o.fa[S] + 32 * i * 128));
+    fa[i] = __builtin_bit_cast(v8h, lds_read16(st + o.fa[S] + 32 * i * 128));
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    fb[j] = __builtin_bit_cast(v8bf, lds_read16(st + o.fb[S] + 32 * j * 128));
+    fb[j] = __builtin_bit_cast(v8h, lds_read16(st + o.fb[S] + 32 * j * 128));
 }
 
 template <int M>
-__device__ __forceinline__ void mfma(const v8bf (&fa)[4], const v8bf (&fb)[4], v16f (&acc)[4][4]) {
+__device__ __forceinline__ void mfma(const v8h (&fa)[4], const v8h (&fb)[4], v16f (&acc)[4][4]) {
   constexpr int i = M >> 2, j = M & 3;
-  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
   asm volatile("" : "+a"(acc[i][j]));  // keeps the pure intrinsic in schedule order
 }
 
@@ -258,18 +266,18 @@ __device__ __forceinline__ void mfma(const v8bf (&fa)[4], const v8bf (&fb)[4], v
 // substep's fragments, and after the barrier the next step's first fragments.
 __device__ __forceinline__ void k_step(uint32_t cur, uint32_t nxt, const TileDesc& t,
                                        const Rsrc& rs, int kt, int nk, int tid, const Offs& o,
-                                       const Raw& xn, Raw& xl, v8bf (&f0a)[4],
-                                       v8bf (&f0b)[4], v8bf (&f1a)[4], v8bf (&f1b)[4],
+                                       const Raw& xn, Raw& xl, v8h (&f0a)[4],
+                                       v8h (&f0b)[4], v8h (&f1a)[4], v8h (&f1b)[4],
                                        v16f (&acc)[4][4]) {
   load_raw(t, rs, kt + 2, kt + 2 < nk, tid, xl);
-  float sd[2];
+  v2h sd[2];
   v4i buf;
   static_for<4>([&](auto sc) {
     constexpr int S = decltype(sc)::value;
-    v8bf(&ca)[4] = (S & 1) ? f1a : f0a;
-    v8bf(&cb)[4] = (S & 1) ? f1b : f0b;
-    v8bf(&na)[4] = (S & 1) ? f0a : f1a;
-    v8bf(&nb)[4] = (S & 1) ? f0b : f1b;
+    v8h(&ca)[4] = (S & 1) ? f1a : f0a;
+    v8h(&cb)[4] = (S & 1) ? f1b : f0b;
+    v8h(&na)[4] = (S & 1) ? f0a : f1a;
+    v8h(&nb)[4] = (S & 1) ? f0b : f1b;
     static_for<16>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
       mfma<m>(ca, cb, acc);
@@ -363,7 +371,7 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
     {
       const Offs o = make_offs(tid, wm, wn, r, h);
       Raw x0, x1;
-      v8bf f0a[4], f0b[4], f1a[4], f1b[4];
+      v8h f0a[4], f0b[4], f1a[4], f1b[4];
       load_raw(t, rs, 0, true, tid, x0);
       load_raw(t, rs, 1, 1 < nk, tid, x1);
       static_for<4>([&](auto pc) { decode_piece<decltype(pc)::value>(st0, o, x0); });
