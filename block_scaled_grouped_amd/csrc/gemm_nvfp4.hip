@@ -77,10 +77,15 @@ struct NvArgs {
   NvGroupTable tab;
 };
 
-constexpr int kStageBytes = (BM + BN) * 128;
+static_assert(BM == BN, "A and B stage halves share one layout");
+constexpr int kHalfStage = BM * 128;  // one operand's rows of one K-step, fp16
+constexpr int kOperandB = 2 * kHalfStage;
 
 struct Smem {
-  uint8_t stage[2][kStageBytes];  // A rows, then B rows, fp16
+  // A stage 0, A stage 1, B stage 0, B stage 1: every offset between the
+  // stages, and between rows r and r + 128, fits an LDS instruction's
+  // immediate offset field
+  uint8_t stage[4][kHalfStage];
   float aout[BM];
   float bout[BN];
   int64_t off[kMaxGroups + 1];
@@ -112,20 +117,17 @@ __device__ __forceinline__ uint32_t dq_pair(uint32_t w, v2h sd2) {
   return __builtin_bit_cast(uint32_t, f * sd2);
 }
 
-// Two E4M3 codes (bytes 0 and 1 of c) as fp16 (exact: every E4M3 value is a
-// normal fp16), without branches: the 7 magnitude bits placed under an fp16
-// exponent field read as 2^(e - 15) (1 + m/8), or m 2^-17 for e = 0, so one
-// multiply by 2^8 gives the E4M3 value 2^(e - 7) (1 + m/8), or m 2^-9.
+// E4M3 codes in bytes 2 HI and 2 HI + 1 of c as fp16 (exact: every E4M3 value
+// is a normal fp16; a unit scale leaves the value as it is).
+template <bool HI>
 __device__ __forceinline__ v2h e4m3_pair_h2(uint32_t c) {
-  const uint32_t lo = ((c & 0x7fu) << 7) | ((c & 0x80u) << 8);
-  const uint32_t hi = ((c & 0x7f00u) << 15) | ((c & 0x8000u) << 16);
-  return __builtin_bit_cast(v2h, lo | hi) * v2h{(_Float16)256.0f, (_Float16)256.0f};
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c, 1.0f, HI);
 }
 
 // Per-lane LDS offsets, computed once per tile and kept opaque so that the
 // compiler does not materialize one address per access.
 struct Offs {
-  int dec[8];       // this thread's decoded row: chunk c of row tid
+  int dec[8];       // chunk c of this thread's first decoded row (tid % 128 of A or B)
   int fa[4], fb[4]; // fragment part S: row wm*128 + r (A) / wn*128 + r (B), chunk 2 S + h
 };
 
@@ -133,13 +135,13 @@ __device__ __forceinline__ Offs make_offs(int tid, int wm, int wn, int r, int h)
   Offs o;
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    o.dec[c] = swz(tid, c);
+    o.dec[c] = (tid >= 128 ? kOperandB : 0) + swz(tid & 127, c);
     asm volatile("" : "+v"(o.dec[c]));
   }
 #pragma unroll
   for (int S = 0; S < 4; ++S) {
     o.fa[S] = swz(wm * 128 + r, 2 * S + h);
-    o.fb[S] = BM * 128 + swz(wn * 128 + r, 2 * S + h);
+    o.fb[S] = kOperandB + swz(wn * 128 + r, 2 * S + h);
     asm volatile("" : "+v"(o.fa[S]));
     asm volatile("" : "+v"(o.fb[S]));
   }
@@ -147,7 +149,8 @@ __device__ __forceinline__ Offs make_offs(int tid, int wm, int wn, int r, int h)
 }
 
 // 16 raw bytes (32 elements, two 16-element blocks with scales s0, s1) -> 32
-// fp16, written as four 16-byte chunks c0 .. c0 + 3 of this thread's row.
+// fp16, written as four 16-byte chunks c0 .. c0 + 3 of a row at `base`
+// relative to this thread's first row.
 template <int C0>
 __device__ __forceinline__ void decode_store(uint32_t base, const Offs& o, const v4i& d, v2h s0,
                                              v2h s1) {
@@ -164,10 +167,11 @@ __device__ __forceinline__ void decode_store(uint32_t base, const Offs& o, const
   }
 }
 
-// Raw bytes of one K-step for this thread's row of A and of B.
+// Raw bytes of one K-step for this thread's two rows (r0 = tid % 128 and
+// r0 + 128 of A for tid < 128, of B otherwise).
 struct Raw {
-  v4i a[2], b[2];
-  int sa, sb;
+  v4i d[2][2];  // [row][half]
+  int s[2];     // the row's four E4M3 block scales
 };
 
 struct TileDesc {
@@ -181,7 +185,7 @@ struct TileDesc {
 };
 
 struct Rsrc {
-  __amdgpu_buffer_rsrc_t a, b, sa, sb, none;
+  __amdgpu_buffer_rsrc_t d, s, none;  // this thread's operand and its scales
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
@@ -189,31 +193,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
                                            0x00020000);
 }
 
-// Thread t loads row t of both operand tiles for K-step kt: 32 bytes of E2M1
-// and 4 scale bytes each.  Rows past the valid ones, and steps past the last
-// (`live` false), read as zeros.
+// Thread t loads its two rows for K-step kt: 32 bytes of E2M1 and 4 scale
+// bytes each.  Rows past the valid ones, and steps past the last (`live`
+// false), read as zeros.
 __device__ __forceinline__ void load_raw(const TileDesc& t, const Rsrc& rs, int kt, bool live,
                                          int tid, Raw& x) {
-  const int od = tid * (int)t.lda + kt * (BK / 2);
-  const int os = tid * (int)t.ldas + kt * (BK / 16);
-  x.a[0] = __builtin_amdgcn_raw_buffer_load_b128(live ? rs.a : rs.none, od, 0, 0);
-  x.a[1] = __builtin_amdgcn_raw_buffer_load_b128(live ? rs.a : rs.none, od + 16, 0, 0);
-  x.b[0] = __builtin_amdgcn_raw_buffer_load_b128(live ? rs.b : rs.none, od, 0, 0);
-  x.b[1] = __builtin_amdgcn_raw_buffer_load_b128(live ? rs.b : rs.none, od + 16, 0, 0);
-  x.sa = __builtin_amdgcn_raw_buffer_load_b32(live ? rs.sa : rs.none, os, 0, 0);
-  x.sb = __builtin_amdgcn_raw_buffer_load_b32(live ? rs.sb : rs.none, os, 0, 0);
+  const int r0 = tid & 127;
+  const int od = r0 * (int)t.lda + kt * (BK / 2);
+  const int os = r0 * (int)t.ldas + kt * (BK / 16);
+  const int od1 = od + 128 * (int)t.lda, os1 = os + 128 * (int)t.ldas;
+  x.d[0][0] = __builtin_amdgcn_raw_buffer_load_b128(live ? rs.d : rs.none, od, 0, 0);
+  x.d[0][1] = __builtin_amdgcn_raw_buffer_load_b128(live ? rs.d : rs.none, od + 16, 0, 0);
+  x.d[1][0] = __builtin_amdgcn_raw_buffer_load_b128(live ? rs.d : rs.none, od1, 0, 0);
+  x.d[1][1] = __builtin_amdgcn_raw_buffer_load_b128(live ? rs.d : rs.none, od1 + 16, 0, 0);
+  x.s[0] = __builtin_amdgcn_raw_buffer_load_b32(live ? rs.s : rs.none, os, 0, 0);
+  x.s[1] = __builtin_amdgcn_raw_buffer_load_b32(live ? rs.s : rs.none, os1, 0, 0);
 }
 
-// Piece P (0: A elements 0..31, 1: A 32..63, 2: B 0..31, 3: B 32..63) of this
-// thread's decode of one K-step into stage buffer `st`.
+// Piece P (0: first row elements 0..31, 1: its 32..63, 2 and 3: the same of
+// the second row, 128 rows further) of this thread's decode of one K-step
+// into the stage at `st`.
 template <int P>
 __device__ __forceinline__ void decode_piece(uint32_t st, const Offs& o, const Raw& x) {
-  constexpr bool isb = P >= 2;
-  constexpr int half = P & 1;
-  const uint32_t sc = (uint32_t)(isb ? x.sb : x.sa);
-  const v2h s01 = e4m3_pair_h2(sc >> (16 * half));
-  decode_store<4 * half>(st + (isb ? BM * 128 : 0), o, isb ? x.b[half] : x.a[half],
-                         v2h{s01[0], s01[0]}, v2h{s01[1], s01[1]});
+  constexpr int row = P >> 1, half = P & 1;
+  const v2h s01 = e4m3_pair_h2<half>((uint32_t)x.s[row]);
+  decode_store<4 * half>(st + row * 128 * 128, o, x.d[row][half], v2h{s01[0], s01[0]},
+                         v2h{s01[1], s01[1]});
 }
 
 // Decode unit U (0..63) of a K-step: piece U / 16 (as decode_piece), word
@@ -224,17 +229,15 @@ template <int U>
 __device__ __forceinline__ void decode_unit(uint32_t st, const Offs& o, const Raw& x, v2h (&sd)[2],
                                             v4i& buf) {
   constexpr int P = U / 16, q = (U / 4) % 4, pr = U % 4;
-  constexpr bool isb = P >= 2;
-  constexpr int half = P & 1;
+  constexpr int row = P >> 1, half = P & 1;
   if constexpr (U % 16 == 0) {
-    const uint32_t sc = (uint32_t)(isb ? x.sb : x.sa);
-    const v2h s01 = e4m3_pair_h2(sc >> (16 * half));
+    const v2h s01 = e4m3_pair_h2<half>((uint32_t)x.s[row]);
     sd[0] = v2h{s01[0], s01[0]};
     sd[1] = v2h{s01[1], s01[1]};
   }
-  const uint32_t w = (uint32_t)(isb ? x.b[half] : x.a[half])[q];
+  const uint32_t w = (uint32_t)x.d[row][half][q];
   buf[pr] = (int)dq_pair<pr>(w, q < 2 ? sd[0] : sd[1]);
-  if constexpr (pr == 3) lds_write16(st + (isb ? BM * 128 : 0) + o.dec[4 * half + q], buf);
+  if constexpr (pr == 3) lds_write16(st + row * 128 * 128 + o.dec[4 * half + q], buf);
 }
 
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
@@ -318,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
   __syncthreads();
   const int total = sm.pre[G];
   const uint32_t st0 = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)sm.stage[0];
-  const uint32_t st1 = st0 + kStageBytes;
+  const uint32_t st1 = st0 + kHalfStage;
 
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
     // opaque per-tile copy of the thread index: keeps the compiler from
@@ -349,11 +352,12 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
     t.a_rows = (int)(rv < BM ? rv : BM);
     t.b_rows = (int)(cv < BN ? cv : BN);
     t.kl = p.k;
+    // waves 0 and 1 decode A, waves 2 and 3 B
+    const bool opb = w >= 2;
     Rsrc rs;
-    rs.a = make_rsrc(t.a, (int64_t)t.a_rows * t.lda);
-    rs.b = make_rsrc(t.b, (int64_t)t.b_rows * t.lda);
-    rs.sa = make_rsrc(t.as, (int64_t)t.a_rows * t.ldas);
-    rs.sb = make_rsrc(t.bs, (int64_t)t.b_rows * t.ldas);
+    rs.d = opb ? make_rsrc(t.b, (int64_t)t.b_rows * t.lda) : make_rsrc(t.a, (int64_t)t.a_rows * t.lda);
+    rs.s = opb ? make_rsrc(t.bs, (int64_t)t.b_rows * t.ldas)
+               : make_rsrc(t.as, (int64_t)t.a_rows * t.ldas);
     rs.none = make_rsrc(t.a, 0);
 
     // outer scales of this tile's rows and columns, for the epilogue
