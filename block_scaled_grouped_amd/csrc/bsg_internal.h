@@ -108,6 +108,40 @@ __device__ __forceinline__ int find_group(const int32_t* s_pre, int G, int t) {
   return lo;
 }
 
+// Workgroup b of a launch runs on XCD b % kXcds, and each XCD has its own L2.
+constexpr int kXcds = 8;
+
+// Position of workgroup b in the tile order: with a grid that is a multiple of
+// kXcds, the workgroups of one XCD take consecutive tiles of each round of
+// gridDim.x tiles, so tiles that share operand rows share that XCD's L2.
+__device__ __forceinline__ int xcd_slot() {
+  const int nxcd = gridDim.x % kXcds == 0 ? kXcds : 1;
+  return (blockIdx.x % nxcd) * (gridDim.x / nxcd) + blockIdx.x / nxcd;
+}
+
+// Position (mt, nt) of local tile u of a group with mtiles x ntiles tiles,
+// enumerated in blocks of SM x SN tiles (row of blocks by row of blocks, m
+// fastest inside a block); only the last block row / column can be partial,
+// so the block of u follows from two divisions.
+template <int SM, int SN>
+__device__ __forceinline__ void super_tile(int u, int mtiles, int ntiles, int& mt, int& nt) {
+  const int full_rows = mtiles / SM;
+  int br, hgt, u2;
+  if (u < full_rows * SM * ntiles) {
+    br = u / (SM * ntiles);
+    hgt = SM;
+    u2 = u - br * SM * ntiles;
+  } else {
+    br = full_rows;
+    hgt = mtiles - full_rows * SM;
+    u2 = u - full_rows * SM * ntiles;
+  }
+  const int bc = u2 / (SN * hgt);
+  const int u3 = u2 - bc * SN * hgt;
+  mt = br * SM + u3 % hgt;
+  nt = bc * SN + u3 / hgt;
+}
+
 // ---------------------------------------------------------------- launchers
 
 struct NvGroupTable {

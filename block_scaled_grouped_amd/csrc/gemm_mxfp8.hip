@@ -77,7 +77,6 @@ constexpr int kRegPerPair = 8;         // and global -> registers -> LDS: B
 constexpr int kBarrierAfter = 2;       // MFMA index of a pair's second step after which it
                                        // waits + barriers
 constexpr int kSuperM = 4, kSuperN = 8;  // tile block one XCD works on
-constexpr int kXcds = 8;
 
 struct MxArgs {
   const uint8_t* a;
@@ -483,28 +482,6 @@ __device__ void run_tile(uint32_t lds, const TileDesc& t, int out_f32) {
   }
 }
 
-// Position (mt, nt) of local tile u of a group with mtiles x ntiles tiles,
-// enumerated in blocks of kSuperM x kSuperN tiles (row of blocks by row of
-// blocks, m fastest inside a block); only the last block row / column can be
-// partial, so the block of u follows from two divisions.
-__device__ __forceinline__ void super_tile(int u, int mtiles, int ntiles, int& mt, int& nt) {
-  const int full_rows = mtiles / kSuperM;
-  int br, hgt, u2;
-  if (u < full_rows * kSuperM * ntiles) {
-    br = u / (kSuperM * ntiles);
-    hgt = kSuperM;
-    u2 = u - br * kSuperM * ntiles;
-  } else {
-    br = full_rows;
-    hgt = mtiles - full_rows * kSuperM;
-    u2 = u - full_rows * kSuperM * ntiles;
-  }
-  const int bc = u2 / (kSuperN * hgt);
-  const int u3 = u2 - bc * kSuperN * hgt;
-  mt = br * kSuperM + u3 % hgt;
-  nt = bc * kSuperN + u3 / hgt;
-}
-
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(MxArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_ring[kBufs * kBufBytes];
@@ -532,11 +509,7 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(MxArgs p) {
   const int total = sm.pre[G];
   const int out_elem = p.out_f32 ? 4 : 2;
 
-  // XCD-aware order: in each round of gridDim.x tiles, the workgroups of XCD x
-  // (b % 8 == x) take consecutive tile indices.
-  const int nxcd = gridDim.x % kXcds == 0 ? kXcds : 1;
-  const int per_xcd = gridDim.x / nxcd;
-  const int slot = (blockIdx.x % nxcd) * per_xcd + blockIdx.x / nxcd;
+  const int slot = xcd_slot();
 
   for (int round = 0;; ++round) {
     const int tile = round * gridDim.x + slot;
@@ -548,7 +521,7 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(MxArgs p) {
       const int64_t m = group_extent(sm.off, g);
       const int mtiles = (int)((m + BM - 1) / BM);
       int mt, nt;
-      super_tile(local, mtiles, (int)ntn, mt, nt);
+      super_tile<kSuperM, kSuperN>(local, mtiles, (int)ntn, mt, nt);
       const int64_t row0 = sm.off[g] + (int64_t)mt * BM;
       const int64_t n0 = (int64_t)nt * BN;
       const int64_t nq = p.k / 128;            // scale words per row
@@ -576,7 +549,7 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(MxArgs p) {
       const bool ok = (sm.off[g] % kColPad) == 0 && (mp % kColPad) == 0;
       const int ntm = (int)((p.n + BM - 1) / BM), ntk = (int)((p.k + BN - 1) / BN);
       int it, jt;
-      super_tile(local, ntm, ntk, it, jt);
+      super_tile<kSuperM, kSuperN>(local, ntm, ntk, it, jt);
       const int64_t n0 = (int64_t)it * BM, c0 = (int64_t)jt * BN;
       const int64_t t0 = sm.off[g];
       // group g's blocks: data [n or k][mp], scales [mp / 128][n or k] words

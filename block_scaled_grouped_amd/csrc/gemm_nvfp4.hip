@@ -23,12 +23,16 @@
 // 4 x 4 MFMA blocks of 32 x 32 (256 accumulator registers per lane).  LDS holds
 // two stages of fp16 rows (128 bytes per row per K-step) with an XOR chunk
 // swizzle that keeps both the row-wise stores and the fragment reads free of
-// bank conflicts.  Thread t decodes row t of both operand tiles: the raw E2M1
-// bytes and E4M3 scales of K-step k + 1 are decoded into the other stage in
-// four pieces placed between the MFMAs of step k, and the raw bytes of step
-// k + 2 are already being loaded.  One barrier per K-step, placed before the
+// bank conflicts.  Waves 0-1 decode A and waves 2-3 B, thread t rows t % 128
+// and t % 128 + 128 of its operand: the raw E2M1 bytes and E4M3 scales of
+// K-step k + 1 are decoded into the other stage, one fp16 pair at a time,
+// between the MFMAs of step k, and the raw bytes of step k + 2 are already
+// being loaded.  One barrier per K-step, placed before the
 // last MFMAs so that the next step's first fragments are read under them.  B is
 // the MFMA's first operand, so each lane holds an output row (see store_tile.h).
+// Tiles are handed out XCD-aware in 4 x 8 blocks of one group, as in the MXFP8
+// GEMM, so the operand rows that the 32 workgroups of an XCD stream meet in its
+// L2.
 #include <utility>
 
 #include "store_tile.h"
@@ -52,6 +56,7 @@ constexpr int BK = 64;          // elements per K-step (32 bytes of E2M1 per row
 constexpr int kThreads = 256;
 constexpr int kDecodeSlots = 48; // the next step's decode is spread over MFMA slots 0 .. 47
 constexpr int kBarrierSlot = 4;  // MFMA slot of the last substep after which the step barriers
+constexpr int kSuperM = 4, kSuperN = 8;  // tile block one XCD works on
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
@@ -93,13 +98,17 @@ struct Smem {
   int32_t pre[kMaxGroups + 1];
 };
 
-// LDS byte offset of 16-byte chunk c (fp16 elements 8 c .. 8 c + 7) of row r.
-// The XOR term takes 8 distinct values over any 8 consecutive rows, and
-// (row % 2, term) 16 distinct values over any 16, so a 16-byte access by lanes
-// of consecutive rows and one chunk is conflict-free whether the LDS serves 8
+// LDS byte offset of 16-byte chunk c (fp16 elements 8 c .. 8 c + 7) of row r:
+// the chunk is XORed with a 3-bit term of r % 16.  Over 8 aligned rows the term
+// takes 8 values (as over the even and the odd rows of 16 aligned ones), and its
+// low two bits 4 values over 4 aligned rows (as over the even and the odd rows
+// of 8 aligned ones), so both 16-byte access patterns used here -- one chunk of
+// 64 consecutive rows (fragment reads), and chunks q and q + 4 of 32 rows by
+// lane pairs (decode stores) -- are conflict-free whether the LDS serves 8
 // lanes per 128-byte bank window or 16 lanes per 256-byte window.
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * 128 + ((chunk ^ ((row >> 1) & 7) ^ ((row & 1) << 2)) << 4);
+  const int term = (row & 3) ^ (((row >> 2) & 1) * 5) ^ ((row >> 3) & 1);
+  return row * 128 + ((chunk ^ term) << 4);
 }
 
 __device__ __forceinline__ v4i lds_read16(uint32_t addr) {
@@ -117,27 +126,29 @@ __device__ __forceinline__ uint32_t dq_pair(uint32_t w, v2h sd2) {
   return __builtin_bit_cast(uint32_t, f * sd2);
 }
 
-// E4M3 codes in bytes 2 HI and 2 HI + 1 of c as fp16 (exact: every E4M3 value
-// is a normal fp16; a unit scale leaves the value as it is).
-template <bool HI>
+// E4M3 codes in bytes 0 and 1 of c as fp16 (exact: every E4M3 value is a
+// normal fp16; a unit scale leaves the value as it is).
 __device__ __forceinline__ v2h e4m3_pair_h2(uint32_t c) {
-  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c, 1.0f, HI);
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c, 1.0f, false);
 }
 
 // Per-lane LDS offsets, computed once per tile and kept opaque so that the
 // compiler does not materialize one address per access.
 struct Offs {
-  int dec[8];       // chunk c of this thread's first decoded row (tid % 128 of A or B)
+  int dec[4];       // chunk 4 hf + q of this thread's first decoded row (see Raw)
   int fa[4], fb[4]; // fragment part S: row wm*128 + r (A) / wn*128 + r (B), chunk 2 S + h
+  int ssh;          // 16 hf: this thread's scale bytes within a row's scale word
 };
 
 __device__ __forceinline__ Offs make_offs(int tid, int wm, int wn, int r, int h) {
   Offs o;
+  const int hf = tid & 1, r0 = (tid & 127) >> 1;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    o.dec[c] = (tid >= 128 ? kOperandB : 0) + swz(tid & 127, c);
-    asm volatile("" : "+v"(o.dec[c]));
+  for (int q = 0; q < 4; ++q) {
+    o.dec[q] = (tid >= 128 ? kOperandB : 0) + swz(r0, 4 * hf + q);
+    asm volatile("" : "+v"(o.dec[q]));
   }
+  o.ssh = 16 * hf;
 #pragma unroll
   for (int S = 0; S < 4; ++S) {
     o.fa[S] = swz(wm * 128 + r, 2 * S + h);
@@ -149,9 +160,8 @@ __device__ __forceinline__ Offs make_offs(int tid, int wm, int wn, int r, int h)
 }
 
 // 16 raw bytes (32 elements, two 16-element blocks with scales s0, s1) -> 32
-// fp16, written as four 16-byte chunks c0 .. c0 + 3 of a row at `base`
-// relative to this thread's first row.
-template <int C0>
+// fp16, written as this thread's four 16-byte chunks of a row at `base`
+// relative to its first row.
 __device__ __forceinline__ void decode_store(uint32_t base, const Offs& o, const v4i& d, v2h s0,
                                              v2h s1) {
 #pragma unroll
@@ -163,15 +173,22 @@ __device__ __forceinline__ void decode_store(uint32_t base, const Offs& o, const
     v[1] = (int)dq_pair<1>(w, sd);
     v[2] = (int)dq_pair<2>(w, sd);
     v[3] = (int)dq_pair<3>(w, sd);
-    lds_write16(base + o.dec[C0 + q], v);
+    lds_write16(base + o.dec[q], v);
   }
 }
 
-// Raw bytes of one K-step for this thread's two rows (r0 = tid % 128 and
-// r0 + 128 of A for tid < 128, of B otherwise).
+// Raw E2M1 bytes of one K-step for this thread: waves 0 and 1 decode A,
+// waves 2 and 3 B; with u = tid % 128, half hf = u % 2 (16 of the row's 32
+// bytes) of rows u / 2 + 64 j, j = 0 .. 3.  The two threads of a row sit in
+// adjacent lanes, so each load instruction reaches 32 rows, not 64.
 struct Raw {
-  v4i d[2][2];  // [row][half]
-  int s[2];     // the row's four E4M3 block scales
+  v4i d[4];
+};
+
+// E4M3 block-scale words of two K-steps (kt, kt + 1; kt even) for the same
+// four rows: word x of step kt, y of kt + 1, four scales each.
+struct Scl {
+  v2i s[4];
 };
 
 struct TileDesc {
@@ -193,51 +210,69 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
                                            0x00020000);
 }
 
-// Thread t loads its two rows for K-step kt: 32 bytes of E2M1 and 4 scale
-// bytes each.  Rows past the valid ones, and steps past the last (`live`
-// false), read as zeros.
+// This thread's raw bytes of K-step kt.  Rows past the valid ones, and steps
+// past the last (`live` false), read as zeros.
 __device__ __forceinline__ void load_raw(const TileDesc& t, const Rsrc& rs, int kt, bool live,
                                          int tid, Raw& x) {
-  const int r0 = tid & 127;
-  const int od = r0 * (int)t.lda + kt * (BK / 2);
-  const int os = r0 * (int)t.ldas + kt * (BK / 16);
-  const int od1 = od + 128 * (int)t.lda, os1 = os + 128 * (int)t.ldas;
-  x.d[0][0] = __builtin_amdgcn_raw_buffer_load_b128(live ? rs.d : rs.none, od, 0, 0);
-  x.d[0][1] = __builtin_amdgcn_raw_buffer_load_b128(live ? rs.d : rs.none, od + 16, 0, 0);
-  x.d[1][0] = __builtin_amdgcn_raw_buffer_load_b128(live ? rs.d : rs.none, od1, 0, 0);
-  x.d[1][1] = __builtin_amdgcn_raw_buffer_load_b128(live ? rs.d : rs.none, od1 + 16, 0, 0);
-  x.s[0] = __builtin_amdgcn_raw_buffer_load_b32(live ? rs.s : rs.none, os, 0, 0);
-  x.s[1] = __builtin_amdgcn_raw_buffer_load_b32(live ? rs.s : rs.none, os1, 0, 0);
+  const int od = ((tid & 127) >> 1) * (int)t.lda + (tid & 1) * 16 + kt * (BK / 2);
+  const int rstep = 64 * (int)t.lda;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    x.d[j] = __builtin_amdgcn_raw_buffer_load_b128(live ? rs.d : rs.none, od + j * rstep, 0, 0);
 }
 
-// Piece P (0: first row elements 0..31, 1: its 32..63, 2 and 3: the same of
-// the second row, 128 rows further) of this thread's decode of one K-step
-// into the stage at `st`.
-template <int P>
-__device__ __forceinline__ void decode_piece(uint32_t st, const Offs& o, const Raw& x) {
-  constexpr int row = P >> 1, half = P & 1;
-  const v2h s01 = e4m3_pair_h2<half>((uint32_t)x.s[row]);
-  decode_store<4 * half>(st + row * 128 * 128, o, x.d[row][half], v2h{s01[0], s01[0]},
-                         v2h{s01[1], s01[1]});
+// The scale words of K-steps kt and kt + 1 (kt even) for this thread's rows;
+// both threads of a row load the same bytes, one request.  With an even step
+// count (PAIRED) a row's two words are one aligned 8-byte load; otherwise
+// each is loaded on its own and a step past the last reads as zero.
+template <bool PAIRED>
+__device__ __forceinline__ void load_scales(const TileDesc& t, const Rsrc& rs, int kt, int nk,
+                                            int tid, Scl& x) {
+  const int os = ((tid & 127) >> 1) * (int)t.ldas + kt * (BK / 16);
+  const int rstep = 64 * (int)t.ldas;
+  const bool l0 = kt < nk, l1 = kt + 1 < nk;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (PAIRED) {
+      x.s[j] = __builtin_amdgcn_raw_buffer_load_b64(l0 ? rs.s : rs.none, os + j * rstep, 0, 0);
+    } else {
+      x.s[j][0] = __builtin_amdgcn_raw_buffer_load_b32(l0 ? rs.s : rs.none, os + j * rstep, 0, 0);
+      x.s[j][1] =
+          __builtin_amdgcn_raw_buffer_load_b32(l1 ? rs.s : rs.none, os + j * rstep + 4, 0, 0);
+    }
+  }
 }
 
-// Decode unit U (0..63) of a K-step: piece U / 16 (as decode_piece), word
+// This thread's two block scales of row j in scale word w, as fp16.
+__device__ __forceinline__ v2h row_scales(uint32_t w, const Offs& o) {
+  return e4m3_pair_h2(w >> o.ssh);
+}
+
+// Row J of this thread's decode of one K-step (scale words in `sw`) into the
+// stage at `st`.
+template <int J>
+__device__ __forceinline__ void decode_row(uint32_t st, const Offs& o, const Raw& x,
+                                           const uint32_t (&sw)[4]) {
+  const v2h s01 = row_scales(sw[J], o);
+  decode_store(st + J * 64 * 128, o, x.d[J], v2h{s01[0], s01[0]}, v2h{s01[1], s01[1]});
+}
+
+// Decode unit U (0..63) of a K-step: row U / 16 (as decode_row), word
 // (U / 4) % 4 of its 16 raw bytes, nibble pair U % 4 -> one fp16 pair into
 // `buf`; the fourth pair of a word writes the 16-byte chunk to LDS.  Spread one
 // or two per MFMA slot, the decode's VALU work runs under the MFMAs.
 template <int U>
-__device__ __forceinline__ void decode_unit(uint32_t st, const Offs& o, const Raw& x, v2h (&sd)[2],
-                                            v4i& buf) {
-  constexpr int P = U / 16, q = (U / 4) % 4, pr = U % 4;
-  constexpr int row = P >> 1, half = P & 1;
+__device__ __forceinline__ void decode_unit(uint32_t st, const Offs& o, const Raw& x,
+                                            const uint32_t (&sw)[4], v2h (&sd)[2], v4i& buf) {
+  constexpr int J = U / 16, q = (U / 4) % 4, pr = U % 4;
   if constexpr (U % 16 == 0) {
-    const v2h s01 = e4m3_pair_h2<half>((uint32_t)x.s[row]);
+    const v2h s01 = row_scales(sw[J], o);
     sd[0] = v2h{s01[0], s01[0]};
     sd[1] = v2h{s01[1], s01[1]};
   }
-  const uint32_t w = (uint32_t)x.d[row][half][q];
+  const uint32_t w = (uint32_t)x.d[J][q];
   buf[pr] = (int)dq_pair<pr>(w, q < 2 ? sd[0] : sd[1]);
-  if constexpr (pr == 3) lds_write16(st + row * 128 * 128 + o.dec[4 * half + q], buf);
+  if constexpr (pr == 3) lds_write16(st + J * 64 * 128 + o.dec[q], buf);
 }
 
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
@@ -264,15 +299,19 @@ __device__ __forceinline__ void mfma(const v8h (&fa)[4], const v8h (&fb)[4], v16
 }
 
 // One K-step from stage `cur` (its substep-0 fragments already in f0): while
-// its 64 MFMAs run, decode the raw bytes of the next step (xn) into stage
-// `nxt`, load the raw bytes of the step after it (into xl), read each next
-// substep's fragments, and after the barrier the next step's first fragments.
+// its 64 MFMAs run, decode the raw bytes of the next step (xn, scale words sw)
+// into stage `nxt`, load the raw bytes of the step after it (into xl) and, for
+// an even step (SCALES), the scale words of that step and the next (into sl),
+// read each next substep's fragments, and after the barrier the next step's
+// first fragments.
+template <bool SCALES, bool PAIRED>
 __device__ __forceinline__ void k_step(uint32_t cur, uint32_t nxt, const TileDesc& t,
                                        const Rsrc& rs, int kt, int nk, int tid, const Offs& o,
-                                       const Raw& xn, Raw& xl, v8h (&f0a)[4],
-                                       v8h (&f0b)[4], v8h (&f1a)[4], v8h (&f1b)[4],
-                                       v16f (&acc)[4][4]) {
+                                       const Raw& xn, const uint32_t (&sw)[4], Raw& xl, Scl& sl,
+                                       v8h (&f0a)[4], v8h (&f0b)[4], v8h (&f1a)[4],
+                                       v8h (&f1b)[4], v16f (&acc)[4][4]) {
   load_raw(t, rs, kt + 2, kt + 2 < nk, tid, xl);
+  if constexpr (SCALES) load_scales<PAIRED>(t, rs, kt + 2, nk, tid, sl);
   v2h sd[2];
   v4i buf;
   static_for<4>([&](auto sc) {
@@ -292,7 +331,7 @@ __device__ __forceinline__ void k_step(uint32_t cur, uint32_t nxt, const TileDes
       constexpr int u1 = ((slot + 1) * 64 + kDecodeSlots - 1) / kDecodeSlots;
       if constexpr (slot < kDecodeSlots) {
         static_for<(u1 < 64 ? u1 : 64) - u0>([&](auto uc) {
-          decode_unit<u0 + decltype(uc)::value>(nxt, o, xn, sd, buf);
+          decode_unit<u0 + decltype(uc)::value>(nxt, o, xn, sw, sd, buf);
         });
       }
       if constexpr (S == 3 && m == kBarrierSlot) {
@@ -305,6 +344,7 @@ __device__ __forceinline__ void k_step(uint32_t cur, uint32_t nxt, const TileDes
   });
 }
 
+template <bool PAIRED>
 __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
   __shared__ Smem sm;
   const int G = p.G;
@@ -323,7 +363,8 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
   const uint32_t st0 = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)sm.stage[0];
   const uint32_t st1 = st0 + kHalfStage;
 
-  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+  const int slot = xcd_slot();
+  for (int tile = slot; tile < total; tile += gridDim.x) {
     // opaque per-tile copy of the thread index: keeps the compiler from
     // hoisting every LDS / global offset of the tile body out of the tile loop
     int tid = tid0;
@@ -336,10 +377,10 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
     const int local = tile - sm.pre[g];
     const int64_t m = group_extent(sm.off, g);
     const int64_t ng = p.tab.n[g];
-    const int64_t mtiles = (m + BM - 1) / BM;
-    const int64_t mt = local % mtiles, nt = local / mtiles;
-    const int64_t row0 = sm.off[g] + mt * BM;
-    const int64_t n0 = nt * BN;
+    int mt, nt;
+    super_tile<kSuperM, kSuperN>(local, (int)((m + BM - 1) / BM), (int)((ng + BN - 1) / BN), mt, nt);
+    const int64_t row0 = sm.off[g] + (int64_t)mt * BM;
+    const int64_t n0 = (int64_t)nt * BN;
     const int64_t brow0 = p.tab.brow[g] + n0;
     TileDesc t;
     t.lda = p.k / 2;
@@ -375,15 +416,28 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
     {
       const Offs o = make_offs(tid, wm, wn, r, h);
       Raw x0, x1;
+      Scl sc0, sc1;  // scale words of steps (kt, kt + 1) and (kt + 2, kt + 3)
       v8h f0a[4], f0b[4], f1a[4], f1b[4];
+      load_scales<PAIRED>(t, rs, 0, nk, tid, sc0);
       load_raw(t, rs, 0, true, tid, x0);
       load_raw(t, rs, 1, 1 < nk, tid, x1);
-      static_for<4>([&](auto pc) { decode_piece<decltype(pc)::value>(st0, o, x0); });
+      {
+        const uint32_t sw[4] = {(uint32_t)sc0.s[0][0], (uint32_t)sc0.s[1][0],
+                                (uint32_t)sc0.s[2][0], (uint32_t)sc0.s[3][0]};
+        static_for<4>([&](auto jc) { decode_row<decltype(jc)::value>(st0, o, x0, sw); });
+      }
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       read_frags<0>(st0, o, f0a, f0b);
       for (int kt = 0; kt < nk2; kt += 2) {
-        k_step(st0, st1, t, rs, kt, nk, tid, o, x1, x0, f0a, f0b, f1a, f1b, acc);
-        k_step(st1, st0, t, rs, kt + 1, nk, tid, o, x0, x1, f0a, f0b, f1a, f1b, acc);
+        const uint32_t swa[4] = {(uint32_t)sc0.s[0][1], (uint32_t)sc0.s[1][1],
+                                 (uint32_t)sc0.s[2][1], (uint32_t)sc0.s[3][1]};
+        k_step<true, PAIRED>(st0, st1, t, rs, kt, nk, tid, o, x1, swa, x0, sc1, f0a, f0b, f1a,
+                             f1b, acc);
+        const uint32_t swb[4] = {(uint32_t)sc1.s[0][0], (uint32_t)sc1.s[1][0],
+                                 (uint32_t)sc1.s[2][0], (uint32_t)sc1.s[3][0]};
+        k_step<false, PAIRED>(st1, st0, t, rs, kt + 1, nk, tid, o, x0, swb, x1, sc1, f0a, f0b,
+                              f1a, f1b, acc);
+        sc0 = sc1;
       }
     }
 
@@ -478,7 +532,11 @@ hipError_t launch_gemm_nvfp4(int G, const uint8_t* a, const uint8_t* a_scales,
   int64_t grid = device_cu_count();
   if (bound < grid) grid = bound;
   if (grid > 0) {
-    hipLaunchKernelGGL(nv_gemm_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+    // an even step count keeps each row's scale words of a step pair 8-aligned
+    if ((k / BK) % 2 == 0)
+      hipLaunchKernelGGL(nv_gemm_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL(nv_gemm_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
