@@ -14,7 +14,11 @@ namespace bsg {
 // (kDropped), which drops it the same way, without a branch.
 //   WIDE, bf16 (row stride and out_cols multiples of 8): the two lanes of a row
 //     trade halves with v_permlane32_swap so that lane h holds columns
-//     16 h .. 16 h + 15 of the block, stored as two 16-byte pieces.
+//     16 h .. 16 h + 15 of the block as two 16-byte pieces; v_permlane16_swap
+//     then regroups the pieces so that each of the two stores covers 16 whole
+//     64-byte block rows (lane L: row L % 16, columns 8 (L / 16) .. + 7, and
+//     the same 16 rows further) rather than half of each of the 32 rows,
+//     which halves the cache lines every store instruction touches.
 //   WIDE, f32 (multiples of 4): each run of four columns is one 16-byte store.
 //   Otherwise: one store per element.
 constexpr uint32_t kDropped = 0xfffffff0u;
@@ -41,12 +45,25 @@ __device__ __forceinline__ void store_block(const v16f& acc, __amdgpu_buffer_rsr
       d[k] = sw[0];
       d[4 + k] = sw[1];
     }
-    const int col = col0 - 4 * h + 16 * h;
-    const int base = row * ldc + col;
-    const int off0 = col < out_cols ? base * esz : (int)kDropped;
-    const int off1 = col + 8 < out_cols ? (base + 8) * esz : (int)kDropped;
-    __builtin_amdgcn_raw_buffer_store_b128((v4i){d[0], d[1], d[4], d[5]}, ro, off0, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b128((v4i){d[2], d[3], d[6], d[7]}, ro, off1, 0, 0);
+    // x: columns 16 h .. + 7 of row r, y: 16 h + 8 .. + 15.  After the swap of
+    // x's odd 16-lane groups with y's even ones, lane L holds in x piece L / 16
+    // of block row L % 16, in y the same piece of block row 16 + L % 16.
+    int x[4] = {d[0], d[1], d[4], d[5]}, y[4] = {d[2], d[3], d[6], d[7]};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const auto sw = __builtin_amdgcn_permlane16_swap(x[k], y[k], false, false);
+      x[k] = sw[0];
+      y[k] = sw[1];
+    }
+    const int lane = threadIdx.x & 63;
+    const int rowx = row - (lane & 31) + (lane & 15);
+    const int col = col0 - 4 * h + 8 * (lane >> 4);
+    const int base = rowx * ldc + col;
+    const bool live = col < out_cols;
+    const int offx = live ? base * esz : (int)kDropped;
+    const int offy = live ? (base + 16 * ldc) * esz : (int)kDropped;
+    __builtin_amdgcn_raw_buffer_store_b128((v4i){x[0], x[1], x[2], x[3]}, ro, offx, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128((v4i){y[0], y[1], y[2], y[3]}, ro, offy, 0, 0);
   } else {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
