@@ -274,16 +274,30 @@ def summarize(case, t, mfma_dtype):
 
 # ---------------------------------------------------------------- CPU baseline (the oracle)
 
+def code_sha256(paths):
+    """sha256 of source files' code: every line with its // comment and
+    surrounding whitespace removed, blank lines dropped, files in the given
+    order, so that editing a comment keeps the hash and editing code changes it."""
+    import hashlib
+    lines = []
+    for path in paths:
+        for line in open(path, encoding="utf-8"):
+            code = line.split("//", 1)[0].strip()
+            if code:
+                lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
+
+
 def gemm_traffic():
     """Counter-measured HBM bytes of one fprop GEMM launch, or None when no
-    record exists or the kernel source has changed since it was taken."""
-    import hashlib
+    record exists or the kernel's code (its source and the local headers it
+    includes) has changed since it was taken."""
     try:
         rec = json.load(open(TRAFFIC_RECORD))
-        src = open(os.path.join(ROOT, rec["kernel_source"]), "rb").read()
+        sha = code_sha256([os.path.join(ROOT, f) for f in rec["kernel_sources"]])
     except (OSError, ValueError, KeyError):
         return None
-    if hashlib.sha256(src).hexdigest() != rec.get("kernel_source_sha256"):
+    if sha != rec.get("kernel_code_sha256"):
         return None
     return int(rec["traffic_bytes"])
 

@@ -18,11 +18,13 @@
 // in a 2 x 2 grid, each owning 128 x 128 of the output as 4 x 4 MFMA blocks of
 // 32 x 32 (256 accumulator registers per lane).
 //
-// Operands go global -> LDS by the buffer unit directly (LDS-DMA: lane l of a
-// load lands at LDS base + 16 l, so a swizzled layout is made by permuting each
-// lane's source address).  An LDS buffer holds two K-steps: 128-byte rows, so
-// every copy request is one whole 128-byte line, plus the one scale dword per
-// row that covers those 128 K.  Two buffers: while pair p is consumed from one,
+// A and the scales go global -> LDS by the buffer unit directly (LDS-DMA: lane
+// l of a load lands at LDS base + 16 l, so a swizzled layout is made by
+// permuting each lane's source address); B goes through registers (ordinary
+// buffer loads issued a pair ahead, each written to its swizzled LDS slot one
+// K-step later), which splits a CU's copy work between the two paths.  An LDS
+// buffer holds two K-steps: 128-byte rows, so every copy request is one whole
+// 128-byte line, plus the one scale dword per row that covers those 128 K.  Two buffers: while pair p is consumed from one,
 // pair p + 1 lands in the other, and the copies of pair p + 2 are issued as soon
 // as pair p's last fragments are in registers.  16-byte chunk c of row r sits
 // in slot c ^ ((r / 2) % 8), which spreads the MFMA fragment reads (32 rows,
