@@ -86,6 +86,12 @@ __device__ __forceinline__ uint2 cvt8(uint4 v, float scale) {
 // lanes form one 32-element block (amax by two xor-shuffles); sixteen lanes
 // form one 128-element stretch whose four scale bytes are written as one
 // dword in the b0, b2, b1, b3 order.
+//
+// The scale words of 32 consecutive rows share one 128-byte line of the
+// [NQ][rows_cap] array, and workgroup b runs on XCD b % 8, each XCD with its
+// own L2.  Workgroups are renumbered so that every XCD takes runs of 32 whole
+// rows: each scale line is then completed in a single L2 and written back
+// once, not as up to 8 partial lines.
 constexpr int kRowChunk = 1024;
 
 __global__ __launch_bounds__(256) void mx_rowwise_kernel(const uint16_t* __restrict__ x,
@@ -102,7 +108,14 @@ __global__ __launch_bounds__(256) void mx_rowwise_kernel(const uint16_t* __restr
   }
   const int lane = threadIdx.x & 63;
   const int64_t chunks = (cols + kRowChunk - 1) / kRowChunk;
-  const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t run = 8 * chunks;  // workgroups (4 units each) per 32 rows
+  const int64_t full = (int64_t)gridDim.x / (kXcds * run) * (kXcds * run);
+  int64_t wg = blockIdx.x;
+  if (wg < full) {  // a permutation of [0, full); the tail keeps its order
+    const int64_t xcd = wg % kXcds, idx = wg / kXcds;
+    wg = ((idx / run) * kXcds + xcd) * run + idx % run;
+  }
+  const int64_t unit = wg * 4 + (threadIdx.x >> 6);
   const int64_t row = unit / chunks;
   if (row >= live) return;
   const int64_t base = (unit % chunks) * kRowChunk;
