@@ -117,3 +117,38 @@ def nvfp4_rowscaled_fprop(a_packed, a_bscales, a_tsi, offsets, b_packed, b_bscal
             np.asarray(b_tsi, np.float64)[boff[g]:boff[g + 1]][None, :]
         result.append((sel, y))
     return result
+
+
+def nvfp4_rowscaled_wgrad(dy_col, dy_bscales, dy_outer, x_col, x_bscales, x_outer,
+                          padded_offsets, n, k, groups=None, out_rows=None):
+    """Row-scaled NVFP4 WGRAD (NT, contraction over each expert's ragged
+    tokens), from the columnwise copies of ``quantize.nvfp4_rowscaled_colwise``
+    ("[Common][PyTorch] Add row-scaled NVFP4 support to grouped-tensor GEMM":
+    the outer scales are neutralized in the GEMM and applied afterwards per
+    expert -- the discrete-out wgrad path -- over each expert's own rows and
+    columns):
+        S[g, i, j]  = sum_{t < m~_g} (e2m1 * sd)(dY^T_g)[i, t] * (e2m1 * sd)(X^T_g)[j, t]
+        dW[g, i, j] = S[g, i, j] * tsi_dY[g, i] * tsi_X[g, j]
+    Padding tokens encode to zero, so the sum over m~_g equals the sum over the
+    expert's m_g tokens; an empty expert gives dW[g] = 0.  ``groups`` /
+    ``out_rows`` optionally restrict the computed experts / rows i.  Returns
+    float64 [len(groups), len(out_rows), k]."""
+    poff = np.asarray(padded_offsets, dtype=np.int64)
+    G = len(poff) - 1
+    groups = list(range(G)) if groups is None else list(groups)
+    out_rows = np.arange(n) if out_rows is None else np.asarray(out_rows, dtype=np.int64)
+    dy_outer = np.asarray(dy_outer, dtype=np.float64).reshape(G, n)
+    x_outer = np.asarray(x_outer, dtype=np.float64).reshape(G, k)
+    out = np.zeros((len(groups), len(out_rows), k), dtype=np.float64)
+    for gi, g in enumerate(groups):
+        mp = int(poff[g + 1] - poff[g])
+        if mp == 0:
+            continue
+        a = np.asarray(dy_col[poff[g] * n // 2:poff[g + 1] * n // 2]).reshape(n, mp // 2)[out_rows]
+        a_s = np.asarray(dy_bscales[poff[g] * n // 16:poff[g + 1] * n // 16]
+                         ).reshape(n, mp // 16)[out_rows]
+        b = np.asarray(x_col[poff[g] * k // 2:poff[g + 1] * k // 2]).reshape(k, mp // 2)
+        b_s = np.asarray(x_bscales[poff[g] * k // 16:poff[g + 1] * k // 16]).reshape(k, mp // 16)
+        s = nvfp4_block_dequant(a, a_s, mp) @ nvfp4_block_dequant(b, b_s, mp).T
+        out[gi] = s * dy_outer[g][out_rows][:, None] * x_outer[g][None, :]
+    return out

@@ -146,6 +146,52 @@ def nvfp4_rowscaled(x_bits, offsets):
     return fp4_pack(q), s8, tsi.astype(np.float32)
 
 
+def nvfp4_rowscaled_colwise(x_bits, offsets, padded_offsets):
+    """Columnwise (transposed) row-scaled NVFP4 quantize for a contraction over
+    ragged token rows (wgrad).  "[Common][PyTorch] Add row-scaled NVFP4 support
+    to grouped-tensor GEMM" lifts the ban on columnwise use of row-scaled
+    grouped tensors so that wgrad can consume the transpose, with the
+    columnwise amax sized per column and split per expert.
+
+    Reading: per group g, the transposed block X_g^T [C, m~_g] -- tokens padded
+    with zeros to m~_g, a multiple of 128, as for the MXFP8 columnwise copies --
+    is quantized row by row exactly as ``nvfp4_rowscaled`` quantizes rows, so
+    column c of group g gets its own outer scale tsi[g, c] = (largest |x| over
+    the group's tokens) / 2688 and 16-token blocks with E4M3 scales.
+
+    Layout: group g's packed E2M1 data is a row-major [C, m~_g / 2] block at
+    byte offset padded_offsets[g] * C / 2 (token 2j in the low nibble of byte
+    j), its E4M3 block scales a row-major [C, m~_g / 16] block at
+    padded_offsets[g] * C / 16, and the outer scales an f32 [G, C] array (0 for
+    an empty group).  Returns (data, block_scales, outer)."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    rows, cols = x_bits.shape
+    if cols % MX_BLOCK:
+        raise ValueError("cols must be a multiple of 32")
+    off = np.asarray(offsets, dtype=np.int64)
+    poff = np.asarray(padded_offsets, dtype=np.int64)
+    G = len(off) - 1
+    if int(off[-1]) > rows:
+        raise ValueError("sum of group sizes exceeds the row capacity")
+    data = np.zeros(int(poff[-1]) * cols // 2, dtype=np.uint8)
+    bscales = np.zeros(int(poff[-1]) * cols // NVFP4_BLOCK, dtype=np.uint8)
+    outer = np.zeros((G, cols), dtype=np.float32)
+    for g in range(G):
+        m = int(off[g + 1] - off[g])
+        mp = int(poff[g + 1] - poff[g])
+        if mp < m or mp % COLWISE_PAD:
+            raise ValueError("padded offsets inconsistent with the group sizes")
+        if mp == 0:
+            continue
+        xt = np.zeros((cols, mp), dtype=np.uint16)              # +0.0 padding
+        xt[:, :m] = x_bits[off[g]:off[g + 1]].T
+        packed, s8, tsi = nvfp4_rowscaled(xt, np.array([0, cols]))
+        data[poff[g] * cols // 2:poff[g + 1] * cols // 2] = packed.reshape(-1)
+        bscales[poff[g] * cols // NVFP4_BLOCK:poff[g + 1] * cols // NVFP4_BLOCK] = s8.reshape(-1)
+        outer[g] = tsi
+    return data, bscales, outer
+
+
 def nvfp4_block_dequant(packed, block_scales, cols):
     """E2M1 element times its decoded E4M3 block scale (no outer scale)."""
     q = fp4_unpack(np.asarray(packed).reshape(-1, cols // 2))

@@ -148,3 +148,54 @@ def test_nvfp4_exact_on_lossless_inputs_and_widths():
         assert np.allclose(y, want, rtol=1e-14, atol=0)
         # and this is the raw product within float32 rounding of the outer scales
         assert np.allclose(y, xv[rows] @ wv[boff[g]:boff[g + 1]].T, rtol=1e-6, atol=1e-9)
+
+
+def test_nvfp4_wgrad_exact_on_lossless_inputs():
+    """Values on the E2M1 grid times a per-column power of two 2^-e_c, with a
+    +-6 * 2^-e_c in every 16-token block of every column of every expert: then
+    S = 448 * 2^e_c, every block scale is 448, enc = 2^e_c and the codes are the
+    grid values, so quantization is lossless and dW must equal the exact
+    per-expert product of the raw inputs.  The per-column powers make every
+    column's outer scale different (an outer scale taken by the wrong index, or
+    a transposed operand, fails); the experts' token counts are not multiples of
+    16 (padding must encode to zero) and one expert is empty (dW = 0)."""
+    rng = np.random.default_rng(25)
+    grid = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -.5, -1, -1.5, -2, -3, -4, -6])
+    sizes = np.array([21, 0, 40, 3], np.int32)
+    M, N, K = int(sizes.sum()), 32, 64
+    _, off = O.group_offsets(sizes)
+    _, poff = O.group_offsets(sizes, pad_to=128)
+
+    def mk(cols):
+        v = rng.choice(grid, (M, cols))
+        for g in range(len(sizes)):
+            v[off[g]:off[g + 1]:16] = rng.choice([6.0, -6.0], v[off[g]:off[g + 1]:16].shape)
+        v = v * 2.0 ** -rng.integers(0, 6, (1, cols))
+        return F.f32_to_bf16_bits_rne(v.astype(np.float32)), v
+
+    dyb, dyv = mk(N)
+    xb, xv = mk(K)
+    dyc, dys, dyo = Q.nvfp4_rowscaled_colwise(dyb, off, poff)
+    xc, xs, xo = Q.nvfp4_rowscaled_colwise(xb, off, poff)
+    for g in (0, 2, 3):
+        m = int(sizes[g])
+        ns = dys[poff[g] * N // 16:poff[g + 1] * N // 16].reshape(N, -1)[:, :(m + 15) // 16]
+        assert np.all(ns == 0x7E)
+    assert len(set(np.round(np.log2(dyo[0] * 2688 / 6)))) > 1
+    dw = GM.nvfp4_rowscaled_wgrad(dyc, dys, dyo, xc, xs, xo, poff, N, K)
+    for g in range(len(sizes)):
+        want = dyv[off[g]:off[g + 1]].T @ xv[off[g]:off[g + 1]]
+        # the outer scales are float32 roundings of amax / 2688
+        assert np.allclose(dw[g], want, rtol=2e-7, atol=0), g
+    assert np.all(dw[1] == 0)
+    # exact once the float32 outer scales are divided back out
+    g = 2
+    s = dw[g] / dyo[g].astype(np.float64)[:, None] / xo[g].astype(np.float64)[None, :]
+    exact = (dyv[off[g]:off[g + 1]].T @ xv[off[g]:off[g + 1]]) * 448.0 * 448.0 * \
+        (6.0 / (np.abs(dyv[off[g]:off[g + 1]]).max(axis=0)))[:, None] * \
+        (6.0 / (np.abs(xv[off[g]:off[g + 1]]).max(axis=0)))[None, :]
+    assert np.allclose(s, exact, rtol=1e-12, atol=0)
+    # restricted evaluation agrees with the full one
+    part = GM.nvfp4_rowscaled_wgrad(dyc, dys, dyo, xc, xs, xo, poff, N, K, groups=[3, 0],
+                                    out_rows=[5, 1])
+    assert np.array_equal(part[0], dw[3][[5, 1]]) and np.array_equal(part[1], dw[0][[5, 1]])

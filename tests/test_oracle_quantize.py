@@ -6,6 +6,7 @@ shared helpers), against the concatenation of per-expert calls, and against the
 invariants the pages state (sum of sizes vs rows)."""
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -15,6 +16,8 @@ from oracle import layout as L
 from oracle import offsets as O
 from oracle import quantize as Q
 import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
 # ---------------------------------------------------------------- offsets
@@ -37,13 +40,13 @@ def test_workload_size_invariants(name):
     _, off = O.group_offsets(w.sizes)
     assert off[-1] == np.sum(w.sizes.astype(np.int64))
     assert O.check_capacity(off, w.rows_cap)
-    if name in ("tiny", "fprop", "wgrad", "zipf"):
+    if name in ("tiny", "fprop", "wgrad", "zipf", "nvfp4_wgrad"):
         assert off[-1] == w.rows_cap
     else:
         assert off[-1] < w.rows_cap
     if name == "fprop":
         assert np.all(w.sizes % 128 == 0) and len(set(w.sizes.tolist())) > 1
-    if name == "wgrad":
+    if name in ("wgrad", "nvfp4_wgrad"):
         assert np.sum(w.sizes == 0) == 2 and np.all(w.sizes[w.sizes > 0] % 32 != 0)
     if name == "zipf":
         assert np.sum(w.sizes == 0) >= 4 and w.G == 64
@@ -238,3 +241,65 @@ def test_nvfp4_matches_slow_rederivation():
                 q = _slow_e2m1(float(f(f(blk[i]) * enc)))
                 got = (packed[r, j // 2] >> (4 * (j % 2))) & 0xF
                 assert got == q, (r, j)
+
+
+def test_nvfp4_colwise_golden_per_expert_columns():
+    """tests/golden/nvfp4_cols.txt: each expert's columns get their own outer
+    scale, blocks run along the expert's tokens, padding encodes to zero."""
+    lines = [ln.split("#")[0].split() for ln in open(os.path.join(GOLDEN, "nvfp4_cols.txt"))]
+    lines = [ln for ln in lines if ln]
+    sizes = np.array([3, 2], np.int32)
+    _, off = O.group_offsets(sizes)
+    _, poff = O.group_offsets(sizes, pad_to=128)
+    x = np.zeros((5, 32), np.float32)
+    for g, c, vals, *_ in lines:
+        v = [float(t) for t in vals.split(",")]
+        x[off[int(g)]:off[int(g)] + len(v), int(c)] = v
+    data, bsc, outer = Q.nvfp4_rowscaled_colwise(F.f32_to_bf16_bits_rne(x), off, poff)
+    assert data.shape == (256 * 32 // 2,) and bsc.shape == (256 * 32 // 16,)
+    assert outer.shape == (2, 32) and np.all(outer[:, 2:] == 0)
+    for g, c, vals, amax, s8, packed in lines:
+        g, c = int(g), int(c)
+        blk = data[poff[g] * 32 // 2:poff[g + 1] * 32 // 2].reshape(32, 64)
+        sc = bsc[poff[g] * 32 // 16:poff[g + 1] * 32 // 16].reshape(32, 8)
+        assert outer[g, c] == np.float32(np.float32(amax) / np.float32(2688))
+        assert sc[c, 0] == int(s8, 16) and np.all(sc[c, 1:] == 0)
+        want = [int(b, 16) for b in packed.split(",")]
+        assert list(blk[c, :len(want)]) == want
+        assert np.all(blk[c, len(want):] == 0)
+    # the all-zero columns: scale 0, codes 0
+    for g in range(2):
+        blk = data[poff[g] * 32 // 2:poff[g + 1] * 32 // 2].reshape(32, 64)
+        assert np.all(blk[2:] == 0)
+
+
+def test_nvfp4_colwise_dequant_within_format_error():
+    """Invariant: e2m1 * block scale * outer scale reproduces every live token
+    of every column within NVFP4's error (half an E2M1 step of the block scale
+    times the outer scale, plus the E4M3 rounding of the scale), and an empty
+    expert writes nothing."""
+    rng = np.random.default_rng(31)
+    sizes = np.array([40, 0, 17, 128], np.int32)
+    M, C = int(sizes.sum()), 64
+    x = rng.standard_normal((M, C)).astype(np.float32) * np.exp(rng.uniform(-3, 3, (1, C)))
+    xb = F.f32_to_bf16_bits_rne(x)
+    xv = F.bf16_bits_to_f64(xb)
+    _, off = O.group_offsets(sizes)
+    _, poff = O.group_offsets(sizes, pad_to=128)
+    data, bsc, outer = Q.nvfp4_rowscaled_colwise(xb, off, poff)
+    assert np.all(outer[1] == 0)
+    for g in (0, 2, 3):
+        m, mp = int(sizes[g]), int(poff[g + 1] - poff[g])
+        blk = data[poff[g] * C // 2:poff[g + 1] * C // 2].reshape(C, mp // 2)
+        sc = bsc[poff[g] * C // 16:poff[g + 1] * C // 16].reshape(C, mp // 16)
+        dq = Q.nvfp4_dequant(blk, sc, outer[g], mp)
+        ref = xv[off[g]:off[g + 1]].T
+        assert np.all(dq[:, m:] == 0)
+        amax = np.abs(ref).max(axis=1)
+        assert np.allclose(outer[g], (amax / 2688).astype(np.float32), rtol=1e-7, atol=0)
+        # per block: |err| <= 0.25 * 2 (E2M1 step at 6 is 2, half of it 1; scaled
+        # by sd * tsi ~ bmax / 6) -> |err| <= bmax / 6 plus 1/16 relative scale error
+        for b in range((m + 15) // 16):
+            seg = slice(16 * b, min(16 * b + 16, m))
+            bmax = np.abs(ref[:, seg]).max(axis=1, keepdims=True)
+            assert np.all(np.abs(dq[:, seg] - ref[:, seg]) <= bmax / 6 * 1.07 + 1e-30)

@@ -21,6 +21,9 @@ zipf   64 experts, K=7168, N=2048, 32768 rows; p_i ~ rank_i^-1.2 over a seeded
 nvfp4  8 experts, K=4096, N_e = 2048 (even e) / 4096 (odd e), 16384 live rows of
        a capacity of 18432 (dead rows hold bf16 NaN); Multinomial(16384,
        Dirichlet(2)); X ~ N(0, 1), W_e ~ N(0, 0.02)
+nvfp4_wgrad
+       the wgrad shapes and size recipe (its own seed) for the row-scaled NVFP4
+       weight gradient: dY [16384, 4096], X [16384, 4096] ~ N(0, 1)
 =====  ===========================================================================
 """
 
@@ -29,7 +32,7 @@ from typing import List, Optional
 
 import numpy as np
 
-CONFIG_NAMES = ("tiny", "fprop", "wgrad", "zipf", "nvfp4")
+CONFIG_NAMES = ("tiny", "fprop", "wgrad", "zipf", "nvfp4", "nvfp4_wgrad")
 SEED_BASE = 1000
 BF16_NAN_BITS = 0x7FC0
 
@@ -73,7 +76,7 @@ def group_sizes(name, seed=None):
         s = np.array([32, 0, 64, 32])
     elif name == "fprop":
         s = 128 * _dirichlet_multinomial(rng, 128, 8)
-    elif name == "wgrad":
+    elif name in ("wgrad", "nvfp4_wgrad"):
         empty = rng.choice(8, size=2, replace=False)
         while True:
             live = _dirichlet_multinomial(rng, 16384, 6)
@@ -103,7 +106,7 @@ def get(name, seed=None):
     if name == "fprop":
         return Workload(name, "fprop", s, 16384, 4096, 14336, seed=sd, x_outlier_p=0.01,
                         x_outlier_mul=20.0, w_std=0.02)
-    if name == "wgrad":
+    if name in ("wgrad", "nvfp4_wgrad"):
         return Workload(name, "wgrad", s, 16384, 4096, 4096, seed=sd)
     if name == "zipf":
         return Workload(name, "fprop", s, 32768, 7168, 2048, seed=sd, w_std=0.02)
