@@ -25,7 +25,8 @@ DEV_OVER_CAPACITY = 2
 DEV_BAD_PADDING = 4
 
 EXPORTS = ("bsg_last_error", "bsg_version", "group_offsets_i32_to_i64", "grouped_quantize_mxfp8",
-           "grouped_quantize_nvfp4_rowscaled", "grouped_gemm_mxfp8", "grouped_gemm_nvfp4_rowscaled")
+           "grouped_quantize_nvfp4_rowscaled", "grouped_quantize_nvfp4_rowscaled_colwise",
+           "grouped_gemm_mxfp8", "grouped_gemm_nvfp4_rowscaled")
 
 _lib = None
 
@@ -56,6 +57,9 @@ def load_library(path=LIB_PATH):
     lib.grouped_quantize_mxfp8.argtypes = [P, I64, I64, I64, P, P, P, P, I64, P, P, P, P]
     lib.grouped_quantize_nvfp4_rowscaled.restype = I32
     lib.grouped_quantize_nvfp4_rowscaled.argtypes = [P, I64, I64, I64, P, P, P, P, P, P]
+    lib.grouped_quantize_nvfp4_rowscaled_colwise.restype = I32
+    lib.grouped_quantize_nvfp4_rowscaled_colwise.argtypes = [P, I64, I64, I64, P, P, I64, P, P, P,
+                                                             P, P]
     lib.grouped_gemm_mxfp8.restype = I32
     lib.grouped_gemm_mxfp8.argtypes = [I32, I64, P, P, P, P, P, I64, I64, I64, P, I32, P, P]
     lib.grouped_gemm_nvfp4_rowscaled.restype = I32
@@ -164,6 +168,30 @@ def grouped_quantize_nvfp4_rowscaled(x, offsets, G=None, data=None, block_scales
     _check(lib.grouped_quantize_nvfp4_rowscaled(_ptr(x), rows_cap, cols, G, _ptr(offsets),
                                                 _ptr(data), _ptr(block_scales), _ptr(outer),
                                                 _ptr(status), _stream(x)))
+    return data, block_scales, outer
+
+
+def grouped_quantize_nvfp4_rowscaled_colwise(x, offsets, padded_offsets, G=None, col_rows_cap=None,
+                                             data=None, block_scales=None, outer=None, status=None):
+    """bf16 [rows_cap, cols] -> per-expert transposed copies: (E2M1 bytes
+    [col_rows_cap * cols / 2], E4M3 [col_rows_cap * cols / 16], f32 outer [G, cols]).
+    See include/bsg.h for the block layout."""
+    import torch
+    lib = load_library()
+    _need_cuda(x, offsets, padded_offsets)
+    rows_cap, cols = x.shape
+    G = offsets.numel() - 1 if G is None else G
+    if col_rows_cap is None:
+        col_rows_cap = rows_cap + BSG_COLWISE_PAD * G
+    if data is None:
+        data = torch.empty(col_rows_cap * cols // 2, dtype=torch.uint8, device=x.device)
+    if block_scales is None:
+        block_scales = torch.empty(col_rows_cap * cols // 16, dtype=torch.uint8, device=x.device)
+    if outer is None:
+        outer = torch.empty((G, cols), dtype=torch.float32, device=x.device)
+    _check(lib.grouped_quantize_nvfp4_rowscaled_colwise(
+        _ptr(x), rows_cap, cols, G, _ptr(offsets), _ptr(padded_offsets), col_rows_cap, _ptr(data),
+        _ptr(block_scales), _ptr(outer), _ptr(status), _stream(x)))
     return data, block_scales, outer
 
 

@@ -123,6 +123,34 @@ int grouped_quantize_nvfp4_rowscaled(const void* x, int64_t rows_cap, int64_t co
                     fn);
 }
 
+int grouped_quantize_nvfp4_rowscaled_colwise(const void* x, int64_t rows_cap, int64_t cols,
+                                             int64_t G, const int64_t* offsets,
+                                             const int64_t* padded_offsets, int64_t col_rows_cap,
+                                             uint8_t* data, uint8_t* block_scales, float* outer,
+                                             uint32_t* dev_status, void* stream) {
+  const char* fn = "grouped_quantize_nvfp4_rowscaled_colwise";
+  if (x == nullptr || offsets == nullptr || padded_offsets == nullptr || data == nullptr ||
+      block_scales == nullptr || outer == nullptr)
+    return fail(BSG_ERR_NULL,
+                "%s: x, offsets, padded_offsets, data, block_scales and outer must be non-NULL", fn);
+  if (G < 1 || G > BSG_MAX_GROUPS)
+    return fail(BSG_ERR_SHAPE, "%s: G=%lld outside [1, %d]", fn, (long long)G, BSG_MAX_GROUPS);
+  if (rows_cap < 0 || col_rows_cap < 0 || cols <= 0 || cols % 32 != 0)
+    return fail(BSG_ERR_SHAPE,
+                "%s: need rows_cap >= 0, col_rows_cap >= 0 and cols a positive multiple of 32", fn);
+  if (cols > 16384)
+    return fail(BSG_ERR_UNSUPPORTED, "%s: cols=%lld above the supported 16384", fn, (long long)cols);
+  if (rows_cap > 0x7fffffffLL || col_rows_cap > 0x7fffffffLL)
+    return fail(BSG_ERR_SHAPE, "%s: rows_cap or col_rows_cap too large", fn);
+  if (!aligned16(x) || !aligned16(data) || !aligned4(outer))
+    return fail(BSG_ERR_ALIGN, "%s: x and data must be 16-byte aligned, outer 4-byte", fn);
+  return hip_result(bsg::launch_quantize_nvfp4_rowscaled_colwise(
+                        static_cast<const uint16_t*>(x), rows_cap, cols, (int)G, offsets,
+                        padded_offsets, col_rows_cap, data, block_scales, outer, dev_status,
+                        (hipStream_t)stream),
+                    fn);
+}
+
 int grouped_gemm_mxfp8(int mode, int64_t G, const uint8_t* a, const uint8_t* a_scales,
                        const uint8_t* b, const uint8_t* b_scales, const int64_t* offsets,
                        int64_t rows_cap, int64_t n, int64_t k, void* out, int out_dtype,

@@ -170,6 +170,13 @@ hipError_t launch_quantize_nvfp4_rowscaled(const uint16_t* x, int64_t rows_cap, 
                                            uint8_t* block_scales, float* outer, uint32_t* status,
                                            hipStream_t stream);
 
+hipError_t launch_quantize_nvfp4_rowscaled_colwise(const uint16_t* x, int64_t rows_cap,
+                                                   int64_t cols, int G, const int64_t* offsets,
+                                                   const int64_t* padded_offsets,
+                                                   int64_t col_rows_cap, uint8_t* data,
+                                                   uint8_t* block_scales, float* outer,
+                                                   uint32_t* status, hipStream_t stream);
+
 hipError_t launch_gemm_mxfp8(int mode, int G, const uint8_t* a, const uint8_t* a_scales,
                              const uint8_t* b, const uint8_t* b_scales, const int64_t* offsets,
                              int64_t rows_cap, int64_t n, int64_t k, void* out, int out_f32,

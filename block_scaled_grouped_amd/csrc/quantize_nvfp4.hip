@@ -126,4 +126,224 @@ hipError_t launch_quantize_nvfp4_rowscaled(const uint16_t* x, int64_t rows_cap, 
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- columnwise
+//
+// Columnwise (transposed) copies for the weight gradient: "[Common][PyTorch]
+// Add row-scaled NVFP4 support to grouped-tensor GEMM" lets wgrad consume the
+// transpose of row-scaled grouped tensors, with the columnwise amax sized per
+// column and split per expert.  Per expert g the block X_g^T [C, m~_g] (tokens
+// padded with zeros to m~_g, a multiple of 128) is quantized row by row exactly
+// as the rowwise kernel above quantizes rows: column c of expert g gets the
+// outer scale amax / 2688 over the expert's tokens, 16-token blocks an E4M3
+// scale, tokens E2M1 codes.  Output: the packed [C, m~_g / 2] block at byte
+// padded_offsets[g] * C / 2, the E4M3 [C, m~_g / 16] block at
+// padded_offsets[g] * C / 16, outer scales [G, C].
+//
+// One workgroup per (expert, 64-column slab) owns its columns' amax outright,
+// so the whole quantize is one launch without atomics or workspace: a first
+// pass over the expert's tokens takes the column maxima, a second pass reads
+// the same tokens again (mostly from the L2 / last-level cache) and converts
+// them.  The second pass stages 128-token x 64-column tiles (16 KiB) in LDS
+// from registers loaded one tile ahead; thread (column pair p, 16-token block
+// b) reads its 16 tokens of the two columns as 4-byte words and writes 8 packed
+// bytes and one scale byte per column, so the 8 threads of a column write its
+// 64 bytes contiguously.
+constexpr int kNvColCols = 64;
+constexpr int kNvColTokens = 128;
+
+namespace {
+
+typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+
+// LDS byte offset of 16-byte chunk q (columns 8 q .. 8 q + 7) of tile row r:
+// the XOR with (r / 16) % 8 puts the 4-byte column-pair reads of one token of
+// eight 16-token blocks on different banks.
+__device__ __forceinline__ uint32_t nvcol_slot(int r, int q) {
+  return (uint32_t)(r * 128 + ((q ^ ((r >> 4) & 7)) << 4));
+}
+
+// This thread's four 16-byte loads of a tile (token rows tid / 8 + 32 i,
+// columns 8 (tid % 8) ..), zeros past the expert's tokens or the last column.
+__device__ __forceinline__ void nvcol_load(const uint16_t* __restrict__ x, int64_t cols,
+                                           int64_t row0, int live_rows, int64_t c0, uint4 (&v)[4]) {
+  const int tid = threadIdx.x;
+  const int64_t c = c0 + 8 * (tid & 7);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (tid >> 3) + 32 * i;
+    v[i] = make_uint4(0, 0, 0, 0);
+    if (r < live_rows && c < cols)
+      v[i] = *reinterpret_cast<const uint4*>(x + (row0 + r) * cols + c);
+  }
+}
+
+__device__ __forceinline__ uint32_t pk_mag_max(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t,
+                            __builtin_elementwise_max(__builtin_bit_cast(v2u16, a & 0x7fff7fffu),
+                                                      __builtin_bit_cast(v2u16, b & 0x7fff7fffu)));
+}
+
+// E2M1 codes of 16 tokens of one column (the bf16 in the low (HI = 0) or high
+// half of w[i]) times enc, token 2j in the low nibble of byte j.
+template <int HI, int J>
+__device__ __forceinline__ uint32_t fp4_col_pair(uint32_t r, const uint32_t (&w)[16], float enc) {
+  const float a = HI ? __uint_as_float(w[2 * J] & 0xffff0000u) : bf16_to_f32(w[2 * J] & 0xffffu);
+  const float b =
+      HI ? __uint_as_float(w[2 * J + 1] & 0xffff0000u) : bf16_to_f32(w[2 * J + 1] & 0xffffu);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, a * enc, b * enc, 1.0f, J & 3);
+}
+
+template <int HI>
+__device__ __forceinline__ uint2 fp4_pack_col16(const uint32_t (&w)[16], float enc) {
+  uint32_t lo = 0, hi = 0;
+  lo = fp4_col_pair<HI, 0>(lo, w, enc);
+  lo = fp4_col_pair<HI, 1>(lo, w, enc);
+  lo = fp4_col_pair<HI, 2>(lo, w, enc);
+  lo = fp4_col_pair<HI, 3>(lo, w, enc);
+  hi = fp4_col_pair<HI, 4>(hi, w, enc);
+  hi = fp4_col_pair<HI, 5>(hi, w, enc);
+  hi = fp4_col_pair<HI, 6>(hi, w, enc);
+  hi = fp4_col_pair<HI, 7>(hi, w, enc);
+  return make_uint2(lo, hi);
+}
+
+// Block scale byte and encode factor of a 16-token block with largest
+// magnitude bits `bm`, in the rowwise kernel's float32 steps.
+__device__ __forceinline__ void nv_block_scale(uint32_t bm, float S, uint32_t& s8, float& enc) {
+  const float bmax = bf16_to_f32(bm);
+  float sf = (bmax / 6.0f) * S;
+  sf = __builtin_fminf(sf, 448.0f);
+  s8 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sf, 0.0f, 0, false) & 0xffu;
+  const float sd = e4m3_decode_pos(s8);
+  enc = 0.0f;
+  if (sd != 0.0f) enc = __builtin_fminf(S / sd, 3.40282346638528859812e+38f);
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kNvThreads) void nvfp4_colwise_kernel(
+    const uint16_t* __restrict__ x, int64_t rows_cap, int64_t cols, int G,
+    const int64_t* __restrict__ offsets, const int64_t* __restrict__ poffsets, int64_t col_cap,
+    uint8_t* __restrict__ data, uint8_t* __restrict__ bscales, float* __restrict__ outer,
+    uint32_t* status) {
+  __shared__ int64_t s_off[kMaxGroups + 1];
+  __shared__ int64_t s_poff[kMaxGroups + 1];
+  __shared__ uint32_t s_amax[4][kNvColCols / 2];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kNvColTokens * kNvColCols * 2];
+  const bool report = blockIdx.x == 0;
+  load_offsets_clamped(offsets, G, rows_cap, s_off, report ? status : nullptr);
+  load_offsets_clamped(poffsets, G, col_cap, s_poff, report ? status : nullptr);
+  const int64_t nslab = (cols + kNvColCols - 1) / kNvColCols;
+  const int g = (int)(blockIdx.x / nslab);
+  const int64_t c0 = (blockIdx.x % nslab) * kNvColCols;
+  if (g >= G) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t m = group_extent(s_off, g), mp = group_extent(s_poff, g);
+  const bool ok = s_poff[g] % kNvColTokens == 0 && mp % kNvColTokens == 0 && mp >= m;
+  if (!ok) {
+    if (tid == 0 && c0 == 0) dev_status_or(status, kDevBadPadding);
+    return;
+  }
+  const int64_t row0 = s_off[g];
+
+  // pass 1: column maxima (bf16 magnitude bits) over the expert's tokens; this
+  // thread sees columns c0 + 8 (tid % 8) .. + 7 as four packed pairs
+  uint32_t am[4] = {0, 0, 0, 0};
+  for (int64_t t0 = 0; t0 < m; t0 += kNvColTokens) {
+    uint4 v[4];
+    nvcol_load(x, cols, row0 + t0, (int)(m - t0 < kNvColTokens ? m - t0 : kNvColTokens), c0, v);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      am[0] = pk_mag_max(am[0], v[i].x);
+      am[1] = pk_mag_max(am[1], v[i].y);
+      am[2] = pk_mag_max(am[2], v[i].z);
+      am[3] = pk_mag_max(am[3], v[i].w);
+    }
+  }
+  // lanes l, l ^ 8, l ^ 16, ... of a wave hold the same columns
+#pragma unroll
+  for (int d = 8; d < 64; d <<= 1)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) am[q] = pk_mag_max(am[q], (uint32_t)__shfl_xor((int)am[q], d, 64));
+  if (lane < 8) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s_amax[w][4 * lane + q] = am[q];
+  }
+  __syncthreads();
+  // thread (p, b): column pair p = tid / 8 (columns c0 + 2 p, + 1), block b = tid % 8
+  const int p = tid >> 3, b = tid & 7;
+  const uint32_t pm = pk_mag_max(pk_mag_max(s_amax[0][p], s_amax[1][p]),
+                                 pk_mag_max(s_amax[2][p], s_amax[3][p]));
+  float S[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const float amax = bf16_to_f32(e ? pm >> 16 : pm & 0xffffu);
+    S[e] = amax > 0.0f ? 2688.0f / amax : 1.0f;
+    S[e] = __builtin_fminf(S[e], 3.40282346638528859812e+38f);
+    const int64_t c = c0 + 2 * p + e;
+    if (b == 0 && c < cols) outer[(int64_t)g * cols + c] = amax / 2688.0f;
+  }
+  if (mp == 0) return;
+
+  // pass 2: convert, one 128-token tile at a time (padding tokens load as zeros)
+  const uint32_t lds = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)tile;
+  uint8_t* dg = data + s_poff[g] * cols / 2;       // expert g's [C, mp / 2] block
+  uint8_t* sg = bscales + s_poff[g] * cols / 16;   // and its [C, mp / 16] scales
+  uint4 v[4];
+  nvcol_load(x, cols, row0, (int)(m < kNvColTokens ? m : kNvColTokens), c0, v);
+  for (int64_t t0 = 0; t0 < mp; t0 += kNvColTokens) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 u = v[i];
+      *reinterpret_cast<__attribute__((address_space(3))) v4i*>(
+          (size_t)(lds + nvcol_slot((tid >> 3) + 32 * i, tid & 7))) =
+          v4i{(int)u.x, (int)u.y, (int)u.z, (int)u.w};
+    }
+    __syncthreads();
+    if (t0 + kNvColTokens < mp) {
+      const int64_t rest = m - (t0 + kNvColTokens);
+      nvcol_load(x, cols, row0 + t0 + kNvColTokens,
+                 (int)(rest < 0 ? 0 : (rest > kNvColTokens ? kNvColTokens : rest)), c0, v);
+    }
+    // tokens 16 b .. 16 b + 15 of columns 2 p, 2 p + 1 as bf16 pairs
+    uint32_t wv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 16 * b + i;
+      wv[i] = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(
+          (size_t)(lds + nvcol_slot(r, p >> 2) + 4 * (p & 3)));
+    }
+    uint32_t bm2 = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) bm2 = pk_mag_max(bm2, wv[i]);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      uint32_t s8;
+      float enc;
+      nv_block_scale(e ? bm2 >> 16 : bm2 & 0xffffu, S[e], s8, enc);
+      const uint2 q = e ? fp4_pack_col16<1>(wv, enc) : fp4_pack_col16<0>(wv, enc);
+      const int64_t c = c0 + 2 * p + e;
+      if (c < cols) {
+        *reinterpret_cast<uint2*>(dg + c * (mp / 2) + t0 / 2 + 8 * b) = q;
+        sg[c * (mp / 16) + t0 / 16 + b] = (uint8_t)s8;
+      }
+    }
+  }
+}
+
+hipError_t launch_quantize_nvfp4_rowscaled_colwise(const uint16_t* x, int64_t rows_cap,
+                                                   int64_t cols, int G, const int64_t* offsets,
+                                                   const int64_t* padded_offsets,
+                                                   int64_t col_rows_cap, uint8_t* data,
+                                                   uint8_t* block_scales, float* outer,
+                                                   uint32_t* status, hipStream_t stream) {
+  const int64_t blocks = (int64_t)G * ((cols + kNvColCols - 1) / kNvColCols);
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(nvfp4_colwise_kernel, dim3((unsigned)blocks), dim3(kNvThreads), 0, stream, x,
+                     rows_cap, cols, G, offsets, padded_offsets, col_rows_cap, data, block_scales,
+                     outer, status);
+  return hipGetLastError();
+}
+
 }  // namespace bsg

@@ -146,6 +146,40 @@ int grouped_quantize_nvfp4_rowscaled(const void* x, int64_t rows_cap, int64_t co
                                      float* outer, uint32_t* dev_status, void* stream);
 
 /*
+ * grouped_quantize_nvfp4_rowscaled_colwise
+ *
+ * Columnwise (transposed) row-scaled NVFP4 copies for the weight gradient
+ * ("[Common][PyTorch] Add row-scaled NVFP4 support to grouped-tensor GEMM":
+ * columnwise use of row-scaled grouped tensors, the columnwise amax sized per
+ * column and split per expert).  Per expert g the block X_g^T [cols, m~_g]
+ * (tokens padded with zeros to m~_g) is quantized row by row with the float32
+ * steps of grouped_quantize_nvfp4_rowscaled: column c of expert g gets the
+ * outer scale amax / 2688 over the expert's tokens, each 16-token block an E4M3
+ * scale, each token an E2M1 code.
+ *
+ *   x              [rows_cap, cols] bf16; rows >= offsets[G] are not read.
+ *   cols           multiple of 32, <= 16384.
+ *   offsets        [G+1] int64 live token offsets (group_offsets_i32_to_i64, pad 1).
+ *   padded_offsets [G+1] int64 (group_offsets_i32_to_i64 with pad_to 128);
+ *                  a group whose padded offsets are not multiples of 128 or
+ *                  smaller than its size is skipped and flagged (bit 2).
+ *   col_rows_cap   capacity of the outputs in padded tokens (>= padded_offsets[G]).
+ *   data           expert g: a [cols, m~_g / 2] byte block at byte
+ *                  padded_offsets[g] * cols / 2; token 2j of a column in the low
+ *                  nibble of byte j; padding tokens encode to 0.
+ *   block_scales   expert g: a [cols, m~_g / 16] E4M3 block at byte
+ *                  padded_offsets[g] * cols / 16 (padding blocks 0x00).
+ *   outer          [G, cols] float32 (0 for an empty expert).
+ * Errors: BSG_ERR_NULL, BSG_ERR_SHAPE, BSG_ERR_UNSUPPORTED (cols > 16384),
+ * BSG_ERR_ALIGN (x and data 16-byte, outer 4-byte).
+ */
+int grouped_quantize_nvfp4_rowscaled_colwise(const void* x, int64_t rows_cap, int64_t cols,
+                                             int64_t G, const int64_t* offsets,
+                                             const int64_t* padded_offsets, int64_t col_rows_cap,
+                                             uint8_t* data, uint8_t* block_scales, float* outer,
+                                             uint32_t* dev_status, void* stream);
+
+/*
  * grouped_gemm_mxfp8
  *
  * One launch over all groups of a grouped MXFP8 GEMM with FP32 accumulation

@@ -186,6 +186,52 @@ def test_nvfp4_quantize_bit_exact(rows_cap, cols, sizes):
     assert np.all(np.isnan(t[live:]))
 
 
+NVCOL_CASES = [
+    (200, 96, [37, 0, 130, 5]),          # a 32-column last slab, an empty expert
+    (800, 4096, [449, 0, 301, 0, 50]),
+    (300, 160, [257, 1]),                # three 128-token tiles, a one-token expert
+    (64, 32, [0, 0, 64]),                # leading empty experts
+]
+
+
+@pytest.mark.parametrize("rows_cap,cols,sizes", NVCOL_CASES)
+def test_nvfp4_colwise_bit_exact(rows_cap, cols, sizes):
+    rng = np.random.default_rng(rows_cap * 5 + cols)
+    bits = _bits(rng, rows_cap, cols, spread=8)
+    sizes = np.array(sizes, np.int32)
+    live = int(sizes.sum())
+    bits[live:] = workloads.BF16_NAN_BITS       # capacity rows: never read
+    bits[:, 1] = 0                              # an all-zero column
+    _, off = O.group_offsets(sizes)
+    _, poff = O.group_offsets(sizes, pad_to=128)
+    wd, ws, wo = Q.nvfp4_rowscaled_colwise(bits, off, poff)
+    G = len(sizes)
+    cap = rows_cap + 128 * G
+    d = filled_u8((cap * cols // 2,))
+    sc = filled_u8((cap * cols // 16,))
+    o = torch.full((G, cols), float("nan"), dtype=torch.float32, device=device())
+    bsg.grouped_quantize_nvfp4_rowscaled_colwise(bf16_dev(bits), to_dev(off), to_dev(poff),
+                                                 col_rows_cap=cap, data=d, block_scales=sc,
+                                                 outer=o)
+    d, sc, o = host_u8(d), host_u8(sc), host(o)
+    n = int(poff[-1]) * cols
+    assert np.array_equal(d[:n // 2], wd)
+    assert np.array_equal(sc[:n // 16], ws)
+    assert np.array_equal(o.view(np.uint32), wo.view(np.uint32))
+    assert np.all(d[n // 2:] == SENTINEL) and np.all(sc[n // 16:] == SENTINEL)
+
+
+def test_nvfp4_colwise_bad_padding_flagged():
+    bits = _bits(np.random.default_rng(4), 64, 64)
+    off = np.array([0, 10, 64])
+    poff = np.array([0, 64, 192])          # expert 0 padded to 64, not 128
+    status = torch.zeros(1, dtype=torch.int32, device=device())
+    bsg.grouped_quantize_nvfp4_rowscaled_colwise(bf16_dev(bits), to_dev(off), to_dev(poff),
+                                                 col_rows_cap=256, status=status)
+    torch.cuda.synchronize()
+    assert int(host(status)[0]) & bsg.DEV_BAD_PADDING
+
+
 def test_determinism_two_runs():
     rng = np.random.default_rng(5)
     bits = _bits(rng, 512, 4096)
