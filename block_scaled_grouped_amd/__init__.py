@@ -26,7 +26,7 @@ DEV_BAD_PADDING = 4
 
 EXPORTS = ("bsg_last_error", "bsg_version", "group_offsets_i32_to_i64", "grouped_quantize_mxfp8",
            "grouped_quantize_nvfp4_rowscaled", "grouped_quantize_nvfp4_rowscaled_colwise",
-           "grouped_gemm_mxfp8", "grouped_gemm_nvfp4_rowscaled")
+           "grouped_gemm_mxfp8", "grouped_gemm_nvfp4_rowscaled", "grouped_gemm_nvfp4_rowscaled_wgrad")
 
 _lib = None
 
@@ -65,6 +65,9 @@ def load_library(path=LIB_PATH):
     lib.grouped_gemm_nvfp4_rowscaled.restype = I32
     lib.grouped_gemm_nvfp4_rowscaled.argtypes = [I64, P, P, P, P, I64, I64, P, P, P, P, P, I64, I32,
                                                  P, P, P]
+    lib.grouped_gemm_nvfp4_rowscaled_wgrad.restype = I32
+    lib.grouped_gemm_nvfp4_rowscaled_wgrad.argtypes = [I64, P, P, P, P, P, P, P, I64, I64, I64, P,
+                                                       I32, P, P]
     _lib = lib
     return lib
 
@@ -235,4 +238,24 @@ def grouped_gemm_nvfp4_rowscaled(a, a_scales, a_outer, offsets, k, b, b_scales, 
                                             _ptr(b_outer), ctypes.cast(host_n, ctypes.c_void_p),
                                             _ptr(out), ld_out, out_dtype, _ptr(scratch),
                                             _ptr(status), _stream(a)))
+    return out
+
+
+def grouped_gemm_nvfp4_rowscaled_wgrad(a, a_scales, a_outer, b, b_scales, b_outer, padded_offsets,
+                                       n, k, col_rows_cap=None, out=None, out_dtype=BSG_OUT_BF16,
+                                       G=None, status=None):
+    """Row-scaled NVFP4 wgrad from the columnwise copies: out [G, n, k].  See
+    include/bsg.h."""
+    import torch
+    lib = load_library()
+    _need_cuda(a, a_scales, a_outer, b, b_scales, b_outer, padded_offsets)
+    G = padded_offsets.numel() - 1 if G is None else G
+    if col_rows_cap is None:
+        col_rows_cap = a.numel() * 2 // n
+    if out is None:
+        dt = torch.float32 if out_dtype == BSG_OUT_F32 else torch.bfloat16
+        out = torch.empty((G, n, k), dtype=dt, device=a.device)
+    _check(lib.grouped_gemm_nvfp4_rowscaled_wgrad(
+        G, _ptr(a), _ptr(a_scales), _ptr(a_outer), _ptr(b), _ptr(b_scales), _ptr(b_outer),
+        _ptr(padded_offsets), col_rows_cap, n, k, _ptr(out), out_dtype, _ptr(status), _stream(a)))
     return out

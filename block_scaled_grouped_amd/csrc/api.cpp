@@ -236,4 +236,35 @@ int grouped_gemm_nvfp4_rowscaled(int64_t G, const uint8_t* a, const uint8_t* a_s
                     fn);
 }
 
+int grouped_gemm_nvfp4_rowscaled_wgrad(int64_t G, const uint8_t* a, const uint8_t* a_scales,
+                                       const float* a_outer, const uint8_t* b,
+                                       const uint8_t* b_scales, const float* b_outer,
+                                       const int64_t* padded_offsets, int64_t col_rows_cap,
+                                       int64_t n, int64_t k, void* out, int out_dtype,
+                                       uint32_t* dev_status, void* stream) {
+  const char* fn = "grouped_gemm_nvfp4_rowscaled_wgrad";
+  if (a == nullptr || a_scales == nullptr || a_outer == nullptr || b == nullptr ||
+      b_scales == nullptr || b_outer == nullptr || padded_offsets == nullptr || out == nullptr)
+    return fail(BSG_ERR_NULL, "%s: operands, scales, padded_offsets and out must be non-NULL", fn);
+  if (out_dtype != BSG_OUT_BF16 && out_dtype != BSG_OUT_F32)
+    return fail(BSG_ERR_UNSUPPORTED, "%s: unknown out_dtype %d", fn, out_dtype);
+  if (G < 1 || G > BSG_MAX_GROUPS)
+    return fail(BSG_ERR_SHAPE, "%s: G=%lld outside [1, %d]", fn, (long long)G, BSG_MAX_GROUPS);
+  if (col_rows_cap < 0 || n < 32 || k < 32 || n % 32 != 0 || k % 32 != 0)
+    return fail(BSG_ERR_SHAPE, "%s: need col_rows_cap >= 0 and n, k positive multiples of 32", fn);
+  const int64_t esz = out_dtype == BSG_OUT_F32 ? 4 : 2;
+  if (256 * (col_rows_cap / 2) >= kMaxTileBytes || 256 * k * esz >= kMaxTileBytes ||
+      n > 0x7fffffffLL || k > 0x7fffffffLL)
+    return fail(BSG_ERR_SHAPE, "%s: col_rows_cap, n or k too large for 32-bit tile offsets", fn);
+  if (!aligned16(a) || !aligned16(b) || !aligned4(a_scales) || !aligned4(b_scales) ||
+      !aligned4(a_outer) || !aligned4(b_outer) || !aligned4(out))
+    return fail(BSG_ERR_ALIGN, "%s: a and b must be 16-byte aligned; scales, outer and out 4-byte",
+                fn);
+  return hip_result(bsg::launch_gemm_nvfp4_wgrad((int)G, a, a_scales, a_outer, b, b_scales,
+                                                 b_outer, padded_offsets, col_rows_cap, n, k, out,
+                                                 out_dtype == BSG_OUT_F32, dev_status,
+                                                 (hipStream_t)stream),
+                    fn);
+}
+
 }  // extern "C"

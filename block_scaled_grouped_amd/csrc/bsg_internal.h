@@ -189,6 +189,12 @@ hipError_t launch_gemm_nvfp4(int G, const uint8_t* a, const uint8_t* a_scales,
                              void* out, int64_t ld_out, int out_f32, float* scratch,
                              uint32_t* status, hipStream_t stream);
 
+hipError_t launch_gemm_nvfp4_wgrad(int G, const uint8_t* a, const uint8_t* a_scales,
+                                   const float* a_outer, const uint8_t* b, const uint8_t* b_scales,
+                                   const float* b_outer, const int64_t* padded_offsets,
+                                   int64_t col_rows_cap, int64_t n, int64_t k, void* out,
+                                   int out_f32, uint32_t* status, hipStream_t stream);
+
 int device_cu_count();
 
 }  // namespace bsg

@@ -67,9 +67,10 @@ struct NvArgs {
   const uint8_t* a;
   const uint8_t* as;
   const float* aout;
-  const int64_t* offsets;
-  int64_t rows_cap;
-  int64_t k;
+  const int64_t* offsets;  // live row offsets; padded token offsets in wgrad
+  int64_t rows_cap;        // capacity those offsets are clamped to
+  int64_t k;               // contraction (fprop); dW columns (wgrad)
+  int64_t n;               // dW rows (wgrad)
   const uint8_t* b;
   const uint8_t* bs;
   const float* bout;
@@ -344,7 +345,11 @@ __device__ __forceinline__ void k_step(uint32_t cur, uint32_t nxt, const TileDes
   });
 }
 
-template <bool PAIRED>
+// WGRAD: expert g contracts its padded tokens, A = dY^T_g [n, m~_g], B =
+// X^T_g [k, m~_g] (the columnwise copies), dW[g] = (S * a_outer[g, i]) *
+// b_outer[g, j] into out [G, n, k]; every expert has its n x k tiles, an empty
+// one (or one whose padded offsets are not multiples of 128, flagged) zeros.
+template <bool PAIRED, bool WGRAD>
 __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
   __shared__ Smem sm;
   const int G = p.G;
@@ -352,9 +357,15 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
   uint32_t* status = blockIdx.x == 0 ? p.status : nullptr;
   load_offsets_clamped(p.offsets, G, p.rows_cap, sm.off, status);
   for (int g = tid0; g < G; g += kThreads) {
-    const int64_t m = group_extent(sm.off, g);
-    const int64_t ng = p.tab.n[g];
-    sm.cnt[g] = (int32_t)(((m + BM - 1) / BM) * ((ng + BN - 1) / BN));
+    if constexpr (WGRAD) {
+      const int64_t mp = group_extent(sm.off, g);
+      if (sm.off[g] % kColPad != 0 || mp % kColPad != 0) dev_status_or(status, kDevBadPadding);
+      sm.cnt[g] = (int32_t)(((p.n + BM - 1) / BM) * ((p.k + BN - 1) / BN));
+    } else {
+      const int64_t m = group_extent(sm.off, g);
+      const int64_t ng = p.tab.n[g];
+      sm.cnt[g] = (int32_t)(((m + BM - 1) / BM) * ((ng + BN - 1) / BN));
+    }
   }
   __syncthreads();
   wave0_exclusive_scan(sm.cnt, G, sm.pre);
@@ -375,24 +386,54 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
     const int r = lane & 31, h = lane >> 5;
     const int g = find_group(sm.pre, G, tile);
     const int local = tile - sm.pre[g];
-    const int64_t m = group_extent(sm.off, g);
-    const int64_t ng = p.tab.n[g];
-    int mt, nt;
-    super_tile<kSuperM, kSuperN>(local, (int)((m + BM - 1) / BM), (int)((ng + BN - 1) / BN), mt, nt);
-    const int64_t row0 = sm.off[g] + (int64_t)mt * BM;
-    const int64_t n0 = (int64_t)nt * BN;
-    const int64_t brow0 = p.tab.brow[g] + n0;
     TileDesc t;
-    t.lda = p.k / 2;
-    t.ldas = p.k / 16;
-    t.a = p.a + row0 * t.lda;
-    t.as = p.as + row0 * t.ldas;
-    t.b = p.b + brow0 * t.lda;
-    t.bs = p.bs + brow0 * t.ldas;
-    const int64_t rv = sm.off[g] + m - row0, cv = ng - n0;
-    t.a_rows = (int)(rv < BM ? rv : BM);
-    t.b_rows = (int)(cv < BN ? cv : BN);
-    t.kl = p.k;
+    const float* aout_t;      // outer scales of the tile's rows / columns
+    const float* bout_t;
+    int64_t out_off, ld_out;  // element offset of the tile's first output, row stride
+    if constexpr (WGRAD) {
+      const int64_t mp = group_extent(sm.off, g);
+      const bool usable = sm.off[g] % kColPad == 0 && mp % kColPad == 0;
+      int mt, nt;
+      super_tile<kSuperM, kSuperN>(local, (int)((p.n + BM - 1) / BM), (int)((p.k + BN - 1) / BN),
+                                   mt, nt);
+      const int64_t i0 = (int64_t)mt * BM, j0 = (int64_t)nt * BN;
+      t.lda = mp / 2;
+      t.ldas = mp / 16;
+      t.a = p.a + sm.off[g] * p.n / 2 + i0 * t.lda;
+      t.as = p.as + sm.off[g] * p.n / 16 + i0 * t.ldas;
+      t.b = p.b + sm.off[g] * p.k / 2 + j0 * t.lda;
+      t.bs = p.bs + sm.off[g] * p.k / 16 + j0 * t.ldas;
+      t.a_rows = (int)(p.n - i0 < BM ? p.n - i0 : BM);
+      t.b_rows = (int)(p.k - j0 < BN ? p.k - j0 : BN);
+      t.kl = usable ? mp : 0;
+      aout_t = p.aout + (int64_t)g * p.n + i0;
+      bout_t = p.bout + (int64_t)g * p.k + j0;
+      out_off = ((int64_t)g * p.n + i0) * p.k + j0;
+      ld_out = p.k;
+    } else {
+      const int64_t m = group_extent(sm.off, g);
+      const int64_t ng = p.tab.n[g];
+      int mt, nt;
+      super_tile<kSuperM, kSuperN>(local, (int)((m + BM - 1) / BM), (int)((ng + BN - 1) / BN), mt,
+                                   nt);
+      const int64_t row0 = sm.off[g] + (int64_t)mt * BM;
+      const int64_t n0 = (int64_t)nt * BN;
+      const int64_t brow0 = p.tab.brow[g] + n0;
+      t.lda = p.k / 2;
+      t.ldas = p.k / 16;
+      t.a = p.a + row0 * t.lda;
+      t.as = p.as + row0 * t.ldas;
+      t.b = p.b + brow0 * t.lda;
+      t.bs = p.bs + brow0 * t.ldas;
+      const int64_t rv = sm.off[g] + m - row0, cv = ng - n0;
+      t.a_rows = (int)(rv < BM ? rv : BM);
+      t.b_rows = (int)(cv < BN ? cv : BN);
+      t.kl = p.k;
+      aout_t = p.aout + row0;
+      bout_t = p.bout + brow0;
+      out_off = row0 * p.ld_out + n0;
+      ld_out = p.ld_out;
+    }
     // waves 0 and 1 decode A, waves 2 and 3 B
     const bool opb = w >= 2;
     Rsrc rs;
@@ -401,9 +442,11 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
                : make_rsrc(t.as, (int64_t)t.a_rows * t.ldas);
     rs.none = make_rsrc(t.a, 0);
 
-    // outer scales of this tile's rows and columns, for the epilogue
-    sm.aout[tid] = tid < t.a_rows ? p.aout[row0 + tid] : 0.0f;
-    sm.bout[tid] = tid < t.b_rows ? p.bout[brow0 + tid] : 0.0f;
+    // outer scales of this tile's rows and columns, for the epilogue (zeros for
+    // a tile with nothing to contract, whose output is then exactly 0)
+    const bool contract = t.kl > 0;
+    sm.aout[tid] = contract && tid < t.a_rows ? aout_t[tid] : 0.0f;
+    sm.bout[tid] = contract && tid < t.b_rows ? bout_t[tid] : 0.0f;
 
     v16f acc[4][4];
 #pragma unroll
@@ -411,9 +454,9 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
 
-    const int nk = (int)(t.kl / BK);   // >= 1
+    const int nk = (int)(t.kl / BK);   // >= 1 unless nothing to contract
     const int nk2 = (nk + 1) & ~1;     // an odd last step runs on zeros
-    {
+    if (nk > 0) {
       const Offs o = make_offs(tid, wm, wn, r, h);
       Raw x0, x1;
       Scl sc0, sc1;  // scale words of steps (kt, kt + 1) and (kt + 2, kt + 3)
@@ -446,9 +489,9 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
     const bool f32out = !fused || p.out_f32;
     const int esz = f32out ? 4 : 2;
     char* obase = fused ? reinterpret_cast<char*>(p.out) : reinterpret_cast<char*>(p.scratch);
-    obase += (row0 * p.ld_out + n0) * esz;
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(obase, (int64_t)t.a_rows * p.ld_out * esz);
-    int ldc = (int)p.ld_out;
+    obase += out_off * esz;
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(obase, (int64_t)t.a_rows * ld_out * esz);
+    int ldc = (int)ld_out;
     asm volatile("" : "+s"(ldc));
     const int row = wm * 128 + r, col = wn * 128 + 4 * h;
     const uint32_t ao_base = (uint32_t)(size_t)(__attribute__((address_space(3))) float*)sm.aout;
@@ -526,6 +569,7 @@ hipError_t launch_gemm_nvfp4(int G, const uint8_t* a, const uint8_t* a_scales,
                              uint32_t* status, hipStream_t stream) {
   NvArgs p;
   p.a = a; p.as = a_scales; p.aout = a_outer; p.offsets = offsets; p.rows_cap = rows_cap; p.k = k;
+  p.n = 0;
   p.b = b; p.bs = b_scales; p.bout = b_outer; p.out = out; p.ld_out = ld_out; p.scratch = scratch;
   p.status = status; p.G = G; p.out_f32 = out_f32; p.tab = table;
   const int64_t bound = ((rows_cap + BM - 1) / BM + G) * ((max_n + BN - 1) / BN);
@@ -534,9 +578,11 @@ hipError_t launch_gemm_nvfp4(int G, const uint8_t* a, const uint8_t* a_scales,
   if (grid > 0) {
     // an even step count keeps each row's scale words of a step pair 8-aligned
     if ((k / BK) % 2 == 0)
-      hipLaunchKernelGGL(nv_gemm_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((nv_gemm_kernel<true, false>), dim3((unsigned)grid), dim3(kThreads), 0,
+                         stream, p);
     else
-      hipLaunchKernelGGL(nv_gemm_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((nv_gemm_kernel<false, false>), dim3((unsigned)grid), dim3(kThreads), 0,
+                         stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -547,6 +593,26 @@ hipError_t launch_gemm_nvfp4(int G, const uint8_t* a, const uint8_t* a_scales,
     return hipGetLastError();
   }
   return hipSuccess;
+}
+
+hipError_t launch_gemm_nvfp4_wgrad(int G, const uint8_t* a, const uint8_t* a_scales,
+                                   const float* a_outer, const uint8_t* b, const uint8_t* b_scales,
+                                   const float* b_outer, const int64_t* padded_offsets,
+                                   int64_t col_rows_cap, int64_t n, int64_t k, void* out,
+                                   int out_f32, uint32_t* status, hipStream_t stream) {
+  NvArgs p;
+  p.a = a; p.as = a_scales; p.aout = a_outer; p.offsets = padded_offsets;
+  p.rows_cap = col_rows_cap; p.k = k; p.n = n;
+  p.b = b; p.bs = b_scales; p.bout = b_outer; p.out = out; p.ld_out = k; p.scratch = nullptr;
+  p.status = status; p.G = G; p.out_f32 = out_f32; p.tab = NvGroupTable{};
+  const int64_t bound = (int64_t)G * ((n + BM - 1) / BM) * ((k + BN - 1) / BN);
+  int64_t grid = device_cu_count();
+  if (bound < grid) grid = bound;
+  if (grid <= 0) return hipSuccess;
+  // padded token counts are multiples of 128: an even number of 64-deep steps
+  hipLaunchKernelGGL((nv_gemm_kernel<true, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                     p);
+  return hipGetLastError();
 }
 
 }  // namespace bsg

@@ -241,6 +241,37 @@ int grouped_gemm_nvfp4_rowscaled(int64_t G, const uint8_t* a, const uint8_t* a_s
                                  int64_t ld_out, int out_dtype, float* scratch,
                                  uint32_t* dev_status, void* stream);
 
+/*
+ * grouped_gemm_nvfp4_rowscaled_wgrad
+ *
+ * Row-scaled NVFP4 weight gradient, NT, over each expert's ragged tokens
+ * ("[Common][PyTorch] Add row-scaled NVFP4 support to grouped-tensor GEMM":
+ * wgrad consumes the columnwise copies; the outer scales are neutralized in
+ * the GEMM and applied afterwards per expert, over its own rows and columns):
+ *   S[g, i, j]  = sum_{t < m~_g} (e2m1 * sd)(A_g)[i, t] * (e2m1 * sd)(B_g)[j, t]
+ *   dW[g, i, j] = (S * a_outer[g, i]) * b_outer[g, j]       (float32)
+ * with A = the columnwise copy of dY ([n, m~_g] per expert) and B that of X
+ * ([k, m~_g] per expert), both as written by
+ * grouped_quantize_nvfp4_rowscaled_colwise.  One launch for all experts; the
+ * outer-scale epilogue is fused (no FP32 scratch).
+ *
+ *   a, a_scales, a_outer  dY copies: data, E4M3 block scales, f32 [G, n].
+ *   b, b_scales, b_outer  X copies: data, E4M3 block scales, f32 [G, k].
+ *   padded_offsets [G+1] int64 (pad 128); col_rows_cap as for the quantize.
+ *   n, k           dW dims, positive multiples of 32.
+ *   out            [G, n, k] bf16 or f32 (out_dtype); an empty expert's block is
+ *                  0, as is that of an expert whose padded offsets are not
+ *                  multiples of 128 (also flagged, bit 2 of *dev_status).
+ * Errors: BSG_ERR_NULL, BSG_ERR_SHAPE, BSG_ERR_UNSUPPORTED (out_dtype),
+ * BSG_ERR_ALIGN (a, b 16-byte; scales, outer scales, out 4-byte).
+ */
+int grouped_gemm_nvfp4_rowscaled_wgrad(int64_t G, const uint8_t* a, const uint8_t* a_scales,
+                                       const float* a_outer, const uint8_t* b,
+                                       const uint8_t* b_scales, const float* b_outer,
+                                       const int64_t* padded_offsets, int64_t col_rows_cap,
+                                       int64_t n, int64_t k, void* out, int out_dtype,
+                                       uint32_t* dev_status, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,7 +16,8 @@ from oracle import gemm as GM
 from oracle import offsets as O
 from oracle import quantize as Q
 import workloads
-from gpu_util import (bf16_dev, bf16_out_to_f64, device, gemm_tolerance_check, host, to_dev)
+from gpu_util import (bf16_dev, bf16_out_to_f64, device, gemm_tolerance_check, host, host_u8,
+                      to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -305,3 +306,50 @@ def test_nvfp4_end_to_end():
     for g, (rows, r) in enumerate(GM.nvfp4_rowscaled_fprop(ap, asc, at, off, bp, bsc, bt, npg, K)):
         if len(rows):
             gemm_tolerance_check(y[rows][:, :npg[g]], r, True, "group %d" % g)
+
+
+# ---------------------------------------------------------------- NVFP4 row-scaled wgrad
+
+NVW_CASES = [
+    ([37, 0, 130, 5], 96, 160),          # ragged n / k tails (not multiples of 256)
+    ([300, 1, 0, 700], 256, 512),
+    ([0, 0, 64], 64, 32),
+    ([1000], 512, 288),                  # a long contraction (1024 padded tokens)
+]
+
+
+@pytest.mark.parametrize("sizes,N,K", NVW_CASES)
+@pytest.mark.parametrize("out_f32", [True, False])
+def test_nvfp4_wgrad_parity(sizes, N, K, out_f32):
+    rng = np.random.default_rng(N * 7 + K)
+    sizes = np.array(sizes, np.int32)
+    G, M = len(sizes), int(sizes.sum())
+    dy = _bits(rng, (max(M, 1), N))
+    x = _bits(rng, (max(M, 1), K))
+    _, off = O.group_offsets(sizes)
+    _, poff = O.group_offsets(sizes, pad_to=128)
+    cap = max(M, 1) + 128 * G
+    dyc, dys, dyo = bsg.grouped_quantize_nvfp4_rowscaled_colwise(
+        bf16_dev(dy), to_dev(off), to_dev(poff), col_rows_cap=cap)
+    xc, xs, xo = bsg.grouped_quantize_nvfp4_rowscaled_colwise(
+        bf16_dev(x), to_dev(off), to_dev(poff), col_rows_cap=cap)
+    # operands are the oracle's bytes (the quantize itself is pinned bit-exact elsewhere)
+    wdyc, wdys, wdyo = Q.nvfp4_rowscaled_colwise(dy, off, poff)
+    n = int(poff[-1])
+    assert np.array_equal(host_u8(dyc)[:n * N // 2], wdyc)
+    assert np.array_equal(host(dyo).view(np.uint32), wdyo.view(np.uint32))
+    wxc, wxs, wxo = Q.nvfp4_rowscaled_colwise(x, off, poff)
+    ref = GM.nvfp4_rowscaled_wgrad(wdyc, wdys, wdyo, wxc, wxs, wxo, poff, N, K)
+    dt = torch.float32 if out_f32 else torch.bfloat16
+    out = torch.full((G, N, K), float("nan"), dtype=dt, device=device())
+    status = torch.zeros(1, dtype=torch.int32, device=device())
+    bsg.grouped_gemm_nvfp4_rowscaled_wgrad(dyc, dys, dyo, xc, xs, xo, to_dev(poff), N, K,
+                                           col_rows_cap=cap, out=out, status=status,
+                                           out_dtype=bsg.BSG_OUT_F32 if out_f32 else bsg.BSG_OUT_BF16)
+    y = bf16_out_to_f64(out)
+    assert int(host(status)[0]) == 0
+    for g in range(G):
+        if sizes[g] == 0:
+            assert np.all(y[g] == 0.0) and not np.any(np.signbit(y[g])), "empty expert must be +0"
+        else:
+            gemm_tolerance_check(y[g], ref[g], out_f32, "group %d" % g)
