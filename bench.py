@@ -163,6 +163,55 @@ class MxWgrad(Case):
         self._rec(ev, 4)
 
 
+class Nvfp4Wgrad(Case):
+    """offsets -> row-scaled NVFP4 columnwise quantize of dY and X -> NVFP4
+    grouped GEMM wgrad with the fused per-expert outer-scale epilogue."""
+
+    def __init__(self, name, dev):
+        self.name = name
+        self.w = w = workloads.get(name)
+        t = workloads.tensors(w, device=dev)
+        self.dy, self.x = t["dy"], t["x"]
+        G, N, K, R = w.G, w.n, w.k, w.rows_cap
+        self.G, self.N, self.K, self.R = G, N, K, R
+        self.sizes = torch.from_numpy(w.sizes).to(dev)
+        self.off = torch.empty(G + 1, dtype=torch.int64, device=dev)
+        self.poff = torch.empty(G + 1, dtype=torch.int64, device=dev)
+        self.cap = R + 128 * G
+        self.dyc = torch.empty(self.cap * N // 2, dtype=torch.uint8, device=dev)
+        self.dys = torch.empty(self.cap * N // 16, dtype=torch.uint8, device=dev)
+        self.dyo = torch.empty((G, N), dtype=torch.float32, device=dev)
+        self.xc = torch.empty(self.cap * K // 2, dtype=torch.uint8, device=dev)
+        self.xs = torch.empty(self.cap * K // 16, dtype=torch.uint8, device=dev)
+        self.xo = torch.empty((G, K), dtype=torch.float32, device=dev)
+        self.dw = torch.empty((G, N, K), dtype=torch.bfloat16, device=dev)
+        self.kernels = ("offsets", "quantize_dy", "quantize_x", "gemm")
+        live = w.live_rows
+        per = 0.5 + 1.0 / 16
+        self.flops = 2.0 * live * N * K
+        self.bytes = {"offsets": 0.0, "quantize_dy": live * N * (2.0 + per) + 4.0 * G * N,
+                      "quantize_x": live * K * (2.0 + per) + 4.0 * G * K,
+                      "gemm": live * (N + K) * per + G * N * K * 2.0}
+
+    def step(self, ev=None):
+        self._rec(ev, 0)
+        bsg.group_offsets_i32_to_i64(self.sizes, offsets=self.off, capacity=self.R)
+        bsg.group_offsets_i32_to_i64(self.sizes, pad_to=128, offsets=self.poff)
+        self._rec(ev, 1)
+        bsg.grouped_quantize_nvfp4_rowscaled_colwise(self.dy, self.off, self.poff,
+                                                     col_rows_cap=self.cap, data=self.dyc,
+                                                     block_scales=self.dys, outer=self.dyo)
+        self._rec(ev, 2)
+        bsg.grouped_quantize_nvfp4_rowscaled_colwise(self.x, self.off, self.poff,
+                                                     col_rows_cap=self.cap, data=self.xc,
+                                                     block_scales=self.xs, outer=self.xo)
+        self._rec(ev, 3)
+        bsg.grouped_gemm_nvfp4_rowscaled_wgrad(self.dyc, self.dys, self.dyo, self.xc, self.xs,
+                                               self.xo, self.poff, self.N, self.K,
+                                               col_rows_cap=self.cap, out=self.dw)
+        self._rec(ev, 4)
+
+
 class Nvfp4Fprop(Case):
     """offsets -> row-scaled NVFP4 quantize of X and W -> grouped GEMM with the
     fused outer-scale epilogue."""
@@ -220,6 +269,8 @@ def make_case(name, dev):
         return MxWgrad(name, dev)
     if name == "nvfp4":
         return Nvfp4Fprop(name, dev)
+    if name == "nvfp4_wgrad":
+        return Nvfp4Wgrad(name, dev)
     raise KeyError(name)
 
 
@@ -365,7 +416,8 @@ def main():
         log("[bench] copy calibration: 3 x 268435456 bytes read + written")
         del src, dst
 
-    names = ["fprop"] if args.no_extra else ["fprop", "tiny", "wgrad", "zipf", "nvfp4"]
+    names = ["fprop"] if args.no_extra else ["fprop", "tiny", "wgrad", "zipf", "nvfp4",
+                                             "nvfp4_wgrad"]
     if args.only:
         names = args.only.split(",")
     results = {}
@@ -375,7 +427,7 @@ def main():
         torch.cuda.synchronize()
         steps = args.steps if name == "fprop" else max(5, args.steps // 2)
         t = time_case(case, steps, args.warmup, flush)
-        results[name] = summarize(case, t, "bf16" if name == "nvfp4" else "fp8")
+        results[name] = summarize(case, t, "bf16" if name.startswith("nvfp4") else "fp8")
         results[name]["steps"] = steps
         log("[bench] %s: %s" % (name, json.dumps(results[name])))
         del case

@@ -143,13 +143,17 @@ hipError_t launch_quantize_nvfp4_rowscaled(const uint16_t* x, int64_t rows_cap, 
 // so the whole quantize is one launch without atomics or workspace: a first
 // pass over the expert's tokens takes the column maxima, a second pass reads
 // the same tokens again (mostly from the L2 / last-level cache) and converts
-// them.  The second pass stages 128-token x 64-column tiles (16 KiB) in LDS
-// from registers loaded one tile ahead; thread (column pair p, 16-token block
-// b) reads its 16 tokens of the two columns as 4-byte words and writes 8 packed
-// bytes and one scale byte per column, so the 8 threads of a column write its
-// 64 bytes contiguously.
+// them.  The workgroup is four 256-thread sub-groups, each taking every fourth
+// 128-token tile in both passes, so an expert's tokens are walked in a quarter
+// of the memory round trips.  The second pass stages each sub-group's
+// 128-token x 64-column tile (16 KiB) in LDS from registers loaded one tile
+// ahead; thread (column pair p, 16-token block b) reads its 16 tokens of the
+// two columns as 4-byte words and writes 8 packed bytes and one scale byte per
+// column, so the 8 threads of a column write its 64 bytes contiguously.
 constexpr int kNvColCols = 64;
 constexpr int kNvColTokens = 128;
+constexpr int kNvColSubs = 4;                      // sub-groups of 256 threads
+constexpr int kNvColThreads = 256 * kNvColSubs;
 
 namespace {
 
@@ -162,11 +166,13 @@ __device__ __forceinline__ uint32_t nvcol_slot(int r, int q) {
   return (uint32_t)(r * 128 + ((q ^ ((r >> 4) & 7)) << 4));
 }
 
-// This thread's four 16-byte loads of a tile (token rows tid / 8 + 32 i,
-// columns 8 (tid % 8) ..), zeros past the expert's tokens or the last column.
+// Thread u's (u < 256, its index in the sub-group) four 16-byte loads of a
+// tile (token rows u / 8 + 32 i, columns 8 (u % 8) ..), zeros past the
+// expert's tokens or the last column.
 __device__ __forceinline__ void nvcol_load(const uint16_t* __restrict__ x, int64_t cols,
-                                           int64_t row0, int live_rows, int64_t c0, uint4 (&v)[4]) {
-  const int tid = threadIdx.x;
+                                           int64_t row0, int live_rows, int64_t c0, int u,
+                                           uint4 (&v)[4]) {
+  const int tid = u;
   const int64_t c = c0 + 8 * (tid & 7);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -221,23 +227,37 @@ __device__ __forceinline__ void nv_block_scale(uint32_t bm, float S, uint32_t& s
 
 }  // namespace
 
-__global__ __launch_bounds__(kNvThreads) void nvfp4_colwise_kernel(
+__global__ __launch_bounds__(kNvColThreads) void nvfp4_colwise_kernel(
     const uint16_t* __restrict__ x, int64_t rows_cap, int64_t cols, int G,
     const int64_t* __restrict__ offsets, const int64_t* __restrict__ poffsets, int64_t col_cap,
     uint8_t* __restrict__ data, uint8_t* __restrict__ bscales, float* __restrict__ outer,
     uint32_t* status) {
   __shared__ int64_t s_off[kMaxGroups + 1];
   __shared__ int64_t s_poff[kMaxGroups + 1];
-  __shared__ uint32_t s_amax[4][kNvColCols / 2];
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kNvColTokens * kNvColCols * 2];
+  __shared__ uint32_t s_amax[kNvColThreads / 64][kNvColCols / 2];
+  __shared__ int s_order[kMaxGroups];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kNvColSubs][kNvColTokens * kNvColCols * 2];
   const bool report = blockIdx.x == 0;
   load_offsets_clamped(offsets, G, rows_cap, s_off, report ? status : nullptr);
   load_offsets_clamped(poffsets, G, col_cap, s_poff, report ? status : nullptr);
+  // experts in decreasing padded size (ties by index), so that the longest
+  // slabs start first and the short ones fill in behind them
+  for (int h = threadIdx.x; h < G; h += blockDim.x) {
+    const int64_t mh = group_extent(s_poff, h);
+    int rank = 0;
+    for (int j = 0; j < G; ++j) {
+      const int64_t mj = group_extent(s_poff, j);
+      rank += (mj > mh || (mj == mh && j < h)) ? 1 : 0;
+    }
+    s_order[rank] = h;
+  }
+  __syncthreads();
   const int64_t nslab = (cols + kNvColCols - 1) / kNvColCols;
-  const int g = (int)(blockIdx.x / nslab);
+  if ((int64_t)blockIdx.x >= (int64_t)G * nslab) return;
+  const int g = s_order[blockIdx.x / nslab];
   const int64_t c0 = (blockIdx.x % nslab) * kNvColCols;
-  if (g >= G) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int sub = tid >> 8, u = tid & 255;  // sub-group, thread within it
   const int64_t m = group_extent(s_off, g), mp = group_extent(s_poff, g);
   const bool ok = s_poff[g] % kNvColTokens == 0 && mp % kNvColTokens == 0 && mp >= m;
   if (!ok) {
@@ -249,9 +269,9 @@ __global__ __launch_bounds__(kNvThreads) void nvfp4_colwise_kernel(
   // pass 1: column maxima (bf16 magnitude bits) over the expert's tokens; this
   // thread sees columns c0 + 8 (tid % 8) .. + 7 as four packed pairs
   uint32_t am[4] = {0, 0, 0, 0};
-  for (int64_t t0 = 0; t0 < m; t0 += kNvColTokens) {
+  for (int64_t t0 = (int64_t)sub * kNvColTokens; t0 < m; t0 += kNvColSubs * kNvColTokens) {
     uint4 v[4];
-    nvcol_load(x, cols, row0 + t0, (int)(m - t0 < kNvColTokens ? m - t0 : kNvColTokens), c0, v);
+    nvcol_load(x, cols, row0 + t0, (int)(m - t0 < kNvColTokens ? m - t0 : kNvColTokens), c0, u, v);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       am[0] = pk_mag_max(am[0], v[i].x);
@@ -270,10 +290,12 @@ __global__ __launch_bounds__(kNvThreads) void nvfp4_colwise_kernel(
     for (int q = 0; q < 4; ++q) s_amax[w][4 * lane + q] = am[q];
   }
   __syncthreads();
-  // thread (p, b): column pair p = tid / 8 (columns c0 + 2 p, + 1), block b = tid % 8
-  const int p = tid >> 3, b = tid & 7;
-  const uint32_t pm = pk_mag_max(pk_mag_max(s_amax[0][p], s_amax[1][p]),
-                                 pk_mag_max(s_amax[2][p], s_amax[3][p]));
+  // thread (p, b) of a sub-group: column pair p = u / 8 (columns c0 + 2 p, + 1),
+  // block b = u % 8
+  const int p = u >> 3, b = u & 7;
+  uint32_t pm = 0;
+#pragma unroll
+  for (int i = 0; i < kNvColThreads / 64; ++i) pm = pk_mag_max(pm, s_amax[i][p]);
   float S[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
@@ -281,31 +303,39 @@ __global__ __launch_bounds__(kNvThreads) void nvfp4_colwise_kernel(
     S[e] = amax > 0.0f ? 2688.0f / amax : 1.0f;
     S[e] = __builtin_fminf(S[e], 3.40282346638528859812e+38f);
     const int64_t c = c0 + 2 * p + e;
-    if (b == 0 && c < cols) outer[(int64_t)g * cols + c] = amax / 2688.0f;
+    if (sub == 0 && b == 0 && c < cols) outer[(int64_t)g * cols + c] = amax / 2688.0f;
   }
   if (mp == 0) return;
 
-  // pass 2: convert, one 128-token tile at a time (padding tokens load as zeros)
-  const uint32_t lds = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)tile;
+  // pass 2: convert, each sub-group one 128-token tile at a time (padding
+  // tokens load as zeros); every sub-group runs the same number of rounds
+  const uint32_t lds = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)tile[sub];
   uint8_t* dg = data + s_poff[g] * cols / 2;       // expert g's [C, mp / 2] block
   uint8_t* sg = bscales + s_poff[g] * cols / 16;   // and its [C, mp / 16] scales
+  const auto live_in = [&](int64_t t) {            // live tokens in the tile at t
+    const int64_t rest = m - t;
+    return (int)(rest < 0 ? 0 : (rest > kNvColTokens ? kNvColTokens : rest));
+  };
   uint4 v[4];
-  nvcol_load(x, cols, row0, (int)(m < kNvColTokens ? m : kNvColTokens), c0, v);
-  for (int64_t t0 = 0; t0 < mp; t0 += kNvColTokens) {
+  nvcol_load(x, cols, row0 + (int64_t)sub * kNvColTokens, live_in((int64_t)sub * kNvColTokens), c0,
+             u, v);
+  for (int64_t base = 0; base < mp; base += kNvColSubs * kNvColTokens) {
+    const int64_t t0 = base + (int64_t)sub * kNvColTokens;
+    const bool has = t0 < mp;
     __syncthreads();
+    if (has) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 u = v[i];
-      *reinterpret_cast<__attribute__((address_space(3))) v4i*>(
-          (size_t)(lds + nvcol_slot((tid >> 3) + 32 * i, tid & 7))) =
-          v4i{(int)u.x, (int)u.y, (int)u.z, (int)u.w};
+      for (int i = 0; i < 4; ++i) {
+        const uint4 q = v[i];
+        *reinterpret_cast<__attribute__((address_space(3))) v4i*>(
+            (size_t)(lds + nvcol_slot((u >> 3) + 32 * i, u & 7))) =
+            v4i{(int)q.x, (int)q.y, (int)q.z, (int)q.w};
+      }
     }
     __syncthreads();
-    if (t0 + kNvColTokens < mp) {
-      const int64_t rest = m - (t0 + kNvColTokens);
-      nvcol_load(x, cols, row0 + t0 + kNvColTokens,
-                 (int)(rest < 0 ? 0 : (rest > kNvColTokens ? kNvColTokens : rest)), c0, v);
-    }
+    const int64_t tn = t0 + kNvColSubs * kNvColTokens;
+    if (tn < mp) nvcol_load(x, cols, row0 + tn, live_in(tn), c0, u, v);
+    if (!has) continue;
     // tokens 16 b .. 16 b + 15 of columns 2 p, 2 p + 1 as bf16 pairs
     uint32_t wv[16];
 #pragma unroll
@@ -340,7 +370,7 @@ hipError_t launch_quantize_nvfp4_rowscaled_colwise(const uint16_t* x, int64_t ro
                                                    uint32_t* status, hipStream_t stream) {
   const int64_t blocks = (int64_t)G * ((cols + kNvColCols - 1) / kNvColCols);
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(nvfp4_colwise_kernel, dim3((unsigned)blocks), dim3(kNvThreads), 0, stream, x,
+  hipLaunchKernelGGL(nvfp4_colwise_kernel, dim3((unsigned)blocks), dim3(kNvColThreads), 0, stream, x,
                      rows_cap, cols, G, offsets, padded_offsets, col_rows_cap, data, block_scales,
                      outer, status);
   return hipGetLastError();

@@ -176,3 +176,42 @@ def test_full_nvfp4_rowscaled():
     live = int(off[-1])
     assert np.isnan(y[live:]).all(), "capacity rows untouched"
     assert not np.isnan(y[:live, :min(npg)]).any()
+
+
+def test_full_nvfp4_wgrad():
+    """Row-scaled NVFP4 wgrad: 8 experts (2 empty), 16384 ragged tokens, dW
+    [8, 4096, 4096]; a sampled 32 x 32 block of every expert's dW, and the
+    columnwise copies of its 32 dY and 32 X columns."""
+    dev = device()
+    case = bench.make_case("nvfp4_wgrad", dev)
+    case.dw.fill_(float("nan"))
+    case.step()
+    torch.cuda.synchronize()
+    w = case.w
+    G, N, K = w.G, w.n, w.k
+    _, off = O.group_offsets(w.sizes)
+    _, poff = O.group_offsets(w.sizes, pad_to=128)
+    rng = np.random.default_rng(9)
+    i0, j0 = 32 * int(rng.integers(0, N // 32)), 32 * int(rng.integers(0, K // 32))
+    dyb = workloads.bf16_bits(case.dy[:, i0:i0 + 32])
+    xb = workloads.bf16_bits(case.x[:, j0:j0 + 32])
+    dyc, dys, dyo = Q.nvfp4_rowscaled_colwise(dyb, off, poff)
+    xc, xs, xo = Q.nvfp4_rowscaled_colwise(xb, off, poff)
+    ref = GM.nvfp4_rowscaled_wgrad(dyc, dys, dyo, xc, xs, xo, poff, 32, 32)
+    gd, gs = host_u8(case.dyc), host_u8(case.dys)
+    go = case.dyo.cpu().numpy()
+    assert np.array_equal(go[:, i0:i0 + 32].view(np.uint32), dyo.view(np.uint32))
+    assert np.array_equal(case.xo.cpu().numpy()[:, j0:j0 + 32].view(np.uint32), xo.view(np.uint32))
+    dw = case.dw
+    for g in range(G):
+        mp = int(poff[g + 1] - poff[g])
+        if w.sizes[g] == 0:
+            assert bool((dw[g] == 0).all()), "empty expert %d must get zeros" % g
+            continue
+        blk = gd[poff[g] * N // 2:poff[g + 1] * N // 2].reshape(N, mp // 2)[i0:i0 + 32]
+        assert np.array_equal(blk, dyc[poff[g] * 16:poff[g + 1] * 16].reshape(32, mp // 2)), g
+        sblk = gs[poff[g] * N // 16:poff[g + 1] * N // 16].reshape(N, mp // 16)[i0:i0 + 32]
+        assert np.array_equal(sblk, dys[poff[g] * 2:poff[g + 1] * 2].reshape(32, mp // 16)), g
+        y = dw[g, i0:i0 + 32, j0:j0 + 32].float().cpu().numpy().astype(np.float64)
+        gemm_tolerance_check(y, ref[g], False, "nvfp4 wgrad group %d" % g)
+    assert not torch.isnan(dw).any()
