@@ -24,6 +24,13 @@ E4M3_MAX = 448.0          # 1.75 * 2**8, code 0x7E
 E4M3_EMAX = 8             # exponent of E4M3_MAX
 E4M3_EMIN = -6            # exponent of the smallest normal value (2**-6); subnormal step 2**-9
 
+# E5M2 (exponent field 31 holds infinities and NaNs): bias 15, 2 mantissa bits.
+E5M2_BIAS = 15
+E5M2_MAN_BITS = 2
+E5M2_MAX = 57344.0        # 1.75 * 2**15, code 0x7B
+E5M2_EMAX = 15            # exponent of E5M2_MAX
+E5M2_EMIN = -14           # exponent of the smallest normal value; subnormal step 2**-16
+
 # E2M1: bias 1, 1 mantissa bit; grid {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
 E2M1_MAX = 6.0
 E2M1_EMIN = 0
@@ -88,6 +95,41 @@ def e4m3_decode(code):
     return np.where(c & 0x80, -mag, mag)
 
 
+def e5m2_encode(v):
+    """Exact values -> E5M2 codes, round half to even, saturating to +-57344.
+
+    Reading: the pages pair E5M2 gradients with E4M3 operands ("gemm.py",
+    ``_compatible_fp8_gemm_dtypes``) but fix no overflow rule; the MX scale
+    leaves a block's maximum below 2**16, and values that round past the
+    largest finite E5M2 value saturate to it, as the E4M3 elements saturate to
+    448, so a finite input never becomes an infinity."""
+    v = np.asarray(v, dtype=np.float64)
+    if not np.all(np.isfinite(v)):
+        raise ValueError("E5M2 encode: non-finite input is outside the contract")
+    neg = np.signbit(v)
+    r = np.minimum(_round_to_grid(np.abs(v), E5M2_EMIN, E5M2_MAN_BITS), E5M2_MAX)
+    code = np.zeros(r.shape, dtype=np.int64)
+    sub = r < 2.0 ** E5M2_EMIN
+    code[sub] = np.rint(r[sub] * 2.0 ** 16).astype(np.int64)           # exponent field 0
+    m, ex = np.frexp(r[~sub])
+    exp_field = (ex - 1) + E5M2_BIAS
+    man_field = np.rint((m * 2.0 - 1.0) * 2 ** E5M2_MAN_BITS).astype(np.int64)
+    code[~sub] = (exp_field << 2) | man_field
+    return (code | (neg.astype(np.int64) << 7)).astype(np.uint8)
+
+
+def e5m2_decode(code):
+    """E5M2 codes -> float64 values (exponent field 31: infinity or NaN)."""
+    c = np.asarray(code, dtype=np.int64)
+    exp_field = (c >> 2) & 0x1F
+    man_field = c & 0x3
+    mag = np.where(exp_field == 0,
+                   man_field * 2.0 ** -16,
+                   (1.0 + man_field / 4.0) * np.ldexp(1.0, exp_field - E5M2_BIAS))
+    mag = np.where(exp_field == 31, np.where(man_field == 0, np.inf, np.nan), mag)
+    return np.where(c & 0x80, -mag, mag)
+
+
 def e2m1_encode(v):
     """Exact values -> E2M1 codes (4-bit, sign in bit 3), round half to even,
     saturating to +-6."""
@@ -120,17 +162,18 @@ def e8m0_decode(byte):
     return np.where(b == 0xFF, np.nan, np.ldexp(1.0, b - E8M0_BIAS))
 
 
-def e8m0_from_amax(amax):
+def e8m0_from_amax(amax, emax=E4M3_EMAX):
     """Shared MX scale of a block from its largest magnitude.
 
     Reading (the pages give only the 32-element block): the OCP Microscaling
-    v1.0 rule, scale exponent = floor(log2(amax)) - emax(E4M3), with emax = 8,
-    biased by 127 and clamped to [0, 254].  A block of zeros gets byte 0.  The
-    block maximum then lands in [256, 512) before saturation, so values in
-    (448, 512) saturate to 448."""
+    v1.0 rule, scale exponent = floor(log2(amax)) - emax of the element format
+    (8 for E4M3, 15 for E5M2), biased by 127 and clamped to [0, 254].  A block
+    of zeros gets byte 0.  For E4M3 the block maximum then lands in [256, 512)
+    before saturation, so values in (448, 512) saturate to 448; for E5M2 in
+    [2**15, 2**16), values above 57344 saturating."""
     a = np.asarray(amax, dtype=np.float64)
     _, ex = np.frexp(a)                         # floor(log2(a)) == ex - 1 for a > 0
-    byte = np.clip((ex - 1) - E4M3_EMAX + E8M0_BIAS, 0, 254)
+    byte = np.clip((ex - 1) - emax + E8M0_BIAS, 0, 254)
     return np.where(a > 0, byte, 0).astype(np.uint8)
 
 

@@ -152,3 +152,34 @@ def nvfp4_rowscaled_wgrad(dy_col, dy_bscales, dy_outer, x_col, x_bscales, x_oute
         s = nvfp4_block_dequant(a, a_s, mp) @ nvfp4_block_dequant(b, b_s, mp).T
         out[gi] = s * dy_outer[g][out_rows][:, None] * x_outer[g][None, :]
     return out
+
+
+def mxfp8_dgrad(dy_data, dy_scales, wt_data, wt_scales, offsets, n, k, rows=None):
+    """MoE DGRAD (NN, "gemm.py", ``grouped_gemm``; E5M2 gradient times E4M3
+    weight, a pairing ``_compatible_fp8_gemm_dtypes`` accepts):
+        dX[r, j] = sum_{i < n} dq_E5M2(dY)[r, i] * dq_E4M3(W_g)[i, j]
+    for rows r of expert g.  dY is the rowwise E5M2 quantize of the
+    [rows, n] gradient (``quantize.mxfp8_rowwise(..., elem="e5m2")``); W is
+    taken from its columnwise copy (``quantize.mxfp8_colwise`` of the
+    [G * n, k] weights with expert offsets g * n), i.e. per expert the
+    transposed [k, n] block quantized along n, with [n / 128, k, 4] scale words.
+    ``rows`` optionally restricts the output rows.  Returns float64 [len(rows), k]."""
+    off = np.asarray(offsets, dtype=np.int64)
+    G = len(off) - 1
+    if rows is None:
+        rows = np.arange(int(off[-1]))
+    rows = np.asarray(rows, dtype=np.int64)
+    grp = _group_of_rows(off, rows)
+    nq = mx_scale_words(n)
+    dy_data = np.asarray(dy_data).reshape(-1, n)
+    dy_scales = np.asarray(dy_scales).reshape(nq, -1, 4)
+    out = np.zeros((len(rows), k), dtype=np.float64)
+    for g in range(G):
+        sel = np.nonzero(grp == g)[0]
+        if len(sel) == 0:
+            continue
+        a = mxfp8_dequant_rows(dy_data[rows[sel]], dy_scales[:, rows[sel], :], n, elem="e5m2")
+        wt = np.asarray(wt_data[g * n * k:(g + 1) * n * k]).reshape(k, n)
+        ws = np.asarray(wt_scales[g * n * k // MX_BLOCK:(g + 1) * n * k // MX_BLOCK]).reshape(nq, k, 4)
+        out[sel] = a @ mxfp8_dequant_rows(wt, ws, n).T
+    return out

@@ -9,8 +9,9 @@ first ``offsets[G]`` rows are live and split into G consecutive groups
 
 import numpy as np
 
-from .formats import (bf16_bits_to_f64, e4m3_encode, e4m3_decode, e2m1_encode, e2m1_decode,
-                      e8m0_from_amax, e8m0_decode, f32, E2M1_MAX, E4M3_MAX)
+from .formats import (bf16_bits_to_f64, e4m3_encode, e4m3_decode, e5m2_encode, e5m2_decode,
+                      e2m1_encode, e2m1_decode, e8m0_from_amax, e8m0_decode, f32, E2M1_MAX,
+                      E4M3_MAX, E4M3_EMAX, E5M2_EMAX)
 from .layout import (mx_scales_to_gemm_order, mx_scales_from_gemm_order, mx_scale_row_bytes,
                      fp4_pack, fp4_unpack)
 
@@ -20,25 +21,32 @@ COLWISE_PAD = 128
 FLT_MAX = np.float32(np.finfo(np.float32).max)
 
 
-def _mx_encode_blocks(vals):
-    """[..., 32] exact values -> (E4M3 codes [..., 32], E8M0 bytes [...]).
+# element formats of MXFP8: (encode, decode, emax)
+MX_ELEMENTS = {"e4m3": (e4m3_encode, e4m3_decode, E4M3_EMAX),
+               "e5m2": (e5m2_encode, e5m2_decode, E5M2_EMAX)}
+
+
+def _mx_encode_blocks(vals, elem="e4m3"):
+    """[..., 32] exact values -> (element codes [..., 32], E8M0 bytes [...]).
 
     One MX block: shared scale from the block's largest magnitude, each element
-    divided by that power of two (exact) and rounded to E4M3 (ties to even,
-    saturating)."""
+    divided by that power of two (exact) and rounded to the element format
+    (E4M3, or E5M2 for gradients; ties to even, saturating)."""
+    encode, _, emax = MX_ELEMENTS[elem]
     amax = np.abs(vals).max(axis=-1)
-    sbyte = e8m0_from_amax(amax)
+    sbyte = e8m0_from_amax(amax, emax)
     scaled = vals / e8m0_decode(sbyte)[..., None]
-    return e4m3_encode(scaled), sbyte
+    return encode(scaled), sbyte
 
 
-def mxfp8_rowwise(x_bits, offsets):
+def mxfp8_rowwise(x_bits, offsets, elem="e4m3"):
     """Rowwise MXFP8 quantize: 32-element blocks along each row (the contraction
     dim of an fprop activation or of a weight, "gemm.py",
-    ``_quantize_gemm_operands``).
+    ``_quantize_gemm_operands``); elements E4M3, or E5M2 for a gradient
+    (``_compatible_fp8_gemm_dtypes`` pairs E5M2 with E4M3).
 
-    Returns (data [live, C] uint8 E4M3, scales [NQ, live, 4] uint8 E8M0 words in
-    the GEMM-ready order, NQ = ceil(C / 128))."""
+    Returns (data [live, C] uint8 codes, scales [NQ, live, 4] uint8 E8M0 words
+    in the GEMM-ready order, NQ = ceil(C / 128))."""
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     rows, cols = x_bits.shape
     if cols % MX_BLOCK:
@@ -47,7 +55,7 @@ def mxfp8_rowwise(x_bits, offsets):
     if live > rows:
         raise ValueError("sum of group sizes exceeds the row capacity")
     x = bf16_bits_to_f64(x_bits[:live]).reshape(live, cols // MX_BLOCK, MX_BLOCK)
-    codes, sbyte = _mx_encode_blocks(x)
+    codes, sbyte = _mx_encode_blocks(x, elem)
     return codes.reshape(live, cols), mx_scales_to_gemm_order(sbyte)
 
 
@@ -90,14 +98,14 @@ def mxfp8_colwise(x_bits, offsets, padded_offsets):
     return data, scales
 
 
-def mxfp8_dequant_rows(data, stored_scales, cols):
+def mxfp8_dequant_rows(data, stored_scales, cols, elem="e4m3"):
     """Q->DQ of MXFP8 rows: undo the GEMM-ready scale order, then
     element * 2**(scale - 127).  data [R, cols], stored_scales [NQ, R, 4]."""
     data = np.asarray(data, dtype=np.uint8).reshape(-1, cols)
     nq = mx_scale_row_bytes(cols // MX_BLOCK) // 4
     sbyte = mx_scales_from_gemm_order(np.asarray(stored_scales).reshape(nq, data.shape[0], 4),
                                       cols // MX_BLOCK)
-    vals = e4m3_decode(data).reshape(data.shape[0], cols // MX_BLOCK, MX_BLOCK)
+    vals = MX_ELEMENTS[elem][1](data).reshape(data.shape[0], cols // MX_BLOCK, MX_BLOCK)
     return (vals * e8m0_decode(sbyte)[..., None]).reshape(data.shape[0], cols)
 
 

@@ -228,3 +228,39 @@ def test_nvfp4_encode_bound():
     # relative reconstruction error of the block maximum stays within the E4M3 + E2M1 steps
     dq = dq_inner * tsi[:, None].astype(np.float64)
     assert np.max(np.abs(dq - xv)) <= 0.25 * np.max(np.abs(xv))
+
+
+def test_e5m2_hand_values():
+    """E5M2: bias 15, 2 mantissa bits, subnormal step 2^-16, largest 57344."""
+    cases = [(1.0, 0x3C), (57344.0, 0x7B), (2.0 ** -16, 0x01), (2.0 ** -14, 0x04),
+             (1.25, 0x3D), (1.375, 0x3E),      # the tie 1.375 goes to the even mantissa (1.5)
+             (1.125, 0x3C), (-3.0, 0xC2), (61440.0, 0x7B), (1e9, 0x7B),   # saturation
+             (0.0, 0x00), (-0.0, 0x80), (3 * 2.0 ** -17, 0x02)]           # 1.5 steps -> 2 (even)
+    for v, code in cases:
+        assert int(F.e5m2_encode(np.array([v]))[0]) == code, (v, hex(code))
+    assert F.e5m2_decode(np.array([0x7C]))[0] == np.inf and np.isnan(F.e5m2_decode(np.array([0x7D]))[0])
+
+
+def test_e5m2_is_the_rounded_top_byte_of_fp16():
+    """Every fp16-representable value: the E5M2 code is the fp16 bit pattern
+    rounded to its upper byte (round half to even on the value, which for
+    same-sign IEEE patterns is integer rounding of the pattern), saturating at
+    0x7B -- numpy's float16 is the independent reference."""
+    bits = np.arange(0x7C00, dtype=np.uint16)                  # all finite non-negative fp16
+    vals = bits.view(np.float16).astype(np.float64)
+    low, high = bits & 0xFF, (bits >> 8).astype(np.int64)
+    up = (low > 0x80) | ((low == 0x80) & (high & 1 == 1))
+    want = np.minimum(high + up, 0x7B)
+    got = F.e5m2_encode(vals).astype(np.int64)
+    assert np.array_equal(got, want)
+    assert np.array_equal(F.e5m2_encode(-vals[1:]).astype(np.int64), want[1:] | 0x80)
+    # and decoding every finite code is exact
+    codes = np.arange(0x7C)
+    assert np.array_equal(F.e5m2_encode(F.e5m2_decode(codes)), codes.astype(np.uint8))
+
+
+def test_e8m0_rule_for_e5m2():
+    """scale exponent = floor(log2 amax) - 15 for E5M2 (OCP MX), biased by 127."""
+    assert int(F.e8m0_from_amax(np.array([1.0]), F.E5M2_EMAX)[0]) == 112
+    assert int(F.e8m0_from_amax(np.array([57344.0]), F.E5M2_EMAX)[0]) == 127
+    assert int(F.e8m0_from_amax(np.array([1.0]))[0]) == 119          # E4M3: - 8

@@ -199,3 +199,48 @@ def test_nvfp4_wgrad_exact_on_lossless_inputs():
     part = GM.nvfp4_rowscaled_wgrad(dyc, dys, dyo, xc, xs, xo, poff, N, K, groups=[3, 0],
                                     out_rows=[5, 1])
     assert np.array_equal(part[0], dw[3][[5, 1]]) and np.array_equal(part[1], dw[0][[5, 1]])
+
+
+def test_dgrad_exact_on_lossless_inputs():
+    """dY and W small integers: lossless in E5M2 (dY) and E4M3 (W) under any MX
+    scale, so dX must equal the exact per-expert integer product dY_g @ W_g.
+    n != k catches a transposed W copy; an empty expert and uneven row counts
+    catch a wrong group range."""
+    rng = np.random.default_rng(26)
+    sizes = np.array([9, 0, 40, 3], np.int32)
+    G, M, N, K = len(sizes), int(sizes.sum()), 256, 96
+    dyb, dyi = _int_bits(rng, (M, N))
+    wb, wi = _int_bits(rng, (G * N, K))
+    _, off = O.group_offsets(sizes)
+    dyd, dys = Q.mxfp8_rowwise(dyb, off, elem="e5m2")
+    woff = np.arange(G + 1, dtype=np.int64) * N
+    wtd, wts = Q.mxfp8_colwise(wb, woff, woff)
+    dx = GM.mxfp8_dgrad(dyd, dys, wtd, wts, off, N, K)
+    for g in range(G):
+        want = dyi[off[g]:off[g + 1]] @ wi[g * N:(g + 1) * N]
+        assert np.array_equal(dx[off[g]:off[g + 1]], want.astype(np.float64)), g
+    part = GM.mxfp8_dgrad(dyd, dys, wtd, wts, off, N, K, rows=[50, 0])
+    assert np.array_equal(part, dx[[50, 0]])
+
+
+def test_dgrad_e5m2_rounding_is_visible():
+    """Non-integer gradients: E5M2 keeps 2 mantissa bits, so dX differs from the
+    bf16 product by the E5M2 rounding, within the format's relative error 2^-3
+    per element (bounded per row by sum |dy_i w_ij| * 2^-3 plus the weights'
+    E4M3 error 2^-4)."""
+    rng = np.random.default_rng(27)
+    sizes = np.array([64], np.int32)
+    N, K = 128, 32
+    dy = rng.standard_normal((64, N)).astype(np.float32)
+    w = rng.standard_normal((N, K)).astype(np.float32)
+    dyb, wb = F.f32_to_bf16_bits_rne(dy), F.f32_to_bf16_bits_rne(w)
+    _, off = O.group_offsets(sizes)
+    dyd, dys = Q.mxfp8_rowwise(dyb, off, elem="e5m2")
+    woff = np.array([0, N])
+    wtd, wts = Q.mxfp8_colwise(wb, woff, woff)
+    dx = GM.mxfp8_dgrad(dyd, dys, wtd, wts, off, N, K)
+    dyv, wv = F.bf16_bits_to_f64(dyb), F.bf16_bits_to_f64(wb)
+    exact = dyv @ wv
+    bound = np.abs(dyv) @ np.abs(wv) * (2.0 ** -3 + 2.0 ** -4 + 2.0 ** -7)
+    assert np.all(np.abs(dx - exact) <= bound)
+    assert np.abs(dx - exact).max() > 0          # the gradient really is E5M2
