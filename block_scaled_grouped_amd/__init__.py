@@ -18,6 +18,7 @@ BSG_FPROP_TN = 0
 BSG_WGRAD_NT = 1
 BSG_OUT_BF16 = 0
 BSG_OUT_F32 = 1
+BSG_DGRAD_NN = 2
 BSG_MAX_GROUPS = 256
 BSG_COLWISE_PAD = 128
 DEV_NEGATIVE_SIZE = 1
@@ -25,6 +26,7 @@ DEV_OVER_CAPACITY = 2
 DEV_BAD_PADDING = 4
 
 EXPORTS = ("bsg_last_error", "bsg_version", "group_offsets_i32_to_i64", "grouped_quantize_mxfp8",
+           "grouped_quantize_mxfp8_rowwise_e5m2",
            "grouped_quantize_nvfp4_rowscaled", "grouped_quantize_nvfp4_rowscaled_colwise",
            "grouped_gemm_mxfp8", "grouped_gemm_nvfp4_rowscaled", "grouped_gemm_nvfp4_rowscaled_wgrad")
 
@@ -55,6 +57,8 @@ def load_library(path=LIB_PATH):
     lib.group_offsets_i32_to_i64.argtypes = [P, I64, I64, I64, P, P, I64, P, P]
     lib.grouped_quantize_mxfp8.restype = I32
     lib.grouped_quantize_mxfp8.argtypes = [P, I64, I64, I64, P, P, P, P, I64, P, P, P, P]
+    lib.grouped_quantize_mxfp8_rowwise_e5m2.restype = I32
+    lib.grouped_quantize_mxfp8_rowwise_e5m2.argtypes = [P, I64, I64, I64, P, P, P, P, P]
     lib.grouped_quantize_nvfp4_rowscaled.restype = I32
     lib.grouped_quantize_nvfp4_rowscaled.argtypes = [P, I64, I64, I64, P, P, P, P, P, P]
     lib.grouped_quantize_nvfp4_rowscaled_colwise.restype = I32
@@ -154,6 +158,25 @@ def grouped_quantize_mxfp8(x, offsets, G=None, rowwise=True, padded_offsets=None
     return out
 
 
+def grouped_quantize_mxfp8_rowwise_e5m2(x, offsets, G=None, row_data=None, row_scales=None,
+                                        status=None):
+    """bf16 [rows_cap, cols] gradient -> (E5M2 [rows_cap, cols], E8M0 scale words as
+    grouped_quantize_mxfp8's rowwise output)."""
+    import torch
+    lib = load_library()
+    _need_cuda(x, offsets)
+    rows_cap, cols = x.shape
+    G = offsets.numel() - 1 if G is None else G
+    if row_data is None:
+        row_data = torch.empty((rows_cap, cols), dtype=torch.uint8, device=x.device)
+    if row_scales is None:
+        row_scales = torch.empty(mx_scale_shape(rows_cap, cols), dtype=torch.uint8, device=x.device)
+    _check(lib.grouped_quantize_mxfp8_rowwise_e5m2(_ptr(x), rows_cap, cols, G, _ptr(offsets),
+                                                   _ptr(row_data), _ptr(row_scales), _ptr(status),
+                                                   _stream(x)))
+    return row_data, row_scales
+
+
 def grouped_quantize_nvfp4_rowscaled(x, offsets, G=None, data=None, block_scales=None, outer=None,
                                      status=None):
     """bf16 [rows_cap, cols] -> (E2M1 [rows_cap, cols/2], E4M3 [rows_cap, cols/16], f32 [rows_cap])."""
@@ -200,14 +223,14 @@ def grouped_quantize_nvfp4_rowscaled_colwise(x, offsets, padded_offsets, G=None,
 
 def grouped_gemm_mxfp8(mode, a, a_scales, b, b_scales, offsets, rows_cap, n, k, out=None,
                        out_dtype=BSG_OUT_BF16, G=None, status=None):
-    """FPROP_TN: out [rows_cap, n]; WGRAD_NT: out [G, n, k].  See include/bsg.h."""
+    """FPROP_TN, DGRAD_NN: out [rows_cap, n]; WGRAD_NT: out [G, n, k].  See include/bsg.h."""
     import torch
     lib = load_library()
     _need_cuda(a, a_scales, b, b_scales, offsets)
     G = offsets.numel() - 1 if G is None else G
     if out is None:
         dt = torch.float32 if out_dtype == BSG_OUT_F32 else torch.bfloat16
-        shape = (rows_cap, n) if mode == BSG_FPROP_TN else (G, n, k)
+        shape = (G, n, k) if mode == BSG_WGRAD_NT else (rows_cap, n)
         out = torch.empty(shape, dtype=dt, device=a.device)
     _check(lib.grouped_gemm_mxfp8(mode, G, _ptr(a), _ptr(a_scales), _ptr(b), _ptr(b_scales),
                                   _ptr(offsets), rows_cap, n, k, _ptr(out), out_dtype, _ptr(status),

@@ -102,6 +102,25 @@ int grouped_quantize_mxfp8(const void* x, int64_t rows_cap, int64_t cols, int64_
                     fn);
 }
 
+int grouped_quantize_mxfp8_rowwise_e5m2(const void* x, int64_t rows_cap, int64_t cols, int64_t G,
+                                        const int64_t* offsets, uint8_t* row_data,
+                                        uint8_t* row_scales, uint32_t* dev_status, void* stream) {
+  const char* fn = "grouped_quantize_mxfp8_rowwise_e5m2";
+  if (x == nullptr || offsets == nullptr || row_data == nullptr || row_scales == nullptr)
+    return fail(BSG_ERR_NULL, "%s: x, offsets, row_data and row_scales must be non-NULL", fn);
+  if (G < 1 || G > BSG_MAX_GROUPS)
+    return fail(BSG_ERR_SHAPE, "%s: G=%lld outside [1, %d]", fn, (long long)G, BSG_MAX_GROUPS);
+  if (rows_cap < 0 || cols <= 0 || cols % 32 != 0)
+    return fail(BSG_ERR_SHAPE, "%s: need rows_cap >= 0 and cols a positive multiple of 32 (got %lld, %lld)",
+                fn, (long long)rows_cap, (long long)cols);
+  if (!aligned16(x) || !aligned16(row_data) || !aligned4(row_scales))
+    return fail(BSG_ERR_ALIGN, "%s: x and row_data must be 16-byte aligned, row_scales 4-byte", fn);
+  return hip_result(bsg::launch_quantize_mxfp8_rowwise(static_cast<const uint16_t*>(x), rows_cap,
+                                                       cols, (int)G, offsets, row_data, row_scales,
+                                                       dev_status, (hipStream_t)stream, true),
+                    fn);
+}
+
 int grouped_quantize_nvfp4_rowscaled(const void* x, int64_t rows_cap, int64_t cols, int64_t G,
                                      const int64_t* offsets, uint8_t* data, uint8_t* block_scales,
                                      float* outer, uint32_t* dev_status, void* stream) {
@@ -159,7 +178,7 @@ int grouped_gemm_mxfp8(int mode, int64_t G, const uint8_t* a, const uint8_t* a_s
   if (a == nullptr || a_scales == nullptr || b == nullptr || b_scales == nullptr || offsets == nullptr ||
       out == nullptr)
     return fail(BSG_ERR_NULL, "%s: operands, scales, offsets and out must be non-NULL", fn);
-  if (mode != BSG_FPROP_TN && mode != BSG_WGRAD_NT)
+  if (mode != BSG_FPROP_TN && mode != BSG_WGRAD_NT && mode != BSG_DGRAD_NN)
     return fail(BSG_ERR_UNSUPPORTED, "%s: unknown mode %d", fn, mode);
   if (out_dtype != BSG_OUT_BF16 && out_dtype != BSG_OUT_F32)
     return fail(BSG_ERR_UNSUPPORTED, "%s: unknown out_dtype %d", fn, out_dtype);
@@ -168,9 +187,9 @@ int grouped_gemm_mxfp8(int mode, int64_t G, const uint8_t* a, const uint8_t* a_s
   if (rows_cap < 0 || n < 1 || k < 1)
     return fail(BSG_ERR_SHAPE, "%s: need rows_cap >= 0, n >= 1, k >= 1", fn);
   const int64_t esz = out_dtype == BSG_OUT_F32 ? 4 : 2;
-  if (mode == BSG_FPROP_TN) {
+  if (mode != BSG_WGRAD_NT) {
     if (k % 128 != 0)
-      return fail(BSG_ERR_SHAPE, "%s: FPROP needs k %% 128 == 0 (got %lld)", fn, (long long)k);
+      return fail(BSG_ERR_SHAPE, "%s: FPROP / DGRAD need k %% 128 == 0 (got %lld)", fn, (long long)k);
     if (256 * k >= kMaxTileBytes || 256 * n * esz >= kMaxTileBytes || n > 0x7fffffffLL)
       return fail(BSG_ERR_SHAPE, "%s: n or k too large for one tile's 32-bit offsets", fn);
     if ((k / 128) * 4 * rows_cap >= kMaxTileBytes || (k / 128) * 4 * G * n >= kMaxTileBytes)

@@ -155,7 +155,7 @@ hipError_t launch_group_offsets(const int32_t* sizes, int G, int64_t multiplier,
 
 hipError_t launch_quantize_mxfp8_rowwise(const uint16_t* x, int64_t rows_cap, int64_t cols, int G,
                                          const int64_t* offsets, uint8_t* data, uint8_t* scales,
-                                         uint32_t* status, hipStream_t stream);
+                                         uint32_t* status, hipStream_t stream, bool e5m2 = false);
 
 // Columnwise (and, if row_data != nullptr, the rowwise output in the same pass).
 hipError_t launch_quantize_mxfp8_colwise(const uint16_t* x, int64_t rows_cap, int64_t cols, int G,

@@ -344,11 +344,13 @@ __device__ __forceinline__ void read_scales(uint32_t lds, int s, int wm, int wn,
 // (i, j) is its transpose: lane (r, h) holds output row 32 i + r, and register
 // v column 32 j + 8 (v / 4) + 4 h + v % 4 -- four runs of four consecutive
 // columns, which the epilogue stores as whole 8- or 16-byte pieces.
-template <int OPSEL, int M>
+// AT: A's element format as the scaled MFMA encodes it (0 = E4M3, 1 = E5M2);
+// B is always E4M3.  B is the instruction's first source, A its second.
+template <int OPSEL, int M, int AT>
 __device__ __forceinline__ void mfma(const v8i (&fa)[4], const v8i (&fb)[4], const int (&sa)[4],
                                      const int (&sb)[4], v16f (&acc)[4][4]) {
   constexpr int i = M >> 2, j = M & 3;
-  acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, OPSEL,
+  acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, AT, OPSEL,
                                                               sb[j], OPSEL, sa[i]);
   // the MFMA intrinsic has no side effects, so IR passes may sink it past the
   // schedule's fences; an opaque use of its result keeps it in place
@@ -360,6 +362,7 @@ __device__ __forceinline__ void mfma(const v8i (&fa)[4], const v8i (&fb)[4], con
 // second K-step (same buffer, which has landed); then, one register at a time,
 // the staged B rows of pair kp + 1 into buffer s ^ 1 (free since the last
 // barrier) and the loads of pair kp + 2's B rows into the freed register.
+template <int AT>
 __device__ __forceinline__ void step_even(uint32_t lds, const Dma& d, int s, int kp, int np,
                                           const FragOff& fo, const v8i (&fa)[4],
                                           const v8i (&fb)[4], const int (&sa)[4],
@@ -368,7 +371,7 @@ __device__ __forceinline__ void step_even(uint32_t lds, const Dma& d, int s, int
   const bool live = kp + 2 < np;
   static_for<16>([&](auto mc) {
     constexpr int m = decltype(mc)::value;
-    mfma<0, m>(fa, fb, sa, sb, acc);
+    mfma<0, m, AT>(fa, fb, sa, sb, acc);
     fence();
     if constexpr (m < 8) read_frag<1, m>(lds, s, fo, na, nb);
     if constexpr (m >= 8) {
@@ -387,6 +390,7 @@ __device__ __forceinline__ void step_even(uint32_t lds, const Dma& d, int s, int
 // the first K-step) is free.  Between the remaining MFMAs, one per slot: the
 // LDS copies of pair kp + 2's A rows and scales into buffer s, and the scales
 // and first-step fragments of pair kp + 1.
+template <int AT>
 __device__ __forceinline__ void step_odd(uint32_t lds, const Dma& d, int w, int s, int kp, int np,
                                          const FragOff& fo, int wm, int wn, int r, int h,
                                          const v8i (&fa)[4], const v8i (&fb)[4],
@@ -398,7 +402,7 @@ __device__ __forceinline__ void step_odd(uint32_t lds, const Dma& d, int w, int 
   const bool live = kp + 2 < np;
   static_for<16>([&](auto mc) {
     constexpr int m = decltype(mc)::value;
-    mfma<1, m>(fa, fb, sa, sb, acc);
+    mfma<1, m, AT>(fa, fb, sa, sb, acc);
     fence();
     if constexpr (m == kBarrierAfter) {
       wait_and_barrier<kRegPerPair>();
@@ -414,6 +418,7 @@ __device__ __forceinline__ void step_odd(uint32_t lds, const Dma& d, int w, int 
   });
 }
 
+template <int AT>
 __device__ void run_tile(uint32_t lds, const TileDesc& t, int out_f32) {
   // opaque per-tile copy of the thread index: keeps the compiler from hoisting
   // every LDS / global offset of the tile body out of the persistent tile loop
@@ -451,8 +456,9 @@ __device__ void run_tile(uint32_t lds, const TileDesc& t, int out_f32) {
     static_for<8>([&](auto kc) { read_frag<0, decltype(kc)::value>(lds, 0, fo, f0a, f0b); });
     for (int kp = 0; kp < np; ++kp) {
       const int s = kp & 1;
-      step_even(lds, d, s, kp, np, fo, f0a, f0b, sca, scb, f1a, f1b, stage, acc);
-      step_odd(lds, d, w, s, kp, np, fo, wm, wn, r, h, f1a, f1b, sca, scb, f0a, f0b, nsa, nsb, acc);
+      step_even<AT>(lds, d, s, kp, np, fo, f0a, f0b, sca, scb, f1a, f1b, stage, acc);
+      step_odd<AT>(lds, d, w, s, kp, np, fo, wm, wn, r, h, f1a, f1b, sca, scb, f0a, f0b, nsa, nsb,
+                   acc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         sca[i] = nsa[i];
@@ -496,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(MxArgs p) {
   const int64_t ntn = (p.n + BN - 1) / BN;
   for (int g = tid; g < G; g += kThreads) {
     int64_t c;
-    if (MODE == 0) {
+    if (MODE != 1) {
       c = ((group_extent(sm.off, g) + BM - 1) / BM) * ntn;
     } else {
       const int64_t mp = group_extent(sm.off, g);
@@ -519,7 +525,7 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(MxArgs p) {
     const int g = find_group(sm.pre, G, tile);
     const int local = tile - sm.pre[g];
     TileDesc t;
-    if (MODE == 0) {
+    if (MODE != 1) {
       const int64_t m = group_extent(sm.off, g);
       const int mtiles = (int)((m + BM - 1) / BM);
       int mt, nt;
@@ -533,9 +539,17 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(MxArgs p) {
       t.as = p.as + 4 * row0;                  // A scales: [nq][rows_cap] words
       t.sqa = 4 * p.rows_cap;
       t.as_bytes = nq * t.sqa - 4 * row0;
-      t.bs = p.bs + 4 * brow0;                 // B scales: [nq][G * n] words
-      t.sqb = 4 * (int64_t)G * p.n;
-      t.bs_bytes = nq * t.sqb - 4 * brow0;
+      if (MODE == 0) {
+        t.bs = p.bs + 4 * brow0;               // B scales: [nq][G * n] words
+        t.sqb = 4 * (int64_t)G * p.n;
+        t.bs_bytes = nq * t.sqb - 4 * brow0;
+      } else {
+        // DGRAD: B = the columnwise copy of W, expert g's [n][k] block with its
+        // own [nq][n] scale words at byte g * n * k / 32
+        t.bs = p.bs + (int64_t)g * p.n * p.k / 32 + 4 * n0;
+        t.sqb = 4 * p.n;
+        t.bs_bytes = nq * t.sqb - 4 * n0;
+      }
       t.lda = t.ldb = p.k;
       const int64_t rv = sm.off[g] + m - row0;
       t.a_rows = (int)(rv < BM ? rv : BM);
@@ -573,7 +587,7 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(MxArgs p) {
       t.out_rows = t.a_rows;
       t.out_cols = t.b_rows;
     }
-    run_tile(lds, t, p.out_f32);
+    run_tile<MODE == 2 ? 1 : 0>(lds, t, p.out_f32);
   }
 }
 
@@ -599,15 +613,17 @@ hipError_t launch_gemm_mxfp8(int mode, int G, const uint8_t* a, const uint8_t* a
   MxArgs p{a, a_scales, b, b_scales, offsets, rows_cap, n, k, out, status, G, out_f32};
   // upper bound of the tile count from host-known shapes
   int64_t bound;
-  if (mode == 0) bound = ((rows_cap + BM - 1) / BM + G) * ((n + BN - 1) / BN);
+  if (mode != 1) bound = ((rows_cap + BM - 1) / BM + G) * ((n + BN - 1) / BN);
   else bound = (int64_t)G * ((n + BM - 1) / BM) * ((k + BN - 1) / BN);
   int64_t grid = device_cu_count();
   if (bound < grid) grid = bound;
   if (grid <= 0) return hipSuccess;
   if (mode == 0)
     hipLaunchKernelGGL(mx_gemm_kernel<0>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
-  else
+  else if (mode == 1)
     hipLaunchKernelGGL(mx_gemm_kernel<1>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(mx_gemm_kernel<2>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

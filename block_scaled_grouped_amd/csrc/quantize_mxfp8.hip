@@ -21,10 +21,13 @@ namespace bsg {
 
 namespace {
 
-// E8M0 byte from the largest bf16 magnitude bits of a block.
+// E8M0 byte from the largest bf16 magnitude bits of a block: the OCP rule,
+// exponent(amax) - emax of the element format (8 for E4M3, 15 for E5M2).
+template <bool E5M2 = false>
 __device__ __forceinline__ uint32_t e8m0_from_amax_bits(uint32_t amax_bits) {
+  constexpr uint32_t emax = E5M2 ? 15u : 8u;
   const uint32_t e = amax_bits >> 7;  // biased exponent of the bf16 magnitude
-  return e > 8u ? e - 8u : 0u;
+  return e > emax ? e - emax : 0u;
 }
 
 // The scale operand of the scaled converts: a float whose exponent field is the
@@ -53,27 +56,38 @@ __device__ __forceinline__ uint32_t amax2(uint32_t a, uint32_t b) {
 // Combines the two halves of an amax2 result.
 __device__ __forceinline__ uint32_t amax_fold(uint32_t m) { return max(m & 0xffffu, m >> 16); }
 
-// Overflowed E4M3 codes (S.1111.111, only produced for magnitudes above 464)
-// become the largest finite code S.1111.110, in each byte of a word.
-__device__ __forceinline__ uint32_t e4m3_saturate(uint32_t x) {
-  const uint32_t m = ((x & 0x7f7f7f7fu) + 0x01010101u) & 0x80808080u;
+// Overflowed codes become the largest finite code, in each byte of a word:
+// E4M3 S.1111.111 (only produced for magnitudes above 464) -> S.1111.110;
+// E5M2 S.11111.00 (the infinity the E5M2 convert gives past 57344, the only
+// exponent-31 code finite input produces) -> S.11110.11.
+template <bool E5M2 = false>
+__device__ __forceinline__ uint32_t fp8_saturate(uint32_t x) {
+  constexpr uint32_t gap = E5M2 ? 0x04040404u : 0x01010101u;  // 0x80 - first overflow code
+  const uint32_t m = ((x & 0x7f7f7f7fu) + gap) & 0x80808080u;
   return x - (m >> 7);
 }
 
-// Two packed bf16 (low element first), scaled -> two E4M3 bytes in the low
-// (HI = false) or high half of `old`.
-template <bool HI>
+// Two packed bf16 (low element first), scaled -> two E4M3 (or E5M2) bytes in
+// the low (HI = false) or high half of `old`.  Both converts are exact
+// round-to-nearest-even of x / 2^scale up to the overflow handled above.
+template <bool HI, bool E5M2 = false>
 __device__ __forceinline__ uint32_t cvt2(uint32_t w, float scale, uint32_t old) {
-  const v2s r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(
-      __builtin_bit_cast(v2s, old), __builtin_bit_cast(v2bf, w), scale, HI);
+  v2s r;
+  if constexpr (E5M2)
+    r = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(__builtin_bit_cast(v2s, old),
+                                                  __builtin_bit_cast(v2bf, w), scale, HI);
+  else
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(__builtin_bit_cast(v2s, old),
+                                                  __builtin_bit_cast(v2bf, w), scale, HI);
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// 8 bf16 (4 dwords) -> 8 E4M3 bytes (2 dwords).
+// 8 bf16 (4 dwords) -> 8 E4M3 (or E5M2) bytes (2 dwords).
+template <bool E5M2 = false>
 __device__ __forceinline__ uint2 cvt8(uint4 v, float scale) {
-  const uint32_t lo = cvt2<true>(v.y, scale, cvt2<false>(v.x, scale, 0u));
-  const uint32_t hi = cvt2<true>(v.w, scale, cvt2<false>(v.z, scale, 0u));
-  return make_uint2(e4m3_saturate(lo), e4m3_saturate(hi));
+  const uint32_t lo = cvt2<true, E5M2>(v.y, scale, cvt2<false, E5M2>(v.x, scale, 0u));
+  const uint32_t hi = cvt2<true, E5M2>(v.w, scale, cvt2<false, E5M2>(v.z, scale, 0u));
+  return make_uint2(fp8_saturate<E5M2>(lo), fp8_saturate<E5M2>(hi));
 }
 
 }  // namespace
@@ -94,6 +108,7 @@ __device__ __forceinline__ uint2 cvt8(uint4 v, float scale) {
 // once, not as up to 8 partial lines.
 constexpr int kRowChunk = 1024;
 
+template <bool E5M2>
 __global__ __launch_bounds__(256) void mx_rowwise_kernel(const uint16_t* __restrict__ x,
                                                          int64_t rows_cap, int64_t cols, int G,
                                                          const int64_t* __restrict__ offsets,
@@ -132,13 +147,13 @@ __global__ __launch_bounds__(256) void mx_rowwise_kernel(const uint16_t* __restr
     uint32_t am = amax_fold(amax2(amax2(v[h].x, v[h].y), amax2(v[h].z, v[h].w)));
     am = max(am, (uint32_t)__shfl_xor((int)am, 1, 64));
     am = max(am, (uint32_t)__shfl_xor((int)am, 2, 64));
-    const uint32_t byte = e8m0_from_amax_bits(am);
+    const uint32_t byte = e8m0_from_amax_bits<E5M2>(am);
     // gather the four block bytes of this lane's 128-element stretch
     const uint32_t b1 = (uint32_t)__shfl_down((int)byte, 4, 16);
     const uint32_t b2 = (uint32_t)__shfl_down((int)byte, 8, 16);
     const uint32_t b3 = (uint32_t)__shfl_down((int)byte, 12, 16);
     if (e[h] < cols) {
-      uint2 q = cvt8(v[h], e8m0_scale(byte));
+      uint2 q = cvt8<E5M2>(v[h], e8m0_scale(byte));
       *reinterpret_cast<uint2*>(data + row * cols + e[h]) = q;
       if ((lane & 15) == 0) {
         const uint32_t dw = byte | (b2 << 8) | (b1 << 16) | (b3 << 24);
@@ -151,13 +166,17 @@ __global__ __launch_bounds__(256) void mx_rowwise_kernel(const uint16_t* __restr
 
 hipError_t launch_quantize_mxfp8_rowwise(const uint16_t* x, int64_t rows_cap, int64_t cols, int G,
                                          const int64_t* offsets, uint8_t* data, uint8_t* scales,
-                                         uint32_t* status, hipStream_t stream) {
+                                         uint32_t* status, hipStream_t stream, bool e5m2) {
   if (rows_cap == 0) return hipSuccess;
   const int64_t chunks = (cols + kRowChunk - 1) / kRowChunk;
   const int64_t units = rows_cap * chunks;
   const int64_t blocks = (units + 3) / 4;
-  hipLaunchKernelGGL(mx_rowwise_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, rows_cap,
-                     cols, G, offsets, data, scales, status);
+  if (e5m2)
+    hipLaunchKernelGGL(mx_rowwise_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, x,
+                       rows_cap, cols, G, offsets, data, scales, status);
+  else
+    hipLaunchKernelGGL(mx_rowwise_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, x,
+                       rows_cap, cols, G, offsets, data, scales, status);
   return hipGetLastError();
 }
 

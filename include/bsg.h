@@ -48,7 +48,7 @@ typedef enum {
 #define BSG_DEV_BAD_PADDING   4u   /* padded offsets not multiples of 128 or smaller than
                                       the live sizes; that group was skipped */
 
-typedef enum { BSG_FPROP_TN = 0, BSG_WGRAD_NT = 1 } bsg_gemm_mode;
+typedef enum { BSG_FPROP_TN = 0, BSG_WGRAD_NT = 1, BSG_DGRAD_NN = 2 } bsg_gemm_mode;
 typedef enum { BSG_OUT_BF16 = 0, BSG_OUT_F32 = 1 } bsg_out_dtype;
 
 #define BSG_MAX_GROUPS 256
@@ -121,6 +121,20 @@ int grouped_quantize_mxfp8(const void* x, int64_t rows_cap, int64_t cols, int64_
                            const int64_t* offsets, uint8_t* row_data, uint8_t* row_scales,
                            const int64_t* padded_offsets, int64_t col_rows_cap, uint8_t* col_data,
                            uint8_t* col_scales, uint32_t* dev_status, void* stream);
+
+/*
+ * grouped_quantize_mxfp8_rowwise_e5m2
+ *
+ * Rowwise MXFP8 quantize of a gradient with E5M2 elements ("gemm.py",
+ * _compatible_fp8_gemm_dtypes: an E5M2 operand pairs with an E4M3 one), for the
+ * MoE dgrad.  Same blocks, scale order and arguments as the rowwise part of
+ * grouped_quantize_mxfp8; the E8M0 byte is exponent(amax) - 15 (the E5M2
+ * maximum 57344 sits in binade 15), elements round to nearest even and
+ * saturate at +-57344.
+ */
+int grouped_quantize_mxfp8_rowwise_e5m2(const void* x, int64_t rows_cap, int64_t cols, int64_t G,
+                                        const int64_t* offsets, uint8_t* row_data,
+                                        uint8_t* row_scales, uint32_t* dev_status, void* stream);
 
 /*
  * grouped_quantize_nvfp4_rowscaled
@@ -201,8 +215,18 @@ int grouped_quantize_nvfp4_rowscaled_colwise(const void* x, int64_t rows_cap, in
  *   offsets  [G+1] padded (multiple-of-128) token offsets of those copies;
  *            rows_cap = their capacity in padded tokens
  *   out      [G, n, k]; a group with no tokens gets zeros.
- * k must be a multiple of 128 (FPROP); n >= 1.  out_dtype: BSG_OUT_BF16 (round to
- * nearest even) or BSG_OUT_F32.
+ * mode BSG_DGRAD_NN (MoE dgrad, dX = dY W_g; an E5M2 gradient times E4M3
+ * weights, a pairing "gemm.py" _compatible_fp8_gemm_dtypes accepts):
+ *   dX[r, j] = sum_i dY[r, i] * W[g, i, j]   for r in [offsets[g], offsets[g+1])
+ *   a        [rows_cap, k] E5M2 rowwise dY (grouped_quantize_mxfp8_rowwise_e5m2,
+ *            cols = k, the contraction), a_scales [k/128][rows_cap] words
+ *   b        the columnwise copy of the weights W [G, k, n] viewed as G * k rows
+ *            of n columns (grouped_quantize_mxfp8 col_data with padded offsets
+ *            g * k): expert g's [n, k] block, i.e. W_g transposed, quantized
+ *            along k; b_scales its col_scales ([k/128][n] words per expert)
+ *   offsets, rows_cap, out as in FPROP (out [rows_cap, n]).
+ * k must be a multiple of 128 (FPROP, DGRAD); n >= 1.  out_dtype: BSG_OUT_BF16
+ * (round to nearest even) or BSG_OUT_F32.
  */
 int grouped_gemm_mxfp8(int mode, int64_t G, const uint8_t* a, const uint8_t* a_scales,
                        const uint8_t* b, const uint8_t* b_scales, const int64_t* offsets,

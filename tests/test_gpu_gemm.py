@@ -353,3 +353,45 @@ def test_nvfp4_wgrad_parity(sizes, N, K, out_f32):
             assert np.all(y[g] == 0.0) and not np.any(np.signbit(y[g])), "empty expert must be +0"
         else:
             gemm_tolerance_check(y[g], ref[g], out_f32, "group %d" % g)
+
+
+# ---------------------------------------------------------------- MXFP8 dgrad (E5M2 x E4M3)
+
+DGRAD_CASES = [
+    ([37, 0, 130, 5], 128, 96),          # n tail (96 < 256), one contraction step pair
+    ([300, 1, 0, 700], 384, 256),
+    ([64], 1024, 160),
+]
+
+
+@pytest.mark.parametrize("sizes,K,N", DGRAD_CASES)
+@pytest.mark.parametrize("out_f32", [True, False])
+def test_dgrad_parity(sizes, K, N, out_f32):
+    """dX [rows, N] = dY [rows, K] (E5M2) x W_g [K, N] (E4M3 columnwise copy)."""
+    rng = np.random.default_rng(K * 11 + N)
+    sizes = np.array(sizes, np.int32)
+    G, M = len(sizes), int(sizes.sum())
+    rows_cap = M + 17
+    dy = _bits(rng, (rows_cap, K))
+    w = _bits(rng, (G * K, N), std=0.05)
+    _, off = O.group_offsets(sizes)
+    woff = np.arange(G + 1, dtype=np.int64) * K
+    dyd, dys = bsg.grouped_quantize_mxfp8_rowwise_e5m2(bf16_dev(dy), to_dev(off))
+    wq = bsg.grouped_quantize_mxfp8(bf16_dev(w), to_dev(woff), rowwise=False,
+                                    padded_offsets=to_dev(woff), col_rows_cap=G * K)
+    rd, rs = Q.mxfp8_rowwise(dy, off, elem="e5m2")
+    wtd, wts = Q.mxfp8_colwise(w, woff, woff)
+    assert np.array_equal(host_u8(dyd)[:M], rd)
+    assert np.array_equal(host_u8(wq["col_data"]), wtd)
+    ref = GM.mxfp8_dgrad(rd, rs, wtd, wts, off, K, N)
+    dt = torch.float32 if out_f32 else torch.bfloat16
+    out = torch.full((rows_cap, N), float("nan"), dtype=dt, device=device())
+    bsg.grouped_gemm_mxfp8(bsg.BSG_DGRAD_NN, dyd, dys, wq["col_data"], wq["col_scales"],
+                           to_dev(off), rows_cap, N, K, out=out,
+                           out_dtype=bsg.BSG_OUT_F32 if out_f32 else bsg.BSG_OUT_BF16)
+    y = bf16_out_to_f64(out)
+    for g in range(G):
+        if sizes[g]:
+            gemm_tolerance_check(y[off[g]:off[g + 1]], ref[off[g]:off[g + 1]], out_f32,
+                                 "group %d" % g)
+    assert np.all(np.isnan(y[M:])), "capacity rows untouched"

@@ -99,6 +99,49 @@ def test_rowwise_codec_sweep_every_exponent():
     assert np.array_equal(host_u8(out["row_scales"]), want_s)
 
 
+@pytest.mark.parametrize("rows_cap,cols,sizes", ROW_CASES)
+def test_rowwise_e5m2_bit_exact(rows_cap, cols, sizes):
+    rng = np.random.default_rng(rows_cap + cols + 1)
+    bits = _bits(rng, rows_cap, cols)
+    sizes = np.array(sizes, np.int32)
+    live = int(sizes.sum())
+    bits[live:] = workloads.BF16_NAN_BITS
+    _, off = O.group_offsets(sizes)
+    want_d, want_s = Q.mxfp8_rowwise(bits, off, elem="e5m2")
+    d = filled_u8((rows_cap, cols))
+    s = filled_u8(bsg.mx_scale_shape(rows_cap, cols))
+    bsg.grouped_quantize_mxfp8_rowwise_e5m2(bf16_dev(bits), to_dev(off), row_data=d, row_scales=s)
+    d, s = host_u8(d), host_u8(s)
+    assert np.array_equal(d[:live], want_d)
+    assert np.array_equal(s[:, :live], want_s)
+    assert np.all(d[live:] == SENTINEL) and np.all(s[:, live:] == SENTINEL)
+
+
+def test_rowwise_e5m2_codec_sweep_every_exponent():
+    """As the E4M3 sweep, for E5M2 elements: every binade, subnormals, zeros,
+    and block members in the top binade that round past 57344 (saturation)."""
+    rng = np.random.default_rng(98)
+    nblk = 1 << 15
+    exp_amax = rng.integers(-133, 128, nblk)
+    man = rng.integers(0, 128, (nblk, 32))
+    exps = exp_amax[:, None] - rng.integers(0, 40, (nblk, 32))
+    exps[:, 0] = exp_amax
+    exps[:, 1] = exp_amax                     # a second top-binade element
+    man[:, 1] = rng.integers(112, 128, nblk)  # near the top: rounds past 1.75 * 2^15 after scaling
+    vals = np.ldexp(1.0 + man / 128.0, exps)
+    vals[rng.random((nblk, 32)) < 0.05] = 0.0
+    vals *= np.where(rng.random((nblk, 32)) < 0.5, -1.0, 1.0)
+    vals = np.clip(vals, -3.0e38, 3.0e38)
+    bits = F.f32_to_bf16_bits_rne(vals.astype(np.float32)).reshape(-1, 1024)
+    rows = bits.shape[0]
+    off = np.array([0, rows])
+    want_d, want_s = Q.mxfp8_rowwise(bits, off, elem="e5m2")
+    assert np.any((want_d & 0x7F) == 0x7B)    # saturation is exercised
+    d, s = bsg.grouped_quantize_mxfp8_rowwise_e5m2(bf16_dev(bits), to_dev(off))
+    assert np.array_equal(host_u8(d), want_d)
+    assert np.array_equal(host_u8(s), want_s)
+
+
 # ---------------------------------------------------------------- MXFP8 columnwise (+ fused rowwise)
 
 COL_CASES = [
