@@ -163,6 +163,50 @@ class MxWgrad(Case):
         self._rec(ev, 4)
 
 
+class MxDgrad(Case):
+    """offsets -> E5M2 rowwise quantize of dY -> columnwise (transposed) E4M3
+    quantize of W -> grouped GEMM dgrad (dX = dY W_g)."""
+
+    def __init__(self, name, dev):
+        self.name = name
+        self.w = w = workloads.get(name)
+        t = workloads.tensors(w, device=dev)
+        self.dy, self.wt = t["dy"], t["w"]
+        G, N, K, R = w.G, w.n, w.k, w.rows_cap      # K: contraction, N: dX columns
+        self.G, self.N, self.K, self.R = G, N, K, R
+        self.sizes = torch.from_numpy(w.sizes).to(dev)
+        self.off = torch.empty(G + 1, dtype=torch.int64, device=dev)
+        # the weights' expert offsets as rows of the [G * K, N] view (static)
+        self.woff = torch.arange(G + 1, dtype=torch.int64, device=dev) * K
+        self.dyd = torch.empty((R, K), dtype=torch.uint8, device=dev)
+        self.dys = torch.empty(bsg.mx_scale_shape(R, K), dtype=torch.uint8, device=dev)
+        self.wc = torch.empty(G * K * N, dtype=torch.uint8, device=dev)
+        self.wcs = torch.empty(G * K * N // 32, dtype=torch.uint8, device=dev)
+        self.dx = torch.empty((R, N), dtype=torch.bfloat16, device=dev)
+        self.kernels = ("offsets", "quantize_dy", "quantize_w", "gemm")
+        live = w.live_rows
+        per = 1.0 + 1.0 / 32
+        self.flops = 2.0 * live * K * N
+        self.bytes = {"offsets": 0.0, "quantize_dy": live * K * (2.0 + per),
+                      "quantize_w": G * K * N * (2.0 + per),
+                      "gemm": (live * K + G * K * N) * per + live * N * 2.0}
+
+    def step(self, ev=None):
+        self._rec(ev, 0)
+        bsg.group_offsets_i32_to_i64(self.sizes, offsets=self.off, capacity=self.R)
+        self._rec(ev, 1)
+        bsg.grouped_quantize_mxfp8_rowwise_e5m2(self.dy, self.off, row_data=self.dyd,
+                                                row_scales=self.dys)
+        self._rec(ev, 2)
+        bsg.grouped_quantize_mxfp8(self.wt.view(self.G * self.K, self.N), self.woff, rowwise=False,
+                                   padded_offsets=self.woff, col_rows_cap=self.G * self.K,
+                                   col_data=self.wc, col_scales=self.wcs)
+        self._rec(ev, 3)
+        bsg.grouped_gemm_mxfp8(bsg.BSG_DGRAD_NN, self.dyd, self.dys, self.wc, self.wcs, self.off,
+                               self.R, self.N, self.K, out=self.dx, out_dtype=bsg.BSG_OUT_BF16)
+        self._rec(ev, 4)
+
+
 class Nvfp4Wgrad(Case):
     """offsets -> row-scaled NVFP4 columnwise quantize of dY and X -> NVFP4
     grouped GEMM wgrad with the fused per-expert outer-scale epilogue."""
@@ -271,6 +315,8 @@ def make_case(name, dev):
         return Nvfp4Fprop(name, dev)
     if name == "nvfp4_wgrad":
         return Nvfp4Wgrad(name, dev)
+    if name == "dgrad":
+        return MxDgrad(name, dev)
     raise KeyError(name)
 
 
@@ -416,7 +462,7 @@ def main():
         log("[bench] copy calibration: 3 x 268435456 bytes read + written")
         del src, dst
 
-    names = ["fprop"] if args.no_extra else ["fprop", "tiny", "wgrad", "zipf", "nvfp4",
+    names = ["fprop"] if args.no_extra else ["fprop", "tiny", "wgrad", "zipf", "dgrad", "nvfp4",
                                              "nvfp4_wgrad"]
     if args.only:
         names = args.only.split(",")
@@ -435,7 +481,7 @@ def main():
 
     head = results.get("fprop") or results[names[0]]
     achieved = head["gemm_tflops"]
-    qx = head["kernels_us"]["quantize_x"]
+    qx = head["kernels_us"].get("quantize_x", {})
     line = {
         "metric": METRIC,
         "value": head["step_tflops"],

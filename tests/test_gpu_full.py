@@ -215,3 +215,40 @@ def test_full_nvfp4_wgrad():
         y = dw[g, i0:i0 + 32, j0:j0 + 32].float().cpu().numpy().astype(np.float64)
         gemm_tolerance_check(y, ref[g], False, "nvfp4 wgrad group %d" % g)
     assert not torch.isnan(dw).any()
+
+
+def test_full_dgrad():
+    """MoE dgrad at the fprop shapes: dX [16384, 4096] = dY [16384, 14336] (E5M2)
+    x W_g [14336, 4096] (E4M3 columnwise copy); sampled rows of every expert
+    and sampled columns, the E5M2 rows and the weights' columns checked
+    bit-exact on the way."""
+    dev = device()
+    case = bench.make_case("dgrad", dev)
+    case.dx.fill_(float("nan"))
+    case.step()
+    torch.cuda.synchronize()
+    w = case.w
+    G, N, K = w.G, w.n, w.k
+    _, off = O.group_offsets(w.sizes)
+    rng = np.random.default_rng(12)
+    rows = _sample_rows(off, rng, per_group=2)
+    cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 14)]))
+    dyb = workloads.bf16_bits(case.dy[torch.from_numpy(rows).to(dev)])
+    ad, asc = Q.mxfp8_rowwise(dyb, np.array([0, len(rows)]), elem="e5m2")
+    assert np.array_equal(host_u8(case.dyd)[rows], ad)
+    assert np.array_equal(host_u8(case.dys)[:, rows, :], asc)
+    grp = np.searchsorted(off, rows, side="right") - 1
+    y = bf16_out_to_f64(case.dx)
+    wcd, wcs = host_u8(case.wc), host_u8(case.wcs)
+    nq = K // 128
+    for g in np.unique(grp):
+        wb = workloads.bf16_bits(case.wt[g][:, torch.from_numpy(cols).to(dev)])    # [K, len(cols)]
+        bd, bs = Q.mxfp8_colwise(wb, np.array([0, K]), np.array([0, K]))
+        blk = wcd[g * K * N:(g + 1) * K * N].reshape(N, K)[cols]
+        assert np.array_equal(blk, bd.reshape(len(cols), K)), "weight copy, expert %d" % g
+        sblk = wcs[g * K * N // 32:(g + 1) * K * N // 32].reshape(nq, N, 4)[:, cols, :]
+        assert np.array_equal(sblk, bs.reshape(nq, len(cols), 4)), "weight scales, expert %d" % g
+        sel = np.nonzero(grp == g)[0]
+        ref = GM.mxfp8_dgrad(ad[sel], asc[:, sel], bd, bs, np.array([0, len(sel)]), K, len(cols))
+        gemm_tolerance_check(y[rows[sel]][:, cols], ref, False, "dgrad group %d" % g)
+    assert not np.isnan(y[:int(off[-1])]).any(), "every live output row written"

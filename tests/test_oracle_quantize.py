@@ -40,11 +40,11 @@ def test_workload_size_invariants(name):
     _, off = O.group_offsets(w.sizes)
     assert off[-1] == np.sum(w.sizes.astype(np.int64))
     assert O.check_capacity(off, w.rows_cap)
-    if name in ("tiny", "fprop", "wgrad", "zipf", "nvfp4_wgrad"):
+    if name in ("tiny", "fprop", "wgrad", "zipf", "nvfp4_wgrad", "dgrad"):
         assert off[-1] == w.rows_cap
     else:
         assert off[-1] < w.rows_cap
-    if name == "fprop":
+    if name in ("fprop", "dgrad"):
         assert np.all(w.sizes % 128 == 0) and len(set(w.sizes.tolist())) > 1
     if name in ("wgrad", "nvfp4_wgrad"):
         assert np.sum(w.sizes == 0) == 2 and np.all(w.sizes[w.sizes > 0] % 32 != 0)

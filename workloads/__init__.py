@@ -24,6 +24,8 @@ nvfp4  8 experts, K=4096, N_e = 2048 (even e) / 4096 (odd e), 16384 live rows of
 nvfp4_wgrad
        the wgrad shapes and size recipe (its own seed) for the row-scaled NVFP4
        weight gradient: dY [16384, 4096], X [16384, 4096] ~ N(0, 1)
+dgrad  the fprop experts' data gradient: sizes as fprop (its own seed), dY
+       [16384, 14336] ~ N(0, 1), W [8, 14336, 4096] ~ N(0, 0.02); dX [16384, 4096]
 =====  ===========================================================================
 """
 
@@ -32,7 +34,7 @@ from typing import List, Optional
 
 import numpy as np
 
-CONFIG_NAMES = ("tiny", "fprop", "wgrad", "zipf", "nvfp4", "nvfp4_wgrad")
+CONFIG_NAMES = ("tiny", "fprop", "wgrad", "zipf", "nvfp4", "nvfp4_wgrad", "dgrad")
 SEED_BASE = 1000
 BF16_NAN_BITS = 0x7FC0
 
@@ -74,7 +76,7 @@ def group_sizes(name, seed=None):
     rng = np.random.Generator(np.random.PCG64(SEED_BASE + idx if seed is None else seed))
     if name == "tiny":
         s = np.array([32, 0, 64, 32])
-    elif name == "fprop":
+    elif name in ("fprop", "dgrad"):
         s = 128 * _dirichlet_multinomial(rng, 128, 8)
     elif name in ("wgrad", "nvfp4_wgrad"):
         empty = rng.choice(8, size=2, replace=False)
@@ -110,6 +112,9 @@ def get(name, seed=None):
         return Workload(name, "wgrad", s, 16384, 4096, 4096, seed=sd)
     if name == "zipf":
         return Workload(name, "fprop", s, 32768, 7168, 2048, seed=sd, w_std=0.02)
+    if name == "dgrad":
+        # k: the contraction (fprop's N), n: dX columns (fprop's K)
+        return Workload(name, "dgrad", s, 16384, 14336, 4096, seed=sd, w_std=0.02)
     if name == "nvfp4":
         npg = [2048 if e % 2 == 0 else 4096 for e in range(8)]
         return Workload(name, "nvfp4", s, 18432, 4096, 4096, n_per_group=npg, seed=sd, w_std=0.02)
@@ -153,6 +158,7 @@ def tensors(w: Workload, device="cpu"):
 
     fprop: {"x": [rows_cap, k], "w": [G, n, k]}
     wgrad: {"dy": [rows_cap, n], "x": [rows_cap, k]}
+    dgrad: {"dy": [rows_cap, k], "w": [G, k, n]}
     nvfp4: {"x": [rows_cap, k], "w": [sum(N_e), k]}
     Rows past sum(sizes) are capacity rows filled with bf16 NaN."""
     import torch
@@ -167,6 +173,9 @@ def tensors(w: Workload, device="cpu"):
     elif w.mode == "wgrad":
         out["dy"] = _randn_bf16(torch, gen, (w.rows_cap, w.n), w.x_std, device)
         out["x"] = _randn_bf16(torch, gen, (w.rows_cap, w.k), w.x_std, device)
+    elif w.mode == "dgrad":
+        out["dy"] = _randn_bf16(torch, gen, (w.rows_cap, w.k), w.x_std, device)
+        out["w"] = _randn_bf16(torch, gen, (w.G, w.k, w.n), w.w_std, device)
     elif w.mode == "nvfp4":
         out["x"] = _randn_bf16(torch, gen, (w.rows_cap, w.k), w.x_std, device)
         out["w"] = _randn_bf16(torch, gen, (int(sum(w.n_per_group)), w.k), w.w_std, device)
