@@ -183,3 +183,28 @@ def mxfp8_dgrad(dy_data, dy_scales, wt_data, wt_scales, offsets, n, k, rows=None
         ws = np.asarray(wt_scales[g * n * k // MX_BLOCK:(g + 1) * n * k // MX_BLOCK]).reshape(nq, k, 4)
         out[sel] = a @ mxfp8_dequant_rows(wt, ws, n).T
     return out
+
+
+def epilogue(s, groups, alpha=None, beta=None, c_old=None, bias=None):
+    """Per-group epilogue of the grouped GEMM ("gemm.py", ``grouped_gemm``: bias
+    of shape (num_gemms, N) over the output columns; the graph-safe grouped
+    primitive's per-group float32 alpha and beta, defaults 1 and 0; "[Common]
+    [PyTorch] Add row-scaled NVFP4 support to grouped-tensor GEMM": copy or
+    accumulate into the output):
+        Y[r, j] = alpha[g] * S[r, j] + beta[g] * C[r, j] + bias[g, j]
+    with g the group of output row r (``groups``, one entry per row of S), C
+    the output's previous contents, read only where beta[g] != 0.  Reading:
+    the three terms are combined before the single rounding to the output
+    type.  Returns float64 like S."""
+    s = np.asarray(s, dtype=np.float64)
+    g = np.asarray(groups, dtype=np.int64)
+    a = 1.0 if alpha is None else np.asarray(alpha, dtype=np.float64)[g][:, None]
+    y = a * s
+    if beta is not None:
+        b = np.asarray(beta, dtype=np.float64)[g]
+        if np.any(b != 0):
+            c = np.asarray(c_old, dtype=np.float64)
+            y = y + np.where(b[:, None] != 0, b[:, None] * np.where(b[:, None] != 0, c, 0.0), 0.0)
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float64)[g]
+    return y

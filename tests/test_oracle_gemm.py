@@ -244,3 +244,34 @@ def test_dgrad_e5m2_rounding_is_visible():
     bound = np.abs(dyv) @ np.abs(wv) * (2.0 ** -3 + 2.0 ** -4 + 2.0 ** -7)
     assert np.all(np.abs(dx - exact) <= bound)
     assert np.abs(dx - exact).max() > 0          # the gradient really is E5M2
+
+
+def test_epilogue_exact_on_lossless_inputs():
+    """alpha, beta and bias values that are exact in fp64 and distinct per
+    group, on lossless integer operands: the fprop output must equal
+    alpha_g * (X_g W_g^T) + beta_g * C + bias_g exactly, row by row in its own
+    group; beta = 0 must not read C (NaN there stays out of the result)."""
+    rng = np.random.default_rng(28)
+    sizes = np.array([5, 0, 9], np.int32)
+    G, M, N, K = 3, 14, 40, 128
+    xb, xi = _int_bits(rng, (M, K))
+    wb, wi = _int_bits(rng, (G * N, K))
+    _, off = O.group_offsets(sizes)
+    ad, asc = Q.mxfp8_rowwise(xb, off)
+    bd, bsc = Q.mxfp8_rowwise(wb, np.array([0, G * N]))
+    s = GM.mxfp8_fprop(ad, asc, bd.reshape(G, N, K), bsc, off, K)
+    grp = np.searchsorted(off, np.arange(M), side="right") - 1
+    alpha = np.array([0.5, 3.0, -2.0])
+    beta = np.array([1.0, 0.0, 0.0])
+    c = rng.integers(-9, 10, (M, N)).astype(np.float64)
+    c[grp == 2] = np.nan                       # beta 0: never read
+    bias = rng.integers(-4, 5, (G, N)).astype(np.float64) * 0.25
+    y = GM.epilogue(s, grp, alpha, beta, c, bias)
+    for r in range(M):
+        g = grp[r]
+        want = alpha[g] * (xi[r] @ wi[g * N:(g + 1) * N].T) + bias[g]
+        if beta[g] != 0:
+            want = want + beta[g] * c[r]
+        assert np.array_equal(y[r], want), r
+    # the defaults are the plain product
+    assert np.array_equal(GM.epilogue(s, grp), s)
