@@ -28,7 +28,8 @@ DEV_BAD_PADDING = 4
 EXPORTS = ("bsg_last_error", "bsg_version", "group_offsets_i32_to_i64", "grouped_quantize_mxfp8",
            "grouped_quantize_mxfp8_rowwise_e5m2",
            "grouped_quantize_nvfp4_rowscaled", "grouped_quantize_nvfp4_rowscaled_colwise",
-           "grouped_gemm_mxfp8", "grouped_gemm_nvfp4_rowscaled", "grouped_gemm_nvfp4_rowscaled_wgrad")
+           "grouped_gemm_mxfp8", "grouped_gemm_mxfp8_ex", "grouped_gemm_nvfp4_rowscaled",
+           "grouped_gemm_nvfp4_rowscaled_wgrad")
 
 _lib = None
 
@@ -66,6 +67,9 @@ def load_library(path=LIB_PATH):
                                                              P, P]
     lib.grouped_gemm_mxfp8.restype = I32
     lib.grouped_gemm_mxfp8.argtypes = [I32, I64, P, P, P, P, P, I64, I64, I64, P, I32, P, P]
+    lib.grouped_gemm_mxfp8_ex.restype = I32
+    lib.grouped_gemm_mxfp8_ex.argtypes = [I32, I64, P, P, P, P, P, I64, I64, I64, P, I32, P, P, P,
+                                          P, P]
     lib.grouped_gemm_nvfp4_rowscaled.restype = I32
     lib.grouped_gemm_nvfp4_rowscaled.argtypes = [I64, P, P, P, P, I64, I64, P, P, P, P, P, I64, I32,
                                                  P, P, P]
@@ -235,6 +239,22 @@ def grouped_gemm_mxfp8(mode, a, a_scales, b, b_scales, offsets, rows_cap, n, k, 
     _check(lib.grouped_gemm_mxfp8(mode, G, _ptr(a), _ptr(a_scales), _ptr(b), _ptr(b_scales),
                                   _ptr(offsets), rows_cap, n, k, _ptr(out), out_dtype, _ptr(status),
                                   _stream(a)))
+    return out
+
+
+def grouped_gemm_mxfp8_ex(mode, a, a_scales, b, b_scales, offsets, rows_cap, n, k, out,
+                          out_dtype=BSG_OUT_BF16, alpha=None, beta=None, bias=None, G=None,
+                          status=None):
+    """grouped_gemm_mxfp8 with out = alpha[g] * S + beta[g] * out + bias[g]
+    (float32 [G] alpha / beta, [G, output columns] bias; None = 1 / 0 / none).
+    `out` is required (it is read where beta != 0).  See include/bsg.h."""
+    lib = load_library()
+    _need_cuda(a, a_scales, b, b_scales, offsets, out)
+    G = offsets.numel() - 1 if G is None else G
+    _check(lib.grouped_gemm_mxfp8_ex(mode, G, _ptr(a), _ptr(a_scales), _ptr(b), _ptr(b_scales),
+                                     _ptr(offsets), rows_cap, n, k, _ptr(out), out_dtype,
+                                     _ptr(alpha), _ptr(beta), _ptr(bias), _ptr(status),
+                                     _stream(a)))
     return out
 
 

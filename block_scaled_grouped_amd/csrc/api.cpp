@@ -170,11 +170,11 @@ int grouped_quantize_nvfp4_rowscaled_colwise(const void* x, int64_t rows_cap, in
                     fn);
 }
 
-int grouped_gemm_mxfp8(int mode, int64_t G, const uint8_t* a, const uint8_t* a_scales,
-                       const uint8_t* b, const uint8_t* b_scales, const int64_t* offsets,
-                       int64_t rows_cap, int64_t n, int64_t k, void* out, int out_dtype,
-                       uint32_t* dev_status, void* stream) {
-  const char* fn = "grouped_gemm_mxfp8";
+static int gemm_mxfp8_impl(const char* fn, int mode, int64_t G, const uint8_t* a,
+                           const uint8_t* a_scales, const uint8_t* b, const uint8_t* b_scales,
+                           const int64_t* offsets, int64_t rows_cap, int64_t n, int64_t k,
+                           void* out, int out_dtype, const float* alpha, const float* beta,
+                           const float* bias, uint32_t* dev_status, void* stream) {
   if (a == nullptr || a_scales == nullptr || b == nullptr || b_scales == nullptr || offsets == nullptr ||
       out == nullptr)
     return fail(BSG_ERR_NULL, "%s: operands, scales, offsets and out must be non-NULL", fn);
@@ -203,10 +203,32 @@ int grouped_gemm_mxfp8(int mode, int64_t G, const uint8_t* a, const uint8_t* a_s
   }
   if (!aligned16(a) || !aligned16(b) || !aligned4(a_scales) || !aligned4(b_scales) || !aligned4(out))
     return fail(BSG_ERR_ALIGN, "%s: a and b must be 16-byte aligned; scales and out 4-byte", fn);
+  if (!aligned4(alpha) || !aligned4(beta) || !aligned16(bias))
+    return fail(BSG_ERR_ALIGN, "%s: alpha and beta must be 4-byte aligned, bias 16-byte", fn);
+  if (bias != nullptr && ((mode == BSG_WGRAD_NT ? k : n) % 4 != 0))
+    return fail(BSG_ERR_SHAPE, "%s: a bias needs a multiple of 4 output columns", fn);
   return hip_result(bsg::launch_gemm_mxfp8(mode, (int)G, a, a_scales, b, b_scales, offsets, rows_cap,
                                            n, k, out, out_dtype == BSG_OUT_F32, dev_status,
-                                           (hipStream_t)stream),
+                                           (hipStream_t)stream, alpha, beta, bias),
                     fn);
+}
+
+int grouped_gemm_mxfp8(int mode, int64_t G, const uint8_t* a, const uint8_t* a_scales,
+                       const uint8_t* b, const uint8_t* b_scales, const int64_t* offsets,
+                       int64_t rows_cap, int64_t n, int64_t k, void* out, int out_dtype,
+                       uint32_t* dev_status, void* stream) {
+  return gemm_mxfp8_impl("grouped_gemm_mxfp8", mode, G, a, a_scales, b, b_scales, offsets,
+                         rows_cap, n, k, out, out_dtype, nullptr, nullptr, nullptr, dev_status,
+                         stream);
+}
+
+int grouped_gemm_mxfp8_ex(int mode, int64_t G, const uint8_t* a, const uint8_t* a_scales,
+                          const uint8_t* b, const uint8_t* b_scales, const int64_t* offsets,
+                          int64_t rows_cap, int64_t n, int64_t k, void* out, int out_dtype,
+                          const float* alpha, const float* beta, const float* bias,
+                          uint32_t* dev_status, void* stream) {
+  return gemm_mxfp8_impl("grouped_gemm_mxfp8_ex", mode, G, a, a_scales, b, b_scales, offsets,
+                         rows_cap, n, k, out, out_dtype, alpha, beta, bias, dev_status, stream);
 }
 
 int grouped_gemm_nvfp4_rowscaled(int64_t G, const uint8_t* a, const uint8_t* a_scales,

@@ -180,7 +180,9 @@ hipError_t launch_quantize_nvfp4_rowscaled_colwise(const uint16_t* x, int64_t ro
 hipError_t launch_gemm_mxfp8(int mode, int G, const uint8_t* a, const uint8_t* a_scales,
                              const uint8_t* b, const uint8_t* b_scales, const int64_t* offsets,
                              int64_t rows_cap, int64_t n, int64_t k, void* out, int out_f32,
-                             uint32_t* status, hipStream_t stream);
+                             uint32_t* status, hipStream_t stream,
+                             const float* alpha = nullptr, const float* beta = nullptr,
+                             const float* bias = nullptr);
 
 hipError_t launch_gemm_nvfp4(int G, const uint8_t* a, const uint8_t* a_scales,
                              const float* a_outer, const int64_t* offsets, int64_t rows_cap,

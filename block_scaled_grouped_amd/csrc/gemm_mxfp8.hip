@@ -93,6 +93,9 @@ struct MxArgs {
   uint32_t* status;
   int G;
   int out_f32;
+  const float* alpha;  // [G] or null (1): epilogue terms, used by the EX kernels
+  const float* beta;   // [G] or null (0)
+  const float* bias;   // [G, output columns] or null
 };
 
 struct TileDesc {
@@ -108,6 +111,8 @@ struct TileDesc {
   char* out;          // element (0, 0) of the output tile
   int64_t ldc;        // output row stride in elements
   int out_rows, out_cols;
+  float alpha, beta;  // the group's epilogue terms (EX kernels)
+  const float* bias;  // the group's bias at the tile's first column, or null
 };
 
 struct Sched {
@@ -418,8 +423,8 @@ __device__ __forceinline__ void step_odd(uint32_t lds, const Dma& d, int w, int 
   });
 }
 
-template <int AT>
-__device__ void run_tile(uint32_t lds, const TileDesc& t, int out_f32) {
+template <int AT, bool EX>
+__device__ __forceinline__ void run_tile(uint32_t lds, const TileDesc& t, int out_f32) {
   // opaque per-tile copy of the thread index: keeps the compiler from hoisting
   // every LDS / global offset of the tile body out of the persistent tile loop
   int tid = threadIdx.x;
@@ -477,6 +482,22 @@ __device__ void run_tile(uint32_t lds, const TileDesc& t, int out_f32) {
   int ldc = (int)t.ldc;
   asm volatile("" : "+s"(ldc));
   const int row = wm * 128 + r, col = wn * 128 + 4 * h;
+  if constexpr (EX) {
+    EpiTerms ep;
+    ep.alpha = t.alpha;
+    ep.beta = t.beta;
+    ep.has_bias = t.bias != nullptr;
+    ep.bias = make_rsrc(t.bias, ep.has_bias ? (int64_t)t.out_cols * 4 : 0);
+    const bool wide = (ldc & 3) == 0 && (t.out_cols & 3) == 0;
+    if (out_f32) {
+      if (wide) store_tile_ex<true, true>(acc, ro, ldc, row, col, t.out_cols, ep);
+      else store_tile_ex<false, true>(acc, ro, ldc, row, col, t.out_cols, ep);
+    } else {
+      if (wide) store_tile_ex<true, false>(acc, ro, ldc, row, col, t.out_cols, ep);
+      else store_tile_ex<false, false>(acc, ro, ldc, row, col, t.out_cols, ep);
+    }
+    return;
+  }
   if (out_f32) {
     if ((ldc & 3) == 0 && (t.out_cols & 3) == 0)
       store_tile<true, true>(acc, ro, ldc, row, col, h, t.out_cols);
@@ -490,7 +511,7 @@ __device__ void run_tile(uint32_t lds, const TileDesc& t, int out_f32) {
   }
 }
 
-template <int MODE>
+template <int MODE, bool EX>
 __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(MxArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_ring[kBufs * kBufBytes];
   __shared__ Sched sm;
@@ -525,6 +546,7 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(MxArgs p) {
     const int g = find_group(sm.pre, G, tile);
     const int local = tile - sm.pre[g];
     TileDesc t;
+    int64_t col_first;  // the tile's first output column
     if (MODE != 1) {
       const int64_t m = group_extent(sm.off, g);
       const int mtiles = (int)((m + BM - 1) / BM);
@@ -532,6 +554,7 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(MxArgs p) {
       super_tile<kSuperM, kSuperN>(local, mtiles, (int)ntn, mt, nt);
       const int64_t row0 = sm.off[g] + (int64_t)mt * BM;
       const int64_t n0 = (int64_t)nt * BN;
+      col_first = n0;
       const int64_t nq = p.k / 128;            // scale words per row
       const int64_t brow0 = (int64_t)g * p.n + n0;
       t.a = p.a + row0 * p.k;
@@ -567,6 +590,7 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(MxArgs p) {
       int it, jt;
       super_tile<kSuperM, kSuperN>(local, ntm, ntk, it, jt);
       const int64_t n0 = (int64_t)it * BM, c0 = (int64_t)jt * BN;
+      col_first = c0;
       const int64_t t0 = sm.off[g];
       // group g's blocks: data [n or k][mp], scales [mp / 128][n or k] words
       t.a = p.a + t0 * p.n + n0 * mp;
@@ -587,7 +611,17 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(MxArgs p) {
       t.out_rows = t.a_rows;
       t.out_cols = t.b_rows;
     }
-    run_tile<MODE == 2 ? 1 : 0>(lds, t, p.out_f32);
+    if constexpr (EX) {
+      // the group's terms, made provably uniform (g comes from LDS)
+      const int64_t outw = MODE == 1 ? p.k : p.n;  // output columns
+      const int gu = __builtin_amdgcn_readfirstlane(g);
+      const float al = p.alpha != nullptr ? p.alpha[gu] : 1.0f;
+      const float be = p.beta != nullptr ? p.beta[gu] : 0.0f;
+      t.alpha = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, al)));
+      t.beta = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, be)));
+      t.bias = p.bias != nullptr ? p.bias + (int64_t)gu * outw + col_first : nullptr;
+    }
+    run_tile<MODE == 2 ? 1 : 0, EX>(lds, t, p.out_f32);
   }
 }
 
@@ -609,8 +643,11 @@ int device_cu_count() {
 hipError_t launch_gemm_mxfp8(int mode, int G, const uint8_t* a, const uint8_t* a_scales,
                              const uint8_t* b, const uint8_t* b_scales, const int64_t* offsets,
                              int64_t rows_cap, int64_t n, int64_t k, void* out, int out_f32,
-                             uint32_t* status, hipStream_t stream) {
-  MxArgs p{a, a_scales, b, b_scales, offsets, rows_cap, n, k, out, status, G, out_f32};
+                             uint32_t* status, hipStream_t stream, const float* alpha,
+                             const float* beta, const float* bias) {
+  MxArgs p{a,      a_scales, b,       b_scales, offsets, rows_cap, n,    k,
+           out,    status,   G,       out_f32,  alpha,   beta,     bias};
+  const bool ex = alpha != nullptr || beta != nullptr || bias != nullptr;
   // upper bound of the tile count from host-known shapes
   int64_t bound;
   if (mode != 1) bound = ((rows_cap + BM - 1) / BM + G) * ((n + BN - 1) / BN);
@@ -618,12 +655,16 @@ hipError_t launch_gemm_mxfp8(int mode, int G, const uint8_t* a, const uint8_t* a
   int64_t grid = device_cu_count();
   if (bound < grid) grid = bound;
   if (grid <= 0) return hipSuccess;
-  if (mode == 0)
-    hipLaunchKernelGGL(mx_gemm_kernel<0>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
-  else if (mode == 1)
-    hipLaunchKernelGGL(mx_gemm_kernel<1>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL(mx_gemm_kernel<2>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  const dim3 gd((unsigned)grid), bd(kThreads);
+  if (!ex) {
+    if (mode == 0) hipLaunchKernelGGL((mx_gemm_kernel<0, false>), gd, bd, 0, stream, p);
+    else if (mode == 1) hipLaunchKernelGGL((mx_gemm_kernel<1, false>), gd, bd, 0, stream, p);
+    else hipLaunchKernelGGL((mx_gemm_kernel<2, false>), gd, bd, 0, stream, p);
+  } else {
+    if (mode == 0) hipLaunchKernelGGL((mx_gemm_kernel<0, true>), gd, bd, 0, stream, p);
+    else if (mode == 1) hipLaunchKernelGGL((mx_gemm_kernel<1, true>), gd, bd, 0, stream, p);
+    else hipLaunchKernelGGL((mx_gemm_kernel<2, true>), gd, bd, 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -234,6 +234,29 @@ int grouped_gemm_mxfp8(int mode, int64_t G, const uint8_t* a, const uint8_t* a_s
                        uint32_t* dev_status, void* stream);
 
 /*
+ * grouped_gemm_mxfp8_ex
+ *
+ * grouped_gemm_mxfp8 with the per-group epilogue of "gemm.py" grouped_gemm (a
+ * bias of shape (num_gemms, N) over the output columns; per-group float32
+ * alpha and beta, defaults 1 and 0) and the copy-or-accumulate output of the
+ * row-scaled NVFP4 flow, e.g. accumulating into an FP32 main-grad:
+ *   out[r, j] = alpha[g] * S[r, j] + beta[g] * out_previous[r, j] + bias[g, j]
+ * combined in float32 and rounded once to out_dtype; out_previous is read only
+ * for groups with beta[g] != 0.  S, g, modes and the other arguments as in
+ * grouped_gemm_mxfp8 (the output columns are n in FPROP / DGRAD, k in WGRAD).
+ *   alpha  [G] float32 or NULL (all 1);  beta [G] float32 or NULL (all 0)
+ *   bias   [G, output columns] float32 or NULL; needs a multiple of 4 columns
+ * With all three NULL it is grouped_gemm_mxfp8.
+ * Errors: those of grouped_gemm_mxfp8, plus BSG_ERR_ALIGN (alpha / beta 4-byte,
+ * bias 16-byte) and BSG_ERR_SHAPE (bias with output columns not a multiple of 4).
+ */
+int grouped_gemm_mxfp8_ex(int mode, int64_t G, const uint8_t* a, const uint8_t* a_scales,
+                          const uint8_t* b, const uint8_t* b_scales, const int64_t* offsets,
+                          int64_t rows_cap, int64_t n, int64_t k, void* out, int out_dtype,
+                          const float* alpha, const float* beta, const float* bias,
+                          uint32_t* dev_status, void* stream);
+
+/*
  * grouped_gemm_nvfp4_rowscaled
  *
  * Row-scaled NVFP4 grouped GEMM ("[Common][PyTorch] Add row-scaled NVFP4

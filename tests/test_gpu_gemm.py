@@ -395,3 +395,89 @@ def test_dgrad_parity(sizes, K, N, out_f32):
             gemm_tolerance_check(y[off[g]:off[g + 1]], ref[off[g]:off[g + 1]], out_f32,
                                  "group %d" % g)
     assert np.all(np.isnan(y[M:])), "capacity rows untouched"
+
+
+# ---------------------------------------------------------------- epilogue terms (alpha, beta, bias)
+
+EPI_CASES = [
+    ([300, 0, 17, 513, 130], 512, 640, 1000),
+    ([5, 300, 0, 40], 128, 258, 400),   # odd row stride: the element path
+]
+
+
+@pytest.mark.parametrize("sizes,K,N,rows_cap", EPI_CASES)
+@pytest.mark.parametrize("out_f32", [True, False])
+@pytest.mark.parametrize("terms", ["all", "bias_only", "alpha_beta"])
+def test_fprop_epilogue_parity(sizes, K, N, rows_cap, out_f32, terms):
+    rng = np.random.default_rng(K + N + 3 * len(sizes))
+    sizes, off, x, w, ad, asc, bd, bsc, rows_cap = _fprop_operands(rng, sizes, K, N, rows_cap)
+    G = len(sizes)
+    s_ref = GM.mxfp8_fprop(ad, asc, bd, bsc, off, K)
+    live = int(off[-1])
+    grp = np.searchsorted(off, np.arange(live), side="right") - 1
+    alpha = (rng.uniform(-2, 2, G)).astype(np.float32) if terms != "bias_only" else None
+    beta = np.where(np.arange(G) % 2 == 0, rng.uniform(0.5, 1.5, G), 0.0).astype(np.float32) \
+        if terms != "bias_only" else None
+    bias = rng.standard_normal((G, N)).astype(np.float32) if (terms != "alpha_beta" and N % 4 == 0) \
+        else None
+    dt = torch.float32 if out_f32 else torch.bfloat16
+    c0 = torch.from_numpy(rng.standard_normal((rows_cap, N)).astype(np.float32)).to(dt)
+    if beta is not None:
+        nan_rows = torch.from_numpy(np.repeat(beta[grp] == 0, 1)).to(device())
+        c0[:live][nan_rows.cpu()] = float("nan")      # groups with beta 0 must not read it
+    c0[live:] = float("nan")
+    out = c0.to(device())
+    c_prev = bf16_out_to_f64(out)
+    a, a_s = _upload_rows(ad, asc, rows_cap)
+    bsg.grouped_gemm_mxfp8_ex(bsg.BSG_FPROP_TN, a, a_s, to_dev(bd), to_dev(bsc), to_dev(off),
+                              rows_cap, N, K, out,
+                              out_dtype=bsg.BSG_OUT_F32 if out_f32 else bsg.BSG_OUT_BF16,
+                              alpha=None if alpha is None else to_dev(alpha),
+                              beta=None if beta is None else to_dev(beta),
+                              bias=None if bias is None else to_dev(bias))
+    ref = GM.epilogue(s_ref[:live], grp, alpha, beta, c_prev[:live], bias)
+    y = bf16_out_to_f64(out)
+    for g in range(G):
+        if sizes[g]:
+            gemm_tolerance_check(y[off[g]:off[g + 1]], ref[off[g]:off[g + 1]], out_f32,
+                                 "group %d" % g)
+    assert np.all(np.isnan(y[live:])), "capacity rows must stay untouched"
+
+
+@pytest.mark.parametrize("out_f32", [True, False])
+def test_wgrad_accumulate_into_main_grad(out_f32):
+    """WGRAD with beta = 1 accumulating into an existing dW (the main-grad use),
+    alpha per expert, a bias over the k output columns; an empty expert gets
+    beta * old + bias (its product is zero)."""
+    rng = np.random.default_rng(41)
+    sizes = np.array([37, 0, 130, 5], np.int32)
+    G, M, N, K = 4, int(sizes.sum()), 160, 96
+    dy = _bits(rng, (M, N))
+    x = _bits(rng, (M, K))
+    _, off = O.group_offsets(sizes)
+    _, poff = O.group_offsets(sizes, pad_to=128)
+    dyc, dys = Q.mxfp8_colwise(dy, off, poff)
+    xc, xs = Q.mxfp8_colwise(x, off, poff)
+    s_ref = GM.mxfp8_wgrad(dyc, dys, xc, xs, poff, N, K)
+    cap = max(int(poff[-1]), 128)
+
+    def pad(arr, n):
+        o = np.zeros(n, np.uint8)
+        o[:len(arr)] = arr
+        return to_dev(o)
+
+    alpha = rng.uniform(0.5, 2, G).astype(np.float32)
+    beta = np.ones(G, np.float32)
+    bias = rng.standard_normal((G, K)).astype(np.float32)
+    dt = torch.float32 if out_f32 else torch.bfloat16
+    out = torch.from_numpy(rng.standard_normal((G, N, K)).astype(np.float32)).to(dt).to(device())
+    c_prev = bf16_out_to_f64(out)
+    bsg.grouped_gemm_mxfp8_ex(bsg.BSG_WGRAD_NT, pad(dyc, cap * N), pad(dys, cap * N // 32),
+                              pad(xc, cap * K), pad(xs, cap * K // 32), to_dev(poff), cap, N, K, out,
+                              out_dtype=bsg.BSG_OUT_F32 if out_f32 else bsg.BSG_OUT_BF16,
+                              alpha=to_dev(alpha), beta=to_dev(beta), bias=to_dev(bias))
+    y = bf16_out_to_f64(out)
+    for g in range(G):
+        ref = GM.epilogue(s_ref[g], np.zeros(N, np.int64), alpha[[g]], beta[[g]], c_prev[g],
+                          bias[[g]])
+        gemm_tolerance_check(y[g], ref, out_f32, "expert %d" % g)
