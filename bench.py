@@ -400,33 +400,39 @@ def gemm_traffic():
 
 
 def cpu_baseline():
-    """The oracle, untuned, on a bounded sample of the fprop workload: one
-    expert's 512 token rows and a 4096-row slice of its weight, quantized
-    (MXFP8, rowwise) and multiplied in fp64.  Reported in the metric's unit."""
+    """The oracle, untuned, on a bounded sample of the fprop workload: its
+    first expert whole (that expert's token rows and its full N x K weight,
+    drawn by the workload's recipe), quantized (MXFP8, rowwise) and multiplied
+    in fp64.  Reported in the metric's unit."""
     from oracle import gemm as GM
     from oracle import quantize as Q
     w = workloads.get("fprop")
     gen = torch.Generator().manual_seed(w.seed)
-    rows, nrows, K = 512, 4096, w.k
-    x = torch.randn((rows, K), generator=gen)
-    x = torch.where(torch.rand((rows, K), generator=gen) < 0.01, x * 20, x).to(torch.bfloat16)
-    wt = (torch.randn((nrows, K), generator=gen) * 0.02).to(torch.bfloat16)
-    xb, wb = workloads.bf16_bits(x), workloads.bf16_bits(wt)
-    t0 = time.perf_counter()
-    ad, asc = Q.mxfp8_rowwise(xb, np.array([0, rows]))
-    bd, bsc = Q.mxfp8_rowwise(wb, np.array([0, nrows]))
-    GM.mxfp8_fprop(ad, asc, bd.reshape(1, nrows, K), bsc, np.array([0, rows]), K)
-    dt = time.perf_counter() - t0
-    flops = 2.0 * rows * nrows * K
+    experts, nrows, K = 4, w.n, w.k
+    dt, flops, rows_done = 0.0, 0.0, 0
+    for e in range(experts):
+        rows = int(w.sizes[e])
+        x = torch.randn((rows, K), generator=gen)
+        x = torch.where(torch.rand((rows, K), generator=gen) < 0.01, x * 20, x).to(torch.bfloat16)
+        wt = (torch.randn((nrows, K), generator=gen) * 0.02).to(torch.bfloat16)
+        xb, wb = workloads.bf16_bits(x), workloads.bf16_bits(wt)
+        t0 = time.perf_counter()
+        ad, asc = Q.mxfp8_rowwise(xb, np.array([0, rows]))
+        bd, bsc = Q.mxfp8_rowwise(wb, np.array([0, nrows]))
+        GM.mxfp8_fprop(ad, asc, bd.reshape(1, nrows, K), bsc, np.array([0, rows]), K)
+        dt += time.perf_counter() - t0
+        flops += 2.0 * rows * nrows * K
+        rows_done += rows
     try:
         threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     except Exception:
         threads = os.cpu_count() or 1
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle", "seconds": round(dt, 2),
-            "sample": "fprop workload, 1 expert: 512 token rows x 4096 weight rows x K=4096; "
-                      "oracle MXFP8 quantize of both + fp64 GEMM (numpy; quantize single-"
-                      "threaded, matmul on BLAS threads)"}
+            "sample": "fprop workload, experts 0-%d whole: %d token rows, %d x %d weights each, "
+                      "K=%d; oracle MXFP8 quantize of both + fp64 GEMM per expert (numpy; "
+                      "quantize single-threaded, matmul on BLAS threads)"
+                      % (experts - 1, rows_done, nrows, K, K)}
 
 
 # ---------------------------------------------------------------- main
