@@ -13,11 +13,14 @@ defined in float32):
 * ``offsets``   -- int32 group sizes -> int64 sizes and exclusive prefix-sum offsets.
 * ``layout``    -- the byte layout the quantizers write and the GEMMs read
                    (the GEMM-ready scale order, written by the quantize itself).
-* ``quantize``  -- grouped MXFP8 rowwise / columnwise quantize and the row-scaled
-                   NVFP4 quantize.
+* ``quantize``  -- grouped MXFP8 rowwise / columnwise quantize (E4M3, and E5M2 for
+                   gradients), the row-scaled NVFP4 quantize (rows and columnwise
+                   copies) and the per-tensor (per-expert) NVFP4 quantize.
 * ``gemm``      -- per-expert dense products of the dequantized operands in fp64:
-                   fprop (TN, ragged rows), wgrad (NT, ragged contraction) and the
-                   row-scaled NVFP4 fprop with its outer-scale epilogue.
+                   fprop (TN, ragged rows), wgrad (NT, ragged contraction), dgrad,
+                   the row-scaled NVFP4 fprop / wgrad with their outer-scale
+                   epilogue, the per-tensor NVFP4 fprop (alpha per group) and the
+                   per-group epilogue terms (alpha, beta, bias).
 
 Sources (the pages): "gemm.py" of TransformerEngine's JAX cpp_extensions
 (``grouped_gemm``, ``_quantize_gemm_operands``, ``_jax_scaled_matmul``,

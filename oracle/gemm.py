@@ -119,6 +119,45 @@ def nvfp4_rowscaled_fprop(a_packed, a_bscales, a_tsi, offsets, b_packed, b_bscal
     return result
 
 
+def nvfp4_pertensor_fprop(a_packed, a_bscales, a_amax, offsets, b_packed, b_bscales, b_amax,
+                          n_per_group, k, rows=None):
+    """Per-tensor NVFP4 FPROP over groups ("gemm.py": for NVFP4 operands the
+    GEMM's alpha is the product of the two operands' tensor scales
+    ``_get_nvfp4_tensor_scale_inv(amax)``, and the product is scaled by it; the
+    graph-safe grouped GEMM takes one alpha per group):
+        S[r, n] = sum_k (e2m1(A) * sd_A)[r, k] * (e2m1(B_g) * sd_B)[n, k]
+        alpha_g = float32(tsi(amax_A[g]) * tsi(amax_B[g]))
+        Y[r, n] = alpha_g * S[r, n]      for live r in g, n < N_g.
+
+    B holds the experts' [N_g, k] weights one after another, each expert one
+    tensor with its amax b_amax[g].  Returns a list, per group, of (row
+    indices, float64 [len(rows in g), N_g])."""
+    from .quantize import nvfp4_tensor_scale_inv
+    off = np.asarray(offsets, dtype=np.int64)
+    npg = [int(v) for v in n_per_group]
+    boff = np.concatenate([[0], np.cumsum(npg)]).astype(np.int64)
+    if rows is None:
+        rows = np.arange(int(off[-1]))
+    rows = np.asarray(rows, dtype=np.int64)
+    grp = _group_of_rows(off, rows)
+    a_packed = np.asarray(a_packed).reshape(-1, k // 2)
+    a_bscales = np.asarray(a_bscales).reshape(-1, k // 16)
+    b_packed = np.asarray(b_packed).reshape(-1, k // 2)
+    b_bscales = np.asarray(b_bscales).reshape(-1, k // 16)
+    alpha = np.float32(nvfp4_tensor_scale_inv(a_amax)) * np.float32(nvfp4_tensor_scale_inv(b_amax))
+    alpha = np.asarray(alpha, dtype=np.float32)
+    result = []
+    for g in range(len(npg)):
+        sel = rows[grp == g]
+        if len(sel) == 0 or npg[g] == 0:
+            result.append((sel, np.zeros((len(sel), npg[g]))))
+            continue
+        a = nvfp4_block_dequant(a_packed[sel], a_bscales[sel], k)
+        b = nvfp4_block_dequant(b_packed[boff[g]:boff[g + 1]], b_bscales[boff[g]:boff[g + 1]], k)
+        result.append((sel, float(alpha[g]) * (a @ b.T)))
+    return result
+
+
 def nvfp4_rowscaled_wgrad(dy_col, dy_bscales, dy_outer, x_col, x_bscales, x_outer,
                           padded_offsets, n, k, groups=None, out_rows=None):
     """Row-scaled NVFP4 WGRAD (NT, contraction over each expert's ragged

@@ -1,5 +1,5 @@
-"""Grouped MXFP8 and row-scaled NVFP4 quantize, and the matching dequantize
-(oracle; test infrastructure only).
+"""Grouped MXFP8, row-scaled NVFP4 and per-tensor NVFP4 quantize, and the
+matching dequantize (oracle; test infrastructure only).
 
 Operands are bf16 bit patterns (uint16) of a row-major [rows, cols] tensor whose
 first ``offsets[G]`` rows are live and split into G consecutive groups
@@ -198,6 +198,66 @@ def nvfp4_rowscaled_colwise(x_bits, offsets, padded_offsets):
         bscales[poff[g] * cols // NVFP4_BLOCK:poff[g + 1] * cols // NVFP4_BLOCK] = s8.reshape(-1)
         outer[g] = tsi
     return data, bscales, outer
+
+
+def nvfp4_tensor_scale_inv(amax):
+    """Tensor-level NVFP4 outer scale, amax / (E2M1 max * E4M3 max) = amax /
+    2688, in float32 ("gemm.py", ``_get_nvfp4_tensor_scale_inv``)."""
+    return f32(np.asarray(amax, dtype=np.float32) / np.float32(E2M1_MAX * E4M3_MAX))
+
+
+def nvfp4_pertensor(x_bits, offsets):
+    """Per-tensor NVFP4 quantize of grouped live rows, each group (expert) one
+    tensor: "gemm.py" derives an NVFP4 operand's outer scale from the tensor's
+    amax (``_get_nvfp4_tensor_scale_inv``, alpha = the product of the two
+    operands' outer scales); split per expert, each group carries its own amax
+    ("[Common][PyTorch] Add row-scaled NVFP4 support to grouped-tensor GEMM":
+    one amax entry per split for tensor-scaled quantizers).
+
+    Reading: the float32 steps of ``nvfp4_rowscaled`` with the row's amax
+    replaced by the group's,
+      S_g  = 2688 / amax_g (1 if amax_g == 0; capped at FLT_MAX)
+      s_f  = (bmax / 6) * S_g        -> s8 = E4M3(s_f), sd = decode(s8)
+      enc  = S_g / sd (0 if sd == 0; capped at FLT_MAX)
+      q    = E2M1(x * enc)
+    so that x ~= e2m1(q) * sd * tsi_g, tsi_g = amax_g / 2688.  An empty group
+    has amax 0.
+
+    Returns (packed [live, C/2] uint8, block scales [live, C/16] uint8 E4M3,
+    amax [G] float32)."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    rows, cols = x_bits.shape
+    if cols % MX_BLOCK:
+        raise ValueError("cols must be a multiple of 32")
+    off = np.asarray(offsets, dtype=np.int64)
+    G = len(off) - 1
+    live = int(off[-1])
+    if live > rows:
+        raise ValueError("sum of group sizes exceeds the row capacity")
+    if np.any(np.diff(off) < 0):
+        raise ValueError("negative group size")
+    x = f32(bf16_bits_to_f64(x_bits[:live]))                    # exact in float32
+    two688 = np.float32(E2M1_MAX * E4M3_MAX)
+    amax = np.zeros(G, np.float32)
+    for g in range(G):
+        if off[g + 1] > off[g] and cols:
+            amax[g] = np.abs(x[off[g]:off[g + 1]]).max()
+    # each live row takes its group's S
+    row_group = np.repeat(np.arange(G), np.diff(off))
+    with np.errstate(divide="ignore", over="ignore", invalid="ignore"):
+        big_s_g = np.where(amax > 0, f32(two688 / amax), np.float32(1.0))
+        big_s_g = np.minimum(big_s_g, FLT_MAX).astype(np.float32)
+        big_s = big_s_g[row_group]
+        blocks = x.reshape(live, cols // NVFP4_BLOCK, NVFP4_BLOCK)
+        bmax = np.abs(blocks).max(axis=2)
+        s_f = f32(f32(bmax / np.float32(E2M1_MAX)) * big_s[:, None])
+        s8 = e4m3_encode(s_f.astype(np.float64))
+        sd = f32(e4m3_decode(s8))
+        enc = np.where(sd == 0, np.float32(0.0), np.minimum(f32(big_s[:, None] / sd), FLT_MAX))
+        enc = enc.astype(np.float32)
+        v = f32(blocks * enc[..., None])
+    q = e2m1_encode(v.astype(np.float64)).reshape(live, cols)
+    return fp4_pack(q), s8, amax
 
 
 def nvfp4_block_dequant(packed, block_scales, cols):

@@ -275,3 +275,47 @@ def test_epilogue_exact_on_lossless_inputs():
         assert np.array_equal(y[r], want), r
     # the defaults are the plain product
     assert np.array_equal(GM.epilogue(s, grp), s)
+
+
+def test_nvfp4_pertensor_exact_on_lossless_inputs():
+    """Per-tensor NVFP4 on lossless operands: every 16-block holds E2M1 grid
+    values times 2^j with a block maximum of exactly 6 * 2^j, and each group's
+    (expert's) largest block reaches 2688 * 2^p, so tsi = 2^p, every scale is a
+    power of two (or 448) and the codes reproduce the inputs exactly.  Y must
+    then equal the exact per-expert product of the raw inputs, over each
+    group's own N_g columns."""
+    rng = np.random.default_rng(26)
+    grid = np.array([0, .5, 1, 1.5, 2, 3, 4, -.5, -1, -1.5, -2, -3, -4])
+    sizes = np.array([3, 0, 5, 2], np.int32)
+    npg = [8, 16, 24, 8]
+    K = 64
+
+    def mk(group_rows, p):
+        v = rng.choice(grid, (group_rows, K))
+        j = rng.integers(-6, 3, (group_rows, K // 16))
+        v[:, ::16] = rng.choice([6.0, -6.0], (group_rows, K // 16))   # block max 6 * 2^j
+        v = v * np.exp2(np.repeat(j, 16, axis=1))
+        v[0, 16:32] *= 448 / 2.0 ** j[0, 1]          # one block at 2688: tsi = 1 before 2^p
+        return v * 2.0 ** p
+
+    xs = [mk(int(m), p) for m, p in zip(sizes, [-3, 0, 4, 1]) if m > 0]
+    xv = np.concatenate(xs + [np.zeros((2, K))])             # 2 capacity rows
+    wv = np.concatenate([mk(n, p) for n, p in zip(npg, [0, -2, 1, 3])])
+    _, off = O.group_offsets(sizes)
+    boff = np.concatenate([[0], np.cumsum(npg)])
+    xb, wb = F.f32_to_bf16_bits_rne(xv.astype(np.float32)), F.f32_to_bf16_bits_rne(wv.astype(np.float32))
+    assert np.array_equal(F.bf16_bits_to_f64(xb), xv) and np.array_equal(F.bf16_bits_to_f64(wb), wv)
+    ap, asc, aam = Q.nvfp4_pertensor(xb, off)
+    bp, bsc, bam = Q.nvfp4_pertensor(wb, boff)
+    for g, p in zip((0, 2, 3), (-3, 4, 1)):
+        assert Q.nvfp4_tensor_scale_inv(aam)[g] == 2.0 ** p
+    # lossless: dequant reproduces the inputs
+    dq = Q.nvfp4_dequant(ap, asc, Q.nvfp4_tensor_scale_inv(aam)[np.repeat(np.arange(4), sizes)], K)
+    assert np.array_equal(dq, xv[:off[-1]])
+    res = GM.nvfp4_pertensor_fprop(ap, asc, aam, off, bp, bsc, bam, npg, K)
+    for g in range(4):
+        rows, y = res[g]
+        assert list(rows) == list(range(off[g], off[g + 1]))
+        assert y.shape == (sizes[g], npg[g])
+        if sizes[g]:
+            assert np.array_equal(y, xv[rows] @ wv[boff[g]:boff[g + 1]].T)

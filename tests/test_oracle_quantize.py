@@ -303,3 +303,84 @@ def test_nvfp4_colwise_dequant_within_format_error():
             seg = slice(16 * b, min(16 * b + 16, m))
             bmax = np.abs(ref[:, seg]).max(axis=1, keepdims=True)
             assert np.all(np.abs(dq[:, seg] - ref[:, seg]) <= bmax / 6 * 1.07 + 1e-30)
+
+
+# ---------------------------------------------------------------- per-tensor NVFP4
+
+def test_nvfp4_pertensor_golden():
+    """tests/golden/nvfp4_pertensor.txt: every row of a group takes the group's
+    amax (a row whose own amax is smaller gets a smaller block scale than the
+    row-scaled cast would give it), an empty group has amax 0."""
+    lines = [ln.split("#")[0].split() for ln in open(os.path.join(GOLDEN, "nvfp4_pertensor.txt"))]
+    lines = [ln for ln in lines if ln]
+    sizes = np.array([2, 1, 0, 1], np.int32)
+    _, off = O.group_offsets(sizes)
+    x = np.zeros((4, 32), np.float32)
+    for r, (g, vals, *_rest) in enumerate(lines):
+        v = [float(t) for t in vals.split(",")]
+        x[r, :len(v)] = v
+    packed, s8, amax = Q.nvfp4_pertensor(F.f32_to_bf16_bits_rne(x), off)
+    assert packed.shape == (4, 16) and s8.shape == (4, 2) and amax.shape == (4,)
+    assert amax[2] == 0.0
+    for r, (g, vals, am, sc, pk) in enumerate(lines):
+        assert amax[int(g)] == np.float32(float(am))
+        assert s8[r, 0] == int(sc, 16) and s8[r, 1] == 0
+        want = [int(b, 16) for b in pk.split(",")]
+        assert list(packed[r, :len(want)]) == want and np.all(packed[r, len(want):] == 0)
+    assert Q.nvfp4_tensor_scale_inv(amax)[0] == np.float32(np.float32(6) / np.float32(2688))
+
+
+def test_nvfp4_pertensor_matches_slow_rederivation():
+    rng = np.random.default_rng(17)
+    bits = _tiny_bits(rng, 7, 64)
+    xv = F.bf16_bits_to_f64(bits)
+    off = np.array([0, 3, 3, 7])
+    packed, s8, amax = Q.nvfp4_pertensor(bits, off)
+    f = np.float32
+    for g in range(3):
+        rows = range(off[g], off[g + 1])
+        am = f(max((abs(v) for r in rows for v in xv[r]), default=0.0))
+        assert amax[g] == am
+        S = f(f(2688) / am) if am > 0 else f(1)
+        for r in rows:
+            for b in range(4):
+                blk = xv[r, b * 16:(b + 1) * 16]
+                sf = f(f(f(max(abs(v) for v in blk)) / f(6)) * S)
+                code8 = _slow_e4m3(float(sf))
+                assert s8[r, b] == code8
+                sd = f(_e4m3_table()[code8 & 0x7F])
+                enc = f(S / sd) if sd != 0 else f(0)
+                for i in range(16):
+                    j = b * 16 + i
+                    q = _slow_e2m1(float(f(f(blk[i]) * enc)))
+                    assert (packed[r, j // 2] >> (4 * (j % 2))) & 0xF == q, (r, j)
+
+
+def test_nvfp4_pertensor_equals_rowscaled_when_rows_share_amax():
+    """Special case: when every row of a group reaches the group's amax, the
+    per-tensor cast is the row-scaled cast (same bytes, tsi_g = tsi_r)."""
+    rng = np.random.default_rng(19)
+    x = rng.standard_normal((9, 96)).astype(np.float32)
+    x[:4, 5] = 7.5
+    x[4:, 40] = -0.3125 * 64
+    xb = F.f32_to_bf16_bits_rne(x)
+    off = np.array([0, 4, 4, 9])
+    p1, s1, amax = Q.nvfp4_pertensor(xb, off)
+    p2, s2, tsi = Q.nvfp4_rowscaled(xb, off)
+    assert np.array_equal(p1, p2) and np.array_equal(s1, s2)
+    tsi_g = Q.nvfp4_tensor_scale_inv(amax)
+    assert np.all(tsi[:4] == tsi_g[0]) and np.all(tsi[4:] == tsi_g[2]) and amax[1] == 0
+
+
+def test_nvfp4_pertensor_grouped_equals_per_expert_concatenation():
+    rng = np.random.default_rng(23)
+    bits = _tiny_bits(rng, 11, 128)
+    sizes = np.array([4, 0, 6, 1], np.int32)
+    _, off = O.group_offsets(sizes)
+    p_all, s_all, a_all = Q.nvfp4_pertensor(bits, off)
+    for g in range(4):
+        part = bits[off[g]:off[g + 1]]
+        p, s, a = Q.nvfp4_pertensor(part, np.array([0, sizes[g]]))
+        assert np.array_equal(p, p_all[off[g]:off[g + 1]])
+        assert np.array_equal(s, s_all[off[g]:off[g + 1]])
+        assert a[0] == a_all[g]
