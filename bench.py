@@ -304,6 +304,55 @@ class Nvfp4Fprop(Case):
         self._rec(ev, 4)
 
 
+class Nvfp4PerTensorFprop(Case):
+    """offsets -> per-tensor NVFP4 quantize of X (one amax per expert's rows)
+    and W (one amax per expert) -> grouped GEMM with alpha_g = tsi_A * tsi_B."""
+
+    def __init__(self, name, dev):
+        self.name = name
+        self.w = w = workloads.get(name)
+        t = workloads.tensors(w, device=dev)
+        self.x, self.wt = t["x"], t["w"]
+        G, K, R = w.G, w.k, w.rows_cap
+        self.npg = list(w.n_per_group)
+        NB = sum(self.npg)
+        self.G, self.K, self.R, self.ld = G, K, R, max(self.npg)
+        self.sizes = torch.from_numpy(w.sizes).to(dev)
+        self.off = torch.empty(G + 1, dtype=torch.int64, device=dev)
+        self.xd = torch.empty((R, K // 2), dtype=torch.uint8, device=dev)
+        self.xs = torch.empty((R, K // 16), dtype=torch.uint8, device=dev)
+        self.xa = torch.empty(G, dtype=torch.float32, device=dev)
+        self.woff = torch.from_numpy(np.concatenate([[0], np.cumsum(self.npg)])).to(dev)
+        self.wd = torch.empty((NB, K // 2), dtype=torch.uint8, device=dev)
+        self.ws = torch.empty((NB, K // 16), dtype=torch.uint8, device=dev)
+        self.wa = torch.empty(G, dtype=torch.float32, device=dev)
+        self.y = torch.empty((R, self.ld), dtype=torch.bfloat16, device=dev)
+        self.kernels = ("offsets", "quantize_x", "quantize_w", "gemm")
+        live = w.live_rows
+        self.flops = 2.0 * K * float(sum(int(m) * n for m, n in zip(w.sizes, self.npg)))
+        per = 0.5 + 1.0 / 16
+        # one read of the input counted (the group amax pass reads it a second time)
+        self.bytes = {"offsets": 0.0, "quantize_x": live * K * (2.0 + per) + 4 * G,
+                      "quantize_w": NB * K * (2.0 + per) + 4 * G,
+                      "gemm": live * K * per + NB * K * per
+                      + 2.0 * float(sum(int(m) * n for m, n in zip(w.sizes, self.npg)))}
+
+    def step(self, ev=None):
+        self._rec(ev, 0)
+        bsg.group_offsets_i32_to_i64(self.sizes, offsets=self.off, capacity=self.R)
+        self._rec(ev, 1)
+        bsg.grouped_quantize_nvfp4_pertensor(self.x, self.off, data=self.xd, block_scales=self.xs,
+                                             amax=self.xa)
+        self._rec(ev, 2)
+        bsg.grouped_quantize_nvfp4_pertensor(self.wt, self.woff, data=self.wd, block_scales=self.ws,
+                                             amax=self.wa)
+        self._rec(ev, 3)
+        bsg.grouped_gemm_nvfp4_pertensor(self.xd, self.xs, self.xa, self.off, self.K, self.wd,
+                                         self.ws, self.wa, self.npg, out=self.y, ld_out=self.ld,
+                                         out_dtype=bsg.BSG_OUT_BF16)
+        self._rec(ev, 4)
+
+
 def make_case(name, dev):
     if name in ("tiny", "zipf"):
         return MxFprop(name, dev, with_colwise=False)
@@ -317,6 +366,8 @@ def make_case(name, dev):
         return Nvfp4Wgrad(name, dev)
     if name == "dgrad":
         return MxDgrad(name, dev)
+    if name == "nvfp4_pertensor":
+        return Nvfp4PerTensorFprop(name, dev)
     raise KeyError(name)
 
 
@@ -469,7 +520,7 @@ def main():
         del src, dst
 
     names = ["fprop"] if args.no_extra else ["fprop", "tiny", "wgrad", "zipf", "dgrad", "nvfp4",
-                                             "nvfp4_wgrad"]
+                                             "nvfp4_wgrad", "nvfp4_pertensor"]
     if args.only:
         names = args.only.split(",")
     results = {}

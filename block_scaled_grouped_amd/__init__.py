@@ -28,8 +28,9 @@ DEV_BAD_PADDING = 4
 EXPORTS = ("bsg_last_error", "bsg_version", "group_offsets_i32_to_i64", "grouped_quantize_mxfp8",
            "grouped_quantize_mxfp8_rowwise_e5m2",
            "grouped_quantize_nvfp4_rowscaled", "grouped_quantize_nvfp4_rowscaled_colwise",
+           "grouped_quantize_nvfp4_pertensor",
            "grouped_gemm_mxfp8", "grouped_gemm_mxfp8_ex", "grouped_gemm_nvfp4_rowscaled",
-           "grouped_gemm_nvfp4_rowscaled_wgrad")
+           "grouped_gemm_nvfp4_rowscaled_wgrad", "grouped_gemm_nvfp4_pertensor")
 
 _lib = None
 
@@ -73,6 +74,11 @@ def load_library(path=LIB_PATH):
     lib.grouped_gemm_nvfp4_rowscaled.restype = I32
     lib.grouped_gemm_nvfp4_rowscaled.argtypes = [I64, P, P, P, P, I64, I64, P, P, P, P, P, I64, I32,
                                                  P, P, P]
+    lib.grouped_quantize_nvfp4_pertensor.restype = I32
+    lib.grouped_quantize_nvfp4_pertensor.argtypes = [P, I64, I64, I64, P, P, P, P, P, P]
+    lib.grouped_gemm_nvfp4_pertensor.restype = I32
+    lib.grouped_gemm_nvfp4_pertensor.argtypes = [I64, P, P, P, P, I64, I64, P, P, P, P, P, I64, I32,
+                                                 P, P]
     lib.grouped_gemm_nvfp4_rowscaled_wgrad.restype = I32
     lib.grouped_gemm_nvfp4_rowscaled_wgrad.argtypes = [I64, P, P, P, P, P, P, P, I64, I64, I64, P,
                                                        I32, P, P]
@@ -201,6 +207,26 @@ def grouped_quantize_nvfp4_rowscaled(x, offsets, G=None, data=None, block_scales
     return data, block_scales, outer
 
 
+def grouped_quantize_nvfp4_pertensor(x, offsets, G=None, data=None, block_scales=None, amax=None,
+                                     status=None):
+    """bf16 [rows_cap, cols] -> (E2M1 [rows_cap, cols/2], E4M3 [rows_cap, cols/16], f32 amax [G])."""
+    import torch
+    lib = load_library()
+    _need_cuda(x, offsets)
+    rows_cap, cols = x.shape
+    G = offsets.numel() - 1 if G is None else G
+    if data is None:
+        data = torch.empty((rows_cap, cols // 2), dtype=torch.uint8, device=x.device)
+    if block_scales is None:
+        block_scales = torch.empty((rows_cap, cols // 16), dtype=torch.uint8, device=x.device)
+    if amax is None:
+        amax = torch.empty(G, dtype=torch.float32, device=x.device)
+    _check(lib.grouped_quantize_nvfp4_pertensor(_ptr(x), rows_cap, cols, G, _ptr(offsets),
+                                                _ptr(data), _ptr(block_scales), _ptr(amax),
+                                                _ptr(status), _stream(x)))
+    return data, block_scales, amax
+
+
 def grouped_quantize_nvfp4_rowscaled_colwise(x, offsets, padded_offsets, G=None, col_rows_cap=None,
                                              data=None, block_scales=None, outer=None, status=None):
     """bf16 [rows_cap, cols] -> per-expert transposed copies: (E2M1 bytes
@@ -281,6 +307,33 @@ def grouped_gemm_nvfp4_rowscaled(a, a_scales, a_outer, offsets, k, b, b_scales, 
                                             _ptr(b_outer), ctypes.cast(host_n, ctypes.c_void_p),
                                             _ptr(out), ld_out, out_dtype, _ptr(scratch),
                                             _ptr(status), _stream(a)))
+    return out
+
+
+def grouped_gemm_nvfp4_pertensor(a, a_scales, a_amax, offsets, k, b, b_scales, b_amax, n_per_group,
+                                 out=None, ld_out=None, out_dtype=BSG_OUT_BF16, G=None,
+                                 status=None):
+    """Per-tensor NVFP4 fprop (alpha per group from the two amax arrays): out
+    [rows_cap, ld_out]; n_per_group is a host list."""
+    import torch
+    lib = load_library()
+    _need_cuda(a, a_scales, a_amax, offsets, b, b_scales, b_amax)
+    rows_cap = a.shape[0]
+    G = offsets.numel() - 1 if G is None else G
+    npg = [int(v) for v in n_per_group]
+    if len(npg) != G:
+        raise ValueError("n_per_group needs G entries")
+    if ld_out is None:
+        ld_out = max(npg) if out is None else out.shape[1]
+    if out is None:
+        dt = torch.float32 if out_dtype == BSG_OUT_F32 else torch.bfloat16
+        out = torch.empty((rows_cap, ld_out), dtype=dt, device=a.device)
+    host_n = (ctypes.c_int64 * G)(*npg)
+    _check(lib.grouped_gemm_nvfp4_pertensor(G, _ptr(a), _ptr(a_scales), _ptr(a_amax),
+                                            _ptr(offsets), rows_cap, k, _ptr(b), _ptr(b_scales),
+                                            _ptr(b_amax), ctypes.cast(host_n, ctypes.c_void_p),
+                                            _ptr(out), ld_out, out_dtype, _ptr(status),
+                                            _stream(a)))
     return out
 
 

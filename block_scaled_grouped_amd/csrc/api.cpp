@@ -142,6 +142,27 @@ int grouped_quantize_nvfp4_rowscaled(const void* x, int64_t rows_cap, int64_t co
                     fn);
 }
 
+int grouped_quantize_nvfp4_pertensor(const void* x, int64_t rows_cap, int64_t cols, int64_t G,
+                                     const int64_t* offsets, uint8_t* data, uint8_t* block_scales,
+                                     float* amax, uint32_t* dev_status, void* stream) {
+  const char* fn = "grouped_quantize_nvfp4_pertensor";
+  if (x == nullptr || offsets == nullptr || data == nullptr || block_scales == nullptr || amax == nullptr)
+    return fail(BSG_ERR_NULL, "%s: x, offsets, data, block_scales and amax must be non-NULL", fn);
+  if (G < 1 || G > BSG_MAX_GROUPS)
+    return fail(BSG_ERR_SHAPE, "%s: G=%lld outside [1, %d]", fn, (long long)G, BSG_MAX_GROUPS);
+  if (rows_cap < 0 || cols <= 0 || cols % 32 != 0)
+    return fail(BSG_ERR_SHAPE, "%s: need rows_cap >= 0 and cols a positive multiple of 32", fn);
+  if (cols > 16384)
+    return fail(BSG_ERR_UNSUPPORTED, "%s: cols=%lld above the supported 16384", fn, (long long)cols);
+  if (rows_cap > 0x7fffffffLL) return fail(BSG_ERR_SHAPE, "%s: rows_cap too large", fn);
+  if (!aligned16(x) || !aligned16(data) || !aligned4(amax))
+    return fail(BSG_ERR_ALIGN, "%s: x and data must be 16-byte aligned, amax 4-byte", fn);
+  return hip_result(bsg::launch_quantize_nvfp4_pertensor(static_cast<const uint16_t*>(x), rows_cap,
+                                                         cols, (int)G, offsets, data, block_scales,
+                                                         amax, dev_status, (hipStream_t)stream),
+                    fn);
+}
+
 int grouped_quantize_nvfp4_rowscaled_colwise(const void* x, int64_t rows_cap, int64_t cols,
                                              int64_t G, const int64_t* offsets,
                                              const int64_t* padded_offsets, int64_t col_rows_cap,
@@ -231,13 +252,12 @@ int grouped_gemm_mxfp8_ex(int mode, int64_t G, const uint8_t* a, const uint8_t* 
                          rows_cap, n, k, out, out_dtype, alpha, beta, bias, dev_status, stream);
 }
 
-int grouped_gemm_nvfp4_rowscaled(int64_t G, const uint8_t* a, const uint8_t* a_scales,
-                                 const float* a_outer, const int64_t* offsets, int64_t rows_cap,
-                                 int64_t k, const uint8_t* b, const uint8_t* b_scales,
-                                 const float* b_outer, const int64_t* n_per_group, void* out,
-                                 int64_t ld_out, int out_dtype, float* scratch,
-                                 uint32_t* dev_status, void* stream) {
-  const char* fn = "grouped_gemm_nvfp4_rowscaled";
+static int gemm_nvfp4_impl(const char* fn, bool per_tensor, int64_t G, const uint8_t* a,
+                           const uint8_t* a_scales, const float* a_outer, const int64_t* offsets,
+                           int64_t rows_cap, int64_t k, const uint8_t* b, const uint8_t* b_scales,
+                           const float* b_outer, const int64_t* n_per_group, void* out,
+                           int64_t ld_out, int out_dtype, float* scratch, uint32_t* dev_status,
+                           void* stream) {
   if (a == nullptr || a_scales == nullptr || a_outer == nullptr || offsets == nullptr || b == nullptr ||
       b_scales == nullptr || b_outer == nullptr || n_per_group == nullptr || out == nullptr)
     return fail(BSG_ERR_NULL, "%s: operands, scales, offsets, n_per_group and out must be non-NULL", fn);
@@ -273,8 +293,29 @@ int grouped_gemm_nvfp4_rowscaled(int64_t G, const uint8_t* a, const uint8_t* a_s
   return hip_result(bsg::launch_gemm_nvfp4((int)G, a, a_scales, a_outer, offsets, rows_cap, k, b,
                                            b_scales, b_outer, tab, (int)max_n, out, ld_out,
                                            out_dtype == BSG_OUT_F32, scratch, dev_status,
-                                           (hipStream_t)stream),
+                                           (hipStream_t)stream, per_tensor),
                     fn);
+}
+
+int grouped_gemm_nvfp4_rowscaled(int64_t G, const uint8_t* a, const uint8_t* a_scales,
+                                 const float* a_outer, const int64_t* offsets, int64_t rows_cap,
+                                 int64_t k, const uint8_t* b, const uint8_t* b_scales,
+                                 const float* b_outer, const int64_t* n_per_group, void* out,
+                                 int64_t ld_out, int out_dtype, float* scratch,
+                                 uint32_t* dev_status, void* stream) {
+  return gemm_nvfp4_impl("grouped_gemm_nvfp4_rowscaled", false, G, a, a_scales, a_outer, offsets,
+                         rows_cap, k, b, b_scales, b_outer, n_per_group, out, ld_out, out_dtype,
+                         scratch, dev_status, stream);
+}
+
+int grouped_gemm_nvfp4_pertensor(int64_t G, const uint8_t* a, const uint8_t* a_scales,
+                                 const float* a_amax, const int64_t* offsets, int64_t rows_cap,
+                                 int64_t k, const uint8_t* b, const uint8_t* b_scales,
+                                 const float* b_amax, const int64_t* n_per_group, void* out,
+                                 int64_t ld_out, int out_dtype, uint32_t* dev_status, void* stream) {
+  return gemm_nvfp4_impl("grouped_gemm_nvfp4_pertensor", true, G, a, a_scales, a_amax, offsets,
+                         rows_cap, k, b, b_scales, b_amax, n_per_group, out, ld_out, out_dtype,
+                         nullptr, dev_status, stream);
 }
 
 int grouped_gemm_nvfp4_rowscaled_wgrad(int64_t G, const uint8_t* a, const uint8_t* a_scales,

@@ -170,6 +170,11 @@ hipError_t launch_quantize_nvfp4_rowscaled(const uint16_t* x, int64_t rows_cap, 
                                            uint8_t* block_scales, float* outer, uint32_t* status,
                                            hipStream_t stream);
 
+hipError_t launch_quantize_nvfp4_pertensor(const uint16_t* x, int64_t rows_cap, int64_t cols,
+                                           int G, const int64_t* offsets, uint8_t* data,
+                                           uint8_t* block_scales, float* amax, uint32_t* status,
+                                           hipStream_t stream);
+
 hipError_t launch_quantize_nvfp4_rowscaled_colwise(const uint16_t* x, int64_t rows_cap,
                                                    int64_t cols, int G, const int64_t* offsets,
                                                    const int64_t* padded_offsets,
@@ -189,7 +194,7 @@ hipError_t launch_gemm_nvfp4(int G, const uint8_t* a, const uint8_t* a_scales,
                              int64_t k, const uint8_t* b, const uint8_t* b_scales,
                              const float* b_outer, const NvGroupTable& table, int max_n,
                              void* out, int64_t ld_out, int out_f32, float* scratch,
-                             uint32_t* status, hipStream_t stream);
+                             uint32_t* status, hipStream_t stream, bool per_tensor = false);
 
 hipError_t launch_gemm_nvfp4_wgrad(int G, const uint8_t* a, const uint8_t* a_scales,
                                    const float* a_outer, const uint8_t* b, const uint8_t* b_scales,

@@ -10,6 +10,10 @@
 //   S[r, n] = sum_k e2m1(A)[r,k] sA[r,k/16] * e2m1(B_g)[n,k] sB_g[n,k/16]
 //   Y[r, n] = (S[r, n] * a_outer[r]) * b_outer_g[n]
 //
+// The same kernel serves per-tensor NVFP4 ("gemm.py": alpha = the product of
+// the two operands' tensor scales amax / (6 * 448)), one tensor per group:
+// Y[r, n] = S[r, n] * alpha_g, alpha_g = (amax_A[g] / 2688) * (amax_B[g] / 2688).
+//
 // gfx950's scaled MFMA takes only power-of-two (E8M0) scales per 32 elements,
 // and E2M1 x E4M3 needs up to 6 significant bits, so no FP8/FP6/FP4 MFMA input
 // holds it exactly.  Each element is instead decoded while it is staged into
@@ -80,6 +84,7 @@ struct NvArgs {
   uint32_t* status;
   int G;
   int out_f32;
+  int per_tensor;  // aout / bout hold one amax per group (per-tensor NVFP4)
   NvGroupTable tab;
 };
 
@@ -445,8 +450,16 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
     // outer scales of this tile's rows and columns, for the epilogue (zeros for
     // a tile with nothing to contract, whose output is then exactly 0)
     const bool contract = t.kl > 0;
-    sm.aout[tid] = contract && tid < t.a_rows ? aout_t[tid] : 0.0f;
-    sm.bout[tid] = contract && tid < t.b_rows ? bout_t[tid] : 0.0f;
+    if (!WGRAD && p.per_tensor) {
+      // per-tensor NVFP4: alpha_g = tsi(amax_A[g]) * tsi(amax_B[g]) on every
+      // row, 1 on every column, so the epilogue computes S * alpha_g
+      const float alpha = (p.aout[g] / 2688.0f) * (p.bout[g] / 2688.0f);
+      sm.aout[tid] = contract && tid < t.a_rows ? alpha : 0.0f;
+      sm.bout[tid] = contract && tid < t.b_rows ? 1.0f : 0.0f;
+    } else {
+      sm.aout[tid] = contract && tid < t.a_rows ? aout_t[tid] : 0.0f;
+      sm.bout[tid] = contract && tid < t.b_rows ? bout_t[tid] : 0.0f;
+    }
 
     v16f acc[4][4];
 #pragma unroll
@@ -566,12 +579,14 @@ hipError_t launch_gemm_nvfp4(int G, const uint8_t* a, const uint8_t* a_scales,
                              int64_t k, const uint8_t* b, const uint8_t* b_scales,
                              const float* b_outer, const NvGroupTable& table, int max_n,
                              void* out, int64_t ld_out, int out_f32, float* scratch,
-                             uint32_t* status, hipStream_t stream) {
+                             uint32_t* status, hipStream_t stream, bool per_tensor) {
   NvArgs p;
   p.a = a; p.as = a_scales; p.aout = a_outer; p.offsets = offsets; p.rows_cap = rows_cap; p.k = k;
   p.n = 0;
   p.b = b; p.bs = b_scales; p.bout = b_outer; p.out = out; p.ld_out = ld_out; p.scratch = scratch;
-  p.status = status; p.G = G; p.out_f32 = out_f32; p.tab = table;
+  p.status = status; p.G = G; p.out_f32 = out_f32; p.per_tensor = per_tensor ? 1 : 0;
+  p.tab = table;
+  if (per_tensor && scratch != nullptr) return hipErrorInvalidValue;
   const int64_t bound = ((rows_cap + BM - 1) / BM + G) * ((max_n + BN - 1) / BN);
   int64_t grid = device_cu_count();
   if (bound < grid) grid = bound;
@@ -604,7 +619,7 @@ hipError_t launch_gemm_nvfp4_wgrad(int G, const uint8_t* a, const uint8_t* a_sca
   p.a = a; p.as = a_scales; p.aout = a_outer; p.offsets = padded_offsets;
   p.rows_cap = col_rows_cap; p.k = k; p.n = n;
   p.b = b; p.bs = b_scales; p.bout = b_outer; p.out = out; p.ld_out = k; p.scratch = nullptr;
-  p.status = status; p.G = G; p.out_f32 = out_f32; p.tab = NvGroupTable{};
+  p.status = status; p.G = G; p.out_f32 = out_f32; p.per_tensor = 0; p.tab = NvGroupTable{};
   const int64_t bound = (int64_t)G * ((n + BM - 1) / BM) * ((k + BN - 1) / BN);
   int64_t grid = device_cu_count();
   if (bound < grid) grid = bound;

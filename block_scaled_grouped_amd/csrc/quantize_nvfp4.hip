@@ -24,6 +24,7 @@ namespace bsg {
 
 constexpr int kNvThreads = 256;
 constexpr int kNvMaxBlocksPerThread = 4;
+static_assert(kMaxGroups <= kNvThreads, "the per-tensor cast gives each group one thread");
 
 namespace {
 
@@ -53,10 +54,14 @@ __device__ __forceinline__ uint32_t fp4_pack8(uint4 v, float enc) {
 
 }  // namespace
 
+// PER_TENSOR: the row's outer scale comes from its group's amax (computed by
+// nvfp4_group_amax_kernel into group_amax), and no per-row outer scale is
+// written; otherwise the row's own amax is reduced here and amax / 2688 stored.
+template <bool PER_TENSOR>
 __global__ __launch_bounds__(kNvThreads) void nvfp4_rowscaled_kernel(
     const uint16_t* __restrict__ x, int64_t rows_cap, int64_t cols, int G,
     const int64_t* __restrict__ offsets, uint8_t* __restrict__ data, uint8_t* __restrict__ bscales,
-    float* __restrict__ outer, uint32_t* status) {
+    float* __restrict__ outer, const float* __restrict__ group_amax, uint32_t* status) {
   __shared__ uint32_t s_wmax[kNvThreads / 64];
   int64_t live = offsets[G];
   if (live < 0) live = 0;
@@ -87,15 +92,33 @@ __global__ __launch_bounds__(kNvThreads) void nvfp4_rowscaled_kernel(
       am = max(am, bm[i]);
     }
   }
-  for (int d = 32; d >= 1; d >>= 1) am = max(am, (uint32_t)__shfl_xor((int)am, d, 64));
-  if ((tid & 63) == 0) s_wmax[tid >> 6] = am;
-  __syncthreads();
-  am = max(max(s_wmax[0], s_wmax[1]), max(s_wmax[2], s_wmax[3]));
-
-  const float amax = bf16_to_f32(am);
+  float amax;
+  if constexpr (PER_TENSOR) {
+    // the row's group amax in one round trip: thread t (G <= 256) loads group
+    // t's offsets and amax together and publishes the amax if the row is
+    // group t's (0 if offsets that fail validation place it in none)
+    bool mine = false;
+    uint32_t val = 0u;
+    if (tid < G) {
+      const int64_t lo = offsets[tid], hi = offsets[tid + 1];
+      val = __float_as_uint(group_amax[tid]);
+      mine = lo <= row && row < hi;
+    }
+    if (tid == 0) s_wmax[0] = 0u;
+    __syncthreads();
+    if (mine) s_wmax[0] = val;
+    __syncthreads();
+    amax = __uint_as_float(s_wmax[0]);
+  } else {
+    for (int d = 32; d >= 1; d >>= 1) am = max(am, (uint32_t)__shfl_xor((int)am, d, 64));
+    if ((tid & 63) == 0) s_wmax[tid >> 6] = am;
+    __syncthreads();
+    am = max(max(s_wmax[0], s_wmax[1]), max(s_wmax[2], s_wmax[3]));
+    amax = bf16_to_f32(am);
+  }
   float S = amax > 0.0f ? 2688.0f / amax : 1.0f;
   S = __builtin_fminf(S, 3.40282346638528859812e+38f);
-  if (tid == 0) outer[row] = amax / 2688.0f;
+  if (!PER_TENSOR && tid == 0) outer[row] = amax / 2688.0f;
 
 #pragma unroll
   for (int i = 0; i < kNvMaxBlocksPerThread; ++i) {
@@ -121,8 +144,112 @@ hipError_t launch_quantize_nvfp4_rowscaled(const uint16_t* x, int64_t rows_cap, 
                                            uint8_t* block_scales, float* outer, uint32_t* status,
                                            hipStream_t stream) {
   if (rows_cap == 0) return hipSuccess;
-  hipLaunchKernelGGL(nvfp4_rowscaled_kernel, dim3((unsigned)rows_cap), dim3(kNvThreads), 0, stream,
-                     x, rows_cap, cols, G, offsets, data, block_scales, outer, status);
+  hipLaunchKernelGGL(nvfp4_rowscaled_kernel<false>, dim3((unsigned)rows_cap), dim3(kNvThreads), 0,
+                     stream, x, rows_cap, cols, G, offsets, data, block_scales, outer, nullptr,
+                     status);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- per tensor
+//
+// Per-tensor NVFP4 of grouped rows: each group (an expert's rows, or an
+// expert's weight) is one tensor whose outer scale is amax_g / 2688 ("gemm.py",
+// _get_nvfp4_tensor_scale_inv; the GEMM's alpha is the product of the two
+// operands' outer scales).  The group amax must be complete before any of the
+// group's blocks is encoded, so it is its own pass: a small kernel clears the
+// G amax words, nvfp4_group_amax_kernel reduces the live rows to one maximum
+// per group (16-byte loads, integer max of the bf16 magnitudes, per-group
+// maxima in LDS, then one atomic max per group and workgroup: atomics on one
+// address from every XCD serialize, so their count is kept to a few hundred;
+// non-negative floats order as their bit patterns), then the cast above runs
+// with the group's amax.  The second read of the rows mostly hits the
+// last-level cache for inputs that fit in it.
+constexpr int kAmaxThreads = 512;
+constexpr int kAmaxBlocksPerCu = 2;
+constexpr int kAmaxBatch = 8;  // 16-byte loads in flight per thread
+
+__global__ __launch_bounds__(256) void nvfp4_amax_clear_kernel(uint32_t* __restrict__ amax_bits,
+                                                               int G) {
+  for (int g = threadIdx.x; g < G; g += blockDim.x) amax_bits[g] = 0u;
+}
+
+// The live rows are one contiguous run of 16-byte chunks; workgroup b takes the
+// b-th contiguous share of it, thread t every 512th chunk from t.  A thread
+// keeps the running max of its current group and folds it into the
+// workgroup's per-group maxima in LDS when its chunks cross into the next
+// group; at the end the workgroup issues one global atomic max per group it
+// saw, so a group receives one atomic from each workgroup that touches it.
+__global__ __launch_bounds__(kAmaxThreads) void nvfp4_group_amax_kernel(
+    const uint16_t* __restrict__ x, int64_t rows_cap, int64_t cols, int G,
+    const int64_t* __restrict__ offsets, uint32_t* __restrict__ amax_bits, uint32_t* status) {
+  __shared__ int64_t s_off[kMaxGroups + 1];
+  __shared__ uint32_t s_max[kMaxGroups];
+  const int tid = threadIdx.x;
+  for (int g = tid; g < G; g += kAmaxThreads) s_max[g] = 0u;
+  load_offsets_clamped(offsets, G, rows_cap, s_off, blockIdx.x == 0 ? status : nullptr);
+  const int64_t cpr = cols / 8;  // 16-byte chunks per row
+  const int64_t total = s_off[G] * cpr;
+  const int64_t per = (total + gridDim.x - 1) / gridDim.x;
+  const int64_t c0 = (int64_t)blockIdx.x * per;
+  const int64_t c1 = c0 + per < total ? c0 + per : total;
+  int64_t c = c0 + tid;
+  if (c < c1) {
+    const int64_t row = c / cpr;
+    int g = 0, hi = G - 1;  // the largest g with s_off[g] <= row
+    while (g < hi) {
+      const int mid = (g + hi + 1) >> 1;
+      if (s_off[mid] <= row) g = mid; else hi = mid - 1;
+    }
+    int64_t bound = s_off[g + 1] * cpr;  // first chunk past group g
+    const uint4* __restrict__ xv = reinterpret_cast<const uint4*>(x);
+    uint32_t m = 0;
+    for (; c < c1; c += kAmaxBatch * kAmaxThreads) {
+      uint4 v[kAmaxBatch];  // the batch's loads are all issued before any is used
+#pragma unroll
+      for (int k = 0; k < kAmaxBatch; ++k) {
+        const int64_t ck = c + (int64_t)k * kAmaxThreads;
+        v[k] = ck < c1 ? xv[ck] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int k = 0; k < kAmaxBatch; ++k) {
+        const int64_t ck = c + (int64_t)k * kAmaxThreads;
+        if (ck >= c1) break;
+        if (ck >= bound) {
+          atomicMax(&s_max[g], m);
+          m = 0;
+          while (g < G - 1 && s_off[g + 1] * cpr <= ck) ++g;
+          bound = s_off[g + 1] * cpr;
+        }
+        m = max(m, max(max(mag_bits(v[k].x), mag_bits(v[k].y)),
+                       max(mag_bits(v[k].z), mag_bits(v[k].w))));
+      }
+    }
+    atomicMax(&s_max[g], m);
+  }
+  __syncthreads();
+  for (int g = tid; g < G; g += kAmaxThreads)
+    if (s_max[g] != 0u) atomicMax(&amax_bits[g], s_max[g] << 16);
+}
+
+hipError_t launch_quantize_nvfp4_pertensor(const uint16_t* x, int64_t rows_cap, int64_t cols,
+                                           int G, const int64_t* offsets, uint8_t* data,
+                                           uint8_t* block_scales, float* amax, uint32_t* status,
+                                           hipStream_t stream) {
+  uint32_t* bits = reinterpret_cast<uint32_t*>(amax);
+  hipLaunchKernelGGL(nvfp4_amax_clear_kernel, dim3(1), dim3(256), 0, stream, bits, G);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || rows_cap == 0) return e;
+  const int64_t chunks = rows_cap * (cols / 8);
+  int64_t blocks = (chunks + kAmaxBatch * kAmaxThreads - 1) / (kAmaxBatch * kAmaxThreads);
+  const int64_t most = (int64_t)device_cu_count() * kAmaxBlocksPerCu;
+  if (blocks > most) blocks = most;
+  hipLaunchKernelGGL(nvfp4_group_amax_kernel, dim3((unsigned)blocks), dim3(kAmaxThreads), 0, stream,
+                     x, rows_cap, cols, G, offsets, bits, status);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(nvfp4_rowscaled_kernel<true>, dim3((unsigned)rows_cap), dim3(kNvThreads), 0,
+                     stream, x, rows_cap, cols, G, offsets, data, block_scales, nullptr, amax,
+                     nullptr);
   return hipGetLastError();
 }
 

@@ -160,6 +160,34 @@ int grouped_quantize_nvfp4_rowscaled(const void* x, int64_t rows_cap, int64_t co
                                      float* outer, uint32_t* dev_status, void* stream);
 
 /*
+ * grouped_quantize_nvfp4_pertensor
+ *
+ * Per-tensor NVFP4 quantize of grouped rows, each group one tensor ("gemm.py":
+ * an NVFP4 operand carries its amax, the GEMM derives the tensor scale
+ * amax / (6 * 448) from it, _get_nvfp4_tensor_scale_inv; split per expert,
+ * each group has its own amax, as the per-split amax entries of "[Common]
+ * [PyTorch] Add row-scaled NVFP4 support to grouped-tensor GEMM").  The
+ * float32 steps of grouped_quantize_nvfp4_rowscaled with the group's amax in
+ * place of the row's: S_g = 2688 / amax_g (1 if amax_g = 0, capped at
+ * FLT_MAX); s8 = E4M3((bmax / 6) * S_g); enc = S_g / decode(s8) (0 if the
+ * scale is 0, capped at FLT_MAX); q = E2M1(x * enc).  Quantize the experts'
+ * weights with offsets at the expert boundaries (0, N_0, N_0 + N_1, ...).
+ *
+ *   x            [rows_cap, cols] bf16; rows >= offsets[G] are not read.
+ *   cols         multiple of 32, <= 16384.
+ *   data         [rows_cap, cols/2]; element 2j in the low nibble of byte j.
+ *   block_scales [rows_cap, cols/16] E4M3, row-major.
+ *   amax         [G] float32 output: each group's largest magnitude (0 for an
+ *                empty group).  Three launches: clear amax, group amax (atomic
+ *                max per group), cast.
+ * Errors: BSG_ERR_NULL, BSG_ERR_SHAPE, BSG_ERR_UNSUPPORTED (cols > 16384),
+ * BSG_ERR_ALIGN (x and data 16-byte, amax 4-byte).
+ */
+int grouped_quantize_nvfp4_pertensor(const void* x, int64_t rows_cap, int64_t cols, int64_t G,
+                                     const int64_t* offsets, uint8_t* data, uint8_t* block_scales,
+                                     float* amax, uint32_t* dev_status, void* stream);
+
+/*
  * grouped_quantize_nvfp4_rowscaled_colwise
  *
  * Columnwise (transposed) row-scaled NVFP4 copies for the weight gradient
@@ -287,6 +315,32 @@ int grouped_gemm_nvfp4_rowscaled(int64_t G, const uint8_t* a, const uint8_t* a_s
                                  const float* b_outer, const int64_t* n_per_group, void* out,
                                  int64_t ld_out, int out_dtype, float* scratch,
                                  uint32_t* dev_status, void* stream);
+
+/*
+ * grouped_gemm_nvfp4_pertensor
+ *
+ * Per-tensor NVFP4 grouped GEMM ("gemm.py": for NVFP4 operands alpha is the
+ * product of the two tensor scales, alpha = tsi(amax_lhs) * tsi(amax_rhs),
+ * tsi(a) = a / (6 * 448), and the product is scaled by it; the graph-safe
+ * grouped GEMM takes one float32 alpha per group):
+ *   S[r, n]  = sum_k e2m1(A)[r,k] * sA[r, k/16] * e2m1(B_g)[n,k] * sB_g[n, k/16]
+ *   alpha_g  = (a_amax[g] / 2688) * (b_amax[g] / 2688)      (float32)
+ *   Y[r, n]  = S[r, n] * alpha_g     for r live in g, n < N_g
+ *
+ *   a, a_scales, a_amax  grouped_quantize_nvfp4_pertensor outputs ([rows_cap] rows)
+ *   offsets              [G+1] live row offsets
+ *   b, b_scales, b_amax  the experts' [N_g, k] weights quantized one after another
+ *                        with one group per expert (b_amax [G])
+ *   n_per_group          [host] [G] int64 output width of each group, >= 0
+ *   out                  [rows_cap, ld_out]; ld_out >= max N_g.  Columns >= N_g of
+ *                        group g's rows and rows >= offsets[G] are untouched.
+ * k must be a positive multiple of 64.  Errors as grouped_gemm_nvfp4_rowscaled.
+ */
+int grouped_gemm_nvfp4_pertensor(int64_t G, const uint8_t* a, const uint8_t* a_scales,
+                                 const float* a_amax, const int64_t* offsets, int64_t rows_cap,
+                                 int64_t k, const uint8_t* b, const uint8_t* b_scales,
+                                 const float* b_amax, const int64_t* n_per_group, void* out,
+                                 int64_t ld_out, int out_dtype, uint32_t* dev_status, void* stream);
 
 /*
  * grouped_gemm_nvfp4_rowscaled_wgrad

@@ -68,6 +68,12 @@ def test_quantize_validation(lib):
     assert n(p, 128, 128, 4, p, p, p, None, None, None) == 1
     assert n(p, 128, 48, 4, p, p, p, p, None, None) == 2
     assert n(p, 128, 32768, 4, p, p, p, p, None, None) == 4
+    t = lib.grouped_quantize_nvfp4_pertensor
+    assert t(p, 128, 128, 4, p, p, p, None, None, None) == 1                        # amax
+    assert t(p, 128, 48, 4, p, p, p, p, None, None) == 2
+    assert t(p, 128, 128, 0, p, p, p, p, None, None) == 2
+    assert t(p, 128, 32768, 4, p, p, p, p, None, None) == 4
+    assert t(p, 128, 128, 4, p, mis, p, p, None, None) == 3
 
 
 def test_gemm_validation(lib):
@@ -85,6 +91,11 @@ def test_gemm_validation(lib):
     assert nv(2, p, p, p, p, 64, 128, p, p, p, None, p, 128, 0, None, None, None) == 1
     assert nv(2, p, p, p, p, 64, 96, p, p, p, hp, p, 128, 0, None, None, None) == 2   # k % 64
     assert nv(2, p, p, p, p, 64, 128, p, p, p, hp, p, 100, 0, None, None, None) == 2  # ld_out
+    pt = lib.grouped_gemm_nvfp4_pertensor
+    assert pt(2, p, p, None, p, 64, 128, p, p, p, hp, p, 128, 0, None, None) == 1
+    assert pt(2, p, p, p, p, 64, 96, p, p, p, hp, p, 128, 0, None, None) == 2       # k % 64
+    assert pt(2, p, p, p, p, 64, 128, p, p, p, hp, p, 100, 0, None, None) == 2      # ld_out
+    assert pt(2, p, p, p, p, 64, 128, p, p, p, hp, p, 128, 5, None, None) == 4      # out_dtype
     neg = (ctypes.c_int64 * 2)(64, -1)
     assert nv(2, p, p, p, p, 64, 128, p, p, p, ctypes.cast(neg, ctypes.c_void_p), p, 128, 0,
               None, None, None) == 2

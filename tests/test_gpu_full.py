@@ -252,3 +252,61 @@ def test_full_dgrad():
         ref = GM.mxfp8_dgrad(ad[sel], asc[:, sel], bd, bs, np.array([0, len(sel)]), K, len(cols))
         gemm_tolerance_check(y[rows[sel]][:, cols], ref, False, "dgrad group %d" % g)
     assert not np.isnan(y[:int(off[-1])]).any(), "every live output row written"
+
+
+def test_full_nvfp4_pertensor():
+    """Per-tensor NVFP4: 8 experts, 16384 live rows of 18432, K=4096, N_e in
+    {2048, 4096}; each expert's activations and each expert's weight carry one
+    amax.  The amax is checked against a plain max over the whole group; the
+    sampled rows are quantized by the oracle together with one added row that
+    holds the group's amax, so the oracle sees the same tensor scale."""
+    dev = device()
+    case = bench.make_case("nvfp4_pertensor", dev)
+    case.y.fill_(float("nan"))
+    case.step()
+    torch.cuda.synchronize()
+    w = case.w
+    K, npg, G = w.k, case.npg, w.G
+    _, off = O.group_offsets(w.sizes)
+    boff = np.concatenate([[0], np.cumsum(npg)])
+    xa, wa = case.xa.cpu().numpy(), case.wa.cpu().numpy()
+
+    def group_amax(t, lo, hi):
+        if hi <= lo:
+            return np.float32(0)
+        return np.float32(t[lo:hi].abs().max().float().item())
+
+    for g in range(G):
+        assert xa[g] == group_amax(case.x, int(off[g]), int(off[g + 1])), g
+        assert wa[g] == group_amax(case.wt, int(boff[g]), int(boff[g + 1])), g
+
+    def quantize_sample(t, rows, amax):
+        xb = workloads.bf16_bits(t[torch.from_numpy(rows).to(dev)])
+        extra = np.zeros((1, K), np.float32)
+        extra[0, 0] = amax
+        xb = np.concatenate([xb, F.f32_to_bf16_bits_rne(extra)])
+        p, s, a = Q.nvfp4_pertensor(xb, np.array([0, len(rows) + 1]))
+        assert a[0] == amax
+        return p[:-1], s[:-1]
+
+    rng = np.random.default_rng(17)
+    rows = _sample_rows(off, rng)
+    grp = np.searchsorted(off, rows, side="right") - 1
+    y = bf16_out_to_f64(case.y)
+    gd, gs, gwd, gws = host_u8(case.xd), host_u8(case.xs), host_u8(case.wd), host_u8(case.ws)
+    for g in np.unique(grp):
+        sel = rows[grp == g]
+        ap, asc = quantize_sample(case.x, sel, xa[g])
+        assert np.array_equal(gd[sel], ap) and np.array_equal(gs[sel], asc)
+        cols = np.unique(np.concatenate([[0, npg[g] - 1], rng.integers(0, npg[g], 24)]))
+        bp, bsc = quantize_sample(case.wt, boff[g] + cols, wa[g])
+        assert np.array_equal(gwd[boff[g] + cols], bp) and np.array_equal(gws[boff[g] + cols], bsc)
+        one = np.array([0, len(sel)])
+        aam, bam = np.array([xa[g]], np.float32), np.array([wa[g]], np.float32)
+        (_, ref), = GM.nvfp4_pertensor_fprop(ap, asc, aam, one, bp, bsc, bam, [len(cols)], K)
+        gemm_tolerance_check(y[sel][:, cols], ref, False, "nvfp4 per-tensor group %d" % g)
+        if npg[g] < case.ld:
+            assert np.isnan(y[sel][:, npg[g]:]).all(), "columns past N_g untouched"
+    live = int(off[-1])
+    assert np.isnan(y[live:]).all(), "capacity rows untouched"
+    assert not np.isnan(y[:live, :min(npg)]).any()

@@ -308,6 +308,72 @@ def test_nvfp4_end_to_end():
             gemm_tolerance_check(y[rows][:, :npg[g]], r, True, "group %d" % g)
 
 
+# ---------------------------------------------------------------- NVFP4 per-tensor
+
+NVT_CASES = [
+    ([100, 0, 257, 31], [64, 128, 96, 256], 256, 450),
+    ([300, 211], [2048, 4096], 512, 600),
+    ([0, 0], [64, 64], 64, 16),
+]
+
+
+@pytest.mark.parametrize("sizes,npg,K,rows_cap", NVT_CASES)
+@pytest.mark.parametrize("out_f32", [True, False])
+def test_nvfp4_pertensor_gemm_parity(sizes, npg, K, rows_cap, out_f32):
+    rng = np.random.default_rng(2 * K + rows_cap)
+    sizes = np.array(sizes, np.int32)
+    _, off = O.group_offsets(sizes)
+    live = int(off[-1])
+    x = _bits(rng, (rows_cap, K))
+    w = _bits(rng, (sum(npg), K), 0.02)
+    boff = np.concatenate([[0], np.cumsum(npg)])
+    ap, asc, aam = Q.nvfp4_pertensor(x, off)
+    bp, bsc, bam = Q.nvfp4_pertensor(w, boff)
+    ld = max(npg) + 8
+
+    def pad_rows(a, rows):
+        o = np.zeros((rows,) + a.shape[1:], a.dtype)
+        o[:a.shape[0]] = a
+        return to_dev(o)
+
+    dt = torch.float32 if out_f32 else torch.bfloat16
+    out = torch.full((rows_cap, ld), float("nan"), dtype=dt, device=device())
+    bsg.grouped_gemm_nvfp4_pertensor(pad_rows(ap, rows_cap), pad_rows(asc, rows_cap), to_dev(aam),
+                                     to_dev(off), K, to_dev(bp), to_dev(bsc), to_dev(bam), npg,
+                                     out=out, ld_out=ld,
+                                     out_dtype=bsg.BSG_OUT_F32 if out_f32 else bsg.BSG_OUT_BF16)
+    y = bf16_out_to_f64(out)
+    ref = GM.nvfp4_pertensor_fprop(ap, asc, aam, off, bp, bsc, bam, npg, K)
+    for g, (rows, r) in enumerate(ref):
+        if len(rows) == 0:
+            continue
+        gemm_tolerance_check(y[rows][:, :npg[g]], r, out_f32, "group %d" % g)
+        assert np.all(np.isnan(y[rows][:, npg[g]:])), "columns past N_g must stay untouched"
+    assert np.all(np.isnan(y[live:])), "capacity rows must stay untouched"
+
+
+def test_nvfp4_pertensor_end_to_end():
+    rng = np.random.default_rng(13)
+    sizes = np.array([150, 0, 106], np.int32)
+    npg = [128, 256, 384]
+    K, rows_cap = 256, 300
+    xb = _bits(rng, (rows_cap, K))
+    wb = _bits(rng, (sum(npg), K), 0.02)
+    _, off = O.group_offsets(sizes)
+    boff = np.concatenate([[0], np.cumsum(npg)])
+    doff = to_dev(off)
+    a = bsg.grouped_quantize_nvfp4_pertensor(bf16_dev(xb), doff)
+    b = bsg.grouped_quantize_nvfp4_pertensor(bf16_dev(wb), to_dev(boff))
+    y = bsg.grouped_gemm_nvfp4_pertensor(a[0], a[1], a[2], doff, K, b[0], b[1], b[2], npg,
+                                         out_dtype=bsg.BSG_OUT_F32)
+    y = host(y).astype(np.float64)
+    ap, asc, aam = Q.nvfp4_pertensor(xb, off)
+    bp, bsc, bam = Q.nvfp4_pertensor(wb, boff)
+    for g, (rows, r) in enumerate(GM.nvfp4_pertensor_fprop(ap, asc, aam, off, bp, bsc, bam, npg, K)):
+        if len(rows):
+            gemm_tolerance_check(y[rows][:, :npg[g]], r, True, "group %d" % g)
+
+
 # ---------------------------------------------------------------- NVFP4 row-scaled wgrad
 
 NVW_CASES = [

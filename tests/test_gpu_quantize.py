@@ -229,6 +229,53 @@ def test_nvfp4_quantize_bit_exact(rows_cap, cols, sizes):
     assert np.all(np.isnan(t[live:]))
 
 
+# ---------------------------------------------------------------- NVFP4 per-tensor
+
+NVT_CASES = [
+    (400, 4096, [100, 0, 157, 43]),
+    (64, 160, [17, 0, 30]),
+    (40, 16384, [33]),
+    (300, 96, [0, 5, 0, 250, 1]),          # leading empty group, a one-row group
+    (16, 32, [0]),                         # empty routing: only the amax is written (0)
+]
+
+
+@pytest.mark.parametrize("rows_cap,cols,sizes", NVT_CASES)
+def test_nvfp4_pertensor_bit_exact(rows_cap, cols, sizes):
+    rng = np.random.default_rng(rows_cap + 5 * cols)
+    bits = _bits(rng, rows_cap, cols, spread=8)
+    sizes = np.array(sizes, np.int32)
+    live = int(sizes.sum())
+    bits[live:] = workloads.BF16_NAN_BITS
+    if live:
+        bits[0] = 0                         # an all-zero row
+    _, off = O.group_offsets(sizes)
+    wd, ws, wa = Q.nvfp4_pertensor(bits, off)
+    d = filled_u8((rows_cap, cols // 2))
+    s = filled_u8((rows_cap, cols // 16))
+    a = torch.full((len(sizes),), float("nan"), dtype=torch.float32, device=device())
+    bsg.grouped_quantize_nvfp4_pertensor(bf16_dev(bits), to_dev(off), data=d, block_scales=s,
+                                         amax=a)
+    d, s, a = host_u8(d), host_u8(s), host(a)
+    assert np.array_equal(a.view(np.uint32), wa.view(np.uint32))
+    assert np.array_equal(d[:live], wd)
+    assert np.array_equal(s[:live], ws)
+    assert np.all(d[live:] == SENTINEL) and np.all(s[live:] == SENTINEL)
+
+
+def test_nvfp4_pertensor_two_calls_reuse_amax():
+    """The amax buffer is cleared by every call: a second call with smaller
+    values and other group sizes must not keep the first call's maxima."""
+    rng = np.random.default_rng(44)
+    bits = _bits(rng, 256, 128, spread=2)
+    small = F.f32_to_bf16_bits_rne(F.bf16_bits_to_f64(bits).astype(np.float32) * np.float32(1e-3))
+    a = torch.empty(3, dtype=torch.float32, device=device())
+    for b, sizes in ((bits, [100, 56, 100]), (small, [10, 0, 200])):
+        _, off = O.group_offsets(np.array(sizes, np.int32))
+        bsg.grouped_quantize_nvfp4_pertensor(bf16_dev(b), to_dev(off), amax=a)
+        assert np.array_equal(host(a).view(np.uint32), Q.nvfp4_pertensor(b, off)[2].view(np.uint32))
+
+
 NVCOL_CASES = [
     (200, 96, [37, 0, 130, 5]),          # a 32-column last slab, an empty expert
     (800, 4096, [449, 0, 301, 0, 50]),

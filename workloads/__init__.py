@@ -26,6 +26,9 @@ nvfp4_wgrad
        weight gradient: dY [16384, 4096], X [16384, 4096] ~ N(0, 1)
 dgrad  the fprop experts' data gradient: sizes as fprop (its own seed), dY
        [16384, 14336] ~ N(0, 1), W [8, 14336, 4096] ~ N(0, 0.02); dX [16384, 4096]
+nvfp4_pertensor
+       the nvfp4 shapes and size recipe (its own seed) for per-tensor NVFP4
+       (one outer scale per expert's activations and per expert's weight)
 =====  ===========================================================================
 """
 
@@ -34,7 +37,8 @@ from typing import List, Optional
 
 import numpy as np
 
-CONFIG_NAMES = ("tiny", "fprop", "wgrad", "zipf", "nvfp4", "nvfp4_wgrad", "dgrad")
+CONFIG_NAMES = ("tiny", "fprop", "wgrad", "zipf", "nvfp4", "nvfp4_wgrad", "dgrad",
+                "nvfp4_pertensor")
 SEED_BASE = 1000
 BF16_NAN_BITS = 0x7FC0
 
@@ -91,7 +95,7 @@ def group_sizes(name, seed=None):
         p = ranks.astype(np.float64) ** -1.2
         p[np.argsort(p)[:4]] = 0.0
         s = rng.multinomial(32768, p / p.sum())
-    elif name == "nvfp4":
+    elif name in ("nvfp4", "nvfp4_pertensor"):
         s = _dirichlet_multinomial(rng, 16384, 8)
     else:
         raise KeyError(name)
@@ -115,7 +119,7 @@ def get(name, seed=None):
     if name == "dgrad":
         # k: the contraction (fprop's N), n: dX columns (fprop's K)
         return Workload(name, "dgrad", s, 16384, 14336, 4096, seed=sd, w_std=0.02)
-    if name == "nvfp4":
+    if name in ("nvfp4", "nvfp4_pertensor"):
         npg = [2048 if e % 2 == 0 else 4096 for e in range(8)]
         return Workload(name, "nvfp4", s, 18432, 4096, 4096, n_per_group=npg, seed=sd, w_std=0.02)
     raise KeyError(name)
