@@ -36,6 +36,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// 16-byte load of an input that is read once (the quantizers' bf16 inputs):
+// non-temporal, so the stream does not displace cached lines on its way.
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  const v4i q = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
+  return make_uint4((uint32_t)q[0], (uint32_t)q[1], (uint32_t)q[2], (uint32_t)q[3]);
+}
+
 __device__ __forceinline__ void dev_status_or(uint32_t* st, uint32_t bits) {
   if (st != nullptr && bits != 0u) atomicOr(st, bits);
 }

@@ -83,8 +83,13 @@ __global__ __launch_bounds__(kNvThreads) void nvfp4_rowscaled_kernel(
     const int64_t j = tid + (int64_t)kNvThreads * i;
     bm[i] = 0;
     if (j < nblk) {
-      v[i][0] = reinterpret_cast<const uint4*>(xr + 16 * j)[0];
-      v[i][1] = reinterpret_cast<const uint4*>(xr + 16 * j)[1];
+      if constexpr (PER_TENSOR) {  // the second read of the rows: do not re-allocate them
+        v[i][0] = load_stream16(xr + 16 * j);
+        v[i][1] = load_stream16(xr + 16 * j + 8);
+      } else {
+        v[i][0] = reinterpret_cast<const uint4*>(xr + 16 * j)[0];
+        v[i][1] = reinterpret_cast<const uint4*>(xr + 16 * j)[1];
+      }
       bm[i] = max(max(max(mag_bits(v[i][0].x), mag_bits(v[i][0].y)),
                       max(mag_bits(v[i][0].z), mag_bits(v[i][0].w))),
                   max(max(mag_bits(v[i][1].x), mag_bits(v[i][1].y)),
