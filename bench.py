@@ -486,6 +486,46 @@ def cpu_baseline():
                       % (experts - 1, rows_done, nrows, K, K)}
 
 
+def vendor_reference(dev, iters):
+    """Dense GEMMs of the vendor library (hipBLASLt, called through
+    torch._scaled_mm) at the fprop shapes, cold cache like the bench: MXFP8
+    (E4M3 with one E8M0 scale per 32 along K, unit scales) and per-tensor FP8.
+    Context for the grouped kernel's figures, not part of the hot path."""
+    flush = torch.ones((512 << 20) // 4, dtype=torch.int32, device=dev)
+    gen = torch.Generator(device=dev).manual_seed(7)
+    out = {"kind": "vendor reference (hipBLASLt via torch._scaled_mm), dense, bf16 out"}
+    for M, N, K in ((16384, 14336, 4096), (3456, 14336, 4096), (8192, 8192, 8192)):
+        a = torch.randn((M, K), generator=gen, device=dev).to(torch.float8_e4m3fn)
+        b = torch.randn((N, K), generator=gen, device=dev).mul_(1.28).to(torch.float8_e4m3fn)
+        unit = lambda r: torch.full((r, K // 32), 127, dtype=torch.uint8,
+                                    device=dev).view(torch.float8_e8m0fnu)
+        one = torch.ones((), device=dev)
+        for name, sa, sb in (("mxfp8", unit(M), unit(N)), ("fp8_per_tensor", one, one)):
+            def call():
+                return torch._scaled_mm(a, b.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16)
+            key = "%s_%dx%dx%d" % (name, M, N, K)
+            try:
+                call()
+            except Exception as e:  # the vendor path may not exist on this build
+                out[key] = {"error": repr(e)[:200]}
+                continue
+            times = []
+            for _ in range(max(iters, 10)):
+                flush.sum()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                call()
+                e1.record()
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            ms = float(np.median(times))
+            tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+            out[key] = {"us": round(ms * 1e3, 1), "tflops": round(tf, 1),
+                        "frac_of_fp8_peak": round(tf / MFMA_PEAK_TFLOPS["fp8"], 4)}
+    return out
+
+
 # ---------------------------------------------------------------- main
 
 def main():
@@ -500,12 +540,19 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device copy (3x), the reference for "
                          "scaling FETCH_SIZE / WRITE_SIZE counter readings")
+    ap.add_argument("--vendor-reference", action="store_true",
+                    help="only time the vendor library's dense GEMMs (hipBLASLt through "
+                         "torch._scaled_mm: MXFP8 with E8M0 scales per 32, and per-tensor FP8) "
+                         "at the fprop shapes, as context; prints one JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
+    if args.vendor_reference:
+        print(json.dumps(vendor_reference(dev, args.steps)))
+        return
     bsg.load_library()
     flush = None
     if not args.no_flush:

@@ -374,6 +374,63 @@ def test_nvfp4_pertensor_end_to_end():
             gemm_tolerance_check(y[rows][:, :npg[g]], r, True, "group %d" % g)
 
 
+def test_nvfp4_pertensor_hip_graph_replay_with_new_sizes():
+    """The per-tensor path (amax clear kernel, group amax with atomics, cast,
+    GEMM) captured once and replayed after the device sizes change: every
+    replay equals the oracle and a fresh eager call (the amax is cleared by a
+    kernel, not a memset, so replays start from zero)."""
+    dev = device()
+    rng = np.random.default_rng(18)
+    G, K, rows_cap = 3, 256, 600
+    npg = [128, 256, 64]
+    xb = _bits(rng, (rows_cap, K))
+    wb = _bits(rng, (sum(npg), K), 0.02)
+    x, wt = bf16_dev(xb), bf16_dev(wb)
+    boff = np.concatenate([[0], np.cumsum(npg)])
+    qb = bsg.grouped_quantize_nvfp4_pertensor(wt, to_dev(boff))
+    sizes = torch.tensor([100, 0, 200], dtype=torch.int32, device=dev)
+    off = torch.empty(G + 1, dtype=torch.int64, device=dev)
+    ad = torch.empty((rows_cap, K // 2), dtype=torch.uint8, device=dev)
+    asc = torch.empty((rows_cap, K // 16), dtype=torch.uint8, device=dev)
+    aam = torch.empty(G, dtype=torch.float32, device=dev)
+    out = torch.empty((rows_cap, max(npg)), dtype=torch.float32, device=dev)
+
+    def step():
+        bsg.group_offsets_i32_to_i64(sizes, offsets=off)
+        bsg.grouped_quantize_nvfp4_pertensor(x, off, data=ad, block_scales=asc, amax=aam)
+        bsg.grouped_gemm_nvfp4_pertensor(ad, asc, aam, off, K, qb[0], qb[1], qb[2], npg, out=out,
+                                         out_dtype=bsg.BSG_OUT_F32)
+
+    step()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.synchronize()
+    bp, bsc, bam = Q.nvfp4_pertensor(wb, boff)
+    for new in ([100, 0, 200], [50, 250, 300], [0, 0, 600], [600, 0, 0], [10, 20, 30]):
+        sizes.copy_(torch.tensor(new, dtype=torch.int32))
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _, o = O.group_offsets(np.array(new))
+        ap, asn, am = Q.nvfp4_pertensor(xb, o)
+        assert np.array_equal(host(aam).view(np.uint32), am.view(np.uint32)), new
+        y = host(out).astype(np.float64)
+        for gi, (rows, r) in enumerate(GM.nvfp4_pertensor_fprop(ap, asn, am, o, bp, bsc, bam, npg, K)):
+            if len(rows):
+                gemm_tolerance_check(y[rows][:, :npg[gi]], r, True, str(new))
+        eager = out.clone()
+        step()
+        torch.cuda.synchronize()
+        live = int(o[-1])
+        assert torch.equal(eager[:live].nan_to_num(7.0), out[:live].nan_to_num(7.0))
+
+
 # ---------------------------------------------------------------- NVFP4 row-scaled wgrad
 
 NVW_CASES = [

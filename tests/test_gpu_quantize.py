@@ -237,6 +237,7 @@ NVT_CASES = [
     (40, 16384, [33]),
     (300, 96, [0, 5, 0, 250, 1]),          # leading empty group, a one-row group
     (16, 32, [0]),                         # empty routing: only the amax is written (0)
+    (3000, 64, [i % 23 for i in range(256)]),   # 256 groups (the maximum), empty ones among them
 ]
 
 
