@@ -586,6 +586,11 @@ def main():
     head = results.get("fprop") or results[names[0]]
     achieved = head["gemm_tflops"]
     qx = head["kernels_us"].get("quantize_x", {})
+    # all quantize launches of the step together (X row + col and W rowwise)
+    qk = [v for k, v in head["kernels_us"].items() if k.startswith("quantize")]
+    q_bytes = sum(v.get("algorithmic_bytes", 0) for v in qk)
+    q_us = sum(v["us"] for v in qk)
+    q_rate = q_bytes / (q_us * 1e-6) / 1e9 if q_us > 0 else None
     line = {
         "metric": METRIC,
         "value": head["step_tflops"],
@@ -606,6 +611,8 @@ def main():
                    else "warm"},
         "quantize_x_GB_s": qx.get("GB_s"),
         "quantize_x_frac_of_hbm": qx.get("frac_of_hbm"),
+        "quantize_step_GB_s": round(q_rate, 1) if q_rate else None,
+        "quantize_step_frac_of_hbm": round(q_rate / HBM_PEAK_GBS, 4) if q_rate else None,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": MFMA_PEAK_TFLOPS["fp8"], "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_PEAK_TFLOPS["fp8"], 4),
