@@ -55,6 +55,7 @@ FPROP_CASES = [
     ([1], 128, 1, 1),
     ([5, 300, 0, 40], 128, 258, 400),   # row stride not a multiple of 4: per-element stores
     ([260, 3], 256, 260, 263),          # a 4-column last tile
+    ([(7 * i) % 41 if i % 5 else 0 for i in range(256)], 128, 64, 5200),   # 256 groups (maximum)
 ]
 
 
@@ -240,6 +241,8 @@ NV_CASES = [
     ([100, 0, 257, 31], [64, 128, 96, 256], 256, 450),
     ([300, 211], [2048, 4096], 512, 600),
     ([0, 0], [64, 64], 64, 16),
+    ([(7 * i) % 41 if i % 5 else 0 for i in range(256)], [32 + 32 * (i % 3) for i in range(256)],
+     64, 5200),                          # 256 groups (maximum), three output widths
 ]
 
 
@@ -314,6 +317,8 @@ NVT_CASES = [
     ([100, 0, 257, 31], [64, 128, 96, 256], 256, 450),
     ([300, 211], [2048, 4096], 512, 600),
     ([0, 0], [64, 64], 64, 16),
+    ([(7 * i) % 41 if i % 5 else 0 for i in range(256)], [32 + 32 * (i % 3) for i in range(256)],
+     64, 5200),                          # 256 groups (maximum), three output widths
 ]
 
 
