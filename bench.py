@@ -506,7 +506,7 @@ def vendor_reference(dev, iters):
             key = "%s_%dx%dx%d" % (name, M, N, K)
             try:
                 call()
-            except Exception as e:  # the vendor path may not exist on this build
+            except Exception as e:  # the vendor library may not offer this path
                 out[key] = {"error": repr(e)[:200]}
                 continue
             times = []
@@ -546,7 +546,7 @@ def main():
                          "at the fprop shapes, as context; prints one JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")

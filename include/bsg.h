@@ -38,7 +38,7 @@ typedef enum {
   BSG_ERR_NULL = 1,        /* a required pointer is NULL */
   BSG_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
   BSG_ERR_ALIGN = 3,       /* a data pointer is not 16-byte aligned */
-  BSG_ERR_UNSUPPORTED = 4, /* a mode / dtype / flag value this build does not support */
+  BSG_ERR_UNSUPPORTED = 4, /* a mode / dtype / flag value the library does not support */
   BSG_ERR_HIP = 6          /* a HIP launch failed */
 } bsg_status;
 

@@ -4,8 +4,8 @@
 swizzle out of the GEMM and into the quantize: the quantize writes its scales
 directly in the order the GEMM consumes, and the Q->DQ test dequantizer first
 undoes that order.  The order itself is the GEMM's business (the pages' one is
-the cuBLAS 128x4 tile swizzle of "gemm.py", ``swizzled_scale``).  This build's
-order:
+the cuBLAS 128x4 tile swizzle of "gemm.py", ``swizzled_scale``).  The
+order used here:
 
 * MXFP8 scales of a rowwise tensor with R rows and K columns: NQ = ceil(K/128)
   groups of 128 columns; the scales are an [NQ][R] array of 4-byte words, word

@@ -5,7 +5,7 @@
 int64 with a multiplier; offsets are the exclusive prefix sums
 ``offsets[0] = 0, offsets[i] = sum_{j<i} first_dims[j] * last_dim`` (G + 1
 values).  "gemm.py", ``grouped_gemm``: padding, if any, is part of the group
-sizes.  This build adds ``pad_to`` (each size rounded up to a multiple of it
+sizes.  ``pad_to`` is added here (each size rounded up to a multiple of it
 before the sum), used for the 128-padded columnwise copies; pad_to = 1 is the
 pages' formula.
 """

@@ -105,3 +105,22 @@ def test_binding_requires_library(monkeypatch, tmp_path):
     monkeypatch.setattr(bsg, "_lib", None)
     with pytest.raises(RuntimeError):
         bsg.load_library(str(tmp_path / "missing.so"))
+
+
+def test_product_path_never_touches_the_oracle():
+    """Nothing under block_scaled_grouped_amd/ (binding, build, HIP sources) may
+    import, load or name the CPU oracle package."""
+    pkg = os.path.join(ROOT, "block_scaled_grouped_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert not re.search(r"\boracle\b", text), os.path.join(dirpath, f)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2 and "one GPU" in r.stderr
