@@ -89,6 +89,12 @@ struct NvArgs {
 };
 
 static_assert(BM == BN, "A and B stage halves share one layout");
+// the next step's decode units (slots 0 .. kDecodeSlots - 1 of the 64) must all
+// be written before the step's barrier, which follows the decode of slot
+// 48 + kBarrierSlot: a later unit would write the stage other waves then read
+static_assert(kDecodeSlots <= 3 * 16 + kBarrierSlot + 1 && kDecodeSlots <= 64 &&
+                  kBarrierSlot >= 0 && kBarrierSlot < 16,
+              "decode must finish before the step's barrier");
 constexpr int kHalfStage = BM * 128;  // one operand's rows of one K-step, fp16
 constexpr int kOperandB = 2 * kHalfStage;
 
