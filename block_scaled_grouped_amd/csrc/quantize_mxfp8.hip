@@ -355,8 +355,25 @@ __global__ __launch_bounds__(256) void mx_colwise_kernel(
   __shared__ int64_t s_poff[kMaxGroups + 1];
   __shared__ __attribute__((aligned(16))) uint8_t tile[kColTileBytes];
   const bool report = blockIdx.x == 0;
-  load_offsets_clamped(offsets, G, rows_cap, s_off, report ? status : nullptr);
-  load_offsets_clamped(poffsets, G, col_cap, s_poff, report ? status : nullptr);
+  {
+    // both offset arrays in one round trip (clamped and checked as
+    // load_offsets_clamped does)
+    uint32_t* st = report ? status : nullptr;
+    for (int g = threadIdx.x; g <= G; g += blockDim.x) {
+      int64_t v = offsets[g], pv = poffsets[g];
+      uint32_t bad = 0;
+      if (v < 0) { v = 0; bad |= kDevNegativeSize; }
+      if (v > rows_cap) { v = rows_cap; bad |= kDevOverCapacity; }
+      if (pv < 0) { pv = 0; bad |= kDevNegativeSize; }
+      if (pv > col_cap) { pv = col_cap; bad |= kDevOverCapacity; }
+      s_off[g] = v;
+      s_poff[g] = pv;
+      dev_status_or(st, bad);
+    }
+    __syncthreads();
+    for (int g = threadIdx.x + 1; g <= G; g += blockDim.x)
+      if (s_off[g] < s_off[g - 1] || s_poff[g] < s_poff[g - 1]) dev_status_or(st, kDevNegativeSize);
+  }
   const uint32_t lds = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)tile;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
