@@ -16,6 +16,11 @@
 //
 // One 256-thread block per live row, each thread holding up to four 16-element
 // blocks in registers (cols <= 16384): the row is read from HBM once.
+//
+// The file also holds the per-tensor form (one outer scale per group from the
+// group's amax: a group-amax pass, then the same cast) and the columnwise
+// (transposed, per-expert) form for the weight gradient; each is described
+// where it starts below.
 #include "bsg_internal.h"
 
 #pragma clang fp contract(off)
