@@ -319,3 +319,53 @@ def test_nvfp4_pertensor_exact_on_lossless_inputs():
         assert y.shape == (sizes[g], npg[g])
         if sizes[g]:
             assert np.array_equal(y, xv[rows] @ wv[boff[g]:boff[g + 1]].T)
+
+
+# ---------------------------------------------------------------- properties over random shapes
+
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+
+@settings(max_examples=30, deadline=None)
+@given(sizes=st.lists(st.integers(0, 70), min_size=1, max_size=6),
+       kq=st.integers(1, 8), n=st.integers(1, 40), spare=st.integers(0, 5),
+       seed=st.integers(0, 2 ** 31 - 1))
+def test_fprop_lossless_property(sizes, kq, n, spare, seed):
+    """Any ragged grouping (empty groups, capacity rows past the live ones),
+    any K that is a multiple of 32: on small-integer operands, which every MX
+    block holds exactly, the grouped fprop equals the exact per-expert integer
+    product."""
+    rng = np.random.default_rng(seed)
+    sizes = np.array(sizes, np.int32)
+    G, K, rows = len(sizes), 32 * kq, int(sizes.sum()) + spare
+    xb, xi = _int_bits(rng, (rows, K))
+    wb, wi = _int_bits(rng, (G * n, K))
+    _, off = O.group_offsets(sizes)
+    ad, asc = Q.mxfp8_rowwise(xb, off)
+    bd, bsc = Q.mxfp8_rowwise(wb, np.array([0, G * n]))
+    y = GM.mxfp8_fprop(ad, asc, bd.reshape(G, n, K), bsc, off, K)
+    for g in range(G):
+        want = xi[off[g]:off[g + 1]] @ wi[g * n:(g + 1) * n].T
+        assert np.array_equal(y[off[g]:off[g + 1]], want.astype(np.float64))
+
+
+@settings(max_examples=20, deadline=None)
+@given(sizes=st.lists(st.integers(0, 200), min_size=1, max_size=5),
+       nq=st.integers(1, 3), kq=st.integers(1, 3), seed=st.integers(0, 2 ** 31 - 1))
+def test_wgrad_lossless_property(sizes, nq, kq, seed):
+    """Any ragged token split (sizes not multiples of 32, empty experts): the
+    columnwise copies padded per expert to 128 tokens give dW[g] = dY_g^T X_g
+    exactly on small-integer operands, and exact zeros for an empty expert."""
+    rng = np.random.default_rng(seed)
+    sizes = np.array(sizes, np.int32)
+    G, N, K, M = len(sizes), 32 * nq, 32 * kq, int(sizes.sum())
+    dyb, dyi = _int_bits(rng, (M, N))
+    xb, xi = _int_bits(rng, (M, K))
+    _, off = O.group_offsets(sizes)
+    _, poff = O.group_offsets(sizes, pad_to=128)
+    dyc, dys = Q.mxfp8_colwise(dyb, off, poff)
+    xc, xs = Q.mxfp8_colwise(xb, off, poff)
+    dw = GM.mxfp8_wgrad(dyc, dys, xc, xs, poff, N, K)
+    for g in range(G):
+        want = dyi[off[g]:off[g + 1]].T @ xi[off[g]:off[g + 1]]
+        assert np.array_equal(dw[g], want.astype(np.float64)), g
