@@ -384,3 +384,47 @@ def test_nvfp4_pertensor_grouped_equals_per_expert_concatenation():
         assert np.array_equal(p, p_all[off[g]:off[g + 1]])
         assert np.array_equal(s, s_all[off[g]:off[g + 1]])
         assert a[0] == a_all[g]
+
+
+# ---------------------------------------------------------------- properties over random groupings
+
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+
+@settings(max_examples=25, deadline=None)
+@given(sizes=st.lists(st.integers(0, 150), min_size=1, max_size=5),
+       cq=st.integers(1, 3), seed=st.integers(0, 2 ** 31 - 1))
+def test_colwise_grouped_equals_per_expert_property(sizes, cq, seed):
+    """The grouped columnwise copy is, byte for byte, the concatenation of each
+    expert quantized alone (blocks restart at every expert's first token,
+    padding to 128 tokens encodes to zero), for any token split."""
+    rng = np.random.default_rng(seed)
+    sizes = np.array(sizes, np.int32)
+    C = 32 * cq
+    bits = _tiny_bits(rng, max(int(sizes.sum()), 1), C)
+    _, off = O.group_offsets(sizes)
+    _, poff = O.group_offsets(sizes, pad_to=128)
+    data, scales = Q.mxfp8_colwise(bits, off, poff)
+    for g in range(len(sizes)):
+        m = int(sizes[g])
+        d1, s1 = Q.mxfp8_colwise(bits[off[g]:off[g + 1]].reshape(m, C), np.array([0, m]),
+                                 O.group_offsets(np.array([m], np.int32), pad_to=128)[1])
+        assert np.array_equal(data[poff[g] * C:poff[g + 1] * C], d1)
+        assert np.array_equal(scales[poff[g] * C // 32:poff[g + 1] * C // 32], s1)
+
+
+@settings(max_examples=25, deadline=None)
+@given(sizes=st.lists(st.integers(0, 40), min_size=1, max_size=6),
+       cq=st.integers(1, 4), seed=st.integers(0, 2 ** 31 - 1))
+def test_nvfp4_pertensor_grouped_equals_per_expert_property(sizes, cq, seed):
+    rng = np.random.default_rng(seed)
+    sizes = np.array(sizes, np.int32)
+    C = 32 * cq
+    bits = _tiny_bits(rng, max(int(sizes.sum()), 1), C)
+    _, off = O.group_offsets(sizes)
+    p_all, s_all, a_all = Q.nvfp4_pertensor(bits, off)
+    for g in range(len(sizes)):
+        p, s, a = Q.nvfp4_pertensor(bits[off[g]:off[g + 1]], np.array([0, sizes[g]]))
+        assert np.array_equal(p, p_all[off[g]:off[g + 1]])
+        assert np.array_equal(s, s_all[off[g]:off[g + 1]])
+        assert a[0] == a_all[g]
