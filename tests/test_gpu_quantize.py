@@ -330,3 +330,48 @@ def test_determinism_two_runs():
     a = bsg.grouped_quantize_mxfp8(bf16_dev(bits), off)
     b = bsg.grouped_quantize_mxfp8(bf16_dev(bits), off)
     assert torch.equal(a["row_data"], b["row_data"]) and torch.equal(a["row_scales"], b["row_scales"])
+
+
+def test_nan_inf_inputs_stay_in_bounds():
+    """NaN and Inf inputs are outside the contract (their codes are
+    unspecified), but every quantizer must still write only its live outputs:
+    the capacity rows and the bytes past the padded outputs keep their
+    sentinels."""
+    rng = np.random.default_rng(46)
+    rows_cap, cols = 300, 128
+    sizes = np.array([100, 0, 57, 43], np.int32)
+    live = int(sizes.sum())
+    bits = _bits(rng, rows_cap, cols)
+    bits[::7, ::5] = 0x7FC0                      # NaN
+    bits[3::11, 1::9] = 0x7F80                   # +Inf
+    bits[5::13, 2::7] = 0xFF80                   # -Inf
+    _, off = O.group_offsets(sizes)
+    _, poff = O.group_offsets(sizes, pad_to=128)
+    x, doff, dpoff = bf16_dev(bits), to_dev(off), to_dev(poff)
+    cap = rows_cap + 128 * len(sizes)
+    rd = filled_u8((rows_cap, cols))
+    rs = filled_u8(bsg.mx_scale_shape(rows_cap, cols))
+    cd = filled_u8((cap * cols,))
+    cs = filled_u8((cap * cols // 32,))
+    bsg.grouped_quantize_mxfp8(x, doff, row_data=rd, row_scales=rs, padded_offsets=dpoff,
+                               col_rows_cap=cap, col_data=cd, col_scales=cs)
+    nd = filled_u8((rows_cap, cols // 2))
+    ns = filled_u8((rows_cap, cols // 16))
+    no = torch.full((rows_cap,), 7.0, dtype=torch.float32, device=device())
+    bsg.grouped_quantize_nvfp4_rowscaled(x, doff, data=nd, block_scales=ns, outer=no)
+    td = filled_u8((rows_cap, cols // 2))
+    ts = filled_u8((rows_cap, cols // 16))
+    bsg.grouped_quantize_nvfp4_pertensor(x, doff, data=td, block_scales=ts)
+    cd2 = filled_u8((cap * cols // 2,))
+    cs2 = filled_u8((cap * cols // 16,))
+    bsg.grouped_quantize_nvfp4_rowscaled_colwise(x, doff, dpoff, col_rows_cap=cap, data=cd2,
+                                                 block_scales=cs2)
+    torch.cuda.synchronize()
+    n = int(poff[-1]) * cols
+    assert np.all(host_u8(rd)[live:] == SENTINEL)
+    assert np.all(host_u8(rs)[:, live:] == SENTINEL)
+    assert np.all(host_u8(cd)[n:] == SENTINEL) and np.all(host_u8(cs)[n // 32:] == SENTINEL)
+    assert np.all(host_u8(nd)[live:] == SENTINEL) and np.all(host_u8(ns)[live:] == SENTINEL)
+    assert np.all(host(no)[live:] == 7.0)
+    assert np.all(host_u8(td)[live:] == SENTINEL) and np.all(host_u8(ts)[live:] == SENTINEL)
+    assert np.all(host_u8(cd2)[n // 2:] == SENTINEL) and np.all(host_u8(cs2)[n // 16:] == SENTINEL)
