@@ -200,8 +200,10 @@ def mxfp8_dgrad(dy_data, dy_scales, wt_data, wt_scales, offsets, n, k, rows=None
     for rows r of expert g.  dY is the rowwise E5M2 quantize of the
     [rows, n] gradient (``quantize.mxfp8_rowwise(..., elem="e5m2")``); W is
     taken from its columnwise copy (``quantize.mxfp8_colwise`` of the
-    [G * n, k] weights with expert offsets g * n), i.e. per expert the
-    transposed [k, n] block quantized along n, with [n / 128, k, 4] scale words.
+    [G * n, k] weights with expert offsets g * n and padded offsets g * n~,
+    n~ = n rounded up to a multiple of 128: every columnwise copy pads a group's
+    tokens to a multiple of 128), i.e. per expert the transposed [k, n~] block
+    quantized along n (zero padding past n), with [n~ / 128, k, 4] scale words.
     ``rows`` optionally restricts the output rows.  Returns float64 [len(rows), k]."""
     off = np.asarray(offsets, dtype=np.int64)
     G = len(off) - 1
@@ -210,6 +212,7 @@ def mxfp8_dgrad(dy_data, dy_scales, wt_data, wt_scales, offsets, n, k, rows=None
     rows = np.asarray(rows, dtype=np.int64)
     grp = _group_of_rows(off, rows)
     nq = mx_scale_words(n)
+    npad = 4 * MX_BLOCK * nq          # the expert's padded token count n~
     dy_data = np.asarray(dy_data).reshape(-1, n)
     dy_scales = np.asarray(dy_scales).reshape(nq, -1, 4)
     out = np.zeros((len(rows), k), dtype=np.float64)
@@ -218,9 +221,10 @@ def mxfp8_dgrad(dy_data, dy_scales, wt_data, wt_scales, offsets, n, k, rows=None
         if len(sel) == 0:
             continue
         a = mxfp8_dequant_rows(dy_data[rows[sel]], dy_scales[:, rows[sel], :], n, elem="e5m2")
-        wt = np.asarray(wt_data[g * n * k:(g + 1) * n * k]).reshape(k, n)
-        ws = np.asarray(wt_scales[g * n * k // MX_BLOCK:(g + 1) * n * k // MX_BLOCK]).reshape(nq, k, 4)
-        out[sel] = a @ mxfp8_dequant_rows(wt, ws, n).T
+        wt = np.asarray(wt_data[g * npad * k:(g + 1) * npad * k]).reshape(k, npad)
+        ws = np.asarray(wt_scales[g * npad * k // MX_BLOCK:(g + 1) * npad * k // MX_BLOCK]
+                        ).reshape(nq, k, 4)
+        out[sel] = a @ mxfp8_dequant_rows(wt, ws, npad)[:, :n].T
     return out
 
 

@@ -114,15 +114,16 @@ def test_grouped_equals_per_expert_gemm():
     assert np.array_equal(sub, y[[5, 40, 63]])
 
 
-def test_nvfp4_exact_on_lossless_inputs_and_widths():
+@pytest.mark.parametrize("K", [64, 32, 96])
+def test_nvfp4_exact_on_lossless_inputs_and_widths(K):
     """Values on the E2M1 grid with row max 6: S = 448, every block scale 448,
     enc = 1, so the codes are the values; Y must equal the integer product times
-    the two outer scales, per group over its own N_g columns."""
-    rng = np.random.default_rng(24)
+    the two outer scales, per group over its own N_g columns (K = 32 and 96 end
+    in half a 64-element step)."""
+    rng = np.random.default_rng(24 + K)
     grid = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -.5, -1, -1.5, -2, -3, -4, -6])
     sizes = np.array([3, 0, 5], np.int32)
     npg = [8, 16, 24]
-    K = 64
 
     def mk(rows):
         v = rng.choice(grid, (rows, K))
@@ -201,20 +202,24 @@ def test_nvfp4_wgrad_exact_on_lossless_inputs():
     assert np.array_equal(part[0], dw[3][[5, 1]]) and np.array_equal(part[1], dw[0][[5, 1]])
 
 
-def test_dgrad_exact_on_lossless_inputs():
+@pytest.mark.parametrize("N,K", [(256, 96), (160, 64), (32, 96)])
+def test_dgrad_exact_on_lossless_inputs(N, K):
     """dY and W small integers: lossless in E5M2 (dY) and E4M3 (W) under any MX
     scale, so dX must equal the exact per-expert integer product dY_g @ W_g.
     n != k catches a transposed W copy; an empty expert and uneven row counts
-    catch a wrong group range."""
-    rng = np.random.default_rng(26)
+    catch a wrong group range; a contraction n that is not a multiple of 128
+    uses the columnwise copy whose experts are padded to 128 tokens (a wrong
+    expert stride or a padding read as data fails)."""
+    rng = np.random.default_rng(26 + N)
     sizes = np.array([9, 0, 40, 3], np.int32)
-    G, M, N, K = len(sizes), int(sizes.sum()), 256, 96
+    G, M = len(sizes), int(sizes.sum())
+    npad = -(-N // 128) * 128
     dyb, dyi = _int_bits(rng, (M, N))
     wb, wi = _int_bits(rng, (G * N, K))
     _, off = O.group_offsets(sizes)
     dyd, dys = Q.mxfp8_rowwise(dyb, off, elem="e5m2")
     woff = np.arange(G + 1, dtype=np.int64) * N
-    wtd, wts = Q.mxfp8_colwise(wb, woff, woff)
+    wtd, wts = Q.mxfp8_colwise(wb, woff, np.arange(G + 1, dtype=np.int64) * npad)
     dx = GM.mxfp8_dgrad(dyd, dys, wtd, wts, off, N, K)
     for g in range(G):
         want = dyi[off[g]:off[g + 1]] @ wi[g * N:(g + 1) * N]
