@@ -106,6 +106,60 @@ def _need_cuda(*ts):
             raise ValueError("bsg operates on device tensors")
 
 
+def _dtype_name(dt):
+    return str(dt).replace("torch.", "")
+
+
+def _req(t, name, nbytes, dtype=None, optional=False):
+    """Checks, before anything is launched, that tensor t can hold what the C
+    call will touch: a contiguous device tensor of at least nbytes bytes (and of
+    the given torch dtype).  A buffer that is too small would otherwise be read
+    or written out of bounds on the device."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError("%s is required" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if dtype is not None:
+        allowed = dtype if isinstance(dtype, tuple) else (dtype,)
+        if t.dtype not in allowed:
+            raise ValueError("%s must be %s, not %s" % (
+                name, " or ".join(_dtype_name(d) for d in allowed), _dtype_name(t.dtype)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError("%s holds %d bytes; the call touches %d" % (name, have, int(nbytes)))
+
+
+def _i64():
+    import torch
+    return torch.int64
+
+
+def _f32():
+    import torch
+    return torch.float32
+
+
+def _bf16_2d(x, name="x"):
+    import torch
+    if x.dim() != 2:
+        raise ValueError("%s must be 2-D [rows, cols]" % name)
+    _req(x, name, 0, torch.bfloat16)
+    return x.shape
+
+
+def _out_dtype(out_dtype):
+    import torch
+    if out_dtype == BSG_OUT_F32:
+        return torch.float32, 4
+    if out_dtype == BSG_OUT_BF16:
+        return torch.bfloat16, 2
+    raise ValueError("unknown out_dtype %r" % (out_dtype,))
+
+
 def mx_scale_row_bytes(cols):
     """Stored E8M0 bytes per row of a rowwise MXFP8 tensor (cols / 32 rounded up to 4)."""
     return ((cols // 32 + 3) // 4) * 4
@@ -121,12 +175,15 @@ def group_offsets_i32_to_i64(sizes, multiplier=1, pad_to=1, capacity=0, sizes_i6
     """int32 [G] sizes -> (int64 [G] sizes * multiplier, int64 [G+1] offsets)."""
     import torch
     lib = load_library()
-    _need_cuda(sizes)
+    _req(sizes, "sizes", 0, torch.int32)
     G = sizes.numel()
     if sizes_i64 is None:
         sizes_i64 = torch.empty(G, dtype=torch.int64, device=sizes.device)
     if offsets is None:
         offsets = torch.empty(G + 1, dtype=torch.int64, device=sizes.device)
+    _req(sizes_i64, "sizes_i64", 8 * G, torch.int64)
+    _req(offsets, "offsets", 8 * (G + 1), torch.int64)
+    _req(status, "status", 4, optional=True)
     _check(lib.group_offsets_i32_to_i64(_ptr(sizes), G, multiplier, pad_to, _ptr(sizes_i64),
                                         _ptr(offsets), capacity, _ptr(status), _stream(sizes)))
     return sizes_i64, offsets
@@ -139,9 +196,9 @@ def grouped_quantize_mxfp8(x, offsets, G=None, rowwise=True, padded_offsets=None
     "col_data"/"col_scales" (when padded_offsets is given), uint8 tensors."""
     import torch
     lib = load_library()
-    _need_cuda(x, offsets)
-    rows_cap, cols = x.shape
+    rows_cap, cols = _bf16_2d(x)
     G = offsets.numel() - 1 if G is None else G
+    _req(offsets, "offsets", 8 * (G + 1), _i64())
     out = {}
     if rowwise:
         if row_data is None:
@@ -161,6 +218,13 @@ def grouped_quantize_mxfp8(x, offsets, G=None, rowwise=True, padded_offsets=None
             col_scales = torch.empty(col_rows_cap * cols // 32, dtype=torch.uint8, device=x.device)
         out["col_data"], out["col_scales"] = col_data, col_scales
         out["col_rows_cap"] = col_rows_cap
+        _req(padded_offsets, "padded_offsets", 8 * (G + 1), _i64())
+        _req(col_data, "col_data", col_rows_cap * cols)
+        _req(col_scales, "col_scales", col_rows_cap * cols // 32)
+    if rowwise:
+        _req(row_data, "row_data", rows_cap * cols)
+        _req(row_scales, "row_scales", rows_cap * mx_scale_row_bytes(cols))
+    _req(status, "status", 4, optional=True)
     _check(lib.grouped_quantize_mxfp8(_ptr(x), rows_cap, cols, G, _ptr(offsets), _ptr(row_data),
                                       _ptr(row_scales), _ptr(padded_offsets),
                                       col_rows_cap or 0, _ptr(col_data), _ptr(col_scales),
@@ -174,13 +238,16 @@ def grouped_quantize_mxfp8_rowwise_e5m2(x, offsets, G=None, row_data=None, row_s
     grouped_quantize_mxfp8's rowwise output)."""
     import torch
     lib = load_library()
-    _need_cuda(x, offsets)
-    rows_cap, cols = x.shape
+    rows_cap, cols = _bf16_2d(x)
     G = offsets.numel() - 1 if G is None else G
+    _req(offsets, "offsets", 8 * (G + 1), torch.int64)
     if row_data is None:
         row_data = torch.empty((rows_cap, cols), dtype=torch.uint8, device=x.device)
     if row_scales is None:
         row_scales = torch.empty(mx_scale_shape(rows_cap, cols), dtype=torch.uint8, device=x.device)
+    _req(row_data, "row_data", rows_cap * cols)
+    _req(row_scales, "row_scales", rows_cap * mx_scale_row_bytes(cols))
+    _req(status, "status", 4, optional=True)
     _check(lib.grouped_quantize_mxfp8_rowwise_e5m2(_ptr(x), rows_cap, cols, G, _ptr(offsets),
                                                    _ptr(row_data), _ptr(row_scales), _ptr(status),
                                                    _stream(x)))
@@ -192,15 +259,19 @@ def grouped_quantize_nvfp4_rowscaled(x, offsets, G=None, data=None, block_scales
     """bf16 [rows_cap, cols] -> (E2M1 [rows_cap, cols/2], E4M3 [rows_cap, cols/16], f32 [rows_cap])."""
     import torch
     lib = load_library()
-    _need_cuda(x, offsets)
-    rows_cap, cols = x.shape
+    rows_cap, cols = _bf16_2d(x)
     G = offsets.numel() - 1 if G is None else G
+    _req(offsets, "offsets", 8 * (G + 1), torch.int64)
     if data is None:
         data = torch.empty((rows_cap, cols // 2), dtype=torch.uint8, device=x.device)
     if block_scales is None:
         block_scales = torch.empty((rows_cap, cols // 16), dtype=torch.uint8, device=x.device)
     if outer is None:
         outer = torch.empty(rows_cap, dtype=torch.float32, device=x.device)
+    _req(data, "data", rows_cap * cols // 2)
+    _req(block_scales, "block_scales", rows_cap * cols // 16)
+    _req(outer, "outer", 4 * rows_cap, torch.float32)
+    _req(status, "status", 4, optional=True)
     _check(lib.grouped_quantize_nvfp4_rowscaled(_ptr(x), rows_cap, cols, G, _ptr(offsets),
                                                 _ptr(data), _ptr(block_scales), _ptr(outer),
                                                 _ptr(status), _stream(x)))
@@ -212,15 +283,19 @@ def grouped_quantize_nvfp4_pertensor(x, offsets, G=None, data=None, block_scales
     """bf16 [rows_cap, cols] -> (E2M1 [rows_cap, cols/2], E4M3 [rows_cap, cols/16], f32 amax [G])."""
     import torch
     lib = load_library()
-    _need_cuda(x, offsets)
-    rows_cap, cols = x.shape
+    rows_cap, cols = _bf16_2d(x)
     G = offsets.numel() - 1 if G is None else G
+    _req(offsets, "offsets", 8 * (G + 1), torch.int64)
     if data is None:
         data = torch.empty((rows_cap, cols // 2), dtype=torch.uint8, device=x.device)
     if block_scales is None:
         block_scales = torch.empty((rows_cap, cols // 16), dtype=torch.uint8, device=x.device)
     if amax is None:
         amax = torch.empty(G, dtype=torch.float32, device=x.device)
+    _req(data, "data", rows_cap * cols // 2)
+    _req(block_scales, "block_scales", rows_cap * cols // 16)
+    _req(amax, "amax", 4 * G, torch.float32)
+    _req(status, "status", 4, optional=True)
     _check(lib.grouped_quantize_nvfp4_pertensor(_ptr(x), rows_cap, cols, G, _ptr(offsets),
                                                 _ptr(data), _ptr(block_scales), _ptr(amax),
                                                 _ptr(status), _stream(x)))
@@ -234,9 +309,10 @@ def grouped_quantize_nvfp4_rowscaled_colwise(x, offsets, padded_offsets, G=None,
     See include/bsg.h for the block layout."""
     import torch
     lib = load_library()
-    _need_cuda(x, offsets, padded_offsets)
-    rows_cap, cols = x.shape
+    rows_cap, cols = _bf16_2d(x)
     G = offsets.numel() - 1 if G is None else G
+    _req(offsets, "offsets", 8 * (G + 1), torch.int64)
+    _req(padded_offsets, "padded_offsets", 8 * (G + 1), torch.int64)
     if col_rows_cap is None:
         col_rows_cap = rows_cap + BSG_COLWISE_PAD * G
     if data is None:
@@ -245,10 +321,41 @@ def grouped_quantize_nvfp4_rowscaled_colwise(x, offsets, padded_offsets, G=None,
         block_scales = torch.empty(col_rows_cap * cols // 16, dtype=torch.uint8, device=x.device)
     if outer is None:
         outer = torch.empty((G, cols), dtype=torch.float32, device=x.device)
+    _req(data, "data", col_rows_cap * cols // 2)
+    _req(block_scales, "block_scales", col_rows_cap * cols // 16)
+    _req(outer, "outer", 4 * G * cols, torch.float32)
+    _req(status, "status", 4, optional=True)
     _check(lib.grouped_quantize_nvfp4_rowscaled_colwise(
         _ptr(x), rows_cap, cols, G, _ptr(offsets), _ptr(padded_offsets), col_rows_cap, _ptr(data),
         _ptr(block_scales), _ptr(outer), _ptr(status), _stream(x)))
     return data, block_scales, outer
+
+
+def _mx_gemm_bytes(mode, G, rows_cap, n, k):
+    """Bytes grouped_gemm_mxfp8 reads from a, a_scales, b, b_scales, and the
+    output's element count (include/bsg.h gives the layouts)."""
+    nq = (k + 127) // 128
+    if mode == BSG_FPROP_TN:
+        return (rows_cap * k, 4 * nq * rows_cap, G * n * k, 4 * nq * G * n, rows_cap * n)
+    if mode == BSG_DGRAD_NN:
+        kpad = 128 * nq   # the weights' columnwise copy pads each expert to 128 tokens
+        return (rows_cap * k, 4 * nq * rows_cap, G * n * kpad, G * n * kpad // 32, rows_cap * n)
+    if mode == BSG_WGRAD_NT:
+        return (rows_cap * n, rows_cap * n // 32, rows_cap * k, rows_cap * k // 32, G * n * k)
+    raise ValueError("unknown mode %r" % (mode,))
+
+
+def _mx_gemm_check(mode, G, a, a_scales, b, b_scales, offsets, rows_cap, n, k, out, out_dtype,
+                   status):
+    na, nas, nb, nbs, nout = _mx_gemm_bytes(mode, G, rows_cap, n, k)
+    _req(a, "a", na)
+    _req(a_scales, "a_scales", nas)
+    _req(b, "b", nb)
+    _req(b_scales, "b_scales", nbs)
+    _req(offsets, "offsets", 8 * (G + 1), _i64())
+    dt, esz = _out_dtype(out_dtype)
+    _req(out, "out", esz * nout, dt)
+    _req(status, "status", 4, optional=True)
 
 
 def grouped_gemm_mxfp8(mode, a, a_scales, b, b_scales, offsets, rows_cap, n, k, out=None,
@@ -259,9 +366,11 @@ def grouped_gemm_mxfp8(mode, a, a_scales, b, b_scales, offsets, rows_cap, n, k, 
     _need_cuda(a, a_scales, b, b_scales, offsets)
     G = offsets.numel() - 1 if G is None else G
     if out is None:
-        dt = torch.float32 if out_dtype == BSG_OUT_F32 else torch.bfloat16
+        dt = _out_dtype(out_dtype)[0]
         shape = (G, n, k) if mode == BSG_WGRAD_NT else (rows_cap, n)
         out = torch.empty(shape, dtype=dt, device=a.device)
+    _mx_gemm_check(mode, G, a, a_scales, b, b_scales, offsets, rows_cap, n, k, out, out_dtype,
+                   status)
     _check(lib.grouped_gemm_mxfp8(mode, G, _ptr(a), _ptr(a_scales), _ptr(b), _ptr(b_scales),
                                   _ptr(offsets), rows_cap, n, k, _ptr(out), out_dtype, _ptr(status),
                                   _stream(a)))
@@ -277,11 +386,32 @@ def grouped_gemm_mxfp8_ex(mode, a, a_scales, b, b_scales, offsets, rows_cap, n, 
     lib = load_library()
     _need_cuda(a, a_scales, b, b_scales, offsets, out)
     G = offsets.numel() - 1 if G is None else G
+    _mx_gemm_check(mode, G, a, a_scales, b, b_scales, offsets, rows_cap, n, k, out, out_dtype,
+                   status)
+    _req(alpha, "alpha", 4 * G, _f32(), optional=True)
+    _req(beta, "beta", 4 * G, _f32(), optional=True)
+    _req(bias, "bias", 4 * G * (k if mode == BSG_WGRAD_NT else n), _f32(), optional=True)
     _check(lib.grouped_gemm_mxfp8_ex(mode, G, _ptr(a), _ptr(a_scales), _ptr(b), _ptr(b_scales),
                                      _ptr(offsets), rows_cap, n, k, _ptr(out), out_dtype,
                                      _ptr(alpha), _ptr(beta), _ptr(bias), _ptr(status),
                                      _stream(a)))
     return out
+
+
+def _nv_gemm_check(G, a, a_scales, a_outer, offsets, rows_cap, k, b, b_scales, b_outer, npg, out,
+                   ld_out, out_dtype, status, per_tensor):
+    nb = sum(npg)
+    _req(a, "a", rows_cap * k // 2)
+    _req(a_scales, "a_scales", rows_cap * k // 16)
+    _req(a_outer, "a_amax" if per_tensor else "a_outer", 4 * (G if per_tensor else rows_cap),
+         _f32())
+    _req(offsets, "offsets", 8 * (G + 1), _i64())
+    _req(b, "b", nb * k // 2)
+    _req(b_scales, "b_scales", nb * k // 16)
+    _req(b_outer, "b_amax" if per_tensor else "b_outer", 4 * (G if per_tensor else nb), _f32())
+    dt, esz = _out_dtype(out_dtype)
+    _req(out, "out", esz * rows_cap * ld_out, dt)
+    _req(status, "status", 4, optional=True)
 
 
 def grouped_gemm_nvfp4_rowscaled(a, a_scales, a_outer, offsets, k, b, b_scales, b_outer,
@@ -299,8 +429,11 @@ def grouped_gemm_nvfp4_rowscaled(a, a_scales, a_outer, offsets, k, b, b_scales, 
     if ld_out is None:
         ld_out = max(npg) if out is None else out.shape[1]
     if out is None:
-        dt = torch.float32 if out_dtype == BSG_OUT_F32 else torch.bfloat16
+        dt = _out_dtype(out_dtype)[0]
         out = torch.empty((rows_cap, ld_out), dtype=dt, device=a.device)
+    _nv_gemm_check(G, a, a_scales, a_outer, offsets, rows_cap, k, b, b_scales, b_outer, npg, out,
+                   ld_out, out_dtype, status, per_tensor=False)
+    _req(scratch, "scratch", 4 * rows_cap * ld_out, torch.float32, optional=True)
     host_n = (ctypes.c_int64 * G)(*npg)
     _check(lib.grouped_gemm_nvfp4_rowscaled(G, _ptr(a), _ptr(a_scales), _ptr(a_outer),
                                             _ptr(offsets), rows_cap, k, _ptr(b), _ptr(b_scales),
@@ -326,8 +459,10 @@ def grouped_gemm_nvfp4_pertensor(a, a_scales, a_amax, offsets, k, b, b_scales, b
     if ld_out is None:
         ld_out = max(npg) if out is None else out.shape[1]
     if out is None:
-        dt = torch.float32 if out_dtype == BSG_OUT_F32 else torch.bfloat16
+        dt = _out_dtype(out_dtype)[0]
         out = torch.empty((rows_cap, ld_out), dtype=dt, device=a.device)
+    _nv_gemm_check(G, a, a_scales, a_amax, offsets, rows_cap, k, b, b_scales, b_amax, npg, out,
+                   ld_out, out_dtype, status, per_tensor=True)
     host_n = (ctypes.c_int64 * G)(*npg)
     _check(lib.grouped_gemm_nvfp4_pertensor(G, _ptr(a), _ptr(a_scales), _ptr(a_amax),
                                             _ptr(offsets), rows_cap, k, _ptr(b), _ptr(b_scales),
@@ -349,8 +484,18 @@ def grouped_gemm_nvfp4_rowscaled_wgrad(a, a_scales, a_outer, b, b_scales, b_oute
     if col_rows_cap is None:
         col_rows_cap = a.numel() * 2 // n
     if out is None:
-        dt = torch.float32 if out_dtype == BSG_OUT_F32 else torch.bfloat16
+        dt = _out_dtype(out_dtype)[0]
         out = torch.empty((G, n, k), dtype=dt, device=a.device)
+    _req(a, "a", col_rows_cap * n // 2)
+    _req(a_scales, "a_scales", col_rows_cap * n // 16)
+    _req(a_outer, "a_outer", 4 * G * n, torch.float32)
+    _req(b, "b", col_rows_cap * k // 2)
+    _req(b_scales, "b_scales", col_rows_cap * k // 16)
+    _req(b_outer, "b_outer", 4 * G * k, torch.float32)
+    _req(padded_offsets, "padded_offsets", 8 * (G + 1), torch.int64)
+    dt, esz = _out_dtype(out_dtype)
+    _req(out, "out", esz * G * n * k, dt)
+    _req(status, "status", 4, optional=True)
     _check(lib.grouped_gemm_nvfp4_rowscaled_wgrad(
         G, _ptr(a), _ptr(a_scales), _ptr(a_outer), _ptr(b), _ptr(b_scales), _ptr(b_outer),
         _ptr(padded_offsets), col_rows_cap, n, k, _ptr(out), out_dtype, _ptr(status), _stream(a)))

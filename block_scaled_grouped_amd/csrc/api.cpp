@@ -131,8 +131,6 @@ int grouped_quantize_nvfp4_rowscaled(const void* x, int64_t rows_cap, int64_t co
     return fail(BSG_ERR_SHAPE, "%s: G=%lld outside [1, %d]", fn, (long long)G, BSG_MAX_GROUPS);
   if (rows_cap < 0 || cols <= 0 || cols % 32 != 0)
     return fail(BSG_ERR_SHAPE, "%s: need rows_cap >= 0 and cols a positive multiple of 32", fn);
-  if (cols > 16384)
-    return fail(BSG_ERR_UNSUPPORTED, "%s: cols=%lld above the supported 16384", fn, (long long)cols);
   if (rows_cap > 0x7fffffffLL) return fail(BSG_ERR_SHAPE, "%s: rows_cap too large", fn);
   if (!aligned16(x) || !aligned16(data) || !aligned4(outer))
     return fail(BSG_ERR_ALIGN, "%s: x and data must be 16-byte aligned, outer 4-byte", fn);
@@ -152,8 +150,6 @@ int grouped_quantize_nvfp4_pertensor(const void* x, int64_t rows_cap, int64_t co
     return fail(BSG_ERR_SHAPE, "%s: G=%lld outside [1, %d]", fn, (long long)G, BSG_MAX_GROUPS);
   if (rows_cap < 0 || cols <= 0 || cols % 32 != 0)
     return fail(BSG_ERR_SHAPE, "%s: need rows_cap >= 0 and cols a positive multiple of 32", fn);
-  if (cols > 16384)
-    return fail(BSG_ERR_UNSUPPORTED, "%s: cols=%lld above the supported 16384", fn, (long long)cols);
   if (rows_cap > 0x7fffffffLL) return fail(BSG_ERR_SHAPE, "%s: rows_cap too large", fn);
   if (!aligned16(x) || !aligned16(data) || !aligned4(amax))
     return fail(BSG_ERR_ALIGN, "%s: x and data must be 16-byte aligned, amax 4-byte", fn);
@@ -178,8 +174,6 @@ int grouped_quantize_nvfp4_rowscaled_colwise(const void* x, int64_t rows_cap, in
   if (rows_cap < 0 || col_rows_cap < 0 || cols <= 0 || cols % 32 != 0)
     return fail(BSG_ERR_SHAPE,
                 "%s: need rows_cap >= 0, col_rows_cap >= 0 and cols a positive multiple of 32", fn);
-  if (cols > 16384)
-    return fail(BSG_ERR_UNSUPPORTED, "%s: cols=%lld above the supported 16384", fn, (long long)cols);
   if (rows_cap > 0x7fffffffLL || col_rows_cap > 0x7fffffffLL)
     return fail(BSG_ERR_SHAPE, "%s: rows_cap or col_rows_cap too large", fn);
   if (!aligned16(x) || !aligned16(data) || !aligned4(outer))
@@ -209,11 +203,12 @@ static int gemm_mxfp8_impl(const char* fn, int mode, int64_t G, const uint8_t* a
     return fail(BSG_ERR_SHAPE, "%s: need rows_cap >= 0, n >= 1, k >= 1", fn);
   const int64_t esz = out_dtype == BSG_OUT_F32 ? 4 : 2;
   if (mode != BSG_WGRAD_NT) {
-    if (k % 128 != 0)
-      return fail(BSG_ERR_SHAPE, "%s: FPROP / DGRAD need k %% 128 == 0 (got %lld)", fn, (long long)k);
-    if (256 * k >= kMaxTileBytes || 256 * n * esz >= kMaxTileBytes || n > 0x7fffffffLL)
+    if (k % 32 != 0)
+      return fail(BSG_ERR_SHAPE, "%s: FPROP / DGRAD need k %% 32 == 0 (got %lld)", fn, (long long)k);
+    const int64_t nq = (k + 127) / 128;  // scale words per row; DGRAD's B rows hold 128 nq bytes
+    if (256 * 128 * nq >= kMaxTileBytes || 256 * n * esz >= kMaxTileBytes || n > 0x7fffffffLL)
       return fail(BSG_ERR_SHAPE, "%s: n or k too large for one tile's 32-bit offsets", fn);
-    if ((k / 128) * 4 * rows_cap >= kMaxTileBytes || (k / 128) * 4 * G * n >= kMaxTileBytes)
+    if (nq * 4 * rows_cap >= kMaxTileBytes || nq * 4 * G * n >= kMaxTileBytes)
       return fail(BSG_ERR_SHAPE, "%s: scale arrays too large for 32-bit offsets", fn);
   } else {
     if (n % 32 != 0 || k % 32 != 0)
@@ -265,8 +260,8 @@ static int gemm_nvfp4_impl(const char* fn, bool per_tensor, int64_t G, const uin
     return fail(BSG_ERR_UNSUPPORTED, "%s: unknown out_dtype %d", fn, out_dtype);
   if (G < 1 || G > BSG_MAX_GROUPS)
     return fail(BSG_ERR_SHAPE, "%s: G=%lld outside [1, %d]", fn, (long long)G, BSG_MAX_GROUPS);
-  if (rows_cap < 0 || k < 64 || k % 64 != 0)
-    return fail(BSG_ERR_SHAPE, "%s: need rows_cap >= 0 and k a positive multiple of 64 (got %lld)", fn,
+  if (rows_cap < 0 || k < 32 || k % 32 != 0)
+    return fail(BSG_ERR_SHAPE, "%s: need rows_cap >= 0 and k a positive multiple of 32 (got %lld)", fn,
                 (long long)k);
   bsg::NvGroupTable tab;
   memset(&tab, 0, sizeof tab);

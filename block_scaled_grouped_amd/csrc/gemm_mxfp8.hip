@@ -107,7 +107,8 @@ struct TileDesc {
   int64_t sqa, sqb;   // bytes between the scale words of consecutive 128-wide K-groups
   int64_t as_bytes, bs_bytes;  // scale bytes readable from `as` / `bs`
   int a_rows, b_rows; // valid rows (rows past them load as zeros)
-  int64_t kl;         // contraction length, multiple of 128
+  int64_t kl;         // contraction length, multiple of 32; data past it (the last
+                      // pair's tail) is copied as zeros
   char* out;          // element (0, 0) of the output tile
   int64_t ldc;        // output row stride in elements
   int out_rows, out_cols;
@@ -219,7 +220,19 @@ struct Dma {
   int bw[2];             // lane LDS offset of its store in the B tile, q = 0 rows, with
                          // the slot swizzle of an even / odd q
   int ldb8;              // 8 rows of B stride (uniform)
+  int ka[2];             // K offset within a pair of this lane's chunk in even / odd loads
+  int kb;                // the same for its register-path B loads
+  int kl;                // contraction length (uniform)
 };
+
+// A lane's copy of a chunk that starts at or past the contraction end gets an
+// offset past every descriptor's range, so the buffer unit returns zeros for it
+// (the bytes past k in a row are the next row's, or stale bytes of rows no group
+// owns, which may hold NaN codes).
+constexpr int kOutOfRange = 0x7ffffff0;
+__device__ __forceinline__ int k_mask(int voff, int kpos, int lim) {
+  return kpos < lim ? voff : kOutOfRange;
+}
 
 __device__ __forceinline__ Dma make_dma(const TileDesc& t, int w, int lane) {
   Dma d;
@@ -234,7 +247,10 @@ __device__ __forceinline__ Dma make_dma(const TileDesc& t, int w, int lane) {
     const int c = (lane & 7) ^ (4 * e + (lane >> 4));
     d.a[e] = row * (int)t.lda + c * 16;
     d.b[e] = row * (int)t.ldb + c * 16;
+    d.ka[e] = c * 16;
   }
+  d.kb = (lane & 7) * 16;
+  d.kl = __builtin_amdgcn_readfirstlane((int)t.kl);
   d.s = 4 * (64 * w + lane);
   d.rbv = make_rsrc(t.b, (int64_t)t.b_rows * t.ldb);
   d.rbv_none = make_rsrc(t.b, 0);
@@ -257,13 +273,14 @@ template <int P>
 __device__ __forceinline__ void dma_piece(const Dma& d, uint32_t lds, int w, int s, int kp,
                                           bool live) {
   const int koff = kp * kPairK;
+  const int lim = d.kl - koff;  // K bytes of this pair inside the contraction
   if constexpr (P < 8) {
     dma16(live ? d.ra : d.rnone, st_a(lds, s) + (64 * w + 8 * P) * kPairK,
-          d.a[P & 1] + (P >> 1) * d.lda16 + koff);
+          k_mask(d.a[P & 1] + (P >> 1) * d.lda16 + koff, d.ka[P & 1], lim));
   } else if constexpr (P < 16) {
     constexpr int q = P - 8;
     dma16(live ? d.rb : d.rnone, st_b(lds, s) + (64 * w + 8 * q) * kPairK,
-          d.b[q & 1] + (q >> 1) * d.ldb16 + koff);
+          k_mask(d.b[q & 1] + (q >> 1) * d.ldb16 + koff, d.ka[q & 1], lim));
   } else if constexpr (P == 16) {
     dma4(live ? d.rsa : d.rnone, st_sa(lds, s) + 4 * 64 * w, d.s + kp * d.sqa);
   } else {
@@ -277,8 +294,9 @@ __device__ __forceinline__ void dma_piece(const Dma& d, uint32_t lds, int w, int
 // into registers; store_b writes it one K-step later to its swizzled slot.
 template <int Q>
 __device__ __forceinline__ void load_b(const Dma& d, int kp, bool live, v4i (&stage)[kRegPerPair]) {
-  stage[Q] = __builtin_amdgcn_raw_buffer_load_b128(live ? d.rbv : d.rbv_none,
-                                                   d.bl + Q * d.ldb8 + kp * kPairK, 0, 0);
+  stage[Q] = __builtin_amdgcn_raw_buffer_load_b128(
+      live ? d.rbv : d.rbv_none,
+      k_mask(d.bl + Q * d.ldb8 + kp * kPairK, d.kb, d.kl - kp * kPairK), 0, 0);
 }
 
 template <int Q>
@@ -440,7 +458,7 @@ __device__ __forceinline__ void run_tile(uint32_t lds, const TileDesc& t, int ou
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
 
-  const int np = (int)(t.kl / kPairK);  // pairs of K-steps (kl is a multiple of 128)
+  const int np = (int)((t.kl + kPairK - 1) / kPairK);  // pairs of K-steps, the last maybe partial
   if (np > 0) {
     const Dma d = make_dma(t, w, lane);
     const FragOff fo = make_frag_off(wm, wn, r, h);
@@ -555,25 +573,30 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(MxArgs p) {
       const int64_t row0 = sm.off[g] + (int64_t)mt * BM;
       const int64_t n0 = (int64_t)nt * BN;
       col_first = n0;
-      const int64_t nq = p.k / 128;            // scale words per row
+      const int64_t nq = (p.k + 127) / 128;    // scale words per row
       const int64_t brow0 = (int64_t)g * p.n + n0;
       t.a = p.a + row0 * p.k;
-      t.b = p.b + brow0 * p.k;
       t.as = p.as + 4 * row0;                  // A scales: [nq][rows_cap] words
       t.sqa = 4 * p.rows_cap;
       t.as_bytes = nq * t.sqa - 4 * row0;
       if (MODE == 0) {
+        t.b = p.b + brow0 * p.k;
         t.bs = p.bs + 4 * brow0;               // B scales: [nq][G * n] words
         t.sqb = 4 * (int64_t)G * p.n;
         t.bs_bytes = nq * t.sqb - 4 * brow0;
+        t.ldb = p.k;
       } else {
-        // DGRAD: B = the columnwise copy of W, expert g's [n][k] block with its
-        // own [nq][n] scale words at byte g * n * k / 32
-        t.bs = p.bs + (int64_t)g * p.n * p.k / 32 + 4 * n0;
+        // DGRAD: B = the columnwise copy of W, whose experts are padded to
+        // kp = 128 nq tokens: expert g's [n][kp] block at byte g * n * kp with
+        // its own [nq][n] scale words at byte g * n * kp / 32
+        const int64_t kpad = 128 * nq;
+        t.b = p.b + (int64_t)g * p.n * kpad + n0 * kpad;
+        t.bs = p.bs + (int64_t)g * p.n * kpad / 32 + 4 * n0;
         t.sqb = 4 * p.n;
         t.bs_bytes = nq * t.sqb - 4 * n0;
+        t.ldb = kpad;
       }
-      t.lda = t.ldb = p.k;
+      t.lda = p.k;
       const int64_t rv = sm.off[g] + m - row0;
       t.a_rows = (int)(rv < BM ? rv : BM);
       const int64_t cv = p.n - n0;

@@ -222,22 +222,39 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
                                            0x00020000);
 }
 
+// How a row's E4M3 scale words are loaded, from the contraction length k:
+//   kScalePaired  k % 128 == 0: the two words of a step pair, one aligned 8-byte load
+//   kScaleWord    k % 64 == 0: one aligned 4-byte load per step
+//   kScaleHalf    k % 64 == 32: the row stride k / 16 is only 2-aligned and the last
+//                 step is half past k: each thread loads its own two scale bytes
+//                 (2-byte loads), and its raw bytes and scales past k read as zeros
+constexpr int kScalePaired = 0, kScaleWord = 1, kScaleHalf = 2;
+
+// An offset past every descriptor's range: the buffer unit returns zeros.
+constexpr int kOutOfRange = 0x7ffffff0;
+
 // This thread's raw bytes of K-step kt.  Rows past the valid ones, and steps
-// past the last (`live` false), read as zeros.
+// past the last (`live` false), read as zeros; with kScaleHalf so does a
+// half step past the contraction end (the bytes there are the next row's).
+template <int SM>
 __device__ __forceinline__ void load_raw(const TileDesc& t, const Rsrc& rs, int kt, bool live,
                                          int tid, Raw& x) {
-  const int od = ((tid & 127) >> 1) * (int)t.lda + (tid & 1) * 16 + kt * (BK / 2);
+  int od = ((tid & 127) >> 1) * (int)t.lda + (tid & 1) * 16 + kt * (BK / 2);
+  if constexpr (SM == kScaleHalf)
+    if (kt * BK + (tid & 1) * (BK / 2) >= (int)t.kl) od = kOutOfRange;
   const int rstep = 64 * (int)t.lda;
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    x.d[j] = __builtin_amdgcn_raw_buffer_load_b128(live ? rs.d : rs.none, od + j * rstep, 0, 0);
+    x.d[j] = __builtin_amdgcn_raw_buffer_load_b128(live ? rs.d : rs.none,
+                                                   od == kOutOfRange ? od : od + j * rstep, 0, 0);
 }
 
 // The scale words of K-steps kt and kt + 1 (kt even) for this thread's rows;
-// both threads of a row load the same bytes, one request.  With an even step
-// count (PAIRED) a row's two words are one aligned 8-byte load; otherwise
-// each is loaded on its own and a step past the last reads as zero.
-template <bool PAIRED>
+// with kScalePaired / kScaleWord both threads of a row load the same bytes, one
+// request, and a step past the last reads as zero.  With kScaleHalf thread half
+// hf loads only the two bytes it decodes, into bits 16 hf .. 16 hf + 15 of the
+// word (where the decode takes them from).
+template <int SM>
 __device__ __forceinline__ void load_scales(const TileDesc& t, const Rsrc& rs, int kt, int nk,
                                             int tid, Scl& x) {
   const int os = ((tid & 127) >> 1) * (int)t.ldas + kt * (BK / 16);
@@ -245,12 +262,23 @@ __device__ __forceinline__ void load_scales(const TileDesc& t, const Rsrc& rs, i
   const bool l0 = kt < nk, l1 = kt + 1 < nk;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    if constexpr (PAIRED) {
+    if constexpr (SM == kScalePaired) {
       x.s[j] = __builtin_amdgcn_raw_buffer_load_b64(l0 ? rs.s : rs.none, os + j * rstep, 0, 0);
-    } else {
+    } else if constexpr (SM == kScaleWord) {
       x.s[j][0] = __builtin_amdgcn_raw_buffer_load_b32(l0 ? rs.s : rs.none, os + j * rstep, 0, 0);
       x.s[j][1] =
           __builtin_amdgcn_raw_buffer_load_b32(l1 ? rs.s : rs.none, os + j * rstep + 4, 0, 0);
+    } else {
+      const int hf = tid & 1;
+      const int kl = (int)t.kl;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int k0 = (kt + e) * BK + hf * (BK / 2);  // first element of this half step
+        const int off = k0 < kl ? os + 4 * e + 2 * hf + j * rstep : kOutOfRange;
+        const uint32_t v = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(
+            (e ? l1 : l0) ? rs.s : rs.none, off, 0, 0);
+        x.s[j][e] = (int)(v << (16 * hf));
+      }
     }
   }
 }
@@ -316,14 +344,14 @@ __device__ __forceinline__ void mfma(const v8h (&fa)[4], const v8h (&fb)[4], v16
 // an even step (SCALES), the scale words of that step and the next (into sl),
 // read each next substep's fragments, and after the barrier the next step's
 // first fragments.
-template <bool SCALES, bool PAIRED>
+template <bool SCALES, int SM>
 __device__ __forceinline__ void k_step(uint32_t cur, uint32_t nxt, const TileDesc& t,
                                        const Rsrc& rs, int kt, int nk, int tid, const Offs& o,
                                        const Raw& xn, const uint32_t (&sw)[4], Raw& xl, Scl& sl,
                                        v8h (&f0a)[4], v8h (&f0b)[4], v8h (&f1a)[4],
                                        v8h (&f1b)[4], v16f (&acc)[4][4]) {
-  load_raw(t, rs, kt + 2, kt + 2 < nk, tid, xl);
-  if constexpr (SCALES) load_scales<PAIRED>(t, rs, kt + 2, nk, tid, sl);
+  load_raw<SM>(t, rs, kt + 2, kt + 2 < nk, tid, xl);
+  if constexpr (SCALES) load_scales<SM>(t, rs, kt + 2, nk, tid, sl);
   v2h sd[2];
   v4i buf;
   static_for<4>([&](auto sc) {
@@ -360,7 +388,7 @@ __device__ __forceinline__ void k_step(uint32_t cur, uint32_t nxt, const TileDes
 // X^T_g [k, m~_g] (the columnwise copies), dW[g] = (S * a_outer[g, i]) *
 // b_outer[g, j] into out [G, n, k]; every expert has its n x k tiles, an empty
 // one (or one whose padded offsets are not multiples of 128, flagged) zeros.
-template <bool PAIRED, bool WGRAD>
+template <int SM, bool WGRAD>
 __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
   __shared__ Smem sm;
   const int G = p.G;
@@ -466,6 +494,9 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
       sm.aout[tid] = contract && tid < t.a_rows ? aout_t[tid] : 0.0f;
       sm.bout[tid] = contract && tid < t.b_rows ? bout_t[tid] : 0.0f;
     }
+    // the epilogue reads entries other waves wrote; a tile with nothing to
+    // contract reaches it without the K-loop's barriers
+    __syncthreads();
 
     v16f acc[4][4];
 #pragma unroll
@@ -473,16 +504,16 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
 
-    const int nk = (int)(t.kl / BK);   // >= 1 unless nothing to contract
+    const int nk = (int)((t.kl + BK - 1) / BK);  // >= 1 unless nothing to contract
     const int nk2 = (nk + 1) & ~1;     // an odd last step runs on zeros
     if (nk > 0) {
       const Offs o = make_offs(tid, wm, wn, r, h);
       Raw x0, x1;
       Scl sc0, sc1;  // scale words of steps (kt, kt + 1) and (kt + 2, kt + 3)
       v8h f0a[4], f0b[4], f1a[4], f1b[4];
-      load_scales<PAIRED>(t, rs, 0, nk, tid, sc0);
-      load_raw(t, rs, 0, true, tid, x0);
-      load_raw(t, rs, 1, 1 < nk, tid, x1);
+      load_scales<SM>(t, rs, 0, nk, tid, sc0);
+      load_raw<SM>(t, rs, 0, true, tid, x0);
+      load_raw<SM>(t, rs, 1, 1 < nk, tid, x1);
       {
         const uint32_t sw[4] = {(uint32_t)sc0.s[0][0], (uint32_t)sc0.s[1][0],
                                 (uint32_t)sc0.s[2][0], (uint32_t)sc0.s[3][0]};
@@ -493,12 +524,12 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
       for (int kt = 0; kt < nk2; kt += 2) {
         const uint32_t swa[4] = {(uint32_t)sc0.s[0][1], (uint32_t)sc0.s[1][1],
                                  (uint32_t)sc0.s[2][1], (uint32_t)sc0.s[3][1]};
-        k_step<true, PAIRED>(st0, st1, t, rs, kt, nk, tid, o, x1, swa, x0, sc1, f0a, f0b, f1a,
-                             f1b, acc);
+        k_step<true, SM>(st0, st1, t, rs, kt, nk, tid, o, x1, swa, x0, sc1, f0a, f0b, f1a,
+                         f1b, acc);
         const uint32_t swb[4] = {(uint32_t)sc1.s[0][0], (uint32_t)sc1.s[1][0],
                                  (uint32_t)sc1.s[2][0], (uint32_t)sc1.s[3][0]};
-        k_step<false, PAIRED>(st1, st0, t, rs, kt + 1, nk, tid, o, x0, swb, x1, sc1, f0a, f0b,
-                              f1a, f1b, acc);
+        k_step<false, SM>(st1, st0, t, rs, kt + 1, nk, tid, o, x0, swb, x1, sc1, f0a, f0b,
+                          f1a, f1b, acc);
         sc0 = sc1;
       }
     }
@@ -559,7 +590,7 @@ __global__ __launch_bounds__(256) void nv_postscale_kernel(const float* __restri
   __shared__ int64_t s_off[kMaxGroups + 1];
   load_offsets_clamped(offsets, G, rows_cap, s_off, nullptr);
   const int64_t row = blockIdx.x;
-  if (row >= s_off[G]) return;
+  if (row < s_off[0] || row >= s_off[G]) return;  // rows no group owns stay untouched
   int lo = 0, hi = G - 1;  // group: largest g with s_off[g] <= row and a non-empty extent
   while (lo < hi) {
     int mid = (lo + hi + 1) >> 1;
@@ -598,12 +629,15 @@ hipError_t launch_gemm_nvfp4(int G, const uint8_t* a, const uint8_t* a_scales,
   if (bound < grid) grid = bound;
   if (grid > 0) {
     // an even step count keeps each row's scale words of a step pair 8-aligned
-    if ((k / BK) % 2 == 0)
-      hipLaunchKernelGGL((nv_gemm_kernel<true, false>), dim3((unsigned)grid), dim3(kThreads), 0,
-                         stream, p);
+    if (k % (2 * BK) == 0)
+      hipLaunchKernelGGL((nv_gemm_kernel<kScalePaired, false>), dim3((unsigned)grid),
+                         dim3(kThreads), 0, stream, p);
+    else if (k % BK == 0)
+      hipLaunchKernelGGL((nv_gemm_kernel<kScaleWord, false>), dim3((unsigned)grid),
+                         dim3(kThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL((nv_gemm_kernel<false, false>), dim3((unsigned)grid), dim3(kThreads), 0,
-                         stream, p);
+      hipLaunchKernelGGL((nv_gemm_kernel<kScaleHalf, false>), dim3((unsigned)grid),
+                         dim3(kThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -631,8 +665,8 @@ hipError_t launch_gemm_nvfp4_wgrad(int G, const uint8_t* a, const uint8_t* a_sca
   if (bound < grid) grid = bound;
   if (grid <= 0) return hipSuccess;
   // padded token counts are multiples of 128: an even number of 64-deep steps
-  hipLaunchKernelGGL((nv_gemm_kernel<true, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                     p);
+  hipLaunchKernelGGL((nv_gemm_kernel<kScalePaired, true>), dim3((unsigned)grid), dim3(kThreads), 0,
+                     stream, p);
   return hipGetLastError();
 }
 

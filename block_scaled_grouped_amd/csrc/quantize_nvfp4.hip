@@ -15,7 +15,8 @@
 // and saturates by itself.
 //
 // One 256-thread block per live row, each thread holding up to four 16-element
-// blocks in registers (cols <= 16384): the row is read from HBM once.
+// blocks in registers: a row of up to 16384 elements is read from HBM once;
+// longer rows read their remaining blocks a second time, from the L2.
 //
 // The file also holds the per-tensor form (one outer scale per group from the
 // group's amax: a group-amax pass, then the same cast) and the columnwise
@@ -59,10 +60,36 @@ __device__ __forceinline__ uint32_t fp4_pack8(uint4 v, float enc) {
 
 }  // namespace
 
+// Largest bf16 magnitude bits of a 16-element block (two 16-byte halves).
+__device__ __forceinline__ uint32_t block_mag(const uint4& a, const uint4& b) {
+  return max(max(max(mag_bits(a.x), mag_bits(a.y)), max(mag_bits(a.z), mag_bits(a.w))),
+             max(max(mag_bits(b.x), mag_bits(b.y)), max(mag_bits(b.z), mag_bits(b.w))));
+}
+
+// Block j of a row: the E4M3 scale from its largest magnitude bits and the
+// row's (or group's) S, then the 16 E2M1 codes, stored.
+__device__ __forceinline__ void nv_cast_block(const uint4& a, const uint4& b, uint32_t bm, float S,
+                                              uint8_t* __restrict__ drow,
+                                              uint8_t* __restrict__ srow, int64_t j) {
+  const float bmax = bf16_to_f32(bm);
+  float sf = (bmax / 6.0f) * S;
+  sf = __builtin_fminf(sf, 448.0f);
+  const uint32_t s8 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sf, 0.0f, 0, false) & 0xffu;
+  const float sd = e4m3_decode_pos(s8);
+  float enc = 0.0f;
+  if (sd != 0.0f) enc = __builtin_fminf(S / sd, 3.40282346638528859812e+38f);
+  *reinterpret_cast<uint2*>(drow + 8 * j) = make_uint2(fp4_pack8(a, enc), fp4_pack8(b, enc));
+  srow[j] = (uint8_t)s8;
+}
+
 // PER_TENSOR: the row's outer scale comes from its group's amax (computed by
-// nvfp4_group_amax_kernel into group_amax), and no per-row outer scale is
-// written; otherwise the row's own amax is reduced here and amax / 2688 stored.
-template <bool PER_TENSOR>
+// nvfp4_group_amax_kernel into group_amax), no per-row outer scale is written,
+// and a row that no group owns (before offsets[0]) is left untouched;
+// otherwise the row's own amax is reduced here and amax / 2688 stored.
+// LONG: rows of more than kNvMaxBlocksPerThread blocks per thread; the blocks
+// past the first kNvMaxBlocksPerThread * 256 are read again for the cast (the
+// row, at least 64 KiB, is still in the L2 then).
+template <bool PER_TENSOR, bool LONG>
 __global__ __launch_bounds__(kNvThreads) void nvfp4_rowscaled_kernel(
     const uint16_t* __restrict__ x, int64_t rows_cap, int64_t cols, int G,
     const int64_t* __restrict__ offsets, uint8_t* __restrict__ data, uint8_t* __restrict__ bscales,
@@ -79,6 +106,9 @@ __global__ __launch_bounds__(kNvThreads) void nvfp4_rowscaled_kernel(
   const int tid = threadIdx.x;
   const int64_t nblk = cols / 16;
   const uint16_t* xr = x + row * cols;
+  uint8_t* drow = data + row * (cols / 2);
+  uint8_t* srow = bscales + row * nblk;
+  constexpr int64_t kRegBlocks = (int64_t)kNvMaxBlocksPerThread * kNvThreads;
 
   uint4 v[kNvMaxBlocksPerThread][2];
   uint32_t bm[kNvMaxBlocksPerThread];
@@ -95,18 +125,21 @@ __global__ __launch_bounds__(kNvThreads) void nvfp4_rowscaled_kernel(
         v[i][0] = reinterpret_cast<const uint4*>(xr + 16 * j)[0];
         v[i][1] = reinterpret_cast<const uint4*>(xr + 16 * j)[1];
       }
-      bm[i] = max(max(max(mag_bits(v[i][0].x), mag_bits(v[i][0].y)),
-                      max(mag_bits(v[i][0].z), mag_bits(v[i][0].w))),
-                  max(max(mag_bits(v[i][1].x), mag_bits(v[i][1].y)),
-                      max(mag_bits(v[i][1].z), mag_bits(v[i][1].w))));
+      bm[i] = block_mag(v[i][0], v[i][1]);
       am = max(am, bm[i]);
+    }
+  }
+  if constexpr (LONG && !PER_TENSOR) {
+    for (int64_t j = kRegBlocks + tid; j < nblk; j += kNvThreads) {
+      const uint4* p = reinterpret_cast<const uint4*>(xr + 16 * j);
+      am = max(am, block_mag(p[0], p[1]));
     }
   }
   float amax;
   if constexpr (PER_TENSOR) {
     // the row's group amax in one round trip: thread t (G <= 256) loads group
     // t's offsets and amax together and publishes the amax if the row is
-    // group t's (0 if offsets that fail validation place it in none)
+    // group t's; word 1 says whether any group owns the row
     bool mine = false;
     uint32_t val = 0u;
     if (tid < G) {
@@ -114,10 +147,17 @@ __global__ __launch_bounds__(kNvThreads) void nvfp4_rowscaled_kernel(
       val = __float_as_uint(group_amax[tid]);
       mine = lo <= row && row < hi;
     }
-    if (tid == 0) s_wmax[0] = 0u;
+    if (tid == 0) {
+      s_wmax[0] = 0u;
+      s_wmax[1] = 0u;
+    }
     __syncthreads();
-    if (mine) s_wmax[0] = val;
+    if (mine) {
+      s_wmax[0] = val;
+      s_wmax[1] = 1u;
+    }
     __syncthreads();
+    if (s_wmax[1] == 0u) return;  // uniform: no group owns this row
     amax = __uint_as_float(s_wmax[0]);
   } else {
     for (int d = 32; d >= 1; d >>= 1) am = max(am, (uint32_t)__shfl_xor((int)am, d, 64));
@@ -133,20 +173,20 @@ __global__ __launch_bounds__(kNvThreads) void nvfp4_rowscaled_kernel(
 #pragma unroll
   for (int i = 0; i < kNvMaxBlocksPerThread; ++i) {
     const int64_t j = tid + (int64_t)kNvThreads * i;
-    if (j < nblk) {
-      const float bmax = bf16_to_f32(bm[i]);
-      float sf = (bmax / 6.0f) * S;
-      sf = __builtin_fminf(sf, 448.0f);
-      const uint32_t s8 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sf, 0.0f, 0, false) & 0xffu;
-      const float sd = e4m3_decode_pos(s8);
-      float enc = 0.0f;
-      if (sd != 0.0f) enc = __builtin_fminf(S / sd, 3.40282346638528859812e+38f);
-      const uint32_t lo = fp4_pack8(v[i][0], enc);
-      const uint32_t hi = fp4_pack8(v[i][1], enc);
-      *reinterpret_cast<uint2*>(data + row * (cols / 2) + 8 * j) = make_uint2(lo, hi);
-      bscales[row * nblk + j] = (uint8_t)s8;
+    if (j < nblk) nv_cast_block(v[i][0], v[i][1], bm[i], S, drow, srow, j);
+  }
+  if constexpr (LONG) {
+    for (int64_t j = kRegBlocks + tid; j < nblk; j += kNvThreads) {
+      const uint4* p = reinterpret_cast<const uint4*>(xr + 16 * j);
+      const uint4 a = p[0], b = p[1];
+      nv_cast_block(a, b, block_mag(a, b), S, drow, srow, j);
     }
   }
+}
+
+// Rows with more blocks than a thread keeps in registers take the LONG form.
+__host__ __forceinline__ bool nv_long_rows(int64_t cols) {
+  return cols / 16 > (int64_t)kNvMaxBlocksPerThread * kNvThreads;
 }
 
 hipError_t launch_quantize_nvfp4_rowscaled(const uint16_t* x, int64_t rows_cap, int64_t cols,
@@ -154,9 +194,14 @@ hipError_t launch_quantize_nvfp4_rowscaled(const uint16_t* x, int64_t rows_cap, 
                                            uint8_t* block_scales, float* outer, uint32_t* status,
                                            hipStream_t stream) {
   if (rows_cap == 0) return hipSuccess;
-  hipLaunchKernelGGL(nvfp4_rowscaled_kernel<false>, dim3((unsigned)rows_cap), dim3(kNvThreads), 0,
-                     stream, x, rows_cap, cols, G, offsets, data, block_scales, outer, nullptr,
-                     status);
+  if (nv_long_rows(cols))
+    hipLaunchKernelGGL((nvfp4_rowscaled_kernel<false, true>), dim3((unsigned)rows_cap),
+                       dim3(kNvThreads), 0, stream, x, rows_cap, cols, G, offsets, data,
+                       block_scales, outer, nullptr, status);
+  else
+    hipLaunchKernelGGL((nvfp4_rowscaled_kernel<false, false>), dim3((unsigned)rows_cap),
+                       dim3(kNvThreads), 0, stream, x, rows_cap, cols, G, offsets, data,
+                       block_scales, outer, nullptr, status);
   return hipGetLastError();
 }
 
@@ -198,9 +243,11 @@ __global__ __launch_bounds__(kAmaxThreads) void nvfp4_group_amax_kernel(
   for (int g = tid; g < G; g += kAmaxThreads) s_max[g] = 0u;
   load_offsets_clamped(offsets, G, rows_cap, s_off, blockIdx.x == 0 ? status : nullptr);
   const int64_t cpr = cols / 8;  // 16-byte chunks per row
-  const int64_t total = s_off[G] * cpr;
-  const int64_t per = (total + gridDim.x - 1) / gridDim.x;
-  const int64_t c0 = (int64_t)blockIdx.x * per;
+  // the groups' rows: [offsets[0], offsets[G]) (rows before offsets[0] belong to no group)
+  const int64_t first = s_off[0] * cpr, total = s_off[G] * cpr;
+  const int64_t span = total > first ? total - first : 0;
+  const int64_t per = (span + gridDim.x - 1) / gridDim.x;
+  const int64_t c0 = first + (int64_t)blockIdx.x * per;
   const int64_t c1 = c0 + per < total ? c0 + per : total;
   int64_t c = c0 + tid;
   if (c < c1) {
@@ -257,9 +304,14 @@ hipError_t launch_quantize_nvfp4_pertensor(const uint16_t* x, int64_t rows_cap, 
                      x, rows_cap, cols, G, offsets, bits, status);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(nvfp4_rowscaled_kernel<true>, dim3((unsigned)rows_cap), dim3(kNvThreads), 0,
-                     stream, x, rows_cap, cols, G, offsets, data, block_scales, nullptr, amax,
-                     nullptr);
+  if (nv_long_rows(cols))
+    hipLaunchKernelGGL((nvfp4_rowscaled_kernel<true, true>), dim3((unsigned)rows_cap),
+                       dim3(kNvThreads), 0, stream, x, rows_cap, cols, G, offsets, data,
+                       block_scales, nullptr, amax, nullptr);
+  else
+    hipLaunchKernelGGL((nvfp4_rowscaled_kernel<true, false>), dim3((unsigned)rows_cap),
+                       dim3(kNvThreads), 0, stream, x, rows_cap, cols, G, offsets, data,
+                       block_scales, nullptr, amax, nullptr);
   return hipGetLastError();
 }
 

@@ -150,7 +150,7 @@ int grouped_quantize_mxfp8_rowwise_e5m2(const void* x, int64_t rows_cap, int64_t
  * call (rows = sum of N_e): the outer scale then is per output column.
  *
  *   x            [rows_cap, cols] bf16; rows >= offsets[G] are not read.
- *   cols         multiple of 32.
+ *   cols         multiple of 32 (rows of more than 16384 elements are read twice).
  *   data         [rows_cap, cols/2]; element 2j in the low nibble of byte j.
  *   block_scales [rows_cap, cols/16] E4M3, row-major (the GEMM reads this order).
  *   outer        [rows_cap] float32.
@@ -173,15 +173,17 @@ int grouped_quantize_nvfp4_rowscaled(const void* x, int64_t rows_cap, int64_t co
  * scale is 0, capped at FLT_MAX); q = E2M1(x * enc).  Quantize the experts'
  * weights with offsets at the expert boundaries (0, N_0, N_0 + N_1, ...).
  *
- *   x            [rows_cap, cols] bf16; rows >= offsets[G] are not read.
- *   cols         multiple of 32, <= 16384.
+ *   x            [rows_cap, cols] bf16; only rows in [offsets[0], offsets[G]) are
+ *                read.
+ *   cols         multiple of 32 (rows of more than 16384 elements are read twice).
  *   data         [rows_cap, cols/2]; element 2j in the low nibble of byte j.
- *   block_scales [rows_cap, cols/16] E4M3, row-major.
+ *   block_scales [rows_cap, cols/16] E4M3, row-major.  Rows outside
+ *                [offsets[0], offsets[G]) (no group owns them) are untouched.
  *   amax         [G] float32 output: each group's largest magnitude (0 for an
  *                empty group).  Three launches: clear amax, group amax (atomic
  *                max per group), cast.
- * Errors: BSG_ERR_NULL, BSG_ERR_SHAPE, BSG_ERR_UNSUPPORTED (cols > 16384),
- * BSG_ERR_ALIGN (x and data 16-byte, amax 4-byte).
+ * Errors: BSG_ERR_NULL, BSG_ERR_SHAPE, BSG_ERR_ALIGN (x and data 16-byte, amax
+ * 4-byte).
  */
 int grouped_quantize_nvfp4_pertensor(const void* x, int64_t rows_cap, int64_t cols, int64_t G,
                                      const int64_t* offsets, uint8_t* data, uint8_t* block_scales,
@@ -200,7 +202,7 @@ int grouped_quantize_nvfp4_pertensor(const void* x, int64_t rows_cap, int64_t co
  * scale, each token an E2M1 code.
  *
  *   x              [rows_cap, cols] bf16; rows >= offsets[G] are not read.
- *   cols           multiple of 32, <= 16384.
+ *   cols           multiple of 32.
  *   offsets        [G+1] int64 live token offsets (group_offsets_i32_to_i64, pad 1).
  *   padded_offsets [G+1] int64 (group_offsets_i32_to_i64 with pad_to 128);
  *                  a group whose padded offsets are not multiples of 128 or
@@ -212,8 +214,8 @@ int grouped_quantize_nvfp4_pertensor(const void* x, int64_t rows_cap, int64_t co
  *   block_scales   expert g: a [cols, m~_g / 16] E4M3 block at byte
  *                  padded_offsets[g] * cols / 16 (padding blocks 0x00).
  *   outer          [G, cols] float32 (0 for an empty expert).
- * Errors: BSG_ERR_NULL, BSG_ERR_SHAPE, BSG_ERR_UNSUPPORTED (cols > 16384),
- * BSG_ERR_ALIGN (x and data 16-byte, outer 4-byte).
+ * Errors: BSG_ERR_NULL, BSG_ERR_SHAPE, BSG_ERR_ALIGN (x and data 16-byte, outer
+ * 4-byte).
  */
 int grouped_quantize_nvfp4_rowscaled_colwise(const void* x, int64_t rows_cap, int64_t cols,
                                              int64_t G, const int64_t* offsets,
@@ -231,8 +233,8 @@ int grouped_quantize_nvfp4_rowscaled_colwise(const void* x, int64_t rows_cap, in
  *
  * mode BSG_FPROP_TN (ragged rows; output rows follow the lhs groups):
  *   Y[r, n] = sum_k A[r, k] * B[g, n, k]   for r in [offsets[g], offsets[g+1])
- *   a        [rows_cap, k] E4M3 rowwise,  a_scales [k/128][rows_cap] words
- *   b        [G, n, k] E4M3 rowwise,      b_scales [k/128][G * n] words (the weights
+ *   a        [rows_cap, k] E4M3 rowwise,  a_scales [ceil(k/128)][rows_cap] words
+ *   b        [G, n, k] E4M3 rowwise,      b_scales [ceil(k/128)][G * n] words (the weights
  *            quantized by grouped_quantize_mxfp8 as G * n rows)
  *   offsets  [G+1] live row offsets; rows_cap = rows of a and out
  *   out      [rows_cap, n]; rows >= offsets[G] untouched.
@@ -247,14 +249,20 @@ int grouped_quantize_nvfp4_rowscaled_colwise(const void* x, int64_t rows_cap, in
  * weights, a pairing "gemm.py" _compatible_fp8_gemm_dtypes accepts):
  *   dX[r, j] = sum_i dY[r, i] * W[g, i, j]   for r in [offsets[g], offsets[g+1])
  *   a        [rows_cap, k] E5M2 rowwise dY (grouped_quantize_mxfp8_rowwise_e5m2,
- *            cols = k, the contraction), a_scales [k/128][rows_cap] words
+ *            cols = k, the contraction), a_scales [ceil(k/128)][rows_cap] words
  *   b        the columnwise copy of the weights W [G, k, n] viewed as G * k rows
- *            of n columns (grouped_quantize_mxfp8 col_data with padded offsets
- *            g * k): expert g's [n, k] block, i.e. W_g transposed, quantized
- *            along k; b_scales its col_scales ([k/128][n] words per expert)
+ *            of n columns (grouped_quantize_mxfp8 col_data with offsets g * k and
+ *            padded offsets g * kp, kp = k rounded up to a multiple of 128):
+ *            expert g's [n, kp] block at byte g * n * kp, i.e. W_g transposed,
+ *            quantized along k, zero past k; b_scales its col_scales ([kp/128][n]
+ *            words per expert, at byte g * n * kp / 32)
  *   offsets, rows_cap, out as in FPROP (out [rows_cap, n]).
- * k must be a multiple of 128 (FPROP, DGRAD); n >= 1.  out_dtype: BSG_OUT_BF16
- * (round to nearest even) or BSG_OUT_F32.
+ * k: any positive multiple of 32 (FPROP, DGRAD; "gemm.py",
+ * assert_cublas_requirements asks only for the block multiple).  No data byte
+ * past k in a row is read; the scale bytes of the last word past k/32 multiply
+ * zeros there and may hold any value but 0xFF (grouped_quantize_mxfp8 writes
+ * 0x00).  n >= 1.  out_dtype: BSG_OUT_BF16 (round to nearest even) or
+ * BSG_OUT_F32.
  */
 int grouped_gemm_mxfp8(int mode, int64_t G, const uint8_t* a, const uint8_t* a_scales,
                        const uint8_t* b, const uint8_t* b_scales, const int64_t* offsets,
@@ -306,8 +314,11 @@ int grouped_gemm_mxfp8_ex(int mode, int64_t G, const uint8_t* a, const uint8_t* 
  *   scratch               NULL: the outer scales are applied in the GEMM's
  *                         epilogue.  Otherwise a [rows_cap, ld_out] float32 buffer:
  *                         S is stored there first and a second kernel applies the
- *                         outer scales into out (the pages' two-step flow).
- * k must be a positive multiple of 64 (one MFMA K-step).
+ *                         outer scales into out (the pages' two-step flow); rows
+ *                         outside [offsets[0], offsets[G]) stay untouched.
+ * k: any positive multiple of 32 ("gemm.py", assert_cublas_requirements: the
+ * contracting dim of an NVFP4 GEMM needs only that multiple); no byte past k
+ * of a row (data or block scales) is read.
  */
 int grouped_gemm_nvfp4_rowscaled(int64_t G, const uint8_t* a, const uint8_t* a_scales,
                                  const float* a_outer, const int64_t* offsets, int64_t rows_cap,
@@ -334,7 +345,7 @@ int grouped_gemm_nvfp4_rowscaled(int64_t G, const uint8_t* a, const uint8_t* a_s
  *   n_per_group          [host] [G] int64 output width of each group, >= 0
  *   out                  [rows_cap, ld_out]; ld_out >= max N_g.  Columns >= N_g of
  *                        group g's rows and rows >= offsets[G] are untouched.
- * k must be a positive multiple of 64.  Errors as grouped_gemm_nvfp4_rowscaled.
+ * k: any positive multiple of 32.  Errors as grouped_gemm_nvfp4_rowscaled.
  */
 int grouped_gemm_nvfp4_pertensor(int64_t G, const uint8_t* a, const uint8_t* a_scales,
                                  const float* a_amax, const int64_t* offsets, int64_t rows_cap,

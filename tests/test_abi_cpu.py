@@ -67,12 +67,13 @@ def test_quantize_validation(lib):
     n = lib.grouped_quantize_nvfp4_rowscaled
     assert n(p, 128, 128, 4, p, p, p, None, None, None) == 1
     assert n(p, 128, 48, 4, p, p, p, p, None, None) == 2
-    assert n(p, 128, 32768, 4, p, p, p, p, None, None) == 4
+    assert n(p, 128, 0, 4, p, p, p, p, None, None) == 2
+    assert n(p, -1, 128, 4, p, p, p, p, None, None) == 2
     t = lib.grouped_quantize_nvfp4_pertensor
     assert t(p, 128, 128, 4, p, p, p, None, None, None) == 1                        # amax
     assert t(p, 128, 48, 4, p, p, p, p, None, None) == 2
     assert t(p, 128, 128, 0, p, p, p, p, None, None) == 2
-    assert t(p, 128, 32768, 4, p, p, p, p, None, None) == 4
+    assert t(p, 128, 16400, 4, p, p, p, p, None, None) == 2                      # cols % 32
     assert t(p, 128, 128, 4, p, mis, p, p, None, None) == 3
 
 
@@ -82,18 +83,21 @@ def test_gemm_validation(lib):
     assert g(0, 4, None, p, p, p, p, 128, 128, 128, p, 0, None, None) == 1
     assert g(7, 4, p, p, p, p, p, 128, 128, 128, p, 0, None, None) == 4
     assert g(0, 4, p, p, p, p, p, 128, 128, 128, p, 9, None, None) == 4
-    assert g(0, 4, p, p, p, p, p, 128, 128, 96, p, 0, None, None) == 2             # fprop k % 128
+    assert g(0, 4, p, p, p, p, p, 128, 128, 100, p, 0, None, None) == 2            # fprop k % 32
+    assert g(2, 4, p, p, p, p, p, 128, 128, 48, p, 0, None, None) == 2             # dgrad k % 32
+    assert g(0, 4, p, p, p, p, p, 128, 128, 0, p, 0, None, None) == 2
     assert g(1, 4, p, p, p, p, p, 128, 100, 128, p, 0, None, None) == 2            # wgrad n % 32
     assert g(0, 300, p, p, p, p, p, 128, 128, 128, p, 0, None, None) == 2
     nv = lib.grouped_gemm_nvfp4_rowscaled
     npg = (ctypes.c_int64 * 2)(64, 128)
     hp = ctypes.cast(npg, ctypes.c_void_p)
     assert nv(2, p, p, p, p, 64, 128, p, p, p, None, p, 128, 0, None, None, None) == 1
-    assert nv(2, p, p, p, p, 64, 96, p, p, p, hp, p, 128, 0, None, None, None) == 2   # k % 64
+    assert nv(2, p, p, p, p, 64, 48, p, p, p, hp, p, 128, 0, None, None, None) == 2   # k % 32
+    assert nv(2, p, p, p, p, 64, 0, p, p, p, hp, p, 128, 0, None, None, None) == 2
     assert nv(2, p, p, p, p, 64, 128, p, p, p, hp, p, 100, 0, None, None, None) == 2  # ld_out
     pt = lib.grouped_gemm_nvfp4_pertensor
     assert pt(2, p, p, None, p, 64, 128, p, p, p, hp, p, 128, 0, None, None) == 1
-    assert pt(2, p, p, p, p, 64, 96, p, p, p, hp, p, 128, 0, None, None) == 2       # k % 64
+    assert pt(2, p, p, p, p, 64, 80, p, p, p, hp, p, 128, 0, None, None) == 2       # k % 32
     assert pt(2, p, p, p, p, 64, 128, p, p, p, hp, p, 100, 0, None, None) == 2      # ld_out
     assert pt(2, p, p, p, p, 64, 128, p, p, p, hp, p, 128, 5, None, None) == 4      # out_dtype
     neg = (ctypes.c_int64 * 2)(64, -1)

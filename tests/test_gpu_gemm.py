@@ -132,9 +132,12 @@ def test_fprop_end_to_end_tiny_config():
     qa = bsg.grouped_quantize_mxfp8(t["x"], doff)
     woff = to_dev(np.array([0, G * N]))
     qb = bsg.grouped_quantize_mxfp8(t["w"].view(G * N, K), woff)
-    y = bsg.grouped_gemm_mxfp8(bsg.BSG_FPROP_TN, qa["row_data"], qa["row_scales"], qb["row_data"],
-                               qb["row_scales"], doff, w.rows_cap, N, K, out_dtype=bsg.BSG_OUT_F32)
-    y = host(y).astype(np.float64)
+    out = torch.full((w.rows_cap, N), float("nan"), dtype=torch.float32, device=device())
+    bsg.grouped_gemm_mxfp8(bsg.BSG_FPROP_TN, qa["row_data"], qa["row_scales"], qb["row_data"],
+                           qb["row_scales"], doff, w.rows_cap, N, K, out=out,
+                           out_dtype=bsg.BSG_OUT_F32)
+    y = host(out).astype(np.float64)
+    assert np.all(np.isnan(y[int(off[-1]):])), "capacity rows must stay untouched"
     for g in range(G):
         gemm_tolerance_check(y[off[g]:off[g + 1]], ref[off[g]:off[g + 1]], True, "group %d" % g)
 
@@ -301,9 +304,11 @@ def test_nvfp4_end_to_end():
     doff = to_dev(off)
     a = bsg.grouped_quantize_nvfp4_rowscaled(bf16_dev(xb), doff)
     b = bsg.grouped_quantize_nvfp4_rowscaled(bf16_dev(wb), to_dev(np.array([0, sum(npg)])))
-    y = bsg.grouped_gemm_nvfp4_rowscaled(a[0], a[1], a[2], doff, K, b[0], b[1], b[2], npg,
-                                         out_dtype=bsg.BSG_OUT_F32)
-    y = host(y).astype(np.float64)
+    out = torch.full((rows_cap, max(npg)), float("nan"), dtype=torch.float32, device=device())
+    bsg.grouped_gemm_nvfp4_rowscaled(a[0], a[1], a[2], doff, K, b[0], b[1], b[2], npg, out=out,
+                                     out_dtype=bsg.BSG_OUT_F32)
+    y = host(out).astype(np.float64)
+    assert np.all(np.isnan(y[int(off[-1]):])), "capacity rows must stay untouched"
     ap, asc, at = Q.nvfp4_rowscaled(xb, off)
     bp, bsc, bt = Q.nvfp4_rowscaled(wb, np.array([0, sum(npg)]))
     for g, (rows, r) in enumerate(GM.nvfp4_rowscaled_fprop(ap, asc, at, off, bp, bsc, bt, npg, K)):
@@ -369,9 +374,11 @@ def test_nvfp4_pertensor_end_to_end():
     doff = to_dev(off)
     a = bsg.grouped_quantize_nvfp4_pertensor(bf16_dev(xb), doff)
     b = bsg.grouped_quantize_nvfp4_pertensor(bf16_dev(wb), to_dev(boff))
-    y = bsg.grouped_gemm_nvfp4_pertensor(a[0], a[1], a[2], doff, K, b[0], b[1], b[2], npg,
-                                         out_dtype=bsg.BSG_OUT_F32)
-    y = host(y).astype(np.float64)
+    out = torch.full((rows_cap, max(npg)), float("nan"), dtype=torch.float32, device=device())
+    bsg.grouped_gemm_nvfp4_pertensor(a[0], a[1], a[2], doff, K, b[0], b[1], b[2], npg, out=out,
+                                     out_dtype=bsg.BSG_OUT_F32)
+    y = host(out).astype(np.float64)
+    assert np.all(np.isnan(y[int(off[-1]):])), "capacity rows must stay untouched"
     ap, asc, aam = Q.nvfp4_pertensor(xb, off)
     bp, bsc, bam = Q.nvfp4_pertensor(wb, boff)
     for g, (rows, r) in enumerate(GM.nvfp4_pertensor_fprop(ap, asc, aam, off, bp, bsc, bam, npg, K)):

@@ -204,6 +204,8 @@ NV_CASES = [
     (64, 160, [17, 0, 30]),
     (40, 16384, [33]),
     (128, 128, [32, 0, 64, 32]),
+    (12, 16416, [3, 0, 5]),              # longer than a thread's registers hold: read twice
+    (6, 32768, [4]),
 ]
 
 
@@ -238,6 +240,8 @@ NVT_CASES = [
     (300, 96, [0, 5, 0, 250, 1]),          # leading empty group, a one-row group
     (16, 32, [0]),                         # empty routing: only the amax is written (0)
     (3000, 64, [i % 23 for i in range(256)]),   # 256 groups (the maximum), empty ones among them
+    (12, 16416, [3, 0, 5]),                # rows read twice by the cast
+    (7, 32768, [2, 3]),
 ]
 
 
@@ -282,6 +286,8 @@ NVCOL_CASES = [
     (800, 4096, [449, 0, 301, 0, 50]),
     (300, 160, [257, 1]),                # three 128-token tiles, a one-token expert
     (64, 32, [0, 0, 64]),                # leading empty experts
+    (12, 16416, [3, 0, 5]),              # more than 16384 columns
+    (5, 32768, [4]),
 ]
 
 
