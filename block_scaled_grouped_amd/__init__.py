@@ -30,7 +30,9 @@ EXPORTS = ("bsg_last_error", "bsg_version", "group_offsets_i32_to_i64", "grouped
            "grouped_quantize_nvfp4_rowscaled", "grouped_quantize_nvfp4_rowscaled_colwise",
            "grouped_quantize_nvfp4_pertensor",
            "grouped_gemm_mxfp8", "grouped_gemm_mxfp8_ex", "grouped_gemm_nvfp4_rowscaled",
-           "grouped_gemm_nvfp4_rowscaled_wgrad", "grouped_gemm_nvfp4_pertensor")
+           "grouped_gemm_nvfp4_rowscaled_wgrad", "grouped_gemm_nvfp4_pertensor",
+           "grouped_gemm_nvfp4_rowscaled_noalloc")
+BSG_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -79,6 +81,9 @@ def load_library(path=LIB_PATH):
     lib.grouped_gemm_nvfp4_pertensor.restype = I32
     lib.grouped_gemm_nvfp4_pertensor.argtypes = [I64, P, P, P, P, I64, I64, P, P, P, P, P, I64, I32,
                                                  P, P]
+    lib.grouped_gemm_nvfp4_rowscaled_noalloc.restype = I32
+    lib.grouped_gemm_nvfp4_rowscaled_noalloc.argtypes = [I64, P, P, P, P, I64, I64, P, P, P, P, P,
+                                                         I64, I32, P, P]
     lib.grouped_gemm_nvfp4_rowscaled_wgrad.restype = I32
     lib.grouped_gemm_nvfp4_rowscaled_wgrad.argtypes = [I64, P, P, P, P, P, P, P, I64, I64, I64, P,
                                                        I32, P, P]
@@ -440,6 +445,32 @@ def grouped_gemm_nvfp4_rowscaled(a, a_scales, a_outer, offsets, k, b, b_scales, 
                                             _ptr(b_outer), ctypes.cast(host_n, ctypes.c_void_p),
                                             _ptr(out), ld_out, out_dtype, _ptr(scratch),
                                             _ptr(status), _stream(a)))
+    return out
+
+
+def grouped_gemm_nvfp4_rowscaled_noalloc(a, a_scales, a_outer, offsets, k, b, b_scales, b_outer,
+                                         n_per_group, out, ld_out=None, out_dtype=BSG_OUT_BF16,
+                                         G=None, status=None):
+    """grouped_gemm_nvfp4_rowscaled's two-step (FP32 S) flow with S in the
+    library's static device scratch: allocates nothing, so `out` is required.
+    rows_cap * ld_out * 4 must fit BSG_NOALLOC_SCRATCH_BYTES; calls that overlap
+    on one GPU race.  See include/bsg.h."""
+    lib = load_library()
+    _need_cuda(a, a_scales, a_outer, offsets, b, b_scales, b_outer, out)
+    rows_cap = a.shape[0]
+    G = offsets.numel() - 1 if G is None else G
+    npg = [int(v) for v in n_per_group]
+    if len(npg) != G:
+        raise ValueError("n_per_group needs G entries")
+    if ld_out is None:
+        ld_out = out.shape[1]
+    _nv_gemm_check(G, a, a_scales, a_outer, offsets, rows_cap, k, b, b_scales, b_outer, npg, out,
+                   ld_out, out_dtype, status, per_tensor=False)
+    host_n = (ctypes.c_int64 * G)(*npg)
+    _check(lib.grouped_gemm_nvfp4_rowscaled_noalloc(
+        G, _ptr(a), _ptr(a_scales), _ptr(a_outer), _ptr(offsets), rows_cap, k, _ptr(b),
+        _ptr(b_scales), _ptr(b_outer), ctypes.cast(host_n, ctypes.c_void_p), _ptr(out), ld_out,
+        out_dtype, _ptr(status), _stream(a)))
     return out
 
 

@@ -252,7 +252,7 @@ static int gemm_nvfp4_impl(const char* fn, bool per_tensor, int64_t G, const uin
                            int64_t rows_cap, int64_t k, const uint8_t* b, const uint8_t* b_scales,
                            const float* b_outer, const int64_t* n_per_group, void* out,
                            int64_t ld_out, int out_dtype, float* scratch, uint32_t* dev_status,
-                           void* stream) {
+                           void* stream, bool noalloc = false) {
   if (a == nullptr || a_scales == nullptr || a_outer == nullptr || offsets == nullptr || b == nullptr ||
       b_scales == nullptr || b_outer == nullptr || n_per_group == nullptr || out == nullptr)
     return fail(BSG_ERR_NULL, "%s: operands, scales, offsets, n_per_group and out must be non-NULL", fn);
@@ -279,12 +279,24 @@ static int gemm_nvfp4_impl(const char* fn, bool per_tensor, int64_t G, const uin
   if (ld_out < max_n || ld_out < 1)
     return fail(BSG_ERR_SHAPE, "%s: ld_out=%lld below the widest group (%lld)", fn, (long long)ld_out,
                 (long long)max_n);
-  const int64_t esz = (out_dtype == BSG_OUT_F32 || scratch != nullptr) ? 4 : 2;
+  if (noalloc && rows_cap * ld_out > (int64_t)(bsg::kNoAllocScratchBytes / sizeof(float)))
+    return fail(BSG_ERR_SHAPE,
+                "%s: rows_cap * ld_out * 4 = %lld bytes exceeds the library's %lld-byte static "
+                "scratch; use grouped_gemm_nvfp4_rowscaled with a caller scratch",
+                fn, (long long)(rows_cap * ld_out * 4), (long long)bsg::kNoAllocScratchBytes);
+  const int64_t esz = (out_dtype == BSG_OUT_F32 || scratch != nullptr || noalloc) ? 4 : 2;
   if (256 * (k / 2) >= kMaxTileBytes || 256 * ld_out * esz >= kMaxTileBytes)
     return fail(BSG_ERR_SHAPE, "%s: k or ld_out too large for 32-bit tile offsets", fn);
   if (!aligned16(a) || !aligned16(b) || !aligned4(a_scales) || !aligned4(b_scales) || !aligned4(out) ||
       (scratch != nullptr && !aligned4(scratch)))
     return fail(BSG_ERR_ALIGN, "%s: a and b must be 16-byte aligned; scales, out and scratch 4-byte", fn);
+  if (noalloc)
+    return hip_result(bsg::launch_gemm_nvfp4_noalloc((int)G, a, a_scales, a_outer, offsets,
+                                                     rows_cap, k, b, b_scales, b_outer, tab,
+                                                     (int)max_n, out, ld_out,
+                                                     out_dtype == BSG_OUT_F32, dev_status,
+                                                     (hipStream_t)stream),
+                      fn);
   return hip_result(bsg::launch_gemm_nvfp4((int)G, a, a_scales, a_outer, offsets, rows_cap, k, b,
                                            b_scales, b_outer, tab, (int)max_n, out, ld_out,
                                            out_dtype == BSG_OUT_F32, scratch, dev_status,
@@ -301,6 +313,17 @@ int grouped_gemm_nvfp4_rowscaled(int64_t G, const uint8_t* a, const uint8_t* a_s
   return gemm_nvfp4_impl("grouped_gemm_nvfp4_rowscaled", false, G, a, a_scales, a_outer, offsets,
                          rows_cap, k, b, b_scales, b_outer, n_per_group, out, ld_out, out_dtype,
                          scratch, dev_status, stream);
+}
+
+int grouped_gemm_nvfp4_rowscaled_noalloc(int64_t G, const uint8_t* a, const uint8_t* a_scales,
+                                         const float* a_outer, const int64_t* offsets,
+                                         int64_t rows_cap, int64_t k, const uint8_t* b,
+                                         const uint8_t* b_scales, const float* b_outer,
+                                         const int64_t* n_per_group, void* out, int64_t ld_out,
+                                         int out_dtype, uint32_t* dev_status, void* stream) {
+  return gemm_nvfp4_impl("grouped_gemm_nvfp4_rowscaled_noalloc", false, G, a, a_scales, a_outer,
+                         offsets, rows_cap, k, b, b_scales, b_outer, n_per_group, out, ld_out,
+                         out_dtype, nullptr, dev_status, stream, true);
 }
 
 int grouped_gemm_nvfp4_pertensor(int64_t G, const uint8_t* a, const uint8_t* a_scales,

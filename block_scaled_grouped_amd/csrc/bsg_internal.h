@@ -200,8 +200,22 @@ hipError_t launch_gemm_nvfp4(int G, const uint8_t* a, const uint8_t* a_scales,
                              const float* a_outer, const int64_t* offsets, int64_t rows_cap,
                              int64_t k, const uint8_t* b, const uint8_t* b_scales,
                              const float* b_outer, const NvGroupTable& table, int max_n,
-                             void* out, int64_t ld_out, int out_f32, float* scratch,
+                             void* out, int64_t ld_out, int out_f32, float* s_buf,
                              uint32_t* status, hipStream_t stream, bool per_tensor = false);
+
+// The FP32 S of grouped_gemm_nvfp4_rowscaled_noalloc lives in a static device
+// array of this many bytes (per GPU).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+
+hipError_t noalloc_scratch_ptr(float** ptr);
+
+hipError_t launch_gemm_nvfp4_noalloc(int G, const uint8_t* a, const uint8_t* a_scales,
+                                     const float* a_outer, const int64_t* offsets,
+                                     int64_t rows_cap, int64_t k, const uint8_t* b,
+                                     const uint8_t* b_scales, const float* b_outer,
+                                     const NvGroupTable& table, int max_n, void* out,
+                                     int64_t ld_out, int out_f32, uint32_t* status,
+                                     hipStream_t stream);
 
 hipError_t launch_gemm_nvfp4_wgrad(int G, const uint8_t* a, const uint8_t* a_scales,
                                    const float* a_outer, const uint8_t* b, const uint8_t* b_scales,

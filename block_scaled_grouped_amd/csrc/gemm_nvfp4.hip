@@ -80,7 +80,7 @@ struct NvArgs {
   const float* bout;
   void* out;
   int64_t ld_out;
-  float* scratch;
+  float* s_buf;            // FP32 S of the two-step flow, or null (fused epilogue)
   uint32_t* status;
   int G;
   int out_f32;
@@ -535,10 +535,10 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
     }
 
     // epilogue: S -> (S * a_outer) * b_outer, or S itself into the scratch
-    const bool fused = p.scratch == nullptr;
+    const bool fused = p.s_buf == nullptr;
     const bool f32out = !fused || p.out_f32;
     const int esz = f32out ? 4 : 2;
-    char* obase = fused ? reinterpret_cast<char*>(p.out) : reinterpret_cast<char*>(p.scratch);
+    char* obase = fused ? reinterpret_cast<char*>(p.out) : reinterpret_cast<char*>(p.s_buf);
     obase += out_off * esz;
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(obase, (int64_t)t.a_rows * ld_out * esz);
     int ldc = (int)ld_out;
@@ -580,7 +580,7 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
 
 // Unfused second step: Y[r, n] = (S[r, n] * a_outer[r]) * b_outer_g[n] for the
 // live rows r of group g and n < N_g, one block per row.
-__global__ __launch_bounds__(256) void nv_postscale_kernel(const float* __restrict__ scratch,
+__global__ __launch_bounds__(256) void nv_postscale_kernel(const float* __restrict__ s_buf,
                                                            const float* __restrict__ aout,
                                                            const float* __restrict__ bout,
                                                            const int64_t* __restrict__ offsets,
@@ -601,7 +601,7 @@ __global__ __launch_bounds__(256) void nv_postscale_kernel(const float* __restri
   const float ao = aout[row];
   const float* bo = bout + tab.brow[g];
   for (int n = threadIdx.x; n < ng; n += blockDim.x) {
-    const float y = (scratch[row * ld_out + n] * ao) * bo[n];
+    const float y = (s_buf[row * ld_out + n] * ao) * bo[n];
     if (out_f32)
       reinterpret_cast<float*>(out)[row * ld_out + n] = y;
     else
@@ -615,15 +615,15 @@ hipError_t launch_gemm_nvfp4(int G, const uint8_t* a, const uint8_t* a_scales,
                              const float* a_outer, const int64_t* offsets, int64_t rows_cap,
                              int64_t k, const uint8_t* b, const uint8_t* b_scales,
                              const float* b_outer, const NvGroupTable& table, int max_n,
-                             void* out, int64_t ld_out, int out_f32, float* scratch,
+                             void* out, int64_t ld_out, int out_f32, float* s_buf,
                              uint32_t* status, hipStream_t stream, bool per_tensor) {
   NvArgs p;
   p.a = a; p.as = a_scales; p.aout = a_outer; p.offsets = offsets; p.rows_cap = rows_cap; p.k = k;
   p.n = 0;
-  p.b = b; p.bs = b_scales; p.bout = b_outer; p.out = out; p.ld_out = ld_out; p.scratch = scratch;
+  p.b = b; p.bs = b_scales; p.bout = b_outer; p.out = out; p.ld_out = ld_out; p.s_buf = s_buf;
   p.status = status; p.G = G; p.out_f32 = out_f32; p.per_tensor = per_tensor ? 1 : 0;
   p.tab = table;
-  if (per_tensor && scratch != nullptr) return hipErrorInvalidValue;
+  if (per_tensor && s_buf != nullptr) return hipErrorInvalidValue;
   const int64_t bound = ((rows_cap + BM - 1) / BM + G) * ((max_n + BN - 1) / BN);
   int64_t grid = device_cu_count();
   if (bound < grid) grid = bound;
@@ -641,13 +641,64 @@ hipError_t launch_gemm_nvfp4(int G, const uint8_t* a, const uint8_t* a_scales,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (scratch != nullptr && rows_cap > 0) {
+  if (s_buf != nullptr && rows_cap > 0) {
     hipLaunchKernelGGL(nv_postscale_kernel, dim3((unsigned)rows_cap), dim3(256), 0, stream,
-                       scratch, a_outer, b_outer, offsets, rows_cap, G, out, ld_out, out_f32,
+                       s_buf, a_outer, b_outer, offsets, rows_cap, G, out, ld_out, out_f32,
                        table);
     return hipGetLastError();
   }
   return hipSuccess;
+}
+
+// ---------------------------------------------------------------- no-allocation form
+//
+// The two-step flow above with its FP32 S in a library-owned device array, for
+// callers that cannot allocate (code under HIP-graph capture, serving loops,
+// harnesses that forbid allocation).  Each GPU holds its own copy of the array
+// until the process ends; every call on a GPU shares it, so calls that overlap
+// on one GPU race.  The GEMM writes S for every (live row, column < N_g) before
+// the post-scale kernel reads exactly those entries, so nothing needs clearing.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+float* g_scratch_ptr[kMaxDevices] = {};  // the array's device address on each GPU
+}  // namespace
+
+// The array's address on the current device, looked up once per device (with
+// that device current); the host-side name `scratch` is not a device address.
+hipError_t noalloc_scratch_ptr(float** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  float* p = __atomic_load_n(&g_scratch_ptr[dev], __ATOMIC_ACQUIRE);
+  if (p == nullptr) {
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (addr == nullptr) return hipErrorInvalidSymbol;
+    p = static_cast<float*>(addr);
+    __atomic_store_n(&g_scratch_ptr[dev], p, __ATOMIC_RELEASE);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
+
+hipError_t launch_gemm_nvfp4_noalloc(int G, const uint8_t* a, const uint8_t* a_scales,
+                                     const float* a_outer, const int64_t* offsets,
+                                     int64_t rows_cap, int64_t k, const uint8_t* b,
+                                     const uint8_t* b_scales, const float* b_outer,
+                                     const NvGroupTable& table, int max_n, void* out,
+                                     int64_t ld_out, int out_f32, uint32_t* status,
+                                     hipStream_t stream) {
+  if (rows_cap * ld_out > (int64_t)(kNoAllocScratchBytes / sizeof(float)))
+    return hipErrorInvalidValue;  // the C-ABI layer rejects this size first
+  float* ptr = nullptr;
+  const hipError_t e = noalloc_scratch_ptr(&ptr);
+  if (e != hipSuccess) return e;
+  return launch_gemm_nvfp4(G, a, a_scales, a_outer, offsets, rows_cap, k, b, b_scales, b_outer,
+                           table, max_n, out, ld_out, out_f32, ptr, status, stream, false);
 }
 
 hipError_t launch_gemm_nvfp4_wgrad(int G, const uint8_t* a, const uint8_t* a_scales,
@@ -658,7 +709,7 @@ hipError_t launch_gemm_nvfp4_wgrad(int G, const uint8_t* a, const uint8_t* a_sca
   NvArgs p;
   p.a = a; p.as = a_scales; p.aout = a_outer; p.offsets = padded_offsets;
   p.rows_cap = col_rows_cap; p.k = k; p.n = n;
-  p.b = b; p.bs = b_scales; p.bout = b_outer; p.out = out; p.ld_out = k; p.scratch = nullptr;
+  p.b = b; p.bs = b_scales; p.bout = b_outer; p.out = out; p.ld_out = k; p.s_buf = nullptr;
   p.status = status; p.G = G; p.out_f32 = out_f32; p.per_tensor = 0; p.tab = NvGroupTable{};
   const int64_t bound = (int64_t)G * ((n + BM - 1) / BM) * ((k + BN - 1) / BN);
   int64_t grid = device_cu_count();

@@ -328,6 +328,33 @@ int grouped_gemm_nvfp4_rowscaled(int64_t G, const uint8_t* a, const uint8_t* a_s
                                  uint32_t* dev_status, void* stream);
 
 /*
+ * grouped_gemm_nvfp4_rowscaled_noalloc
+ *
+ * For callers that cannot allocate device memory -- code under HIP-graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: the two-step
+ * flow of grouped_gemm_nvfp4_rowscaled (FP32 S first, then a post-scale kernel
+ * applies the outer scales) with S in a static device array that the library
+ * owns, instead of a caller scratch.  Arguments, results and errors are those
+ * of grouped_gemm_nvfp4_rowscaled with a non-NULL scratch; the outputs are
+ * bit-identical to it.
+ *   Limit: rows_cap * ld_out * 4 <= BSG_NOALLOC_SCRATCH_BYTES (64 MiB), else
+ *   BSG_ERR_SHAPE and nothing is enqueued.
+ * Each GPU the library runs on holds its own copy of the array until the
+ * process ends; its device address is looked up on the first call on that
+ * GPU (with it current).  Every call on one GPU shares the array: calls that
+ * overlap on one GPU (concurrent streams, or threads) race and must be
+ * serialized by the caller.  No hipMalloc, hipFree or allocating library
+ * routine is called.
+ */
+#define BSG_NOALLOC_SCRATCH_BYTES (64u << 20)
+int grouped_gemm_nvfp4_rowscaled_noalloc(int64_t G, const uint8_t* a, const uint8_t* a_scales,
+                                         const float* a_outer, const int64_t* offsets,
+                                         int64_t rows_cap, int64_t k, const uint8_t* b,
+                                         const uint8_t* b_scales, const float* b_outer,
+                                         const int64_t* n_per_group, void* out, int64_t ld_out,
+                                         int out_dtype, uint32_t* dev_status, void* stream);
+
+/*
  * grouped_gemm_nvfp4_pertensor
  *
  * Per-tensor NVFP4 grouped GEMM ("gemm.py": for NVFP4 operands alpha is the
