@@ -258,11 +258,13 @@ class Nvfp4Wgrad(Case):
 
 class Nvfp4Fprop(Case):
     """offsets -> row-scaled NVFP4 quantize of X and W -> grouped GEMM with the
-    fused outer-scale epilogue."""
+    fused outer-scale epilogue, or (scratch) the pages' two-step flow: the GEMM
+    stores FP32 S in a [rows_cap, ld] scratch and a second kernel applies the
+    outer scales into the bf16 output ("gemm" then times both kernels)."""
 
-    def __init__(self, name, dev):
+    def __init__(self, name, dev, scratch=False):
         self.name = name
-        self.w = w = workloads.get(name)
+        self.w = w = workloads.get("nvfp4" if scratch else name)
         t = workloads.tensors(w, device=dev)
         self.x, self.wt = t["x"], t["w"]
         G, K, R = w.G, w.k, w.rows_cap
@@ -279,6 +281,8 @@ class Nvfp4Fprop(Case):
         self.ws = torch.empty((NB, K // 16), dtype=torch.uint8, device=dev)
         self.wo = torch.empty(NB, dtype=torch.float32, device=dev)
         self.y = torch.empty((R, self.ld), dtype=torch.bfloat16, device=dev)
+        self.scratch = (torch.empty((R, self.ld), dtype=torch.float32, device=dev) if scratch
+                        else None)
         self.kernels = ("offsets", "quantize_x", "quantize_w", "gemm")
         live = w.live_rows
         self.flops = 2.0 * K * float(sum(int(m) * n for m, n in zip(w.sizes, self.npg)))
@@ -300,7 +304,7 @@ class Nvfp4Fprop(Case):
         self._rec(ev, 3)
         bsg.grouped_gemm_nvfp4_rowscaled(self.xd, self.xs, self.xo, self.off, self.K, self.wd, self.ws,
                                          self.wo, self.npg, out=self.y, ld_out=self.ld,
-                                         out_dtype=bsg.BSG_OUT_BF16)
+                                         out_dtype=bsg.BSG_OUT_BF16, scratch=self.scratch)
         self._rec(ev, 4)
 
 
@@ -362,6 +366,8 @@ def make_case(name, dev):
         return MxWgrad(name, dev)
     if name == "nvfp4":
         return Nvfp4Fprop(name, dev)
+    if name == "nvfp4_scratch":
+        return Nvfp4Fprop(name, dev, scratch=True)
     if name == "nvfp4_wgrad":
         return Nvfp4Wgrad(name, dev)
     if name == "dgrad":
@@ -372,6 +378,12 @@ def make_case(name, dev):
 
 
 # ---------------------------------------------------------------- timing
+
+# GPU cycles of the spin kernel queued ahead of every timed step: while the GPU
+# spins, the host enqueues the whole step, so the events around each kernel see
+# the GPU go from one kernel to the next without waiting for the host
+SPIN_CYCLES = 3_000_000
+
 
 def time_case(case, steps, warmup, flush_buf):
     for _ in range(warmup):
@@ -386,6 +398,7 @@ def time_case(case, steps, warmup, flush_buf):
     for s in range(steps):
         if flush_buf is not None:
             flush_buf.sum()
+        torch.cuda._sleep(SPIN_CYCLES)
         case.step(evs[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -394,21 +407,26 @@ def time_case(case, steps, warmup, flush_buf):
             per_kernel[s, i] = evs[s][i].elapsed_time(evs[s][i + 1])
         step_ms[s] = evs[s][0].elapsed_time(evs[s][nk])
     return {
-        "step_ms": float(step_ms.mean()),
+        "step_ms": float(np.median(step_ms)),
+        "step_ms_mean": float(step_ms.mean()),
         "wall_ms_per_step": 1e3 * wall / steps,
-        "kernel_ms": {k: float(per_kernel[:, i].mean()) for i, k in enumerate(case.kernels)},
+        "kernel_ms": {k: float(np.median(per_kernel[:, i])) for i, k in enumerate(case.kernels)},
     }
 
 
 def summarize(case, t, mfma_dtype):
     km = t["kernel_ms"]
+    gemm_tf = case.flops / (km["gemm"] * 1e-3) / 1e12
     out = {"workload": case.name, "step_ms": round(t["step_ms"], 4),
+           "step_ms_mean": round(t["step_ms_mean"], 4),
            "step_tflops": round(case.flops / (t["step_ms"] * 1e-3) / 1e12, 2),
            "gemm_us": round(km["gemm"] * 1e3, 2),
-           "gemm_tflops": round(case.flops / (km["gemm"] * 1e-3) / 1e12, 2),
-           "gemm_frac_of_peak": round(case.flops / (km["gemm"] * 1e-3) / 1e12
-                                      / MFMA_PEAK_TFLOPS[mfma_dtype], 4),
+           "gemm_tflops": round(gemm_tf, 2),
+           "gemm_frac_of_peak": round(gemm_tf / MFMA_PEAK_TFLOPS[mfma_dtype], 4),
            "mfma_peak_tflops": MFMA_PEAK_TFLOPS[mfma_dtype], "kernels_us": {}}
+    if mfma_dtype == "bf16":
+        # the NVFP4 GEMM runs on fp16 MFMA (the design bound); the FP4 peak alongside
+        out["gemm_frac_of_fp4_peak"] = round(gemm_tf / MFMA_PEAK_TFLOPS["fp4"], 4)
     for k, ms in km.items():
         ent = {"us": round(ms * 1e3, 2)}
         b = case.bytes.get(k, 0.0)
@@ -417,7 +435,50 @@ def summarize(case, t, mfma_dtype):
             ent.update({"algorithmic_bytes": int(b), "GB_s": round(gbs, 1),
                         "frac_of_hbm": round(gbs / HBM_PEAK_GBS, 4)})
         out["kernels_us"][k] = ent
+    w = case.w
+    out["group_sizes"] = [int(v) for v in w.sizes]
+    if w.n_per_group is not None:
+        out["n_per_group"] = [int(v) for v in w.n_per_group]
     return out
+
+
+def input_digests(case):
+    """SHA-256 of every bf16 input tensor of a case (the bytes on the device)."""
+    import hashlib
+    out = {}
+    for key in ("x", "wt", "dy"):
+        t = getattr(case, key, None)
+        if t is None:
+            continue
+        h = hashlib.sha256()
+        flat = t.reshape(-1).view(torch.int16)
+        step = 1 << 26
+        for i in range(0, flat.numel(), step):
+            h.update(flat[i:i + step].cpu().numpy().tobytes())
+        out["w" if key == "wt" else key] = h.hexdigest()
+    return out
+
+
+def device_copy_rate(dev, flush_buf, nbytes=256 << 20, iters=20):
+    """Median rate of the runtime's device-to-device copy of nbytes, cold,
+    counting bytes read + written: a practical ceiling for HBM-bound kernels."""
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    ts = []
+    for _ in range(iters):
+        if flush_buf is not None:
+            flush_buf.sum()
+        torch.cuda._sleep(SPIN_CYCLES // 4)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts))
+    del src, dst
+    return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
 
 
 # ---------------------------------------------------------------- CPU baseline (the oracle)
@@ -437,53 +498,154 @@ def code_sha256(paths):
 
 
 def gemm_traffic():
-    """Counter-measured HBM bytes of one fprop GEMM launch, or None when no
-    record exists or the kernel's code (its source and the local headers it
-    includes) has changed since it was taken."""
+    """Counter-measured HBM bytes of one fprop GEMM launch and the record they
+    come from, or (None, reason) when no record exists or the kernel's code (its
+    source and the local headers it includes) has changed since it was taken."""
+    rel = os.path.relpath(TRAFFIC_RECORD, ROOT)
     try:
         rec = json.load(open(TRAFFIC_RECORD))
         sha = code_sha256([os.path.join(ROOT, f) for f in rec["kernel_sources"]])
     except (OSError, ValueError, KeyError):
-        return None
+        return None, "no traffic record"
     if sha != rec.get("kernel_code_sha256"):
+        return None, "%s was taken with other kernel code" % rel
+    return int(rec["traffic_bytes"]), ("rocprofv3 FETCH_SIZE + WRITE_SIZE of the same kernel code, "
+                                       "recorded in %s" % rel)
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _blas_threads():
+    try:
+        import threadpoolctl
+        n = [i.get("num_threads") for i in threadpoolctl.threadpool_info()
+             if i.get("user_api") == "blas"]
+        return max(n) if n else None
+    except Exception:
         return None
-    return int(rec["traffic_bytes"])
+
+
+def _host_bf16(shape, std, seed, outlier_p=0.0, outlier_mul=1.0):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(shape, generator=g) * std
+    if outlier_p:
+        x = torch.where(torch.rand(shape, generator=g) < outlier_p, x * outlier_mul, x)
+    return workloads.bf16_bits(x.to(torch.bfloat16))
 
 
 def cpu_baseline():
-    """The oracle, untuned, on a bounded sample of the fprop workload: its
-    first expert whole (that expert's token rows and its full N x K weight,
-    drawn by the workload's recipe), quantized (MXFP8, rowwise) and multiplied
-    in fp64.  Reported in the metric's unit."""
+    """The oracle, untuned, on bounded samples of each workload (same value
+    distributions, smaller shapes, drawn on the host), timed on this host's
+    cores: quantize GB/s (numpy, single-threaded) and fp64 GEMM GFLOP/s (numpy
+    matmul on BLAS threads).  The headline value is the fprop sample's
+    quantize + GEMM work in the metric's unit (TFLOP/s)."""
     from oracle import gemm as GM
     from oracle import quantize as Q
-    w = workloads.get("fprop")
-    gen = torch.Generator().manual_seed(w.seed)
-    experts, nrows, K = 4, w.n, w.k
-    dt, flops, rows_done = 0.0, 0.0, 0
-    for e in range(experts):
-        rows = int(w.sizes[e])
-        x = torch.randn((rows, K), generator=gen)
-        x = torch.where(torch.rand((rows, K), generator=gen) < 0.01, x * 20, x).to(torch.bfloat16)
-        wt = (torch.randn((nrows, K), generator=gen) * 0.02).to(torch.bfloat16)
-        xb, wb = workloads.bf16_bits(x), workloads.bf16_bits(wt)
+    per = {}
+
+    def tq(fn):
         t0 = time.perf_counter()
-        ad, asc = Q.mxfp8_rowwise(xb, np.array([0, rows]))
-        bd, bsc = Q.mxfp8_rowwise(wb, np.array([0, nrows]))
-        GM.mxfp8_fprop(ad, asc, bd.reshape(1, nrows, K), bsc, np.array([0, rows]), K)
-        dt += time.perf_counter() - t0
-        flops += 2.0 * rows * nrows * K
-        rows_done += rows
+        r = fn()
+        return r, time.perf_counter() - t0
+
+    # fprop: the first expert whole (its token rows and its 14336 x 4096 weight)
+    w = workloads.get("fprop")
+    rows, N, K = int(w.sizes[0]), w.n, w.k
+    xb = _host_bf16((rows, K), 1.0, w.seed, 0.01, 20.0)
+    wb = _host_bf16((N, K), 0.02, w.seed + 1)
+    (ad, asc), tqx = tq(lambda: Q.mxfp8_rowwise(xb, np.array([0, rows])))
+    (bd, bsc), tqw = tq(lambda: Q.mxfp8_rowwise(wb, np.array([0, N])))
+    _, tg = tq(lambda: GM.mxfp8_fprop(ad, asc, bd.reshape(1, N, K), bsc, np.array([0, rows]), K))
+    fl = 2.0 * rows * N * K
+    qbytes = (rows + N) * K * (2 + 1 + 1 / 32)
+    per["fprop"] = {"sample": "expert 0 whole: %d x %d activations, %d x %d weight" % (rows, K, N, K),
+                    "quantize_GB_s": round(qbytes / (tqx + tqw) / 1e9, 3),
+                    "gemm_GFLOP_s": round(fl / tg / 1e9, 2), "seconds": round(tqx + tqw + tg, 2)}
+    head = {"value": round(fl / (tqx + tqw + tg) / 1e12, 6), "seconds": round(tqx + tqw + tg, 2)}
+
+    # wgrad: 1024 tokens of one expert, columnwise copies of dY and X, the NT product
+    M, N, K = 1024, 4096, 4096
+    dy = _host_bf16((M, N), 1.0, 21)
+    x = _host_bf16((M, K), 1.0, 22)
+    off, poff = np.array([0, M]), np.array([0, M])
+    (dyc, dys), t1 = tq(lambda: Q.mxfp8_colwise(dy, off, poff))
+    (xc, xs), t2 = tq(lambda: Q.mxfp8_colwise(x, off, poff))
+    _, tg = tq(lambda: GM.mxfp8_wgrad(dyc, dys, xc, xs, poff, N, K))
+    per["wgrad"] = {"sample": "1024 tokens of one expert, N = K = 4096",
+                    "quantize_GB_s": round(M * (N + K) * (2 + 1 + 1 / 32) / (t1 + t2) / 1e9, 3),
+                    "gemm_GFLOP_s": round(2.0 * M * N * K / tg / 1e9, 2),
+                    "seconds": round(t1 + t2 + tg, 2)}
+
+    # zipf: 512 rows of one expert against its 2048 x 7168 weight
+    M, N, K = 512, 2048, 7168
+    xb = _host_bf16((M, K), 1.0, 31)
+    wb = _host_bf16((N, K), 0.02, 32)
+    (ad, asc), t1 = tq(lambda: Q.mxfp8_rowwise(xb, np.array([0, M])))
+    (bd, bsc), t2 = tq(lambda: Q.mxfp8_rowwise(wb, np.array([0, N])))
+    _, tg = tq(lambda: GM.mxfp8_fprop(ad, asc, bd.reshape(1, N, K), bsc, np.array([0, M]), K))
+    per["zipf"] = {"sample": "512 rows of one expert, K = 7168, N = 2048",
+                   "quantize_GB_s": round((M + N) * K * (2 + 1 + 1 / 32) / (t1 + t2) / 1e9, 3),
+                   "gemm_GFLOP_s": round(2.0 * M * N * K / tg / 1e9, 2),
+                   "seconds": round(t1 + t2 + tg, 2)}
+
+    # dgrad: 512 rows of dY (E5M2) against 512 output columns of one expert's weight
+    M, Kc, N = 512, 14336, 512
+    dyb = _host_bf16((M, Kc), 1.0, 41)
+    wb = _host_bf16((Kc, N), 0.02, 42)
+    (dd, ds), t1 = tq(lambda: Q.mxfp8_rowwise(dyb, np.array([0, M]), elem="e5m2"))
+    (wd, ws), t2 = tq(lambda: Q.mxfp8_colwise(wb, np.array([0, Kc]), np.array([0, Kc])))
+    _, tg = tq(lambda: GM.mxfp8_dgrad(dd, ds, wd, ws, np.array([0, M]), Kc, N))
+    per["dgrad"] = {"sample": "512 rows of dY [., 14336] against 512 output columns of one expert",
+                    "quantize_GB_s": round((M + N) * Kc * (2 + 1 + 1 / 32) / (t1 + t2) / 1e9, 3),
+                    "gemm_GFLOP_s": round(2.0 * M * Kc * N / tg / 1e9, 2),
+                    "seconds": round(t1 + t2 + tg, 2)}
+
+    # row-scaled and per-tensor NVFP4: 512 rows against a 2048 x 4096 expert weight
+    M, N, K = 512, 2048, 4096
+    xb = _host_bf16((M, K), 1.0, 51)
+    wb = _host_bf16((N, K), 0.02, 52)
+    for name, qf, gf in (("nvfp4", Q.nvfp4_rowscaled, GM.nvfp4_rowscaled_fprop),
+                         ("nvfp4_pertensor", Q.nvfp4_pertensor, GM.nvfp4_pertensor_fprop)):
+        (a0, a1, a2), t1 = tq(lambda: qf(xb, np.array([0, M])))
+        (b0, b1, b2), t2 = tq(lambda: qf(wb, np.array([0, N])))
+        _, tg = tq(lambda: gf(a0, a1, a2, np.array([0, M]), b0, b1, b2, [N], K))
+        per[name] = {"sample": "512 rows against one 2048 x 4096 expert weight",
+                     "quantize_GB_s": round((M + N) * K * (2 + 0.5 + 1 / 16) / (t1 + t2) / 1e9, 3),
+                     "gemm_GFLOP_s": round(2.0 * M * N * K / tg / 1e9, 2),
+                     "seconds": round(t1 + t2 + tg, 2)}
+
+    # row-scaled NVFP4 wgrad: 512 tokens of one expert, columnwise copies, N = K = 4096
+    M, N, K = 512, 4096, 4096
+    dy = _host_bf16((M, N), 1.0, 61)
+    x = _host_bf16((M, K), 1.0, 62)
+    off, poff = np.array([0, M]), np.array([0, M])
+    a, t1 = tq(lambda: Q.nvfp4_rowscaled_colwise(dy, off, poff))
+    b, t2 = tq(lambda: Q.nvfp4_rowscaled_colwise(x, off, poff))
+    _, tg = tq(lambda: GM.nvfp4_rowscaled_wgrad(*a, *b, poff, N, K))
+    per["nvfp4_wgrad"] = {"sample": "512 tokens of one expert, N = K = 4096",
+                          "quantize_GB_s": round(M * (N + K) * (2 + 0.5 + 1 / 16) / (t1 + t2) / 1e9, 3),
+                          "gemm_GFLOP_s": round(2.0 * M * N * K / tg / 1e9, 2),
+                          "seconds": round(t1 + t2 + tg, 2)}
+
+    threads = _blas_threads()
     try:
-        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+        affinity = len(os.sched_getaffinity(0))
     except Exception:
-        threads = os.cpu_count() or 1
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": "fprop workload, experts 0-%d whole: %d token rows, %d x %d weights each, "
-                      "K=%d; oracle MXFP8 quantize of both + fp64 GEMM per expert (numpy; "
-                      "quantize single-threaded, matmul on BLAS threads)"
-                      % (experts - 1, rows_done, nrows, K, K)}
+        affinity = os.cpu_count()
+    return {"value": head["value"], "unit": "TFLOP/s", "cores": threads or affinity,
+            "kind": "oracle", "seconds": round(sum(v["seconds"] for v in per.values()), 2),
+            "sample": "fprop expert 0 whole (%s): oracle MXFP8 rowwise quantize of both operands "
+                      "+ fp64 GEMM; per-config samples under per_config" % per["fprop"]["sample"],
+            "cpu_model": _cpu_model(), "blas_threads": threads, "host_cpus": affinity,
+            "quantize_threads": 1, "per_config": per}
 
 
 def vendor_reference(dev, iters):
@@ -531,11 +693,12 @@ def vendor_reference(dev, iters):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--no-digests", action="store_true", help="skip the input SHA-256 digests")
     ap.add_argument("--only", default=None, help="comma list of workloads to time")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device copy (3x), the reference for "
@@ -567,7 +730,7 @@ def main():
         del src, dst
 
     names = ["fprop"] if args.no_extra else ["fprop", "tiny", "wgrad", "zipf", "dgrad", "nvfp4",
-                                             "nvfp4_wgrad", "nvfp4_pertensor"]
+                                             "nvfp4_scratch", "nvfp4_wgrad", "nvfp4_pertensor"]
     if args.only:
         names = args.only.split(",")
     results = {}
@@ -575,13 +738,16 @@ def main():
         log("[bench] %s: setup" % name)
         case = make_case(name, dev)
         torch.cuda.synchronize()
-        steps = args.steps if name == "fprop" else max(5, args.steps // 2)
-        t = time_case(case, steps, args.warmup, flush)
+        t = time_case(case, args.steps, args.warmup, flush)
         results[name] = summarize(case, t, "bf16" if name.startswith("nvfp4") else "fp8")
-        results[name]["steps"] = steps
+        results[name]["steps"] = args.steps
+        if not args.no_digests:
+            results[name]["input_sha256"] = input_digests(case)
         log("[bench] %s: %s" % (name, json.dumps(results[name])))
         del case
         torch.cuda.empty_cache()
+    copy_gbs = device_copy_rate(dev, flush)
+    log("[bench] device copy: %.1f GB/s (read + write)" % copy_gbs)
 
     head = results.get("fprop") or results[names[0]]
     achieved = head["gemm_tflops"]
@@ -591,12 +757,13 @@ def main():
     q_bytes = sum(v.get("algorithmic_bytes", 0) for v in qk)
     q_us = sum(v["us"] for v in qk)
     q_rate = q_bytes / (q_us * 1e-6) / 1e9 if q_us > 0 else None
+    traffic, traffic_src = gemm_traffic() if head is results.get("fprop") else (None, None)
     line = {
         "metric": METRIC,
         "value": head["step_tflops"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": results.get("fprop", head)["steps"],
+        "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": head["step_ms"],
         "higher_is_better": True,
@@ -608,15 +775,25 @@ def main():
                                "of 128), K=4096, N=14336; step = offsets + quantize X (row+col) + "
                                "quantize W + grouped GEMM",
                    "cache": "cold (a 512 MiB buffer read before each step)" if flush is not None
-                   else "warm"},
+                   else "warm",
+                   "timing": "median over %d steps after %d warm-up steps; HIP events around "
+                             "each kernel on its stream, a spin kernel queued ahead of each step"
+                             % (args.steps, args.warmup)},
+        "targets": {
+            "gemm_frac_of_mxfp8_peak": {"value": head["gemm_frac_of_peak"], "target": 0.60},
+            "quantize_x_frac_of_hbm": {"value": qx.get("frac_of_hbm"), "target": 0.70,
+                                       "what": "grouped activation quantize, rowwise + columnwise "
+                                               "in one pass (16384 x 4096 bf16)"},
+        },
         "quantize_x_GB_s": qx.get("GB_s"),
         "quantize_x_frac_of_hbm": qx.get("frac_of_hbm"),
-        "quantize_step_GB_s": round(q_rate, 1) if q_rate else None,
-        "quantize_step_frac_of_hbm": round(q_rate / HBM_PEAK_GBS, 4) if q_rate else None,
+        "quantize_xw_GB_s": round(q_rate, 1) if q_rate else None,
+        "quantize_xw_frac_of_hbm": round(q_rate / HBM_PEAK_GBS, 4) if q_rate else None,
+        "device_copy_GB_s": copy_gbs,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": MFMA_PEAK_TFLOPS["fp8"], "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_PEAK_TFLOPS["fp8"], 4),
-                     "traffic": gemm_traffic() if head is results.get("fprop") else None,
+                     "traffic": traffic, "traffic_source": traffic_src,
                      "kernel": "grouped_gemm_mxfp8 (fprop)"},
         "configs": results,
     }

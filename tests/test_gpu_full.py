@@ -141,10 +141,12 @@ def test_full_wgrad():
     assert not torch.isnan(dw).any()
 
 
-def test_full_nvfp4_rowscaled():
-    """8 experts, 16384 live rows of 18432, K=4096, N_e in {2048, 4096}."""
+@pytest.mark.parametrize("flow", ["nvfp4", "nvfp4_scratch"])
+def test_full_nvfp4_rowscaled(flow):
+    """8 experts, 16384 live rows of 18432, K=4096, N_e in {2048, 4096}; fused
+    outer-scale epilogue, and the FP32-scratch + post-scale flow."""
     dev = device()
-    case = bench.make_case("nvfp4", dev)
+    case = bench.make_case(flow, dev)
     case.y.fill_(float("nan"))
     case.step()
     torch.cuda.synchronize()
