@@ -15,7 +15,10 @@ defined in float32):
                    (the GEMM-ready scale order, written by the quantize itself).
 * ``quantize``  -- grouped MXFP8 rowwise / columnwise quantize (E4M3, and E5M2 for
                    gradients), the row-scaled NVFP4 quantize (rows and columnwise
-                   copies) and the per-tensor (per-expert) NVFP4 quantize.
+                   copies) and the per-tensor (per-expert) NVFP4 quantize, also
+                   with a randomized Hadamard transform along the contraction
+                   and with 2-D (16 x 16) block scales.
+* ``rht``       -- the randomized Hadamard transform of 16-element blocks.
 * ``gemm``      -- per-expert dense products of the dequantized operands in fp64:
                    fprop (TN, ragged rows), wgrad (NT, ragged contraction), dgrad,
                    the row-scaled NVFP4 fprop / wgrad with their outer-scale
@@ -32,8 +35,9 @@ the function that takes it.
 
 Parity unpinned by the pages (pinned instead by the OCP MX / NVFP4 format
 definitions, closed forms and brute force in ``tests/test_oracle_*.py``):
-the E8M0 exponent rule, the NVFP4 float32 operation order, and the GEMM-ready
-scale byte order.
+the E8M0 exponent rule, the NVFP4 float32 operation order, the GEMM-ready
+scale byte order, the RHT's size and float32 butterfly order, and the 2-D
+block shape.
 """
 
-from . import formats, offsets, layout, quantize, gemm  # noqa: F401
+from . import formats, offsets, layout, quantize, gemm, rht  # noqa: F401

@@ -221,7 +221,7 @@ def nvfp4_pertensor(x_bits, offsets):
       enc  = S_g / sd (0 if sd == 0; capped at FLT_MAX)
       q    = E2M1(x * enc)
     so that x ~= e2m1(q) * sd * tsi_g, tsi_g = amax_g / 2688.  An empty group
-    has amax 0.
+    has amax 0.  The groups start at row 0 (offsets[0] == 0).
 
     Returns (packed [live, C/2] uint8, block scales [live, C/16] uint8 E4M3,
     amax [G] float32)."""
@@ -229,14 +229,23 @@ def nvfp4_pertensor(x_bits, offsets):
     rows, cols = x_bits.shape
     if cols % MX_BLOCK:
         raise ValueError("cols must be a multiple of 32")
-    off = np.asarray(offsets, dtype=np.int64)
-    G = len(off) - 1
-    live = int(off[-1])
+    live = int(np.asarray(offsets)[-1])
     if live > rows:
         raise ValueError("sum of group sizes exceeds the row capacity")
+    return nvfp4_pertensor_values(f32(bf16_bits_to_f64(x_bits[:live])), offsets)
+
+
+def nvfp4_pertensor_values(x, offsets):
+    """``nvfp4_pertensor`` of float32 values x [live, C] (the bf16 inputs, or
+    their randomized Hadamard transform)."""
+    x = np.asarray(x, dtype=np.float32)
+    live, cols = x.shape
+    off = np.asarray(offsets, dtype=np.int64)
+    G = len(off) - 1
+    if int(off[0]) != 0 or int(off[-1]) != live:
+        raise ValueError("offsets must run from 0 to the live rows")
     if np.any(np.diff(off) < 0):
         raise ValueError("negative group size")
-    x = f32(bf16_bits_to_f64(x_bits[:live]))                    # exact in float32
     two688 = np.float32(E2M1_MAX * E4M3_MAX)
     amax = np.zeros(G, np.float32)
     for g in range(G):
@@ -258,6 +267,76 @@ def nvfp4_pertensor(x_bits, offsets):
         v = f32(blocks * enc[..., None])
     q = e2m1_encode(v.astype(np.float64)).reshape(live, cols)
     return fp4_pack(q), s8, amax
+
+
+def nvfp4_pertensor_rht(x_bits, offsets, sign_mask):
+    """Per-tensor NVFP4 of the randomized Hadamard transform of the rows
+    ("gemm.py", ``_quantize_gemm_operands``: with NVFP4 1-D scaling both GEMM
+    operands carry the RHT so that it cancels; transform in ``oracle.rht``):
+    the rows' 16-element blocks along the contraction are transformed in
+    float32, then quantized exactly as ``nvfp4_pertensor`` quantizes values, the
+    group amax taken over the transformed values.  Returns what
+    ``nvfp4_pertensor`` returns."""
+    from .rht import rht16
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    rows, cols = x_bits.shape
+    if cols % MX_BLOCK:
+        raise ValueError("cols must be a multiple of 32")
+    live = int(np.asarray(offsets)[-1])
+    if live > rows:
+        raise ValueError("sum of group sizes exceeds the row capacity")
+    return nvfp4_pertensor_values(rht16(f32(bf16_bits_to_f64(x_bits[:live])), sign_mask), offsets)
+
+
+def nvfp4_pertensor_2d(x_bits, offsets):
+    """Per-tensor NVFP4 with 2-D block scales ("gemm.py", ``_jax_scaled_matmul``
+    accepts an ``NVFP4_2D_SCALING`` mode next to the 1-D one; the pages give no
+    block shape).  Reading: one E4M3 scale per 16 x 16 block -- 16 rows by 16
+    columns, the NVFP4 block size in both directions, so that a tensor and its
+    transpose quantize to transposed codes -- with the float32 steps of
+    ``nvfp4_pertensor`` and the block maximum taken over the whole 16 x 16
+    block.  Block rows start at each group's first row; a group's last block
+    row holds its remaining (fewer than 16) rows.  The group's amax and outer
+    scale are the per-tensor ones.  The scales are written in the GEMM's
+    per-row layout: each row of a block row carries its block's scale byte, so
+    ``grouped_gemm_nvfp4_pertensor`` consumes the result unchanged.  Returns
+    what ``nvfp4_pertensor`` returns."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    rows, cols = x_bits.shape
+    if cols % MX_BLOCK:
+        raise ValueError("cols must be a multiple of 32")
+    off = np.asarray(offsets, dtype=np.int64)
+    live = int(off[-1])
+    if live > rows or int(off[0]) != 0 or np.any(np.diff(off) < 0):
+        raise ValueError("offsets must run from 0 to at most the row capacity")
+    x = f32(bf16_bits_to_f64(x_bits[:live]))
+    G = len(off) - 1
+    two688 = np.float32(E2M1_MAX * E4M3_MAX)
+    nb = cols // NVFP4_BLOCK
+    codes = np.zeros((live, cols), np.uint8)
+    s8 = np.zeros((live, nb), np.uint8)
+    amax = np.zeros(G, np.float32)
+    with np.errstate(divide="ignore", over="ignore", invalid="ignore"):
+        for g in range(G):
+            r0, r1 = int(off[g]), int(off[g + 1])
+            if r1 == r0:
+                continue
+            amax[g] = np.abs(x[r0:r1]).max() if cols else np.float32(0)
+            big_s = f32(two688 / amax[g]) if amax[g] > 0 else np.float32(1.0)
+            big_s = np.float32(min(big_s, FLT_MAX))
+            for b0 in range(r0, r1, NVFP4_BLOCK):
+                b1 = min(b0 + NVFP4_BLOCK, r1)
+                blk = x[b0:b1].reshape(b1 - b0, nb, NVFP4_BLOCK)
+                bmax = np.abs(blk).max(axis=(0, 2))                    # [nb]
+                s_f = f32(f32(bmax / np.float32(E2M1_MAX)) * big_s)
+                sc = e4m3_encode(s_f.astype(np.float64))
+                sd = f32(e4m3_decode(sc))
+                enc = np.where(sd == 0, np.float32(0.0), np.minimum(f32(big_s / sd), FLT_MAX))
+                enc = enc.astype(np.float32)
+                v = f32(blk * enc[None, :, None])
+                codes[b0:b1] = e2m1_encode(v.astype(np.float64)).reshape(b1 - b0, cols)
+                s8[b0:b1] = sc[None, :]
+    return fp4_pack(codes), s8, amax
 
 
 def nvfp4_block_dequant(packed, block_scales, cols):
