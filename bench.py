@@ -310,11 +310,16 @@ class Nvfp4Fprop(Case):
 
 class Nvfp4PerTensorFprop(Case):
     """offsets -> per-tensor NVFP4 quantize of X (one amax per expert's rows)
-    and W (one amax per expert) -> grouped GEMM with alpha_g = tsi_A * tsi_B."""
+    and W (one amax per expert) -> grouped GEMM with alpha_g = tsi_A * tsi_B.
+    variant "rht": X and W both through the randomized Hadamard transform with
+    the same 16 signs (drawn from the workload's seed); "2d": W with 16 x 16
+    block scales."""
 
-    def __init__(self, name, dev):
+    def __init__(self, name, dev, variant=None):
         self.name = name
-        self.w = w = workloads.get(name)
+        self.variant = variant
+        self.w = w = workloads.get("nvfp4_pertensor" if variant else name)
+        self.rht_mask = int(np.random.default_rng(w.seed).integers(0, 1 << 16))
         t = workloads.tensors(w, device=dev)
         self.x, self.wt = t["x"], t["w"]
         G, K, R = w.G, w.k, w.rows_cap
@@ -345,11 +350,23 @@ class Nvfp4PerTensorFprop(Case):
         self._rec(ev, 0)
         bsg.group_offsets_i32_to_i64(self.sizes, offsets=self.off, capacity=self.R)
         self._rec(ev, 1)
-        bsg.grouped_quantize_nvfp4_pertensor(self.x, self.off, data=self.xd, block_scales=self.xs,
-                                             amax=self.xa)
+        if self.variant == "rht":
+            bsg.grouped_quantize_nvfp4_pertensor_rht(self.x, self.off, self.rht_mask, data=self.xd,
+                                                     block_scales=self.xs, amax=self.xa)
+        else:
+            bsg.grouped_quantize_nvfp4_pertensor(self.x, self.off, data=self.xd,
+                                                 block_scales=self.xs, amax=self.xa)
         self._rec(ev, 2)
-        bsg.grouped_quantize_nvfp4_pertensor(self.wt, self.woff, data=self.wd, block_scales=self.ws,
-                                             amax=self.wa)
+        if self.variant == "rht":
+            bsg.grouped_quantize_nvfp4_pertensor_rht(self.wt, self.woff, self.rht_mask,
+                                                     data=self.wd, block_scales=self.ws,
+                                                     amax=self.wa)
+        elif self.variant == "2d":
+            bsg.grouped_quantize_nvfp4_pertensor_2d(self.wt, self.woff, data=self.wd,
+                                                    block_scales=self.ws, amax=self.wa)
+        else:
+            bsg.grouped_quantize_nvfp4_pertensor(self.wt, self.woff, data=self.wd,
+                                                 block_scales=self.ws, amax=self.wa)
         self._rec(ev, 3)
         bsg.grouped_gemm_nvfp4_pertensor(self.xd, self.xs, self.xa, self.off, self.K, self.wd,
                                          self.ws, self.wa, self.npg, out=self.y, ld_out=self.ld,
@@ -374,6 +391,10 @@ def make_case(name, dev):
         return MxDgrad(name, dev)
     if name == "nvfp4_pertensor":
         return Nvfp4PerTensorFprop(name, dev)
+    if name == "nvfp4_rht":
+        return Nvfp4PerTensorFprop(name, dev, variant="rht")
+    if name == "nvfp4_2d":
+        return Nvfp4PerTensorFprop(name, dev, variant="2d")
     raise KeyError(name)
 
 
@@ -730,7 +751,8 @@ def main():
         del src, dst
 
     names = ["fprop"] if args.no_extra else ["fprop", "tiny", "wgrad", "zipf", "dgrad", "nvfp4",
-                                             "nvfp4_scratch", "nvfp4_wgrad", "nvfp4_pertensor"]
+                                             "nvfp4_scratch", "nvfp4_wgrad", "nvfp4_pertensor",
+                                             "nvfp4_rht", "nvfp4_2d"]
     if args.only:
         names = args.only.split(",")
     results = {}

@@ -31,7 +31,8 @@ EXPORTS = ("bsg_last_error", "bsg_version", "group_offsets_i32_to_i64", "grouped
            "grouped_quantize_nvfp4_pertensor",
            "grouped_gemm_mxfp8", "grouped_gemm_mxfp8_ex", "grouped_gemm_nvfp4_rowscaled",
            "grouped_gemm_nvfp4_rowscaled_wgrad", "grouped_gemm_nvfp4_pertensor",
-           "grouped_gemm_nvfp4_rowscaled_noalloc")
+           "grouped_gemm_nvfp4_rowscaled_noalloc", "grouped_quantize_nvfp4_pertensor_rht",
+           "grouped_quantize_nvfp4_pertensor_2d")
 BSG_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
@@ -78,6 +79,11 @@ def load_library(path=LIB_PATH):
                                                  P, P, P]
     lib.grouped_quantize_nvfp4_pertensor.restype = I32
     lib.grouped_quantize_nvfp4_pertensor.argtypes = [P, I64, I64, I64, P, P, P, P, P, P]
+    lib.grouped_quantize_nvfp4_pertensor_rht.restype = I32
+    lib.grouped_quantize_nvfp4_pertensor_rht.argtypes = [P, I64, I64, I64, P, ctypes.c_uint32, P, P,
+                                                         P, P, P]
+    lib.grouped_quantize_nvfp4_pertensor_2d.restype = I32
+    lib.grouped_quantize_nvfp4_pertensor_2d.argtypes = [P, I64, I64, I64, P, P, P, P, P, P]
     lib.grouped_gemm_nvfp4_pertensor.restype = I32
     lib.grouped_gemm_nvfp4_pertensor.argtypes = [I64, P, P, P, P, I64, I64, P, P, P, P, P, I64, I32,
                                                  P, P]
@@ -305,6 +311,47 @@ def grouped_quantize_nvfp4_pertensor(x, offsets, G=None, data=None, block_scales
                                                 _ptr(data), _ptr(block_scales), _ptr(amax),
                                                 _ptr(status), _stream(x)))
     return data, block_scales, amax
+
+
+def _pertensor_variant(cfn, x, offsets, G, data, block_scales, amax, status, *extra):
+    import torch
+    rows_cap, cols = _bf16_2d(x)
+    G = offsets.numel() - 1 if G is None else G
+    _req(offsets, "offsets", 8 * (G + 1), torch.int64)
+    if data is None:
+        data = torch.empty((rows_cap, cols // 2), dtype=torch.uint8, device=x.device)
+    if block_scales is None:
+        block_scales = torch.empty((rows_cap, cols // 16), dtype=torch.uint8, device=x.device)
+    if amax is None:
+        amax = torch.empty(G, dtype=torch.float32, device=x.device)
+    _req(data, "data", rows_cap * cols // 2)
+    _req(block_scales, "block_scales", rows_cap * cols // 16)
+    _req(amax, "amax", 4 * G, torch.float32)
+    _req(status, "status", 4, optional=True)
+    args = [_ptr(x), rows_cap, cols, G, _ptr(offsets)] + list(extra) + [
+        _ptr(data), _ptr(block_scales), _ptr(amax), _ptr(status), _stream(x)]
+    _check(cfn(*args))
+    return data, block_scales, amax
+
+
+def grouped_quantize_nvfp4_pertensor_rht(x, offsets, rht_sign_mask, G=None, data=None,
+                                         block_scales=None, amax=None, status=None):
+    """Per-tensor NVFP4 of the rows' randomized Hadamard transform (16-element
+    blocks, signs from the 16-bit mask): outputs as
+    grouped_quantize_nvfp4_pertensor.  See include/bsg.h."""
+    lib = load_library()
+    return _pertensor_variant(lib.grouped_quantize_nvfp4_pertensor_rht, x, offsets, G, data,
+                              block_scales, amax, status, ctypes.c_uint32(int(rht_sign_mask)))
+
+
+def grouped_quantize_nvfp4_pertensor_2d(x, offsets, G=None, data=None, block_scales=None, amax=None,
+                                        status=None):
+    """Per-tensor NVFP4 with one E4M3 scale per 16 x 16 block (written into each
+    row of the block): outputs as grouped_quantize_nvfp4_pertensor.  See
+    include/bsg.h."""
+    lib = load_library()
+    return _pertensor_variant(lib.grouped_quantize_nvfp4_pertensor_2d, x, offsets, G, data,
+                              block_scales, amax, status)
 
 
 def grouped_quantize_nvfp4_rowscaled_colwise(x, offsets, padded_offsets, G=None, col_rows_cap=None,

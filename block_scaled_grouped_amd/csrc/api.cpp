@@ -159,6 +159,51 @@ int grouped_quantize_nvfp4_pertensor(const void* x, int64_t rows_cap, int64_t co
                     fn);
 }
 
+static int pertensor_args(const char* fn, const void* x, int64_t rows_cap, int64_t cols, int64_t G,
+                          const int64_t* offsets, const uint8_t* data, const uint8_t* block_scales,
+                          const float* amax) {
+  if (x == nullptr || offsets == nullptr || data == nullptr || block_scales == nullptr || amax == nullptr)
+    return fail(BSG_ERR_NULL, "%s: x, offsets, data, block_scales and amax must be non-NULL", fn);
+  if (G < 1 || G > BSG_MAX_GROUPS)
+    return fail(BSG_ERR_SHAPE, "%s: G=%lld outside [1, %d]", fn, (long long)G, BSG_MAX_GROUPS);
+  if (rows_cap < 0 || cols <= 0 || cols % 32 != 0)
+    return fail(BSG_ERR_SHAPE, "%s: need rows_cap >= 0 and cols a positive multiple of 32", fn);
+  if (rows_cap > 0x7fffffffLL) return fail(BSG_ERR_SHAPE, "%s: rows_cap too large", fn);
+  if (!aligned16(x) || !aligned16(data) || !aligned4(amax))
+    return fail(BSG_ERR_ALIGN, "%s: x and data must be 16-byte aligned, amax 4-byte", fn);
+  return BSG_OK;
+}
+
+int grouped_quantize_nvfp4_pertensor_rht(const void* x, int64_t rows_cap, int64_t cols, int64_t G,
+                                         const int64_t* offsets, uint32_t rht_sign_mask,
+                                         uint8_t* data, uint8_t* block_scales, float* amax,
+                                         uint32_t* dev_status, void* stream) {
+  const char* fn = "grouped_quantize_nvfp4_pertensor_rht";
+  const int rc = pertensor_args(fn, x, rows_cap, cols, G, offsets, data, block_scales, amax);
+  if (rc != BSG_OK) return rc;
+  if (rht_sign_mask > 0xffffu)
+    return fail(BSG_ERR_SHAPE, "%s: rht_sign_mask has bits above the 16 signs", fn);
+  return hip_result(bsg::launch_quantize_nvfp4_pertensor_rht(static_cast<const uint16_t*>(x),
+                                                             rows_cap, cols, (int)G, offsets,
+                                                             rht_sign_mask, data, block_scales,
+                                                             amax, dev_status, (hipStream_t)stream),
+                    fn);
+}
+
+int grouped_quantize_nvfp4_pertensor_2d(const void* x, int64_t rows_cap, int64_t cols, int64_t G,
+                                        const int64_t* offsets, uint8_t* data,
+                                        uint8_t* block_scales, float* amax, uint32_t* dev_status,
+                                        void* stream) {
+  const char* fn = "grouped_quantize_nvfp4_pertensor_2d";
+  const int rc = pertensor_args(fn, x, rows_cap, cols, G, offsets, data, block_scales, amax);
+  if (rc != BSG_OK) return rc;
+  return hip_result(bsg::launch_quantize_nvfp4_pertensor_2d(static_cast<const uint16_t*>(x),
+                                                            rows_cap, cols, (int)G, offsets, data,
+                                                            block_scales, amax, dev_status,
+                                                            (hipStream_t)stream),
+                    fn);
+}
+
 int grouped_quantize_nvfp4_rowscaled_colwise(const void* x, int64_t rows_cap, int64_t cols,
                                              int64_t G, const int64_t* offsets,
                                              const int64_t* padded_offsets, int64_t col_rows_cap,

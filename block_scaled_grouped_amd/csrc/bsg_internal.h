@@ -182,6 +182,16 @@ hipError_t launch_quantize_nvfp4_pertensor(const uint16_t* x, int64_t rows_cap, 
                                            uint8_t* block_scales, float* amax, uint32_t* status,
                                            hipStream_t stream);
 
+hipError_t launch_quantize_nvfp4_pertensor_rht(const uint16_t* x, int64_t rows_cap, int64_t cols,
+                                               int G, const int64_t* offsets, uint32_t sign_mask,
+                                               uint8_t* data, uint8_t* block_scales, float* amax,
+                                               uint32_t* status, hipStream_t stream);
+
+hipError_t launch_quantize_nvfp4_pertensor_2d(const uint16_t* x, int64_t rows_cap, int64_t cols,
+                                              int G, const int64_t* offsets, uint8_t* data,
+                                              uint8_t* block_scales, float* amax, uint32_t* status,
+                                              hipStream_t stream);
+
 hipError_t launch_quantize_nvfp4_rowscaled_colwise(const uint16_t* x, int64_t rows_cap,
                                                    int64_t cols, int G, const int64_t* offsets,
                                                    const int64_t* padded_offsets,

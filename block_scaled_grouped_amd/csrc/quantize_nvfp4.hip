@@ -19,9 +19,10 @@
 // longer rows read their remaining blocks a second time, from the L2.
 //
 // The file also holds the per-tensor form (one outer scale per group from the
-// group's amax: a group-amax pass, then the same cast) and the columnwise
-// (transposed, per-expert) form for the weight gradient; each is described
-// where it starts below.
+// group's amax: a group-amax pass, then the same cast), its randomized-Hadamard
+// and 2-D (16 x 16 block scale) variants, and the columnwise (transposed,
+// per-expert) form for the weight gradient; each is described where it starts
+// below.
 #include "bsg_internal.h"
 
 #pragma clang fp contract(off)
@@ -312,6 +313,336 @@ hipError_t launch_quantize_nvfp4_pertensor(const uint16_t* x, int64_t rows_cap, 
     hipLaunchKernelGGL((nvfp4_rowscaled_kernel<true, false>), dim3((unsigned)rows_cap),
                        dim3(kNvThreads), 0, stream, x, rows_cap, cols, G, offsets, data,
                        block_scales, nullptr, amax, nullptr);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- per tensor, RHT
+//
+// Per-tensor NVFP4 of the randomized Hadamard transform of the rows ("gemm.py",
+// _quantize_gemm_operands: with NVFP4 1-D scaling both GEMM operands carry the
+// RHT, so that it cancels in the product).  Each 16-element block x along the
+// contraction becomes y = (1/4) H16 diag(s) x, H16 the Sylvester Hadamard
+// matrix and s the caller's 16 signs (bit i of the mask set: s_i = -1), in
+// float32: the sign flips, a four-stage butterfly (stage d = 1, 2, 4, 8 replaces
+// (y[i], y[i + d]) by (y[i] + y[i + d], y[i] - y[i + d]) for the i with bit d
+// clear), then the exact product by 1/4.  The group amax is taken over the
+// transformed values (their float32 magnitude bits, an order-preserving key for
+// non-negative floats), and the cast quantizes the transformed values with the
+// per-tensor float32 steps.  Both passes transform each block in registers from
+// its 32 bytes; nothing transformed is written back.
+
+namespace {
+
+__device__ __forceinline__ void rht16(const uint4& a, const uint4& b, uint32_t mask,
+                                      float (&y)[16]) {
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    y[2 * i] = bf16_to_f32(w[i] & 0xffffu);
+    y[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i)  // sign flip: exact
+    y[i] = __uint_as_float(__float_as_uint(y[i]) ^ (((mask >> i) & 1u) << 31));
+#pragma unroll
+  for (int d = 1; d < 16; d <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if ((i & d) == 0) {
+        const float u = y[i], v = y[i + d];
+        y[i] = u + v;
+        y[i + d] = u - v;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) y[i] *= 0.25f;
+}
+
+// Largest magnitude of 16 floats, as the float32 bits of it.
+__device__ __forceinline__ uint32_t fmag_bits(const float (&y)[16]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m = max(m, __float_as_uint(y[i]) & 0x7fffffffu);
+  return m;
+}
+
+// 8 floats times enc -> 8 E2M1 nibbles in one dword (element 2j low nibble of byte j).
+__device__ __forceinline__ uint32_t fp4_pack8f(const float* y, float enc) {
+  uint32_t r = 0;
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[0] * enc, y[1] * enc, 1.0f, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[2] * enc, y[3] * enc, 1.0f, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[4] * enc, y[5] * enc, 1.0f, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[6] * enc, y[7] * enc, 1.0f, 3);
+  return r;
+}
+
+// E4M3 scale code and encode factor of a block with largest magnitude bmax
+// under the group's S (the per-tensor float32 steps).
+__device__ __forceinline__ void nv_scale_enc(float bmax, float S, uint32_t& s8, float& enc) {
+  float sf = (bmax / 6.0f) * S;
+  sf = __builtin_fminf(sf, 448.0f);
+  s8 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sf, 0.0f, 0, false) & 0xffu;
+  const float sd = e4m3_decode_pos(s8);
+  enc = 0.0f;
+  if (sd != 0.0f) enc = __builtin_fminf(S / sd, 3.40282346638528859812e+38f);
+}
+
+constexpr int kRhtBatch = 4;  // blocks (32 bytes each) in flight per thread
+
+}  // namespace
+
+// The group amax pass over transformed blocks: as nvfp4_group_amax_kernel, with
+// 16-element blocks (two 16-byte loads) in place of 16-byte chunks.
+__global__ __launch_bounds__(kAmaxThreads) void nvfp4_group_amax_rht_kernel(
+    const uint16_t* __restrict__ x, int64_t rows_cap, int64_t cols, int G,
+    const int64_t* __restrict__ offsets, uint32_t mask, uint32_t* __restrict__ amax_bits,
+    uint32_t* status) {
+  __shared__ int64_t s_off[kMaxGroups + 1];
+  __shared__ uint32_t s_max[kMaxGroups];
+  const int tid = threadIdx.x;
+  for (int g = tid; g < G; g += kAmaxThreads) s_max[g] = 0u;
+  load_offsets_clamped(offsets, G, rows_cap, s_off, blockIdx.x == 0 ? status : nullptr);
+  const int64_t bpr = cols / 16;  // 16-element blocks per row
+  const int64_t first = s_off[0] * bpr, total = s_off[G] * bpr;
+  const int64_t span = total > first ? total - first : 0;
+  const int64_t per = (span + gridDim.x - 1) / gridDim.x;
+  const int64_t c0 = first + (int64_t)blockIdx.x * per;
+  const int64_t c1 = c0 + per < total ? c0 + per : total;
+  int64_t c = c0 + tid;
+  if (c < c1) {
+    const int64_t row = c / bpr;
+    int g = 0, hi = G - 1;  // the largest g with s_off[g] <= row
+    while (g < hi) {
+      const int mid = (g + hi + 1) >> 1;
+      if (s_off[mid] <= row) g = mid; else hi = mid - 1;
+    }
+    int64_t bound = s_off[g + 1] * bpr;  // first block past group g
+    const uint4* __restrict__ xv = reinterpret_cast<const uint4*>(x);
+    uint32_t m = 0;
+    for (; c < c1; c += kRhtBatch * kAmaxThreads) {
+      uint4 v[kRhtBatch][2];  // the batch's loads are all issued before any is used
+#pragma unroll
+      for (int k = 0; k < kRhtBatch; ++k) {
+        const int64_t ck = c + (int64_t)k * kAmaxThreads;
+        v[k][0] = ck < c1 ? xv[2 * ck] : make_uint4(0, 0, 0, 0);
+        v[k][1] = ck < c1 ? xv[2 * ck + 1] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int k = 0; k < kRhtBatch; ++k) {
+        const int64_t ck = c + (int64_t)k * kAmaxThreads;
+        if (ck >= c1) break;
+        if (ck >= bound) {
+          atomicMax(&s_max[g], m);
+          m = 0;
+          while (g < G - 1 && s_off[g + 1] * bpr <= ck) ++g;
+          bound = s_off[g + 1] * bpr;
+        }
+        float y[16];
+        rht16(v[k][0], v[k][1], mask, y);
+        m = max(m, fmag_bits(y));
+      }
+    }
+    atomicMax(&s_max[g], m);
+  }
+  __syncthreads();
+  for (int g = tid; g < G; g += kAmaxThreads)
+    if (s_max[g] != 0u) atomicMax(&amax_bits[g], s_max[g]);
+}
+
+// The cast of transformed rows: one 256-thread block per live row, each thread
+// transforming up to four 16-element blocks in registers (LONG: the blocks past
+// them are read and transformed again); the row's group amax as in the plain
+// per-tensor cast; rows that no group owns are left untouched.
+template <bool LONG>
+__global__ __launch_bounds__(kNvThreads) void nvfp4_pertensor_rht_kernel(
+    const uint16_t* __restrict__ x, int64_t rows_cap, int64_t cols, int G,
+    const int64_t* __restrict__ offsets, uint32_t mask, uint8_t* __restrict__ data,
+    uint8_t* __restrict__ bscales, const float* __restrict__ group_amax) {
+  __shared__ uint32_t s_grp[2];
+  int64_t live = offsets[G];
+  if (live < 0) live = 0;
+  if (live > rows_cap) live = rows_cap;
+  const int64_t row = blockIdx.x;
+  if (row >= live) return;
+  const int tid = threadIdx.x;
+  const int64_t nblk = cols / 16;
+  const uint16_t* xr = x + row * cols;
+  uint8_t* drow = data + row * (cols / 2);
+  uint8_t* srow = bscales + row * nblk;
+  constexpr int64_t kRegBlocks = (int64_t)kNvMaxBlocksPerThread * kNvThreads;
+
+  float y[kNvMaxBlocksPerThread][16];
+  uint32_t bm[kNvMaxBlocksPerThread];
+#pragma unroll
+  for (int i = 0; i < kNvMaxBlocksPerThread; ++i) {
+    const int64_t j = tid + (int64_t)kNvThreads * i;
+    bm[i] = 0;
+    if (j < nblk) {
+      const uint4 a = load_stream16(xr + 16 * j), b = load_stream16(xr + 16 * j + 8);
+      rht16(a, b, mask, y[i]);
+      bm[i] = fmag_bits(y[i]);
+    }
+  }
+  // the row's group amax in one round trip (see nvfp4_rowscaled_kernel)
+  bool mine = false;
+  uint32_t val = 0u;
+  if (tid < G) {
+    const int64_t lo = offsets[tid], hi = offsets[tid + 1];
+    val = __float_as_uint(group_amax[tid]);
+    mine = lo <= row && row < hi;
+  }
+  if (tid == 0) {
+    s_grp[0] = 0u;
+    s_grp[1] = 0u;
+  }
+  __syncthreads();
+  if (mine) {
+    s_grp[0] = val;
+    s_grp[1] = 1u;
+  }
+  __syncthreads();
+  if (s_grp[1] == 0u) return;  // uniform: no group owns this row
+  const float amax = __uint_as_float(s_grp[0]);
+  float S = amax > 0.0f ? 2688.0f / amax : 1.0f;
+  S = __builtin_fminf(S, 3.40282346638528859812e+38f);
+#pragma unroll
+  for (int i = 0; i < kNvMaxBlocksPerThread; ++i) {
+    const int64_t j = tid + (int64_t)kNvThreads * i;
+    if (j < nblk) {
+      uint32_t s8;
+      float enc;
+      nv_scale_enc(__uint_as_float(bm[i]), S, s8, enc);
+      *reinterpret_cast<uint2*>(drow + 8 * j) =
+          make_uint2(fp4_pack8f(&y[i][0], enc), fp4_pack8f(&y[i][8], enc));
+      srow[j] = (uint8_t)s8;
+    }
+  }
+  if constexpr (LONG) {
+    for (int64_t j = kRegBlocks + tid; j < nblk; j += kNvThreads) {
+      const uint4* p = reinterpret_cast<const uint4*>(xr + 16 * j);
+      float t[16];
+      rht16(p[0], p[1], mask, t);
+      uint32_t s8;
+      float enc;
+      nv_scale_enc(__uint_as_float(fmag_bits(t)), S, s8, enc);
+      *reinterpret_cast<uint2*>(drow + 8 * j) = make_uint2(fp4_pack8f(&t[0], enc),
+                                                           fp4_pack8f(&t[8], enc));
+      srow[j] = (uint8_t)s8;
+    }
+  }
+}
+
+hipError_t launch_quantize_nvfp4_pertensor_rht(const uint16_t* x, int64_t rows_cap, int64_t cols,
+                                               int G, const int64_t* offsets, uint32_t sign_mask,
+                                               uint8_t* data, uint8_t* block_scales, float* amax,
+                                               uint32_t* status, hipStream_t stream) {
+  uint32_t* bits = reinterpret_cast<uint32_t*>(amax);
+  hipLaunchKernelGGL(nvfp4_amax_clear_kernel, dim3(1), dim3(256), 0, stream, bits, G);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || rows_cap == 0) return e;
+  const int64_t nb = rows_cap * (cols / 16);
+  int64_t blocks = (nb + kRhtBatch * kAmaxThreads - 1) / (kRhtBatch * kAmaxThreads);
+  const int64_t most = (int64_t)device_cu_count() * kAmaxBlocksPerCu;
+  if (blocks > most) blocks = most;
+  hipLaunchKernelGGL(nvfp4_group_amax_rht_kernel, dim3((unsigned)blocks), dim3(kAmaxThreads), 0,
+                     stream, x, rows_cap, cols, G, offsets, sign_mask, bits, status);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (nv_long_rows(cols))
+    hipLaunchKernelGGL(nvfp4_pertensor_rht_kernel<true>, dim3((unsigned)rows_cap),
+                       dim3(kNvThreads), 0, stream, x, rows_cap, cols, G, offsets, sign_mask,
+                       data, block_scales, amax);
+  else
+    hipLaunchKernelGGL(nvfp4_pertensor_rht_kernel<false>, dim3((unsigned)rows_cap),
+                       dim3(kNvThreads), 0, stream, x, rows_cap, cols, G, offsets, sign_mask,
+                       data, block_scales, amax);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- per tensor, 2-D scales
+//
+// Per-tensor NVFP4 with one E4M3 scale per 16 x 16 block ("gemm.py",
+// _jax_scaled_matmul: the NVFP4_2D_SCALING mode; 16 rows by 16 columns, the
+// NVFP4 block in both directions, so a tensor and its transpose quantize to
+// transposed codes).  Block rows start at each group's first row (a group's
+// last one holds its remaining rows).  The group amax comes from the same pass
+// as the 1-D per-tensor quantize; then one workgroup per (group, block row):
+// thread t takes block columns t, t + 256, ..., holds the block's 16 rows of 32
+// bytes in registers, takes the block maximum, and writes the 16 rows' codes
+// and the block's scale byte in every row of it (the GEMM's per-row layout).
+
+__global__ __launch_bounds__(kNvThreads) void nvfp4_pertensor_2d_kernel(
+    const uint16_t* __restrict__ x, int64_t rows_cap, int64_t cols, int G,
+    const int64_t* __restrict__ offsets, uint8_t* __restrict__ data,
+    uint8_t* __restrict__ bscales, const float* __restrict__ group_amax) {
+  __shared__ int64_t s_off[kMaxGroups + 1];
+  __shared__ int32_t s_cnt[kMaxGroups];
+  __shared__ int32_t s_pre[kMaxGroups + 1];
+  load_offsets_clamped(offsets, G, rows_cap, s_off, nullptr);
+  for (int g = threadIdx.x; g < G; g += blockDim.x)
+    s_cnt[g] = (int32_t)((group_extent(s_off, g) + 15) / 16);
+  __syncthreads();
+  wave0_exclusive_scan(s_cnt, G, s_pre);
+  __syncthreads();
+  const int unit = blockIdx.x;
+  if (unit >= s_pre[G]) return;
+  const int g = find_group(s_pre, G, unit);
+  const int64_t r0 = s_off[g] + 16 * (int64_t)(unit - s_pre[g]);
+  const int64_t rest = s_off[g + 1] - r0;
+  const int nr = (int)(rest < 16 ? rest : 16);
+  const float amax = group_amax[g];
+  float S = amax > 0.0f ? 2688.0f / amax : 1.0f;
+  S = __builtin_fminf(S, 3.40282346638528859812e+38f);
+  const int64_t nblk = cols / 16;
+  for (int64_t j = threadIdx.x; j < nblk; j += kNvThreads) {
+    uint4 v[16][2];
+    uint32_t bm = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      v[r][0] = v[r][1] = make_uint4(0, 0, 0, 0);
+      if (r < nr) {
+        const uint16_t* p = x + (r0 + r) * cols + 16 * j;
+        v[r][0] = load_stream16(p);
+        v[r][1] = load_stream16(p + 8);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) bm = max(bm, block_mag(v[r][0], v[r][1]));
+    uint32_t s8;
+    float enc;
+    nv_scale_enc(bf16_to_f32(bm), S, s8, enc);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if (r < nr) {
+        *reinterpret_cast<uint2*>(data + (r0 + r) * (cols / 2) + 8 * j) =
+            make_uint2(fp4_pack8(v[r][0], enc), fp4_pack8(v[r][1], enc));
+        bscales[(r0 + r) * nblk + j] = (uint8_t)s8;
+      }
+    }
+  }
+}
+
+hipError_t launch_quantize_nvfp4_pertensor_2d(const uint16_t* x, int64_t rows_cap, int64_t cols,
+                                              int G, const int64_t* offsets, uint8_t* data,
+                                              uint8_t* block_scales, float* amax, uint32_t* status,
+                                              hipStream_t stream) {
+  uint32_t* bits = reinterpret_cast<uint32_t*>(amax);
+  hipLaunchKernelGGL(nvfp4_amax_clear_kernel, dim3(1), dim3(256), 0, stream, bits, G);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || rows_cap == 0) return e;
+  const int64_t chunks = rows_cap * (cols / 8);
+  int64_t blocks = (chunks + kAmaxBatch * kAmaxThreads - 1) / (kAmaxBatch * kAmaxThreads);
+  const int64_t most = (int64_t)device_cu_count() * kAmaxBlocksPerCu;
+  if (blocks > most) blocks = most;
+  hipLaunchKernelGGL(nvfp4_group_amax_kernel, dim3((unsigned)blocks), dim3(kAmaxThreads), 0, stream,
+                     x, rows_cap, cols, G, offsets, bits, status);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // upper bound of the block rows: every group adds at most one partial one
+  const int64_t units = rows_cap / 16 + G;
+  hipLaunchKernelGGL(nvfp4_pertensor_2d_kernel, dim3((unsigned)units), dim3(kNvThreads), 0, stream,
+                     x, rows_cap, cols, G, offsets, data, block_scales, amax);
   return hipGetLastError();
 }
 

@@ -190,6 +190,53 @@ int grouped_quantize_nvfp4_pertensor(const void* x, int64_t rows_cap, int64_t co
                                      float* amax, uint32_t* dev_status, void* stream);
 
 /*
+ * grouped_quantize_nvfp4_pertensor_rht
+ *
+ * grouped_quantize_nvfp4_pertensor of the rows' randomized Hadamard transform
+ * along the contraction ("gemm.py", _quantize_gemm_operands: with NVFP4 1-D
+ * scaling, if one GEMM operand is quantized with RHT the other must be too,
+ * so that the transform cancels in the GEMM; quantize both operands with the
+ * same mask and multiply them with grouped_gemm_nvfp4_pertensor).  Every
+ * 16-element block x of a row becomes y = (1/4) H16 diag(s) x -- H16 the
+ * 16 x 16 Sylvester Hadamard matrix, s_i = -1 where bit i of rht_sign_mask is
+ * set -- computed in float32 as: sign flips, a butterfly of four stages d = 1,
+ * 2, 4, 8 (each replacing (y[i], y[i + d]) by (y[i] + y[i + d], y[i] - y[i + d])
+ * for the i with bit d clear), the exact product by 1/4.  amax[g] is the
+ * largest transformed magnitude of group g; the cast then follows
+ * grouped_quantize_nvfp4_pertensor's float32 steps on the transformed values.
+ * (The pages give neither the size nor the signs of the transform: 16, the
+ * NVFP4 block, and caller-chosen signs are this library's reading.)
+ *
+ *   rht_sign_mask  [host] the 16 signs, bits 0..15 (higher bits: BSG_ERR_SHAPE).
+ *   Other arguments, outputs and errors as grouped_quantize_nvfp4_pertensor.
+ */
+int grouped_quantize_nvfp4_pertensor_rht(const void* x, int64_t rows_cap, int64_t cols, int64_t G,
+                                         const int64_t* offsets, uint32_t rht_sign_mask,
+                                         uint8_t* data, uint8_t* block_scales, float* amax,
+                                         uint32_t* dev_status, void* stream);
+
+/*
+ * grouped_quantize_nvfp4_pertensor_2d
+ *
+ * Per-tensor NVFP4 with 2-D block scales ("gemm.py", _jax_scaled_matmul accepts
+ * an NVFP4_2D_SCALING mode): one E4M3 scale per 16 x 16 block -- 16 rows by 16
+ * columns, so a tensor and its transpose quantize to transposed codes -- whose
+ * maximum is taken over the whole block, with the float32 steps of
+ * grouped_quantize_nvfp4_pertensor (S_g from the group's amax).  Block rows
+ * start at each group's first row; a group's last block row holds its
+ * remaining rows.  block_scales keeps the per-row layout [rows_cap, cols/16]:
+ * each row of a block row carries its block's scale byte, so
+ * grouped_gemm_nvfp4_pertensor consumes the outputs unchanged.  (The pages give
+ * no block shape: 16 x 16 is this library's reading.)
+ *
+ *   Arguments, outputs and errors as grouped_quantize_nvfp4_pertensor.
+ */
+int grouped_quantize_nvfp4_pertensor_2d(const void* x, int64_t rows_cap, int64_t cols, int64_t G,
+                                        const int64_t* offsets, uint8_t* data,
+                                        uint8_t* block_scales, float* amax, uint32_t* dev_status,
+                                        void* stream);
+
+/*
  * grouped_quantize_nvfp4_rowscaled_colwise
  *
  * Columnwise (transposed) row-scaled NVFP4 copies for the weight gradient

@@ -16,6 +16,7 @@ from oracle import formats as F
 from oracle import gemm as GM
 from oracle import offsets as O
 from oracle import quantize as Q
+from oracle import rht as R
 import workloads
 from gpu_util import bf16_out_to_f64, device, gemm_tolerance_check, host_u8
 
@@ -256,14 +257,18 @@ def test_full_dgrad():
     assert not np.isnan(y[:int(off[-1])]).any(), "every live output row written"
 
 
-def test_full_nvfp4_pertensor():
+@pytest.mark.parametrize("flow", ["nvfp4_pertensor", "nvfp4_rht", "nvfp4_2d"])
+def test_full_nvfp4_pertensor(flow):
     """Per-tensor NVFP4: 8 experts, 16384 live rows of 18432, K=4096, N_e in
     {2048, 4096}; each expert's activations and each expert's weight carry one
-    amax.  The amax is checked against a plain max over the whole group; the
-    sampled rows are quantized by the oracle together with one added row that
-    holds the group's amax, so the oracle sees the same tensor scale."""
+    amax.  The amax is checked against a plain max over the whole group (of
+    the transformed rows with RHT); the sampled rows are quantized by the
+    oracle together with one added row that holds the group's amax, so the
+    oracle sees the same tensor scale.  "nvfp4_rht": both operands through the
+    randomized Hadamard transform (same signs); "nvfp4_2d": weights with 16 x
+    16 block scales, sampled by whole block rows."""
     dev = device()
-    case = bench.make_case("nvfp4_pertensor", dev)
+    case = bench.make_case(flow, dev)
     case.y.fill_(float("nan"))
     case.step()
     torch.cuda.synchronize()
@@ -272,11 +277,19 @@ def test_full_nvfp4_pertensor():
     _, off = O.group_offsets(w.sizes)
     boff = np.concatenate([[0], np.cumsum(npg)])
     xa, wa = case.xa.cpu().numpy(), case.wa.cpu().numpy()
+    rht = flow == "nvfp4_rht"
+    mask = case.rht_mask
+
+    def values(t, lo, hi):
+        v = t[lo:hi].float()
+        if rht:   # the transform of whole rows, in the oracle's float32 steps
+            v = torch.from_numpy(R.rht16(v.cpu().numpy(), mask))
+        return v
 
     def group_amax(t, lo, hi):
         if hi <= lo:
             return np.float32(0)
-        return np.float32(t[lo:hi].abs().max().float().item())
+        return np.float32(values(t, lo, hi).abs().max().item())
 
     for g in range(G):
         assert xa[g] == group_amax(case.x, int(off[g]), int(off[g + 1])), g
@@ -284,10 +297,17 @@ def test_full_nvfp4_pertensor():
 
     def quantize_sample(t, rows, amax):
         xb = workloads.bf16_bits(t[torch.from_numpy(rows).to(dev)])
-        extra = np.zeros((1, K), np.float32)
-        extra[0, 0] = amax
-        xb = np.concatenate([xb, F.f32_to_bf16_bits_rne(extra)])
-        p, s, a = Q.nvfp4_pertensor(xb, np.array([0, len(rows) + 1]))
+        if rht:
+            v = R.rht16(F.bf16_bits_to_f64(xb).astype(np.float32), mask)
+            extra = np.zeros((1, K), np.float32)
+            extra[0, 0] = amax
+            p, s, a = Q.nvfp4_pertensor_values(np.concatenate([v, extra]),
+                                               np.array([0, len(rows) + 1]))
+        else:
+            extra = np.zeros((1, K), np.float32)
+            extra[0, 0] = amax
+            xb = np.concatenate([xb, F.f32_to_bf16_bits_rne(extra)])
+            p, s, a = Q.nvfp4_pertensor(xb, np.array([0, len(rows) + 1]))
         assert a[0] == amax
         return p[:-1], s[:-1]
 
@@ -300,13 +320,39 @@ def test_full_nvfp4_pertensor():
         sel = rows[grp == g]
         ap, asc = quantize_sample(case.x, sel, xa[g])
         assert np.array_equal(gd[sel], ap) and np.array_equal(gs[sel], asc)
-        cols = np.unique(np.concatenate([[0, npg[g] - 1], rng.integers(0, npg[g], 24)]))
-        bp, bsc = quantize_sample(case.wt, boff[g] + cols, wa[g])
-        assert np.array_equal(gwd[boff[g] + cols], bp) and np.array_equal(gws[boff[g] + cols], bsc)
+        if flow == "nvfp4_2d":
+            # two whole block rows of the expert's weight (16 output columns each)
+            nbr = (npg[g] + 15) // 16
+            brs = np.unique(np.array([0, nbr - 1, int(rng.integers(0, nbr))]))
+            cols = np.concatenate([np.arange(16 * b, min(16 * b + 16, npg[g])) for b in brs])
+            wrows = boff[g] + cols
+            # the oracle's 2-D quantize of each sampled block row, after a block
+            # row whose only nonzero is the expert's amax (so S is the expert's)
+            pieces = []
+            for b in brs:
+                r = boff[g] + np.arange(16 * b, min(16 * b + 16, npg[g]))
+                blk = F.bf16_bits_to_f64(workloads.bf16_bits(case.wt[torch.from_numpy(r).to(dev)]))
+                pieces.append(blk)
+            bp_list, bs_list = [], []
+            for blk in pieces:
+                v = blk.astype(np.float32)
+                extra = np.zeros((16, K), np.float32)
+                extra[0, 0] = wa[g]
+                p, s, a = Q.nvfp4_pertensor_2d(
+                    F.f32_to_bf16_bits_rne(np.concatenate([extra, v])), np.array([0, 16 + len(v)]))
+                assert a[0] == wa[g]
+                bp_list.append(p[16:])
+                bs_list.append(s[16:])
+            bp, bsc = np.concatenate(bp_list), np.concatenate(bs_list)
+        else:
+            cols = np.unique(np.concatenate([[0, npg[g] - 1], rng.integers(0, npg[g], 24)]))
+            wrows = boff[g] + cols
+            bp, bsc = quantize_sample(case.wt, wrows, wa[g])
+        assert np.array_equal(gwd[wrows], bp) and np.array_equal(gws[wrows], bsc)
         one = np.array([0, len(sel)])
         aam, bam = np.array([xa[g]], np.float32), np.array([wa[g]], np.float32)
         (_, ref), = GM.nvfp4_pertensor_fprop(ap, asc, aam, one, bp, bsc, bam, [len(cols)], K)
-        gemm_tolerance_check(y[sel][:, cols], ref, False, "nvfp4 per-tensor group %d" % g)
+        gemm_tolerance_check(y[sel][:, cols], ref, False, "%s group %d" % (flow, g))
         if npg[g] < case.ld:
             assert np.isnan(y[sel][:, npg[g]:]).all(), "columns past N_g untouched"
     live = int(off[-1])
