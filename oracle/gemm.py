@@ -52,10 +52,12 @@ def mxfp8_fprop(a_data, a_scales, b_data, b_scales, offsets, k, rows=None):
 
 
 def mxfp8_wgrad(dy_col, dy_col_scales, x_col, x_col_scales, padded_offsets, n, k, groups=None,
-                out_rows=None):
+                out_rows=None, elem_a="e4m3"):
     """WGRAD (NT, ragged contraction; "gemm.py", ``grouped_gemm`` with rhs first
     dims ragged, uniform (G, ...) output):
         dW[g, i, j] = sum_{t < m_g} dq(dY)[off[g] + t, i] * dq(X)[off[g] + t, j]
+    with dY's elements E4M3, or E5M2 (``elem_a``; an E5M2 gradient times E4M3
+    activations, a pairing ``_compatible_fp8_gemm_dtypes`` accepts)
 
     taken from the columnwise copies (group g: dY^T block [n, m~_g], X^T block
     [k, m~_g], zero padding beyond m_g; scales [m~_g/128, n or k, 4] words).  An empty group gives dW[g] = 0.
@@ -77,7 +79,7 @@ def mxfp8_wgrad(dy_col, dy_col_scales, x_col, x_col_scales, padded_offsets, n, k
         b = np.asarray(x_col[poff[g] * k:poff[g + 1] * k]).reshape(k, mp)
         b_s = np.asarray(x_col_scales[poff[g] * k // MX_BLOCK:poff[g + 1] * k // MX_BLOCK]
                          ).reshape(nq, k, 4)
-        out[gi] = mxfp8_dequant_rows(a, a_s, mp) @ mxfp8_dequant_rows(b, b_s, mp).T
+        out[gi] = mxfp8_dequant_rows(a, a_s, mp, elem=elem_a) @ mxfp8_dequant_rows(b, b_s, mp).T
     return out
 
 

@@ -59,10 +59,11 @@ def mxfp8_rowwise(x_bits, offsets, elem="e4m3"):
     return codes.reshape(live, cols), mx_scales_to_gemm_order(sbyte)
 
 
-def mxfp8_colwise(x_bits, offsets, padded_offsets):
+def mxfp8_colwise(x_bits, offsets, padded_offsets, elem="e4m3"):
     """Columnwise MXFP8 quantize for a contraction over ragged token rows
     (wgrad): per group g and column c, 32-token blocks starting at the group's
-    first row, written transposed.
+    first row, written transposed; elements E4M3, or E5M2 for a gradient
+    ("gemm.py", ``_compatible_fp8_gemm_dtypes`` pairs E5M2 with E4M3).
 
     Reading: a group's token count is padded to a multiple of 128 with zero
     values (so padding encodes to 0x00 and all-padding blocks get scale 0x00),
@@ -91,7 +92,7 @@ def mxfp8_colwise(x_bits, offsets, padded_offsets):
             continue
         xt = np.zeros((cols, mp), dtype=np.float64)
         xt[:, :m] = bf16_bits_to_f64(x_bits[off[g]:off[g + 1]]).T
-        codes, sbyte = _mx_encode_blocks(xt.reshape(cols, mp // MX_BLOCK, MX_BLOCK))
+        codes, sbyte = _mx_encode_blocks(xt.reshape(cols, mp // MX_BLOCK, MX_BLOCK), elem)
         data[poff[g] * cols:poff[g + 1] * cols] = codes.reshape(-1)
         scales[poff[g] * cols // MX_BLOCK:poff[g + 1] * cols // MX_BLOCK] = \
             mx_scales_to_gemm_order(sbyte).reshape(-1)

@@ -41,7 +41,10 @@ def test_fprop_exact_on_lossless_inputs():
         assert np.array_equal(y[off[g]:off[g + 1]], want.astype(np.float64))
 
 
-def test_wgrad_exact_on_lossless_inputs():
+@pytest.mark.parametrize("elem", ["e4m3", "e5m2"])
+def test_wgrad_exact_on_lossless_inputs(elem):
+    """Small integers are exact in E4M3 and E5M2 under any MX scale: dW must be
+    the exact per-expert integer product, whichever element format dY uses."""
     rng = np.random.default_rng(22)
     sizes = np.array([37, 0, 130, 5], np.int32)
     M, N, K = int(sizes.sum()), 40, 64
@@ -49,9 +52,9 @@ def test_wgrad_exact_on_lossless_inputs():
     xb, xi = _int_bits(rng, (M, K))
     _, off = O.group_offsets(sizes)
     _, poff = O.group_offsets(sizes, pad_to=128)
-    dyc, dys = Q.mxfp8_colwise(dyb, off, poff)
+    dyc, dys = Q.mxfp8_colwise(dyb, off, poff, elem=elem)
     xc, xs = Q.mxfp8_colwise(xb, off, poff)
-    dw = GM.mxfp8_wgrad(dyc, dys, xc, xs, poff, N, K)
+    dw = GM.mxfp8_wgrad(dyc, dys, xc, xs, poff, N, K, elem_a=elem)
     for g in range(4):
         want = dyi[off[g]:off[g + 1]].T @ xi[off[g]:off[g + 1]]
         assert np.array_equal(dw[g], want.astype(np.float64)), g
@@ -249,6 +252,44 @@ def test_dgrad_e5m2_rounding_is_visible():
     bound = np.abs(dyv) @ np.abs(wv) * (2.0 ** -3 + 2.0 ** -4 + 2.0 ** -7)
     assert np.all(np.abs(dx - exact) <= bound)
     assert np.abs(dx - exact).max() > 0          # the gradient really is E5M2
+
+
+def test_wgrad_e5m2_rounding_is_visible():
+    """The E5M2 wgrad equals the product of dY's E5M2 codes decoded by their
+    bit fields (sign, 5 exponent bits with bias 15, 2 mantissa bits) times the
+    block scales read from the words by hand, and differs from the E4M3 wgrad
+    (values with more significant bits than E5M2 keeps)."""
+    rng = np.random.default_rng(27)
+    sizes = np.array([64, 40], np.int32)
+    M, N, K = int(sizes.sum()), 32, 32
+    dyb = F.f32_to_bf16_bits_rne(rng.standard_normal((M, N)).astype(np.float32))
+    xb, xi = _int_bits(rng, (M, K))
+    _, off = O.group_offsets(sizes)
+    _, poff = O.group_offsets(sizes, pad_to=128)
+    c5, s5 = Q.mxfp8_colwise(dyb, off, poff, elem="e5m2")
+    c4, s4 = Q.mxfp8_colwise(dyb, off, poff)
+    xc, xs = Q.mxfp8_colwise(xb, off, poff)
+    dw5 = GM.mxfp8_wgrad(c5, s5, xc, xs, poff, N, K, elem_a="e5m2")
+    dw4 = GM.mxfp8_wgrad(c4, s4, xc, xs, poff, N, K)
+    for g in range(2):
+        mp = int(poff[g + 1] - poff[g])
+        codes = c5[poff[g] * N:poff[g + 1] * N].reshape(N, mp)
+        words = s5[poff[g] * N // 32:poff[g + 1] * N // 32].reshape(mp // 128, N, 4)
+        dq = np.zeros((N, mp))
+        for c in range(N):
+            for t in range(mp):
+                code = int(codes[c, t])
+                e, m = (code >> 2) & 31, code & 3
+                v = m / 4 * 2.0 ** -14 if e == 0 else (1 + m / 4) * 2.0 ** (e - 15)
+                if code & 0x80:
+                    v = -v
+                blk = t // 32
+                stored = words[blk // 4, c]              # bytes b0, b2, b1, b3
+                byte = int(stored[[0, 2, 1, 3].index(blk % 4)])
+                dq[c, t] = v * 2.0 ** (byte - 127)
+        want = dq[:, :sizes[g]] @ xi[off[g]:off[g + 1]]
+        assert np.allclose(dw5[g], want, rtol=1e-12, atol=0), g
+        assert not np.allclose(dw5[g], dw4[g])
 
 
 def test_epilogue_exact_on_lossless_inputs():
