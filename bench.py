@@ -121,11 +121,13 @@ class MxFprop(Case):
 
 
 class MxWgrad(Case):
-    """offsets -> columnwise quantize of dY and X -> grouped GEMM wgrad."""
+    """offsets -> columnwise quantize of dY and X -> grouped GEMM wgrad (e5m2:
+    dY's copy in E5M2, the E5M2 x E4M3 product)."""
 
-    def __init__(self, name, dev):
+    def __init__(self, name, dev, e5m2=False):
         self.name = name
-        self.w = w = workloads.get(name)
+        self.e5m2 = e5m2
+        self.w = w = workloads.get("wgrad" if e5m2 else name)
         t = workloads.tensors(w, device=dev)
         self.dy, self.x = t["dy"], t["x"]
         G, N, K, R = w.G, w.n, w.k, w.rows_cap
@@ -152,14 +154,21 @@ class MxWgrad(Case):
         bsg.group_offsets_i32_to_i64(self.sizes, offsets=self.off, capacity=self.R)
         bsg.group_offsets_i32_to_i64(self.sizes, pad_to=128, offsets=self.poff)
         self._rec(ev, 1)
-        bsg.grouped_quantize_mxfp8(self.dy, self.off, rowwise=False, padded_offsets=self.poff,
-                                   col_rows_cap=self.cap, col_data=self.dyc, col_scales=self.dycs)
+        if self.e5m2:
+            bsg.grouped_quantize_mxfp8_colwise_e5m2(self.dy, self.off, self.poff,
+                                                    col_rows_cap=self.cap, col_data=self.dyc,
+                                                    col_scales=self.dycs)
+        else:
+            bsg.grouped_quantize_mxfp8(self.dy, self.off, rowwise=False, padded_offsets=self.poff,
+                                       col_rows_cap=self.cap, col_data=self.dyc,
+                                       col_scales=self.dycs)
         self._rec(ev, 2)
         bsg.grouped_quantize_mxfp8(self.x, self.off, rowwise=False, padded_offsets=self.poff,
                                    col_rows_cap=self.cap, col_data=self.xc, col_scales=self.xcs)
         self._rec(ev, 3)
-        bsg.grouped_gemm_mxfp8(bsg.BSG_WGRAD_NT, self.dyc, self.dycs, self.xc, self.xcs, self.poff,
-                               self.cap, self.N, self.K, out=self.dw, out_dtype=bsg.BSG_OUT_BF16)
+        bsg.grouped_gemm_mxfp8(bsg.BSG_WGRAD_NT_E5M2 if self.e5m2 else bsg.BSG_WGRAD_NT, self.dyc,
+                               self.dycs, self.xc, self.xcs, self.poff, self.cap, self.N, self.K,
+                               out=self.dw, out_dtype=bsg.BSG_OUT_BF16)
         self._rec(ev, 4)
 
 
@@ -381,6 +390,8 @@ def make_case(name, dev):
         return MxFprop(name, dev, with_colwise=True)
     if name == "wgrad":
         return MxWgrad(name, dev)
+    if name == "wgrad_e5m2":
+        return MxWgrad(name, dev, e5m2=True)
     if name == "nvfp4":
         return Nvfp4Fprop(name, dev)
     if name == "nvfp4_scratch":
@@ -750,7 +761,8 @@ def main():
         log("[bench] copy calibration: 3 x 268435456 bytes read + written")
         del src, dst
 
-    names = ["fprop"] if args.no_extra else ["fprop", "tiny", "wgrad", "zipf", "dgrad", "nvfp4",
+    names = ["fprop"] if args.no_extra else ["fprop", "tiny", "wgrad", "wgrad_e5m2", "zipf", "dgrad",
+                                             "nvfp4",
                                              "nvfp4_scratch", "nvfp4_wgrad", "nvfp4_pertensor",
                                              "nvfp4_rht", "nvfp4_2d"]
     if args.only:

@@ -19,6 +19,7 @@ BSG_WGRAD_NT = 1
 BSG_OUT_BF16 = 0
 BSG_OUT_F32 = 1
 BSG_DGRAD_NN = 2
+BSG_WGRAD_NT_E5M2 = 3
 BSG_MAX_GROUPS = 256
 BSG_COLWISE_PAD = 128
 DEV_NEGATIVE_SIZE = 1
@@ -32,7 +33,7 @@ EXPORTS = ("bsg_last_error", "bsg_version", "group_offsets_i32_to_i64", "grouped
            "grouped_gemm_mxfp8", "grouped_gemm_mxfp8_ex", "grouped_gemm_nvfp4_rowscaled",
            "grouped_gemm_nvfp4_rowscaled_wgrad", "grouped_gemm_nvfp4_pertensor",
            "grouped_gemm_nvfp4_rowscaled_noalloc", "grouped_quantize_nvfp4_pertensor_rht",
-           "grouped_quantize_nvfp4_pertensor_2d")
+           "grouped_quantize_nvfp4_pertensor_2d", "grouped_quantize_mxfp8_colwise_e5m2")
 BSG_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
@@ -64,6 +65,8 @@ def load_library(path=LIB_PATH):
     lib.grouped_quantize_mxfp8.argtypes = [P, I64, I64, I64, P, P, P, P, I64, P, P, P, P]
     lib.grouped_quantize_mxfp8_rowwise_e5m2.restype = I32
     lib.grouped_quantize_mxfp8_rowwise_e5m2.argtypes = [P, I64, I64, I64, P, P, P, P, P]
+    lib.grouped_quantize_mxfp8_colwise_e5m2.restype = I32
+    lib.grouped_quantize_mxfp8_colwise_e5m2.argtypes = [P, I64, I64, I64, P, P, I64, P, P, P, P]
     lib.grouped_quantize_nvfp4_rowscaled.restype = I32
     lib.grouped_quantize_nvfp4_rowscaled.argtypes = [P, I64, I64, I64, P, P, P, P, P, P]
     lib.grouped_quantize_nvfp4_rowscaled_colwise.restype = I32
@@ -265,6 +268,32 @@ def grouped_quantize_mxfp8_rowwise_e5m2(x, offsets, G=None, row_data=None, row_s
     return row_data, row_scales
 
 
+def grouped_quantize_mxfp8_colwise_e5m2(x, offsets, padded_offsets, G=None, col_rows_cap=None,
+                                        col_data=None, col_scales=None, status=None):
+    """bf16 [rows_cap, cols] gradient -> its E5M2 columnwise copy (col_data,
+    col_scales) in grouped_quantize_mxfp8's columnwise layout."""
+    import torch
+    lib = load_library()
+    rows_cap, cols = _bf16_2d(x)
+    G = offsets.numel() - 1 if G is None else G
+    _req(offsets, "offsets", 8 * (G + 1), torch.int64)
+    _req(padded_offsets, "padded_offsets", 8 * (G + 1), torch.int64)
+    if col_rows_cap is None:
+        col_rows_cap = rows_cap + BSG_COLWISE_PAD * G
+    if col_data is None:
+        col_data = torch.empty(col_rows_cap * cols, dtype=torch.uint8, device=x.device)
+    if col_scales is None:
+        col_scales = torch.empty(col_rows_cap * cols // 32, dtype=torch.uint8, device=x.device)
+    _req(col_data, "col_data", col_rows_cap * cols)
+    _req(col_scales, "col_scales", col_rows_cap * cols // 32)
+    _req(status, "status", 4, optional=True)
+    _check(lib.grouped_quantize_mxfp8_colwise_e5m2(_ptr(x), rows_cap, cols, G, _ptr(offsets),
+                                                   _ptr(padded_offsets), col_rows_cap,
+                                                   _ptr(col_data), _ptr(col_scales), _ptr(status),
+                                                   _stream(x)))
+    return col_data, col_scales
+
+
 def grouped_quantize_nvfp4_rowscaled(x, offsets, G=None, data=None, block_scales=None, outer=None,
                                      status=None):
     """bf16 [rows_cap, cols] -> (E2M1 [rows_cap, cols/2], E4M3 [rows_cap, cols/16], f32 [rows_cap])."""
@@ -392,7 +421,7 @@ def _mx_gemm_bytes(mode, G, rows_cap, n, k):
     if mode == BSG_DGRAD_NN:
         kpad = 128 * nq   # the weights' columnwise copy pads each expert to 128 tokens
         return (rows_cap * k, 4 * nq * rows_cap, G * n * kpad, G * n * kpad // 32, rows_cap * n)
-    if mode == BSG_WGRAD_NT:
+    if mode in (BSG_WGRAD_NT, BSG_WGRAD_NT_E5M2):
         return (rows_cap * n, rows_cap * n // 32, rows_cap * k, rows_cap * k // 32, G * n * k)
     raise ValueError("unknown mode %r" % (mode,))
 
@@ -419,7 +448,7 @@ def grouped_gemm_mxfp8(mode, a, a_scales, b, b_scales, offsets, rows_cap, n, k, 
     G = offsets.numel() - 1 if G is None else G
     if out is None:
         dt = _out_dtype(out_dtype)[0]
-        shape = (G, n, k) if mode == BSG_WGRAD_NT else (rows_cap, n)
+        shape = (G, n, k) if mode in (BSG_WGRAD_NT, BSG_WGRAD_NT_E5M2) else (rows_cap, n)
         out = torch.empty(shape, dtype=dt, device=a.device)
     _mx_gemm_check(mode, G, a, a_scales, b, b_scales, offsets, rows_cap, n, k, out, out_dtype,
                    status)
@@ -442,7 +471,8 @@ def grouped_gemm_mxfp8_ex(mode, a, a_scales, b, b_scales, offsets, rows_cap, n, 
                    status)
     _req(alpha, "alpha", 4 * G, _f32(), optional=True)
     _req(beta, "beta", 4 * G, _f32(), optional=True)
-    _req(bias, "bias", 4 * G * (k if mode == BSG_WGRAD_NT else n), _f32(), optional=True)
+    _req(bias, "bias", 4 * G * (k if mode in (BSG_WGRAD_NT, BSG_WGRAD_NT_E5M2) else n), _f32(),
+         optional=True)
     _check(lib.grouped_gemm_mxfp8_ex(mode, G, _ptr(a), _ptr(a_scales), _ptr(b), _ptr(b_scales),
                                      _ptr(offsets), rows_cap, n, k, _ptr(out), out_dtype,
                                      _ptr(alpha), _ptr(beta), _ptr(bias), _ptr(status),

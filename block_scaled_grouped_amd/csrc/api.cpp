@@ -102,6 +102,32 @@ int grouped_quantize_mxfp8(const void* x, int64_t rows_cap, int64_t cols, int64_
                     fn);
 }
 
+int grouped_quantize_mxfp8_colwise_e5m2(const void* x, int64_t rows_cap, int64_t cols, int64_t G,
+                                        const int64_t* offsets, const int64_t* padded_offsets,
+                                        int64_t col_rows_cap, uint8_t* col_data,
+                                        uint8_t* col_scales, uint32_t* dev_status, void* stream) {
+  const char* fn = "grouped_quantize_mxfp8_colwise_e5m2";
+  if (x == nullptr || offsets == nullptr || padded_offsets == nullptr || col_data == nullptr ||
+      col_scales == nullptr)
+    return fail(BSG_ERR_NULL, "%s: x, offsets, padded_offsets, col_data and col_scales must be non-NULL",
+                fn);
+  if (G < 1 || G > BSG_MAX_GROUPS)
+    return fail(BSG_ERR_SHAPE, "%s: G=%lld outside [1, %d]", fn, (long long)G, BSG_MAX_GROUPS);
+  if (rows_cap < 0 || cols <= 0 || cols % 32 != 0)
+    return fail(BSG_ERR_SHAPE, "%s: need rows_cap >= 0 and cols a positive multiple of 32 (got %lld, %lld)",
+                fn, (long long)rows_cap, (long long)cols);
+  if (col_rows_cap < 0 || col_rows_cap * cols >= ((int64_t)1 << 40))
+    return fail(BSG_ERR_SHAPE, "%s: col_rows_cap=%lld out of range", fn, (long long)col_rows_cap);
+  if (!aligned16(x) || !aligned16(col_data))
+    return fail(BSG_ERR_ALIGN, "%s: x and col_data must be 16-byte aligned", fn);
+  return hip_result(bsg::launch_quantize_mxfp8_colwise(static_cast<const uint16_t*>(x), rows_cap,
+                                                       cols, (int)G, offsets, padded_offsets,
+                                                       col_rows_cap, col_data, col_scales, nullptr,
+                                                       nullptr, dev_status, (hipStream_t)stream,
+                                                       true),
+                    fn);
+}
+
 int grouped_quantize_mxfp8_rowwise_e5m2(const void* x, int64_t rows_cap, int64_t cols, int64_t G,
                                         const int64_t* offsets, uint8_t* row_data,
                                         uint8_t* row_scales, uint32_t* dev_status, void* stream) {
@@ -238,7 +264,8 @@ static int gemm_mxfp8_impl(const char* fn, int mode, int64_t G, const uint8_t* a
   if (a == nullptr || a_scales == nullptr || b == nullptr || b_scales == nullptr || offsets == nullptr ||
       out == nullptr)
     return fail(BSG_ERR_NULL, "%s: operands, scales, offsets and out must be non-NULL", fn);
-  if (mode != BSG_FPROP_TN && mode != BSG_WGRAD_NT && mode != BSG_DGRAD_NN)
+  if (mode != BSG_FPROP_TN && mode != BSG_WGRAD_NT && mode != BSG_DGRAD_NN &&
+      mode != BSG_WGRAD_NT_E5M2)
     return fail(BSG_ERR_UNSUPPORTED, "%s: unknown mode %d", fn, mode);
   if (out_dtype != BSG_OUT_BF16 && out_dtype != BSG_OUT_F32)
     return fail(BSG_ERR_UNSUPPORTED, "%s: unknown out_dtype %d", fn, out_dtype);
@@ -247,7 +274,8 @@ static int gemm_mxfp8_impl(const char* fn, int mode, int64_t G, const uint8_t* a
   if (rows_cap < 0 || n < 1 || k < 1)
     return fail(BSG_ERR_SHAPE, "%s: need rows_cap >= 0, n >= 1, k >= 1", fn);
   const int64_t esz = out_dtype == BSG_OUT_F32 ? 4 : 2;
-  if (mode != BSG_WGRAD_NT) {
+  const bool wgrad = mode == BSG_WGRAD_NT || mode == BSG_WGRAD_NT_E5M2;
+  if (!wgrad) {
     if (k % 32 != 0)
       return fail(BSG_ERR_SHAPE, "%s: FPROP / DGRAD need k %% 32 == 0 (got %lld)", fn, (long long)k);
     const int64_t nq = (k + 127) / 128;  // scale words per row; DGRAD's B rows hold 128 nq bytes
@@ -266,7 +294,7 @@ static int gemm_mxfp8_impl(const char* fn, int mode, int64_t G, const uint8_t* a
     return fail(BSG_ERR_ALIGN, "%s: a and b must be 16-byte aligned; scales and out 4-byte", fn);
   if (!aligned4(alpha) || !aligned4(beta) || !aligned16(bias))
     return fail(BSG_ERR_ALIGN, "%s: alpha and beta must be 4-byte aligned, bias 16-byte", fn);
-  if (bias != nullptr && ((mode == BSG_WGRAD_NT ? k : n) % 4 != 0))
+  if (bias != nullptr && ((wgrad ? k : n) % 4 != 0))
     return fail(BSG_ERR_SHAPE, "%s: a bias needs a multiple of 4 output columns", fn);
   return hip_result(bsg::launch_gemm_mxfp8(mode, (int)G, a, a_scales, b, b_scales, offsets, rows_cap,
                                            n, k, out, out_dtype == BSG_OUT_F32, dev_status,

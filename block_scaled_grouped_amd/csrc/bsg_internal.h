@@ -164,13 +164,14 @@ hipError_t launch_quantize_mxfp8_rowwise(const uint16_t* x, int64_t rows_cap, in
                                          const int64_t* offsets, uint8_t* data, uint8_t* scales,
                                          uint32_t* status, hipStream_t stream, bool e5m2 = false);
 
-// Columnwise (and, if row_data != nullptr, the rowwise output in the same pass).
+// Columnwise (and, if row_data != nullptr, the rowwise output in the same pass);
+// e5m2: E5M2 elements, columnwise only.
 hipError_t launch_quantize_mxfp8_colwise(const uint16_t* x, int64_t rows_cap, int64_t cols, int G,
                                          const int64_t* offsets, const int64_t* padded_offsets,
                                          int64_t col_rows_cap, uint8_t* col_data,
                                          uint8_t* col_scales, uint8_t* row_data,
                                          uint8_t* row_scales, uint32_t* status,
-                                         hipStream_t stream);
+                                         hipStream_t stream, bool e5m2 = false);
 
 hipError_t launch_quantize_nvfp4_rowscaled(const uint16_t* x, int64_t rows_cap, int64_t cols,
                                            int G, const int64_t* offsets, uint8_t* data,

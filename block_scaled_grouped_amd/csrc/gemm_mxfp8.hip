@@ -529,8 +529,10 @@ __device__ __forceinline__ void run_tile(uint32_t lds, const TileDesc& t, int ou
   }
 }
 
+// MODE: 0 FPROP_TN, 1 WGRAD_NT, 2 DGRAD_NN (E5M2 A), 3 WGRAD_NT with an E5M2 A.
 template <int MODE, bool EX>
 __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(MxArgs p) {
+  constexpr bool kWgrad = MODE == 1 || MODE == 3;
   __shared__ __attribute__((aligned(16))) uint8_t lds_ring[kBufs * kBufBytes];
   __shared__ Sched sm;
   const uint32_t lds = lds_offset(lds_ring);
@@ -541,7 +543,7 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(MxArgs p) {
   const int64_t ntn = (p.n + BN - 1) / BN;
   for (int g = tid; g < G; g += kThreads) {
     int64_t c;
-    if (MODE != 1) {
+    if (!kWgrad) {
       c = ((group_extent(sm.off, g) + BM - 1) / BM) * ntn;
     } else {
       const int64_t mp = group_extent(sm.off, g);
@@ -565,7 +567,7 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(MxArgs p) {
     const int local = tile - sm.pre[g];
     TileDesc t;
     int64_t col_first;  // the tile's first output column
-    if (MODE != 1) {
+    if (!kWgrad) {
       const int64_t m = group_extent(sm.off, g);
       const int mtiles = (int)((m + BM - 1) / BM);
       int mt, nt;
@@ -636,7 +638,7 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(MxArgs p) {
     }
     if constexpr (EX) {
       // the group's terms, made provably uniform (g comes from LDS)
-      const int64_t outw = MODE == 1 ? p.k : p.n;  // output columns
+      const int64_t outw = kWgrad ? p.k : p.n;  // output columns
       const int gu = __builtin_amdgcn_readfirstlane(g);
       const float al = p.alpha != nullptr ? p.alpha[gu] : 1.0f;
       const float be = p.beta != nullptr ? p.beta[gu] : 0.0f;
@@ -644,7 +646,7 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(MxArgs p) {
       t.beta = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, be)));
       t.bias = p.bias != nullptr ? p.bias + (int64_t)gu * outw + col_first : nullptr;
     }
-    run_tile<MODE == 2 ? 1 : 0, EX>(lds, t, p.out_f32);
+    run_tile<(MODE == 2 || MODE == 3) ? 1 : 0, EX>(lds, t, p.out_f32);
   }
 }
 
@@ -673,7 +675,7 @@ hipError_t launch_gemm_mxfp8(int mode, int G, const uint8_t* a, const uint8_t* a
   const bool ex = alpha != nullptr || beta != nullptr || bias != nullptr;
   // upper bound of the tile count from host-known shapes
   int64_t bound;
-  if (mode != 1) bound = ((rows_cap + BM - 1) / BM + G) * ((n + BN - 1) / BN);
+  if (mode != 1 && mode != 3) bound = ((rows_cap + BM - 1) / BM + G) * ((n + BN - 1) / BN);
   else bound = (int64_t)G * ((n + BM - 1) / BM) * ((k + BN - 1) / BN);
   int64_t grid = device_cu_count();
   if (bound < grid) grid = bound;
@@ -682,10 +684,12 @@ hipError_t launch_gemm_mxfp8(int mode, int G, const uint8_t* a, const uint8_t* a
   if (!ex) {
     if (mode == 0) hipLaunchKernelGGL((mx_gemm_kernel<0, false>), gd, bd, 0, stream, p);
     else if (mode == 1) hipLaunchKernelGGL((mx_gemm_kernel<1, false>), gd, bd, 0, stream, p);
+    else if (mode == 3) hipLaunchKernelGGL((mx_gemm_kernel<3, false>), gd, bd, 0, stream, p);
     else hipLaunchKernelGGL((mx_gemm_kernel<2, false>), gd, bd, 0, stream, p);
   } else {
     if (mode == 0) hipLaunchKernelGGL((mx_gemm_kernel<0, true>), gd, bd, 0, stream, p);
     else if (mode == 1) hipLaunchKernelGGL((mx_gemm_kernel<1, true>), gd, bd, 0, stream, p);
+    else if (mode == 3) hipLaunchKernelGGL((mx_gemm_kernel<3, true>), gd, bd, 0, stream, p);
     else hipLaunchKernelGGL((mx_gemm_kernel<2, true>), gd, bd, 0, stream, p);
   }
   return hipGetLastError();

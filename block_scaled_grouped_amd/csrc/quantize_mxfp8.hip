@@ -215,10 +215,12 @@ __device__ __forceinline__ uint32_t lds_ld4(uint32_t a) {
   return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>((size_t)a);
 }
 
-// 16 E4M3 bytes from 16 values given as bf16 bits (element i in halves of w[i/2]).
+// 16 E4M3 (or E5M2) bytes from 16 values given as bf16 bits (element i in
+// halves of w[i/2]).
+template <bool E5M2 = false>
 __device__ __forceinline__ uint4 cvt16(const uint32_t (&w)[8], float f) {
-  const uint2 a = cvt8(make_uint4(w[0], w[1], w[2], w[3]), f);
-  const uint2 b = cvt8(make_uint4(w[4], w[5], w[6], w[7]), f);
+  const uint2 a = cvt8<E5M2>(make_uint4(w[0], w[1], w[2], w[3]), f);
+  const uint2 b = cvt8<E5M2>(make_uint4(w[4], w[5], w[6], w[7]), f);
   return make_uint4(a.x, a.y, b.x, b.y);
 }
 
@@ -254,8 +256,9 @@ __device__ __forceinline__ ColTile col_tile_info(int64_t id, int64_t nslab, int 
 // takes a column pair 2 pc, 2 pc + 1 (pc = 8 w + q + the pass's base) and
 // tokens [16 k, 16 k + 16) (4-byte LDS reads), so a column's 32-token block is split over lanes k, k ^ 1 and its 128
 // output bytes are written by 8 neighbouring lanes, 16 bytes each; the column's
-// four block scales become one word of the GEMM order.
-template <int NW>
+// four block scales become one word of the GEMM order.  E5M2: gradient elements
+// (scale byte exponent(amax) - 15).
+template <int NW, bool E5M2>
 __device__ __forceinline__ void col_convert_columns(uint32_t lds, const ColTile& t, int64_t cols,
                                                     int64_t poff, int w, int lane,
                                                     uint8_t* __restrict__ col_data,
@@ -278,8 +281,8 @@ __device__ __forceinline__ void col_convert_columns(uint32_t lds, const ColTile&
     uint32_t am = amax_fold(amax2(amax2(amax2(pk[0], pk[1]), amax2(pk[2], pk[3])),
                                   amax2(amax2(pk[4], pk[5]), amax2(pk[6], pk[7]))));
     am = max(am, dpp_xor1(am));   // the block's other 16 tokens
-    const uint32_t byte = e8m0_from_amax_bits(am);
-    const uint4 q = cvt16(pk, e8m0_scale(byte));
+    const uint32_t byte = e8m0_from_amax_bits<E5M2>(am);
+    const uint4 q = cvt16<E5M2>(pk, e8m0_scale(byte));
     // block bytes of tokens [0, 32), [32, 64), ... sit in lanes k = 0, 2, 4, 6
     const uint32_t b1 = dpp_down<2>(byte), b2 = dpp_down<4>(byte), b3 = dpp_down<6>(byte);
     const int64_t c = t.c0 + 2 * pc + e;
@@ -346,6 +349,7 @@ __device__ __forceinline__ void lds_st16(uint32_t a, uint4 v) {
   *reinterpret_cast<lds_v4i*>((size_t)a) = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
 }
 
+template <bool E5M2>
 __global__ __launch_bounds__(256) void mx_colwise_kernel(
     const uint16_t* __restrict__ x, int64_t rows_cap, int64_t cols, int G,
     const int64_t* __restrict__ offsets, const int64_t* __restrict__ poffsets, int64_t col_cap,
@@ -399,8 +403,9 @@ __global__ __launch_bounds__(256) void mx_colwise_kernel(
       if (tid == 0 && t.t0 == s_poff[t.g] && t.c0 == 0) dev_status_or(status, kDevBadPadding);
       continue;
     }
-    col_convert_columns<4>(lds, t, cols, s_poff[t.g], w, lane, col_data, col_scales);
-    if (row_data != nullptr) col_convert_rows<4>(lds, t, cols, rows_cap, w, lane, row_data, row_scales);
+    col_convert_columns<4, E5M2>(lds, t, cols, s_poff[t.g], w, lane, col_data, col_scales);
+    if (!E5M2 && row_data != nullptr)
+      col_convert_rows<4>(lds, t, cols, rows_cap, w, lane, row_data, row_scales);
   }
 }
 
@@ -409,15 +414,20 @@ hipError_t launch_quantize_mxfp8_colwise(const uint16_t* x, int64_t rows_cap, in
                                          int64_t col_rows_cap, uint8_t* col_data,
                                          uint8_t* col_scales, uint8_t* row_data,
                                          uint8_t* row_scales, uint32_t* status,
-                                         hipStream_t stream) {
+                                         hipStream_t stream, bool e5m2) {
   // upper bound of the tile count from the host-known capacity
   const int64_t bound = ((col_rows_cap + kColTokens - 1) / kColTokens) * ((cols + kColCols - 1) / kColCols);
   int64_t blocks = (int64_t)device_cu_count() * kColBlocksPerCu;
   if (bound < blocks) blocks = bound;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(mx_colwise_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, rows_cap,
-                     cols, G, offsets, padded_offsets, col_rows_cap, col_data, col_scales, row_data,
-                     row_scales, status);
+  if (e5m2)  // the gradient's columnwise copy only (no rowwise output)
+    hipLaunchKernelGGL(mx_colwise_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, x,
+                       rows_cap, cols, G, offsets, padded_offsets, col_rows_cap, col_data,
+                       col_scales, nullptr, nullptr, status);
+  else
+    hipLaunchKernelGGL(mx_colwise_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, x,
+                       rows_cap, cols, G, offsets, padded_offsets, col_rows_cap, col_data,
+                       col_scales, row_data, row_scales, status);
   return hipGetLastError();
 }
 

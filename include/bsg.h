@@ -48,7 +48,12 @@ typedef enum {
 #define BSG_DEV_BAD_PADDING   4u   /* padded offsets not multiples of 128 or smaller than
                                       the live sizes; that group was skipped */
 
-typedef enum { BSG_FPROP_TN = 0, BSG_WGRAD_NT = 1, BSG_DGRAD_NN = 2 } bsg_gemm_mode;
+typedef enum {
+  BSG_FPROP_TN = 0,
+  BSG_WGRAD_NT = 1,
+  BSG_DGRAD_NN = 2,
+  BSG_WGRAD_NT_E5M2 = 3
+} bsg_gemm_mode;
 typedef enum { BSG_OUT_BF16 = 0, BSG_OUT_F32 = 1 } bsg_out_dtype;
 
 #define BSG_MAX_GROUPS 256
@@ -135,6 +140,20 @@ int grouped_quantize_mxfp8(const void* x, int64_t rows_cap, int64_t cols, int64_
 int grouped_quantize_mxfp8_rowwise_e5m2(const void* x, int64_t rows_cap, int64_t cols, int64_t G,
                                         const int64_t* offsets, uint8_t* row_data,
                                         uint8_t* row_scales, uint32_t* dev_status, void* stream);
+
+/*
+ * grouped_quantize_mxfp8_colwise_e5m2
+ *
+ * Columnwise (transposed) MXFP8 copy of a gradient with E5M2 elements, for the
+ * weight gradient's E5M2 x E4M3 product ("gemm.py", _compatible_fp8_gemm_dtypes).
+ * Blocks, layout, padding and arguments as the columnwise part of
+ * grouped_quantize_mxfp8; the E8M0 byte is exponent(amax) - 15, elements round
+ * to nearest even and saturate at +-57344 (as grouped_quantize_mxfp8_rowwise_e5m2).
+ */
+int grouped_quantize_mxfp8_colwise_e5m2(const void* x, int64_t rows_cap, int64_t cols, int64_t G,
+                                        const int64_t* offsets, const int64_t* padded_offsets,
+                                        int64_t col_rows_cap, uint8_t* col_data,
+                                        uint8_t* col_scales, uint32_t* dev_status, void* stream);
 
 /*
  * grouped_quantize_nvfp4_rowscaled
@@ -304,6 +323,10 @@ int grouped_quantize_nvfp4_rowscaled_colwise(const void* x, int64_t rows_cap, in
  *            quantized along k, zero past k; b_scales its col_scales ([kp/128][n]
  *            words per expert, at byte g * n * kp / 32)
  *   offsets, rows_cap, out as in FPROP (out [rows_cap, n]).
+ * mode BSG_WGRAD_NT_E5M2: BSG_WGRAD_NT with an E5M2 gradient (dW = dY^T X, an
+ *   E5M2 x E4M3 product "gemm.py" _compatible_fp8_gemm_dtypes accepts): a is dY's
+ *   columnwise copy from grouped_quantize_mxfp8_colwise_e5m2, b is X's E4M3
+ *   columnwise copy; everything else as BSG_WGRAD_NT.
  * k: any positive multiple of 32 (FPROP, DGRAD; "gemm.py",
  * assert_cublas_requirements asks only for the block multiple).  No data byte
  * past k in a row is read; the scale bytes of the last word past k/32 multiply

@@ -110,10 +110,13 @@ def test_full_tiny_all_outputs():
         gemm_tolerance_check(y[off[g]:off[g + 1]], ref[off[g]:off[g + 1]], False, "group %d" % g)
 
 
-def test_full_wgrad():
-    """8 experts (2 empty), 16384 ragged tokens, dW [8, 4096, 4096]."""
+@pytest.mark.parametrize("flow", ["wgrad", "wgrad_e5m2"])
+def test_full_wgrad(flow):
+    """8 experts (2 empty), 16384 ragged tokens, dW [8, 4096, 4096]; dY's
+    columnwise copy in E4M3, or in E5M2 (wgrad_e5m2)."""
     dev = device()
-    case = bench.make_case("wgrad", dev)
+    case = bench.make_case(flow, dev)
+    elem = "e5m2" if flow == "wgrad_e5m2" else "e4m3"
     case.dw.fill_(float("nan"))
     case.step()
     torch.cuda.synchronize()
@@ -125,9 +128,9 @@ def test_full_wgrad():
     i0, j0 = 32 * int(rng.integers(0, N // 32)), 32 * int(rng.integers(0, K // 32))
     dyb = workloads.bf16_bits(case.dy[:, i0:i0 + 32])
     xb = workloads.bf16_bits(case.x[:, j0:j0 + 32])
-    dyc, dys = Q.mxfp8_colwise(dyb, off, poff)
+    dyc, dys = Q.mxfp8_colwise(dyb, off, poff, elem=elem)
     xc, xs = Q.mxfp8_colwise(xb, off, poff)
-    ref = GM.mxfp8_wgrad(dyc, dys, xc, xs, poff, 32, 32)
+    ref = GM.mxfp8_wgrad(dyc, dys, xc, xs, poff, 32, 32, elem_a=elem)
     gd = host_u8(case.dyc)
     dw = case.dw
     for g in range(G):
@@ -138,7 +141,7 @@ def test_full_wgrad():
         blk = gd[poff[g] * N:poff[g + 1] * N].reshape(N, mp)[i0:i0 + 32]
         assert np.array_equal(blk, dyc[poff[g] * 32:poff[g + 1] * 32].reshape(32, mp)), g
         y = dw[g, i0:i0 + 32, j0:j0 + 32].float().cpu().numpy().astype(np.float64)
-        gemm_tolerance_check(y, ref[g], False, "wgrad group %d" % g)
+        gemm_tolerance_check(y, ref[g], False, "%s group %d" % (flow, g))
     assert not torch.isnan(dw).any()
 
 

@@ -117,6 +117,42 @@ def test_wgrad_parity(sizes, N, K, out_f32):
             gemm_tolerance_check(y[g], ref[g], out_f32, "group %d" % g)
 
 
+@pytest.mark.parametrize("sizes,N,K", WGRAD_CASES)
+@pytest.mark.parametrize("out_f32", [True, False])
+def test_wgrad_e5m2_parity(sizes, N, K, out_f32):
+    """dW = dY^T X with dY's columnwise copy in E5M2 (GPU quantize, checked
+    bit-exact) times X's E4M3 copy."""
+    rng = np.random.default_rng(N * 5 + K)
+    sizes = np.array(sizes, np.int32)
+    G, M = len(sizes), int(sizes.sum())
+    dy = _bits(rng, (max(M, 1), N))
+    x = _bits(rng, (max(M, 1), K))
+    _, off = O.group_offsets(sizes)
+    _, poff = O.group_offsets(sizes, pad_to=128)
+    cap = max(int(poff[-1]), 128)
+    dyc, dys = bsg.grouped_quantize_mxfp8_colwise_e5m2(bf16_dev(dy), to_dev(off), to_dev(poff),
+                                                       col_rows_cap=cap)
+    wdyc, wdys = Q.mxfp8_colwise(dy, off, poff, elem="e5m2")
+    n = int(poff[-1])
+    assert np.array_equal(host_u8(dyc)[:n * N], wdyc)
+    assert np.array_equal(host_u8(dys)[:n * N // 32], wdys)
+    xq = bsg.grouped_quantize_mxfp8(bf16_dev(x), to_dev(off), rowwise=False,
+                                    padded_offsets=to_dev(poff), col_rows_cap=cap)
+    xc, xs = Q.mxfp8_colwise(x, off, poff)
+    ref = GM.mxfp8_wgrad(wdyc, wdys, xc, xs, poff, N, K, elem_a="e5m2")
+    dt = torch.float32 if out_f32 else torch.bfloat16
+    out = torch.full((G, N, K), float("nan"), dtype=dt, device=device())
+    bsg.grouped_gemm_mxfp8(bsg.BSG_WGRAD_NT_E5M2, dyc, dys, xq["col_data"], xq["col_scales"],
+                           to_dev(poff), cap, N, K, out=out,
+                           out_dtype=bsg.BSG_OUT_F32 if out_f32 else bsg.BSG_OUT_BF16)
+    y = bf16_out_to_f64(out)
+    for g in range(G):
+        if sizes[g] == 0:
+            assert np.all(y[g] == 0.0) and not np.any(np.signbit(y[g])), "empty expert must be +0"
+        else:
+            gemm_tolerance_check(y[g], ref[g], out_f32, "group %d" % g)
+
+
 def test_fprop_end_to_end_tiny_config():
     """The tiny MoE config: GPU quantize -> GPU GEMM vs oracle quantize -> oracle GEMM."""
     w = workloads.get("tiny")

@@ -186,6 +186,31 @@ def test_colwise_bit_exact(rows_cap, cols, sizes, with_rows):
         assert np.all(host_u8(out["row_data"])[live:] == SENTINEL)
 
 
+@pytest.mark.parametrize("rows_cap,cols,sizes", COL_CASES)
+def test_colwise_e5m2_bit_exact(rows_cap, cols, sizes):
+    """The gradient's E5M2 columnwise copy, with values spread over many
+    binades (including blocks past the E5M2 range after scaling)."""
+    rng = np.random.default_rng(rows_cap * 13 + cols)
+    bits = _bits(rng, rows_cap, cols, spread=12, outliers=0.05)
+    sizes = np.array(sizes, np.int32)
+    live = int(sizes.sum())
+    bits[live:] = workloads.BF16_NAN_BITS
+    _, off = O.group_offsets(sizes)
+    _, poff = O.group_offsets(sizes, pad_to=128)
+    want_d, want_s = Q.mxfp8_colwise(bits, off, poff, elem="e5m2")
+    G = len(sizes)
+    cap = rows_cap + 128 * G
+    cd = filled_u8((cap * cols,))
+    cs = filled_u8((cap * cols // 32,))
+    bsg.grouped_quantize_mxfp8_colwise_e5m2(bf16_dev(bits), to_dev(off), to_dev(poff),
+                                            col_rows_cap=cap, col_data=cd, col_scales=cs)
+    d, s = host_u8(cd), host_u8(cs)
+    n = int(poff[-1]) * cols
+    assert np.array_equal(d[:n], want_d)
+    assert np.array_equal(s[:n // 32], want_s)
+    assert np.all(d[n:] == SENTINEL) and np.all(s[n // 32:] == SENTINEL)
+
+
 def test_colwise_bad_padding_flagged():
     bits = _bits(np.random.default_rng(3), 64, 64)
     off = np.array([0, 10, 64])
