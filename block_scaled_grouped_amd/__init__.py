@@ -33,7 +33,8 @@ EXPORTS = ("bsg_last_error", "bsg_version", "group_offsets_i32_to_i64", "grouped
            "grouped_gemm_mxfp8", "grouped_gemm_mxfp8_ex", "grouped_gemm_nvfp4_rowscaled",
            "grouped_gemm_nvfp4_rowscaled_wgrad", "grouped_gemm_nvfp4_pertensor",
            "grouped_gemm_nvfp4_rowscaled_noalloc", "grouped_quantize_nvfp4_pertensor_rht",
-           "grouped_quantize_nvfp4_pertensor_2d", "grouped_quantize_mxfp8_colwise_e5m2")
+           "grouped_quantize_nvfp4_pertensor_2d", "grouped_quantize_mxfp8_colwise_e5m2",
+           "grouped_gemm_nvfp4_rowscaled_ex", "grouped_gemm_nvfp4_rowscaled_wgrad_ex")
 BSG_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
@@ -90,6 +91,12 @@ def load_library(path=LIB_PATH):
     lib.grouped_gemm_nvfp4_pertensor.restype = I32
     lib.grouped_gemm_nvfp4_pertensor.argtypes = [I64, P, P, P, P, I64, I64, P, P, P, P, P, I64, I32,
                                                  P, P]
+    lib.grouped_gemm_nvfp4_rowscaled_ex.restype = I32
+    lib.grouped_gemm_nvfp4_rowscaled_ex.argtypes = [I64, P, P, P, P, I64, I64, P, P, P, P, P, I64,
+                                                    I32, P, I32, P, P]
+    lib.grouped_gemm_nvfp4_rowscaled_wgrad_ex.restype = I32
+    lib.grouped_gemm_nvfp4_rowscaled_wgrad_ex.argtypes = [I64, P, P, P, P, P, P, P, I64, I64, I64,
+                                                          P, I32, I32, P, P]
     lib.grouped_gemm_nvfp4_rowscaled_noalloc.restype = I32
     lib.grouped_gemm_nvfp4_rowscaled_noalloc.argtypes = [I64, P, P, P, P, I64, I64, P, P, P, P, P,
                                                          I64, I32, P, P]
@@ -498,8 +505,9 @@ def _nv_gemm_check(G, a, a_scales, a_outer, offsets, rows_cap, k, b, b_scales, b
 
 def grouped_gemm_nvfp4_rowscaled(a, a_scales, a_outer, offsets, k, b, b_scales, b_outer,
                                  n_per_group, out=None, ld_out=None, out_dtype=BSG_OUT_BF16,
-                                 scratch=None, G=None, status=None):
-    """Row-scaled NVFP4 fprop: out [rows_cap, ld_out]; n_per_group is a host list."""
+                                 scratch=None, G=None, status=None, accumulate=False):
+    """Row-scaled NVFP4 fprop: out [rows_cap, ld_out]; n_per_group is a host list.
+    accumulate=True adds Y to out's previous contents (grouped_gemm_nvfp4_rowscaled_ex)."""
     import torch
     lib = load_library()
     _need_cuda(a, a_scales, a_outer, offsets, b, b_scales, b_outer)
@@ -517,6 +525,12 @@ def grouped_gemm_nvfp4_rowscaled(a, a_scales, a_outer, offsets, k, b, b_scales, 
                    ld_out, out_dtype, status, per_tensor=False)
     _req(scratch, "scratch", 4 * rows_cap * ld_out, torch.float32, optional=True)
     host_n = (ctypes.c_int64 * G)(*npg)
+    if accumulate:
+        _check(lib.grouped_gemm_nvfp4_rowscaled_ex(
+            G, _ptr(a), _ptr(a_scales), _ptr(a_outer), _ptr(offsets), rows_cap, k, _ptr(b),
+            _ptr(b_scales), _ptr(b_outer), ctypes.cast(host_n, ctypes.c_void_p), _ptr(out), ld_out,
+            out_dtype, _ptr(scratch), 1, _ptr(status), _stream(a)))
+        return out
     _check(lib.grouped_gemm_nvfp4_rowscaled(G, _ptr(a), _ptr(a_scales), _ptr(a_outer),
                                             _ptr(offsets), rows_cap, k, _ptr(b), _ptr(b_scales),
                                             _ptr(b_outer), ctypes.cast(host_n, ctypes.c_void_p),
@@ -582,9 +596,10 @@ def grouped_gemm_nvfp4_pertensor(a, a_scales, a_amax, offsets, k, b, b_scales, b
 
 def grouped_gemm_nvfp4_rowscaled_wgrad(a, a_scales, a_outer, b, b_scales, b_outer, padded_offsets,
                                        n, k, col_rows_cap=None, out=None, out_dtype=BSG_OUT_BF16,
-                                       G=None, status=None):
-    """Row-scaled NVFP4 wgrad from the columnwise copies: out [G, n, k].  See
-    include/bsg.h."""
+                                       G=None, status=None, accumulate=False):
+    """Row-scaled NVFP4 wgrad from the columnwise copies: out [G, n, k];
+    accumulate=True adds to out's previous contents
+    (grouped_gemm_nvfp4_rowscaled_wgrad_ex).  See include/bsg.h."""
     import torch
     lib = load_library()
     _need_cuda(a, a_scales, a_outer, b, b_scales, b_outer, padded_offsets)
@@ -604,6 +619,12 @@ def grouped_gemm_nvfp4_rowscaled_wgrad(a, a_scales, a_outer, b, b_scales, b_oute
     dt, esz = _out_dtype(out_dtype)
     _req(out, "out", esz * G * n * k, dt)
     _req(status, "status", 4, optional=True)
+    if accumulate:
+        _check(lib.grouped_gemm_nvfp4_rowscaled_wgrad_ex(
+            G, _ptr(a), _ptr(a_scales), _ptr(a_outer), _ptr(b), _ptr(b_scales), _ptr(b_outer),
+            _ptr(padded_offsets), col_rows_cap, n, k, _ptr(out), out_dtype, 1, _ptr(status),
+            _stream(a)))
+        return out
     _check(lib.grouped_gemm_nvfp4_rowscaled_wgrad(
         G, _ptr(a), _ptr(a_scales), _ptr(a_outer), _ptr(b), _ptr(b_scales), _ptr(b_outer),
         _ptr(padded_offsets), col_rows_cap, n, k, _ptr(out), out_dtype, _ptr(status), _stream(a)))

@@ -325,7 +325,7 @@ static int gemm_nvfp4_impl(const char* fn, bool per_tensor, int64_t G, const uin
                            int64_t rows_cap, int64_t k, const uint8_t* b, const uint8_t* b_scales,
                            const float* b_outer, const int64_t* n_per_group, void* out,
                            int64_t ld_out, int out_dtype, float* scratch, uint32_t* dev_status,
-                           void* stream, bool noalloc = false) {
+                           void* stream, bool noalloc = false, bool accumulate = false) {
   if (a == nullptr || a_scales == nullptr || a_outer == nullptr || offsets == nullptr || b == nullptr ||
       b_scales == nullptr || b_outer == nullptr || n_per_group == nullptr || out == nullptr)
     return fail(BSG_ERR_NULL, "%s: operands, scales, offsets, n_per_group and out must be non-NULL", fn);
@@ -373,7 +373,7 @@ static int gemm_nvfp4_impl(const char* fn, bool per_tensor, int64_t G, const uin
   return hip_result(bsg::launch_gemm_nvfp4((int)G, a, a_scales, a_outer, offsets, rows_cap, k, b,
                                            b_scales, b_outer, tab, (int)max_n, out, ld_out,
                                            out_dtype == BSG_OUT_F32, scratch, dev_status,
-                                           (hipStream_t)stream, per_tensor),
+                                           (hipStream_t)stream, per_tensor, accumulate),
                     fn);
 }
 
@@ -386,6 +386,19 @@ int grouped_gemm_nvfp4_rowscaled(int64_t G, const uint8_t* a, const uint8_t* a_s
   return gemm_nvfp4_impl("grouped_gemm_nvfp4_rowscaled", false, G, a, a_scales, a_outer, offsets,
                          rows_cap, k, b, b_scales, b_outer, n_per_group, out, ld_out, out_dtype,
                          scratch, dev_status, stream);
+}
+
+int grouped_gemm_nvfp4_rowscaled_ex(int64_t G, const uint8_t* a, const uint8_t* a_scales,
+                                    const float* a_outer, const int64_t* offsets, int64_t rows_cap,
+                                    int64_t k, const uint8_t* b, const uint8_t* b_scales,
+                                    const float* b_outer, const int64_t* n_per_group, void* out,
+                                    int64_t ld_out, int out_dtype, float* scratch, int accumulate,
+                                    uint32_t* dev_status, void* stream) {
+  if (accumulate != 0 && accumulate != 1)
+    return fail(BSG_ERR_UNSUPPORTED, "grouped_gemm_nvfp4_rowscaled_ex: accumulate must be 0 or 1");
+  return gemm_nvfp4_impl("grouped_gemm_nvfp4_rowscaled_ex", false, G, a, a_scales, a_outer, offsets,
+                         rows_cap, k, b, b_scales, b_outer, n_per_group, out, ld_out, out_dtype,
+                         scratch, dev_status, stream, false, accumulate == 1);
 }
 
 int grouped_gemm_nvfp4_rowscaled_noalloc(int64_t G, const uint8_t* a, const uint8_t* a_scales,
@@ -409,13 +422,11 @@ int grouped_gemm_nvfp4_pertensor(int64_t G, const uint8_t* a, const uint8_t* a_s
                          nullptr, dev_status, stream);
 }
 
-int grouped_gemm_nvfp4_rowscaled_wgrad(int64_t G, const uint8_t* a, const uint8_t* a_scales,
-                                       const float* a_outer, const uint8_t* b,
-                                       const uint8_t* b_scales, const float* b_outer,
-                                       const int64_t* padded_offsets, int64_t col_rows_cap,
-                                       int64_t n, int64_t k, void* out, int out_dtype,
-                                       uint32_t* dev_status, void* stream) {
-  const char* fn = "grouped_gemm_nvfp4_rowscaled_wgrad";
+static int nv_wgrad_impl(const char* fn, int64_t G, const uint8_t* a, const uint8_t* a_scales,
+                         const float* a_outer, const uint8_t* b, const uint8_t* b_scales,
+                         const float* b_outer, const int64_t* padded_offsets, int64_t col_rows_cap,
+                         int64_t n, int64_t k, void* out, int out_dtype, bool accumulate,
+                         uint32_t* dev_status, void* stream) {
   if (a == nullptr || a_scales == nullptr || a_outer == nullptr || b == nullptr ||
       b_scales == nullptr || b_outer == nullptr || padded_offsets == nullptr || out == nullptr)
     return fail(BSG_ERR_NULL, "%s: operands, scales, padded_offsets and out must be non-NULL", fn);
@@ -436,8 +447,32 @@ int grouped_gemm_nvfp4_rowscaled_wgrad(int64_t G, const uint8_t* a, const uint8_
   return hip_result(bsg::launch_gemm_nvfp4_wgrad((int)G, a, a_scales, a_outer, b, b_scales,
                                                  b_outer, padded_offsets, col_rows_cap, n, k, out,
                                                  out_dtype == BSG_OUT_F32, dev_status,
-                                                 (hipStream_t)stream),
+                                                 (hipStream_t)stream, accumulate),
                     fn);
+}
+
+int grouped_gemm_nvfp4_rowscaled_wgrad(int64_t G, const uint8_t* a, const uint8_t* a_scales,
+                                       const float* a_outer, const uint8_t* b,
+                                       const uint8_t* b_scales, const float* b_outer,
+                                       const int64_t* padded_offsets, int64_t col_rows_cap,
+                                       int64_t n, int64_t k, void* out, int out_dtype,
+                                       uint32_t* dev_status, void* stream) {
+  return nv_wgrad_impl("grouped_gemm_nvfp4_rowscaled_wgrad", G, a, a_scales, a_outer, b, b_scales,
+                       b_outer, padded_offsets, col_rows_cap, n, k, out, out_dtype, false,
+                       dev_status, stream);
+}
+
+int grouped_gemm_nvfp4_rowscaled_wgrad_ex(int64_t G, const uint8_t* a, const uint8_t* a_scales,
+                                          const float* a_outer, const uint8_t* b,
+                                          const uint8_t* b_scales, const float* b_outer,
+                                          const int64_t* padded_offsets, int64_t col_rows_cap,
+                                          int64_t n, int64_t k, void* out, int out_dtype,
+                                          int accumulate, uint32_t* dev_status, void* stream) {
+  const char* fn = "grouped_gemm_nvfp4_rowscaled_wgrad_ex";
+  if (accumulate != 0 && accumulate != 1)
+    return fail(BSG_ERR_UNSUPPORTED, "%s: accumulate must be 0 or 1", fn);
+  return nv_wgrad_impl(fn, G, a, a_scales, a_outer, b, b_scales, b_outer, padded_offsets,
+                       col_rows_cap, n, k, out, out_dtype, accumulate == 1, dev_status, stream);
 }
 
 }  // extern "C"

@@ -212,7 +212,8 @@ hipError_t launch_gemm_nvfp4(int G, const uint8_t* a, const uint8_t* a_scales,
                              int64_t k, const uint8_t* b, const uint8_t* b_scales,
                              const float* b_outer, const NvGroupTable& table, int max_n,
                              void* out, int64_t ld_out, int out_f32, float* s_buf,
-                             uint32_t* status, hipStream_t stream, bool per_tensor = false);
+                             uint32_t* status, hipStream_t stream, bool per_tensor = false,
+                             bool accumulate = false);
 
 // The FP32 S of grouped_gemm_nvfp4_rowscaled_noalloc lives in a static device
 // array of this many bytes (per GPU).
@@ -232,7 +233,8 @@ hipError_t launch_gemm_nvfp4_wgrad(int G, const uint8_t* a, const uint8_t* a_sca
                                    const float* a_outer, const uint8_t* b, const uint8_t* b_scales,
                                    const float* b_outer, const int64_t* padded_offsets,
                                    int64_t col_rows_cap, int64_t n, int64_t k, void* out,
-                                   int out_f32, uint32_t* status, hipStream_t stream);
+                                   int out_f32, uint32_t* status, hipStream_t stream,
+                                   bool accumulate = false);
 
 int device_cu_count();
 

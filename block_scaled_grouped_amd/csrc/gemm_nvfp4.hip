@@ -85,6 +85,7 @@ struct NvArgs {
   int G;
   int out_f32;
   int per_tensor;  // aout / bout hold one amax per group (per-tensor NVFP4)
+  int accumulate;  // out = out_previous + Y instead of Y (row-scaled flows)
   NvGroupTable tab;
 };
 
@@ -565,7 +566,22 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
           }
         }
         const int rr = row + 32 * i, cc = col + 32 * j;
-        if (f32out) {
+        if (fused && p.accumulate) {
+          // copy-or-accumulate: Y + the output's previous value, rounded once
+          EpiTerms ep;
+          ep.alpha = 1.0f;
+          ep.beta = 1.0f;
+          ep.has_bias = false;
+          ep.bias = ro;
+          const bool wide4 = (ldc & 3) == 0 && (t.b_rows & 3) == 0;
+          if (p.out_f32) {
+            if (wide4) store_block_ex<true, true>(y, ro, ldc, rr, cc, t.b_rows, ep);
+            else store_block_ex<false, true>(y, ro, ldc, rr, cc, t.b_rows, ep);
+          } else {
+            if (wide4) store_block_ex<true, false>(y, ro, ldc, rr, cc, t.b_rows, ep);
+            else store_block_ex<false, false>(y, ro, ldc, rr, cc, t.b_rows, ep);
+          }
+        } else if (f32out) {
           if (wide) store_block<true, true>(y, ro, ldc, rr, cc, h, t.b_rows);
           else store_block<false, true>(y, ro, ldc, rr, cc, h, t.b_rows);
         } else {
@@ -586,7 +602,7 @@ __global__ __launch_bounds__(256) void nv_postscale_kernel(const float* __restri
                                                            const int64_t* __restrict__ offsets,
                                                            int64_t rows_cap, int G, void* out,
                                                            int64_t ld_out, int out_f32,
-                                                           NvGroupTable tab) {
+                                                           int accumulate, NvGroupTable tab) {
   __shared__ int64_t s_off[kMaxGroups + 1];
   load_offsets_clamped(offsets, G, rows_cap, s_off, nullptr);
   const int64_t row = blockIdx.x;
@@ -601,11 +617,16 @@ __global__ __launch_bounds__(256) void nv_postscale_kernel(const float* __restri
   const float ao = aout[row];
   const float* bo = bout + tab.brow[g];
   for (int n = threadIdx.x; n < ng; n += blockDim.x) {
-    const float y = (s_buf[row * ld_out + n] * ao) * bo[n];
-    if (out_f32)
-      reinterpret_cast<float*>(out)[row * ld_out + n] = y;
-    else
-      reinterpret_cast<uint16_t*>(out)[row * ld_out + n] = (uint16_t)f32_to_bf16_rne(y);
+    float y = (s_buf[row * ld_out + n] * ao) * bo[n];
+    if (out_f32) {
+      float* o = reinterpret_cast<float*>(out) + row * ld_out + n;
+      if (accumulate) y = *o + y;
+      *o = y;
+    } else {
+      uint16_t* o = reinterpret_cast<uint16_t*>(out) + row * ld_out + n;
+      if (accumulate) y = bf16_to_f32(*o) + y;
+      *o = (uint16_t)f32_to_bf16_rne(y);
+    }
   }
 }
 
@@ -616,12 +637,14 @@ hipError_t launch_gemm_nvfp4(int G, const uint8_t* a, const uint8_t* a_scales,
                              int64_t k, const uint8_t* b, const uint8_t* b_scales,
                              const float* b_outer, const NvGroupTable& table, int max_n,
                              void* out, int64_t ld_out, int out_f32, float* s_buf,
-                             uint32_t* status, hipStream_t stream, bool per_tensor) {
+                             uint32_t* status, hipStream_t stream, bool per_tensor,
+                             bool accumulate) {
   NvArgs p;
   p.a = a; p.as = a_scales; p.aout = a_outer; p.offsets = offsets; p.rows_cap = rows_cap; p.k = k;
   p.n = 0;
   p.b = b; p.bs = b_scales; p.bout = b_outer; p.out = out; p.ld_out = ld_out; p.s_buf = s_buf;
   p.status = status; p.G = G; p.out_f32 = out_f32; p.per_tensor = per_tensor ? 1 : 0;
+  p.accumulate = accumulate ? 1 : 0;
   p.tab = table;
   if (per_tensor && s_buf != nullptr) return hipErrorInvalidValue;
   const int64_t bound = ((rows_cap + BM - 1) / BM + G) * ((max_n + BN - 1) / BN);
@@ -644,7 +667,7 @@ hipError_t launch_gemm_nvfp4(int G, const uint8_t* a, const uint8_t* a_scales,
   if (s_buf != nullptr && rows_cap > 0) {
     hipLaunchKernelGGL(nv_postscale_kernel, dim3((unsigned)rows_cap), dim3(256), 0, stream,
                        s_buf, a_outer, b_outer, offsets, rows_cap, G, out, ld_out, out_f32,
-                       table);
+                       accumulate ? 1 : 0, table);
     return hipGetLastError();
   }
   return hipSuccess;
@@ -698,19 +721,21 @@ hipError_t launch_gemm_nvfp4_noalloc(int G, const uint8_t* a, const uint8_t* a_s
   const hipError_t e = noalloc_scratch_ptr(&ptr);
   if (e != hipSuccess) return e;
   return launch_gemm_nvfp4(G, a, a_scales, a_outer, offsets, rows_cap, k, b, b_scales, b_outer,
-                           table, max_n, out, ld_out, out_f32, ptr, status, stream, false);
+                           table, max_n, out, ld_out, out_f32, ptr, status, stream, false, false);
 }
 
 hipError_t launch_gemm_nvfp4_wgrad(int G, const uint8_t* a, const uint8_t* a_scales,
                                    const float* a_outer, const uint8_t* b, const uint8_t* b_scales,
                                    const float* b_outer, const int64_t* padded_offsets,
                                    int64_t col_rows_cap, int64_t n, int64_t k, void* out,
-                                   int out_f32, uint32_t* status, hipStream_t stream) {
+                                   int out_f32, uint32_t* status, hipStream_t stream,
+                                   bool accumulate) {
   NvArgs p;
   p.a = a; p.as = a_scales; p.aout = a_outer; p.offsets = padded_offsets;
   p.rows_cap = col_rows_cap; p.k = k; p.n = n;
   p.b = b; p.bs = b_scales; p.bout = b_outer; p.out = out; p.ld_out = k; p.s_buf = nullptr;
   p.status = status; p.G = G; p.out_f32 = out_f32; p.per_tensor = 0; p.tab = NvGroupTable{};
+  p.accumulate = accumulate ? 1 : 0;
   const int64_t bound = (int64_t)G * ((n + BM - 1) / BM) * ((k + BN - 1) / BN);
   int64_t grid = device_cu_count();
   if (bound < grid) grid = bound;

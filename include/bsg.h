@@ -398,6 +398,27 @@ int grouped_gemm_nvfp4_rowscaled(int64_t G, const uint8_t* a, const uint8_t* a_s
                                  uint32_t* dev_status, void* stream);
 
 /*
+ * grouped_gemm_nvfp4_rowscaled_ex
+ *
+ * grouped_gemm_nvfp4_rowscaled with the copy-or-accumulate output of its flow
+ * ("[Common][PyTorch] Add row-scaled NVFP4 support to grouped-tensor GEMM",
+ * Greptile flow: apply the outer scales, then copy or accumulate into the
+ * output; an accumulate flag rather than a general beta, which that path
+ * rejects):
+ *   accumulate 0: out = Y (as grouped_gemm_nvfp4_rowscaled)
+ *   accumulate 1: out = out_previous + Y, added in float32 and rounded once
+ *                 to out_dtype (e.g. accumulating into an FP32 buffer)
+ * for the same live rows and columns n < N_g; everything else untouched.  With
+ * a scratch the post-scale kernel accumulates.  Other values: BSG_ERR_UNSUPPORTED.
+ */
+int grouped_gemm_nvfp4_rowscaled_ex(int64_t G, const uint8_t* a, const uint8_t* a_scales,
+                                    const float* a_outer, const int64_t* offsets, int64_t rows_cap,
+                                    int64_t k, const uint8_t* b, const uint8_t* b_scales,
+                                    const float* b_outer, const int64_t* n_per_group, void* out,
+                                    int64_t ld_out, int out_dtype, float* scratch, int accumulate,
+                                    uint32_t* dev_status, void* stream);
+
+/*
  * grouped_gemm_nvfp4_rowscaled_noalloc
  *
  * For callers that cannot allocate device memory -- code under HIP-graph
@@ -480,6 +501,21 @@ int grouped_gemm_nvfp4_rowscaled_wgrad(int64_t G, const uint8_t* a, const uint8_
                                        const int64_t* padded_offsets, int64_t col_rows_cap,
                                        int64_t n, int64_t k, void* out, int out_dtype,
                                        uint32_t* dev_status, void* stream);
+
+/*
+ * grouped_gemm_nvfp4_rowscaled_wgrad_ex
+ *
+ * grouped_gemm_nvfp4_rowscaled_wgrad with the flow's copy-or-accumulate output:
+ * accumulate 1 gives dW[g] = dW_previous[g] + (S * a_outer) * b_outer, added in
+ * float32 and rounded once (e.g. into an FP32 main-grad; an empty expert leaves
+ * its block as it was); accumulate 0 is grouped_gemm_nvfp4_rowscaled_wgrad.
+ */
+int grouped_gemm_nvfp4_rowscaled_wgrad_ex(int64_t G, const uint8_t* a, const uint8_t* a_scales,
+                                          const float* a_outer, const uint8_t* b,
+                                          const uint8_t* b_scales, const float* b_outer,
+                                          const int64_t* padded_offsets, int64_t col_rows_cap,
+                                          int64_t n, int64_t k, void* out, int out_dtype,
+                                          int accumulate, uint32_t* dev_status, void* stream);
 
 #ifdef __cplusplus
 }

@@ -100,6 +100,11 @@ def test_gemm_validation(lib):
     assert pt(2, p, p, p, p, 64, 80, p, p, p, hp, p, 128, 0, None, None) == 2       # k % 32
     assert pt(2, p, p, p, p, 64, 128, p, p, p, hp, p, 100, 0, None, None) == 2      # ld_out
     assert pt(2, p, p, p, p, 64, 128, p, p, p, hp, p, 128, 5, None, None) == 4      # out_dtype
+    ex = lib.grouped_gemm_nvfp4_rowscaled_ex
+    assert ex(2, p, p, p, p, 64, 128, p, p, p, hp, p, 128, 0, None, 2, None, None) == 4  # flag
+    assert ex(2, p, p, p, p, 64, 48, p, p, p, hp, p, 128, 0, None, 1, None, None) == 2   # k % 32
+    wx = lib.grouped_gemm_nvfp4_rowscaled_wgrad_ex
+    assert wx(2, p, p, p, p, p, p, p, 256, 128, 128, p, 0, -1, None, None) == 4          # flag
     neg = (ctypes.c_int64 * 2)(64, -1)
     assert nv(2, p, p, p, p, 64, 128, p, p, p, ctypes.cast(neg, ctypes.c_void_p), p, 128, 0,
               None, None, None) == 2

@@ -479,6 +479,45 @@ def test_nvfp4_pertensor_hip_graph_replay_with_new_sizes():
         assert torch.equal(eager[:live].nan_to_num(7.0), out[:live].nan_to_num(7.0))
 
 
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("out_f32", [True, False])
+def test_nvfp4_gemm_accumulate(fused, out_f32):
+    """Copy-or-accumulate of the row-scaled flow: with the accumulate flag the
+    live rows and columns n < N_g become previous + Y (added in float32 and
+    rounded once); columns past N_g and capacity rows keep their contents."""
+    rng = np.random.default_rng(93 + fused)
+    sizes, npg, K, rows_cap = [100, 0, 257, 31], [64, 128, 96, 256], 256, 450
+    sizes, off, ap, asc, at, bp, bsc, bt = _nv_operands(rng, sizes, npg, K, rows_cap)
+    live = int(off[-1])
+    ld = max(npg) + 8
+    prev = (rng.standard_normal((rows_cap, ld)) * 3).astype(np.float32)
+    prev[live:] = np.nan
+    for g in range(len(npg)):
+        prev[off[g]:off[g + 1], npg[g]:] = np.nan
+    dt = torch.float32 if out_f32 else torch.bfloat16
+    out = torch.from_numpy(prev).to(dt).to(device())
+    c_prev = bf16_out_to_f64(out)
+    scratch = None if fused else torch.empty((rows_cap, ld), dtype=torch.float32, device=device())
+
+    def pad_rows(a):
+        o = np.zeros((rows_cap,) + a.shape[1:], a.dtype)
+        o[:a.shape[0]] = a
+        return to_dev(o)
+
+    bsg.grouped_gemm_nvfp4_rowscaled(pad_rows(ap), pad_rows(asc), pad_rows(at), to_dev(off), K,
+                                     to_dev(bp), to_dev(bsc), to_dev(bt), npg, out=out, ld_out=ld,
+                                     out_dtype=bsg.BSG_OUT_F32 if out_f32 else bsg.BSG_OUT_BF16,
+                                     scratch=scratch, accumulate=True)
+    y = bf16_out_to_f64(out)
+    for g, (rows, r) in enumerate(GM.nvfp4_rowscaled_fprop(ap, asc, at, off, bp, bsc, bt, npg, K)):
+        if len(rows) == 0:
+            continue
+        gemm_tolerance_check(y[rows][:, :npg[g]], r + c_prev[rows][:, :npg[g]], out_f32,
+                             "group %d" % g)
+        assert np.all(np.isnan(y[rows][:, npg[g]:])), "columns past N_g must stay untouched"
+    assert np.all(np.isnan(y[live:])), "capacity rows must stay untouched"
+
+
 # ---------------------------------------------------------------- NVFP4 row-scaled wgrad
 
 NVW_CASES = [
@@ -652,3 +691,37 @@ def test_wgrad_accumulate_into_main_grad(out_f32):
         ref = GM.epilogue(s_ref[g], np.zeros(N, np.int64), alpha[[g]], beta[[g]], c_prev[g],
                           bias[[g]])
         gemm_tolerance_check(y[g], ref, out_f32, "expert %d" % g)
+
+
+@pytest.mark.parametrize("out_f32", [True, False])
+def test_nvfp4_wgrad_accumulate_into_main_grad(out_f32):
+    """Row-scaled NVFP4 wgrad with the accumulate flag: dW[g] = previous +
+    (S * a_outer) * b_outer, rounded once; an empty expert keeps its block
+    exactly."""
+    rng = np.random.default_rng(57)
+    sizes = np.array([37, 0, 130, 5], np.int32)
+    G, M, N, K = 4, int(sizes.sum()), 96, 160
+    dy = _bits(rng, (M, N))
+    x = _bits(rng, (M, K))
+    _, off = O.group_offsets(sizes)
+    _, poff = O.group_offsets(sizes, pad_to=128)
+    cap = M + 128 * G
+    dyc, dys, dyo = bsg.grouped_quantize_nvfp4_rowscaled_colwise(
+        bf16_dev(dy), to_dev(off), to_dev(poff), col_rows_cap=cap)
+    xc, xs, xo = bsg.grouped_quantize_nvfp4_rowscaled_colwise(
+        bf16_dev(x), to_dev(off), to_dev(poff), col_rows_cap=cap)
+    wdyc, wdys, wdyo = Q.nvfp4_rowscaled_colwise(dy, off, poff)
+    wxc, wxs, wxo = Q.nvfp4_rowscaled_colwise(x, off, poff)
+    ref = GM.nvfp4_rowscaled_wgrad(wdyc, wdys, wdyo, wxc, wxs, wxo, poff, N, K)
+    dt = torch.float32 if out_f32 else torch.bfloat16
+    out = torch.from_numpy(rng.standard_normal((G, N, K)).astype(np.float32)).to(dt).to(device())
+    c_prev = bf16_out_to_f64(out)
+    bsg.grouped_gemm_nvfp4_rowscaled_wgrad(dyc, dys, dyo, xc, xs, xo, to_dev(poff), N, K,
+                                           col_rows_cap=cap, out=out, accumulate=True,
+                                           out_dtype=bsg.BSG_OUT_F32 if out_f32 else bsg.BSG_OUT_BF16)
+    y = bf16_out_to_f64(out)
+    for g in range(G):
+        if sizes[g] == 0:
+            assert np.array_equal(y[g], c_prev[g]), "an empty expert keeps its block"
+        else:
+            gemm_tolerance_check(y[g], ref[g] + c_prev[g], out_f32, "group %d" % g)
