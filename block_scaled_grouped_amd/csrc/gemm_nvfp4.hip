@@ -16,29 +16,37 @@
 //
 // gfx950's scaled MFMA takes only power-of-two (E8M0) scales per 32 elements,
 // and E2M1 x E4M3 needs up to 6 significant bits, so no FP8/FP6/FP4 MFMA input
-// holds it exactly.  Each element is instead decoded while it is staged into
-// LDS: E2M1 -> fp16 pairs (hardware convert, unit scale), times its decoded E4M3
-// block scale with one packed fp16 multiply per pair -- exact, since the product
-// has at most 6 significant bits and lies in [2^-10, 2688], all normal fp16.
-// The product then runs on fp16 MFMA (v_mfma_f32_32x32x16_f16, the bf16 rate)
-// with FP32 accumulation: exact products, FP32 sums.
+// holds it exactly.  Each element is instead decoded in registers right before
+// the MFMA that uses it: E2M1 -> fp16 pairs (hardware convert, unit scale),
+// times its decoded E4M3 block scale with one packed fp16 multiply per pair --
+// exact, since the product has at most 6 significant bits and lies in
+// [2^-10, 2688], all normal fp16.  The product then runs on fp16 MFMA
+// (v_mfma_f32_32x32x16_f16, the bf16 rate) with FP32 accumulation: exact
+// products, FP32 sums.
 //
 // Tile 256 x 256, K-steps of 64, 4 wavefronts (2 x 2) of 128 x 128, each as
-// 4 x 4 MFMA blocks of 32 x 32 (256 accumulator registers per lane).  LDS holds
-// two stages of fp16 rows (128 bytes per row per K-step) with an XOR chunk
-// swizzle that keeps both the row-wise stores and the fragment reads free of
-// bank conflicts.  Waves 0-1 decode A and waves 2-3 B, thread t rows t % 128
-// and t % 128 + 128 of its operand: the raw E2M1 bytes and E4M3 scales of
-// K-step k + 1 are decoded into the other stage, one fp16 pair at a time,
-// between the MFMAs of step k, and the raw bytes of step k + 2 are already
-// being loaded.  One barrier per K-step, placed before the
-// last MFMAs so that the next step's first fragments are read under them.  B is
-// the MFMA's first operand, so each lane holds an output row (see store_tile.h).
-// Tiles are handed out XCD-aware in 4 x 8 blocks of one group, as in the MXFP8
-// GEMM, so the operand rows that the 32 workgroups of an XCD stream meet in its
-// L2.
+// 4 x 4 MFMA blocks of 32 x 32 (256 accumulator registers per lane).  What LDS
+// holds is the packed operands, not decoded ones: a 3-deep ring of stages of
+// two K-steps (64 bytes of E2M1 per row, XOR chunk swizzle) plus each row's
+// E4M3 scale bytes of the stage, all copied global -> LDS by the buffer unit
+// (LDS-DMA), a quarter of the LDS traffic of staging fp16.  Each wave reads,
+// per K-step, 16 bytes and one scale dword for each of its 4 + 4 row blocks
+// and decodes its own fragments: a lane's 16 bytes hold 32 consecutive
+// elements, of which MFMA substep S takes dword S, and A and B lanes take the
+// same elements in the same substep, so the contraction runs over the K-step's
+// 64 elements in a permuted order.  The next K-step's bytes are read during
+// the first substep and each next substep is decoded under the current one's
+// MFMAs.  One barrier per stage; the copies of the stage three ahead are spread
+// over the substeps that follow it.  Tiles are software-pipelined: the next
+// tile's first stages and outer scales are copied before this tile's epilogue
+// stores, and the epilogue reads one 32 x 32 accumulator block at a time.  B
+// is the MFMA's first operand, so each lane holds an output row (see
+// store_tile.h).  Tiles are handed out XCD-aware in 4 x 8 blocks of one group,
+// as in the MXFP8 GEMM, so the operand rows that the 32 workgroups of an XCD
+// stream meet in its L2.
 #include <utility>
 
+#include "lds_dma.h"
 #include "store_tile.h"
 
 namespace bsg {
@@ -56,15 +64,36 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 constexpr int BM = 256;
 constexpr int BN = 256;
-constexpr int BK = 64;          // elements per K-step (32 bytes of E2M1 per row)
+constexpr int BK = 64;                  // elements per K-step: four 16-deep MFMA substeps
+constexpr int kStageK = 2 * BK;         // elements per LDS stage (two K-steps)
+constexpr int kRowB = kStageK / 2;      // staged E2M1 bytes per row: 64
+constexpr int kStages = 3;              // LDS ring depth
 constexpr int kThreads = 256;
-constexpr int kDecodeSlots = 48; // the next step's decode is spread over MFMA slots 0 .. 47
-constexpr int kBarrierSlot = 4;  // MFMA slot of the last substep after which the step barriers
-constexpr int kSuperM = 4, kSuperN = 8;  // tile block one XCD works on
+constexpr int kOpB = BM * kRowB;        // one operand's rows of a stage: 16 KiB
+constexpr int kSclRowB = 16;            // staged scale bytes per row (room for the 2-byte form)
+constexpr int kSclOpB = BM * kSclRowB;  // 4 KiB
+constexpr int kStageB = 2 * kOpB + 2 * kSclOpB;  // A rows, B rows, A scales, B scales
+constexpr int kBarrierSlot = 2;         // MFMA slot of an odd K-step's first substep after
+                                        // which it waits for the next stage and barriers
+constexpr int kSuperM = 4, kSuperN = 8; // tile block one XCD works on
+
+// How a stage's E4M3 block scales are copied, from the contraction length k:
+//   kSclDword  k % 64 == 0: a row's scale bytes of a stage are two aligned dwords,
+//              one per K-step (4-byte copies; 8 staged bytes per row)
+//   kSclShort  k % 64 == 32: the row stride k / 16 is only 2-aligned: four 2-byte
+//              copies per row, (K-step ks, half h) into dword 2 ks + h
+constexpr int kSclDword = 0, kSclShort = 1;
+template <int SM>
+constexpr int scl_row_bytes() { return SM == kSclDword ? 8 : 16; }
+template <int SM>
+constexpr int scl_copies() { return SM == kSclDword ? 2 : 4; }  // per operand, wave and stage
+template <int SM>
+constexpr int copies_per_stage() { return 8 + 2 * scl_copies<SM>(); }  // per wave
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v4i lds_v4i;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
 typedef __attribute__((address_space(3))) float lds_f32;
 
 struct NvArgs {
@@ -89,50 +118,35 @@ struct NvArgs {
   NvGroupTable tab;
 };
 
-static_assert(BM == BN, "A and B stage halves share one layout");
-// the next step's decode units (slots 0 .. kDecodeSlots - 1 of the 64) must all
-// be written before the step's barrier, which follows the decode of slot
-// 48 + kBarrierSlot: a later unit would write the stage other waves then read
-static_assert(kDecodeSlots <= 3 * 16 + kBarrierSlot + 1 && kDecodeSlots <= 64 &&
-                  kBarrierSlot >= 0 && kBarrierSlot < 16,
-              "decode must finish before the step's barrier");
-constexpr int kHalfStage = BM * 128;  // one operand's rows of one K-step, fp16
-constexpr int kOperandB = 2 * kHalfStage;
-
 struct Smem {
-  // A stage 0, A stage 1, B stage 0, B stage 1: every offset between the
-  // stages, and between rows r and r + 128, fits an LDS instruction's
-  // immediate offset field
-  uint8_t stage[4][kHalfStage];
-  float aout[BM];
-  float bout[BN];
+  uint8_t ring[kStages][kStageB];
+  float aout[2][BM];  // outer scales of a tile's rows and columns, for its epilogue;
+  float bout[2][BN];  // two sets, so the next tile's can land during this one's
   int64_t off[kMaxGroups + 1];
   int32_t cnt[kMaxGroups];
   int32_t pre[kMaxGroups + 1];
 };
 
-// LDS byte offset of 16-byte chunk c (fp16 elements 8 c .. 8 c + 7) of row r:
-// the chunk is XORed with a 3-bit term of r % 16.  Over 8 aligned rows the term
-// takes 8 values (as over the even and the odd rows of 16 aligned ones), and its
-// low two bits 4 values over 4 aligned rows (as over the even and the odd rows
-// of 8 aligned ones), so both 16-byte access patterns used here -- one chunk of
-// 64 consecutive rows (fragment reads), and chunks q and q + 4 of 32 rows by
-// lane pairs (decode stores) -- are conflict-free whether the LDS serves 8
-// lanes per 128-byte bank window or 16 lanes per 256-byte window.
-__device__ __forceinline__ int swz(int row, int chunk) {
-  const int term = (row & 3) ^ (((row >> 2) & 1) * 5) ^ ((row >> 3) & 1);
-  return row * 128 + ((chunk ^ term) << 4);
+// Staged rows are 64 bytes, four 16-byte chunks; logical chunk c of row r sits
+// in slot c ^ sw4(r).  sw4 takes bits 1..3 of r, so it is the same for rows 16
+// apart (every copy covers 16 aligned rows, every fragment read 32), and both
+// the 16 rows that one read cycle of a 64-bank LDS serves and the 8 of a
+// 32-bank one land on distinct banks.
+__device__ __forceinline__ int sw4(int r) {
+  return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1);
 }
 
 __device__ __forceinline__ v4i lds_read16(uint32_t addr) {
   return *reinterpret_cast<const lds_v4i*>((size_t)addr);
 }
-__device__ __forceinline__ void lds_write16(uint32_t addr, v4i v) {
-  *reinterpret_cast<lds_v4i*>((size_t)addr) = v;
+__device__ __forceinline__ uint32_t lds_read4(uint32_t addr) {
+  return *reinterpret_cast<const lds_u32*>((size_t)addr);
 }
 
 // One byte (two E2M1 nibbles, low nibble first) of dword w, times the block
 // scale (in both halves of sd2), as a packed fp16 pair (low element first).
+// The convert takes only the exponent of its scale operand, so the E4M3 scale
+// is applied by the multiply (exact: at most 6 significant bits).
 template <int SEL>
 __device__ __forceinline__ uint32_t dq_pair(uint32_t w, v2h sd2) {
   const v2h f = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
@@ -145,77 +159,14 @@ __device__ __forceinline__ v2h e4m3_pair_h2(uint32_t c) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c, 1.0f, false);
 }
 
-// Per-lane LDS offsets, computed once per tile and kept opaque so that the
-// compiler does not materialize one address per access.
-struct Offs {
-  int dec[4];       // chunk 4 hf + q of this thread's first decoded row (see Raw)
-  int fa[4], fb[4]; // fragment part S: row wm*128 + r (A) / wn*128 + r (B), chunk 2 S + h
-  int ssh;          // 16 hf: this thread's scale bytes within a row's scale word
-};
-
-__device__ __forceinline__ Offs make_offs(int tid, int wm, int wn, int r, int h) {
-  Offs o;
-  const int hf = tid & 1, r0 = (tid & 127) >> 1;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    o.dec[q] = (tid >= 128 ? kOperandB : 0) + swz(r0, 4 * hf + q);
-    asm volatile("" : "+v"(o.dec[q]));
-  }
-  o.ssh = 16 * hf;
-#pragma unroll
-  for (int S = 0; S < 4; ++S) {
-    o.fa[S] = swz(wm * 128 + r, 2 * S + h);
-    o.fb[S] = kOperandB + swz(wn * 128 + r, 2 * S + h);
-    asm volatile("" : "+v"(o.fa[S]));
-    asm volatile("" : "+v"(o.fb[S]));
-  }
-  return o;
-}
-
-// 16 raw bytes (32 elements, two 16-element blocks with scales s0, s1) -> 32
-// fp16, written as this thread's four 16-byte chunks of a row at `base`
-// relative to its first row.
-__device__ __forceinline__ void decode_store(uint32_t base, const Offs& o, const v4i& d, v2h s0,
-                                             v2h s1) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t w = (uint32_t)d[q];
-    const v2h sd = q < 2 ? s0 : s1;
-    v4i v;
-    v[0] = (int)dq_pair<0>(w, sd);
-    v[1] = (int)dq_pair<1>(w, sd);
-    v[2] = (int)dq_pair<2>(w, sd);
-    v[3] = (int)dq_pair<3>(w, sd);
-    lds_write16(base + o.dec[q], v);
-  }
-}
-
-// Raw E2M1 bytes of one K-step for this thread: waves 0 and 1 decode A,
-// waves 2 and 3 B; with u = tid % 128, half hf = u % 2 (16 of the row's 32
-// bytes) of rows u / 2 + 64 j, j = 0 .. 3.  The two threads of a row sit in
-// adjacent lanes, so each load instruction reaches 32 rows, not 64.
-struct Raw {
-  v4i d[4];
-};
-
-// E4M3 block-scale words of two K-steps (kt, kt + 1; kt even) for the same
-// four rows: word x of step kt, y of kt + 1, four scales each.
-struct Scl {
-  v2i s[4];
-};
-
 struct TileDesc {
   const uint8_t* a;
   const uint8_t* as;
   const uint8_t* b;
   const uint8_t* bs;
-  int64_t lda, ldas;  // bytes per row: k/2 and k/16
+  int64_t lda, ldas;  // bytes per row: k/2 and k/16 (the same for both operands)
   int a_rows, b_rows;
   int64_t kl;
-};
-
-struct Rsrc {
-  __amdgpu_buffer_rsrc_t d, s, none;  // this thread's operand and its scales
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
@@ -223,166 +174,350 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
                                            0x00020000);
 }
 
-// How a row's E4M3 scale words are loaded, from the contraction length k:
-//   kScalePaired  k % 128 == 0: the two words of a step pair, one aligned 8-byte load
-//   kScaleWord    k % 64 == 0: one aligned 4-byte load per step
-//   kScaleHalf    k % 64 == 32: the row stride k / 16 is only 2-aligned and the last
-//                 step is half past k: each thread loads its own two scale bytes
-//                 (2-byte loads), and its raw bytes and scales past k read as zeros
-constexpr int kScalePaired = 0, kScaleWord = 1, kScaleHalf = 2;
+// A wavefront's share of one stage's copies: rows [64 w, 64 w + 64) of both
+// operands, 16 rows (1 KiB) per data copy -- in copy q lane l fills row
+// 64 w + 16 q + l / 4, slot l % 4, which must hold logical chunk
+// (l % 4) ^ sw4(l / 4) -- and the same rows' scale bytes of the stage (32 rows
+// of two dwords, or 16 rows of four 2-byte pieces, per copy).  A chunk or scale
+// piece that starts at or past the contraction end is given an offset past
+// every range, so it lands as zeros (the bytes there belong to the next row).
+struct Dma {
+  v4i ra, rb, rsa, rsb;  // descriptors (uniform)
+  int src;               // lane data offset, copy q = 0, stage 0
+  int kc;                // first element of its chunk within a stage
+  int ld16;              // 16 rows of data stride (uniform)
+  int ssrc;              // lane scale offset, copy q = 0, stage 0
+  int skc;               // first element its scale piece covers within a stage
+  int sstep;             // rows of one scale copy times the scale row stride (uniform)
+  int kl;                // contraction length (uniform)
+};
 
-// An offset past every descriptor's range: the buffer unit returns zeros.
-constexpr int kOutOfRange = 0x7ffffff0;
-
-// This thread's raw bytes of K-step kt.  Rows past the valid ones, and steps
-// past the last (`live` false), read as zeros; with kScaleHalf so does a
-// half step past the contraction end (the bytes there are the next row's).
 template <int SM>
-__device__ __forceinline__ void load_raw(const TileDesc& t, const Rsrc& rs, int kt, bool live,
-                                         int tid, Raw& x) {
-  int od = ((tid & 127) >> 1) * (int)t.lda + (tid & 1) * 16 + kt * (BK / 2);
-  if constexpr (SM == kScaleHalf)
-    if (kt * BK + (tid & 1) * (BK / 2) >= (int)t.kl) od = kOutOfRange;
-  const int rstep = 64 * (int)t.lda;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    x.d[j] = __builtin_amdgcn_raw_buffer_load_b128(live ? rs.d : rs.none,
-                                                   od == kOutOfRange ? od : od + j * rstep, 0, 0);
+__device__ __forceinline__ Dma make_dma(const TileDesc& t, int w, int lane) {
+  Dma d;
+  d.ra = make_rsrc_words(t.a, (int64_t)t.a_rows * t.lda);
+  d.rb = make_rsrc_words(t.b, (int64_t)t.b_rows * t.lda);
+  d.rsa = make_rsrc_words(t.as, (int64_t)t.a_rows * t.ldas);
+  d.rsb = make_rsrc_words(t.bs, (int64_t)t.b_rows * t.ldas);
+  const int c = (lane & 3) ^ sw4(lane >> 2);
+  d.src = (64 * w + (lane >> 2)) * (int)t.lda + 16 * c;
+  d.kc = 32 * c;
+  d.ld16 = __builtin_amdgcn_readfirstlane(16 * (int)t.lda);
+  if constexpr (SM == kSclDword) {
+    d.ssrc = (64 * w + (lane >> 1)) * (int)t.ldas + 4 * (lane & 1);
+    d.skc = BK * (lane & 1);
+    d.sstep = __builtin_amdgcn_readfirstlane(32 * (int)t.ldas);
+  } else {
+    d.ssrc = (64 * w + (lane >> 2)) * (int)t.ldas + 2 * (lane & 3);
+    d.skc = (BK / 2) * (lane & 3);
+    d.sstep = __builtin_amdgcn_readfirstlane(16 * (int)t.ldas);
+  }
+  d.kl = __builtin_amdgcn_readfirstlane((int)t.kl);
+  return d;
 }
 
-// The scale words of K-steps kt and kt + 1 (kt even) for this thread's rows;
-// with kScalePaired / kScaleWord both threads of a row load the same bytes, one
-// request, and a step past the last reads as zero.  With kScaleHalf thread half
-// hf loads only the two bytes it decodes, into bits 16 hf .. 16 hf + 15 of the
-// word (where the decode takes them from).
-template <int SM>
-__device__ __forceinline__ void load_scales(const TileDesc& t, const Rsrc& rs, int kt, int nk,
-                                            int tid, Scl& x) {
-  const int os = ((tid & 127) >> 1) * (int)t.ldas + kt * (BK / 16);
-  const int rstep = 64 * (int)t.ldas;
-  const bool l0 = kt < nk, l1 = kt + 1 < nk;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if constexpr (SM == kScalePaired) {
-      x.s[j] = __builtin_amdgcn_raw_buffer_load_b64(l0 ? rs.s : rs.none, os + j * rstep, 0, 0);
-    } else if constexpr (SM == kScaleWord) {
-      x.s[j][0] = __builtin_amdgcn_raw_buffer_load_b32(l0 ? rs.s : rs.none, os + j * rstep, 0, 0);
-      x.s[j][1] =
-          __builtin_amdgcn_raw_buffer_load_b32(l1 ? rs.s : rs.none, os + j * rstep + 4, 0, 0);
-    } else {
-      const int hf = tid & 1;
-      const int kl = (int)t.kl;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int k0 = (kt + e) * BK + hf * (BK / 2);  // first element of this half step
-        const int off = k0 < kl ? os + 4 * e + 2 * hf + j * rstep : kOutOfRange;
-        const uint32_t v = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(
-            (e ? l1 : l0) ? rs.s : rs.none, off, 0, 0);
-        x.s[j][e] = (int)(v << (16 * hf));
-      }
-    }
+// Copy Q of this wave's share of stage sp into ring buffer `buf`: Q 0..3 A
+// rows, 4..7 B rows, then the A and B scale copies.  A stage past the last
+// (sp * 128 >= kl) has every piece past the contraction end, so it lands as
+// zeros without reading.
+template <int Q, int SM>
+__device__ __forceinline__ void dma_piece(const Dma& d, uint32_t ring, int w, int buf, int sp) {
+  const uint32_t st = ring + (uint32_t)(buf * kStageB);
+  constexpr int SC = scl_copies<SM>();
+  if constexpr (Q < 8) {
+    constexpr int op = Q >> 2, q = Q & 3;
+    const int off = d.kc + kStageK * sp < d.kl ? d.src + q * d.ld16 + kRowB * sp : kDmaOutOfRange;
+    dma16(op ? d.rb : d.ra, st + op * kOpB + (64 * w + 16 * q) * kRowB, off);
+  } else {
+    constexpr int op = (Q - 8) / SC, q = (Q - 8) % SC;
+    constexpr int rows = 64 / SC;  // rows per scale copy
+    const uint32_t dst =
+        st + 2 * kOpB + op * kSclOpB + (64 * w + rows * q) * scl_row_bytes<SM>();
+    const int off = d.skc + kStageK * sp < d.kl ? d.ssrc + q * d.sstep + (kStageK / 16) * sp
+                                                : kDmaOutOfRange;
+    if constexpr (SM == kSclDword) dma4(op ? d.rsb : d.rsa, dst, off);
+    else dma2(op ? d.rsb : d.rsa, dst, off);
   }
 }
 
-// This thread's two block scales of row j in scale word w, as fp16.
-__device__ __forceinline__ v2h row_scales(uint32_t w, const Offs& o) {
-  return e4m3_pair_h2(w >> o.ssh);
-}
+// Per-lane LDS offsets of the fragment reads within a stage, for its K-steps
+// ks = 0, 1.  Lane (r, h) of wave (wm, wn) reads, of rows wm*128 + 32 i + r of A
+// (wn*128 + 32 j + r of B), the 16 bytes of K-step ks that hold elements
+// 32 h .. 32 h + 31 (logical chunk 2 ks + h), and the dword that holds the
+// scales of their blocks 2 h and 2 h + 1 (bits ssh .. ssh + 15).
+struct Frag {
+  int da[2], db[2], sa[2], sb[2];
+  int ssh;
+};
 
-// Row J of this thread's decode of one K-step (scale words in `sw`) into the
-// stage at `st`.
-template <int J>
-__device__ __forceinline__ void decode_row(uint32_t st, const Offs& o, const Raw& x,
-                                           const uint32_t (&sw)[4]) {
-  const v2h s01 = row_scales(sw[J], o);
-  decode_store(st + J * 64 * 128, o, x.d[J], v2h{s01[0], s01[0]}, v2h{s01[1], s01[1]});
-}
-
-// Decode unit U (0..63) of a K-step: row U / 16 (as decode_row), word
-// (U / 4) % 4 of its 16 raw bytes, nibble pair U % 4 -> one fp16 pair into
-// `buf`; the fourth pair of a word writes the 16-byte chunk to LDS.  Spread one
-// or two per MFMA slot, the decode's VALU work runs under the MFMAs.
-template <int U>
-__device__ __forceinline__ void decode_unit(uint32_t st, const Offs& o, const Raw& x,
-                                            const uint32_t (&sw)[4], v2h (&sd)[2], v4i& buf) {
-  constexpr int J = U / 16, q = (U / 4) % 4, pr = U % 4;
-  if constexpr (U % 16 == 0) {
-    const v2h s01 = row_scales(sw[J], o);
-    sd[0] = v2h{s01[0], s01[0]};
-    sd[1] = v2h{s01[1], s01[1]};
+template <int SM>
+__device__ __forceinline__ Frag make_frag(int wm, int wn, int r, int h) {
+  Frag f;
+  constexpr int SR = scl_row_bytes<SM>();
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int c = ((2 * ks + h) ^ sw4(r)) << 4;
+    const int sd = SM == kSclDword ? 4 * ks : 4 * (2 * ks + h);
+    f.da[ks] = (wm * 128 + r) * kRowB + c;
+    f.db[ks] = kOpB + (wn * 128 + r) * kRowB + c;
+    f.sa[ks] = 2 * kOpB + (wm * 128 + r) * SR + sd;
+    f.sb[ks] = 2 * kOpB + kSclOpB + (wn * 128 + r) * SR + sd;
+    asm volatile("" : "+v"(f.da[ks]));
+    asm volatile("" : "+v"(f.db[ks]));
+    asm volatile("" : "+v"(f.sa[ks]));
+    asm volatile("" : "+v"(f.sb[ks]));
   }
-  const uint32_t w = (uint32_t)x.d[J][q];
-  buf[pr] = (int)dq_pair<pr>(w, q < 2 ? sd[0] : sd[1]);
-  if constexpr (pr == 3) lds_write16(st + J * 64 * 128 + o.dec[q], buf);
+  f.ssh = SM == kSclDword ? 16 * h : 0;
+  return f;
+}
+
+// One K-step's packed operands of this lane: 16 bytes and a scale dword for
+// each of its four A and four B row blocks (0..3 A, 4..7 B).
+struct Raw {
+  v4i d[8];
+  uint32_t s[8];
+};
+
+// Read item I (0..15) of a K-step from the stage at `st`: I < 8 the data of
+// row block I, else the scale dword of row block I - 8.
+template <int I, int KS, int SM>
+__device__ __forceinline__ void read_item(uint32_t st, const Frag& f, Raw& x) {
+  constexpr int SR = scl_row_bytes<SM>();
+  if constexpr (I < 4) x.d[I] = lds_read16(st + f.da[KS] + 32 * I * kRowB);
+  else if constexpr (I < 8) x.d[I] = lds_read16(st + f.db[KS] + 32 * (I - 4) * kRowB);
+  else if constexpr (I < 12) x.s[I - 8] = lds_read4(st + f.sa[KS] + 32 * (I - 8) * SR);
+  else x.s[I - 8] = lds_read4(st + f.sb[KS] + 32 * (I - 12) * SR);
+}
+
+// Half HALF (fp16 pairs 2 HALF, 2 HALF + 1) of the decoded fragment of substep
+// S of a row block: dword S of its 16 bytes (elements 32 h + 8 S .. + 7, all in
+// block 2 h + S / 2) times that block's scale.  A and B lanes hold the same
+// elements in every substep, so the substeps together contract all 64 elements
+// of the K-step in a permuted order.
+template <int S, int HALF>
+__device__ __forceinline__ void decode_half(const v4i& x, v2h s01, v4i& out) {
+  const uint32_t w = (uint32_t)x[S];
+  const _Float16 s = s01[S >> 1];
+  const v2h s2 = v2h{s, s};
+  out[2 * HALF] = (int)dq_pair<2 * HALF>(w, s2);
+  out[2 * HALF + 1] = (int)dq_pair<2 * HALF + 1>(w, s2);
 }
 
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 
-// The fragments of substep S (16 elements of the K-step) for this lane: rows
-// wm*128 + 32 i + r of A, wn*128 + 32 j + r of B, elements 16 S + 8 h .. + 7.
-template <int S>
-__device__ __forceinline__ void read_frags(uint32_t st, const Offs& o, v8h (&fa)[4],
-                                           v8h (&fb)[4]) {
-  // rows 32 apart share the lane's swizzle term: the row step is an immediate
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    fa[i] = __builtin_bit_cast(v8h, lds_read16(st + o.fa[S] + 32 * i * 128));
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    fb[j] = __builtin_bit_cast(v8h, lds_read16(st + o.fb[S] + 32 * j * 128));
-}
-
+// B is the MFMA's first operand and A its second, so each lane holds output
+// rows (see store_tile.h).
 template <int M>
-__device__ __forceinline__ void mfma(const v8h (&fa)[4], const v8h (&fb)[4], v16f (&acc)[4][4]) {
+__device__ __forceinline__ void mfma(const v4i (&df)[8], v16f (&acc)[4][4]) {
   constexpr int i = M >> 2, j = M & 3;
-  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, df[4 + j]),
+                                                      __builtin_bit_cast(v8h, df[i]), acc[i][j],
+                                                      0, 0, 0);
   asm volatile("" : "+a"(acc[i][j]));  // keeps the pure intrinsic in schedule order
 }
 
-// One K-step from stage `cur` (its substep-0 fragments already in f0): while
-// its 64 MFMAs run, decode the raw bytes of the next step (xn, scale words sw)
-// into stage `nxt`, load the raw bytes of the step after it (into xl) and, for
-// an even step (SCALES), the scale words of that step and the next (into sl),
-// read each next substep's fragments, and after the barrier the next step's
-// first fragments.
-template <bool SCALES, int SM>
-__device__ __forceinline__ void k_step(uint32_t cur, uint32_t nxt, const TileDesc& t,
-                                       const Rsrc& rs, int kt, int nk, int tid, const Offs& o,
-                                       const Raw& xn, const uint32_t (&sw)[4], Raw& xl, Scl& sl,
-                                       v8h (&f0a)[4], v8h (&f0b)[4], v8h (&f1a)[4],
-                                       v8h (&f1b)[4], v16f (&acc)[4][4]) {
-  load_raw<SM>(t, rs, kt + 2, kt + 2 < nk, tid, xl);
-  if constexpr (SCALES) load_scales<SM>(t, rs, kt + 2, nk, tid, sl);
-  v2h sd[2];
-  v4i buf;
-  static_for<4>([&](auto sc) {
-    constexpr int S = decltype(sc)::value;
-    v8h(&ca)[4] = (S & 1) ? f1a : f0a;
-    v8h(&cb)[4] = (S & 1) ? f1b : f0b;
-    v8h(&na)[4] = (S & 1) ? f0a : f1a;
-    v8h(&nb)[4] = (S & 1) ? f0b : f1b;
+// K-step 2 sp + ODD of stage sp (ring buffer sp % 3), whose substep-0
+// fragments are decoded in d0 and whose operands and block scales are in xc and
+// sc.  Between its 64 MFMAs: the next K-step's operands are read into xn during
+// the first substep (an odd step first waits until the next stage has landed
+// for every wave and barriers; by then every wave has read the last of stage
+// sp), each next substep's fragments are decoded, and during the fourth
+// substep the next K-step's scales (into sn) and substep-0 fragments (into d0)
+// follow.  An odd step also issues, spread over its last three substeps, the
+// copies of stage sp + 3 into the buffer that stage sp leaves; at its barrier
+// the copies issued after stage sp + 1's are exactly those of stage sp + 2.
+template <bool ODD, int SM>
+__device__ __forceinline__ void k_step(uint32_t ring, const Dma& d, const Frag& f, int w, int sp,
+                                       int np, const Raw& xc, const v2h (&sc)[8], Raw& xn,
+                                       v2h (&sn)[8], v4i (&d0)[8], v4i (&d1)[8],
+                                       v16f (&acc)[4][4]) {
+  constexpr int KS = ODD ? 0 : 1;  // the next K-step's half of its stage
+  constexpr int kCopies = copies_per_stage<SM>();
+  constexpr int kReadSlot = ODD ? kBarrierSlot + 1 : 0;
+  constexpr int kCopyGap = 48 / kCopies;  // the copies spread over substeps 1 .. 3
+  static_assert(kReadSlot + 8 <= 16 && kCopyGap >= 1, "K-step schedule");
+  const bool more = !ODD || sp + 1 < np;
+  const uint32_t rd = ring + (uint32_t)(((ODD ? sp + 1 : sp) % kStages) * kStageB);
+  static_for<4>([&](auto sc_) {
+    constexpr int S = decltype(sc_)::value;
+    v4i(&cur)[8] = (S & 1) ? d1 : d0;
+    v4i(&nxt)[8] = (S & 1) ? d0 : d1;
     static_for<16>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
-      mfma<m>(ca, cb, acc);
+      constexpr int b = m >> 1;  // the row block this slot decodes
+      mfma<m>(cur, acc);
       fence();
-      if constexpr (m == 0 && S < 3) read_frags<S + 1>(cur, o, na, nb);
-      // decode units assigned to this slot: U with floor(U * kDecodeSlots / 64) == slot
-      constexpr int slot = 16 * S + m;
-      constexpr int u0 = (slot * 64 + kDecodeSlots - 1) / kDecodeSlots;
-      constexpr int u1 = ((slot + 1) * 64 + kDecodeSlots - 1) / kDecodeSlots;
-      if constexpr (slot < kDecodeSlots) {
-        static_for<(u1 < 64 ? u1 : 64) - u0>([&](auto uc) {
-          decode_unit<u0 + decltype(uc)::value>(nxt, o, xn, sw, sd, buf);
-        });
+      if constexpr (S == 0) {
+        if constexpr (ODD && m == kBarrierSlot)
+          asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kCopies) : "memory");
+        if constexpr (m >= kReadSlot && m < kReadSlot + 8) {
+          if (more) {
+            read_item<m - kReadSlot, KS, SM>(rd, f, xn);
+            read_item<m - kReadSlot + 8, KS, SM>(rd, f, xn);
+          }
+        }
       }
-      if constexpr (S == 3 && m == kBarrierSlot) {
-        // the decode of the next step is in LDS and nobody still reads `cur`
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        read_frags<0>(nxt, o, na, nb);
+      // one copy every kCopyGap MFMA slots from the second substep on, so
+      // that the copies do not queue up behind each other in the memory pipe
+      constexpr int slot = 16 * S + m - 16;
+      if constexpr (ODD && slot >= 0 && slot % kCopyGap == 0 && slot / kCopyGap < kCopies)
+        dma_piece<slot / kCopyGap, SM>(d, ring, w, (sp + 3) % kStages, sp + 3);
+      if constexpr (S < 3) {
+        decode_half<S + 1, m & 1>(xc.d[b], sc[b], nxt[b]);
+      } else {
+        if constexpr ((m & 1) == 0) sn[b] = e4m3_pair_h2(xn.s[b] >> f.ssh);
+        decode_half<0, m & 1>(xn.d[b], sn[b], nxt[b]);
       }
       fence();
     });
   });
+}
+
+// The epilogue of a tile, one 32 x 32 block at a time: the block's
+// accumulators are read into a temporary (pinned to that block, so that the
+// whole tile is never copied out of the accumulators at once), scaled by
+// a_outer[r] * b_outer[n] when fused, and stored (or, ACC, added to the
+// output's previous contents and stored).
+template <bool F32, bool WIDE, bool ACC>
+__device__ __forceinline__ void epilogue_tile(const v16f (&acc)[4][4], bool fused,
+                                              uint32_t ao_base, uint32_t bo_base,
+                                              __amdgpu_buffer_rsrc_t ro, int ldc, int row, int col,
+                                              int h, int out_cols) {
+  static_for<16>([&](auto bc) {
+    constexpr int i = decltype(bc)::value >> 2, j = decltype(bc)::value & 3;
+    fence();
+    v16f y = acc[i][j];
+    asm volatile("" : "+v"(y));
+    if (fused) {
+      const float ao = *reinterpret_cast<const lds_f32*>((size_t)(ao_base + 4 * (row + 32 * i)));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const v4i bo = lds_read16(bo_base + 4 * (col + 32 * j + 8 * q));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[4 * q + e] = (y[4 * q + e] * ao) * __int_as_float(bo[e]);
+      }
+    }
+    const int rr = row + 32 * i, cc = col + 32 * j;
+    if constexpr (ACC) {
+      // copy-or-accumulate: Y + the output's previous value, rounded once
+      EpiTerms ep;
+      ep.alpha = 1.0f;
+      ep.beta = 1.0f;
+      ep.has_bias = false;
+      ep.bias = ro;
+      store_block_ex<WIDE, F32>(y, ro, ldc, rr, cc, out_cols, ep);
+    } else {
+      store_block<WIDE, F32>(y, ro, ldc, rr, cc, h, out_cols);
+    }
+    fence();
+  });
+}
+
+// What a tile's epilogue needs besides its TileDesc.
+struct TileJob {
+  TileDesc t;
+  int64_t out_off, ld_out;  // element offset of the tile's first output, row stride
+};
+
+// Tile `tile`'s descriptor, output position and outer-scale sources.
+template <bool WGRAD>
+__device__ __forceinline__ TileJob make_job(const NvArgs& p, const Smem& sm, int G, int tile,
+                                            int& g, const float*& aout_t, const float*& bout_t) {
+  g = __builtin_amdgcn_readfirstlane(find_group(sm.pre, G, tile));
+  const int local = tile - sm.pre[g];
+  TileJob job;
+  TileDesc& t = job.t;
+  if constexpr (WGRAD) {
+    const int64_t mp = group_extent(sm.off, g);
+    const bool usable = sm.off[g] % kColPad == 0 && mp % kColPad == 0;
+    int mt, nt;
+    super_tile<kSuperM, kSuperN>(local, (int)((p.n + BM - 1) / BM), (int)((p.k + BN - 1) / BN),
+                                 mt, nt);
+    const int64_t i0 = (int64_t)mt * BM, j0 = (int64_t)nt * BN;
+    t.lda = mp / 2;
+    t.ldas = mp / 16;
+    t.a = p.a + sm.off[g] * p.n / 2 + i0 * t.lda;
+    t.as = p.as + sm.off[g] * p.n / 16 + i0 * t.ldas;
+    t.b = p.b + sm.off[g] * p.k / 2 + j0 * t.lda;
+    t.bs = p.bs + sm.off[g] * p.k / 16 + j0 * t.ldas;
+    t.a_rows = (int)(p.n - i0 < BM ? p.n - i0 : BM);
+    t.b_rows = (int)(p.k - j0 < BN ? p.k - j0 : BN);
+    t.kl = usable ? mp : 0;
+    aout_t = p.aout + (int64_t)g * p.n + i0;
+    bout_t = p.bout + (int64_t)g * p.k + j0;
+    job.out_off = ((int64_t)g * p.n + i0) * p.k + j0;
+    job.ld_out = p.k;
+  } else {
+    const int64_t m = group_extent(sm.off, g);
+    const int64_t ng = p.tab.n[g];
+    int mt, nt;
+    super_tile<kSuperM, kSuperN>(local, (int)((m + BM - 1) / BM), (int)((ng + BN - 1) / BN), mt,
+                                 nt);
+    const int64_t row0 = sm.off[g] + (int64_t)mt * BM;
+    const int64_t n0 = (int64_t)nt * BN;
+    const int64_t brow0 = p.tab.brow[g] + n0;
+    t.lda = p.k / 2;
+    t.ldas = p.k / 16;
+    t.a = p.a + row0 * t.lda;
+    t.as = p.as + row0 * t.ldas;
+    t.b = p.b + brow0 * t.lda;
+    t.bs = p.bs + brow0 * t.ldas;
+    const int64_t rv = sm.off[g] + m - row0, cv = ng - n0;
+    t.a_rows = (int)(rv < BM ? rv : BM);
+    t.b_rows = (int)(cv < BN ? cv : BN);
+    t.kl = p.k;
+    aout_t = p.aout + row0;
+    bout_t = p.bout + brow0;
+    job.out_off = row0 * p.ld_out + n0;
+    job.ld_out = p.ld_out;
+  }
+  return job;
+}
+
+// The start of tile `tile`: the copies of its first three stages into ring
+// buffers 0, 1, 2, and its outer scales into outer-scale set `set` (copied by
+// the buffer unit too; zeros for rows and columns past the tile's and for a
+// tile with nothing to contract, whose output is then exactly 0).  The caller
+// waits for all of it (vmcnt(0) and a barrier) before use; the ring and the
+// set must be free.
+template <int SM, bool WGRAD>
+__device__ __forceinline__ void start_tile(const NvArgs& p, Smem& sm, uint32_t ring, int G,
+                                           int tile, int set, int tid) {
+  // opaque copy of the thread index: keeps the per-lane copy offsets from being
+  // hoisted out of the tile loop (and spilled)
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int g;
+  const float* aout_t;
+  const float* bout_t;
+  const TileJob job = make_job<WGRAD>(p, sm, G, tile, g, aout_t, bout_t);
+  const TileDesc& t = job.t;
+  const bool contract = t.kl > 0;
+  // per-tensor NVFP4: alpha_g = tsi(amax_A[g]) * tsi(amax_B[g]) on every row,
+  // 1 on every column, so the epilogue computes S * alpha_g (read before the
+  // copies are issued, so that waiting for it does not wait for them)
+  const bool pt = !WGRAD && p.per_tensor;
+  const float alpha = pt ? (p.aout[g] / 2688.0f) * (p.bout[g] / 2688.0f) : 0.0f;
+  if (contract) {
+    const Dma d = make_dma<SM>(t, w, lane);
+    for (int sp = 0; sp < 3; ++sp)
+      static_for<copies_per_stage<SM>()>([&](auto qc) {
+        dma_piece<decltype(qc)::value, SM>(d, ring, w, sp, sp);
+      });
+  }
+  const uint32_t ao = (uint32_t)(size_t)(__attribute__((address_space(3))) float*)sm.aout[set];
+  const uint32_t bo = (uint32_t)(size_t)(__attribute__((address_space(3))) float*)sm.bout[set];
+  if (pt) {
+    sm.aout[set][tid] = contract && tid < t.a_rows ? alpha : 0.0f;
+    sm.bout[set][tid] = contract && tid < t.b_rows ? 1.0f : 0.0f;
+  } else {
+    // wave w copies rows / columns 64 w .. 64 w + 63
+    dma4(make_rsrc_words(aout_t, contract ? (int64_t)t.a_rows * 4 : 0), ao + 256 * w,
+         4 * (64 * w + lane));
+    dma4(make_rsrc_words(bout_t, contract ? (int64_t)t.b_rows * 4 : 0), bo + 256 * w,
+         4 * (64 * w + lane));
+  }
 }
 
 // WGRAD: expert g contracts its padded tokens, A = dY^T_g [n, m~_g], B =
@@ -411,129 +546,70 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
   wave0_exclusive_scan(sm.cnt, G, sm.pre);
   __syncthreads();
   const int total = sm.pre[G];
-  const uint32_t st0 = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)sm.stage[0];
-  const uint32_t st1 = st0 + kHalfStage;
+  const uint32_t ring = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)sm.ring[0];
 
   const int slot = xcd_slot();
-  for (int tile = slot; tile < total; tile += gridDim.x) {
-    // opaque per-tile copy of the thread index: keeps the compiler from
-    // hoisting every LDS / global offset of the tile body out of the tile loop
+  // Tiles are software-pipelined: the next tile's set-up, its first three
+  // stages' copies and its outer scales are issued before this tile's
+  // epilogue, so they land while its stores drain.
+  int tile = slot, set = 0;
+  if (tile < total) start_tile<SM, WGRAD>(p, sm, ring, G, tile, set, tid0);
+  while (tile < total) {
+    // opaque copies of the thread and tile indices: keep the compiler from
+    // hoisting every LDS / global offset of the tile body out of the tile loop,
+    // or carrying the tile's descriptor through the previous epilogue
     int tid = tid0;
     asm volatile("" : "+v"(tid));
+    asm volatile("" : "+s"(tile));
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = w >> 1, wn = w & 1;
     const int r = lane & 31, h = lane >> 5;
-    const int g = find_group(sm.pre, G, tile);
-    const int local = tile - sm.pre[g];
-    TileDesc t;
-    const float* aout_t;      // outer scales of the tile's rows / columns
-    const float* bout_t;
-    int64_t out_off, ld_out;  // element offset of the tile's first output, row stride
-    if constexpr (WGRAD) {
-      const int64_t mp = group_extent(sm.off, g);
-      const bool usable = sm.off[g] % kColPad == 0 && mp % kColPad == 0;
-      int mt, nt;
-      super_tile<kSuperM, kSuperN>(local, (int)((p.n + BM - 1) / BM), (int)((p.k + BN - 1) / BN),
-                                   mt, nt);
-      const int64_t i0 = (int64_t)mt * BM, j0 = (int64_t)nt * BN;
-      t.lda = mp / 2;
-      t.ldas = mp / 16;
-      t.a = p.a + sm.off[g] * p.n / 2 + i0 * t.lda;
-      t.as = p.as + sm.off[g] * p.n / 16 + i0 * t.ldas;
-      t.b = p.b + sm.off[g] * p.k / 2 + j0 * t.lda;
-      t.bs = p.bs + sm.off[g] * p.k / 16 + j0 * t.ldas;
-      t.a_rows = (int)(p.n - i0 < BM ? p.n - i0 : BM);
-      t.b_rows = (int)(p.k - j0 < BN ? p.k - j0 : BN);
-      t.kl = usable ? mp : 0;
-      aout_t = p.aout + (int64_t)g * p.n + i0;
-      bout_t = p.bout + (int64_t)g * p.k + j0;
-      out_off = ((int64_t)g * p.n + i0) * p.k + j0;
-      ld_out = p.k;
-    } else {
-      const int64_t m = group_extent(sm.off, g);
-      const int64_t ng = p.tab.n[g];
-      int mt, nt;
-      super_tile<kSuperM, kSuperN>(local, (int)((m + BM - 1) / BM), (int)((ng + BN - 1) / BN), mt,
-                                   nt);
-      const int64_t row0 = sm.off[g] + (int64_t)mt * BM;
-      const int64_t n0 = (int64_t)nt * BN;
-      const int64_t brow0 = p.tab.brow[g] + n0;
-      t.lda = p.k / 2;
-      t.ldas = p.k / 16;
-      t.a = p.a + row0 * t.lda;
-      t.as = p.as + row0 * t.ldas;
-      t.b = p.b + brow0 * t.lda;
-      t.bs = p.bs + brow0 * t.ldas;
-      const int64_t rv = sm.off[g] + m - row0, cv = ng - n0;
-      t.a_rows = (int)(rv < BM ? rv : BM);
-      t.b_rows = (int)(cv < BN ? cv : BN);
-      t.kl = p.k;
-      aout_t = p.aout + row0;
-      bout_t = p.bout + brow0;
-      out_off = row0 * p.ld_out + n0;
-      ld_out = p.ld_out;
-    }
-    // waves 0 and 1 decode A, waves 2 and 3 B
-    const bool opb = w >= 2;
-    Rsrc rs;
-    rs.d = opb ? make_rsrc(t.b, (int64_t)t.b_rows * t.lda) : make_rsrc(t.a, (int64_t)t.a_rows * t.lda);
-    rs.s = opb ? make_rsrc(t.bs, (int64_t)t.b_rows * t.ldas)
-               : make_rsrc(t.as, (int64_t)t.a_rows * t.ldas);
-    rs.none = make_rsrc(t.a, 0);
-
-    // outer scales of this tile's rows and columns, for the epilogue (zeros for
-    // a tile with nothing to contract, whose output is then exactly 0)
-    const bool contract = t.kl > 0;
-    if (!WGRAD && p.per_tensor) {
-      // per-tensor NVFP4: alpha_g = tsi(amax_A[g]) * tsi(amax_B[g]) on every
-      // row, 1 on every column, so the epilogue computes S * alpha_g
-      const float alpha = (p.aout[g] / 2688.0f) * (p.bout[g] / 2688.0f);
-      sm.aout[tid] = contract && tid < t.a_rows ? alpha : 0.0f;
-      sm.bout[tid] = contract && tid < t.b_rows ? 1.0f : 0.0f;
-    } else {
-      sm.aout[tid] = contract && tid < t.a_rows ? aout_t[tid] : 0.0f;
-      sm.bout[tid] = contract && tid < t.b_rows ? bout_t[tid] : 0.0f;
-    }
-    // the epilogue reads entries other waves wrote; a tile with nothing to
-    // contract reaches it without the K-loop's barriers
-    __syncthreads();
-
+    int g_unused;
+    const float* ao_unused;
+    const float* bo_unused;
+    const TileJob job = make_job<WGRAD>(p, sm, G, tile, g_unused, ao_unused, bo_unused);
+    const TileDesc& t = job.t;
     v16f acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
 
-    const int nk = (int)((t.kl + BK - 1) / BK);  // >= 1 unless nothing to contract
-    const int nk2 = (nk + 1) & ~1;     // an odd last step runs on zeros
-    if (nk > 0) {
-      const Offs o = make_offs(tid, wm, wn, r, h);
+    // every copy of the tile's start (and the previous tile's stores) has
+    // landed; the outer scales written by other waves are visible
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const int np = (int)((t.kl + kStageK - 1) / kStageK);  // stages; >= 1 unless nothing to
+                                                             // contract (a tail reads as zeros)
+    if (np > 0) {
+      const Dma d = make_dma<SM>(t, w, lane);
+      const Frag f = make_frag<SM>(wm, wn, r, h);
+      // K-step 0's operands and scales (stage 0), and its substep-0 fragments
       Raw x0, x1;
-      Scl sc0, sc1;  // scale words of steps (kt, kt + 1) and (kt + 2, kt + 3)
-      v8h f0a[4], f0b[4], f1a[4], f1b[4];
-      load_scales<SM>(t, rs, 0, nk, tid, sc0);
-      load_raw<SM>(t, rs, 0, true, tid, x0);
-      load_raw<SM>(t, rs, 1, 1 < nk, tid, x1);
-      {
-        const uint32_t sw[4] = {(uint32_t)sc0.s[0][0], (uint32_t)sc0.s[1][0],
-                                (uint32_t)sc0.s[2][0], (uint32_t)sc0.s[3][0]};
-        static_for<4>([&](auto jc) { decode_row<decltype(jc)::value>(st0, o, x0, sw); });
+      v2h s0[8], s1[8];
+      v4i d0[8], d1[8];
+      static_for<16>([&](auto ic) { read_item<decltype(ic)::value, 0, SM>(ring, f, x0); });
+      static_for<8>([&](auto bc) {
+        constexpr int b = decltype(bc)::value;
+        s0[b] = e4m3_pair_h2(x0.s[b] >> f.ssh);
+        decode_half<0, 0>(x0.d[b], s0[b], d0[b]);
+        decode_half<0, 1>(x0.d[b], s0[b], d0[b]);
+      });
+      for (int sp = 0; sp < np; ++sp) {
+        k_step<false, SM>(ring, d, f, w, sp, np, x0, s0, x1, s1, d0, d1, acc);
+        k_step<true, SM>(ring, d, f, w, sp, np, x1, s1, x0, s0, d0, d1, acc);
       }
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      read_frags<0>(st0, o, f0a, f0b);
-      for (int kt = 0; kt < nk2; kt += 2) {
-        const uint32_t swa[4] = {(uint32_t)sc0.s[0][1], (uint32_t)sc0.s[1][1],
-                                 (uint32_t)sc0.s[2][1], (uint32_t)sc0.s[3][1]};
-        k_step<true, SM>(st0, st1, t, rs, kt, nk, tid, o, x1, swa, x0, sc1, f0a, f0b, f1a,
-                         f1b, acc);
-        const uint32_t swb[4] = {(uint32_t)sc1.s[0][0], (uint32_t)sc1.s[1][0],
-                                 (uint32_t)sc1.s[2][0], (uint32_t)sc1.s[3][0]};
-        k_step<false, SM>(st1, st0, t, rs, kt + 1, nk, tid, o, x0, swb, x1, sc1, f0a, f0b,
-                          f1a, f1b, acc);
-        sc0 = sc1;
-      }
+      // every copy (those of the stages past the last included) has landed and
+      // no wave still reads the ring before the next tile's copies
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
+
+    // the next tile's start, into the other outer-scale set (whose last reader,
+    // the previous epilogue, every wave has left at the barriers above)
+    const int64_t out_off = job.out_off, ld_out = job.ld_out;
+    const int a_rows = t.a_rows, b_rows = t.b_rows;
+    const int next = tile + (int)gridDim.x;
+    if (next < total) start_tile<SM, WGRAD>(p, sm, ring, G, next, set ^ 1, tid0);
 
     // epilogue: S -> (S * a_outer) * b_outer, or S itself into the scratch
     const bool fused = p.s_buf == nullptr;
@@ -541,57 +617,36 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
     const int esz = f32out ? 4 : 2;
     char* obase = fused ? reinterpret_cast<char*>(p.out) : reinterpret_cast<char*>(p.s_buf);
     obase += out_off * esz;
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(obase, (int64_t)t.a_rows * ld_out * esz);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(obase, (int64_t)a_rows * ld_out * esz);
     int ldc = (int)ld_out;
     asm volatile("" : "+s"(ldc));
     const int row = wm * 128 + r, col = wn * 128 + 4 * h;
-    const uint32_t ao_base = (uint32_t)(size_t)(__attribute__((address_space(3))) float*)sm.aout;
-    const uint32_t bo_base = (uint32_t)(size_t)(__attribute__((address_space(3))) float*)sm.bout;
-    const bool wide = f32out ? ((ldc & 3) == 0 && (t.b_rows & 3) == 0)
-                             : ((ldc & 7) == 0 && (t.b_rows & 7) == 0);
-    // one 32 x 32 block at a time: scaled into a temporary (fused) and stored
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float ao = fused ? *reinterpret_cast<const lds_f32*>((size_t)(ao_base + 4 * (row + 32 * i)))
-                             : 1.0f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v16f y = acc[i][j];
-        if (fused) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const v4i bo = lds_read16(bo_base + 4 * (col + 32 * j + 8 * q));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) y[4 * q + e] = (y[4 * q + e] * ao) * __int_as_float(bo[e]);
-          }
-        }
-        const int rr = row + 32 * i, cc = col + 32 * j;
-        if (fused && p.accumulate) {
-          // copy-or-accumulate: Y + the output's previous value, rounded once
-          EpiTerms ep;
-          ep.alpha = 1.0f;
-          ep.beta = 1.0f;
-          ep.has_bias = false;
-          ep.bias = ro;
-          const bool wide4 = (ldc & 3) == 0 && (t.b_rows & 3) == 0;
-          if (p.out_f32) {
-            if (wide4) store_block_ex<true, true>(y, ro, ldc, rr, cc, t.b_rows, ep);
-            else store_block_ex<false, true>(y, ro, ldc, rr, cc, t.b_rows, ep);
-          } else {
-            if (wide4) store_block_ex<true, false>(y, ro, ldc, rr, cc, t.b_rows, ep);
-            else store_block_ex<false, false>(y, ro, ldc, rr, cc, t.b_rows, ep);
-          }
-        } else if (f32out) {
-          if (wide) store_block<true, true>(y, ro, ldc, rr, cc, h, t.b_rows);
-          else store_block<false, true>(y, ro, ldc, rr, cc, h, t.b_rows);
-        } else {
-          if (wide) store_block<true, false>(y, ro, ldc, rr, cc, h, t.b_rows);
-          else store_block<false, false>(y, ro, ldc, rr, cc, h, t.b_rows);
-        }
+    const uint32_t ao_base = (uint32_t)(size_t)(__attribute__((address_space(3))) float*)sm.aout[set];
+    const uint32_t bo_base = (uint32_t)(size_t)(__attribute__((address_space(3))) float*)sm.bout[set];
+    const bool wide = f32out ? ((ldc & 3) == 0 && (b_rows & 3) == 0)
+                             : ((ldc & 7) == 0 && (b_rows & 7) == 0);
+    if (fused && p.accumulate) {
+      const bool wide4 = (ldc & 3) == 0 && (b_rows & 3) == 0;
+      if (p.out_f32) {
+        if (wide4) epilogue_tile<true, true, true>(acc, true, ao_base, bo_base, ro, ldc, row, col, h, b_rows);
+        else epilogue_tile<true, false, true>(acc, true, ao_base, bo_base, ro, ldc, row, col, h, b_rows);
+      } else {
+        if (wide4) epilogue_tile<false, true, true>(acc, true, ao_base, bo_base, ro, ldc, row, col, h, b_rows);
+        else epilogue_tile<false, false, true>(acc, true, ao_base, bo_base, ro, ldc, row, col, h, b_rows);
       }
+    } else if (f32out) {
+      if (wide) epilogue_tile<true, true, false>(acc, fused, ao_base, bo_base, ro, ldc, row, col, h, b_rows);
+      else epilogue_tile<true, false, false>(acc, fused, ao_base, bo_base, ro, ldc, row, col, h, b_rows);
+    } else {
+      if (wide) epilogue_tile<false, true, false>(acc, fused, ao_base, bo_base, ro, ldc, row, col, h, b_rows);
+      else epilogue_tile<false, false, false>(acc, fused, ao_base, bo_base, ro, ldc, row, col, h, b_rows);
     }
-    __syncthreads();  // aout / bout and the stages are rewritten by the next tile
+    tile = next;
+    set ^= 1;
   }
+  // the last tile's stores, and copies of a start that had no tile, complete
+  // before the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // Unfused second step: Y[r, n] = (S[r, n] * a_outer[r]) * b_outer_g[n] for the
@@ -651,15 +706,12 @@ hipError_t launch_gemm_nvfp4(int G, const uint8_t* a, const uint8_t* a_scales,
   int64_t grid = device_cu_count();
   if (bound < grid) grid = bound;
   if (grid > 0) {
-    // an even step count keeps each row's scale words of a step pair 8-aligned
-    if (k % (2 * BK) == 0)
-      hipLaunchKernelGGL((nv_gemm_kernel<kScalePaired, false>), dim3((unsigned)grid),
-                         dim3(kThreads), 0, stream, p);
-    else if (k % BK == 0)
-      hipLaunchKernelGGL((nv_gemm_kernel<kScaleWord, false>), dim3((unsigned)grid),
+    // k % 64 == 0 keeps each row's scale dword of a K-step 4-aligned
+    if (k % BK == 0)
+      hipLaunchKernelGGL((nv_gemm_kernel<kSclDword, false>), dim3((unsigned)grid),
                          dim3(kThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL((nv_gemm_kernel<kScaleHalf, false>), dim3((unsigned)grid),
+      hipLaunchKernelGGL((nv_gemm_kernel<kSclShort, false>), dim3((unsigned)grid),
                          dim3(kThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -740,8 +792,8 @@ hipError_t launch_gemm_nvfp4_wgrad(int G, const uint8_t* a, const uint8_t* a_sca
   int64_t grid = device_cu_count();
   if (bound < grid) grid = bound;
   if (grid <= 0) return hipSuccess;
-  // padded token counts are multiples of 128: an even number of 64-deep steps
-  hipLaunchKernelGGL((nv_gemm_kernel<kScalePaired, true>), dim3((unsigned)grid), dim3(kThreads), 0,
+  // padded token counts are multiples of 128: 4-aligned scale dwords
+  hipLaunchKernelGGL((nv_gemm_kernel<kSclDword, true>), dim3((unsigned)grid), dim3(kThreads), 0,
                      stream, p);
   return hipGetLastError();
 }

@@ -113,66 +113,92 @@ struct EpiTerms {
 // stride and out_cols multiples of 4): each run of four columns is one vector
 // load of C, one of the bias and one store; otherwise one element at a time.
 // The three terms are combined in float32, then rounded once to the output.
+// All of the block's loads are issued before its first store, so their
+// latencies overlap (no store of the block writes a position one of its loads
+// reads).
 template <bool WIDE, bool F32>
 __device__ __forceinline__ void store_block_ex(const v16f& acc, __amdgpu_buffer_rsrc_t ro, int ldc,
                                                int row, int col0, int out_cols, const EpiTerms& ep) {
   constexpr int esz = F32 ? 4 : 2;
   const bool read_c = ep.beta != 0.0f;
+  float c[16], bs[16];
+  int off[16];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int col = col0 + 8 * q;
-    float y[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) y[e] = ep.alpha * acc[4 * q + e];
     if constexpr (WIDE) {
-      const int off = col < out_cols ? (row * ldc + col) * esz : (int)kDropped;
+      const int o = col < out_cols ? (row * ldc + col) * esz : (int)kDropped;
+      off[4 * q] = o;
       if (read_c) {
         if constexpr (F32) {
-          const v4i c = __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0);
+          const v4i cv = __builtin_amdgcn_raw_buffer_load_b128(ro, o, 0, 0);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] += ep.beta * __int_as_float(c[e]);
+          for (int e = 0; e < 4; ++e) c[4 * q + e] = __int_as_float(cv[e]);
         } else {
-          const v2i c = __builtin_amdgcn_raw_buffer_load_b64(ro, off, 0, 0);
+          const v2i cv = __builtin_amdgcn_raw_buffer_load_b64(ro, o, 0, 0);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const uint32_t w = (uint32_t)c[e >> 1];
-            y[e] += ep.beta * __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+            const uint32_t w = (uint32_t)cv[e >> 1];
+            c[4 * q + e] = __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
           }
         }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c[4 * q + e] = 0.0f;
       }
       if (ep.has_bias) {
         const v4i bv = __builtin_amdgcn_raw_buffer_load_b128(ep.bias, col * 4, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] += __int_as_float(bv[e]);
-      }
-      if constexpr (F32) {
-        __builtin_amdgcn_raw_buffer_store_b128(
-            (v4i){__float_as_int(y[0]), __float_as_int(y[1]), __float_as_int(y[2]),
-                  __float_as_int(y[3])},
-            ro, off, 0, 0);
+        for (int e = 0; e < 4; ++e) bs[4 * q + e] = __int_as_float(bv[e]);
       } else {
-        const int lo = __builtin_bit_cast(int, __builtin_convertvector((v2f){y[0], y[1]}, v2bf));
-        const int hi = __builtin_bit_cast(int, __builtin_convertvector((v2f){y[2], y[3]}, v2bf));
-        __builtin_amdgcn_raw_buffer_store_b64((v2i){lo, hi}, ro, off, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bs[4 * q + e] = 0.0f;
       }
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int cc = col + e;
-        const int off = cc < out_cols ? (row * ldc + cc) * esz : (int)kDropped;
-        float v = y[e];
+        const int o = cc < out_cols ? (row * ldc + cc) * esz : (int)kDropped;
+        off[4 * q + e] = o;
+        c[4 * q + e] = 0.0f;
         if (read_c) {
           if constexpr (F32)
-            v += ep.beta * __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, off, 0, 0));
+            c[4 * q + e] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, o, 0, 0));
           else
-            v += ep.beta * __uint_as_float(
-                                 (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(ro, off, 0, 0) << 16);
+            c[4 * q + e] = __uint_as_float(
+                (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(ro, o, 0, 0) << 16);
         }
-        if (ep.has_bias) v += __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(ep.bias, cc * 4, 0, 0));
+        bs[4 * q + e] =
+            ep.has_bias ? __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(ep.bias, cc * 4, 0, 0))
+                        : 0.0f;
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      y[e] = ep.alpha * acc[4 * q + e] + ep.beta * c[4 * q + e] + bs[4 * q + e];
+    if constexpr (WIDE) {
+      if constexpr (F32) {
+        __builtin_amdgcn_raw_buffer_store_b128(
+            (v4i){__float_as_int(y[0]), __float_as_int(y[1]), __float_as_int(y[2]),
+                  __float_as_int(y[3])},
+            ro, off[4 * q], 0, 0);
+      } else {
+        const int lo = __builtin_bit_cast(int, __builtin_convertvector((v2f){y[0], y[1]}, v2bf));
+        const int hi = __builtin_bit_cast(int, __builtin_convertvector((v2f){y[2], y[3]}, v2bf));
+        __builtin_amdgcn_raw_buffer_store_b64((v2i){lo, hi}, ro, off[4 * q], 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
         if constexpr (F32)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v), ro, off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(y[e]), ro, off[4 * q + e], 0, 0);
         else
-          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16_rne(v), ro, off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16_rne(y[e]), ro,
+                                                off[4 * q + e], 0, 0);
       }
     }
   }
