@@ -46,6 +46,7 @@
 #include <utility>
 
 #include "bsg_internal.h"
+#include "lds_dma.h"
 #include "store_tile.h"
 
 namespace bsg {
@@ -149,47 +150,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
                                            0x00020000);
 }
 
-// The same descriptor as four uniform dwords, for the inline-asm LDS-DMA loads.
-__device__ __forceinline__ v4i make_rsrc_words(const void* base, int64_t bytes) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  v4i r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(b & 0xffffffffu));
-  r[1] = __builtin_amdgcn_readfirstlane((int)(b >> 32));
-  r[2] = __builtin_amdgcn_readfirstlane((int)(bytes > 0 ? bytes : 0));
-  r[3] = 0x00020000;
-  return r;
-}
-
-// LDS-DMA: lane l copies 16 (or 4) bytes from rsrc + voff to LDS address
-// m0 + 16 l (or 4 l); the whole offset is in voff, so the buffer range check
-// covers it (a lane past the valid rows copies zeros instead of reading).
-// Issued through inline asm so that the compiler does not add waits for it in
-// front of LDS reads of other stages; the K-loop waits for it explicitly
-// (vmcnt) before its barrier.  m0 is saved and restored around the load.
-__device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds, int voff) {
-  int save;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(save)
-      : "s"(lds), "v"(voff), "s"(rsrc)
-      : "memory");
-}
-
-__device__ __forceinline__ void dma4(v4i rsrc, uint32_t lds, int voff) {
-  int save;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "buffer_load_dword %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(save)
-      : "s"(lds), "v"(voff), "s"(rsrc)
-      : "memory");
-}
-
 // Vector-memory operations complete in issue order, so "at most N
 // outstanding" means everything but the N most recent has landed.  Also waits
 // for this wave's LDS reads, then joins the barrier: afterwards the stage whose
@@ -229,9 +189,8 @@ struct Dma {
 // offset past every descriptor's range, so the buffer unit returns zeros for it
 // (the bytes past k in a row are the next row's, or stale bytes of rows no group
 // owns, which may hold NaN codes).
-constexpr int kOutOfRange = 0x7ffffff0;
 __device__ __forceinline__ int k_mask(int voff, int kpos, int lim) {
-  return kpos < lim ? voff : kOutOfRange;
+  return kpos < lim ? voff : kDmaOutOfRange;
 }
 
 __device__ __forceinline__ Dma make_dma(const TileDesc& t, int w, int lane) {

@@ -204,6 +204,9 @@ __device__ __forceinline__ void store_block_ex(const v16f& acc, __amdgpu_buffer_
   }
 }
 
+// One block at a time: each block's accumulators are copied out right before
+// its loads and stores (scheduling fences keep the compiler from copying the
+// whole tile out of the accumulators at once).
 template <bool WIDE, bool F32>
 __device__ __forceinline__ void store_tile_ex(const v16f (&acc)[4][4], __amdgpu_buffer_rsrc_t ro,
                                               int ldc, int row, int col, int out_cols,
@@ -211,8 +214,13 @@ __device__ __forceinline__ void store_tile_ex(const v16f (&acc)[4][4], __amdgpu_
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      store_block_ex<WIDE, F32>(acc[i][j], ro, ldc, row + 32 * i, col + 32 * j, out_cols, ep);
+    for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_sched_barrier(0);
+      v16f y = acc[i][j];
+      asm volatile("" : "+v"(y));
+      store_block_ex<WIDE, F32>(y, ro, ldc, row + 32 * i, col + 32 * j, out_cols, ep);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 }  // namespace bsg
