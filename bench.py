@@ -86,6 +86,7 @@ class MxFprop(Case):
         self.wq = torch.empty((G * N, K), dtype=torch.uint8, device=dev)
         self.wqs = torch.empty(bsg.mx_scale_shape(G * N, K), dtype=torch.uint8, device=dev)
         self.y = torch.empty((R, N), dtype=torch.bfloat16, device=dev)
+        self.ws = bsg.gemm_workspace(dev)  # lets the GEMM split a partly filled last round
         self.kernels = ("offsets", "quantize_x", "quantize_w", "gemm")
         live = w.live_rows
         self.flops = 2.0 * live * N * K
@@ -116,7 +117,8 @@ class MxFprop(Case):
                                    row_scales=self.wqs)
         self._rec(ev, 3)
         bsg.grouped_gemm_mxfp8(bsg.BSG_FPROP_TN, self.xr, self.xrs, self.wq, self.wqs, self.off,
-                               self.R, self.N, self.K, out=self.y, out_dtype=bsg.BSG_OUT_BF16)
+                               self.R, self.N, self.K, out=self.y, out_dtype=bsg.BSG_OUT_BF16,
+                               workspace=self.ws)
         self._rec(ev, 4)
 
 
@@ -192,6 +194,7 @@ class MxDgrad(Case):
         self.wc = torch.empty(G * K * N, dtype=torch.uint8, device=dev)
         self.wcs = torch.empty(G * K * N // 32, dtype=torch.uint8, device=dev)
         self.dx = torch.empty((R, N), dtype=torch.bfloat16, device=dev)
+        self.ws = bsg.gemm_workspace(dev)  # lets the GEMM split a partly filled last round
         self.kernels = ("offsets", "quantize_dy", "quantize_w", "gemm")
         live = w.live_rows
         per = 1.0 + 1.0 / 32
@@ -212,7 +215,8 @@ class MxDgrad(Case):
                                    col_data=self.wc, col_scales=self.wcs)
         self._rec(ev, 3)
         bsg.grouped_gemm_mxfp8(bsg.BSG_DGRAD_NN, self.dyd, self.dys, self.wc, self.wcs, self.off,
-                               self.R, self.N, self.K, out=self.dx, out_dtype=bsg.BSG_OUT_BF16)
+                               self.R, self.N, self.K, out=self.dx, out_dtype=bsg.BSG_OUT_BF16,
+                               workspace=self.ws)
         self._rec(ev, 4)
 
 

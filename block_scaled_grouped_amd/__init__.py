@@ -34,7 +34,8 @@ EXPORTS = ("bsg_last_error", "bsg_version", "group_offsets_i32_to_i64", "grouped
            "grouped_gemm_nvfp4_rowscaled_wgrad", "grouped_gemm_nvfp4_pertensor",
            "grouped_gemm_nvfp4_rowscaled_noalloc", "grouped_quantize_nvfp4_pertensor_rht",
            "grouped_quantize_nvfp4_pertensor_2d", "grouped_quantize_mxfp8_colwise_e5m2",
-           "grouped_gemm_nvfp4_rowscaled_ex", "grouped_gemm_nvfp4_rowscaled_wgrad_ex")
+           "grouped_gemm_nvfp4_rowscaled_ex", "grouped_gemm_nvfp4_rowscaled_wgrad_ex",
+           "grouped_gemm_mxfp8_workspace_size", "grouped_gemm_mxfp8_ws")
 BSG_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
@@ -75,6 +76,11 @@ def load_library(path=LIB_PATH):
                                                              P, P]
     lib.grouped_gemm_mxfp8.restype = I32
     lib.grouped_gemm_mxfp8.argtypes = [I32, I64, P, P, P, P, P, I64, I64, I64, P, I32, P, P]
+    lib.grouped_gemm_mxfp8_workspace_size.restype = ctypes.c_size_t
+    lib.grouped_gemm_mxfp8_workspace_size.argtypes = []
+    lib.grouped_gemm_mxfp8_ws.restype = I32
+    lib.grouped_gemm_mxfp8_ws.argtypes = [I32, I64, P, P, P, P, P, I64, I64, I64, P, I32, P,
+                                          ctypes.c_size_t, P, P]
     lib.grouped_gemm_mxfp8_ex.restype = I32
     lib.grouped_gemm_mxfp8_ex.argtypes = [I32, I64, P, P, P, P, P, I64, I64, I64, P, I32, P, P, P,
                                           P, P]
@@ -446,9 +452,21 @@ def _mx_gemm_check(mode, G, a, a_scales, b, b_scales, offsets, rows_cap, n, k, o
     _req(status, "status", 4, optional=True)
 
 
+def gemm_workspace(device=None):
+    """A uint8 device tensor of grouped_gemm_mxfp8_workspace_size() bytes (256-byte
+    aligned: torch's caching allocator aligns blocks to 512), for the `workspace`
+    argument of grouped_gemm_mxfp8."""
+    import torch
+    lib = load_library()
+    n = int(lib.grouped_gemm_mxfp8_workspace_size())
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
 def grouped_gemm_mxfp8(mode, a, a_scales, b, b_scales, offsets, rows_cap, n, k, out=None,
-                       out_dtype=BSG_OUT_BF16, G=None, status=None):
-    """FPROP_TN, DGRAD_NN: out [rows_cap, n]; WGRAD_NT: out [G, n, k].  See include/bsg.h."""
+                       out_dtype=BSG_OUT_BF16, G=None, status=None, workspace=None):
+    """FPROP_TN, DGRAD_NN: out [rows_cap, n]; WGRAD_NT: out [G, n, k].  With a
+    `workspace` (gemm_workspace()), grouped_gemm_mxfp8_ws: the last round of
+    tiles is split along the contraction.  See include/bsg.h."""
     import torch
     lib = load_library()
     _need_cuda(a, a_scales, b, b_scales, offsets)
@@ -459,6 +477,14 @@ def grouped_gemm_mxfp8(mode, a, a_scales, b, b_scales, offsets, rows_cap, n, k, 
         out = torch.empty(shape, dtype=dt, device=a.device)
     _mx_gemm_check(mode, G, a, a_scales, b, b_scales, offsets, rows_cap, n, k, out, out_dtype,
                    status)
+    if workspace is not None:
+        _need_cuda(workspace)
+        _check(lib.grouped_gemm_mxfp8_ws(mode, G, _ptr(a), _ptr(a_scales), _ptr(b), _ptr(b_scales),
+                                         _ptr(offsets), rows_cap, n, k, _ptr(out), out_dtype,
+                                         _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(),
+                                         _ptr(status), _stream(a)))
+        return out
     _check(lib.grouped_gemm_mxfp8(mode, G, _ptr(a), _ptr(a_scales), _ptr(b), _ptr(b_scales),
                                   _ptr(offsets), rows_cap, n, k, _ptr(out), out_dtype, _ptr(status),
                                   _stream(a)))

@@ -260,7 +260,8 @@ static int gemm_mxfp8_impl(const char* fn, int mode, int64_t G, const uint8_t* a
                            const uint8_t* a_scales, const uint8_t* b, const uint8_t* b_scales,
                            const int64_t* offsets, int64_t rows_cap, int64_t n, int64_t k,
                            void* out, int out_dtype, const float* alpha, const float* beta,
-                           const float* bias, uint32_t* dev_status, void* stream) {
+                           const float* bias, uint32_t* dev_status, void* stream,
+                           void* ws = nullptr) {
   if (a == nullptr || a_scales == nullptr || b == nullptr || b_scales == nullptr || offsets == nullptr ||
       out == nullptr)
     return fail(BSG_ERR_NULL, "%s: operands, scales, offsets and out must be non-NULL", fn);
@@ -298,7 +299,7 @@ static int gemm_mxfp8_impl(const char* fn, int mode, int64_t G, const uint8_t* a
     return fail(BSG_ERR_SHAPE, "%s: a bias needs a multiple of 4 output columns", fn);
   return hip_result(bsg::launch_gemm_mxfp8(mode, (int)G, a, a_scales, b, b_scales, offsets, rows_cap,
                                            n, k, out, out_dtype == BSG_OUT_F32, dev_status,
-                                           (hipStream_t)stream, alpha, beta, bias),
+                                           (hipStream_t)stream, alpha, beta, bias, ws),
                     fn);
 }
 
@@ -309,6 +310,25 @@ int grouped_gemm_mxfp8(int mode, int64_t G, const uint8_t* a, const uint8_t* a_s
   return gemm_mxfp8_impl("grouped_gemm_mxfp8", mode, G, a, a_scales, b, b_scales, offsets,
                          rows_cap, n, k, out, out_dtype, nullptr, nullptr, nullptr, dev_status,
                          stream);
+}
+
+size_t grouped_gemm_mxfp8_workspace_size(void) { return bsg::gemm_mxfp8_workspace_bytes(); }
+
+int grouped_gemm_mxfp8_ws(int mode, int64_t G, const uint8_t* a, const uint8_t* a_scales,
+                          const uint8_t* b, const uint8_t* b_scales, const int64_t* offsets,
+                          int64_t rows_cap, int64_t n, int64_t k, void* out, int out_dtype,
+                          void* workspace, size_t workspace_bytes, uint32_t* dev_status,
+                          void* stream) {
+  const char* fn = "grouped_gemm_mxfp8_ws";
+  if (workspace == nullptr) return fail(BSG_ERR_NULL, "%s: workspace is NULL", fn);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(BSG_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+  const size_t need = bsg::gemm_mxfp8_workspace_bytes();
+  if (workspace_bytes < need)
+    return fail(BSG_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes,
+                need);
+  return gemm_mxfp8_impl(fn, mode, G, a, a_scales, b, b_scales, offsets, rows_cap, n, k, out,
+                         out_dtype, nullptr, nullptr, nullptr, dev_status, stream, workspace);
 }
 
 int grouped_gemm_mxfp8_ex(int mode, int64_t G, const uint8_t* a, const uint8_t* a_scales,

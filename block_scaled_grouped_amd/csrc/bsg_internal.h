@@ -205,7 +205,11 @@ hipError_t launch_gemm_mxfp8(int mode, int G, const uint8_t* a, const uint8_t* a
                              int64_t rows_cap, int64_t n, int64_t k, void* out, int out_f32,
                              uint32_t* status, hipStream_t stream,
                              const float* alpha = nullptr, const float* beta = nullptr,
-                             const float* bias = nullptr);
+                             const float* bias = nullptr, void* ws = nullptr);
+
+// Bytes of the workspace that lets launch_gemm_mxfp8 split its last round of
+// tiles along the contraction (on the current device).
+size_t gemm_mxfp8_workspace_bytes();
 
 hipError_t launch_gemm_nvfp4(int G, const uint8_t* a, const uint8_t* a_scales,
                              const float* a_outer, const int64_t* offsets, int64_t rows_cap,

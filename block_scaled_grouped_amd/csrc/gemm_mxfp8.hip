@@ -97,6 +97,28 @@ struct MxArgs {
   const float* alpha;  // [G] or null (1): epilogue terms, used by the EX kernels
   const float* beta;   // [G] or null (0)
   const float* bias;   // [G, output columns] or null
+  char* ws;            // split workspace (see below) or null: no split
+};
+
+// Split of the last round.  With T output tiles and a grid of P workgroups,
+// the last round holds L = T mod P tiles and leaves P - L workgroups idle.
+// Given a workspace, each of those L tiles is split along the contraction into
+// S <= min(P / L, kSplitMax) parts of whole K-step pairs (at least two each);
+// workgroup L * S' + s of the last round takes part s of tile L' and writes its
+// FP32 accumulators to the workspace, and mx_split_reduce_kernel, launched after
+// the GEMM on the same stream, sums each tile's parts in the order s = 0, 1, ..
+// (so the result does not depend on which part finished first) and stores the
+// tile.  Workspace layout: a header (L, S), one record per split tile (where
+// its output goes), then the parts, kPartBytes each, the accumulators of each
+// wave's 4 x 4 blocks lane by lane.
+constexpr int kSplitMax = 8;
+constexpr int64_t kWsHeader = 16384;
+constexpr int64_t kPartBytes = (int64_t)BM * BN * 4;
+constexpr int kMaxSplitTiles = (int)((kWsHeader - 64) / 32);
+
+struct SplitRecord {
+  int64_t out_off;  // byte offset of the tile's first output element
+  int32_t out_rows, out_cols, ldc, pad;
 };
 
 struct TileDesc {
@@ -400,8 +422,27 @@ __device__ __forceinline__ void step_odd(uint32_t lds, const Dma& d, int w, int 
   });
 }
 
+// The accumulators of one part of a split tile: unit u = 16 w + 4 i + j (wave
+// w's block (i, j)) at part + 1024 u floats, lane l's 16 values at + 16 l.
+__device__ __forceinline__ void store_part(float* __restrict__ part, const v16f (&acc)[4][4],
+                                           int w, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float* dst = part + (int64_t)(16 * w + 4 * i + j) * 1024 + 16 * lane;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<v4f*>(dst + 4 * q) =
+            v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+    }
+}
+
+// One tile: its K-loop, then the epilogue into the output, or (part != null)
+// the accumulators into a part of the split workspace.
 template <int AT, bool EX>
-__device__ __forceinline__ void run_tile(uint32_t lds, const TileDesc& t, int out_f32) {
+__device__ __forceinline__ void run_tile(uint32_t lds, const TileDesc& t, int out_f32,
+                                         float* part) {
   // opaque per-tile copy of the thread index: keeps the compiler from hoisting
   // every LDS / global offset of the tile body out of the persistent tile loop
   int tid = threadIdx.x;
@@ -451,6 +492,10 @@ __device__ __forceinline__ void run_tile(uint32_t lds, const TileDesc& t, int ou
   // every copy has landed and no wave still reads a stage before the next
   // tile's prologue copies into them
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (part != nullptr) {
+    store_part(part, acc, w, lane);
+    return;
+  }
 
   const int esz = out_f32 ? 4 : 2;
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(t.out, (int64_t)t.out_rows * t.ldc * esz);
@@ -517,10 +562,33 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(MxArgs p) {
   const int total = sm.pre[G];
   const int out_elem = p.out_f32 ? 4 : 2;
 
+  // the split of the last round (fprop / dgrad, whose tiles all contract k)
+  const int grid = (int)gridDim.x;
+  const int full = total / grid, left = total - full * grid;
+  int nsplit = 1;
+  if (!kWgrad && p.ws != nullptr && left > 0 && left <= kMaxSplitTiles) {
+    const int np = (int)((p.k + kPairK - 1) / kPairK);
+    nsplit = grid / left;
+    if (nsplit > kSplitMax) nsplit = kSplitMax;
+    if (nsplit > np / 2) nsplit = np / 2;
+    if (nsplit < 2) nsplit = 1;
+  }
+  if (p.ws != nullptr && blockIdx.x == 0 && tid == 0) {
+    int32_t* hdr = reinterpret_cast<int32_t*>(p.ws);
+    hdr[0] = nsplit > 1 ? left : 0;
+    hdr[1] = nsplit;
+  }
+
   const int slot = xcd_slot();
 
   for (int round = 0;; ++round) {
-    const int tile = round * gridDim.x + slot;
+    int tile = round * grid + slot;
+    int part = -1;  // >= 0: part `part` of a split tile
+    if (nsplit > 1 && round == full) {
+      if (slot >= left * nsplit) break;
+      tile = full * grid + slot / nsplit;
+      part = slot % nsplit;
+    }
     if (tile >= total) break;
     const int g = find_group(sm.pre, G, tile);
     const int local = tile - sm.pre[g];
@@ -605,7 +673,79 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(MxArgs p) {
       t.beta = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, be)));
       t.bias = p.bias != nullptr ? p.bias + (int64_t)gu * outw + col_first : nullptr;
     }
-    run_tile<(MODE == 2 || MODE == 3) ? 1 : 0, EX>(lds, t, p.out_f32);
+    float* part_dst = nullptr;
+    if (part >= 0) {
+      // pairs [np * part / S, np * (part + 1) / S) of the contraction
+      const int np = (int)((t.kl + kPairK - 1) / kPairK);
+      const int p0 = np * part / nsplit, p1 = np * (part + 1) / nsplit;
+      const int64_t k0 = (int64_t)p0 * kPairK;
+      const int64_t k1 = (int64_t)p1 * kPairK < t.kl ? (int64_t)p1 * kPairK : t.kl;
+      t.a += k0;
+      t.b += k0;
+      t.as += p0 * t.sqa;
+      t.as_bytes -= p0 * t.sqa;
+      t.bs += p0 * t.sqb;
+      t.bs_bytes -= p0 * t.sqb;
+      t.kl = k1 - k0;
+      part_dst = reinterpret_cast<float*>(p.ws + kWsHeader + (int64_t)slot * kPartBytes);
+      if (part == 0 && tid == 0) {
+        SplitRecord* rec = reinterpret_cast<SplitRecord*>(p.ws + 64) + slot / nsplit;
+        rec->out_off = t.out - reinterpret_cast<char*>(p.out);
+        rec->out_rows = t.out_rows;
+        rec->out_cols = t.out_cols;
+        rec->ldc = (int32_t)t.ldc;
+        rec->pad = 0;
+      }
+    }
+    run_tile<(MODE == 2 || MODE == 3) ? 1 : 0, EX>(lds, t, p.out_f32, part_dst);
+  }
+}
+
+// The second step of a split: each split tile's parts summed in the order
+// s = 0, 1, .. and stored as the plain epilogue stores a tile.  Work item
+// (tile l, group ug of four units): wave w sums unit 4 ug + w of the parts.
+__global__ __launch_bounds__(kThreads) void mx_split_reduce_kernel(const char* __restrict__ ws,
+                                                                   void* out, int out_f32) {
+  const int32_t* hdr = reinterpret_cast<const int32_t*>(ws);
+  const int nl = hdr[0], nsplit = hdr[1];
+  if (nl <= 0) return;
+  const SplitRecord* recs = reinterpret_cast<const SplitRecord*>(ws + 64);
+  const float* parts = reinterpret_cast<const float*>(ws + kWsHeader);
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int r = lane & 31, h = lane >> 5;
+  const int esz = out_f32 ? 4 : 2;
+  for (int it = blockIdx.x; it < nl * 16; it += gridDim.x) {
+    const int l = it / 16;
+    const int u = 4 * (it % 16) + w;  // unit: source wave u / 16, block ((u / 4) % 4, u % 4)
+    v16f y = v16f{};
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float* src = parts + (int64_t)(l * nsplit + sp) * (kPartBytes / 4) +
+                         (int64_t)u * 1024 + 16 * lane;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const v4f v = *reinterpret_cast<const v4f*>(src + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[4 * q + e] += v[e];
+      }
+    }
+    const SplitRecord rec = recs[l];
+    const int wsrc = u / 16, i = (u / 4) % 4, j = u % 4;
+    const int row = (wsrc >> 1) * 128 + 32 * i + r, col = (wsrc & 1) * 128 + 32 * j + 4 * h;
+    const __amdgpu_buffer_rsrc_t ro =
+        make_rsrc(reinterpret_cast<char*>(out) + rec.out_off, (int64_t)rec.out_rows * rec.ldc * esz);
+    const int ldc = rec.ldc;
+    if (out_f32) {
+      if ((ldc & 3) == 0 && (rec.out_cols & 3) == 0)
+        store_block<true, true>(y, ro, ldc, row, col, h, rec.out_cols);
+      else
+        store_block<false, true>(y, ro, ldc, row, col, h, rec.out_cols);
+    } else {
+      if ((ldc & 7) == 0 && (rec.out_cols & 7) == 0)
+        store_block<true, false>(y, ro, ldc, row, col, h, rec.out_cols);
+      else
+        store_block<false, false>(y, ro, ldc, row, col, h, rec.out_cols);
+    }
   }
 }
 
@@ -624,14 +764,19 @@ int device_cu_count() {
   return cached[dev];
 }
 
+size_t gemm_mxfp8_workspace_bytes() {
+  return (size_t)kWsHeader + (size_t)device_cu_count() * (size_t)kPartBytes;
+}
+
 hipError_t launch_gemm_mxfp8(int mode, int G, const uint8_t* a, const uint8_t* a_scales,
                              const uint8_t* b, const uint8_t* b_scales, const int64_t* offsets,
                              int64_t rows_cap, int64_t n, int64_t k, void* out, int out_f32,
                              uint32_t* status, hipStream_t stream, const float* alpha,
-                             const float* beta, const float* bias) {
-  MxArgs p{a,      a_scales, b,       b_scales, offsets, rows_cap, n,    k,
-           out,    status,   G,       out_f32,  alpha,   beta,     bias};
+                             const float* beta, const float* bias, void* ws) {
   const bool ex = alpha != nullptr || beta != nullptr || bias != nullptr;
+  if (ex) ws = nullptr;  // the epilogue terms are applied by the plain epilogue only
+  MxArgs p{a,      a_scales, b,       b_scales, offsets, rows_cap, n,    k,
+           out,    status,   G,       out_f32,  alpha,   beta,     bias, static_cast<char*>(ws)};
   // upper bound of the tile count from host-known shapes
   int64_t bound;
   if (mode != 1 && mode != 3) bound = ((rows_cap + BM - 1) / BM + G) * ((n + BN - 1) / BN);
@@ -651,6 +796,12 @@ hipError_t launch_gemm_mxfp8(int mode, int G, const uint8_t* a, const uint8_t* a
     else if (mode == 3) hipLaunchKernelGGL((mx_gemm_kernel<3, true>), gd, bd, 0, stream, p);
     else hipLaunchKernelGGL((mx_gemm_kernel<2, true>), gd, bd, 0, stream, p);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ws == nullptr) return e;
+  // the split tiles' second step (returns at once when the GEMM split nothing)
+  const int64_t rgrid = device_cu_count();
+  hipLaunchKernelGGL(mx_split_reduce_kernel, dim3((unsigned)rgrid), dim3(kThreads), 0, stream,
+                     static_cast<const char*>(ws), out, out_f32);
   return hipGetLastError();
 }
 

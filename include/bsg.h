@@ -39,6 +39,7 @@ typedef enum {
   BSG_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
   BSG_ERR_ALIGN = 3,       /* a data pointer is not 16-byte aligned */
   BSG_ERR_UNSUPPORTED = 4, /* a mode / dtype / flag value the library does not support */
+  BSG_ERR_WORKSPACE = 5,   /* a workspace is smaller than its query function returns */
   BSG_ERR_HIP = 6          /* a HIP launch failed */
 } bsg_status;
 
@@ -338,6 +339,35 @@ int grouped_gemm_mxfp8(int mode, int64_t G, const uint8_t* a, const uint8_t* a_s
                        const uint8_t* b, const uint8_t* b_scales, const int64_t* offsets,
                        int64_t rows_cap, int64_t n, int64_t k, void* out, int out_dtype,
                        uint32_t* dev_status, void* stream);
+
+/*
+ * grouped_gemm_mxfp8_workspace_size / grouped_gemm_mxfp8_ws
+ *
+ * grouped_gemm_mxfp8 with a workspace that removes most of its last, partly
+ * filled round of output tiles (a persistent grid of one workgroup per compute
+ * unit takes the tiles in rounds; with T tiles and P workgroups the last round
+ * holds T mod P and leaves the rest idle).  FPROP and DGRAD, whose tiles all
+ * contract k, split each tile of that round along the contraction into S parts
+ * (2 <= S <= 8, at most P / (T mod P), each at least two 64-deep K-steps
+ * pairs); the parts' FP32 accumulators go to the workspace and a second kernel
+ * on the same stream adds them in a fixed order and stores the tiles.  The
+ * result is deterministic, but a split tile's sums are rounded in a different
+ * order than grouped_gemm_mxfp8's (differences within FP32 rounding); WGRAD
+ * modes never split.  Same arguments and errors as grouped_gemm_mxfp8, plus:
+ *   workspace        [device] grouped_gemm_mxfp8_workspace_size() bytes, 256-byte
+ *                    aligned, owned by the caller; its contents on entry do not
+ *                    matter, and calls that share it must not overlap.
+ *   workspace_bytes  its size: less than the query gives BSG_ERR_WORKSPACE; NULL
+ *                    workspace BSG_ERR_NULL; misaligned BSG_ERR_ALIGN.
+ * The size depends on the current device's compute-unit count: 16 KiB plus
+ * 256 KiB per unit (64 MiB on 256 units).
+ */
+size_t grouped_gemm_mxfp8_workspace_size(void);
+int grouped_gemm_mxfp8_ws(int mode, int64_t G, const uint8_t* a, const uint8_t* a_scales,
+                          const uint8_t* b, const uint8_t* b_scales, const int64_t* offsets,
+                          int64_t rows_cap, int64_t n, int64_t k, void* out, int out_dtype,
+                          void* workspace, size_t workspace_bytes, uint32_t* dev_status,
+                          void* stream);
 
 /*
  * grouped_gemm_mxfp8_ex

@@ -17,7 +17,7 @@ HEADER = os.path.join(ROOT, "include", "bsg.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(?:int|const char\*)\s+(\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(?:int|size_t|const char\*)\s+(\w+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -88,6 +88,16 @@ def test_gemm_validation(lib):
     assert g(0, 4, p, p, p, p, p, 128, 128, 0, p, 0, None, None) == 2
     assert g(1, 4, p, p, p, p, p, 128, 100, 128, p, 0, None, None) == 2            # wgrad n % 32
     assert g(0, 300, p, p, p, p, p, 128, 128, 128, p, 0, None, None) == 2
+    need = lib.grouped_gemm_mxfp8_workspace_size()
+    assert need >= 16384 + 256 * 1024                # header and at least one 256 KiB part
+    wsg = lib.grouped_gemm_mxfp8_ws
+    big, wsp = _buf(4096 + 256)
+    wsa = ctypes.c_void_p((wsp.value + 255) & ~255)
+    assert wsg(0, 4, p, p, p, p, p, 128, 128, 128, p, 0, None, need, None, None) == 1     # NULL
+    assert wsg(0, 4, p, p, p, p, p, 128, 128, 128, p, 0, wsa, need - 1, None, None) == 5  # small
+    assert wsg(0, 4, p, p, p, p, p, 128, 128, 128, p, 0, ctypes.c_void_p(wsa.value + 16), need,
+               None, None) == 3                                                        # aligned
+    assert wsg(0, 4, p, p, p, p, p, 128, 128, 100, p, 0, wsa, need, None, None) == 2      # k % 32
     nv = lib.grouped_gemm_nvfp4_rowscaled
     npg = (ctypes.c_int64 * 2)(64, 128)
     hp = ctypes.cast(npg, ctypes.c_void_p)
