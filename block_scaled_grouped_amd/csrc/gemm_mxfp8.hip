@@ -797,7 +797,9 @@ hipError_t launch_gemm_mxfp8(int mode, int G, const uint8_t* a, const uint8_t* a
     else hipLaunchKernelGGL((mx_gemm_kernel<2, true>), gd, bd, 0, stream, p);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || ws == nullptr) return e;
+  // a split needs FPROP / DGRAD and at least two parts of two pairs each
+  const bool may_split = mode != 1 && mode != 3 && (k + kPairK - 1) / kPairK >= 4;
+  if (e != hipSuccess || ws == nullptr || !may_split) return e;
   // the split tiles' second step (returns at once when the GEMM split nothing)
   const int64_t rgrid = device_cu_count();
   hipLaunchKernelGGL(mx_split_reduce_kernel, dim3((unsigned)rgrid), dim3(kThreads), 0, stream,
