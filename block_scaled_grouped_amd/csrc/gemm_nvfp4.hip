@@ -650,7 +650,12 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
 }
 
 // Unfused second step: Y[r, n] = (S[r, n] * a_outer[r]) * b_outer_g[n] for the
-// live rows r of group g and n < N_g, one block per row.
+// live rows r of group g and n < N_g, one block per row (with the accumulate
+// flag, Y is added to the output's previous value, then rounded once).  VEC
+// (row stride a multiple of 4, 16-byte aligned buffers): each thread takes four
+// consecutive columns per step -- one 16-byte read of S (streamed: read once)
+// and of b_outer, one 16- or 8-byte store; the last N_g mod 4 columns one by one.
+template <bool VEC>
 __global__ __launch_bounds__(256) void nv_postscale_kernel(const float* __restrict__ s_buf,
                                                            const float* __restrict__ aout,
                                                            const float* __restrict__ bout,
@@ -671,8 +676,41 @@ __global__ __launch_bounds__(256) void nv_postscale_kernel(const float* __restri
   const int ng = tab.n[g];
   const float ao = aout[row];
   const float* bo = bout + tab.brow[g];
-  for (int n = threadIdx.x; n < ng; n += blockDim.x) {
-    float y = (s_buf[row * ld_out + n] * ao) * bo[n];
+  const float* srow = s_buf + row * ld_out;
+  int n0 = 0;
+  if constexpr (VEC) {
+    const int n4 = ng & ~3;
+    for (int n = 4 * (int)threadIdx.x; n < n4; n += 4 * (int)blockDim.x) {
+      const v4f sv = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(srow + n));
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = (sv[e] * ao) * bo[n + e];
+      if (out_f32) {
+        v4f* o = reinterpret_cast<v4f*>(reinterpret_cast<float*>(out) + row * ld_out + n);
+        if (accumulate) {
+          const v4f old = *o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = old[e] + y[e];
+        }
+        *o = v4f{y[0], y[1], y[2], y[3]};
+      } else {
+        v2i* o = reinterpret_cast<v2i*>(reinterpret_cast<uint16_t*>(out) + row * ld_out + n);
+        if (accumulate) {
+          const v2i old = *o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t wd = (uint32_t)old[e >> 1];
+            y[e] = bf16_to_f32((e & 1) ? (wd >> 16) : (wd & 0xffffu)) + y[e];
+          }
+        }
+        *o = v2i{(int)(f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16)),
+                 (int)(f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16))};
+      }
+    }
+    n0 = n4;
+  }
+  for (int n = n0 + (int)threadIdx.x; n < ng; n += blockDim.x) {
+    float y = (srow[n] * ao) * bo[n];
     if (out_f32) {
       float* o = reinterpret_cast<float*>(out) + row * ld_out + n;
       if (accumulate) y = *o + y;
@@ -717,9 +755,16 @@ hipError_t launch_gemm_nvfp4(int G, const uint8_t* a, const uint8_t* a_scales,
     if (e != hipSuccess) return e;
   }
   if (s_buf != nullptr && rows_cap > 0) {
-    hipLaunchKernelGGL(nv_postscale_kernel, dim3((unsigned)rows_cap), dim3(256), 0, stream,
-                       s_buf, a_outer, b_outer, offsets, rows_cap, G, out, ld_out, out_f32,
-                       accumulate ? 1 : 0, table);
+    const bool vec = ld_out % 4 == 0 && reinterpret_cast<uintptr_t>(s_buf) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(out) % 16 == 0;
+    if (vec)
+      hipLaunchKernelGGL(nv_postscale_kernel<true>, dim3((unsigned)rows_cap), dim3(256), 0, stream,
+                         s_buf, a_outer, b_outer, offsets, rows_cap, G, out, ld_out, out_f32,
+                         accumulate ? 1 : 0, table);
+    else
+      hipLaunchKernelGGL(nv_postscale_kernel<false>, dim3((unsigned)rows_cap), dim3(256), 0,
+                         stream, s_buf, a_outer, b_outer, offsets, rows_cap, G, out, ld_out,
+                         out_f32, accumulate ? 1 : 0, table);
     return hipGetLastError();
   }
   return hipSuccess;

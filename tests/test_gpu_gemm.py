@@ -518,6 +518,44 @@ def test_nvfp4_gemm_accumulate(fused, out_f32):
     assert np.all(np.isnan(y[live:])), "capacity rows must stay untouched"
 
 
+@pytest.mark.parametrize("ld_extra", [1, 2])
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_nvfp4_scratch_postscale_strides_and_tails(ld_extra, accumulate):
+    """The two-step flow's post-scale kernel with output widths that are not
+    multiples of 4 (its element-wise tail) and a row stride that is (four
+    columns per thread) or is not (element-wise throughout)."""
+    rng = np.random.default_rng(61 + ld_extra + 2 * accumulate)
+    npg = [36, 130, 64]
+    sizes, off, ap, asc, at, bp, bsc, bt = _nv_operands(rng, [70, 0, 150], npg, 128, 260)
+    live = int(off[-1])
+    ld = max(npg) + ld_extra                  # 131: odd stride; 132: multiple of 4
+    prev = (rng.standard_normal((260, ld)) * 2).astype(np.float32)
+    prev[live:] = np.nan
+    for g in range(len(npg)):
+        prev[off[g]:off[g + 1], npg[g]:] = np.nan
+    out = torch.from_numpy(prev).to(device())
+    c_prev = bf16_out_to_f64(out)
+    scratch = torch.empty((260, ld), dtype=torch.float32, device=device())
+
+    def pad_rows(a):
+        o = np.zeros((260,) + a.shape[1:], a.dtype)
+        o[:a.shape[0]] = a
+        return to_dev(o)
+
+    bsg.grouped_gemm_nvfp4_rowscaled(pad_rows(ap), pad_rows(asc), pad_rows(at), to_dev(off), 128,
+                                     to_dev(bp), to_dev(bsc), to_dev(bt), npg, out=out, ld_out=ld,
+                                     out_dtype=bsg.BSG_OUT_F32, scratch=scratch,
+                                     accumulate=accumulate)
+    y = bf16_out_to_f64(out)
+    for g, (rows, r) in enumerate(GM.nvfp4_rowscaled_fprop(ap, asc, at, off, bp, bsc, bt, npg, 128)):
+        if len(rows) == 0:
+            continue
+        want = r + c_prev[rows][:, :npg[g]] if accumulate else r
+        gemm_tolerance_check(y[rows][:, :npg[g]], want, True, "group %d" % g)
+        assert np.all(np.isnan(y[rows][:, npg[g]:])), "columns past N_g must stay untouched"
+    assert np.all(np.isnan(y[live:])), "capacity rows must stay untouched"
+
+
 # ---------------------------------------------------------------- NVFP4 row-scaled wgrad
 
 NVW_CASES = [
