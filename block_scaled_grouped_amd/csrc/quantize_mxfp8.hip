@@ -63,8 +63,9 @@ __device__ __forceinline__ uint32_t amax_fold(uint32_t m) { return max(m & 0xfff
 template <bool E5M2 = false>
 __device__ __forceinline__ uint32_t fp8_saturate(uint32_t x) {
   constexpr uint32_t gap = E5M2 ? 0x04040404u : 0x01010101u;  // 0x80 - first overflow code
-  const uint32_t m = ((x & 0x7f7f7f7fu) + gap) & 0x80808080u;
-  return x - (m >> 7);
+  const uint32_t t = (((x & 0x7f7f7f7fu) + gap) >> 7) & 0x01010101u;
+  // E4M3: S.1111.111 -> S.1111.110 flips bit 0 (one bitwise op with the mask)
+  return E5M2 ? x - t : x ^ t;
 }
 
 // Two packed bf16 (low element first), scaled -> two E4M3 (or E5M2) bytes in
@@ -85,8 +86,11 @@ __device__ __forceinline__ uint32_t cvt2(uint32_t w, float scale, uint32_t old) 
 // 8 bf16 (4 dwords) -> 8 E4M3 (or E5M2) bytes (2 dwords).
 template <bool E5M2 = false>
 __device__ __forceinline__ uint2 cvt8(uint4 v, float scale) {
-  const uint32_t lo = cvt2<true, E5M2>(v.y, scale, cvt2<false, E5M2>(v.x, scale, 0u));
-  const uint32_t hi = cvt2<true, E5M2>(v.w, scale, cvt2<false, E5M2>(v.z, scale, 0u));
+  // The first convert's other half is written by the second, so its prior
+  // contents do not matter: passing the source word lets the result take the
+  // source's register (no copy into a zeroed one).
+  const uint32_t lo = cvt2<true, E5M2>(v.y, scale, cvt2<false, E5M2>(v.x, scale, v.x));
+  const uint32_t hi = cvt2<true, E5M2>(v.w, scale, cvt2<false, E5M2>(v.z, scale, v.z));
   return make_uint2(fp8_saturate<E5M2>(lo), fp8_saturate<E5M2>(hi));
 }
 
