@@ -206,6 +206,14 @@ hipError_t launch_quantize_nvfp4_rowscaled(const uint16_t* x, int64_t rows_cap, 
   return hipGetLastError();
 }
 
+// A 64-bit value as the first lane holds it (for values the same in every
+// lane, so the compiler can keep them in scalar registers).
+__device__ __forceinline__ int64_t first_lane64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // ---------------------------------------------------------------- per tensor
 //
 // Per-tensor NVFP4 of grouped rows: each group (an expert's rows, or an
@@ -218,8 +226,7 @@ hipError_t launch_quantize_nvfp4_rowscaled(const uint16_t* x, int64_t rows_cap, 
 // maxima in LDS, then one atomic max per group and workgroup: atomics on one
 // address from every XCD serialize, so their count is kept to a few hundred;
 // non-negative floats order as their bit patterns), then the cast above runs
-// with the group's amax.  The second read of the rows mostly hits the
-// last-level cache for inputs that fit in it.
+// with the group's amax, reading the rows a second time.
 constexpr int kAmaxThreads = 512;
 constexpr int kAmaxBlocksPerCu = 2;
 constexpr int kAmaxBatch = 8;  // 16-byte loads in flight per thread
@@ -250,8 +257,10 @@ __global__ __launch_bounds__(kAmaxThreads) void nvfp4_group_amax_kernel(
   const int64_t per = (span + gridDim.x - 1) / gridDim.x;
   const int64_t c0 = first + (int64_t)blockIdx.x * per;
   const int64_t c1 = c0 + per < total ? c0 + per : total;
-  int64_t c = c0 + tid;
-  if (c < c1) {
+  // every thread runs the same number of batches (chunks past the share read
+  // zeros), so the loop and its waits are uniform
+  {
+    int64_t c = c0 + tid;
     const int64_t row = c / cpr;
     int g = 0, hi = G - 1;  // the largest g with s_off[g] <= row
     while (g < hi) {
@@ -259,19 +268,33 @@ __global__ __launch_bounds__(kAmaxThreads) void nvfp4_group_amax_kernel(
       if (s_off[mid] <= row) g = mid; else hi = mid - 1;
     }
     int64_t bound = s_off[g + 1] * cpr;  // first chunk past group g
-    const uint4* __restrict__ xv = reinterpret_cast<const uint4*>(x);
+    // the workgroup's share as one buffer range: loads past it read zeros, so
+    // every load is issued unconditionally and the wait for a batch counts
+    // only the loads issued before it
+    const uint64_t xb = reinterpret_cast<uint64_t>(x + c0 * 8);
+    const uint32_t xlo = __builtin_amdgcn_readfirstlane((uint32_t)xb);
+    const uint32_t xhi = __builtin_amdgcn_readfirstlane((uint32_t)(xb >> 32));
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(((uint64_t)xhi << 32) | xlo), (short)0,
+        __builtin_amdgcn_readfirstlane((int)(c1 > c0 ? (c1 - c0) * 16 : 0)), 0x00020000);
     uint32_t m = 0;
-    for (; c < c1; c += kAmaxBatch * kAmaxThreads) {
-      uint4 v[kAmaxBatch];  // the batch's loads are all issued before any is used
+    constexpr int64_t kStep = (int64_t)kAmaxBatch * kAmaxThreads;
+    // two batches in flight: the next batch's loads are issued before the
+    // current one is folded
+    auto load = [&](uint4 (&v)[kAmaxBatch], int64_t cb) {
 #pragma unroll
       for (int k = 0; k < kAmaxBatch; ++k) {
-        const int64_t ck = c + (int64_t)k * kAmaxThreads;
-        v[k] = ck < c1 ? xv[ck] : make_uint4(0, 0, 0, 0);
+        const int64_t ck = cb + (int64_t)k * kAmaxThreads;
+        const v4i q = __builtin_amdgcn_raw_buffer_load_b128(
+            rx, ck < c1 ? (int)((ck - c0) * 16) : 0x7ffffff0, 0, 0);
+        v[k] = make_uint4((uint32_t)q[0], (uint32_t)q[1], (uint32_t)q[2], (uint32_t)q[3]);
       }
+    };
+    auto fold = [&](const uint4 (&v)[kAmaxBatch], int64_t cb) {
 #pragma unroll
       for (int k = 0; k < kAmaxBatch; ++k) {
-        const int64_t ck = c + (int64_t)k * kAmaxThreads;
-        if (ck >= c1) break;
+        // chunks past the share read zeros, which leave every maximum as it is
+        const int64_t ck = cb + (int64_t)k * kAmaxThreads;
         if (ck >= bound) {
           atomicMax(&s_max[g], m);
           m = 0;
@@ -281,6 +304,16 @@ __global__ __launch_bounds__(kAmaxThreads) void nvfp4_group_amax_kernel(
         m = max(m, max(max(mag_bits(v[k].x), mag_bits(v[k].y)),
                        max(mag_bits(v[k].z), mag_bits(v[k].w))));
       }
+    };
+    const int64_t nb = first_lane64(c1 > c0 ? (c1 - c0 + kStep - 1) / kStep : 0);
+    uint4 va[kAmaxBatch], vb[kAmaxBatch];
+    if (nb > 0) load(va, c);
+    for (int64_t b = 0; b < nb; b += 2, c += 2 * kStep) {
+      load(vb, c + kStep);
+      fold(va, c);
+      if (b + 1 >= nb) break;
+      load(va, c + 2 * kStep);
+      fold(vb, c + kStep);
     }
     atomicMax(&s_max[g], m);
   }
