@@ -296,6 +296,8 @@ class Nvfp4Fprop(Case):
         self.y = torch.empty((R, self.ld), dtype=torch.bfloat16, device=dev)
         self.scratch = (torch.empty((R, self.ld), dtype=torch.float32, device=dev) if scratch
                         else None)
+        # the fused flow may split a partly filled last round of tiles
+        self.gws = None if scratch else bsg.gemm_workspace(dev)
         self.kernels = ("offsets", "quantize_x", "quantize_w", "gemm")
         live = w.live_rows
         self.flops = 2.0 * K * float(sum(int(m) * n for m, n in zip(w.sizes, self.npg)))
@@ -317,7 +319,8 @@ class Nvfp4Fprop(Case):
         self._rec(ev, 3)
         bsg.grouped_gemm_nvfp4_rowscaled(self.xd, self.xs, self.xo, self.off, self.K, self.wd, self.ws,
                                          self.wo, self.npg, out=self.y, ld_out=self.ld,
-                                         out_dtype=bsg.BSG_OUT_BF16, scratch=self.scratch)
+                                         out_dtype=bsg.BSG_OUT_BF16, scratch=self.scratch,
+                                         workspace=self.gws)
         self._rec(ev, 4)
 
 
@@ -349,6 +352,7 @@ class Nvfp4PerTensorFprop(Case):
         self.ws = torch.empty((NB, K // 16), dtype=torch.uint8, device=dev)
         self.wa = torch.empty(G, dtype=torch.float32, device=dev)
         self.y = torch.empty((R, self.ld), dtype=torch.bfloat16, device=dev)
+        self.gws = bsg.gemm_workspace(dev)  # lets the GEMM split a partly filled last round
         self.kernels = ("offsets", "quantize_x", "quantize_w", "gemm")
         live = w.live_rows
         self.flops = 2.0 * K * float(sum(int(m) * n for m, n in zip(w.sizes, self.npg)))
@@ -383,7 +387,7 @@ class Nvfp4PerTensorFprop(Case):
         self._rec(ev, 3)
         bsg.grouped_gemm_nvfp4_pertensor(self.xd, self.xs, self.xa, self.off, self.K, self.wd,
                                          self.ws, self.wa, self.npg, out=self.y, ld_out=self.ld,
-                                         out_dtype=bsg.BSG_OUT_BF16)
+                                         out_dtype=bsg.BSG_OUT_BF16, workspace=self.gws)
         self._rec(ev, 4)
 
 

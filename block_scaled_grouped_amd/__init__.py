@@ -35,7 +35,9 @@ EXPORTS = ("bsg_last_error", "bsg_version", "group_offsets_i32_to_i64", "grouped
            "grouped_gemm_nvfp4_rowscaled_noalloc", "grouped_quantize_nvfp4_pertensor_rht",
            "grouped_quantize_nvfp4_pertensor_2d", "grouped_quantize_mxfp8_colwise_e5m2",
            "grouped_gemm_nvfp4_rowscaled_ex", "grouped_gemm_nvfp4_rowscaled_wgrad_ex",
-           "grouped_gemm_mxfp8_workspace_size", "grouped_gemm_mxfp8_ws")
+           "grouped_gemm_mxfp8_workspace_size", "grouped_gemm_mxfp8_ws",
+           "grouped_gemm_nvfp4_workspace_size", "grouped_gemm_nvfp4_rowscaled_ws",
+           "grouped_gemm_nvfp4_pertensor_ws")
 BSG_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
@@ -106,6 +108,14 @@ def load_library(path=LIB_PATH):
     lib.grouped_gemm_nvfp4_rowscaled_noalloc.restype = I32
     lib.grouped_gemm_nvfp4_rowscaled_noalloc.argtypes = [I64, P, P, P, P, I64, I64, P, P, P, P, P,
                                                          I64, I32, P, P]
+    lib.grouped_gemm_nvfp4_workspace_size.restype = ctypes.c_size_t
+    lib.grouped_gemm_nvfp4_workspace_size.argtypes = []
+    lib.grouped_gemm_nvfp4_rowscaled_ws.restype = I32
+    lib.grouped_gemm_nvfp4_rowscaled_ws.argtypes = [I64, P, P, P, P, I64, I64, P, P, P, P, P, I64,
+                                                    I32, I32, P, ctypes.c_size_t, P, P]
+    lib.grouped_gemm_nvfp4_pertensor_ws.restype = I32
+    lib.grouped_gemm_nvfp4_pertensor_ws.argtypes = [I64, P, P, P, P, I64, I64, P, P, P, P, P, I64,
+                                                    I32, P, ctypes.c_size_t, P, P]
     lib.grouped_gemm_nvfp4_rowscaled_wgrad.restype = I32
     lib.grouped_gemm_nvfp4_rowscaled_wgrad.argtypes = [I64, P, P, P, P, P, P, P, I64, I64, I64, P,
                                                        I32, P, P]
@@ -453,12 +463,14 @@ def _mx_gemm_check(mode, G, a, a_scales, b, b_scales, offsets, rows_cap, n, k, o
 
 
 def gemm_workspace(device=None):
-    """A uint8 device tensor of grouped_gemm_mxfp8_workspace_size() bytes (256-byte
-    aligned: torch's caching allocator aligns blocks to 512), for the `workspace`
-    argument of grouped_gemm_mxfp8."""
+    """A uint8 device tensor of max(grouped_gemm_mxfp8_workspace_size(),
+    grouped_gemm_nvfp4_workspace_size()) bytes (256-byte aligned: torch's caching
+    allocator aligns blocks to 512), for the `workspace` argument of
+    grouped_gemm_mxfp8, grouped_gemm_nvfp4_rowscaled and grouped_gemm_nvfp4_pertensor."""
     import torch
     lib = load_library()
-    n = int(lib.grouped_gemm_mxfp8_workspace_size())
+    n = max(int(lib.grouped_gemm_mxfp8_workspace_size()),
+            int(lib.grouped_gemm_nvfp4_workspace_size()))
     return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
 
 
@@ -531,9 +543,13 @@ def _nv_gemm_check(G, a, a_scales, a_outer, offsets, rows_cap, k, b, b_scales, b
 
 def grouped_gemm_nvfp4_rowscaled(a, a_scales, a_outer, offsets, k, b, b_scales, b_outer,
                                  n_per_group, out=None, ld_out=None, out_dtype=BSG_OUT_BF16,
-                                 scratch=None, G=None, status=None, accumulate=False):
+                                 scratch=None, G=None, status=None, accumulate=False,
+                                 workspace=None):
     """Row-scaled NVFP4 fprop: out [rows_cap, ld_out]; n_per_group is a host list.
-    accumulate=True adds Y to out's previous contents (grouped_gemm_nvfp4_rowscaled_ex)."""
+    accumulate=True adds Y to out's previous contents (grouped_gemm_nvfp4_rowscaled_ex).
+    With a `workspace` (gemm_workspace(), fused epilogue only),
+    grouped_gemm_nvfp4_rowscaled_ws: the last round of tiles is split along the
+    contraction."""
     import torch
     lib = load_library()
     _need_cuda(a, a_scales, a_outer, offsets, b, b_scales, b_outer)
@@ -551,6 +567,16 @@ def grouped_gemm_nvfp4_rowscaled(a, a_scales, a_outer, offsets, k, b, b_scales, 
                    ld_out, out_dtype, status, per_tensor=False)
     _req(scratch, "scratch", 4 * rows_cap * ld_out, torch.float32, optional=True)
     host_n = (ctypes.c_int64 * G)(*npg)
+    if workspace is not None:
+        if scratch is not None:
+            raise ValueError("a workspace serves the fused epilogue only (no scratch)")
+        _need_cuda(workspace)
+        _check(lib.grouped_gemm_nvfp4_rowscaled_ws(
+            G, _ptr(a), _ptr(a_scales), _ptr(a_outer), _ptr(offsets), rows_cap, k, _ptr(b),
+            _ptr(b_scales), _ptr(b_outer), ctypes.cast(host_n, ctypes.c_void_p), _ptr(out), ld_out,
+            out_dtype, 1 if accumulate else 0, _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _ptr(status), _stream(a)))
+        return out
     if accumulate:
         _check(lib.grouped_gemm_nvfp4_rowscaled_ex(
             G, _ptr(a), _ptr(a_scales), _ptr(a_outer), _ptr(offsets), rows_cap, k, _ptr(b),
@@ -593,9 +619,11 @@ def grouped_gemm_nvfp4_rowscaled_noalloc(a, a_scales, a_outer, offsets, k, b, b_
 
 def grouped_gemm_nvfp4_pertensor(a, a_scales, a_amax, offsets, k, b, b_scales, b_amax, n_per_group,
                                  out=None, ld_out=None, out_dtype=BSG_OUT_BF16, G=None,
-                                 status=None):
+                                 status=None, workspace=None):
     """Per-tensor NVFP4 fprop (alpha per group from the two amax arrays): out
-    [rows_cap, ld_out]; n_per_group is a host list."""
+    [rows_cap, ld_out]; n_per_group is a host list.  With a `workspace`
+    (gemm_workspace()), grouped_gemm_nvfp4_pertensor_ws: the last round of tiles
+    is split along the contraction."""
     import torch
     lib = load_library()
     _need_cuda(a, a_scales, a_amax, offsets, b, b_scales, b_amax)
@@ -612,6 +640,14 @@ def grouped_gemm_nvfp4_pertensor(a, a_scales, a_amax, offsets, k, b, b_scales, b
     _nv_gemm_check(G, a, a_scales, a_amax, offsets, rows_cap, k, b, b_scales, b_amax, npg, out,
                    ld_out, out_dtype, status, per_tensor=True)
     host_n = (ctypes.c_int64 * G)(*npg)
+    if workspace is not None:
+        _need_cuda(workspace)
+        _check(lib.grouped_gemm_nvfp4_pertensor_ws(
+            G, _ptr(a), _ptr(a_scales), _ptr(a_amax), _ptr(offsets), rows_cap, k, _ptr(b),
+            _ptr(b_scales), _ptr(b_amax), ctypes.cast(host_n, ctypes.c_void_p), _ptr(out), ld_out,
+            out_dtype, _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(status),
+            _stream(a)))
+        return out
     _check(lib.grouped_gemm_nvfp4_pertensor(G, _ptr(a), _ptr(a_scales), _ptr(a_amax),
                                             _ptr(offsets), rows_cap, k, _ptr(b), _ptr(b_scales),
                                             _ptr(b_amax), ctypes.cast(host_n, ctypes.c_void_p),

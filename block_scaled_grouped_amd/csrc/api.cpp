@@ -345,7 +345,8 @@ static int gemm_nvfp4_impl(const char* fn, bool per_tensor, int64_t G, const uin
                            int64_t rows_cap, int64_t k, const uint8_t* b, const uint8_t* b_scales,
                            const float* b_outer, const int64_t* n_per_group, void* out,
                            int64_t ld_out, int out_dtype, float* scratch, uint32_t* dev_status,
-                           void* stream, bool noalloc = false, bool accumulate = false) {
+                           void* stream, bool noalloc = false, bool accumulate = false,
+                           void* ws = nullptr) {
   if (a == nullptr || a_scales == nullptr || a_outer == nullptr || offsets == nullptr || b == nullptr ||
       b_scales == nullptr || b_outer == nullptr || n_per_group == nullptr || out == nullptr)
     return fail(BSG_ERR_NULL, "%s: operands, scales, offsets, n_per_group and out must be non-NULL", fn);
@@ -393,8 +394,52 @@ static int gemm_nvfp4_impl(const char* fn, bool per_tensor, int64_t G, const uin
   return hip_result(bsg::launch_gemm_nvfp4((int)G, a, a_scales, a_outer, offsets, rows_cap, k, b,
                                            b_scales, b_outer, tab, (int)max_n, out, ld_out,
                                            out_dtype == BSG_OUT_F32, scratch, dev_status,
-                                           (hipStream_t)stream, per_tensor, accumulate),
+                                           (hipStream_t)stream, per_tensor, accumulate, ws),
                     fn);
+}
+
+// Checks a split workspace argument; 0 when usable.
+static int check_nvfp4_workspace(const char* fn, void* workspace, size_t workspace_bytes) {
+  if (workspace == nullptr) return fail(BSG_ERR_NULL, "%s: workspace is NULL", fn);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(BSG_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+  const size_t need = bsg::gemm_nvfp4_workspace_bytes();
+  if (workspace_bytes < need)
+    return fail(BSG_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes,
+                need);
+  return BSG_OK;
+}
+
+size_t grouped_gemm_nvfp4_workspace_size(void) { return bsg::gemm_nvfp4_workspace_bytes(); }
+
+int grouped_gemm_nvfp4_rowscaled_ws(int64_t G, const uint8_t* a, const uint8_t* a_scales,
+                                    const float* a_outer, const int64_t* offsets, int64_t rows_cap,
+                                    int64_t k, const uint8_t* b, const uint8_t* b_scales,
+                                    const float* b_outer, const int64_t* n_per_group, void* out,
+                                    int64_t ld_out, int out_dtype, int accumulate, void* workspace,
+                                    size_t workspace_bytes, uint32_t* dev_status, void* stream) {
+  const char* fn = "grouped_gemm_nvfp4_rowscaled_ws";
+  if (accumulate != 0 && accumulate != 1)
+    return fail(BSG_ERR_UNSUPPORTED, "%s: accumulate must be 0 or 1", fn);
+  const int wc = check_nvfp4_workspace(fn, workspace, workspace_bytes);
+  if (wc != BSG_OK) return wc;
+  return gemm_nvfp4_impl(fn, false, G, a, a_scales, a_outer, offsets, rows_cap, k, b, b_scales,
+                         b_outer, n_per_group, out, ld_out, out_dtype, nullptr, dev_status, stream,
+                         false, accumulate == 1, workspace);
+}
+
+int grouped_gemm_nvfp4_pertensor_ws(int64_t G, const uint8_t* a, const uint8_t* a_scales,
+                                    const float* a_amax, const int64_t* offsets, int64_t rows_cap,
+                                    int64_t k, const uint8_t* b, const uint8_t* b_scales,
+                                    const float* b_amax, const int64_t* n_per_group, void* out,
+                                    int64_t ld_out, int out_dtype, void* workspace,
+                                    size_t workspace_bytes, uint32_t* dev_status, void* stream) {
+  const char* fn = "grouped_gemm_nvfp4_pertensor_ws";
+  const int wc = check_nvfp4_workspace(fn, workspace, workspace_bytes);
+  if (wc != BSG_OK) return wc;
+  return gemm_nvfp4_impl(fn, true, G, a, a_scales, a_amax, offsets, rows_cap, k, b, b_scales,
+                         b_amax, n_per_group, out, ld_out, out_dtype, nullptr, dev_status, stream,
+                         false, false, workspace);
 }
 
 int grouped_gemm_nvfp4_rowscaled(int64_t G, const uint8_t* a, const uint8_t* a_scales,

@@ -217,7 +217,11 @@ hipError_t launch_gemm_nvfp4(int G, const uint8_t* a, const uint8_t* a_scales,
                              const float* b_outer, const NvGroupTable& table, int max_n,
                              void* out, int64_t ld_out, int out_f32, float* s_buf,
                              uint32_t* status, hipStream_t stream, bool per_tensor = false,
-                             bool accumulate = false);
+                             bool accumulate = false, void* ws = nullptr);
+
+// Bytes of the workspace that lets launch_gemm_nvfp4 split its last round of
+// tiles along the contraction (on the current device).
+size_t gemm_nvfp4_workspace_bytes();
 
 // The FP32 S of grouped_gemm_nvfp4_rowscaled_noalloc lives in a static device
 // array of this many bytes (per GPU).

@@ -110,6 +110,7 @@ struct NvArgs {
   void* out;
   int64_t ld_out;
   float* s_buf;            // FP32 S of the two-step flow, or null (fused epilogue)
+  char* ws;                // split workspace (fused fprop epilogue only), or null
   uint32_t* status;
   int G;
   int out_f32;
@@ -117,6 +118,26 @@ struct NvArgs {
   int accumulate;  // out = out_previous + Y instead of Y (row-scaled flows)
   NvGroupTable tab;
 };
+
+// The split of a partly filled last round of tiles along the contraction
+// (fprop with the fused epilogue, as in the MXFP8 GEMM): the workspace holds a
+// 16 KiB header -- the number of split tiles and of parts per tile, then one
+// NvSplitRecord per split tile from byte 64 -- and one 256 KiB FP32 part per
+// workgroup of that round; a second kernel sums each tile's parts in a fixed
+// order and applies the outer scales (or alpha) and the store.
+constexpr int kSplitMax = 8;
+constexpr int64_t kWsHeader = 16384;
+constexpr int64_t kPartBytes = (int64_t)BM * BN * 4;
+
+struct NvSplitRecord {
+  int64_t out_off;      // byte offset of the tile's first output element
+  const float* aout_t;  // row-scaled: the outer scales of the tile's rows
+  const float* bout_t;  // and of its columns
+  float alpha;          // per-tensor: alpha_g of every row (columns 1)
+  int32_t out_rows, out_cols, ldc, per_tensor;
+};
+static_assert(sizeof(NvSplitRecord) == 48, "split record layout");
+constexpr int kMaxSplitTiles = (int)((kWsHeader - 64) / sizeof(NvSplitRecord));
 
 struct Smem {
   uint8_t ring[kStages][kStageB];
@@ -413,6 +434,24 @@ __device__ __forceinline__ void epilogue_tile(const v16f (&acc)[4][4], bool fuse
   });
 }
 
+// The accumulators of one part of a split tile: unit u = 16 w + 4 i + j (wave
+// w's block (i, j)) at part + 1024 u floats, lane l's 16 values at + 16 l; one
+// block at a time, like the epilogue.
+__device__ __forceinline__ void store_part(float* __restrict__ part, const v16f (&acc)[4][4],
+                                           int w, int lane) {
+  static_for<16>([&](auto bc) {
+    constexpr int i = decltype(bc)::value >> 2, j = decltype(bc)::value & 3;
+    fence();
+    v16f y = acc[i][j];
+    asm volatile("" : "+v"(y));
+    float* dst = part + (int64_t)(16 * w + 4 * i + j) * 1024 + 16 * lane;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<v4f*>(dst + 4 * q) = v4f{y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]};
+    fence();
+  });
+}
+
 // What a tile's epilogue needs besides its TileDesc.
 struct TileJob {
   TileDesc t;
@@ -420,9 +459,12 @@ struct TileJob {
 };
 
 // Tile `tile`'s descriptor, output position and outer-scale sources.
+// part >= 0 (fprop): the tile's part `part` of `nsplit`, stages
+// [np * part / nsplit, np * (part + 1) / nsplit) of the contraction.
 template <bool WGRAD>
 __device__ __forceinline__ TileJob make_job(const NvArgs& p, const Smem& sm, int G, int tile,
-                                            int& g, const float*& aout_t, const float*& bout_t) {
+                                            int& g, const float*& aout_t, const float*& bout_t,
+                                            int part = -1, int nsplit = 1) {
   g = __builtin_amdgcn_readfirstlane(find_group(sm.pre, G, tile));
   const int local = tile - sm.pre[g];
   TileJob job;
@@ -470,6 +512,17 @@ __device__ __forceinline__ TileJob make_job(const NvArgs& p, const Smem& sm, int
     bout_t = p.bout + brow0;
     job.out_off = row0 * p.ld_out + n0;
     job.ld_out = p.ld_out;
+    if (part >= 0) {
+      const int np = (int)((p.k + kStageK - 1) / kStageK);
+      const int p0 = np * part / nsplit, p1 = np * (part + 1) / nsplit;
+      const int64_t k0 = (int64_t)p0 * kStageK;
+      const int64_t k1 = (int64_t)p1 * kStageK < p.k ? (int64_t)p1 * kStageK : p.k;
+      t.a += k0 / 2;
+      t.as += k0 / 16;
+      t.b += k0 / 2;
+      t.bs += k0 / 16;
+      t.kl = k1 - k0;
+    }
   }
   return job;
 }
@@ -482,7 +535,7 @@ __device__ __forceinline__ TileJob make_job(const NvArgs& p, const Smem& sm, int
 // set must be free.
 template <int SM, bool WGRAD>
 __device__ __forceinline__ void start_tile(const NvArgs& p, Smem& sm, uint32_t ring, int G,
-                                           int tile, int set, int tid) {
+                                           int tile, int part, int nsplit, int set, int tid) {
   // opaque copy of the thread index: keeps the per-lane copy offsets from being
   // hoisted out of the tile loop (and spilled)
   asm volatile("" : "+v"(tid));
@@ -491,7 +544,7 @@ __device__ __forceinline__ void start_tile(const NvArgs& p, Smem& sm, uint32_t r
   int g;
   const float* aout_t;
   const float* bout_t;
-  const TileJob job = make_job<WGRAD>(p, sm, G, tile, g, aout_t, bout_t);
+  const TileJob job = make_job<WGRAD>(p, sm, G, tile, g, aout_t, bout_t, part, nsplit);
   const TileDesc& t = job.t;
   const bool contract = t.kl > 0;
   // per-tensor NVFP4: alpha_g = tsi(amax_A[g]) * tsi(amax_B[g]) on every row,
@@ -548,27 +601,59 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
   const int total = sm.pre[G];
   const uint32_t ring = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)sm.ring[0];
 
+  // the split of a partly filled last round (fprop, fused epilogue)
+  const int grid = (int)gridDim.x;
+  const int full = total / grid, left = total - full * grid;
+  int nsplit = 1;
+  if (!WGRAD && p.ws != nullptr && p.s_buf == nullptr && left > 0 && left <= kMaxSplitTiles) {
+    const int np = (int)((p.k + kStageK - 1) / kStageK);
+    nsplit = grid / left;
+    if (nsplit > kSplitMax) nsplit = kSplitMax;
+    if (nsplit > np / 2) nsplit = np / 2;
+    if (nsplit < 2) nsplit = 1;
+  }
+  if (p.ws != nullptr && blockIdx.x == 0 && tid0 == 0) {
+    int32_t* hdr = reinterpret_cast<int32_t*>(p.ws);
+    hdr[0] = nsplit > 1 ? left : 0;
+    hdr[1] = nsplit;
+  }
+
   const int slot = xcd_slot();
+  // This workgroup's unit of round r: a whole tile (part -1), or in a split
+  // last round part slot % nsplit of tile full * grid + slot / nsplit.
+  auto unit = [&](int r, int& tl, int& pt) -> bool {
+    if (nsplit > 1 && r >= full) {
+      if (r > full || slot >= left * nsplit) return false;
+      tl = full * grid + slot / nsplit;
+      pt = slot % nsplit;
+      return true;
+    }
+    tl = r * grid + slot;
+    pt = -1;
+    return tl < total;
+  };
   // Tiles are software-pipelined: the next tile's set-up, its first three
   // stages' copies and its outer scales are issued before this tile's
   // epilogue, so they land while its stores drain.
-  int tile = slot, set = 0;
-  if (tile < total) start_tile<SM, WGRAD>(p, sm, ring, G, tile, set, tid0);
-  while (tile < total) {
+  int round = 0, tile = 0, part = -1, set = 0;
+  bool have = unit(0, tile, part);
+  if (have) start_tile<SM, WGRAD>(p, sm, ring, G, tile, part, nsplit, set, tid0);
+  while (have) {
     // opaque copies of the thread and tile indices: keep the compiler from
     // hoisting every LDS / global offset of the tile body out of the tile loop,
     // or carrying the tile's descriptor through the previous epilogue
     int tid = tid0;
     asm volatile("" : "+v"(tid));
     asm volatile("" : "+s"(tile));
+    asm volatile("" : "+s"(part));
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = w >> 1, wn = w & 1;
     const int r = lane & 31, h = lane >> 5;
-    int g_unused;
-    const float* ao_unused;
-    const float* bo_unused;
-    const TileJob job = make_job<WGRAD>(p, sm, G, tile, g_unused, ao_unused, bo_unused);
+    int g_t;
+    const float* aout_t;
+    const float* bout_t;
+    const TileJob job = make_job<WGRAD>(p, sm, G, tile, g_t, aout_t, bout_t, part, nsplit);
     const TileDesc& t = job.t;
     v16f acc[4][4];
 #pragma unroll
@@ -608,8 +693,33 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
     // the previous epilogue, every wave has left at the barriers above)
     const int64_t out_off = job.out_off, ld_out = job.ld_out;
     const int a_rows = t.a_rows, b_rows = t.b_rows;
-    const int next = tile + (int)gridDim.x;
-    if (next < total) start_tile<SM, WGRAD>(p, sm, ring, G, next, set ^ 1, tid0);
+    int next = 0, npart = -1;
+    const bool nhave = unit(round + 1, next, npart);
+    if (nhave) start_tile<SM, WGRAD>(p, sm, ring, G, next, npart, nsplit, set ^ 1, tid0);
+
+    if (part >= 0) {
+      // a part of a split tile: its raw sums into this workgroup's part slot;
+      // part 0 records where the tile's output and outer scales are
+      store_part(reinterpret_cast<float*>(p.ws + kWsHeader + (int64_t)slot * kPartBytes), acc, w,
+                 lane);
+      if (part == 0 && tid0 == 0) {
+        NvSplitRecord* rec = reinterpret_cast<NvSplitRecord*>(p.ws + 64) + slot / nsplit;
+        rec->out_off = out_off * (p.out_f32 ? 4 : 2);
+        rec->aout_t = aout_t;
+        rec->bout_t = bout_t;
+        rec->alpha = p.per_tensor ? (p.aout[g_t] / 2688.0f) * (p.bout[g_t] / 2688.0f) : 0.0f;
+        rec->out_rows = a_rows;
+        rec->out_cols = b_rows;
+        rec->ldc = (int32_t)ld_out;
+        rec->per_tensor = p.per_tensor;
+      }
+      tile = next;
+      part = npart;
+      have = nhave;
+      ++round;
+      set ^= 1;
+      continue;
+    }
 
     // epilogue: S -> (S * a_outer) * b_outer, or S itself into the scratch
     const bool fused = p.s_buf == nullptr;
@@ -642,6 +752,9 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(NvArgs p) {
       else epilogue_tile<false, false, false>(acc, fused, ao_base, bo_base, ro, ldc, row, col, h, b_rows);
     }
     tile = next;
+    part = npart;
+    have = nhave;
+    ++round;
     set ^= 1;
   }
   // the last tile's stores, and copies of a start that had no tile, complete
@@ -723,7 +836,96 @@ __global__ __launch_bounds__(256) void nv_postscale_kernel(const float* __restri
   }
 }
 
+// The second step of a split: each split tile's parts summed in the order
+// s = 0, 1, .., then Y = (S * a_outer[r]) * b_outer[n] (per-tensor: S * alpha_g)
+// and the fused epilogue's store (or, with accumulate, its read-add-store).
+// Work item (tile l, group ug of four units): wave w takes unit 4 ug + w.
+__global__ __launch_bounds__(kThreads) void nv_split_reduce_kernel(const char* __restrict__ ws,
+                                                                   void* out, int out_f32,
+                                                                   int accumulate) {
+  const int32_t* hdr = reinterpret_cast<const int32_t*>(ws);
+  const int nl = hdr[0], nsplit = hdr[1];
+  if (nl <= 0) return;
+  const NvSplitRecord* recs = reinterpret_cast<const NvSplitRecord*>(ws + 64);
+  const float* parts = reinterpret_cast<const float*>(ws + kWsHeader);
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int r = lane & 31, h = lane >> 5;
+  const int esz = out_f32 ? 4 : 2;
+  for (int it = blockIdx.x; it < nl * 16; it += gridDim.x) {
+    const int l = it / 16;
+    const int u = 4 * (it % 16) + w;  // unit: source wave u / 16, block ((u / 4) % 4, u % 4)
+    v16f y = v16f{};
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float* src = parts + (int64_t)(l * nsplit + sp) * (kPartBytes / 4) +
+                         (int64_t)u * 1024 + 16 * lane;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const v4f v = *reinterpret_cast<const v4f*>(src + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[4 * q + e] += v[e];
+      }
+    }
+    const NvSplitRecord rec = recs[l];
+    const int wsrc = u / 16, i = (u / 4) % 4, j = u % 4;
+    const int row = (wsrc >> 1) * 128 + 32 * i + r, col = (wsrc & 1) * 128 + 32 * j + 4 * h;
+    // outer scales as the fused epilogue takes them: rows and columns past
+    // the tile's read 0 (their stores are dropped anyway)
+    float ao;
+    if (rec.per_tensor) {
+      ao = rec.alpha;
+    } else {
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(rec.aout_t, (int64_t)rec.out_rows * 4);
+      ao = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(ra, 4 * row, 0, 0));
+    }
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc(rec.bout_t, rec.per_tensor ? 0 : (int64_t)rec.out_cols * 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float bo = rec.per_tensor ? 1.0f
+                                        : __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                              rb, 4 * (col + 8 * q + e), 0, 0));
+        y[4 * q + e] = (y[4 * q + e] * ao) * bo;
+      }
+    }
+    const __amdgpu_buffer_rsrc_t ro =
+        make_rsrc(reinterpret_cast<char*>(out) + rec.out_off, (int64_t)rec.out_rows * rec.ldc * esz);
+    const int ldc = rec.ldc;
+    if (accumulate) {
+      EpiTerms ep;
+      ep.alpha = 1.0f;
+      ep.beta = 1.0f;
+      ep.has_bias = false;
+      ep.bias = ro;
+      const bool wide4 = (ldc & 3) == 0 && (rec.out_cols & 3) == 0;
+      if (out_f32) {
+        if (wide4) store_block_ex<true, true>(y, ro, ldc, row, col, rec.out_cols, ep);
+        else store_block_ex<false, true>(y, ro, ldc, row, col, rec.out_cols, ep);
+      } else {
+        if (wide4) store_block_ex<true, false>(y, ro, ldc, row, col, rec.out_cols, ep);
+        else store_block_ex<false, false>(y, ro, ldc, row, col, rec.out_cols, ep);
+      }
+    } else if (out_f32) {
+      if ((ldc & 3) == 0 && (rec.out_cols & 3) == 0)
+        store_block<true, true>(y, ro, ldc, row, col, h, rec.out_cols);
+      else
+        store_block<false, true>(y, ro, ldc, row, col, h, rec.out_cols);
+    } else {
+      if ((ldc & 7) == 0 && (rec.out_cols & 7) == 0)
+        store_block<true, false>(y, ro, ldc, row, col, h, rec.out_cols);
+      else
+        store_block<false, false>(y, ro, ldc, row, col, h, rec.out_cols);
+    }
+  }
+}
+
 }  // namespace
+
+size_t gemm_nvfp4_workspace_bytes() {
+  return (size_t)kWsHeader + (size_t)device_cu_count() * (size_t)kPartBytes;
+}
 
 hipError_t launch_gemm_nvfp4(int G, const uint8_t* a, const uint8_t* a_scales,
                              const float* a_outer, const int64_t* offsets, int64_t rows_cap,
@@ -731,11 +933,13 @@ hipError_t launch_gemm_nvfp4(int G, const uint8_t* a, const uint8_t* a_scales,
                              const float* b_outer, const NvGroupTable& table, int max_n,
                              void* out, int64_t ld_out, int out_f32, float* s_buf,
                              uint32_t* status, hipStream_t stream, bool per_tensor,
-                             bool accumulate) {
+                             bool accumulate, void* ws) {
   NvArgs p;
   p.a = a; p.as = a_scales; p.aout = a_outer; p.offsets = offsets; p.rows_cap = rows_cap; p.k = k;
   p.n = 0;
   p.b = b; p.bs = b_scales; p.bout = b_outer; p.out = out; p.ld_out = ld_out; p.s_buf = s_buf;
+  if (s_buf != nullptr) ws = nullptr;  // the split serves the fused epilogue only
+  p.ws = static_cast<char*>(ws);
   p.status = status; p.G = G; p.out_f32 = out_f32; p.per_tensor = per_tensor ? 1 : 0;
   p.accumulate = accumulate ? 1 : 0;
   p.tab = table;
@@ -753,6 +957,14 @@ hipError_t launch_gemm_nvfp4(int G, const uint8_t* a, const uint8_t* a_scales,
                          dim3(kThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    // the split tiles' second step (returns at once when the GEMM split
+    // nothing); a split needs at least two parts of two stages each
+    if (ws != nullptr && (k + kStageK - 1) / kStageK >= 4) {
+      hipLaunchKernelGGL(nv_split_reduce_kernel, dim3((unsigned)device_cu_count()), dim3(kThreads),
+                         0, stream, static_cast<const char*>(ws), out, out_f32, accumulate ? 1 : 0);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   if (s_buf != nullptr && rows_cap > 0) {
     const bool vec = ld_out % 4 == 0 && reinterpret_cast<uintptr_t>(s_buf) % 16 == 0 &&
@@ -831,6 +1043,7 @@ hipError_t launch_gemm_nvfp4_wgrad(int G, const uint8_t* a, const uint8_t* a_sca
   p.a = a; p.as = a_scales; p.aout = a_outer; p.offsets = padded_offsets;
   p.rows_cap = col_rows_cap; p.k = k; p.n = n;
   p.b = b; p.bs = b_scales; p.bout = b_outer; p.out = out; p.ld_out = k; p.s_buf = nullptr;
+  p.ws = nullptr;
   p.status = status; p.G = G; p.out_f32 = out_f32; p.per_tensor = 0; p.tab = NvGroupTable{};
   p.accumulate = accumulate ? 1 : 0;
   const int64_t bound = (int64_t)G * ((n + BM - 1) / BM) * ((k + BN - 1) / BN);

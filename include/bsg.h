@@ -502,6 +502,46 @@ int grouped_gemm_nvfp4_pertensor(int64_t G, const uint8_t* a, const uint8_t* a_s
                                  int64_t ld_out, int out_dtype, uint32_t* dev_status, void* stream);
 
 /*
+ * grouped_gemm_nvfp4_workspace_size / grouped_gemm_nvfp4_rowscaled_ws /
+ * grouped_gemm_nvfp4_pertensor_ws
+ *
+ * The row-scaled NVFP4 GEMM with its fused outer-scale epilogue (and the
+ * copy-or-accumulate flag of grouped_gemm_nvfp4_rowscaled_ex), and the
+ * per-tensor NVFP4 GEMM, with a workspace that removes most of their last,
+ * partly filled round of output tiles, as grouped_gemm_mxfp8_ws does: each
+ * tile of that round is split along the contraction into S parts (2 <= S <= 8,
+ * at most P / (T mod P) for T tiles on P workgroups, each part at least two
+ * 128-deep stages), the parts' FP32 sums go to the workspace, and a second
+ * kernel on the same stream adds them in a fixed order, then applies
+ * (S * a_outer[r]) * b_outer[n] -- per-tensor: S * alpha_g -- and the store (or
+ * accumulate) exactly as the fused epilogue does.  Deterministic; a split
+ * tile's S is summed in a different order than without the workspace
+ * (differences within FP32 rounding).  Arguments and errors as
+ * grouped_gemm_nvfp4_rowscaled_ex (no scratch: the fused epilogue only) and
+ * grouped_gemm_nvfp4_pertensor, plus:
+ *   workspace        [device] grouped_gemm_nvfp4_workspace_size() bytes, 256-byte
+ *                    aligned, owned by the caller; its contents on entry do not
+ *                    matter, and calls that share it must not overlap.
+ *   workspace_bytes  its size: less than the query gives BSG_ERR_WORKSPACE; NULL
+ *                    workspace BSG_ERR_NULL; misaligned BSG_ERR_ALIGN.
+ * The size depends on the current device's compute-unit count: 16 KiB plus
+ * 256 KiB per unit (64 MiB on 256 units).
+ */
+size_t grouped_gemm_nvfp4_workspace_size(void);
+int grouped_gemm_nvfp4_rowscaled_ws(int64_t G, const uint8_t* a, const uint8_t* a_scales,
+                                    const float* a_outer, const int64_t* offsets, int64_t rows_cap,
+                                    int64_t k, const uint8_t* b, const uint8_t* b_scales,
+                                    const float* b_outer, const int64_t* n_per_group, void* out,
+                                    int64_t ld_out, int out_dtype, int accumulate, void* workspace,
+                                    size_t workspace_bytes, uint32_t* dev_status, void* stream);
+int grouped_gemm_nvfp4_pertensor_ws(int64_t G, const uint8_t* a, const uint8_t* a_scales,
+                                    const float* a_amax, const int64_t* offsets, int64_t rows_cap,
+                                    int64_t k, const uint8_t* b, const uint8_t* b_scales,
+                                    const float* b_amax, const int64_t* n_per_group, void* out,
+                                    int64_t ld_out, int out_dtype, void* workspace,
+                                    size_t workspace_bytes, uint32_t* dev_status, void* stream);
+
+/*
  * grouped_gemm_nvfp4_rowscaled_wgrad
  *
  * Row-scaled NVFP4 weight gradient, NT, over each expert's ragged tokens

@@ -112,6 +112,19 @@ def test_gemm_validation(lib):
     assert pt(2, p, p, p, p, 64, 128, p, p, p, hp, p, 128, 5, None, None) == 4      # out_dtype
     ex = lib.grouped_gemm_nvfp4_rowscaled_ex
     assert ex(2, p, p, p, p, 64, 128, p, p, p, hp, p, 128, 0, None, 2, None, None) == 4  # flag
+    nneed = lib.grouped_gemm_nvfp4_workspace_size()
+    assert nneed >= 16384 + 256 * 1024
+    nws = lib.grouped_gemm_nvfp4_rowscaled_ws
+    assert nws(2, p, p, p, p, 64, 128, p, p, p, hp, p, 128, 0, 0, None, nneed, None, None) == 1
+    assert nws(2, p, p, p, p, 64, 128, p, p, p, hp, p, 128, 0, 0, wsa, nneed - 1, None, None) == 5
+    assert nws(2, p, p, p, p, 64, 128, p, p, p, hp, p, 128, 0, 0,
+               ctypes.c_void_p(wsa.value + 64), nneed, None, None) == 3
+    assert nws(2, p, p, p, p, 64, 128, p, p, p, hp, p, 128, 0, 2, wsa, nneed, None, None) == 4
+    assert nws(2, p, p, p, p, 64, 48, p, p, p, hp, p, 128, 0, 0, wsa, nneed, None, None) == 2
+    pws = lib.grouped_gemm_nvfp4_pertensor_ws
+    assert pws(2, p, p, p, p, 64, 128, p, p, p, hp, p, 128, 0, None, nneed, None, None) == 1
+    assert pws(2, p, p, p, p, 64, 128, p, p, p, hp, p, 128, 0, wsa, nneed - 1, None, None) == 5
+    assert pws(2, p, p, p, p, 64, 80, p, p, p, hp, p, 128, 0, wsa, nneed, None, None) == 2
     assert ex(2, p, p, p, p, 64, 48, p, p, p, hp, p, 128, 0, None, 1, None, None) == 2   # k % 32
     wx = lib.grouped_gemm_nvfp4_rowscaled_wgrad_ex
     assert wx(2, p, p, p, p, p, p, p, 256, 128, 128, p, 0, -1, None, None) == 4          # flag

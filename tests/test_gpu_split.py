@@ -200,3 +200,161 @@ def test_split_hip_graph_replay_with_new_sizes():
         torch.cuda.synchronize()
         live = new[-1]
         assert torch.equal(replayed[:live], out[:live]), new
+
+
+# ---------------------------------------------------------------- NVFP4
+# (sizes, n_per_group, K, rows_cap): every tile split (13 tiles on a grid of
+# 126), and a full round followed by a partial one (296 tiles on 256)
+NV_SPLIT_CASES = [
+    ([300, 0, 700], [512, 256, 768], 1024, 9984),
+    ([2560, 1000, 0, 6170], [2048, 1024, 512, 2048], 1024, 9984),
+]
+
+
+def _nv_tiles(sizes, npg):
+    return sum(-(-int(m) // 256) * -(-int(n) // 256) for m, n in zip(sizes, npg))
+
+
+def _pad_rows(a, rows):
+    o = np.zeros((rows,) + a.shape[1:], a.dtype)
+    o[:a.shape[0]] = a
+    return to_dev(o)
+
+
+def _nv_check(y, ref, npg, off, live, out_f32):
+    for g, (rows, r) in enumerate(ref):
+        if len(rows) == 0:
+            continue
+        gemm_tolerance_check(y[rows][:, :npg[g]], r, out_f32, "group %d" % g)
+        assert np.all(np.isnan(y[rows][:, npg[g]:])), "columns past N_g must stay untouched"
+    assert np.all(np.isnan(y[live:])), "capacity rows must stay untouched"
+
+
+def _nv_header(ws, sizes, npg):
+    ntiles = _nv_tiles(sizes, npg)
+    hdr = host(ws[:8].view(torch.int32))
+    assert hdr[0] == ntiles % min(ntiles, 256) or hdr[0] == ntiles, hdr
+    assert 2 <= hdr[1] <= 8, hdr
+
+
+@pytest.mark.parametrize("sizes,npg,K,rows_cap", NV_SPLIT_CASES)
+@pytest.mark.parametrize("out_f32", [True, False])
+def test_nvfp4_pertensor_split_matches_unsplit_and_oracle(sizes, npg, K, rows_cap, out_f32):
+    rng = np.random.default_rng(3 * K + rows_cap + out_f32)
+    sizes = np.array(sizes, np.int32)
+    _, off = O.group_offsets(sizes)
+    live = int(off[-1])
+    x = _bits(rng, (rows_cap, K))
+    w = _bits(rng, (sum(npg), K), 0.02)
+    boff = np.concatenate([[0], np.cumsum(npg)])
+    ap, asc, aam = Q.nvfp4_pertensor(x, off)
+    bp, bsc, bam = Q.nvfp4_pertensor(w, boff)
+    ld = max(npg) + 8
+    args = (_pad_rows(ap, rows_cap), _pad_rows(asc, rows_cap), to_dev(aam), to_dev(off), K,
+            to_dev(bp), to_dev(bsc), to_dev(bam), npg)
+    dt = torch.float32 if out_f32 else torch.bfloat16
+    od = bsg.BSG_OUT_F32 if out_f32 else bsg.BSG_OUT_BF16
+    ws = bsg.gemm_workspace(device())
+    outs = []
+    for wsx in (None, ws):
+        out = torch.full((rows_cap, ld), float("nan"), dtype=dt, device=device())
+        bsg.grouped_gemm_nvfp4_pertensor(*args, out=out, ld_out=ld, out_dtype=od, workspace=wsx)
+        torch.cuda.synchronize()
+        outs.append(bf16_out_to_f64(out))
+    plain, split = outs
+    _nv_check(split, GM.nvfp4_pertensor_fprop(ap, asc, aam, off, bp, bsc, bam, npg, K), npg, off,
+              live, out_f32)
+    _nv_header(ws, sizes, npg)
+    fin = np.isfinite(plain)
+    assert np.array_equal(fin, np.isfinite(split))
+    scale = np.max(np.abs(plain[fin]))
+    if out_f32:
+        assert np.max(np.abs(split[fin] - plain[fin])) <= 1e-5 * scale
+    else:
+        assert np.all(np.abs(split[fin] - plain[fin]) <= 2.0 ** -7 * np.abs(plain[fin]) + 1e-6 * scale)
+
+
+@pytest.mark.parametrize("sizes,npg,K,rows_cap", NV_SPLIT_CASES)
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_nvfp4_rowscaled_split_matches_oracle(sizes, npg, K, rows_cap, accumulate):
+    """The split's second kernel applies the row and column outer scales, and
+    with the accumulate flag adds to the output's previous contents."""
+    rng = np.random.default_rng(5 * K + rows_cap + accumulate)
+    sizes = np.array(sizes, np.int32)
+    _, off = O.group_offsets(sizes)
+    live = int(off[-1])
+    x = _bits(rng, (rows_cap, K))
+    w = _bits(rng, (sum(npg), K), 0.02)
+    ap, asc, at = Q.nvfp4_rowscaled(x, off)
+    bp, bsc, bt = Q.nvfp4_rowscaled(w, np.array([0, sum(npg)]))
+    ld = max(npg) + 4
+    prev = (rng.standard_normal((rows_cap, ld)) * 3).astype(np.float32)
+    prev[live:] = np.nan
+    for g in range(len(npg)):
+        prev[off[g]:off[g + 1], npg[g]:] = np.nan
+    out = torch.from_numpy(prev if accumulate else np.full_like(prev, np.nan)).to(device())
+    c_prev = bf16_out_to_f64(out)
+    ws = bsg.gemm_workspace(device())
+    bsg.grouped_gemm_nvfp4_rowscaled(_pad_rows(ap, rows_cap), _pad_rows(asc, rows_cap),
+                                     _pad_rows(at, rows_cap), to_dev(off), K, to_dev(bp),
+                                     to_dev(bsc), to_dev(bt), npg, out=out, ld_out=ld,
+                                     out_dtype=bsg.BSG_OUT_F32, accumulate=accumulate,
+                                     workspace=ws)
+    torch.cuda.synchronize()
+    y = bf16_out_to_f64(out)
+    ref = GM.nvfp4_rowscaled_fprop(ap, asc, at, off, bp, bsc, bt, npg, K)
+    if accumulate:
+        ref = [(rows, r + c_prev[rows][:, :npg[g]]) for g, (rows, r) in enumerate(ref)]
+    _nv_check(y, ref, npg, off, live, True)
+    _nv_header(ws, sizes, npg)
+
+
+def test_nvfp4_split_is_deterministic_and_graph_safe():
+    """Two split calls give the same bits (also with another call through the
+    same workspace between them), and a captured split call replays them."""
+    rng = np.random.default_rng(41)
+    sizes, npg, K, rows_cap = NV_SPLIT_CASES[1]
+    sizes = np.array(sizes, np.int32)
+    _, off = O.group_offsets(sizes)
+    live = int(off[-1])
+    x = _bits(rng, (rows_cap, K))
+    w = _bits(rng, (sum(npg), K), 0.02)
+    boff = np.concatenate([[0], np.cumsum(npg)])
+    a = bsg.grouped_quantize_nvfp4_pertensor(bf16_dev(x), to_dev(off))
+    b = bsg.grouped_quantize_nvfp4_pertensor(bf16_dev(w), to_dev(boff))
+    ws = bsg.gemm_workspace(device())
+    ld = max(npg)
+    out = torch.zeros((rows_cap, ld), dtype=torch.float32, device=device())
+    doff = to_dev(off)
+
+    def step():
+        bsg.grouped_gemm_nvfp4_pertensor(a[0], a[1], a[2], doff, K, b[0], b[1], b[2], npg, out=out,
+                                         out_dtype=bsg.BSG_OUT_F32, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    first = out.clone()
+    # another call through the workspace (all of its tiles split)
+    s2, n2, k2, r2 = NV_SPLIT_CASES[0]
+    _, o2 = O.group_offsets(np.array(s2, np.int32))
+    x2 = _bits(rng, (r2, k2))
+    w2 = _bits(rng, (sum(n2), k2), 0.02)
+    a2 = bsg.grouped_quantize_nvfp4_pertensor(bf16_dev(x2), to_dev(o2))
+    b2 = bsg.grouped_quantize_nvfp4_pertensor(bf16_dev(w2), to_dev(np.concatenate([[0], np.cumsum(n2)])))
+    bsg.grouped_gemm_nvfp4_pertensor(a2[0], a2[1], a2[2], to_dev(o2), k2, b2[0], b2[1], b2[2], n2,
+                                     out_dtype=bsg.BSG_OUT_F32, workspace=ws)
+    out.zero_()
+    step()
+    torch.cuda.synchronize()
+    assert torch.equal(first[:live], out[:live])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    for _ in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(first[:live], out[:live])
