@@ -208,6 +208,8 @@ def test_split_hip_graph_replay_with_new_sizes():
 NV_SPLIT_CASES = [
     ([300, 0, 700], [512, 256, 768], 1024, 9984),
     ([2560, 1000, 0, 6170], [2048, 1024, 512, 2048], 1024, 9984),
+    # k % 64 == 32 (2-byte scale pieces) and a partial last stage in the last part
+    ([300, 0, 700], [512, 256, 768], 1056, 9984),
 ]
 
 
