@@ -210,6 +210,9 @@ NV_SPLIT_CASES = [
     ([2560, 1000, 0, 6170], [2048, 1024, 512, 2048], 1024, 9984),
     # k % 64 == 32 (2-byte scale pieces) and a partial last stage in the last part
     ([300, 0, 700], [512, 256, 768], 1056, 9984),
+    # 200 groups, every other one empty: 100 tiles of one group each, split 2 ways
+    ([(37 * i) % 200 + 1 if i % 2 else 0 for i in range(200)],
+     [32 * (1 + i % 8) for i in range(200)], 512, 10500),
 ]
 
 
