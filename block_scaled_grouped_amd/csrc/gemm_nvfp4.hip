@@ -958,9 +958,11 @@ hipError_t launch_gemm_nvfp4(int G, const uint8_t* a, const uint8_t* a_scales,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // the split tiles' second step (returns at once when the GEMM split
-    // nothing); a split needs at least two parts of two stages each
+    // nothing); a split needs at least two parts of two stages each.  Eight
+    // workgroups per CU: each work item is a short chain of loads, so many
+    // in flight keep it from being latency-bound (empty, it costs the same)
     if (ws != nullptr && (k + kStageK - 1) / kStageK >= 4) {
-      hipLaunchKernelGGL(nv_split_reduce_kernel, dim3((unsigned)device_cu_count()), dim3(kThreads),
+      hipLaunchKernelGGL(nv_split_reduce_kernel, dim3((unsigned)(8 * device_cu_count())), dim3(kThreads),
                          0, stream, static_cast<const char*>(ws), out, out_f32, accumulate ? 1 : 0);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
