@@ -363,3 +363,39 @@ def test_nvfp4_split_is_deterministic_and_graph_safe():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(first[:live], out[:live])
+
+
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_nvfp4_split_bf16_odd_row_stride(accumulate):
+    """The second kernel's element-wise stores: bf16 output with a row stride
+    that is not a multiple of 4 (with and without the accumulate flag)."""
+    rng = np.random.default_rng(71 + accumulate)
+    sizes, npg, K, rows_cap = NV_SPLIT_CASES[0]
+    sizes = np.array(sizes, np.int32)
+    _, off = O.group_offsets(sizes)
+    live = int(off[-1])
+    x = _bits(rng, (rows_cap, K))
+    w = _bits(rng, (sum(npg), K), 0.02)
+    ap, asc, at = Q.nvfp4_rowscaled(x, off)
+    bp, bsc, bt = Q.nvfp4_rowscaled(w, np.array([0, sum(npg)]))
+    ld = max(npg) + 3
+    prev = (rng.standard_normal((rows_cap, ld)) * 3).astype(np.float32)
+    prev[live:] = np.nan
+    for g in range(len(npg)):
+        prev[off[g]:off[g + 1], npg[g]:] = np.nan
+    start = prev if accumulate else np.full_like(prev, np.nan)
+    out = torch.from_numpy(start).to(torch.bfloat16).to(device())
+    c_prev = bf16_out_to_f64(out)
+    ws = bsg.gemm_workspace(device())
+    bsg.grouped_gemm_nvfp4_rowscaled(_pad_rows(ap, rows_cap), _pad_rows(asc, rows_cap),
+                                     _pad_rows(at, rows_cap), to_dev(off), K, to_dev(bp),
+                                     to_dev(bsc), to_dev(bt), npg, out=out, ld_out=ld,
+                                     out_dtype=bsg.BSG_OUT_BF16, accumulate=accumulate,
+                                     workspace=ws)
+    torch.cuda.synchronize()
+    y = bf16_out_to_f64(out)
+    ref = GM.nvfp4_rowscaled_fprop(ap, asc, at, off, bp, bsc, bt, npg, K)
+    if accumulate:
+        ref = [(rows, r + c_prev[rows][:, :npg[g]]) for g, (rows, r) in enumerate(ref)]
+    _nv_check(y, ref, npg, off, live, False)
+    _nv_header(ws, sizes, npg)
