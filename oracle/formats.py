@@ -42,7 +42,10 @@ E8M0_BIAS = 127
 def bf16_bits_to_f64(bits):
     """bf16 bit patterns (uint16) -> exact float64 values."""
     u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
-    return u.view(np.float32).astype(np.float64)
+    # signalling-NaN patterns become quiet NaNs when widened; numpy flags that
+    # as an invalid operation, which is expected here
+    with np.errstate(invalid="ignore"):
+        return u.view(np.float32).astype(np.float64)
 
 
 def f32_to_bf16_bits_rne(x):
