@@ -53,10 +53,13 @@ def _run(args, rows_cap, N, out_f32, ws=None):
     return out
 
 
-# (sizes, K, N, rows_cap): every tile split (10 tiles on a grid of 38), and a
-# full round followed by a partial one (312 tiles on up to 256 workgroups)
+# (sizes, K, N, rows_cap): every tile split (10 tiles on a grid of 38), the
+# same at K = 1056 (9 pairs, the last a quarter full, in 3 parts of 3: the
+# last part ends in the contraction tail), and a full round followed by a partial one
+# (312 tiles on up to 256 workgroups)
 SPLIT_CASES = [
     ([300, 0, 700], 1024, 512, 4096),
+    ([300, 0, 700], 1056, 512, 4096),
     ([2560, 1000, 0, 6170], 1024, 2048, 9984),
 ]
 
@@ -92,7 +95,7 @@ def test_split_fprop_matches_unsplit_and_oracle(sizes, K, N, rows_cap, out_f32):
 def test_split_is_deterministic_and_ignores_a_stale_workspace():
     rng = np.random.default_rng(5)
     ws = bsg.gemm_workspace(device())
-    sizes, K, N, rows_cap = SPLIT_CASES[1]
+    sizes, K, N, rows_cap = SPLIT_CASES[2]
     args, off, ref, live = _fprop(rng, sizes, K, N, rows_cap)
     first = _run(args, rows_cap, N, True, ws)
     # another call through the same workspace, with another shape and split
