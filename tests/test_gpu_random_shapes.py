@@ -252,3 +252,81 @@ def test_random_nvfp4_wgrad(seed):
             assert np.all(y[g] == 0.0) and not np.any(np.signbit(y[g]))
         else:
             gemm_tolerance_check(y[g], ref[g], out_f32, "seed %d group %d" % (seed, g))
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_mxfp8_fprop_epilogue_terms(seed):
+    """grouped_gemm_mxfp8_ex: per-group alpha, beta (0 for some groups, whose
+    previous output holds NaN and must not be read) and a bias, random shapes."""
+    rng = np.random.default_rng(7000 + seed)
+    sizes = _sizes(rng, 10, 300)
+    G, live = len(sizes), int(sizes.sum())
+    N, K = 32 * int(rng.integers(1, 17)), 32 * int(rng.integers(1, 17))
+    rows_cap = live + int(rng.integers(1, 30))
+    out_f32 = bool(rng.integers(0, 2))
+    x = _bits(rng, (rows_cap, K))
+    w = _bits(rng, (G * N, K), 0.02)
+    _, off = O.group_offsets(sizes)
+    woff = np.array([0, G * N])
+    qa = bsg.grouped_quantize_mxfp8(bf16_dev(x), to_dev(off))
+    qb = bsg.grouped_quantize_mxfp8(bf16_dev(w), to_dev(woff))
+    ad, asc = Q.mxfp8_rowwise(x, off)
+    bd, bsc = Q.mxfp8_rowwise(w, woff)
+    s_ref = GM.mxfp8_fprop(ad, asc, bd.reshape(G, N, K), bsc, off, K)
+    grp = np.searchsorted(off, np.arange(live), side="right") - 1
+    alpha = rng.uniform(-2, 2, G).astype(np.float32)
+    beta = np.where(rng.random(G) < 0.5, rng.uniform(0.5, 1.5, G), 0.0).astype(np.float32)
+    bias = rng.standard_normal((G, N)).astype(np.float32)
+    dt = torch.float32 if out_f32 else torch.bfloat16
+    c0 = torch.from_numpy(rng.standard_normal((rows_cap, N)).astype(np.float32)).to(dt)
+    c0[:live][torch.from_numpy(beta[grp] == 0)] = float("nan")
+    c0[live:] = float("nan")
+    out = c0.to(device())
+    c_prev = bf16_out_to_f64(out)
+    bsg.grouped_gemm_mxfp8_ex(bsg.BSG_FPROP_TN, qa["row_data"], qa["row_scales"], qb["row_data"],
+                              qb["row_scales"], to_dev(off), rows_cap, N, K, out,
+                              out_dtype=bsg.BSG_OUT_F32 if out_f32 else bsg.BSG_OUT_BF16,
+                              alpha=to_dev(alpha), beta=to_dev(beta), bias=to_dev(bias))
+    ref = GM.epilogue(s_ref[:live], grp, alpha, beta, c_prev[:live], bias)
+    y = bf16_out_to_f64(out)
+    for g in range(G):
+        if sizes[g]:
+            gemm_tolerance_check(y[off[g]:off[g + 1]], ref[off[g]:off[g + 1]], out_f32,
+                                 "seed %d group %d" % (seed, g))
+    assert np.all(np.isnan(y[live:]))
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_nvfp4_rowscaled_accumulate(seed):
+    """Row-scaled NVFP4 with the accumulate flag (out = out_old + Y), fused or
+    through the FP32 scratch, random shapes."""
+    rng = np.random.default_rng(8000 + seed)
+    sizes = _sizes(rng, 8, 300)
+    G, live = len(sizes), int(sizes.sum())
+    npg = _npg(rng, G)
+    K = 32 * int(rng.integers(1, 17))
+    rows_cap = live + int(rng.integers(1, 40))
+    ld = max(npg) + int(rng.integers(0, 9))
+    fused = bool(rng.integers(0, 2))
+    x = _bits(rng, (rows_cap, K))
+    w = _bits(rng, (sum(npg), K), 0.02)
+    _, off = O.group_offsets(sizes)
+    boff = np.concatenate([[0], np.cumsum(npg)])
+    a = bsg.grouped_quantize_nvfp4_rowscaled(bf16_dev(x), to_dev(off))
+    b = bsg.grouped_quantize_nvfp4_rowscaled(bf16_dev(w), to_dev(boff))
+    ap, asc, at = Q.nvfp4_rowscaled(x, off)
+    bp, bsc, bt = Q.nvfp4_rowscaled(w, boff)
+    c0 = rng.standard_normal((rows_cap, ld)).astype(np.float32)
+    out = torch.from_numpy(c0).to(device())
+    scratch = None if fused else torch.empty((rows_cap, ld), dtype=torch.float32, device=device())
+    bsg.grouped_gemm_nvfp4_rowscaled(a[0], a[1], a[2], to_dev(off), K, b[0], b[1], b[2], npg,
+                                     out=out, ld_out=ld, out_dtype=bsg.BSG_OUT_F32,
+                                     scratch=scratch, accumulate=True,
+                                     workspace=_workspace(rng) if fused else None)
+    y = host(out).astype(np.float64)
+    for g, (rows, r) in enumerate(GM.nvfp4_rowscaled_fprop(ap, asc, at, off, bp, bsc, bt, npg, K)):
+        if len(rows):
+            gemm_tolerance_check(y[rows][:, :npg[g]], r + c0[rows][:, :npg[g]], True,
+                                 "seed %d group %d" % (seed, g))
+            assert np.array_equal(y[rows][:, npg[g]:], c0[rows][:, npg[g]:])
+    assert np.array_equal(y[live:], c0[live:])
