@@ -330,3 +330,50 @@ def test_random_nvfp4_rowscaled_accumulate(seed):
                                  "seed %d group %d" % (seed, g))
             assert np.array_equal(y[rows][:, npg[g]:], c0[rows][:, npg[g]:])
     assert np.array_equal(y[live:], c0[live:])
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_nvfp4_rht_and_2d_gemm(seed):
+    """Per-tensor NVFP4 with the Hadamard transform (a random sign mask) on both
+    operands, or with 2-D block scales on the weights: quantized bytes and amax
+    bit-exact, the GEMM within the tolerance of the oracle's."""
+    rng = np.random.default_rng(9000 + seed)
+    sizes = _sizes(rng, 8, 300)
+    G, live = len(sizes), int(sizes.sum())
+    npg = [16 * int(rng.integers(2, 17)) for _ in range(G)]
+    K = 32 * int(rng.integers(1, 17))
+    rows_cap = live + int(rng.integers(1, 40))
+    out_f32 = bool(rng.integers(0, 2))
+    rht = bool(rng.integers(0, 2))
+    mask = int(rng.integers(0, 1 << 16))
+    x = _bits(rng, (rows_cap, K))
+    w = _bits(rng, (sum(npg), K), 0.02)
+    _, off = O.group_offsets(sizes)
+    boff = np.concatenate([[0], np.cumsum(npg)])
+    if rht:
+        a = bsg.grouped_quantize_nvfp4_pertensor_rht(bf16_dev(x), to_dev(off), mask)
+        b = bsg.grouped_quantize_nvfp4_pertensor_rht(bf16_dev(w), to_dev(boff), mask)
+        ap, asc, aam = Q.nvfp4_pertensor_rht(x, off, mask)
+        bp, bsc, bam = Q.nvfp4_pertensor_rht(w, boff, mask)
+    else:
+        a = bsg.grouped_quantize_nvfp4_pertensor(bf16_dev(x), to_dev(off))
+        b = bsg.grouped_quantize_nvfp4_pertensor_2d(bf16_dev(w), to_dev(boff))
+        ap, asc, aam = Q.nvfp4_pertensor(x, off)
+        bp, bsc, bam = Q.nvfp4_pertensor_2d(w, boff)
+    assert np.array_equal(host_u8(a[0])[:live], ap[:live])
+    assert np.array_equal(host_u8(a[1])[:live], asc[:live])
+    assert np.array_equal(host(a[2]).view(np.uint32), aam.view(np.uint32))
+    assert np.array_equal(host_u8(b[0]), bp)
+    assert np.array_equal(host_u8(b[1]), bsc)
+    assert np.array_equal(host(b[2]).view(np.uint32), bam.view(np.uint32))
+    dt = torch.float32 if out_f32 else torch.bfloat16
+    out = torch.full((rows_cap, max(npg)), float("nan"), dtype=dt, device=device())
+    bsg.grouped_gemm_nvfp4_pertensor(a[0], a[1], a[2], to_dev(off), K, b[0], b[1], b[2], npg,
+                                     out=out,
+                                     out_dtype=bsg.BSG_OUT_F32 if out_f32 else bsg.BSG_OUT_BF16,
+                                     workspace=_workspace(rng))
+    y = bf16_out_to_f64(out)
+    for g, (rows, r) in enumerate(GM.nvfp4_pertensor_fprop(ap, asc, aam, off, bp, bsc, bam, npg, K)):
+        if len(rows):
+            gemm_tolerance_check(y[rows][:, :npg[g]], r, out_f32, "seed %d group %d" % (seed, g))
+    assert np.all(np.isnan(y[live:]))
