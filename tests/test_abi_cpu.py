@@ -156,3 +156,56 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def _prototypes():
+    """(name, [(type, arg name)]) of every function include/bsg.h declares."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = []
+    for m in re.finditer(r"\b(?:int|size_t|const char\*)\s+(\w+)\s*\(([^)]*)\)\s*;", text):
+        params = [p.strip() for p in m.group(2).replace("\n", " ").split(",") if p.strip()]
+        if params == ["void"]:
+            params = []
+        args = []
+        for p in params:
+            t, name = re.match(r"(.*?)(\w+)$", p).groups()
+            args.append((t.strip(), name))
+        out.append((m.group(1), args))
+    return out
+
+
+_SIZES = {"G": 2, "rows_cap": 256, "cols": 128, "n": 128, "k": 128, "ld_out": 256,
+          "col_rows_cap": 512, "multiplier": 1, "pad_to": 1, "capacity": 0}
+
+
+def _call(lib, name, args, G, ptr):
+    vals = []
+    for t, a in args:
+        if "*" in t:
+            vals.append(ptr)
+        elif a == "G":
+            vals.append(G)
+        else:
+            vals.append(_SIZES.get(a, 0))
+    return getattr(lib, name)(*vals)
+
+
+def test_every_entry_point_validates_before_any_hip_call(lib):
+    """Every compute entry point returns a host validation error -- not success,
+    and not BSG_ERR_HIP (this container has no GPU, so a HIP call would fail
+    with it) -- when given NULL buffers, and when given G outside [1, 256] with
+    buffers present (host memory stands in for them: nothing may be read but
+    the [host] arrays, which hold zeros)."""
+    raw, p = _buf(1 << 16)
+    seen = 0
+    for name, args in _prototypes():
+        if not any("*" in t for t, _ in args):
+            continue                               # version, last error, workspace queries
+        rc = _call(lib, name, args, 2, None)
+        assert rc in (1, 2, 3, 4, 5), (name, rc, lib.bsg_last_error())
+        if any(a == "G" for _, a in args):
+            for G in (0, 257):
+                rc = _call(lib, name, args, G, p)
+                assert rc in (1, 2, 3, 4, 5), (name, G, rc, lib.bsg_last_error())
+        seen += 1
+    assert seen >= 20, seen
